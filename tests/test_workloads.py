@@ -1,0 +1,74 @@
+"""The seeded generators: determinism, shapes, tree validity and the
+statistics each workload promises."""
+import hashlib
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import CONFIGS, bf16_bits_to_f32, f32_to_bf16_bits, generate
+
+SMALL = {1: {}, 2: dict(prefix=40), 3: dict(B=3, prefix=40), 4: dict(B=2, prefix=40),
+         5: dict(B=6, prefix=(16, 90))}
+
+
+def digest(w):
+    h = hashlib.sha256()
+    for name in ("parents", "n_nodes", "prefix_len", "tok", "tgt", "q", "k_new", "v_new",
+                 "k_cache", "v_cache"):
+        h.update(np.ascontiguousarray(getattr(w, name)).tobytes())
+    return h.hexdigest()
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_same_seed_same_workload(cfg):
+    a = generate(cfg, **SMALL[cfg])
+    b = generate(cfg, **SMALL[cfg])
+    c = generate(cfg, seed=1000 + cfg, **SMALL[cfg])
+    assert digest(a) == digest(b)
+    assert digest(a) != digest(c)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_shapes_and_trees(cfg):
+    w = generate(cfg, **SMALL[cfg])
+    c = CONFIGS[cfg]
+    assert w.q.shape == (w.B, c["n"], c["Hq"], c["D"])
+    assert w.k_cache.shape == (w.B, c["Hkv"], w.cap, c["D"])
+    assert w.cap >= int(w.prefix_len.max()) + w.n_max
+    for b in range(w.B):
+        n = int(w.n_nodes[b])
+        assert n == c["n"]
+        par = [int(x) for x in w.parents[b, :n]]
+        assert oracle.tree_is_valid(par)
+        assert max(oracle.tree_depth(par)) <= c["max_depth"]
+        for p in range(n):   # sibling tokens distinct
+            kids = [i for i in range(n) if par[i] == p]
+            assert len({int(w.tok[b, i]) for i in kids}) == len(kids)
+    if cfg == 4:
+        assert (w.parents == w.parents[0]).all()
+
+
+def test_bf16_rounding_is_nearest_even():
+    x = np.array([1.0, 1.00390625, 1.01171875, -2.5, 3.0e-3], dtype=np.float32)
+    bits = f32_to_bf16_bits(x)
+    back = bf16_bits_to_f32(bits)
+    # 1 + 2^-8 is a tie between 1 and 1 + 2^-7: even mantissa (1.0) wins
+    assert back[1] == 1.0
+    # 1 + 3*2^-8 is a tie between 1+2^-7 and 1+2^-6: even mantissa (1+2^-6) wins
+    assert back[2] == np.float32(1.015625)
+    assert back[0] == 1.0 and back[3] == -2.5
+    assert abs(back[4] - 3.0e-3) <= 2 ** -8 * 3.0e-3   # half an ulp at 8 significant bits
+
+
+def test_eagle_tree_acceptance_follows_path_confidence():
+    # a kept node is accepted with probability equal to its path confidence;
+    # check the mean accepted depth against the mean over the generator's own
+    # draws over many seeds (loose statistical bound)
+    lens = []
+    for s in range(300):
+        w = generate(3, seed=s, B=1, prefix=8)
+        acc = oracle.accept(w.tok, w.tgt, w.parents, w.n_nodes)[0]
+        lens.append(int(acc[0]))
+    m = np.mean(lens)
+    assert 1.0 < m < 6.0
