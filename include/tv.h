@@ -1,0 +1,203 @@
+/*
+ * tv.h -- C ABI of the draft-tree verification library (libtv.so, gfx950).
+ *
+ * One verification step of self-speculative decoding (Medusa / EAGLE): the
+ * target model scores a whole flattened draft tree in one pass, keeps the
+ * longest root path it agrees with, and keeps only that path's KV.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [MEDUSA-EAGLE] "Medusa and EAGLE: self-speculative decoding heads,
+ *                  explained" (pofe.ai), "Medusa: heads, losses and trees".
+ *   [MEDUSA-EXPL]  "Medusa, explained" (vibeengines.com), steps 6 and 7.
+ *   [INFRA-5.3]    "5.3 Medusa、EAGLE 与 MTP" (infra-guide), sections 3.1,
+ *                  3.2, 8 and 9.2.
+ *   [DRAFTERS]     "Drafters: draft models, Medusa, EAGLE, MTP, DFlash,
+ *                  DSpark" (robertz.co), "Why the answer does not change".
+ *
+ * Conventions for every call:
+ *   - Every pointer argument is DEVICE memory owned by the caller, except the
+ *     args struct of tv_tree_attention, which is host memory read during the
+ *     call only. The library never allocates or frees device memory on these
+ *     paths and keeps no per-call state.
+ *   - Every call is asynchronous on the given HIP stream (0 = null stream)
+ *     and never synchronises. The return value reports host-side argument
+ *     checks and launch errors only.
+ *   - Data-dependent problems are reported per sequence in a device array
+ *     `err[B]` (0 = ok, TV_ERR_BAD_TREE, TV_ERR_CAPACITY). Later calls treat
+ *     a sequence with err != 0 as inactive.
+ *   - Trees: node 0 is the root (the last verified token), parents[b][0] ==
+ *     -1 and 0 <= parents[b][i] < i for 1 <= i < n_nodes[b]; nodes
+ *     n_nodes[b] .. n_max-1 are padding and ignored. n_nodes[b] == 0 marks an
+ *     inactive sequence. At most TV_MAX_NODES nodes per tree.
+ *   - Integer arrays are int32 unless noted; tensors are row-major in the
+ *     shapes given, all of one dtype (TV_F32 or TV_BF16).
+ */
+#ifndef TV_H
+#define TV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TV_MAX_NODES 64
+
+typedef enum tv_status {
+  TV_OK = 0,
+  TV_ERR_INVALID_ARG = 1,   /* null pointer, bad size or bad enum          */
+  TV_ERR_BAD_TREE = 2,      /* per-sequence only: parents not a tree        */
+  TV_ERR_CAPACITY = 3,      /* per-sequence only: prefix + tree > cache     */
+  TV_ERR_UNSUPPORTED = 4,   /* valid but not implemented (e.g. head dim)    */
+  TV_ERR_HIP = 5            /* a HIP launch or runtime call failed          */
+} tv_status;
+
+typedef enum tv_dtype { TV_F32 = 0, TV_BF16 = 1 } tv_dtype;
+
+/* Human-readable name of a status code (static string). */
+const char* tv_status_string(tv_status s);
+
+/* Library version string (static). */
+const char* tv_version(void);
+
+/*
+ * tv_build_tree -- parents array -> ancestor bitmask and depth per node.
+ *
+ * Defines the tree mask of [INFRA-5.3] section 3.1 (a node sees the shared
+ * prefix, its ancestors and itself; siblings and other branches are hidden)
+ * and the depth-based position ids of section 3.2 / [MEDUSA-EXPL] step 6.
+ *
+ *   parents  [B][n_max]  parent index of each node (see conventions)
+ *   n_nodes  [B]         live nodes per sequence, 0 <= n_nodes[b] <= n_max
+ *   anc      [B][n_max]  uint64 out: bit j set iff node j is node i or an
+ *                        ancestor of it (least significant bit = node 0)
+ *   depth    [B][n_max]  out: edges from the root (root = 0)
+ *   err      [B]         out: 0, or TV_ERR_BAD_TREE if the tree is not laid
+ *                        out parents-first or n_nodes is out of range
+ * Padding nodes, and every node of a bad tree, get anc = 0 and depth = 0.
+ * Host checks: pointers non-null (unless B == 0), B >= 0,
+ * 1 <= n_max <= TV_MAX_NODES. B == 0 is a no-op.
+ */
+tv_status tv_build_tree(const int32_t* parents, const int32_t* n_nodes, int32_t B,
+                        int32_t n_max, uint64_t* anc, int32_t* depth, int32_t* err,
+                        hipStream_t stream);
+
+/*
+ * tv_tree_attention -- tree-masked GQA attention of every tree node over the
+ * shared-prefix KV cache plus its own ancestors, one attention layer.
+ *
+ * For node i of sequence b (P = prefix_len[b]) and query head h, with KV head
+ * g = h / (Hq / Hkv): the keys are the P prefix keys of head g followed by the
+ * keys of the nodes on the root..i path, RoPE-rotated at position P + depth;
+ * the query is rotated at P + depth[i]; output = softmax(scale * q.K) V.
+ * This is [INFRA-5.3] sections 3.1-3.2 and [MEDUSA-EAGLE] ("Trees"): every
+ * node shares the prefix KV and sees only its ancestors.
+ *
+ * Side effect (the tree's temporary KV, [INFRA-5.3] section 3.2): cache slots
+ * [P, P + n_nodes[b]) of every KV head receive the rotated tree keys and the
+ * raw tree values in flattened node order (rounded to the cache dtype).
+ * Prefix slots [0, P) are read only; they must already hold rotated keys.
+ */
+typedef struct tv_attn_args {
+  const void* q;          /* [B][n_max][Hq][D]   tree queries, before RoPE   */
+  const void* k_new;      /* [B][n_max][Hkv][D]  tree keys, before RoPE      */
+  const void* v_new;      /* [B][n_max][Hkv][D]  tree values                 */
+  void* k_cache;          /* [B][Hkv][cap][D]    prefix keys (rotated)       */
+  void* v_cache;          /* [B][Hkv][cap][D]    prefix values               */
+  const int32_t* prefix_len;  /* [B] P, 0 <= P                               */
+  const int32_t* n_nodes;     /* [B]                                         */
+  const uint64_t* anc;        /* [B][n_max] from tv_build_tree               */
+  const int32_t* depth;       /* [B][n_max] from tv_build_tree               */
+  int32_t* err;               /* [B] in/out: sequences with err != 0 are
+                                 skipped (output rows zero); set to
+                                 TV_ERR_CAPACITY when P + n_nodes > cap      */
+  void* out;              /* [B][n_max][Hq][D]   attention output; rows of
+                             padding nodes and skipped sequences are zero    */
+  void* workspace;        /* device scratch, >= tv_tree_attention_workspace_size
+                             bytes (may be NULL when that size is 0)         */
+  size_t workspace_bytes;
+  int32_t B, n_max, Hq, Hkv, D, cap;
+  int32_t dtype;          /* tv_dtype                                        */
+  float rope_theta;       /* RoPE base (rotate-half pairing); 0 = no RoPE    */
+  float softmax_scale;    /* <= 0 selects 1/sqrt(D)                          */
+} tv_attn_args;
+
+/*
+ * Workspace bytes tv_tree_attention needs for these shapes (0 if none).
+ * Depends only on B, n_max, Hq, Hkv, D, cap and dtype. Returns 0 and leaves
+ * nothing set for arguments tv_tree_attention would reject.
+ */
+size_t tv_tree_attention_workspace_size(const tv_attn_args* a);
+
+/*
+ * Host checks: a non-null; tensor pointers non-null unless B == 0;
+ * 1 <= n_max <= TV_MAX_NODES; Hq % Hkv == 0; D in {64, 128} (TV_BF16 needs
+ * D == 128); cap >= n_max; workspace large enough. B == 0 is a no-op.
+ */
+tv_status tv_tree_attention(const tv_attn_args* a, hipStream_t stream);
+
+/*
+ * tv_accept -- greedy longest-accepted-path selection.
+ *
+ * Under greedy decoding a drafted token is kept iff it equals the target's
+ * own argmax ([MEDUSA-EAGLE] "Typical acceptance", [DRAFTERS]); the longest
+ * fully valid root path is kept ([MEDUSA-EXPL] step 7); checking stops at the
+ * first miss on a path ([INFRA-5.3] section 9.2). Readings fixed here:
+ *   - tgt_argmax[b][i] is the target's argmax computed AT node i (it predicts
+ *     the token after i); node c >= 1 is valid iff cand_tok[b][c] ==
+ *     tgt_argmax[b][parent(c)], and accepted iff valid and its parent is
+ *     accepted; the root is always accepted;
+ *   - the deepest accepted node e wins; equal depths go to the lower index;
+ *   - accept_len = depth(e) = accepted drafted tokens; the step emits
+ *     accept_len + 1 tokens, the last being the bonus tgt_argmax[b][e].
+ *
+ *   cand_tok   [B][n_max]  token of each node ([0] = root token, unused)
+ *   tgt_argmax [B][n_max]
+ *   parents, anc, depth, n_nodes as from tv_build_tree
+ *   err        [B] or NULL: sequences with err != 0 are skipped
+ *   accept_len [B]         out; -1 for skipped or empty sequences
+ *   path       [B][n_max]  out: nodes root..e (ascending), then -1
+ *   bonus_tok  [B]         out; -1 for skipped sequences
+ *   out_tokens [B][n_max]  out, may be NULL: the accept_len + 1 emitted
+ *                          tokens (drafted tokens of path[1..], then bonus),
+ *                          then -1
+ * Host checks as tv_build_tree. B == 0 is a no-op.
+ */
+tv_status tv_accept(const int32_t* cand_tok, const int32_t* tgt_argmax,
+                    const int32_t* parents, const uint64_t* anc, const int32_t* depth,
+                    const int32_t* n_nodes, const int32_t* err, int32_t B, int32_t n_max,
+                    int32_t* accept_len, int32_t* path, int32_t* bonus_tok,
+                    int32_t* out_tokens, hipStream_t stream);
+
+/*
+ * tv_commit -- keep the accepted path's KV in place, drop the other branches.
+ *
+ * [INFRA-5.3] section 3.2 and summary: only the accepted path is committed.
+ * For each sequence with accept_len[b] = L >= 0 and P = prefix_len_in[b]:
+ * slot P + d <- slot P + path[b][d] for d = 0..L, every KV head, K and V, as
+ * one simultaneous move (all sources read before any slot is written); then
+ * prefix_len_out[b] = P + L + 1. Sequences with L < 0 are copied through
+ * unchanged. Slots from P + L + 1 on are left as they were (free space).
+ *
+ *   k_cache, v_cache [B][Hkv][cap][D]  in place
+ *   prefix_len_in    [B]
+ *   accept_len, path as from tv_accept (path rows of length n_max)
+ *   prefix_len_out   [B] out; may be the same array as prefix_len_in
+ * Host checks: pointers non-null unless B == 0, Hkv >= 1, D in {64, 128},
+ * 1 <= n_max <= TV_MAX_NODES, cap >= n_max, dtype valid. Device side,
+ * a path that would read or write outside [P, cap) leaves that sequence
+ * unchanged.
+ */
+tv_status tv_commit(void* k_cache, void* v_cache, int32_t B, int32_t Hkv, int32_t cap,
+                    int32_t D, int32_t dtype, const int32_t* prefix_len_in,
+                    const int32_t* accept_len, const int32_t* path, int32_t n_max,
+                    int32_t* prefix_len_out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TV_H */

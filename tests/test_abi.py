@@ -1,0 +1,107 @@
+"""The C ABI library: it loads, exports every symbol include/tv.h declares,
+and rejects bad arguments on the host before any device call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tree_attention_verification_tv_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tv.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
+                                reason="libtv.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tv_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_expected_calls():
+    names = declared_functions()
+    for must in ("tv_build_tree", "tv_tree_attention", "tv_accept", "tv_commit"):
+        assert must in names
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    lib = _lib.load()
+    names = declared_functions()
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(_lib.SIGNATURES), "binding and header disagree"
+
+
+def test_status_strings_and_version():
+    lib = _lib.load()
+    assert lib.tv_version().decode().startswith("tv ")
+    for code in range(6):
+        assert lib.tv_status_string(code)
+    assert lib.tv_status_string(_lib.TV_ERR_CAPACITY).decode().startswith("prefix")
+
+
+def test_struct_layout_matches_header_order():
+    # pointers first, then size_t, then the int32 / float fields
+    offs = [f[0] for f in _lib.TvAttnArgs._fields_]
+    assert offs[0] == "q" and offs[-1] == "softmax_scale"
+    assert ctypes.sizeof(_lib.TvAttnArgs) == 12 * 8 + 8 + 7 * 4 + 2 * 4 + 4  # padded to 8
+
+
+def test_host_validation_without_device():
+    lib = _lib.load()
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails its checks
+    null = None
+    # build_tree
+    assert lib.tv_build_tree(fake, fake, -1, 5, fake, fake, fake, null) == _lib.TV_ERR_INVALID_ARG
+    assert lib.tv_build_tree(fake, fake, 1, 0, fake, fake, fake, null) == _lib.TV_ERR_INVALID_ARG
+    assert lib.tv_build_tree(fake, fake, 1, 65, fake, fake, fake, null) == _lib.TV_ERR_INVALID_ARG
+    assert lib.tv_build_tree(null, fake, 1, 5, fake, fake, fake, null) == _lib.TV_ERR_INVALID_ARG
+    assert lib.tv_build_tree(null, null, 0, 5, null, null, null, null) == _lib.TV_OK   # empty batch
+    # accept
+    assert lib.tv_accept(fake, fake, fake, fake, fake, fake, null, 1, 70, fake, fake, fake, null,
+                         null) == _lib.TV_ERR_INVALID_ARG
+    assert lib.tv_accept(fake, fake, fake, fake, fake, fake, null, 1, 5, null, fake, fake, null,
+                         null) == _lib.TV_ERR_INVALID_ARG
+    assert lib.tv_accept(null, null, null, null, null, null, null, 0, 5, null, null, null, null,
+                         null) == _lib.TV_OK
+    # commit
+    assert lib.tv_commit(fake, fake, 1, 0, 10, 128, 1, fake, fake, fake, 5, fake, null) == _lib.TV_ERR_INVALID_ARG
+    assert lib.tv_commit(fake, fake, 1, 2, 4, 128, 1, fake, fake, fake, 5, fake, null) == _lib.TV_ERR_INVALID_ARG
+    assert lib.tv_commit(fake, fake, 1, 2, 10, 96, 1, fake, fake, fake, 5, fake, null) == _lib.TV_ERR_UNSUPPORTED
+    assert lib.tv_commit(fake, fake, 1, 2, 10, 128, 7, fake, fake, fake, 5, fake, null) == _lib.TV_ERR_INVALID_ARG
+    assert lib.tv_commit(null, fake, 1, 2, 10, 128, 1, fake, fake, fake, 5, fake, null) == _lib.TV_ERR_INVALID_ARG
+
+
+def attn(**kw):
+    a = _lib.TvAttnArgs()
+    for f in ("q", "k_new", "v_new", "k_cache", "v_cache", "prefix_len", "n_nodes", "anc", "depth",
+              "err", "out"):
+        setattr(a, f, 0x1000)
+    a.B, a.n_max, a.Hq, a.Hkv, a.D, a.cap, a.dtype = 8, 60, 32, 8, 128, 4156, _lib.TV_BF16
+    a.rope_theta, a.softmax_scale = 10000.0, 0.0
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_attention_host_validation_and_workspace():
+    lib = _lib.load()
+    run = lambda a: lib.tv_tree_attention(ctypes.byref(a), None)   # noqa: E731
+    assert lib.tv_tree_attention(None, None) == _lib.TV_ERR_INVALID_ARG
+    assert run(attn(Hq=30)) == _lib.TV_ERR_INVALID_ARG           # Hq % Hkv
+    assert run(attn(n_max=65)) == _lib.TV_ERR_INVALID_ARG
+    assert run(attn(cap=10)) == _lib.TV_ERR_INVALID_ARG
+    assert run(attn(D=64)) == _lib.TV_ERR_UNSUPPORTED            # bf16 needs D = 128
+    assert run(attn(dtype=_lib.TV_F32, D=96)) == _lib.TV_ERR_UNSUPPORTED
+    assert run(attn(dtype=9)) == _lib.TV_ERR_INVALID_ARG
+    assert run(attn(q=None)) == _lib.TV_ERR_INVALID_ARG
+    assert run(attn(B=0)) == _lib.TV_OK
+    # the headline shape splits the prefix, so it needs a workspace
+    need = lib.tv_tree_attention_workspace_size(ctypes.byref(attn()))
+    assert need > 0
+    assert run(attn(workspace=0x1000, workspace_bytes=need - 1)) == _lib.TV_ERR_INVALID_ARG
+    assert lib.tv_tree_attention_workspace_size(ctypes.byref(attn(dtype=_lib.TV_F32))) == 0
+    assert lib.tv_tree_attention_workspace_size(ctypes.byref(attn(Hq=30))) == 0

@@ -1,0 +1,272 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle.
+
+Integer results (ancestor words, depths, error codes, accepted length, path,
+bonus, emitted tokens, committed cache bytes, new prefix lengths) must match
+bit for bit. Attention outputs must be within 2e-2 max abs error for bf16
+inputs and within 1e-5 max row-relative error for fp32 inputs. Appended cache
+keys are the rotated tree keys rounded to the cache dtype: within half a bf16
+ulp plus the fp32 rotation error (fp32: 1e-6); appended values are exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_util import attention_error, host_f64, run_step, tolerance, upload
+from tests.test_oracle_tree import all_trees
+from workloads import bf16_bits_to_f32, f32_to_bf16_bits, generate
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def cache_bits(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy().view(np.uint32)
+
+
+def check_step(w, res, rows=None, untouched=True):
+    """Compares every output of one step with the oracle (rows: sample of
+    (b, i) for the attention; None = all). untouched: also check that the
+    attention wrote no cache slot outside [P, P + n) of live sequences."""
+    ref_anc, ref_depth, ref_err = oracle.build_tree(w.parents, w.n_nodes)
+    assert np.array_equal(res["anc"], ref_anc)
+    assert np.array_equal(res["depth"], ref_depth)
+    acc, path, bonus, toks = oracle.accept(w.tok, w.tgt, w.parents, w.n_nodes, err_in=res["err"])
+    assert np.array_equal(res["accept_len"], acc)
+    assert np.array_equal(res["path"], path)
+    assert np.array_equal(res["bonus"], bonus)
+    assert np.array_equal(res["out_tokens"], toks)
+
+    # attention, one sequence at a time (keeps the oracle's copies small)
+    worst = 0.0
+    err_after = np.array(ref_err, copy=True)
+    for b in range(w.B):
+        sub_rows = None
+        if rows is not None:
+            sub_rows = [(0, i) for (bb, i) in rows if bb == b]
+            if not sub_rows:
+                continue
+        inp = w.oracle_inputs(b)
+        out, kc, vc, e = oracle.tree_attention(inp["q"], inp["k_new"], inp["v_new"], inp["k_cache"],
+                                               inp["v_cache"], inp["prefix_len"], inp["n_nodes"],
+                                               inp["parents"], w.rope_theta, 0.0,
+                                               err_in=ref_err[b:b + 1], rows=sub_rows)
+        err_after[b] = e[0]
+        sel = [i for (_, i) in sub_rows] if sub_rows is not None else list(range(w.n_max))
+        got = res["out"][b, sel]
+        worst = max(worst, attention_error(w.dtype, got, out[0, sel]))
+        # appended tree KV in the cache
+        n, P = int(w.n_nodes[b]), int(w.prefix_len[b])
+        if e[0] == 0 and n > 0:
+            kg = host_f64(res["k_after_attn"][b, :, P:P + n])
+            vg = cache_bits(res["v_after_attn"][b, :, P:P + n])
+            vref = w.v_new[b, :n].transpose(1, 0, 2)
+            assert np.array_equal(vg, vref.view(vg.dtype)), f"appended V of sequence {b}"
+            kref = kc[0, :, P:P + n]
+            if w.dtype == "bf16":
+                # the kernel rotates in fp32 (error a few 2^-24 of |x| ~ 1e-6
+                # absolute, which near a cancellation spans several bf16 ulps
+                # of a tiny result), then rounds to bf16 (half an ulp <= 2^-8
+                # relative)
+                assert np.all(np.abs(kg - kref) <= 2.0 ** -8 * np.abs(kref) + 1e-5), \
+                    f"appended K of sequence {b}"
+            else:
+                assert np.allclose(kg, kref, rtol=1e-6, atol=1e-6), f"appended K of sequence {b}"
+    assert worst <= tolerance(w.dtype), f"attention error {worst}"
+    assert np.array_equal(res["err"], err_after)
+    if untouched:
+        for name in ("k", "v"):
+            got = cache_bits(res[f"{name}_after_attn"])
+            orig = getattr(w, f"{name}_cache").view(got.dtype)
+            for b in range(w.B):
+                n, P = int(w.n_nodes[b]), int(w.prefix_len[b])
+                if err_after[b] == 0 and n > 0:
+                    assert np.array_equal(got[b, :, :P], orig[b, :, :P])
+                    assert np.array_equal(got[b, :, P + n:], orig[b, :, P + n:])
+                else:
+                    assert np.array_equal(got[b], orig[b])
+    return worst
+
+
+def check_commit(w, res, k_final: torch.Tensor, v_final: torch.Tensor):
+    """Commit is a pure copy: compare with the oracle's commit applied to the
+    library's own post-attention cache, bit for bit."""
+    kb = cache_bits(res["k_after_attn"])
+    vb = cache_bits(res["v_after_attn"])
+    k_exp, v_exp, plen = oracle.commit(kb, vb, w.prefix_len, res["accept_len"], res["path"])
+    assert np.array_equal(res["prefix_len_out"], plen)
+    assert np.array_equal(cache_bits(k_final), k_exp)
+    assert np.array_equal(cache_bits(v_final), v_exp)
+
+
+SMALL = [
+    (1, {}),
+    (2, dict(prefix=300)),
+    (3, dict(B=3, prefix=150)),
+    (3, dict(B=2, prefix=1100)),       # several KV splits, ragged last tile
+    (4, dict(B=2, prefix=200)),        # 512 rows per KV head: two row blocks
+    (5, dict(B=6, prefix=(16, 300))),  # ragged prefixes
+    (2, dict(prefix=0)),               # no prefix: the tree alone
+    (5, dict(B=3, prefix=(1, 70), n=7)),
+]
+
+
+@pytest.mark.parametrize("cfg,over", SMALL, ids=[f"cfg{c}-{i}" for i, (c, _) in enumerate(SMALL)])
+def test_small_workloads_full_parity(cfg, over):
+    print(f"[gpu] small workload cfg={cfg} {over}", flush=True)
+    w = generate(cfg, **over)
+    d = upload(w, DEV)
+    res = run_step(w, d)
+    worst = check_step(w, res)
+    check_commit(w, res, d["k_cache"], d["v_cache"])
+    print(f"  attention error {worst:.3g}; accepted {res['accept_len'].tolist()}", flush=True)
+
+
+def sample_rows(w, per_seq=3, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = []
+    for b in range(w.B):
+        n = int(w.n_nodes[b])
+        depth = oracle.tree_depth([int(x) for x in w.parents[b, :n]])
+        cand = {0, n - 1, int(np.argmax(depth))}
+        cand |= set(int(x) for x in rng.choice(n, size=min(per_seq, n), replace=False))
+        rows += [(b, i) for i in sorted(cand)]
+    return rows
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_full_size_workloads_sampled(cfg):
+    """The workloads at their full sizes, in the launch configuration the
+    benchmark times; attention checked on sampled rows of every sequence."""
+    print(f"[gpu] full workload cfg={cfg}", flush=True)
+    w = generate(cfg)
+    d = upload(w, DEV)
+    k0, v0 = d["k_cache"].clone(), d["v_cache"].clone()
+    res = run_step(w, d)
+    per = 3 if cfg in (3, 5) else 2
+    rows = sample_rows(w, per_seq=per) if cfg != 2 else None
+    if cfg == 5:
+        rows = [r for r in rows if r[0] % 4 == 0]
+    worst = check_step(w, res, rows=rows, untouched=False)
+    # commit on the device: prefix slots untouched, path slots moved
+    for b in range(w.B):
+        P, L = int(w.prefix_len[b]), int(res["accept_len"][b])
+        assert torch.equal(d["k_cache"][b, :, :P], k0[b, :, :P])
+        assert torch.equal(d["v_cache"][b, :, :P], v0[b, :, :P])
+        src = torch.as_tensor(res["path"][b, :L + 1], device=DEV, dtype=torch.long) + P
+        assert torch.equal(d["k_cache"][b, :, P:P + L + 1], res["k_after_attn"][b, :, src])
+        assert torch.equal(d["v_cache"][b, :, P:P + L + 1], res["v_after_attn"][b, :, src])
+        assert res["prefix_len_out"][b] == P + L + 1
+    print(f"  attention error {worst:.3g}; mean accepted {res['accept_len'].mean():.2f}", flush=True)
+
+
+def test_edge_cases_batch():
+    """One batch mixing a normal tree, a single node, an inactive slot, a bad
+    tree and a tree that does not fit in the cache."""
+    print("[gpu] edge-case batch", flush=True)
+    w = generate(3, B=6, prefix=40)
+    w.n_nodes[1] = 1                    # plain decode step
+    w.parents[1, 1:] = -1
+    w.n_nodes[2] = 0                    # inactive slot
+    w.parents[3, 5] = 7                 # parent after child: bad tree
+    w.prefix_len[4] = w.cap - 10        # prefix + 60 nodes > capacity
+    w.prefix_len[5] = 0                 # no prefix
+    d = upload(w, DEV)
+    res = run_step(w, d)
+    assert res["err"].tolist() == [0, 0, 0, 2, 3, 0]
+    check_step(w, res)
+    check_commit(w, res, d["k_cache"], d["v_cache"])
+    assert (res["out"][2] == 0).all() and (res["out"][3] == 0).all() and (res["out"][4] == 0).all()
+    assert res["accept_len"][1] == 0 and res["path"][1, 0] == 0
+    assert res["accept_len"].tolist()[2:5] == [-1, -1, -1]
+
+
+def test_deep_chain_and_wide_star():
+    """A 64-node chain (depth 63) and a 64-node star in one batch, G = 1."""
+    print("[gpu] chain and star", flush=True)
+    w = generate(2, B=2, prefix=130)
+    w.parents[0] = [-1] + list(range(63))
+    w.parents[1] = [-1] + [0] * 63
+    w.tgt[0, :63] = w.tok[0, 1:]        # the chain is fully accepted
+    d = upload(w, DEV)
+    res = run_step(w, d)
+    check_step(w, res)
+    check_commit(w, res, d["k_cache"], d["v_cache"])
+    assert res["accept_len"][0] == 63
+
+
+def test_all_small_trees_one_batch():
+    """Every tree with 1..5 nodes in one batch (34 sequences), fp32."""
+    print("[gpu] all trees up to 5 nodes", flush=True)
+    trees = [t for n in range(1, 6) for t in all_trees(n)]
+    B = len(trees)
+    w = generate(1, B=B, prefix=33)
+    rng = np.random.default_rng(7)
+    for b, t in enumerate(trees):
+        w.parents[b] = -1
+        w.parents[b, :len(t)] = t
+        w.n_nodes[b] = len(t)
+        for i in range(1, len(t)):          # random agreement pattern
+            if rng.random() < 0.6:
+                w.tok[b, i] = w.tgt[b, t[i]]
+    d = upload(w, DEV)
+    res = run_step(w, d)
+    check_step(w, res)
+    check_commit(w, res, d["k_cache"], d["v_cache"])
+
+
+def test_accept_brute_force_seven_nodes():
+    """Every tree with 7 nodes x 8 agreement patterns, acceptance bit-exact."""
+    import tree_attention_verification_tv_amd as tv
+    print("[gpu] accept over all 7-node trees", flush=True)
+    trees = list(all_trees(7))
+    rng = np.random.default_rng(1)
+    rows_p, rows_tok, rows_tgt = [], [], []
+    for t in trees:
+        for _ in range(8):
+            tgt = np.arange(7, dtype=np.int32) + 1000
+            tok = np.full(7, 9, dtype=np.int32)
+            for i in range(1, 7):
+                tok[i] = tgt[t[i]] if rng.random() < 0.7 else 5000 + i
+            rows_p.append(t)
+            rows_tok.append(tok)
+            rows_tgt.append(tgt)
+    P = np.array(rows_p, dtype=np.int32)
+    tok = np.stack(rows_tok)
+    tgt = np.stack(rows_tgt)
+    nn = np.full(len(P), 7, dtype=np.int32)
+    dP, dn = torch.from_numpy(P).to(DEV), torch.from_numpy(nn).to(DEV)
+    anc, depth, err = tv.build_tree(dP, dn)
+    acc, path, bonus, toks = tv.accept(torch.from_numpy(tok).to(DEV), torch.from_numpy(tgt).to(DEV),
+                                       dP, anc, depth, dn, err)
+    ref = oracle.accept(tok, tgt, P, nn)
+    assert np.array_equal(acc.cpu().numpy(), ref[0])
+    assert np.array_equal(path.cpu().numpy(), ref[1])
+    assert np.array_equal(bonus.cpu().numpy(), ref[2])
+    assert np.array_equal(toks.cpu().numpy(), ref[3])
+
+
+def test_non_ancestors_leave_outputs_bit_identical():
+    """Changing a node's q/k/v never changes the output of a node that is not
+    its descendant (the mask is exact, not approximate)."""
+    print("[gpu] non-ancestor independence", flush=True)
+    w = generate(3, B=1, prefix=200)
+    d = upload(w, DEV)
+    base = run_step(w, d)["out"]
+    n = int(w.n_nodes[0])
+    par = [int(x) for x in w.parents[0, :n]]
+    mask = oracle.tree_mask(par)
+    j = n - 1                          # a leaf: only it sees itself
+    w2 = generate(3, B=1, prefix=200)
+    if w2.dtype == "bf16":
+        for name in ("q", "k_new", "v_new"):
+            arr = getattr(w2, name)
+            arr[0, j] = f32_to_bf16_bits(bf16_bits_to_f32(arr[0, j]) * -3.0 + 1.0)
+    d2 = upload(w2, DEV)
+    out2 = run_step(w2, d2)["out"]
+    for i in range(n):
+        if not mask[i, j]:
+            assert np.array_equal(out2[0, i], base[0, i]), i
+    assert not np.array_equal(out2[0, j], base[0, j])

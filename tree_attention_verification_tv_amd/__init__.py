@@ -1,0 +1,183 @@
+"""Draft-tree verification for self-speculative decoding on MI355X (gfx950).
+
+Thin Python binding of libtv.so (include/tv.h). Each function checks and
+marshals torch tensors (device memory, current HIP stream) and calls the C
+ABI; every step of the verification runs in the HIP kernels. There is no CPU
+fallback: if the library is not built, the calls raise.
+
+Step order for one verification pass of one layer:
+    anc, depth, err = build_tree(parents, n_nodes)
+    out = tree_attention(q, k_new, v_new, k_cache, v_cache, prefix_len,
+                         n_nodes, anc, depth, err)
+    accept_len, path, bonus, tokens = accept(cand_tok, tgt_argmax, parents,
+                                             anc, depth, n_nodes, err)
+    new_prefix_len = commit(k_cache, v_cache, prefix_len, accept_len, path)
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import (TV_BF16, TV_ERR_BAD_TREE, TV_ERR_CAPACITY, TV_F32, TV_MAX_NODES,  # noqa: F401
+                   TvAttnArgs, TvError)
+
+__all__ = ["build_tree", "tree_attention", "tree_attention_workspace_size", "accept", "commit",
+           "version", "TvError", "TV_ERR_BAD_TREE", "TV_ERR_CAPACITY", "attn_args"]
+
+
+def version() -> str:
+    return _lib.load().tv_version().decode()
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    return t
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+_DTYPES = {torch.float32: TV_F32, torch.bfloat16: TV_BF16}
+
+
+def build_tree(parents: torch.Tensor, n_nodes: torch.Tensor, anc=None, depth=None, err=None,
+               stream=None):
+    """parents [B, n_max] int32, n_nodes [B] int32 -> (anc uint64 as int64
+    [B, n_max], depth int32 [B, n_max], err int32 [B])."""
+    lib = _lib.load()
+    _dev(parents, "parents", torch.int32)
+    _dev(n_nodes, "n_nodes", torch.int32)
+    B, n_max = parents.shape
+    dev = parents.device
+    anc = torch.empty((B, n_max), dtype=torch.int64, device=dev) if anc is None else _dev(anc, "anc", torch.int64)
+    depth = torch.empty((B, n_max), dtype=torch.int32, device=dev) if depth is None else _dev(depth, "depth", torch.int32)
+    err = torch.empty((B,), dtype=torch.int32, device=dev) if err is None else _dev(err, "err", torch.int32)
+    _lib.check("tv_build_tree", lib.tv_build_tree(_ptr(parents), _ptr(n_nodes), B, n_max, _ptr(anc),
+                                                  _ptr(depth), _ptr(err), _stream(stream)))
+    return anc, depth, err
+
+
+def attn_args(q, k_new, v_new, k_cache, v_cache, prefix_len, n_nodes, anc, depth, err, out,
+              rope_theta=10000.0, softmax_scale=0.0, workspace=None) -> TvAttnArgs:
+    """Checks the tensors of one tree_attention call and fills tv_attn_args."""
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"q must be float32 or bfloat16 (got {q.dtype})")
+    dt = q.dtype
+    for name, t in (("q", q), ("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache),
+                    ("v_cache", v_cache), ("out", out)):
+        _dev(t, name, dt)
+    for name, t in (("prefix_len", prefix_len), ("n_nodes", n_nodes), ("depth", depth), ("err", err)):
+        _dev(t, name, torch.int32)
+    _dev(anc, "anc", torch.int64)
+    B, n_max, Hq, D = q.shape
+    Hkv = k_new.shape[2]
+    cap = k_cache.shape[2]
+    if tuple(k_new.shape) != (B, n_max, Hkv, D) or tuple(v_new.shape) != (B, n_max, Hkv, D):
+        raise ValueError("k_new / v_new must be [B, n_max, Hkv, D]")
+    if tuple(k_cache.shape) != (B, Hkv, cap, D) or tuple(v_cache.shape) != (B, Hkv, cap, D):
+        raise ValueError("k_cache / v_cache must be [B, Hkv, cap, D]")
+    if tuple(out.shape) != (B, n_max, Hq, D):
+        raise ValueError("out must be [B, n_max, Hq, D]")
+    if tuple(anc.shape) != (B, n_max) or tuple(depth.shape) != (B, n_max):
+        raise ValueError("anc / depth must be [B, n_max]")
+    if prefix_len.numel() != B or n_nodes.numel() != B or err.numel() != B:
+        raise ValueError("prefix_len / n_nodes / err must have B entries")
+    a = TvAttnArgs()
+    a.q, a.k_new, a.v_new = q.data_ptr(), k_new.data_ptr(), v_new.data_ptr()
+    a.k_cache, a.v_cache = k_cache.data_ptr(), v_cache.data_ptr()
+    a.prefix_len, a.n_nodes = prefix_len.data_ptr(), n_nodes.data_ptr()
+    a.anc, a.depth, a.err, a.out = anc.data_ptr(), depth.data_ptr(), err.data_ptr(), out.data_ptr()
+    if workspace is not None:
+        _dev(workspace, "workspace", torch.uint8)
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
+    else:
+        a.workspace, a.workspace_bytes = None, 0
+    a.B, a.n_max, a.Hq, a.Hkv, a.D, a.cap = B, n_max, Hq, Hkv, D, cap
+    a.dtype = _DTYPES[dt]
+    a.rope_theta = float(rope_theta)
+    a.softmax_scale = float(softmax_scale)
+    return a
+
+
+def tree_attention_workspace_size(args: TvAttnArgs) -> int:
+    return int(_lib.load().tv_tree_attention_workspace_size(ctypes.byref(args)))
+
+
+def tree_attention(q, k_new, v_new, k_cache, v_cache, prefix_len, n_nodes, anc, depth, err,
+                   rope_theta=10000.0, softmax_scale=0.0, out=None, workspace=None, stream=None):
+    """Tree-masked attention of every node over prefix + ancestors; appends
+    the rotated tree K and raw tree V to cache slots [P, P + n). Returns out
+    [B, n_max, Hq, D] in the dtype of q."""
+    lib = _lib.load()
+    if out is None:
+        out = torch.empty_like(q)
+    a = attn_args(q, k_new, v_new, k_cache, v_cache, prefix_len, n_nodes, anc, depth, err, out,
+                  rope_theta, softmax_scale, workspace)
+    need = tree_attention_workspace_size(a)
+    if need > a.workspace_bytes:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), need
+    _lib.check("tv_tree_attention", lib.tv_tree_attention(ctypes.byref(a), _stream(stream)))
+    return out
+
+
+def accept(cand_tok, tgt_argmax, parents, anc, depth, n_nodes, err=None, accept_len=None, path=None,
+           bonus=None, out_tokens=None, want_tokens=True, stream=None):
+    """Greedy longest accepted path -> (accept_len [B], path [B, n_max],
+    bonus [B], out_tokens [B, n_max] or None), all int32."""
+    lib = _lib.load()
+    for name, t in (("cand_tok", cand_tok), ("tgt_argmax", tgt_argmax), ("parents", parents),
+                    ("depth", depth), ("n_nodes", n_nodes)):
+        _dev(t, name, torch.int32)
+    _dev(anc, "anc", torch.int64)
+    if err is not None:
+        _dev(err, "err", torch.int32)
+    B, n_max = parents.shape
+    dev = parents.device
+    accept_len = torch.empty(B, dtype=torch.int32, device=dev) if accept_len is None else accept_len
+    path = torch.empty((B, n_max), dtype=torch.int32, device=dev) if path is None else path
+    bonus = torch.empty(B, dtype=torch.int32, device=dev) if bonus is None else bonus
+    if want_tokens and out_tokens is None:
+        out_tokens = torch.empty((B, n_max), dtype=torch.int32, device=dev)
+    _lib.check("tv_accept", lib.tv_accept(_ptr(cand_tok), _ptr(tgt_argmax), _ptr(parents), _ptr(anc),
+                                          _ptr(depth), _ptr(n_nodes), _ptr(err), B, n_max,
+                                          _ptr(accept_len), _ptr(path), _ptr(bonus), _ptr(out_tokens),
+                                          _stream(stream)))
+    return accept_len, path, bonus, out_tokens
+
+
+def commit(k_cache, v_cache, prefix_len_in, accept_len, path, prefix_len_out=None, stream=None):
+    """Moves the accepted path's KV to slots [P, P + L + 1) in place; returns
+    the new prefix lengths (prefix_len_out, which may be prefix_len_in)."""
+    lib = _lib.load()
+    if k_cache.dtype not in _DTYPES:
+        raise ValueError("cache must be float32 or bfloat16")
+    _dev(k_cache, "k_cache", k_cache.dtype)
+    _dev(v_cache, "v_cache", k_cache.dtype)
+    for name, t in (("prefix_len_in", prefix_len_in), ("accept_len", accept_len), ("path", path)):
+        _dev(t, name, torch.int32)
+    B, Hkv, cap, D = k_cache.shape
+    n_max = path.shape[1]
+    if prefix_len_out is None:
+        prefix_len_out = torch.empty_like(prefix_len_in)
+    _dev(prefix_len_out, "prefix_len_out", torch.int32)
+    _lib.check("tv_commit", lib.tv_commit(_ptr(k_cache), _ptr(v_cache), B, Hkv, cap, D,
+                                          _DTYPES[k_cache.dtype], _ptr(prefix_len_in), _ptr(accept_len),
+                                          _ptr(path), n_max, _ptr(prefix_len_out), _stream(stream)))
+    return prefix_len_out

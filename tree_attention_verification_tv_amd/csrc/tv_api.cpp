@@ -1,0 +1,101 @@
+// C ABI of libtv: host-side argument checks, launch planning and dispatch.
+// Every check happens before the first HIP call, so invalid arguments are
+// reported without touching the device.
+#include <hip/hip_runtime.h>
+
+#include "tv.h"
+#include "tv_internal.h"
+
+namespace {
+
+bool dtype_ok(int32_t d) { return d == TV_F32 || d == TV_BF16; }
+int elem_bytes(int32_t d) { return d == TV_F32 ? 4 : 2; }
+
+tv_status from_hip(hipError_t e) { return e == hipSuccess ? TV_OK : TV_ERR_HIP; }
+
+// Shapes of tv_tree_attention that the kernels accept.
+tv_status check_attn_shapes(const tv_attn_args* a) {
+  if (a == nullptr) return TV_ERR_INVALID_ARG;
+  if (a->B < 0 || a->n_max < 1 || a->n_max > TV_MAX_NODES) return TV_ERR_INVALID_ARG;
+  if (a->Hq < 1 || a->Hkv < 1 || a->Hq % a->Hkv != 0) return TV_ERR_INVALID_ARG;
+  if (a->cap < a->n_max || a->D < 1) return TV_ERR_INVALID_ARG;
+  if (!dtype_ok(a->dtype)) return TV_ERR_INVALID_ARG;
+  if (a->dtype == TV_BF16 && a->D != 128) return TV_ERR_UNSUPPORTED;
+  if (a->dtype == TV_F32 && a->D != 64 && a->D != 128) return TV_ERR_UNSUPPORTED;
+  return TV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tv_status_string(tv_status s) {
+  switch (s) {
+    case TV_OK: return "ok";
+    case TV_ERR_INVALID_ARG: return "invalid argument";
+    case TV_ERR_BAD_TREE: return "parents array is not a parents-first tree";
+    case TV_ERR_CAPACITY: return "prefix plus tree exceeds the cache capacity";
+    case TV_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case TV_ERR_HIP: return "HIP runtime or launch error";
+  }
+  return "unknown status";
+}
+
+const char* tv_version(void) { return "tv 0.1.0 (gfx950)"; }
+
+tv_status tv_build_tree(const int32_t* parents, const int32_t* n_nodes, int32_t B, int32_t n_max,
+                        uint64_t* anc, int32_t* depth, int32_t* err, hipStream_t stream) {
+  if (B < 0 || n_max < 1 || n_max > TV_MAX_NODES) return TV_ERR_INVALID_ARG;
+  if (B == 0) return TV_OK;
+  if (!parents || !n_nodes || !anc || !depth || !err) return TV_ERR_INVALID_ARG;
+  return from_hip(tv::launch_build_tree(parents, n_nodes, B, n_max, anc, depth, err, stream));
+}
+
+size_t tv_tree_attention_workspace_size(const tv_attn_args* a) {
+  if (check_attn_shapes(a) != TV_OK || a->B == 0) return 0;
+  if (a->dtype != TV_BF16) return 0;
+  return tv::plan_attention_bf16(a).workspace_bytes;
+}
+
+tv_status tv_tree_attention(const tv_attn_args* a, hipStream_t stream) {
+  const tv_status st = check_attn_shapes(a);
+  if (st != TV_OK) return st;
+  if (a->B == 0) return TV_OK;
+  if (!a->q || !a->k_new || !a->v_new || !a->k_cache || !a->v_cache || !a->prefix_len ||
+      !a->n_nodes || !a->anc || !a->depth || !a->err || !a->out)
+    return TV_ERR_INVALID_ARG;
+  if (a->dtype == TV_F32) return from_hip(tv::launch_attention_f32(a, stream));
+  const tv::AttnPlan plan = tv::plan_attention_bf16(a);
+  if (plan.workspace_bytes > 0 && (a->workspace == nullptr || a->workspace_bytes < plan.workspace_bytes))
+    return TV_ERR_INVALID_ARG;
+  return from_hip(tv::launch_attention_bf16(a, plan, stream));
+}
+
+tv_status tv_accept(const int32_t* cand_tok, const int32_t* tgt_argmax, const int32_t* parents,
+                    const uint64_t* anc, const int32_t* depth, const int32_t* n_nodes,
+                    const int32_t* err, int32_t B, int32_t n_max, int32_t* accept_len,
+                    int32_t* path, int32_t* bonus_tok, int32_t* out_tokens, hipStream_t stream) {
+  if (B < 0 || n_max < 1 || n_max > TV_MAX_NODES) return TV_ERR_INVALID_ARG;
+  if (B == 0) return TV_OK;
+  if (!cand_tok || !tgt_argmax || !parents || !anc || !depth || !n_nodes || !accept_len || !path ||
+      !bonus_tok)
+    return TV_ERR_INVALID_ARG;
+  return from_hip(tv::launch_accept(cand_tok, tgt_argmax, parents, anc, depth, n_nodes, err, B,
+                                    n_max, accept_len, path, bonus_tok, out_tokens, stream));
+}
+
+tv_status tv_commit(void* k_cache, void* v_cache, int32_t B, int32_t Hkv, int32_t cap, int32_t D,
+                    int32_t dtype, const int32_t* prefix_len_in, const int32_t* accept_len,
+                    const int32_t* path, int32_t n_max, int32_t* prefix_len_out,
+                    hipStream_t stream) {
+  if (B < 0 || Hkv < 1 || n_max < 1 || n_max > TV_MAX_NODES || cap < n_max) return TV_ERR_INVALID_ARG;
+  if (!dtype_ok(dtype)) return TV_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return TV_ERR_UNSUPPORTED;
+  if (B == 0) return TV_OK;
+  if (!k_cache || !v_cache || !prefix_len_in || !accept_len || !path || !prefix_len_out)
+    return TV_ERR_INVALID_ARG;
+  return from_hip(tv::launch_commit(k_cache, v_cache, B, Hkv, cap, D, elem_bytes(dtype),
+                                    prefix_len_in, accept_len, path, n_max, prefix_len_out, stream));
+}
+
+}  // extern "C"

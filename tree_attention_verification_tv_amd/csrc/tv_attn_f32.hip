@@ -1,0 +1,198 @@
+// fp32 tree-verification attention on the vector ALUs.
+//
+// Serves fp32 inputs, whose tolerance (1e-5 relative) rules out bf16 matrix
+// cores. Every tree node attends to the P prefix keys of its KV head and to
+// the keys of its ancestors-or-self, selected by the node's ancestor bitmask
+// (infra-guide "5.3 Medusa、EAGLE 与 MTP", section 3.1); queries and tree
+// keys are rotated at position P + depth (section 3.2).
+//
+// Grid (ceil(G*n_max/4), Hkv, B), 256 threads. The block first rotates the n
+// tree keys of its KV head into LDS (angles in double precision); the block
+// with blockIdx.x == 0 also appends them, and the raw tree values, to cache
+// slots [P, P+n). Each wavefront then computes one query row (node i, head
+// g*G + hh, rows ordered node-major): lane l owns key t0+l of each 64-key
+// tile for the scores and dims {l, l+64} of the output.
+#include <math.h>
+
+#include "tv_device.h"
+#include "tv_internal.h"
+
+namespace tv {
+
+namespace {
+
+struct F32Params {
+  const float* q;
+  const float* k_new;
+  const float* v_new;
+  float* k_cache;
+  float* v_cache;
+  const int32_t* prefix_len;
+  const int32_t* n_nodes;
+  const uint64_t* anc;
+  const int32_t* depth;
+  int32_t* err;
+  float* out;
+  int n_max, Hq, Hkv, G, D, cap;
+  float theta, scale;
+};
+
+__device__ __forceinline__ void rope_cs(int pos, int pair, int D, float theta, float* c, float* s) {
+  if (theta == 0.0f) {
+    *c = 1.0f;
+    *s = 0.0f;
+    return;
+  }
+  const double inv_freq = pow(static_cast<double>(theta), -2.0 * pair / D);
+  double sd, cd;
+  sincos(static_cast<double>(pos) * inv_freq, &sd, &cd);
+  *c = static_cast<float>(cd);
+  *s = static_cast<float>(sd);
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+__global__ __launch_bounds__(256) void attn_f32_kernel(F32Params p) {
+  __shared__ float ktree[TV_MAX_NODES_DEV][128];
+  __shared__ float qrow[4][128];
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int D = p.D, half = D / 2;
+  const int n = p.n_nodes[b];
+  const int P = p.prefix_len[b];
+  const int e_in = p.err[b];
+  const bool cap_bad = (e_in == 0) && (n > 0) && (n <= p.n_max) && (P < 0 || P + n > p.cap);
+  const bool skip = (e_in != 0) || (n <= 0) || (n > p.n_max) || cap_bad;
+  if (cap_bad && blockIdx.x == 0 && g == 0 && tid == 0) p.err[b] = TV_ERR_CAPACITY;
+
+  if (!skip) {
+    // rotated tree keys of head g, and the append into the cache
+    for (int idx = tid; idx < n * half; idx += blockDim.x) {
+      const int a = idx / half, pr = idx % half;
+      const float* kr = p.k_new + ((static_cast<size_t>(b) * p.n_max + a) * p.Hkv + g) * D;
+      float c, s;
+      rope_cs(P + p.depth[static_cast<size_t>(b) * p.n_max + a], pr, D, p.theta, &c, &s);
+      const float lo = kr[pr], hi = kr[pr + half];
+      const float rlo = lo * c - hi * s, rhi = hi * c + lo * s;
+      ktree[a][pr] = rlo;
+      ktree[a][pr + half] = rhi;
+      if (blockIdx.x == 0) {
+        const size_t slot = ((static_cast<size_t>(b) * p.Hkv + g) * p.cap + P + a) * D;
+        const float* vr = p.v_new + ((static_cast<size_t>(b) * p.n_max + a) * p.Hkv + g) * D;
+        p.k_cache[slot + pr] = rlo;
+        p.k_cache[slot + pr + half] = rhi;
+        p.v_cache[slot + pr] = vr[pr];
+        p.v_cache[slot + pr + half] = vr[pr + half];
+      }
+    }
+  }
+  __syncthreads();
+
+  // No wavefront leaves before the barrier below; rows past the end only
+  // skip the work.
+  const int r = blockIdx.x * 4 + wave;
+  const bool row_exists = r < p.G * p.n_max;
+  const int i = row_exists ? r / p.G : 0, head = g * p.G + (row_exists ? r % p.G : 0);
+  float* orow = p.out + ((static_cast<size_t>(b) * p.n_max + i) * p.Hq + head) * D;
+  const bool live = row_exists && !skip && i < n;
+  uint64_t anc_i = 0;
+  if (live) {
+    anc_i = p.anc[static_cast<size_t>(b) * p.n_max + i];
+    const int pos_i = P + p.depth[static_cast<size_t>(b) * p.n_max + i];
+    const float* qr = p.q + ((static_cast<size_t>(b) * p.n_max + i) * p.Hq + head) * D;
+    if (lane < half) {
+      float c, s;
+      rope_cs(pos_i, lane, D, p.theta, &c, &s);
+      const float lo = qr[lane], hi = qr[lane + half];
+      qrow[wave][lane] = lo * c - hi * s;
+      qrow[wave][lane + half] = hi * c + lo * s;
+    }
+  }
+  __syncthreads();
+  if (!row_exists) return;
+  if (!live) {
+    for (int d = lane; d < D; d += 64) orow[d] = 0.0f;
+    return;
+  }
+
+  const float* kc = p.k_cache + (static_cast<size_t>(b) * p.Hkv + g) * p.cap * D;
+  const float* vc = p.v_cache + (static_cast<size_t>(b) * p.Hkv + g) * p.cap * D;
+  float m = -INFINITY, l = 0.0f, acc0 = 0.0f, acc1 = 0.0f;
+  const int total = P + n;
+  for (int t0 = 0; t0 < total; t0 += 64) {
+    const int j = t0 + lane;
+    float sc = -INFINITY;
+    if (j < P) {
+      const float* kr = kc + static_cast<size_t>(j) * D;
+      float acc = 0.0f;
+      for (int d = 0; d < D; ++d) acc = fmaf(qrow[wave][d], kr[d], acc);
+      sc = acc * p.scale;
+    } else if (j < total && ((anc_i >> (j - P)) & 1ull)) {
+      const float* kr = ktree[j - P];
+      float acc = 0.0f;
+      for (int d = 0; d < D; ++d) acc = fmaf(qrow[wave][d], kr[d], acc);
+      sc = acc * p.scale;
+    }
+    const float mt = wave_max_f32(sc);
+    const float m_new = fmaxf(m, mt);
+    const float alpha = (m == -INFINITY) ? 0.0f : expf(m - m_new);
+    const float pj = (sc == -INFINITY) ? 0.0f : expf(sc - m_new);
+    l = l * alpha + wave_sum_f32(pj);
+    acc0 *= alpha;
+    acc1 *= alpha;
+    m = m_new;
+    const int kt = min(64, total - t0);
+    for (int jj = 0; jj < kt; ++jj) {
+      const float w = __shfl(pj, jj);
+      if (w == 0.0f) continue;
+      const int key = t0 + jj;
+      const float* vr = (key < P)
+                            ? vc + static_cast<size_t>(key) * D
+                            : p.v_new + ((static_cast<size_t>(b) * p.n_max + (key - P)) * p.Hkv + g) * D;
+      acc0 = fmaf(w, vr[lane], acc0);
+      if (D > 64) acc1 = fmaf(w, vr[lane + 64], acc1);
+    }
+  }
+  const float inv = 1.0f / l;
+  orow[lane] = acc0 * inv;
+  if (D > 64) orow[lane + 64] = acc1 * inv;
+}
+
+}  // namespace
+
+hipError_t launch_attention_f32(const tv_attn_args* a, hipStream_t s) {
+  F32Params p;
+  p.q = static_cast<const float*>(a->q);
+  p.k_new = static_cast<const float*>(a->k_new);
+  p.v_new = static_cast<const float*>(a->v_new);
+  p.k_cache = static_cast<float*>(a->k_cache);
+  p.v_cache = static_cast<float*>(a->v_cache);
+  p.prefix_len = a->prefix_len;
+  p.n_nodes = a->n_nodes;
+  p.anc = a->anc;
+  p.depth = a->depth;
+  p.err = a->err;
+  p.out = static_cast<float*>(a->out);
+  p.n_max = a->n_max;
+  p.Hq = a->Hq;
+  p.Hkv = a->Hkv;
+  p.G = a->Hq / a->Hkv;
+  p.D = a->D;
+  p.cap = a->cap;
+  p.theta = a->rope_theta;
+  p.scale = a->softmax_scale > 0.0f ? a->softmax_scale : 1.0f / sqrtf(static_cast<float>(a->D));
+  dim3 grid((p.G * p.n_max + 3) / 4, p.Hkv, a->B);
+  hipLaunchKernelGGL(attn_f32_kernel, grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace tv

@@ -1,0 +1,41 @@
+// Internal launch interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "tv.h"
+
+#define TV_MAX_NODES_DEV 64
+
+namespace tv {
+
+hipError_t launch_build_tree(const int32_t* parents, const int32_t* n_nodes, int B, int n_max,
+                             uint64_t* anc, int32_t* depth, int32_t* err, hipStream_t s);
+
+hipError_t launch_accept(const int32_t* cand_tok, const int32_t* tgt, const int32_t* parents,
+                         const uint64_t* anc, const int32_t* depth, const int32_t* n_nodes,
+                         const int32_t* err, int B, int n_max, int32_t* accept_len,
+                         int32_t* path, int32_t* bonus, int32_t* out_tokens, hipStream_t s);
+
+hipError_t launch_commit(void* k_cache, void* v_cache, int B, int Hkv, int cap, int D,
+                         int elem_bytes, const int32_t* prefix_len_in, const int32_t* accept_len,
+                         const int32_t* path, int n_max, int32_t* prefix_len_out, hipStream_t s);
+
+// Launch plan of the bf16 attention: waves per workgroup, row blocks, KV
+// splits and the workspace they need.
+struct AttnPlan {
+  int waves;       // wavefronts per workgroup (32 query rows each)
+  int row_blocks;  // workgroups along the (node, head-in-group) rows
+  int splits;      // workgroups along the prefix keys
+  int rows_pad;    // row_blocks * waves * 32
+  size_t workspace_bytes;
+};
+
+AttnPlan plan_attention_bf16(const tv_attn_args* a);
+
+hipError_t launch_attention_bf16(const tv_attn_args* a, const AttnPlan& plan, hipStream_t s);
+hipError_t launch_attention_f32(const tv_attn_args* a, hipStream_t s);
+
+}  // namespace tv

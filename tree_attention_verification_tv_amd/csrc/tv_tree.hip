@@ -1,0 +1,232 @@
+// Tree set-up, greedy acceptance and KV commit: the integer side of a
+// verification step. One 64-lane wavefront per sequence; lane i is node i.
+//
+// Tree mask and depth positions: infra-guide "5.3 Medusa、EAGLE 与 MTP",
+// sections 3.1, 3.2 and 8. Acceptance: pofe.ai "Medusa and EAGLE ...",
+// greedy case of "Typical acceptance"; vibeengines.com "Medusa, explained",
+// step 7; infra-guide section 9.2. Commit: infra-guide section 3.2 and summary.
+#include "tv_device.h"
+#include "tv_internal.h"
+
+namespace tv {
+
+// ---------------------------------------------------------------------------
+// build_tree: ancestors-or-self bitmask and depth by pointer jumping.
+//
+// Each lane keeps (J, A, d): J is an ancestor of node i (initially its
+// parent), A the set of nodes from i up to but excluding J, d the number of
+// edges from i to J (or the depth once J == -1). One round replaces J by J's
+// own J and merges A and d, so after round r, J is the 2^r-th ancestor; six
+// rounds cover any depth below 64.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void build_tree_kernel(const int32_t* __restrict__ parents,
+                                                        const int32_t* __restrict__ n_nodes,
+                                                        int n_max, uint64_t* __restrict__ anc,
+                                                        int32_t* __restrict__ depth,
+                                                        int32_t* __restrict__ err) {
+  const int b = blockIdx.x;
+  const int i = threadIdx.x;
+  const int n = n_nodes[b];
+  const bool n_ok = (n >= 0) && (n <= n_max);
+  const bool live = n_ok && (i < n);
+  const int p = live ? parents[static_cast<size_t>(b) * n_max + i] : -1;
+  const bool ok_i = !live || (i == 0 ? (p == -1) : (p >= 0 && p < i));
+  const bool tree_ok = n_ok && __all(ok_i);
+
+  int J = (live && tree_ok) ? p : -1;
+  uint64_t A = live ? (1ull << i) : 0ull;
+  int d = (J >= 0) ? 1 : 0;
+#pragma unroll
+  for (int r = 0; r < 6; ++r) {
+    const int src = (J >= 0) ? J : i;
+    const uint64_t A_src = shfl_u64(A, src);
+    const int d_src = __shfl(d, src);
+    const int J_src = __shfl(J, src);
+    if (J >= 0) {
+      A |= A_src;
+      d += d_src;
+      J = J_src;
+    }
+  }
+  if (i < n_max) {
+    const bool keep = live && tree_ok;
+    anc[static_cast<size_t>(b) * n_max + i] = keep ? A : 0ull;
+    depth[static_cast<size_t>(b) * n_max + i] = keep ? d : 0;
+  }
+  if (i == 0) err[b] = tree_ok ? 0 : static_cast<int32_t>(TV_ERR_BAD_TREE);
+}
+
+// ---------------------------------------------------------------------------
+// accept: node c >= 1 matches iff its token equals the target's choice at its
+// parent; the root always matches. A node is accepted iff every node in its
+// ancestors-or-self mask matches, i.e. (anc & ~match_mask) == 0. The deepest
+// accepted node wins (ties: lowest index); its mask, read bit by bit in
+// ascending order, is the path.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void accept_kernel(
+    const int32_t* __restrict__ cand_tok, const int32_t* __restrict__ tgt,
+    const int32_t* __restrict__ parents, const uint64_t* __restrict__ anc,
+    const int32_t* __restrict__ depth, const int32_t* __restrict__ n_nodes,
+    const int32_t* __restrict__ err, int n_max, int32_t* __restrict__ accept_len,
+    int32_t* __restrict__ path, int32_t* __restrict__ bonus, int32_t* __restrict__ out_tokens) {
+  const int b = blockIdx.x;
+  const int i = threadIdx.x;
+  const size_t row = static_cast<size_t>(b) * n_max;
+  const int n = n_nodes[b];
+  const int e_in = err ? err[b] : 0;
+  bool active = (e_in == 0) && (n > 0) && (n <= n_max);
+
+  const bool live = active && (i < n);
+  const int p = live ? parents[row + i] : -1;
+  const int tk = live ? cand_tok[row + i] : 0;
+  const int tg = live ? tgt[row + i] : 0;
+  const uint64_t a = live ? anc[row + i] : 0ull;
+  const int dp = live ? depth[row + i] : 0;
+
+  const int tg_parent = __shfl(tg, (p >= 0 && p < 64) ? p : i);
+  const bool match = live && (i == 0 || tk == tg_parent);
+  const uint64_t M = __ballot(match);
+  const bool accepted = live && (a != 0ull) && ((a & ~M) == 0ull);
+  int key = accepted ? ((dp << 8) | (255 - i)) : -1;
+  key = wave_max_i32(key);
+  if (key < 0) active = false;   // no accepted root: tree unusable
+
+  if (!active) {
+    if (i < n_max) {
+      path[row + i] = -1;
+      if (out_tokens) out_tokens[row + i] = -1;
+    }
+    if (i == 0) {
+      accept_len[b] = -1;
+      bonus[b] = -1;
+    }
+    return;
+  }
+  const int e = 255 - (key & 255);
+  const int L = key >> 8;
+  const uint64_t ae = shfl_u64(a, e);
+  const int bonus_tok = __shfl(tg, e);
+  if (i < n_max) {
+    const bool on = (ae >> i) & 1ull;
+    const int pos = __popcll(ae & ((1ull << i) - 1ull));
+    if (on) path[row + pos] = i;
+    if (i > L) path[row + i] = -1;
+    if (out_tokens) {
+      if (on && i != 0 && pos >= 1) out_tokens[row + pos - 1] = tk;
+      if (i == L) out_tokens[row + i] = bonus_tok;
+      if (i > L) out_tokens[row + i] = -1;
+    }
+  }
+  if (i == 0) {
+    accept_len[b] = L;
+    bonus[b] = bonus_tok;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// commit: slot P+d <- slot P+path[d] for d = 0..L. path is strictly increasing
+// with path[d] >= d, so a source slot may be another lane's destination; all
+// sources of one KV head are staged in LDS before any slot is written.
+// Grid: (Hkv / heads_per_block, B). The block of head 0 writes prefix_len_out;
+// when that array is also prefix_len_in, one block per sequence walks every
+// head, so no block can read a length another block has already replaced.
+// ---------------------------------------------------------------------------
+template <int ELEM_BYTES>
+__global__ __launch_bounds__(256) void commit_kernel(
+    uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache, int Hkv, int cap, int D,
+    const int32_t* prefix_len_in, const int32_t* __restrict__ accept_len,
+    const int32_t* __restrict__ path, int n_max, int32_t* prefix_len_out, int heads_per_block) {
+  constexpr int kMaxRowBytes = 128 * 4;
+  __shared__ uint4 stage[2][TV_MAX_NODES_DEV * kMaxRowBytes / 16];
+  __shared__ int s_path[TV_MAX_NODES_DEV];
+  __shared__ int s_L, s_P, s_ok;
+
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    const int L = accept_len[b];
+    const int P = prefix_len_in[b];
+    int ok = (L >= 0) && (L < n_max) && (P >= 0) && (P + L < cap);
+    s_L = L;
+    s_P = P;
+    s_ok = ok;
+  }
+  __syncthreads();
+  const int L = s_L, P = s_P;
+  if (tid <= L && tid < n_max && s_ok) {
+    const int src = path[static_cast<size_t>(b) * n_max + tid];
+    s_path[tid] = src;
+    // every source must lie in [P, cap)
+    if (src < 0 || P + src >= cap) atomicAnd(&s_ok, 0);
+  }
+  __syncthreads();
+  const bool ok = s_ok;
+  if ((heads_per_block == Hkv || blockIdx.x == 0) && tid == 0) prefix_len_out[b] = ok ? P + L + 1 : P;
+  if (!ok) return;
+
+  const int row_chunks = D * ELEM_BYTES / 16;
+  const int g0 = (heads_per_block == Hkv) ? 0 : blockIdx.x;
+  for (int gg = 0; gg < heads_per_block; ++gg) {
+    const int g = g0 + gg;
+    const size_t head_base = (static_cast<size_t>(b) * Hkv + g) * cap;
+    const int total = (L + 1) * row_chunks;
+    for (int idx = tid; idx < total; idx += blockDim.x) {
+      const int d = idx / row_chunks, c = idx % row_chunks;
+      const int src = s_path[d];
+      if (src == d) continue;
+      const size_t off = (head_base + P + src) * D * ELEM_BYTES / 16 + c;
+      stage[0][idx] = reinterpret_cast<const uint4*>(k_cache)[off];
+      stage[1][idx] = reinterpret_cast<const uint4*>(v_cache)[off];
+    }
+    __syncthreads();
+    for (int idx = tid; idx < total; idx += blockDim.x) {
+      const int d = idx / row_chunks, c = idx % row_chunks;
+      if (s_path[d] == d) continue;
+      const size_t off = (head_base + P + d) * D * ELEM_BYTES / 16 + c;
+      reinterpret_cast<uint4*>(k_cache)[off] = stage[0][idx];
+      reinterpret_cast<uint4*>(v_cache)[off] = stage[1][idx];
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------ launches
+
+hipError_t launch_build_tree(const int32_t* parents, const int32_t* n_nodes, int B, int n_max,
+                             uint64_t* anc, int32_t* depth, int32_t* err, hipStream_t s) {
+  hipLaunchKernelGGL(build_tree_kernel, dim3(B), dim3(64), 0, s, parents, n_nodes, n_max, anc,
+                     depth, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_accept(const int32_t* cand_tok, const int32_t* tgt, const int32_t* parents,
+                         const uint64_t* anc, const int32_t* depth, const int32_t* n_nodes,
+                         const int32_t* err, int B, int n_max, int32_t* accept_len,
+                         int32_t* path, int32_t* bonus, int32_t* out_tokens, hipStream_t s) {
+  hipLaunchKernelGGL(accept_kernel, dim3(B), dim3(64), 0, s, cand_tok, tgt, parents, anc, depth,
+                     n_nodes, err, n_max, accept_len, path, bonus, out_tokens);
+  return hipGetLastError();
+}
+
+hipError_t launch_commit(void* k_cache, void* v_cache, int B, int Hkv, int cap, int D,
+                         int elem_bytes, const int32_t* prefix_len_in, const int32_t* accept_len,
+                         const int32_t* path, int n_max, int32_t* prefix_len_out, hipStream_t s) {
+  // One block per (kv head, sequence) unless the new prefix lengths overwrite
+  // the old ones, in which case one block per sequence walks every head so
+  // that no block reads a length another block has already replaced.
+  const bool alias = (prefix_len_in == prefix_len_out);
+  const int hpb = alias ? Hkv : 1;
+  dim3 grid(alias ? 1 : Hkv, B);
+  if (elem_bytes == 2) {
+    hipLaunchKernelGGL(commit_kernel<2>, grid, dim3(256), 0, s, static_cast<uint8_t*>(k_cache),
+                       static_cast<uint8_t*>(v_cache), Hkv, cap, D, prefix_len_in, accept_len,
+                       path, n_max, prefix_len_out, hpb);
+  } else {
+    hipLaunchKernelGGL(commit_kernel<4>, grid, dim3(256), 0, s, static_cast<uint8_t*>(k_cache),
+                       static_cast<uint8_t*>(v_cache), Hkv, cap, D, prefix_len_in, accept_len,
+                       path, n_max, prefix_len_out, hpb);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tv
