@@ -133,6 +133,7 @@ def main() -> None:
     parents, n_nodes, plen = up(w.parents), up(w.n_nodes), up(w.prefix_len)
     tok, tgt = up(w.tok), up(w.tgt)
     base = {k: up(getattr(w, k)) for k in ("q", "k_new", "v_new", "k_cache", "v_cache")}
+    base["v_cache"] = tv.v_cache_blocked(base["v_cache"])
     per_copy = sum(t.numel() * t.element_size() for t in base.values())
     copies = args.copies or max(2, -(-4 * INFINITY_CACHE_BYTES // per_copy))
     sets = [base] + [{k: t.clone() for k, t in base.items()} for _ in range(copies - 1)]

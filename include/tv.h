@@ -96,6 +96,11 @@ tv_status tv_build_tree(const int32_t* parents, const int32_t* n_nodes, int32_t 
  * This is [INFRA-5.3] sections 3.1-3.2 and [MEDUSA-EAGLE] ("Trees"): every
  * node shares the prefix KV and sees only its ancestors.
  *
+ * Cache layouts: K is slot-major, [B][Hkv][cap][D]. V is stored in blocks
+ * of 64 slots, head-dim-major inside a block, [B][Hkv][cap/64][D][64], so that
+ * 64 consecutive slots of one head dim are contiguous (the order in which the
+ * value product consumes them); cap must be a multiple of 64.
+ *
  * Side effect (the tree's temporary KV, [INFRA-5.3] section 3.2): cache slots
  * [P, P + n_nodes[b]) of every KV head receive the rotated tree keys and the
  * raw tree values in flattened node order (rounded to the cache dtype).
@@ -106,7 +111,8 @@ typedef struct tv_attn_args {
   const void* k_new;      /* [B][n_max][Hkv][D]  tree keys, before RoPE      */
   const void* v_new;      /* [B][n_max][Hkv][D]  tree values                 */
   void* k_cache;          /* [B][Hkv][cap][D]    prefix keys (rotated)       */
-  void* v_cache;          /* [B][Hkv][cap][D]    prefix values               */
+  void* v_cache;          /* [B][Hkv][cap/64][D][64]  prefix values, blocked:
+                             slot s, dim d at ((s/64)*D + d)*64 + s%64      */
   const int32_t* prefix_len;  /* [B] P, 0 <= P                               */
   const int32_t* n_nodes;     /* [B]                                         */
   const uint64_t* anc;        /* [B][n_max] from tv_build_tree               */
@@ -135,7 +141,8 @@ size_t tv_tree_attention_workspace_size(const tv_attn_args* a);
 /*
  * Host checks: a non-null; tensor pointers non-null unless B == 0;
  * 1 <= n_max <= TV_MAX_NODES; Hq % Hkv == 0; D in {64, 128} (TV_BF16 needs
- * D == 128); cap >= n_max; workspace large enough. B == 0 is a no-op.
+ * D == 128); cap >= n_max and cap % 64 == 0; workspace large enough.
+ * B == 0 is a no-op.
  */
 tv_status tv_tree_attention(const tv_attn_args* a, hipStream_t stream);
 
@@ -182,12 +189,13 @@ tv_status tv_accept(const int32_t* cand_tok, const int32_t* tgt_argmax,
  * prefix_len_out[b] = P + L + 1. Sequences with L < 0 are copied through
  * unchanged. Slots from P + L + 1 on are left as they were (free space).
  *
- *   k_cache, v_cache [B][Hkv][cap][D]  in place
+ *   k_cache [B][Hkv][cap][D], v_cache [B][Hkv][cap/64][D][64]  in place
+ *                    (the layouts of tv_tree_attention)
  *   prefix_len_in    [B]
  *   accept_len, path as from tv_accept (path rows of length n_max)
  *   prefix_len_out   [B] out; may be the same array as prefix_len_in
  * Host checks: pointers non-null unless B == 0, Hkv >= 1, D in {64, 128},
- * 1 <= n_max <= TV_MAX_NODES, cap >= n_max, dtype valid. Device side,
+ * 1 <= n_max <= TV_MAX_NODES, cap >= n_max, cap % 64 == 0, dtype valid. Device side,
  * a path that would read or write outside [P, cap) leaves that sequence
  * unchanged.
  */

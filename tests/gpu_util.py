@@ -20,10 +20,12 @@ def to_dev(a: np.ndarray, dtype: str, dev) -> torch.Tensor:
 
 
 def upload(w, dev="cuda:0") -> dict:
+    """Device copies of a workload; V goes to the library's blocked layout."""
     d = {}
     for name in ("parents", "n_nodes", "prefix_len", "tok", "tgt", "q", "k_new", "v_new",
                  "k_cache", "v_cache"):
         d[name] = to_dev(getattr(w, name), w.dtype, dev)
+    d["v_cache"] = tv.v_cache_blocked(d["v_cache"])
     return d
 
 
@@ -37,7 +39,7 @@ def run_step(w, d: dict, parents_override=None, n_nodes_override=None, prefix_ov
     out = tv.tree_attention(d["q"], d["k_new"], d["v_new"], d["k_cache"], d["v_cache"], plen,
                             n_nodes, anc, depth, err, rope_theta=w.rope_theta)
     k_after_attn = d["k_cache"].clone()
-    v_after_attn = d["v_cache"].clone()
+    v_after_attn = tv.v_cache_rows(d["v_cache"])
     acc, path, bonus, toks = tv.accept(d["tok"], d["tgt"], parents, anc, depth, n_nodes, err)
     new_plen = tv.commit(d["k_cache"], d["v_cache"], plen, acc, path)
     torch.cuda.synchronize()

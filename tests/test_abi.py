@@ -70,9 +70,10 @@ def test_host_validation_without_device():
     # commit
     assert lib.tv_commit(fake, fake, 1, 0, 10, 128, 1, fake, fake, fake, 5, fake, null) == _lib.TV_ERR_INVALID_ARG
     assert lib.tv_commit(fake, fake, 1, 2, 4, 128, 1, fake, fake, fake, 5, fake, null) == _lib.TV_ERR_INVALID_ARG
-    assert lib.tv_commit(fake, fake, 1, 2, 10, 96, 1, fake, fake, fake, 5, fake, null) == _lib.TV_ERR_UNSUPPORTED
-    assert lib.tv_commit(fake, fake, 1, 2, 10, 128, 7, fake, fake, fake, 5, fake, null) == _lib.TV_ERR_INVALID_ARG
-    assert lib.tv_commit(null, fake, 1, 2, 10, 128, 1, fake, fake, fake, 5, fake, null) == _lib.TV_ERR_INVALID_ARG
+    assert lib.tv_commit(fake, fake, 1, 2, 100, 128, 1, fake, fake, fake, 5, fake, null) == _lib.TV_ERR_INVALID_ARG
+    assert lib.tv_commit(fake, fake, 1, 2, 64, 96, 1, fake, fake, fake, 5, fake, null) == _lib.TV_ERR_UNSUPPORTED
+    assert lib.tv_commit(fake, fake, 1, 2, 64, 128, 7, fake, fake, fake, 5, fake, null) == _lib.TV_ERR_INVALID_ARG
+    assert lib.tv_commit(null, fake, 1, 2, 64, 128, 1, fake, fake, fake, 5, fake, null) == _lib.TV_ERR_INVALID_ARG
 
 
 def attn(**kw):
@@ -80,7 +81,7 @@ def attn(**kw):
     for f in ("q", "k_new", "v_new", "k_cache", "v_cache", "prefix_len", "n_nodes", "anc", "depth",
               "err", "out"):
         setattr(a, f, 0x1000)
-    a.B, a.n_max, a.Hq, a.Hkv, a.D, a.cap, a.dtype = 8, 60, 32, 8, 128, 4156, _lib.TV_BF16
+    a.B, a.n_max, a.Hq, a.Hkv, a.D, a.cap, a.dtype = 8, 60, 32, 8, 128, 4160, _lib.TV_BF16
     a.rope_theta, a.softmax_scale = 10000.0, 0.0
     for k, v in kw.items():
         setattr(a, k, v)
@@ -94,6 +95,7 @@ def test_attention_host_validation_and_workspace():
     assert run(attn(Hq=30)) == _lib.TV_ERR_INVALID_ARG           # Hq % Hkv
     assert run(attn(n_max=65)) == _lib.TV_ERR_INVALID_ARG
     assert run(attn(cap=10)) == _lib.TV_ERR_INVALID_ARG
+    assert run(attn(cap=4156)) == _lib.TV_ERR_INVALID_ARG        # V blocks of 64 slots
     assert run(attn(D=64)) == _lib.TV_ERR_UNSUPPORTED            # bf16 needs D = 128
     assert run(attn(dtype=_lib.TV_F32, D=96)) == _lib.TV_ERR_UNSUPPORTED
     assert run(attn(dtype=9)) == _lib.TV_ERR_INVALID_ARG

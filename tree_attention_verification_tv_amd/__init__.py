@@ -25,7 +25,25 @@ from ._lib import (TV_BF16, TV_ERR_BAD_TREE, TV_ERR_CAPACITY, TV_F32, TV_MAX_NOD
                    TvAttnArgs, TvError)
 
 __all__ = ["build_tree", "tree_attention", "tree_attention_workspace_size", "accept", "commit",
-           "version", "TvError", "TV_ERR_BAD_TREE", "TV_ERR_CAPACITY", "attn_args"]
+           "version", "TvError", "TV_ERR_BAD_TREE", "TV_ERR_CAPACITY", "attn_args",
+           "v_cache_blocked", "v_cache_rows", "V_BLOCK"]
+
+V_BLOCK = 64   # slots per block of the V cache
+
+
+def v_cache_blocked(v_rows: torch.Tensor) -> torch.Tensor:
+    """Layout helper: V cache [B, Hkv, cap, D] (slot-major) -> the library's
+    blocked layout [B, Hkv, cap/64, D, 64]. cap must be a multiple of 64."""
+    B, H, cap, D = v_rows.shape
+    if cap % V_BLOCK:
+        raise ValueError("cap must be a multiple of 64")
+    return v_rows.reshape(B, H, cap // V_BLOCK, V_BLOCK, D).transpose(-1, -2).contiguous()
+
+
+def v_cache_rows(v_blocked: torch.Tensor) -> torch.Tensor:
+    """Inverse of v_cache_blocked: [B, Hkv, cap/64, D, 64] -> [B, Hkv, cap, D]."""
+    B, H, nb, D, blk = v_blocked.shape
+    return v_blocked.transpose(-1, -2).reshape(B, H, nb * blk, D).contiguous()
 
 
 def version() -> str:
@@ -90,8 +108,12 @@ def attn_args(q, k_new, v_new, k_cache, v_cache, prefix_len, n_nodes, anc, depth
     cap = k_cache.shape[2]
     if tuple(k_new.shape) != (B, n_max, Hkv, D) or tuple(v_new.shape) != (B, n_max, Hkv, D):
         raise ValueError("k_new / v_new must be [B, n_max, Hkv, D]")
-    if tuple(k_cache.shape) != (B, Hkv, cap, D) or tuple(v_cache.shape) != (B, Hkv, cap, D):
-        raise ValueError("k_cache / v_cache must be [B, Hkv, cap, D]")
+    if cap % V_BLOCK:
+        raise ValueError("cache capacity must be a multiple of 64")
+    if tuple(k_cache.shape) != (B, Hkv, cap, D):
+        raise ValueError("k_cache must be [B, Hkv, cap, D]")
+    if tuple(v_cache.shape) != (B, Hkv, cap // V_BLOCK, D, V_BLOCK):
+        raise ValueError("v_cache must be [B, Hkv, cap/64, D, 64] (see v_cache_blocked)")
     if tuple(out.shape) != (B, n_max, Hq, D):
         raise ValueError("out must be [B, n_max, Hq, D]")
     if tuple(anc.shape) != (B, n_max) or tuple(depth.shape) != (B, n_max):
@@ -163,8 +185,9 @@ def accept(cand_tok, tgt_argmax, parents, anc, depth, n_nodes, err=None, accept_
 
 
 def commit(k_cache, v_cache, prefix_len_in, accept_len, path, prefix_len_out=None, stream=None):
-    """Moves the accepted path's KV to slots [P, P + L + 1) in place; returns
-    the new prefix lengths (prefix_len_out, which may be prefix_len_in)."""
+    """Moves the accepted path's KV to slots [P, P + L + 1) in place (k_cache
+    [B, Hkv, cap, D], v_cache [B, Hkv, cap/64, D, 64]); returns the new prefix
+    lengths (prefix_len_out, which may be prefix_len_in)."""
     lib = _lib.load()
     if k_cache.dtype not in _DTYPES:
         raise ValueError("cache must be float32 or bfloat16")
@@ -173,6 +196,8 @@ def commit(k_cache, v_cache, prefix_len_in, accept_len, path, prefix_len_out=Non
     for name, t in (("prefix_len_in", prefix_len_in), ("accept_len", accept_len), ("path", path)):
         _dev(t, name, torch.int32)
     B, Hkv, cap, D = k_cache.shape
+    if tuple(v_cache.shape) != (B, Hkv, cap // V_BLOCK, D, V_BLOCK):
+        raise ValueError("v_cache must be [B, Hkv, cap/64, D, 64]")
     n_max = path.shape[1]
     if prefix_len_out is None:
         prefix_len_out = torch.empty_like(prefix_len_in)

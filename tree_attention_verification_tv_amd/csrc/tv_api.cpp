@@ -18,7 +18,7 @@ tv_status check_attn_shapes(const tv_attn_args* a) {
   if (a == nullptr) return TV_ERR_INVALID_ARG;
   if (a->B < 0 || a->n_max < 1 || a->n_max > TV_MAX_NODES) return TV_ERR_INVALID_ARG;
   if (a->Hq < 1 || a->Hkv < 1 || a->Hq % a->Hkv != 0) return TV_ERR_INVALID_ARG;
-  if (a->cap < a->n_max || a->D < 1) return TV_ERR_INVALID_ARG;
+  if (a->cap < a->n_max || a->cap % 64 != 0 || a->D < 1) return TV_ERR_INVALID_ARG;
   if (!dtype_ok(a->dtype)) return TV_ERR_INVALID_ARG;
   if (a->dtype == TV_BF16 && a->D != 128) return TV_ERR_UNSUPPORTED;
   if (a->dtype == TV_F32 && a->D != 64 && a->D != 128) return TV_ERR_UNSUPPORTED;
@@ -88,7 +88,8 @@ tv_status tv_commit(void* k_cache, void* v_cache, int32_t B, int32_t Hkv, int32_
                     int32_t dtype, const int32_t* prefix_len_in, const int32_t* accept_len,
                     const int32_t* path, int32_t n_max, int32_t* prefix_len_out,
                     hipStream_t stream) {
-  if (B < 0 || Hkv < 1 || n_max < 1 || n_max > TV_MAX_NODES || cap < n_max) return TV_ERR_INVALID_ARG;
+  if (B < 0 || Hkv < 1 || n_max < 1 || n_max > TV_MAX_NODES || cap < n_max || cap % 64 != 0)
+    return TV_ERR_INVALID_ARG;
   if (!dtype_ok(dtype)) return TV_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return TV_ERR_UNSUPPORTED;
   if (B == 0) return TV_OK;

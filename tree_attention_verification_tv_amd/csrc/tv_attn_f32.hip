@@ -6,6 +6,9 @@
 // (infra-guide "5.3 Medusa、EAGLE 与 MTP", section 3.1); queries and tree
 // keys are rotated at position P + depth (section 3.2).
 //
+// Caches: K [B][Hkv][cap][D]; V [B][Hkv][cap/64][D][64] (blocks of 64 slots,
+// head dim major inside a block).
+//
 // Grid (ceil(G*n_max/4), Hkv, B), 256 threads. The block first rotates the n
 // tree keys of its KV head into LDS (angles in double precision); the block
 // with blockIdx.x == 0 also appends them, and the raw tree values, to cache
@@ -50,6 +53,12 @@ __device__ __forceinline__ void rope_cs(int pos, int pair, int D, float theta, f
   *s = static_cast<float>(sd);
 }
 
+// Element offset of (slot, d) inside one head's V cache, which is stored in
+// blocks of 64 slots, head dim major within a block: [cap/64][D][64].
+__device__ __forceinline__ size_t v_off(int slot, int d, int D) {
+  return (static_cast<size_t>(slot >> 6) * D + d) * 64 + (slot & 63);
+}
+
 __device__ __forceinline__ float wave_max_f32(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
@@ -86,12 +95,13 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(F32Params p) {
       ktree[a][pr] = rlo;
       ktree[a][pr + half] = rhi;
       if (blockIdx.x == 0) {
-        const size_t slot = ((static_cast<size_t>(b) * p.Hkv + g) * p.cap + P + a) * D;
+        const size_t head = (static_cast<size_t>(b) * p.Hkv + g) * p.cap * D;
+        const size_t slot = head + static_cast<size_t>(P + a) * D;
         const float* vr = p.v_new + ((static_cast<size_t>(b) * p.n_max + a) * p.Hkv + g) * D;
         p.k_cache[slot + pr] = rlo;
         p.k_cache[slot + pr + half] = rhi;
-        p.v_cache[slot + pr] = vr[pr];
-        p.v_cache[slot + pr + half] = vr[pr + half];
+        p.v_cache[head + v_off(P + a, pr, D)] = vr[pr];
+        p.v_cache[head + v_off(P + a, pr + half, D)] = vr[pr + half];
       }
     }
   }
@@ -155,11 +165,14 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(F32Params p) {
       const float w = __shfl(pj, jj);
       if (w == 0.0f) continue;
       const int key = t0 + jj;
-      const float* vr = (key < P)
-                            ? vc + static_cast<size_t>(key) * D
-                            : p.v_new + ((static_cast<size_t>(b) * p.n_max + (key - P)) * p.Hkv + g) * D;
-      acc0 = fmaf(w, vr[lane], acc0);
-      if (D > 64) acc1 = fmaf(w, vr[lane + 64], acc1);
+      if (key < P) {
+        acc0 = fmaf(w, vc[v_off(key, lane, D)], acc0);
+        if (D > 64) acc1 = fmaf(w, vc[v_off(key, lane + 64, D)], acc1);
+      } else {
+        const float* vr = p.v_new + ((static_cast<size_t>(b) * p.n_max + (key - P)) * p.Hkv + g) * D;
+        acc0 = fmaf(w, vr[lane], acc0);
+        if (D > 64) acc1 = fmaf(w, vr[lane + 64], acc1);
+      }
     }
   }
   const float inv = 1.0f / l;

@@ -26,7 +26,8 @@ hipError_t launch_commit(void* k_cache, void* v_cache, int B, int Hkv, int cap, 
 // Launch plan of the bf16 attention: waves per workgroup, row blocks, KV
 // splits and the workspace they need.
 struct AttnPlan {
-  int waves;       // wavefronts per workgroup (32 query rows each)
+  int waves;       // wavefronts per workgroup
+  int qt;          // 32-row query tiles per wavefront
   int row_blocks;  // workgroups along the (node, head-in-group) rows
   int splits;      // workgroups along the prefix keys
   int rows_pad;    // row_blocks * waves * 32

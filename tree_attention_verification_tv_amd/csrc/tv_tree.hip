@@ -127,17 +127,19 @@ __global__ __launch_bounds__(64) void accept_kernel(
 // commit: slot P+d <- slot P+path[d] for d = 0..L. path is strictly increasing
 // with path[d] >= d, so a source slot may be another lane's destination; all
 // sources of one KV head are staged in LDS before any slot is written.
+// K is [cap][D] per head; V is blocked [cap/64][D][64] per head.
 // Grid: (Hkv / heads_per_block, B). The block of head 0 writes prefix_len_out;
 // when that array is also prefix_len_in, one block per sequence walks every
 // head, so no block can read a length another block has already replaced.
 // ---------------------------------------------------------------------------
-template <int ELEM_BYTES>
+template <typename T>
 __global__ __launch_bounds__(256) void commit_kernel(
-    uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache, int Hkv, int cap, int D,
+    T* __restrict__ k_cache, T* __restrict__ v_cache, int Hkv, int cap, int D,
     const int32_t* prefix_len_in, const int32_t* __restrict__ accept_len,
     const int32_t* __restrict__ path, int n_max, int32_t* prefix_len_out, int heads_per_block) {
-  constexpr int kMaxRowBytes = 128 * 4;
-  __shared__ uint4 stage[2][TV_MAX_NODES_DEV * kMaxRowBytes / 16];
+  constexpr int kStage = TV_MAX_NODES_DEV * 128 * 4 / sizeof(T);   // elements
+  __shared__ T k_stage[kStage];
+  __shared__ T v_stage[kStage];
   __shared__ int s_path[TV_MAX_NODES_DEV];
   __shared__ int s_L, s_P, s_ok;
 
@@ -164,27 +166,24 @@ __global__ __launch_bounds__(256) void commit_kernel(
   if ((heads_per_block == Hkv || blockIdx.x == 0) && tid == 0) prefix_len_out[b] = ok ? P + L + 1 : P;
   if (!ok) return;
 
-  const int row_chunks = D * ELEM_BYTES / 16;
   const int g0 = (heads_per_block == Hkv) ? 0 : blockIdx.x;
+  const int total = (L + 1) * D;
   for (int gg = 0; gg < heads_per_block; ++gg) {
-    const int g = g0 + gg;
-    const size_t head_base = (static_cast<size_t>(b) * Hkv + g) * cap;
-    const int total = (L + 1) * row_chunks;
+    const size_t head = (static_cast<size_t>(b) * Hkv + g0 + gg) * cap * D;
     for (int idx = tid; idx < total; idx += blockDim.x) {
-      const int d = idx / row_chunks, c = idx % row_chunks;
-      const int src = s_path[d];
-      if (src == d) continue;
-      const size_t off = (head_base + P + src) * D * ELEM_BYTES / 16 + c;
-      stage[0][idx] = reinterpret_cast<const uint4*>(k_cache)[off];
-      stage[1][idx] = reinterpret_cast<const uint4*>(v_cache)[off];
+      const int d = idx / D, c = idx % D;
+      const int src = P + s_path[d];
+      if (src == P + d) continue;
+      k_stage[idx] = k_cache[head + static_cast<size_t>(src) * D + c];
+      v_stage[idx] = v_cache[head + (static_cast<size_t>(src >> 6) * D + c) * 64 + (src & 63)];
     }
     __syncthreads();
     for (int idx = tid; idx < total; idx += blockDim.x) {
-      const int d = idx / row_chunks, c = idx % row_chunks;
+      const int d = idx / D, c = idx % D;
       if (s_path[d] == d) continue;
-      const size_t off = (head_base + P + d) * D * ELEM_BYTES / 16 + c;
-      reinterpret_cast<uint4*>(k_cache)[off] = stage[0][idx];
-      reinterpret_cast<uint4*>(v_cache)[off] = stage[1][idx];
+      const int dst = P + d;
+      k_cache[head + static_cast<size_t>(dst) * D + c] = k_stage[idx];
+      v_cache[head + (static_cast<size_t>(dst >> 6) * D + c) * 64 + (dst & 63)] = v_stage[idx];
     }
     __syncthreads();
   }
@@ -218,12 +217,12 @@ hipError_t launch_commit(void* k_cache, void* v_cache, int B, int Hkv, int cap, 
   const int hpb = alias ? Hkv : 1;
   dim3 grid(alias ? 1 : Hkv, B);
   if (elem_bytes == 2) {
-    hipLaunchKernelGGL(commit_kernel<2>, grid, dim3(256), 0, s, static_cast<uint8_t*>(k_cache),
-                       static_cast<uint8_t*>(v_cache), Hkv, cap, D, prefix_len_in, accept_len,
+    hipLaunchKernelGGL(commit_kernel<uint16_t>, grid, dim3(256), 0, s, static_cast<uint16_t*>(k_cache),
+                       static_cast<uint16_t*>(v_cache), Hkv, cap, D, prefix_len_in, accept_len,
                        path, n_max, prefix_len_out, hpb);
   } else {
-    hipLaunchKernelGGL(commit_kernel<4>, grid, dim3(256), 0, s, static_cast<uint8_t*>(k_cache),
-                       static_cast<uint8_t*>(v_cache), Hkv, cap, D, prefix_len_in, accept_len,
+    hipLaunchKernelGGL(commit_kernel<uint32_t>, grid, dim3(256), 0, s, static_cast<uint32_t*>(k_cache),
+                       static_cast<uint32_t*>(v_cache), Hkv, cap, D, prefix_len_in, accept_len,
                        path, n_max, prefix_len_out, hpb);
   }
   return hipGetLastError();

@@ -377,6 +377,7 @@ def generate(cfg: int, seed: Optional[int] = None, **over) -> Workload:
     else:
         prefix_len = np.full(B, pre, dtype=np.int32)
     cap = int(prefix_len.max()) + n_max + int(c.get("cap_extra", 0))
+    cap = -(-cap // 64) * 64     # the library keeps V in blocks of 64 slots
 
     dt = c["dtype"]
     q = _normal(r_q, (B, n_max, Hq, D), dt)
