@@ -151,7 +151,7 @@ def main() -> None:
     a0 = tv.attn_args(base["q"], base["k_new"], base["v_new"], base["k_cache"], base["v_cache"],
                       plen, n_nodes, anc, depth, err, out, w.rope_theta)
     ws_bytes = tv.tree_attention_workspace_size(a0)
-    workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    workspace = tv.new_workspace(ws_bytes, dev)
 
     stream = torch.cuda.current_stream()
 

@@ -123,7 +123,9 @@ typedef struct tv_attn_args {
   void* out;              /* [B][n_max][Hq][D]   attention output; rows of
                              padding nodes and skipped sequences are zero    */
   void* workspace;        /* device scratch, >= tv_tree_attention_workspace_size
-                             bytes (may be NULL when that size is 0)         */
+                             bytes (may be NULL when that size is 0); no
+                             initial contents needed. Calls that may run at
+                             the same time need separate workspaces.        */
   size_t workspace_bytes;
   int32_t B, n_max, Hq, Hkv, D, cap;
   int32_t dtype;          /* tv_dtype                                        */

@@ -24,7 +24,7 @@ from . import _lib
 from ._lib import (TV_BF16, TV_ERR_BAD_TREE, TV_ERR_CAPACITY, TV_F32, TV_MAX_NODES,  # noqa: F401
                    TvAttnArgs, TvError)
 
-__all__ = ["build_tree", "tree_attention", "tree_attention_workspace_size", "accept", "commit",
+__all__ = ["build_tree", "tree_attention", "tree_attention_workspace_size", "new_workspace", "accept", "commit",
            "version", "TvError", "TV_ERR_BAD_TREE", "TV_ERR_CAPACITY", "attn_args",
            "v_cache_blocked", "v_cache_rows", "V_BLOCK"]
 
@@ -141,6 +141,25 @@ def tree_attention_workspace_size(args: TvAttnArgs) -> int:
     return int(_lib.load().tv_tree_attention_workspace_size(ctypes.byref(args)))
 
 
+def new_workspace(nbytes: int, device) -> torch.Tensor:
+    """A workspace for tree_attention (its contents need no initialisation)."""
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+_WORKSPACES: dict = {}
+
+
+def _default_workspace(device, need: int) -> torch.Tensor:
+    """Per-device workspace shared by calls that pass none (calls on one
+    device must then not overlap on different streams)."""
+    key = torch.device(device).index
+    ws = _WORKSPACES.get(key)
+    if ws is None or ws.numel() < need:
+        ws = new_workspace(need, device)
+        _WORKSPACES[key] = ws
+    return ws
+
+
 def tree_attention(q, k_new, v_new, k_cache, v_cache, prefix_len, n_nodes, anc, depth, err,
                    rope_theta=10000.0, softmax_scale=0.0, out=None, workspace=None, stream=None):
     """Tree-masked attention of every node over prefix + ancestors; appends
@@ -153,8 +172,10 @@ def tree_attention(q, k_new, v_new, k_cache, v_cache, prefix_len, n_nodes, anc, 
                   rope_theta, softmax_scale, workspace)
     need = tree_attention_workspace_size(a)
     if need > a.workspace_bytes:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-        a.workspace, a.workspace_bytes = workspace.data_ptr(), need
+        if workspace is not None:
+            raise ValueError(f"workspace holds {a.workspace_bytes} bytes, {need} needed")
+        workspace = _default_workspace(q.device, need)
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
     _lib.check("tv_tree_attention", lib.tv_tree_attention(ctypes.byref(a), _stream(stream)))
     return out
 

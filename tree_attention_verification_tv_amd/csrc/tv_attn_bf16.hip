@@ -7,49 +7,67 @@
 // P + depth. Siblings and other branches are masked out by the node's
 // ancestor bitmask.
 //
-// How (this file's design, not the pages'):
-//   * Workgroup = (sequence b, KV head g, row block rb, KV split s). Its query
-//     rows are the G query heads of g for every tree node, node-major
-//     (row = node * G + head_in_group); each wavefront owns QT tiles of 32
-//     rows, so every K or V fragment read from LDS feeds QT MFMAs. All rows
-//     share one pass over the prefix K/V of (b, g): the prefix is read from
-//     HBM once per split, coalesced, and copied straight into LDS in 64-key
-//     tiles (global_load_lds into a ring of four stages, three tiles in
-//     flight), so the copies cost no registers and no LDS write instructions.
-//   * Scores are computed transposed, S^T = K Q^T, with
-//     v_mfma_f32_32x32x16_bf16: a lane then holds 16 keys of ONE query row,
-//     so the row max is lane-local plus one v_permlane32_swap. The output is
-//     also transposed, O^T = V^T P^T, so the probabilities go from the score
-//     accumulator straight into the B operand, and a row's rescale factor is
-//     lane-local.
-//   * The queries are pre-scaled by softmax_scale * log2(e) and the score
-//     MFMA starts from an accumulator holding -r, where r is the row's score
-//     against the tree root (visible to every node), so the accumulator IS
-//     the exponent: p = exp2(acc), with no running max and no branch in the
-//     tile loop. A row whose later scores rise more than 2^62 above r is
-//     caught from its final sum; the workgroup then finds every row's exact
-//     max in a scores-only pass and redoes the pass with r = max, where
-//     every p <= 1 (exact for any score range).
-//     Row sums are dot products of the bf16 probabilities with ones, i.e.
-//     exactly the weights the PV product used.
-//   * The score MFMA reads K rows in a permuted order (row m of a 32-key block
-//     is key perm(m)), so each lane half holds 8 CONSECUTIVE keys per 16-key
-//     group: the probabilities then match the V tile in natural key order.
-//   * V is cached tile-blocked and d-major ([cap/64][D][64]), so a 64-key V
-//     tile is one contiguous 16 KB block whose rows (one per head dim) are
-//     exactly the A operand of the PV product. K rows and V rows sit in LDS
-//     with 16-byte units XOR-swizzled against bank conflicts.
-//   * The tree tile (n <= 64 nodes) is one more 64-key tile, processed first
-//     (in the ring's fourth stage, while the first prefix tiles are in
-//     flight), whose keys are the tree nodes rotated on the fly from k_new; a
-//     key j is visible to row r iff bit j of anc[node(r)] is set. The
-//     workgroup of the last split with rb == 0 also appends the rotated tree
-//     keys and raw values to cache slots [P, P+n).
-//   * RoPE angles: the host passes theta^(-2d/D) in double precision; the
-//     kernel forms pos * inv_freq in double, reduces it to [-pi, pi] and
-//     takes a single-precision sincos.
-//   * With several splits, each writes (reference score, sum, unnormalised
-//     output) to the workspace and a merge kernel combines them.
+// How (this file's design, not the pages'): three kernels on one stream.
+//
+//   prep   one workgroup per (node, sequence). Rotates the node's queries at
+//          P + depth, scales them by softmax_scale * log2(e), rounds them to
+//          bf16 and stores them in the exact register order of the score
+//          MFMA's B operand; computes each row's score against the tree root
+//          (the reference r below); rotates the node's keys and appends them,
+//          with the raw values, to cache slots P + i. It also flags
+//          sequences whose prefix plus tree exceeds the cache.
+//
+//   main   workgroup = (row block rb, KV split s) of (sequence b, KV head g).
+//          Its query rows are the G query heads of g for every tree node,
+//          node-major (row = node * G + head_in_group); each wavefront owns
+//          QT tiles of 32 rows, so every K or V fragment read from LDS feeds
+//          QT MFMAs. The keys of b are slots [0, P + n) of the cache: the
+//          prefix followed by the tree appended by prep, cut into 64-key
+//          tiles that the splits share out. Tiles are copied straight into
+//          LDS (global_load_lds into a ring of four stages, three tiles in
+//          flight), so the copies cost no registers and no LDS writes.
+//          The copies are issued from inline assembly: the compiler then does
+//          not see an LDS write it cannot tell apart from the fragment reads,
+//          and does not drain every copy in flight before each tile; the
+//          kernel waits for exactly the tile it needs (s_waitcnt vmcnt) and a
+//          barrier. Vector memory operations complete in order, so the few
+//          operand loads (queries, reference scores, ancestor masks) are
+//          issued right after the first tile and consumed before the others.
+//
+//          Scores are computed transposed, S^T = K Q^T, with
+//          v_mfma_f32_32x32x16_bf16: a lane then holds 16 keys of ONE query
+//          row, so row reductions are lane-local plus one v_permlane32_swap.
+//          The output is also transposed, O^T = V^T P^T, so probabilities go
+//          from the score accumulator straight into the B operand. The score
+//          MFMA starts from an accumulator holding -r, so the accumulator IS
+//          the exponent: p = exp2(acc), with no running max and no branch in
+//          the tile loop. A row whose later scores rise more than 2^62 above
+//          r is caught from its final sum; the workgroup then finds every
+//          row's exact max in a scores-only pass and redoes the pass with
+//          r = max, where every p <= 1 (exact for any score range). Row sums
+//          are dot products of the bf16 probabilities with ones, i.e. exactly
+//          the weights the PV product used.
+//
+//          The score MFMA reads K rows in a permuted order (row m of a 32-key
+//          block is key perm(m)), so each lane half holds 8 CONSECUTIVE keys
+//          per 16-key group: the probabilities then match the V tile in
+//          natural key order. V is cached tile-blocked and d-major
+//          ([cap/64][D][64]), so a 64-key V tile is one contiguous 16 KB block
+//          whose rows (one per head dim) are exactly the A operand of the PV
+//          product. K rows and V rows sit in LDS with 16-byte units
+//          XOR-swizzled against bank conflicts.
+//
+//          Only the last one or two tiles of b reach past the prefix: there a
+//          key j >= P is visible to a row iff bit j - P of its node's
+//          ancestor mask is set, and value rows past P + n are zeroed.
+//
+//   merge  with several splits, each writes (reference, row sum,
+//          unnormalised output) to the workspace in register order; the merge
+//          combines them in split order (deterministic) and writes the rows.
+//
+// RoPE angles: the host passes theta^(-2d/D) in double precision; prep forms
+// pos * inv_freq in double, reduces it to [-pi, pi] and takes a
+// single-precision sincos.
 #include <math.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -68,11 +86,12 @@ namespace {
 constexpr int kD = 128;                 // head dim (bf16 path)
 constexpr int kKT = 64;                 // keys per LDS stage (= V cache block)
 constexpr int kStageElems = kKT * kD;   // bf16 elements of one K (or V) stage
-constexpr int kStages = 4;              // LDS ring of prefix tiles (3 in flight)
-constexpr int kTableDepths = 16;        // cos/sin rows kept in LDS
+constexpr int kStages = 4;              // LDS ring of key tiles (3 in flight)
+constexpr int kMaxSplits = 8;           // key splits per row block
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct BfParams {
   const uint16_t* q;
@@ -86,8 +105,10 @@ struct BfParams {
   const int32_t* depth;
   int32_t* err;
   uint16_t* out;
-  float* part_o;     // [B][Hkv][S][rows_pad][D]
-  float2* part_ml;   // [B][Hkv][S][rows_pad]  (reference max in log2 units, sum)
+  uint4* qprep;      // [B][Hkv][rows_pad/32][8][64] x 8 bf16: MFMA B operands
+  float* rref;       // [B][Hkv][rows_pad] reference score per row
+  float4* part_o;    // split partials, register order (see the main epilogue)
+  float2* part_ml;   // split (reference, row sum) per lane
   int n_max, Hq, Hkv, G, cap;
   int splits, row_blocks, rows_pad;
   int rope;          // 0: no rotation
@@ -100,10 +121,15 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   f32x2 v = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 __device__ __forceinline__ uint16_t u4_elem(const uint4& v, int t) {
   const uint32_t w = (t < 2) ? v.x : (t < 4) ? v.y : (t < 6) ? v.z : v.w;
   return static_cast<uint16_t>((t & 1) ? (w >> 16) : (w & 0xFFFFu));
+}
+__device__ __forceinline__ uint32_t u4_word(const uint4& v, int t) {
+  return (t == 0) ? v.x : (t == 1) ? v.y : (t == 2) ? v.z : v.w;
 }
 
 // Row m of a 32-key score block reads key perm(m): then lane half h holds
@@ -142,6 +168,163 @@ __device__ __forceinline__ float row_sum2(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// LDS byte address of a shared-memory pointer.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
+}
+
+// Direct global -> LDS copy of 16 bytes per lane: lane i reads base + voff
+// and writes LDS bytes [lds + 16 i, +16). base and lds are wave-uniform.
+// Issued from assembly, so the compiler neither tracks it (the kernel waits
+// for it explicitly) nor treats later LDS reads as dependent on it.
+__device__ __forceinline__ void dma16(const uint16_t* base, uint32_t voff, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds) : "memory");
+}
+// Waits until at most N vector memory operations of this wavefront are
+// outstanding (N must be a compile-time constant).
+template <int N>
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+// Forces a loaded value to have arrived here (the compiler inserts the wait).
+__device__ __forceinline__ void touch(const bf16x8& v) { asm volatile("" ::"v"(__builtin_bit_cast(u32x4, v))); }
+__device__ __forceinline__ void touch(uint64_t v) { asm volatile("" ::"v"(v)); }
+__device__ __forceinline__ void touch(float v) { asm volatile("" ::"v"(v)); }
+
+// Sequence status shared by the three kernels: skipped (earlier error, empty
+// or oversized tree) or over the cache capacity.
+struct SeqState {
+  int n, P;
+  bool cap_bad, skip;
+};
+__device__ __forceinline__ SeqState seq_state(const BfParams& p, int b) {
+  SeqState q;
+  q.n = p.n_nodes[b];
+  q.P = p.prefix_len[b];
+  const int e_in = p.err[b];
+  q.cap_bad = (e_in == 0) && (q.n > 0) && (q.n <= p.n_max) && (q.P < 0 || q.P + q.n > p.cap);
+  q.skip = (e_in != 0) || (q.n <= 0) || (q.n > p.n_max) || q.cap_bad;
+  return q;
+}
+
+// ---------------------------------------------------------------------------
+// prep: grid (n_max, B), 256 threads
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void prep_bf16_kernel(BfParams p) {
+  __shared__ float2 cs_node[kD / 2];   // angle (P + depth) f_j
+  __shared__ float2 cs_root[kD / 2];   // angle P f_j
+  const int i = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const SeqState sq = seq_state(p, b);
+  if (sq.cap_bad && i == 0 && tid == 0) p.err[b] = TV_ERR_CAPACITY;
+  if (sq.skip) return;   // the main and merge kernels zero the rows of b
+  const int P = sq.P;
+  const bool live = i < sq.n;
+  const int dep = live ? min(max(p.depth[static_cast<size_t>(b) * p.n_max + i], 0), TV_MAX_NODES_DEV - 1) : 0;
+  if (tid < kD / 2) {
+    cs_node[tid] = p.rope ? rope_cs(P + dep, p.inv_freq[tid]) : make_float2(1.0f, 0.0f);
+    cs_root[tid] = p.rope ? rope_cs(P, p.inv_freq[tid]) : make_float2(1.0f, 0.0f);
+  }
+  __syncthreads();
+
+  const int G = p.G;
+  const int row_tiles = p.rows_pad / 32;
+  const float qs = p.scale_log2;
+  const size_t node_row = static_cast<size_t>(b) * p.n_max + i;
+
+  // Queries: item (head hq, c) covers dims 8c..8c+7 and 64+8c..64+8c+7 (the
+  // rotate-half pairs); the 8 items of one head are 8 consecutive lanes.
+  for (int it = tid; it < p.Hq * 8; it += 256) {
+    const int hq = it >> 3, c = it & 7;
+    const int g = hq / G, row = i * G + hq % G;
+    uint32_t wl[4] = {0, 0, 0, 0}, wh[4] = {0, 0, 0, 0};
+    float part = 0.0f;
+    if (live) {
+      const uint16_t* qrow = p.q + (node_row * p.Hq + hq) * kD;
+      const uint16_t* krow = p.k_new + (static_cast<size_t>(b) * p.n_max * p.Hkv + g) * kD;   // root
+      const uint4 qlo = *reinterpret_cast<const uint4*>(qrow + 8 * c);
+      const uint4 qhi = *reinterpret_cast<const uint4*>(qrow + 64 + 8 * c);
+      const uint4 klo = *reinterpret_cast<const uint4*>(krow + 8 * c);
+      const uint4 khi = *reinterpret_cast<const uint4*>(krow + 64 + 8 * c);
+#pragma unroll
+      for (int u2 = 0; u2 < 4; ++u2) {
+        float rl[2], rh[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int j = 8 * c + 2 * u2 + u;
+          const float2 cn = cs_node[j];
+          const float xl = bf16_bits_to_f32(u4_elem(qlo, 2 * u2 + u));
+          const float xh = bf16_bits_to_f32(u4_elem(qhi, 2 * u2 + u));
+          rl[u] = (xl * cn.x - xh * cn.y) * qs;
+          rh[u] = (xh * cn.x + xl * cn.y) * qs;
+        }
+        wl[u2] = pack_bf16(rl[0], rl[1]);
+        wh[u2] = pack_bf16(rh[0], rh[1]);
+        // score against the rotated root key as stored (bf16), with the
+        // rounded query as the matrix cores see it
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int j = 8 * c + 2 * u2 + u;
+          const float2 c0 = cs_root[j];
+          const float kxl = bf16_bits_to_f32(u4_elem(klo, 2 * u2 + u));
+          const float kxh = bf16_bits_to_f32(u4_elem(khi, 2 * u2 + u));
+          const float kl = bf16_bits_to_f32(f32_to_bf16_bits(kxl * c0.x - kxh * c0.y));
+          const float kh = bf16_bits_to_f32(f32_to_bf16_bits(kxh * c0.x + kxl * c0.y));
+          const float ql = u ? bf16_hi(wl[u2]) : bf16_lo(wl[u2]);
+          const float qh = u ? bf16_hi(wh[u2]) : bf16_lo(wh[u2]);
+          part = fmaf(ql, kl, part);
+          part = fmaf(qh, kh, part);
+        }
+      }
+    }
+    part += __shfl_xor(part, 1);
+    part += __shfl_xor(part, 2);
+    part += __shfl_xor(part, 4);
+    // B operand of lane (row % 32) + 32 h, k-step kk holds dims 16 kk + 8 h + 0..7
+    const size_t tile = (static_cast<size_t>(b) * p.Hkv + g) * row_tiles + (row >> 5);
+    const int m = row & 31;
+    p.qprep[(tile * 8 + (c >> 1)) * 64 + m + 32 * (c & 1)] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
+    p.qprep[(tile * 8 + 4 + (c >> 1)) * 64 + m + 32 * (c & 1)] = make_uint4(wh[0], wh[1], wh[2], wh[3]);
+    if (c == 0) p.rref[(static_cast<size_t>(b) * p.Hkv + g) * p.rows_pad + row] = part;
+  }
+  if (!live) return;
+
+  // Tree keys, rotated at P + depth, and raw values go to cache slot P + i.
+  const int slot = P + i;
+  for (int it = tid; it < p.Hkv * 8; it += 256) {
+    const int g = it >> 3, c = it & 7;
+    const uint16_t* krow = p.k_new + (node_row * p.Hkv + g) * kD;
+    const uint4 lo = *reinterpret_cast<const uint4*>(krow + 8 * c);
+    const uint4 hi = *reinterpret_cast<const uint4*>(krow + 64 + 8 * c);
+    uint32_t wl[4], wh[4];
+#pragma unroll
+    for (int u2 = 0; u2 < 4; ++u2) {
+      float rl[2], rh[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const float2 cn = cs_node[8 * c + 2 * u2 + u];
+        const float xl = bf16_bits_to_f32(u4_elem(lo, 2 * u2 + u));
+        const float xh = bf16_bits_to_f32(u4_elem(hi, 2 * u2 + u));
+        rl[u] = xl * cn.x - xh * cn.y;
+        rh[u] = xh * cn.x + xl * cn.y;
+      }
+      wl[u2] = pack_bf16(rl[0], rl[1]);
+      wh[u2] = pack_bf16(rh[0], rh[1]);
+    }
+    uint16_t* kdst = p.k_cache + ((static_cast<size_t>(b) * p.Hkv + g) * p.cap + slot) * kD;
+    *reinterpret_cast<uint4*>(kdst + 8 * c) = make_uint4(wl[0], wl[1], wl[2], wl[3]);
+    *reinterpret_cast<uint4*>(kdst + 64 + 8 * c) = make_uint4(wh[0], wh[1], wh[2], wh[3]);
+  }
+  for (int it = tid; it < p.Hkv * 16; it += 256) {
+    const int g = it >> 4, c = it & 15;
+    const uint4 v = *reinterpret_cast<const uint4*>(p.v_new + (node_row * p.Hkv + g) * kD + 8 * c);
+    uint16_t* vh = p.v_cache + (static_cast<size_t>(b) * p.Hkv + g) * p.cap * kD;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) vh[v_cache_off(slot, 8 * c + u)] = u4_elem(v, u);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// main: grid (splits * row_blocks, Hkv, B), WAVES * 64 threads
+// ---------------------------------------------------------------------------
+
 // Running softmax state of one 32-row query tile.
 struct RowState {
   f32x16 o[4];      // O^T accumulator: d = 32 dt + 8 (e>>2) + 4 h + (e&3)
@@ -150,19 +333,24 @@ struct RowState {
   float l;          // this lane's share of the row sum
 };
 
+// Key j of a tile is visible to a row iff j < P, or bit j - P of the row's
+// ancestor mask is set; rel = j - P.
+__device__ __forceinline__ bool key_visible(int rel, uint64_t anc) {
+  return rel < 0 || (rel < 64 && ((anc >> rel) & 1ull) != 0ull);
+}
+
 // Softmax of one 32-key score block of one query tile. x holds the scores
 // minus the row's reference r (fixed for the pass): no max, no branch.
 // Returns the probabilities packed as two B operands (keys 16 half + 8 h +
-// 0..7).
-template <bool MASKED, bool TREE>
-__device__ __forceinline__ void block_softmax(RowState& st, f32x16& x, bf16x8 (&pf)[2], int sub, int h,
-                                              int valid_keys, uint64_t anc) {
+// 0..7). rel0 = (first key of the tile) - P for masked tiles.
+template <bool MASKED>
+__device__ __forceinline__ void block_softmax(RowState& st, f32x16& x, bf16x8 (&pf)[2], int sub, int h, int rel0,
+                                              uint64_t anc) {
   if (MASKED) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int key = 32 * sub + 16 * (e >> 3) + 8 * h + (e & 7);
-      const bool vis = TREE ? ((anc >> key) & 1ull) != 0ull : key < valid_keys;
-      if (!vis) x[e] = -INFINITY;
+      if (!key_visible(rel0 + key, anc)) x[e] = -INFINITY;
     }
   }
   float pe[16];
@@ -180,15 +368,12 @@ __device__ __forceinline__ void block_softmax(RowState& st, f32x16& x, bf16x8 (&
 }
 
 // One staged 64-key tile times the QT query tiles of a wavefront, in two
-// 32-key halves. Each K and V fragment read from LDS feeds QT MFMAs. All
-// fragment reads are issued up front and the whole tile is one basic block,
-// so the scheduler can overlap one half's exponentials with the other half's
-// matrix work.
-template <int QT, bool MASKED, bool TREE>
+// 32-key halves. Each K and V fragment read from LDS feeds QT MFMAs.
+template <int QT, bool MASKED>
 __device__ __forceinline__ void tile_product(RowState (&st)[QT], const uint16_t* __restrict__ ks,
                                              const uint16_t* __restrict__ vs, const bf16x8 (&qf)[QT][8],
-                                             const int (&k_addr)[8], const int (&v_addr)[4], int h,
-                                             int valid_keys, const uint64_t (&anc)[QT]) {
+                                             const int (&k_addr)[8], const int (&v_addr)[4], int h, int rel0,
+                                             const uint64_t (&anc)[QT]) {
   f32x16 x[2][QT];
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub) {
@@ -213,7 +398,7 @@ __device__ __forceinline__ void tile_product(RowState (&st)[QT], const uint16_t*
         va[2 * dt + half] = *reinterpret_cast<const bf16x8*>(vs + v_addr[2 * sub + half] + dt * 32 * kKT);
     bf16x8 pf[QT][2];
 #pragma unroll
-    for (int t = 0; t < QT; ++t) block_softmax<MASKED, TREE>(st[t], x[sub][t], pf[t], sub, h, valid_keys, anc[t]);
+    for (int t = 0; t < QT; ++t) block_softmax<MASKED>(st[t], x[sub][t], pf[t], sub, h, rel0, anc[t]);
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -226,9 +411,9 @@ __device__ __forceinline__ void tile_product(RowState (&st)[QT], const uint16_t*
 
 // Scores only: raises mx[t] to this lane's max visible score (log2 units) of
 // one staged tile. Used by the fallback that finds each row's exact max.
-template <int QT, bool MASKED, bool TREE>
+template <int QT, bool MASKED>
 __device__ __forceinline__ void tile_max(float (&mx)[QT], const uint16_t* __restrict__ ks, const bf16x8 (&qf)[QT][8],
-                                         const int (&k_addr)[8], int h, int valid_keys, const uint64_t (&anc)[QT]) {
+                                         const int (&k_addr)[8], int h, int rel0, const uint64_t (&anc)[QT]) {
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub) {
     bf16x8 ka[8];
@@ -242,54 +427,63 @@ __device__ __forceinline__ void tile_max(float (&mx)[QT], const uint16_t* __rest
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int key = 32 * sub + 16 * (e >> 3) + 8 * h + (e & 7);
-        const bool vis = !MASKED || (TREE ? ((anc[t] >> key) & 1ull) != 0ull : key < valid_keys);
-        if (vis) mx[t] = fmaxf(mx[t], x[e]);
+        if (!MASKED || key_visible(rel0 + key, anc[t])) mx[t] = fmaxf(mx[t], x[e]);
       }
     }
   }
 }
 
-// Direct global -> LDS copy of 16 bytes per lane: lane i of the wavefront
-// writes LDS bytes [lds_base + 16 i, +16). lds_base must be wave-uniform.
-__device__ __forceinline__ void load_lds16(const uint16_t* gsrc, uint16_t* lds_base) {
-  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)gsrc,
-                                   (void __attribute__((address_space(3)))*)lds_base, 16, 0, 0);
+// Writes normalised rows of one wavefront (lane: row row0 + 32 t + l%32,
+// dims 32 dt + 8 i4 + 4 h + 0..3); dead rows get zeros.
+template <int QT>
+__device__ __forceinline__ void write_rows(const BfParams& p, int b, int g, int row0, int rows_live, int rows_all,
+                                           int lane, const f32x16 (&o)[QT][4], const float (&l)[QT]) {
+  const int h = lane >> 5;
+#pragma unroll
+  for (int t = 0; t < QT; ++t) {
+    const int row = row0 + 32 * t + (lane & 31);
+    if (row < rows_all) {
+      const bool live = row < rows_live;
+      const int head = g * p.G + row % p.G, node = row / p.G;
+      uint16_t* orow = p.out + ((static_cast<size_t>(b) * p.n_max + node) * p.Hq + head) * kD;
+      const float inv = (live && l[t] > 0.0f) ? 1.0f / l[t] : 0.0f;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          uint2 w;
+          w.x = live ? pack_bf16(o[t][dt][4 * i4 + 0] * inv, o[t][dt][4 * i4 + 1] * inv) : 0u;
+          w.y = live ? pack_bf16(o[t][dt][4 * i4 + 2] * inv, o[t][dt][4 * i4 + 3] * inv) : 0u;
+          *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * i4 + 4 * h) = w;
+        }
+    }
+  }
 }
-// Waits until at most N vector memory operations of this wavefront are
-// outstanding (N must be a compile-time constant).
-template <int N>
-__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
 template <int WAVES, int QT>
 __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   constexpr int NT = WAVES * 64;
   constexpr int ROWS = WAVES * 32 * QT;      // query rows of the workgroup
   constexpr int CPT = (kKT * kD / 8) / NT;   // 16-byte chunks per thread per K (or V) stage
-  static_assert(2 * CPT * (kStages - 2) <= 63, "vmcnt range");
+  static_assert(2 * CPT * (kStages - 1) <= 63, "vmcnt range");
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kStages * kStageElems];  // (K, V) x stages
-  __shared__ float2 cs_table[kTableDepths * 64];
-  __shared__ int s_dmax;
 
   const int s = blockIdx.x % p.splits;
   const int rb = blockIdx.x / p.splits;
   const int g = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = p.G;
 
-  const int n = p.n_nodes[b];
-  const int P = p.prefix_len[b];
-  const int e_in = p.err[b];
-  const bool cap_bad = (e_in == 0) && (n > 0) && (n <= p.n_max) && (P < 0 || P + n > p.cap);
-  const bool skip = (e_in != 0) || (n <= 0) || (n > p.n_max) || cap_bad;
-  if (cap_bad && blockIdx.x == 0 && g == 0 && tid == 0) p.err[b] = TV_ERR_CAPACITY;
-
-  const int rows_live = skip ? 0 : G * n;
+  const SeqState sq = seq_state(p, b);
+  const int n = sq.n, P = sq.P;
+  const int rows_live = sq.skip ? 0 : G * n;
   const int rows_all = G * p.n_max;
   const int rb0 = rb * ROWS;
   const int r0 = rb0 + wave * 32 * QT;       // first row of this wavefront
 
   if (rb0 >= rows_live) {
-    // nothing live in this row block: zero rows (single split) and leave
+    // nothing live in this row block; with splits the merge writes the zeros
     if (p.splits == 1) {
       for (int r = rb0 + tid / 16; r < min(rb0 + ROWS, rows_all); r += NT / 16) {
         const int i = r / G, head = g * G + r % G;
@@ -300,27 +494,19 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
     return;
   }
 
-  int my_row[QT];
-  bool row_live[QT];
-  uint64_t my_anc[QT];
-#pragma unroll
-  for (int t = 0; t < QT; ++t) {
-    my_row[t] = r0 + 32 * t + (lane & 31);
-    row_live[t] = my_row[t] < rows_live;
-    my_anc[t] = row_live[t] ? p.anc[static_cast<size_t>(b) * p.n_max + my_row[t] / G] : 0ull;
-  }
-
-  // prefix keys of this split, in whole 64-key tiles
-  const int n_tiles_all = (P + kKT - 1) / kKT;
-  const int tiles_per_split = (n_tiles_all + p.splits - 1) / p.splits;
-  const int k_begin = min(P, s * tiles_per_split * kKT);
-  const int k_end = min(P, k_begin + tiles_per_split * kKT);
-  const int n_tiles = (k_end - k_begin + kKT - 1) / kKT;
-  const bool last_split = (s == p.splits - 1);
+  // Keys of b: slots [0, P + n), in aligned 64-key tiles shared out over the
+  // splits. Tiles ending past P are masked (they hold the tree).
+  const int key_end = P + n;
+  const int tiles_all = (key_end + kKT - 1) / kKT;
+  const int tiles_per_split = (tiles_all + p.splits - 1) / p.splits;
+  const int t_begin = min(tiles_all, s * tiles_per_split);
+  const int n_tiles = min(tiles_all, t_begin + tiles_per_split) - t_begin;
+  const int k_begin = t_begin * kKT;
 
   // stage buf: K at smem + 2 buf * kStageElems, V right after it
   auto Ks = [&](int buf) { return smem + 2 * buf * kStageElems; };
   auto Vs = [&](int buf) { return smem + (2 * buf + 1) * kStageElems; };
+  const uint32_t lds_base = lds_addr(smem);
 
   const size_t head_off = (static_cast<size_t>(b) * p.Hkv + g) * p.cap * kD;
   const uint16_t* kc = p.k_cache + head_off;
@@ -337,118 +523,61 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
     for (int u = 0; u < 4; ++u) v_addr[u] = vs_off(d, 2 * u + h);
   }
 
-  // Issues the copy of prefix tile [kt0, kt0+64) into stage `buf`. LDS chunk
-  // c (16 bytes) of a stage is K row c/16, position c%16 (unit swizzled by
-  // key) and V row c/8, position c%8 (unit swizzled by d); the lane that
-  // writes chunk c fetches the matching global chunk. Keys past the prefix
-  // are still inside the (64-slot aligned) cache; they are masked later.
+  // Copies key tile [kt0, kt0+64) into stage `buf`. LDS chunk c (16 bytes)
+  // of a stage is K row c/16, position c%16 (unit swizzled by key) and V row
+  // c/8, position c%8 (unit swizzled by d); the lane that writes chunk c
+  // fetches the matching global chunk.
+  uint32_t k_voff[CPT], v_voff[CPT];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) {
+    const int c = j * NT + tid;
+    const int key = c >> 4, kpos = c & 15;
+    k_voff[j] = static_cast<uint32_t>(key * kD + ((kpos ^ k_swz(key)) << 3)) * 2u;
+    const int d = c >> 3, vpos = c & 7;
+    v_voff[j] = static_cast<uint32_t>(d * kKT + ((vpos ^ (d & 7)) << 3)) * 2u;
+  }
   auto issue_tile = [&](int kt0, int buf) {
     const uint16_t* ktile = kc + static_cast<size_t>(kt0) * kD;
     const uint16_t* vtile = vc + static_cast<size_t>(kt0) * kD;   // kt0 is a multiple of 64
+    const uint32_t kl = lds_base + static_cast<uint32_t>(2 * buf * kStageElems + wave * 64 * 8) * 2u;
+    const uint32_t vl = kl + kStageElems * 2u;
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
-      const int c = j * NT + tid;
-      const int key = c >> 4, kpos = c & 15;
-      load_lds16(ktile + key * kD + ((kpos ^ k_swz(key)) << 3), Ks(buf) + (j * NT + wave * 64) * 8);
-      const int d = c >> 3, vpos = c & 7;
-      load_lds16(vtile + d * kKT + ((vpos ^ (d & 7)) << 3), Vs(buf) + (j * NT + wave * 64) * 8);
+      dma16(ktile, k_voff[j], kl + j * NT * 16);
+      dma16(vtile, v_voff[j], vl + j * NT * 16);
     }
   };
 
-  // ---- 1. start copying the first prefix tiles (overlaps the prologue)
-#pragma unroll
-  for (int t = 0; t < kStages - 1; ++t)
-    if (t < n_tiles) issue_tile(k_begin + t * kKT, t);
+  // ---- 1. first tile, then the operands (consumed before the next tiles)
+  if (n_tiles > 0) issue_tile(k_begin, 0);
 
-  // ---- 2. cos/sin table for the tree's depths (positions P + depth)
-  if (wave == 0) {
-    int dv = (lane < n) ? p.depth[static_cast<size_t>(b) * p.n_max + lane] : 0;
-    dv = wave_max_i32(dv);
-    if (lane == 0) s_dmax = dv;
-  }
-  __syncthreads();
-  const int table_rows = min(s_dmax, kTableDepths - 1) + 1;
-  for (int idx = tid; idx < table_rows * 64; idx += NT)
-    cs_table[idx] = p.rope ? rope_cs(P + (idx >> 6), p.inv_freq[idx & 63]) : make_float2(1.0f, 0.0f);
-  __syncthreads();
-  auto cs_at = [&](int dep, int pair) -> float2 {
-    if (dep < kTableDepths) return cs_table[dep * 64 + pair];
-    return p.rope ? rope_cs(P + dep, p.inv_freq[pair]) : make_float2(1.0f, 0.0f);
-  };
-
-  // ---- 3. rotated, pre-scaled queries as B operands:
-  //         qf[t][kk] = Q[row][16kk + 8h .. +8] * scale * log2(e)
-  bf16x8 qf[QT][8];
-  const float qs = p.scale_log2;
+  int my_row[QT];
+  bool row_live[QT];
+  uint64_t my_anc[QT];
+  float r_ref[QT];
+  bf16x8 qf[QT][8];   // qf[t][kk] = rotated, scaled Q[row][16kk + 8h .. +8]
+  const size_t head_rows = (static_cast<size_t>(b) * p.Hkv + g) * p.rows_pad;
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
-    if (row_live[t]) {
-      const int node = my_row[t] / G;
-      const int head = g * G + my_row[t] % G;
-      const int dep = p.depth[static_cast<size_t>(b) * p.n_max + node];
-      const uint16_t* qrow = p.q + ((static_cast<size_t>(b) * p.n_max + node) * p.Hq + head) * kD;
+    my_row[t] = r0 + 32 * t + (lane & 31);
+    row_live[t] = my_row[t] < rows_live;
+    const int node = min(my_row[t] / G, p.n_max - 1);   // padding rows load a valid row
+    my_anc[t] = p.anc[static_cast<size_t>(b) * p.n_max + node];
+    r_ref[t] = p.rref[head_rows + my_row[t]];
+    const uint4* qsrc = p.qprep + ((head_rows + r0 + 32 * t) / 32) * 8 * 64 + lane;
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        const int d0 = 16 * s4 + 8 * h;
-        const uint4 lo = *reinterpret_cast<const uint4*>(qrow + d0);
-        const uint4 hi = *reinterpret_cast<const uint4*>(qrow + 64 + d0);
-        uint32_t wl[4], wh[4];
-#pragma unroll
-        for (int u2 = 0; u2 < 8; u2 += 2) {
-          float rl[2], rh[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const float2 cs = cs_at(dep, d0 + u2 + u);
-            const float xl = bf16_bits_to_f32(u4_elem(lo, u2 + u));
-            const float xh = bf16_bits_to_f32(u4_elem(hi, u2 + u));
-            rl[u] = (xl * cs.x - xh * cs.y) * qs;
-            rh[u] = (xh * cs.x + xl * cs.y) * qs;
-          }
-          wl[u2 >> 1] = pack_bf16(rl[0], rl[1]);
-          wh[u2 >> 1] = pack_bf16(rh[0], rh[1]);
-        }
-        qf[t][s4] = __builtin_bit_cast(bf16x8, make_uint4(wl[0], wl[1], wl[2], wl[3]));
-        qf[t][s4 + 4] = __builtin_bit_cast(bf16x8, make_uint4(wh[0], wh[1], wh[2], wh[3]));
-      }
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) qf[t][kk] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
-    }
+    for (int kk = 0; kk < 8; ++kk) qf[t][kk] = __builtin_bit_cast(bf16x8, qsrc[kk * 64]);
   }
-
-  // ---- 4. reference score per row: the row's score against the tree root,
-  // which every node sees. Scores are taken relative to it, so on the fast
-  // path no running max is needed.
-  float r_root[QT];
-  {
-    const uint16_t* kr = p.k_new + (static_cast<size_t>(b) * p.n_max * p.Hkv + g) * kD;   // node 0
 #pragma unroll
-    for (int t = 0; t < QT; ++t) r_root[t] = 0.0f;
+  for (int t = 0; t < QT; ++t) {
+    touch(my_anc[t]);
+    touch(r_ref[t]);
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      const int d0 = 16 * s4 + 8 * h;
-      const uint4 lo = *reinterpret_cast<const uint4*>(kr + d0);
-      const uint4 hi = *reinterpret_cast<const uint4*>(kr + 64 + d0);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float2 cs = cs_at(0, d0 + u);
-        const float xl = bf16_bits_to_f32(u4_elem(lo, u));
-        const float xh = bf16_bits_to_f32(u4_elem(hi, u));
-        // the rotated root key as stored (rounded to bf16)
-        const float kl = bf16_bits_to_f32(f32_to_bf16_bits(xl * cs.x - xh * cs.y));
-        const float kh = bf16_bits_to_f32(f32_to_bf16_bits(xh * cs.x + xl * cs.y));
-#pragma unroll
-        for (int t = 0; t < QT; ++t) {
-          const uint4 ql = __builtin_bit_cast(uint4, qf[t][s4]);
-          const uint4 qh = __builtin_bit_cast(uint4, qf[t][s4 + 4]);
-          r_root[t] = fmaf(bf16_bits_to_f32(u4_elem(ql, u)), kl, r_root[t]);
-          r_root[t] = fmaf(bf16_bits_to_f32(u4_elem(qh, u)), kh, r_root[t]);
-        }
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < QT; ++t) r_root[t] = row_sum2(r_root[t]);
+    for (int kk = 0; kk < 8; ++kk) touch(qf[t][kk]);
   }
+#pragma unroll
+  for (int t = 1; t < kStages - 1; ++t)
+    if (t < n_tiles) issue_tile(k_begin + t * kKT, t);
 
   RowState st[QT];
   auto reset_state = [&]() {
@@ -456,98 +585,38 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
     for (int t = 0; t < QT; ++t) {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) st[t].o[dt] = f32x16{};
-      st[t].r = r_root[t];
-      st[t].negr = f32x16{} - r_root[t];
+      st[t].r = r_ref[t];
+      st[t].negr = f32x16{} - r_ref[t];
       st[t].l = 0.0f;
     }
   };
   reset_state();
 
-  // One pass over the tree tile and the prefix tiles; the first kStages - 1
-  // prefix tiles must already be in flight. MAX_ONLY passes only raise mx to
-  // the row maxima of the scores.
+  // One pass over this split's tiles (the first kStages - 1 already in
+  // flight). MAX_ONLY passes only raise mx to the row maxima of the scores.
   float mx[QT];
   auto run_pass = [&](auto mode_tag) {
     constexpr bool MAX_ONLY = decltype(mode_tag)::value;
-    auto product = [&](auto masked_tag, auto tree_tag, const uint16_t* ks_, const uint16_t* vs_, int valid_) {
-      constexpr bool M = decltype(masked_tag)::value, T = decltype(tree_tag)::value;
+    auto product = [&](auto masked_tag, const uint16_t* ks_, const uint16_t* vs_, int rel0) {
+      constexpr bool M = decltype(masked_tag)::value;
       if constexpr (MAX_ONLY)
-        tile_max<QT, M, T>(mx, ks_, qf, k_addr, h, valid_, my_anc);
+        tile_max<QT, M>(mx, ks_, qf, k_addr, h, rel0, my_anc);
       else
-        tile_product<QT, M, T>(st, ks_, vs_, qf, k_addr, v_addr, h, valid_, my_anc);
+        tile_product<QT, M>(st, ks_, vs_, qf, k_addr, v_addr, h, rel0, my_anc);
     };
-    // ---- 4. tree tile (last split only), in the ring's last stage, which no
-    // prefix tile occupies before the first loop iteration: rotate k_new,
-    // stage, append to the cache, multiply
-    if (last_split) {
-      uint16_t* ksT = Ks(kStages - 1);
-      uint16_t* vsT = Vs(kStages - 1);
-      const size_t new_base = static_cast<size_t>(b) * p.n_max;
-      const bool append = (rb == 0);
-      for (int it = tid; it < 64 * 8; it += NT) {
-        const int a = it >> 3, c = it & 7;
-        uint4 lo_o = make_uint4(0, 0, 0, 0), hi_o = make_uint4(0, 0, 0, 0);
-        if (a < n) {
-          const uint16_t* kr = p.k_new + ((new_base + a) * p.Hkv + g) * kD;
-          const uint4 lo = *reinterpret_cast<const uint4*>(kr + 8 * c);
-          const uint4 hi = *reinterpret_cast<const uint4*>(kr + 64 + 8 * c);
-          const int dep = p.depth[new_base + a];
-          uint32_t wl[4], wh[4];
-  #pragma unroll
-          for (int u2 = 0; u2 < 8; u2 += 2) {
-            float rl[2], rh[2];
-  #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              const float2 cs = cs_at(dep, 8 * c + u2 + u);
-              const float xl = bf16_bits_to_f32(u4_elem(lo, u2 + u));
-              const float xh = bf16_bits_to_f32(u4_elem(hi, u2 + u));
-              rl[u] = xl * cs.x - xh * cs.y;
-              rh[u] = xh * cs.x + xl * cs.y;
-            }
-            wl[u2 >> 1] = pack_bf16(rl[0], rl[1]);
-            wh[u2 >> 1] = pack_bf16(rh[0], rh[1]);
-          }
-          lo_o = make_uint4(wl[0], wl[1], wl[2], wl[3]);
-          hi_o = make_uint4(wh[0], wh[1], wh[2], wh[3]);
-          if (append) {
-            uint16_t* kdst = p.k_cache + head_off + static_cast<size_t>(P + a) * kD;
-            *reinterpret_cast<uint4*>(kdst + 8 * c) = lo_o;
-            *reinterpret_cast<uint4*>(kdst + 64 + 8 * c) = hi_o;
-          }
-        }
-        *reinterpret_cast<uint4*>(ksT + ks_off(a, c)) = lo_o;
-        *reinterpret_cast<uint4*>(ksT + ks_off(a, c + 8)) = hi_o;
-      }
-      // V: lane <-> node, so the appends of one head dim are consecutive slots
-      for (int it = tid; it < 64 * 16; it += NT) {
-        const int a = it & 63, c = it >> 6;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (a < n) v = *reinterpret_cast<const uint4*>(p.v_new + ((new_base + a) * p.Hkv + g) * kD + 8 * c);
-  #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int d = 8 * c + u;
-          const uint16_t e = u4_elem(v, u);
-          vsT[vs_off(d, a >> 3) + (a & 7)] = e;
-          if (append && a < n) p.v_cache[head_off + v_cache_off(P + a, d)] = e;
-        }
-      }
-      __syncthreads();
-      product(std::true_type{}, std::true_type{}, ksT, vsT, kKT);
-    }
-
-    // ---- 5. prefix tiles: a ring of kStages LDS stages, kStages - 1 tiles in
-    // flight; tile t lives in stage t % kStages. The steady-state loop only sees
-    // full tiles with kStages - 2 later tiles outstanding, so it is one straight
-    // block; the last kStages - 1 tiles (the drain, and a partial last tile) are
-    // peeled off below. Wavefronts whose rows are all padding compute on zero
-    // queries rather than branch around the products.
+    // A ring of kStages LDS stages, kStages - 1 tiles in flight; tile t lives
+    // in stage t % kStages. The steady-state loop only sees prefix tiles with
+    // kStages - 2 later tiles outstanding, so it is one straight block; the
+    // last kStages - 1 tiles (the drain, which holds the at most two masked
+    // tiles) are peeled off below. Wavefronts whose rows are all padding
+    // compute on their (zero) queries rather than branch around the products.
     int t = 0;
     for (; t + kStages - 1 < n_tiles; ++t) {
       const int cur = t % kStages;
       wait_vm<2 * CPT * (kStages - 2)>();
       __syncthreads();   // tile t has landed for every wave; stage (t-1) % kStages is free
       issue_tile(k_begin + (t + kStages - 1) * kKT, (t + kStages - 1) % kStages);
-      product(std::false_type{}, std::false_type{}, Ks(cur), Vs(cur), kKT);
+      product(std::false_type{}, Ks(cur), Vs(cur), 0);
     }
     for (; t < n_tiles; ++t) {
       const int cur = t % kStages;
@@ -557,23 +626,25 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
       else if (later == 1) wait_vm<2 * CPT>();
       else wait_vm<0>();
       __syncthreads();
-      const int valid = min(kKT, k_end - (k_begin + t * kKT));
-      if (valid == kKT) {
-        product(std::false_type{}, std::false_type{}, Ks(cur), Vs(cur), kKT);
+      const int kt0 = k_begin + t * kKT;
+      if (kt0 + kKT <= P) {
+        product(std::false_type{}, Ks(cur), Vs(cur), 0);
       } else {
-        // stale slots past the prefix may hold anything: zero their V
-        for (int idx = tid; idx < (kKT - valid) * kD; idx += NT) {
-          const int key = valid + idx / kD, d = idx % kD;
+        // slots past P + n are not this call's keys and may hold anything:
+        // zero their values (their scores are masked)
+        const int stale0 = max(0, key_end - kt0);
+        for (int idx = tid; idx < (kKT - stale0) * kD; idx += NT) {
+          const int key = stale0 + idx / kD, d = idx % kD;
           Vs(cur)[vs_off(d, key >> 3) + (key & 7)] = 0;
         }
         __syncthreads();
-        product(std::true_type{}, std::false_type{}, Ks(cur), Vs(cur), valid);
+        product(std::true_type{}, Ks(cur), Vs(cur), kt0 - P);
       }
     }
-
   };
 
   run_pass(std::false_type{});
+
   // A row whose scores rose far above its root score (p > 2^62) would lose
   // precision or overflow on that reference: find every row's exact max in a
   // scores-only pass, then redo the pass with r = max (all p <= 1).
@@ -590,7 +661,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
       const float m = row_max2(mx[t]);
-      r_root[t] = (m == -INFINITY) ? r_root[t] : m;
+      r_ref[t] = (m == -INFINITY) ? r_ref[t] : m;
     }
     reset_state();
     __syncthreads();
@@ -600,76 +671,88 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
     run_pass(std::false_type{});
   }
 
-  // ---- 6. epilogue
+  // ---- epilogue
+  float l_row[QT];
+#pragma unroll
+  for (int t = 0; t < QT; ++t) l_row[t] = row_sum2(st[t].l);
+  if (p.splits == 1) {
+    f32x16 o[QT][4];
+#pragma unroll
+    for (int t = 0; t < QT; ++t)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) o[t][dt] = st[t].o[dt];
+    write_rows<QT>(p, b, g, r0, rows_live, rows_all, lane, o, l_row);
+    return;
+  }
+  // Split partial in register order: the float4 of (wave, t, dt, i4) for
+  // lane l sits at (((wave * QT + t) * 16 + dt * 4 + i4) * 64 + l) within
+  // this workgroup's block; the (r, l) pair of (wave, t) for lane l at
+  // ((wave * QT + t) * 64 + l). Blocks are ordered (b, g, rb, s).
+  const size_t wg_id = ((static_cast<size_t>(b) * p.Hkv + g) * p.row_blocks + rb) * p.splits + s;
+  float4* po = p.part_o + wg_id * (ROWS * 32) + wave * (QT * 16 * 64) + lane;
+  float2* pm = p.part_ml + wg_id * (ROWS * 2) + wave * (QT * 64) + lane;
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
-    const float l_tot = row_sum2(st[t].l);
-    const int row = my_row[t];
-    if (p.splits == 1) {
-      if (row < rows_all) {
-        const int head = g * G + row % G;
-        const int node = row / G;
-        uint16_t* orow = p.out + ((static_cast<size_t>(b) * p.n_max + node) * p.Hq + head) * kD;
-        const float inv = (row_live[t] && l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-          for (int i4 = 0; i4 < 4; ++i4) {
-            const int d0 = 32 * dt + 8 * i4 + 4 * h;
-            uint2 w;
-            w.x = pack_bf16(st[t].o[dt][4 * i4 + 0] * inv, st[t].o[dt][4 * i4 + 1] * inv);
-            w.y = pack_bf16(st[t].o[dt][4 * i4 + 2] * inv, st[t].o[dt][4 * i4 + 3] * inv);
-            *reinterpret_cast<uint2*>(orow + d0) = w;
-          }
-      }
-    } else {
-      const size_t prow = ((static_cast<size_t>(b) * p.Hkv + g) * p.splits + s) * p.rows_pad + row;
-      float* po = p.part_o + prow * kD;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int d0 = 32 * dt + 8 * i4 + 4 * h;
-          *reinterpret_cast<float4*>(po + d0) = make_float4(st[t].o[dt][4 * i4 + 0], st[t].o[dt][4 * i4 + 1],
-                                                            st[t].o[dt][4 * i4 + 2], st[t].o[dt][4 * i4 + 3]);
-        }
-      if (h == 0) p.part_ml[prow] = make_float2(st[t].r, l_tot);
-    }
+      for (int i4 = 0; i4 < 4; ++i4)
+        po[(t * 16 + dt * 4 + i4) * 64] = make_float4(st[t].o[dt][4 * i4 + 0], st[t].o[dt][4 * i4 + 1],
+                                                      st[t].o[dt][4 * i4 + 2], st[t].o[dt][4 * i4 + 3]);
+    pm[t * 64] = make_float2(st[t].r, l_row[t]);
   }
 }
 
-// Combines the split partials of each row: one wavefront per row, two output
-// dims per lane.
+// ---------------------------------------------------------------------------
+// merge: grid (row_blocks * ROWS / 8, Hkv, B), 256 threads; thread = one
+// float4 of one lane's partial (same register order as the main kernel)
+// ---------------------------------------------------------------------------
+template <int WAVES, int QT>
 __global__ __launch_bounds__(256) void merge_bf16_kernel(BfParams p) {
+  constexpr int ROWS = WAVES * 32 * QT;
   const int g = blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r = blockIdx.x * 4 + wave;
-  if (r >= p.G * p.n_max) return;
-  const int node = r / p.G, head = g * p.G + r % p.G;
-  const int n = p.n_nodes[b];
-  const int P = p.prefix_len[b];
-  const bool skip = (p.err[b] != 0) || (n <= 0) || (n > p.n_max) || (P < 0) || (P + n > p.cap);
-  uint16_t* orow = p.out + ((static_cast<size_t>(b) * p.n_max + node) * p.Hq + head) * kD;
-  float o0 = 0.0f, o1 = 0.0f;
-  if (!skip && node < n) {
-    const size_t base = (static_cast<size_t>(b) * p.Hkv + g) * p.splits;
-    float M = -INFINITY;
-    for (int s = 0; s < p.splits; ++s) M = fmaxf(M, p.part_ml[(base + s) * p.rows_pad + r].x);
-    float L = 0.0f;
-    for (int s = 0; s < p.splits; ++s) {
-      const size_t prow = (base + s) * p.rows_pad + r;
-      const float2 ml = p.part_ml[prow];
-      const float w = (ml.x == -INFINITY) ? 0.0f : exp2f(ml.x - M);
-      L += w * ml.y;
-      const float2 o = *reinterpret_cast<const float2*>(p.part_o + prow * kD + 2 * lane);
-      o0 += w * o.x;
-      o1 += w * o.y;
-    }
-    const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
-    o0 *= inv;
-    o1 *= inv;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  const int rb = idx / (ROWS * 32);
+  const int rem = idx % (ROWS * 32);
+  const int lane = rem & 63, slot = rem >> 6;          // slot = (wave * QT + t) * 16 + dt * 4 + i4
+  const int wt = slot >> 4, dt = (slot >> 2) & 3, i4 = slot & 3;
+  const int row = rb * ROWS + wt * 32 + (lane & 31);   // wave * 32 QT + 32 t = 32 wt
+  const int rows_all = p.G * p.n_max;
+  if (rb >= p.row_blocks || row >= rows_all) return;
+  const SeqState sq = seq_state(p, b);
+  const int rows_live = sq.skip ? 0 : p.G * sq.n;
+  const int head = g * p.G + row % p.G, node = row / p.G;
+  uint16_t* dst = p.out + ((static_cast<size_t>(b) * p.n_max + node) * p.Hq + head) * kD +
+                  32 * dt + 8 * i4 + 4 * (lane >> 5);
+  if (row >= rows_live) {
+    *reinterpret_cast<uint2*>(dst) = make_uint2(0u, 0u);
+    return;
   }
-  reinterpret_cast<uint32_t*>(orow)[lane] = pack_bf16(o0, o1);
+  const size_t wg0 = ((static_cast<size_t>(b) * p.Hkv + g) * p.row_blocks + rb) * p.splits;
+  float2 ml[kMaxSplits];
+  float M = -INFINITY;
+#pragma unroll
+  for (int ss = 0; ss < kMaxSplits; ++ss) {
+    ml[ss] = (ss < p.splits) ? p.part_ml[(wg0 + ss) * (ROWS * 2) + wt * 64 + lane] : make_float2(-INFINITY, 0.0f);
+    M = fmaxf(M, ml[ss].x);
+  }
+  float4 o[kMaxSplits];
+#pragma unroll
+  for (int ss = 0; ss < kMaxSplits; ++ss)
+    o[ss] = (ss < p.splits) ? p.part_o[(wg0 + ss) * (ROWS * 32) + slot * 64 + lane] : make_float4(0, 0, 0, 0);
+  float L = 0.0f;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+  for (int ss = 0; ss < kMaxSplits; ++ss) {
+    const float w = (ml[ss].x == -INFINITY) ? 0.0f : exp2f(ml[ss].x - M);
+    L = fmaf(w, ml[ss].y, L);
+    acc.x = fmaf(w, o[ss].x, acc.x);
+    acc.y = fmaf(w, o[ss].y, acc.y);
+    acc.z = fmaf(w, o[ss].z, acc.z);
+    acc.w = fmaf(w, o[ss].w, acc.w);
+  }
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16(acc.x * inv, acc.y * inv), pack_bf16(acc.z * inv, acc.w * inv));
 }
 
 // Optional launch-shape override for tuning sweeps, read once:
@@ -686,6 +769,27 @@ const Tune& tune() {
     return r;
   }();
   return t;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Workspace layout: qprep | rref | part_ml | part_o (the last two only with
+// several splits).
+struct WsLayout {
+  size_t qprep, rref, part_ml, part_o, total;
+};
+WsLayout ws_layout(const tv_attn_args* a, const AttnPlan& pl) {
+  WsLayout w;
+  const size_t heads = static_cast<size_t>(a->B) * a->Hkv;
+  const size_t wg_rows = static_cast<size_t>(pl.waves) * 32 * pl.qt;
+  const size_t wgs = heads * pl.row_blocks * pl.splits;
+  w.qprep = 0;
+  w.rref = align_up(heads * pl.rows_pad * kD * 2);
+  w.part_ml = w.rref + align_up(heads * pl.rows_pad * sizeof(float));
+  w.part_o = w.part_ml + (pl.splits > 1 ? align_up(wgs * wg_rows * 2 * sizeof(float2)) : 0);
+  w.total = w.part_o + (pl.splits > 1 ? wgs * wg_rows * 32 * sizeof(float4) : 0);
+  return w;
 }
 
 }  // namespace
@@ -706,20 +810,16 @@ AttnPlan plan_attention_bf16(const tv_attn_args* a) {
   const int wg_rows = pl.waves * 32 * pl.qt;
   pl.row_blocks = (rows + wg_rows - 1) / wg_rows;
   const long units = static_cast<long>(a->B) * a->Hkv * pl.row_blocks;
-  // Split the prefix until the grid covers the 256 compute units, keeping at
+  // Split the keys until the grid covers the 256 compute units, keeping at
   // least four 64-key tiles per split. The prefix length lives on the device,
   // so the cache capacity bounds it here.
   const int max_tiles = (a->cap + kKT - 1) / kKT;
   int splits = 1;
-  while (units * splits < 256 && (max_tiles / (splits * 2)) >= 4) splits *= 2;
-  if (tn.splits > 0) splits = std::min(tn.splits, std::max(1, max_tiles));
+  while (units * splits < 256 && splits < kMaxSplits && (max_tiles / (splits * 2)) >= 4) splits *= 2;
+  if (tn.splits > 0) splits = std::min(std::min(tn.splits, kMaxSplits), std::max(1, max_tiles));
   pl.splits = splits;
   pl.rows_pad = pl.row_blocks * wg_rows;
-  pl.workspace_bytes = 0;
-  if (splits > 1) {
-    const size_t rows_total = static_cast<size_t>(a->B) * a->Hkv * splits * pl.rows_pad;
-    pl.workspace_bytes = rows_total * kD * sizeof(float) + rows_total * sizeof(float2);
-  }
+  pl.workspace_bytes = ws_layout(a, pl).total;
   return pl;
 }
 
@@ -749,24 +849,32 @@ hipError_t launch_attention_bf16(const tv_attn_args* a, const AttnPlan& pl, hipS
     p.inv_freq[d] = p.rope ? pow(static_cast<double>(a->rope_theta), -2.0 * d / kD) : 0.0;
   const float scale = a->softmax_scale > 0.0f ? a->softmax_scale : 1.0f / sqrtf(static_cast<float>(kD));
   p.scale_log2 = scale * 1.4426950408889634f;
-  p.part_o = nullptr;
-  p.part_ml = nullptr;
-  if (pl.splits > 1) {
-    const size_t rows_total = static_cast<size_t>(a->B) * a->Hkv * pl.splits * pl.rows_pad;
-    p.part_o = static_cast<float*>(a->workspace);
-    p.part_ml = reinterpret_cast<float2*>(static_cast<char*>(a->workspace) + rows_total * kD * sizeof(float));
-  }
+  const WsLayout w = ws_layout(a, pl);
+  char* ws = static_cast<char*>(a->workspace);
+  p.qprep = reinterpret_cast<uint4*>(ws + w.qprep);
+  p.rref = reinterpret_cast<float*>(ws + w.rref);
+  p.part_ml = pl.splits > 1 ? reinterpret_cast<float2*>(ws + w.part_ml) : nullptr;
+  p.part_o = pl.splits > 1 ? reinterpret_cast<float4*>(ws + w.part_o) : nullptr;
+
+  hipLaunchKernelGGL(prep_bf16_kernel, dim3(a->n_max, a->B), dim3(256), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   dim3 grid(pl.splits * pl.row_blocks, a->Hkv, a->B);
+  const int wg_rows = pl.waves * 32 * pl.qt;
+  dim3 mgrid(pl.row_blocks * wg_rows / 8, a->Hkv, a->B);
   const int key = pl.waves * 10 + pl.qt;
   switch (key) {
     case 21: hipLaunchKernelGGL((attn_bf16_kernel<2, 1>), grid, dim3(128), 0, s, p); break;
     case 41: hipLaunchKernelGGL((attn_bf16_kernel<4, 1>), grid, dim3(256), 0, s, p); break;
     default: hipLaunchKernelGGL((attn_bf16_kernel<4, 2>), grid, dim3(256), 0, s, p); break;
   }
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess || pl.splits == 1) return e;
-  dim3 mgrid((p.G * p.n_max + 3) / 4, a->Hkv, a->B);
-  hipLaunchKernelGGL(merge_bf16_kernel, mgrid, dim3(256), 0, s, p);
+  switch (key) {
+    case 21: hipLaunchKernelGGL((merge_bf16_kernel<2, 1>), mgrid, dim3(256), 0, s, p); break;
+    case 41: hipLaunchKernelGGL((merge_bf16_kernel<4, 1>), mgrid, dim3(256), 0, s, p); break;
+    default: hipLaunchKernelGGL((merge_bf16_kernel<4, 2>), mgrid, dim3(256), 0, s, p); break;
+  }
   return hipGetLastError();
 }
 
