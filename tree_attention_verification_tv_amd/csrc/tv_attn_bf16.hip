@@ -12,10 +12,9 @@
 //   prep   one workgroup per (node, sequence). Rotates the node's queries at
 //          P + depth, scales them by softmax_scale * log2(e), rounds them to
 //          bf16 and stores them in the exact register order of the score
-//          MFMA's B operand; computes each row's score against the tree root
-//          (the reference r below); rotates the node's keys and appends them,
-//          with the raw values, to cache slots P + i. It also flags
-//          sequences whose prefix plus tree exceeds the cache.
+//          MFMA's B operand; rotates the node's keys and appends them, with
+//          the raw values, to cache slots P + i. It also flags sequences
+//          whose prefix plus tree exceeds the cache.
 //
 //   main   workgroup = (row block rb, KV split s) of (sequence b, KV head g).
 //          Its query rows are the G query heads of g for every tree node,
@@ -38,15 +37,16 @@
 //          v_mfma_f32_32x32x16_bf16: a lane then holds 16 keys of ONE query
 //          row, so row reductions are lane-local plus one v_permlane32_swap.
 //          The output is also transposed, O^T = V^T P^T, so probabilities go
-//          from the score accumulator straight into the B operand. The score
-//          MFMA starts from an accumulator holding -r, so the accumulator IS
-//          the exponent: p = exp2(acc), with no running max and no branch in
-//          the tile loop. A row whose later scores rise more than 2^62 above
-//          r is caught from its final sum; the workgroup then finds every
-//          row's exact max in a scores-only pass and redoes the pass with
-//          r = max, where every p <= 1 (exact for any score range). Row sums
-//          are dot products of the bf16 probabilities with ones, i.e. exactly
-//          the weights the PV product used.
+//          from the score accumulator straight into the B operand. Softmax
+//          is invariant to a per-row shift, and fp32 / bf16 hold 2^s for
+//          scores s in log2 units far beyond any usual range, so the fast
+//          pass takes p = exp2(s) with no running max, no shift and no
+//          branch in the tile loop. A row whose sum left [2^-60, 2^62] is
+//          caught at the end; the workgroup then finds every row's exact max
+//          in a scores-only pass and redoes the pass with p = exp2(s - max)
+//          (exact for any score range). Row sums are dot products of the
+//          bf16 probabilities with ones, i.e. exactly the weights the PV
+//          product used.
 //
 //          The score MFMA reads K rows in a permuted order (row m of a 32-key
 //          block is key perm(m)), so each lane half holds 8 CONSECUTIVE keys
@@ -106,7 +106,6 @@ struct BfParams {
   int32_t* err;
   uint16_t* out;
   uint4* qprep;      // [B][Hkv][rows_pad/32][8][64] x 8 bf16: MFMA B operands
-  float* rref;       // [B][Hkv][rows_pad] reference score per row
   float4* part_o;    // split partials, register order (see the main epilogue)
   float2* part_ml;   // split (reference, row sum) per lane
   int n_max, Hq, Hkv, G, cap;
@@ -208,116 +207,106 @@ __device__ __forceinline__ SeqState seq_state(const BfParams& p, int b) {
 // ---------------------------------------------------------------------------
 // prep: grid (n_max, B), 256 threads
 // ---------------------------------------------------------------------------
+
+// Rotates 8 rotate-half pairs (dims 8c..8c+7 with 64+8c..64+8c+7) by the
+// angles cs[8c..8c+7], scales them and packs them to bf16.
+__device__ __forceinline__ void rotate8(const uint4& lo, const uint4& hi, const float2* cs, int c, float scale,
+                                        uint4& lo_out, uint4& hi_out) {
+  uint32_t wl[4], wh[4];
+#pragma unroll
+  for (int u2 = 0; u2 < 4; ++u2) {
+    float rl[2], rh[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const float2 cn = cs[8 * c + 2 * u2 + u];
+      const float xl = bf16_bits_to_f32(u4_elem(lo, 2 * u2 + u));
+      const float xh = bf16_bits_to_f32(u4_elem(hi, 2 * u2 + u));
+      rl[u] = (xl * cn.x - xh * cn.y) * scale;
+      rh[u] = (xh * cn.x + xl * cn.y) * scale;
+    }
+    wl[u2] = pack_bf16(rl[0], rl[1]);
+    wh[u2] = pack_bf16(rh[0], rh[1]);
+  }
+  lo_out = make_uint4(wl[0], wl[1], wl[2], wl[3]);
+  hi_out = make_uint4(wh[0], wh[1], wh[2], wh[3]);
+}
+
 __global__ __launch_bounds__(256) void prep_bf16_kernel(BfParams p) {
   __shared__ float2 cs_node[kD / 2];   // angle (P + depth) f_j
-  __shared__ float2 cs_root[kD / 2];   // angle P f_j
   const int i = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const size_t node_row = static_cast<size_t>(b) * p.n_max + i;
+  const int nq = p.Hq * 8, nk = p.Hkv * 8, nv = p.Hkv * 16;
+
+  // Every load of this thread's first items goes out before anything waits:
+  // their addresses do not depend on the sequence's state.
+  uint4 q_lo = make_uint4(0, 0, 0, 0), q_hi = q_lo, k_lo = q_lo, k_hi = q_lo, v_raw = q_lo;
+  if (tid < nq) {
+    const uint16_t* src = p.q + (node_row * p.Hq + (tid >> 3)) * kD + 8 * (tid & 7);
+    q_lo = *reinterpret_cast<const uint4*>(src);
+    q_hi = *reinterpret_cast<const uint4*>(src + 64);
+  }
+  if (tid < nk) {
+    const uint16_t* src = p.k_new + (node_row * p.Hkv + (tid >> 3)) * kD + 8 * (tid & 7);
+    k_lo = *reinterpret_cast<const uint4*>(src);
+    k_hi = *reinterpret_cast<const uint4*>(src + 64);
+  }
+  if (tid < nv) v_raw = *reinterpret_cast<const uint4*>(p.v_new + (node_row * p.Hkv + (tid >> 4)) * kD + 8 * (tid & 15));
+  const double freq = (tid < kD / 2) ? p.inv_freq[tid] : 0.0;
+  const int dep_raw = p.depth[node_row];
+
   const SeqState sq = seq_state(p, b);
   if (sq.cap_bad && i == 0 && tid == 0) p.err[b] = TV_ERR_CAPACITY;
   if (sq.skip) return;   // the main and merge kernels zero the rows of b
   const int P = sq.P;
   const bool live = i < sq.n;
-  const int dep = live ? min(max(p.depth[static_cast<size_t>(b) * p.n_max + i], 0), TV_MAX_NODES_DEV - 1) : 0;
-  if (tid < kD / 2) {
-    cs_node[tid] = p.rope ? rope_cs(P + dep, p.inv_freq[tid]) : make_float2(1.0f, 0.0f);
-    cs_root[tid] = p.rope ? rope_cs(P, p.inv_freq[tid]) : make_float2(1.0f, 0.0f);
-  }
+  const int dep = live ? min(max(dep_raw, 0), TV_MAX_NODES_DEV - 1) : 0;
+  if (tid < kD / 2) cs_node[tid] = p.rope ? rope_cs(P + dep, freq) : make_float2(1.0f, 0.0f);
   __syncthreads();
 
   const int G = p.G;
   const int row_tiles = p.rows_pad / 32;
-  const float qs = p.scale_log2;
-  const size_t node_row = static_cast<size_t>(b) * p.n_max + i;
-
-  // Queries: item (head hq, c) covers dims 8c..8c+7 and 64+8c..64+8c+7 (the
-  // rotate-half pairs); the 8 items of one head are 8 consecutive lanes.
-  for (int it = tid; it < p.Hq * 8; it += 256) {
+  // Queries: item it = (head it/8, c = it%8) covers dims 8c..8c+7 and
+  // 64+8c..; stored as the B operand of lane (row % 32) + 32 (c % 2) at
+  // k-steps c/2 and 4 + c/2 (k-step kk holds dims 16 kk + 8 h + 0..7).
+  // Nodes past n store zeros.
+  for (int it = tid; it < nq; it += 256) {
     const int hq = it >> 3, c = it & 7;
     const int g = hq / G, row = i * G + hq % G;
-    uint32_t wl[4] = {0, 0, 0, 0}, wh[4] = {0, 0, 0, 0};
-    float part = 0.0f;
-    if (live) {
-      const uint16_t* qrow = p.q + (node_row * p.Hq + hq) * kD;
-      const uint16_t* krow = p.k_new + (static_cast<size_t>(b) * p.n_max * p.Hkv + g) * kD;   // root
-      const uint4 qlo = *reinterpret_cast<const uint4*>(qrow + 8 * c);
-      const uint4 qhi = *reinterpret_cast<const uint4*>(qrow + 64 + 8 * c);
-      const uint4 klo = *reinterpret_cast<const uint4*>(krow + 8 * c);
-      const uint4 khi = *reinterpret_cast<const uint4*>(krow + 64 + 8 * c);
-#pragma unroll
-      for (int u2 = 0; u2 < 4; ++u2) {
-        float rl[2], rh[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int j = 8 * c + 2 * u2 + u;
-          const float2 cn = cs_node[j];
-          const float xl = bf16_bits_to_f32(u4_elem(qlo, 2 * u2 + u));
-          const float xh = bf16_bits_to_f32(u4_elem(qhi, 2 * u2 + u));
-          rl[u] = (xl * cn.x - xh * cn.y) * qs;
-          rh[u] = (xh * cn.x + xl * cn.y) * qs;
-        }
-        wl[u2] = pack_bf16(rl[0], rl[1]);
-        wh[u2] = pack_bf16(rh[0], rh[1]);
-        // score against the rotated root key as stored (bf16), with the
-        // rounded query as the matrix cores see it
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int j = 8 * c + 2 * u2 + u;
-          const float2 c0 = cs_root[j];
-          const float kxl = bf16_bits_to_f32(u4_elem(klo, 2 * u2 + u));
-          const float kxh = bf16_bits_to_f32(u4_elem(khi, 2 * u2 + u));
-          const float kl = bf16_bits_to_f32(f32_to_bf16_bits(kxl * c0.x - kxh * c0.y));
-          const float kh = bf16_bits_to_f32(f32_to_bf16_bits(kxh * c0.x + kxl * c0.y));
-          const float ql = u ? bf16_hi(wl[u2]) : bf16_lo(wl[u2]);
-          const float qh = u ? bf16_hi(wh[u2]) : bf16_lo(wh[u2]);
-          part = fmaf(ql, kl, part);
-          part = fmaf(qh, kh, part);
-        }
-      }
+    if (it != tid) {
+      const uint16_t* src = p.q + (node_row * p.Hq + hq) * kD + 8 * c;
+      q_lo = *reinterpret_cast<const uint4*>(src);
+      q_hi = *reinterpret_cast<const uint4*>(src + 64);
     }
-    part += __shfl_xor(part, 1);
-    part += __shfl_xor(part, 2);
-    part += __shfl_xor(part, 4);
-    // B operand of lane (row % 32) + 32 h, k-step kk holds dims 16 kk + 8 h + 0..7
+    uint4 lo = make_uint4(0, 0, 0, 0), hi = lo;
+    if (live) rotate8(q_lo, q_hi, cs_node, c, p.scale_log2, lo, hi);
     const size_t tile = (static_cast<size_t>(b) * p.Hkv + g) * row_tiles + (row >> 5);
-    const int m = row & 31;
-    p.qprep[(tile * 8 + (c >> 1)) * 64 + m + 32 * (c & 1)] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
-    p.qprep[(tile * 8 + 4 + (c >> 1)) * 64 + m + 32 * (c & 1)] = make_uint4(wh[0], wh[1], wh[2], wh[3]);
-    if (c == 0) p.rref[(static_cast<size_t>(b) * p.Hkv + g) * p.rows_pad + row] = part;
+    const int lane = (row & 31) + 32 * (c & 1);
+    p.qprep[(tile * 8 + (c >> 1)) * 64 + lane] = lo;
+    p.qprep[(tile * 8 + 4 + (c >> 1)) * 64 + lane] = hi;
   }
   if (!live) return;
 
   // Tree keys, rotated at P + depth, and raw values go to cache slot P + i.
   const int slot = P + i;
-  for (int it = tid; it < p.Hkv * 8; it += 256) {
+  for (int it = tid; it < nk; it += 256) {
     const int g = it >> 3, c = it & 7;
-    const uint16_t* krow = p.k_new + (node_row * p.Hkv + g) * kD;
-    const uint4 lo = *reinterpret_cast<const uint4*>(krow + 8 * c);
-    const uint4 hi = *reinterpret_cast<const uint4*>(krow + 64 + 8 * c);
-    uint32_t wl[4], wh[4];
-#pragma unroll
-    for (int u2 = 0; u2 < 4; ++u2) {
-      float rl[2], rh[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const float2 cn = cs_node[8 * c + 2 * u2 + u];
-        const float xl = bf16_bits_to_f32(u4_elem(lo, 2 * u2 + u));
-        const float xh = bf16_bits_to_f32(u4_elem(hi, 2 * u2 + u));
-        rl[u] = xl * cn.x - xh * cn.y;
-        rh[u] = xh * cn.x + xl * cn.y;
-      }
-      wl[u2] = pack_bf16(rl[0], rl[1]);
-      wh[u2] = pack_bf16(rh[0], rh[1]);
+    if (it != tid) {
+      const uint16_t* src = p.k_new + (node_row * p.Hkv + g) * kD + 8 * c;
+      k_lo = *reinterpret_cast<const uint4*>(src);
+      k_hi = *reinterpret_cast<const uint4*>(src + 64);
     }
+    uint4 lo, hi;
+    rotate8(k_lo, k_hi, cs_node, c, 1.0f, lo, hi);
     uint16_t* kdst = p.k_cache + ((static_cast<size_t>(b) * p.Hkv + g) * p.cap + slot) * kD;
-    *reinterpret_cast<uint4*>(kdst + 8 * c) = make_uint4(wl[0], wl[1], wl[2], wl[3]);
-    *reinterpret_cast<uint4*>(kdst + 64 + 8 * c) = make_uint4(wh[0], wh[1], wh[2], wh[3]);
+    *reinterpret_cast<uint4*>(kdst + 8 * c) = lo;
+    *reinterpret_cast<uint4*>(kdst + 64 + 8 * c) = hi;
   }
-  for (int it = tid; it < p.Hkv * 16; it += 256) {
+  for (int it = tid; it < nv; it += 256) {
     const int g = it >> 4, c = it & 15;
-    const uint4 v = *reinterpret_cast<const uint4*>(p.v_new + (node_row * p.Hkv + g) * kD + 8 * c);
+    if (it != tid) v_raw = *reinterpret_cast<const uint4*>(p.v_new + (node_row * p.Hkv + g) * kD + 8 * c);
     uint16_t* vh = p.v_cache + (static_cast<size_t>(b) * p.Hkv + g) * p.cap * kD;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) vh[v_cache_off(slot, 8 * c + u)] = u4_elem(v, u);
+    for (int u = 0; u < 8; ++u) vh[v_cache_off(slot, 8 * c + u)] = u4_elem(v_raw, u);
   }
 }
 
@@ -328,8 +317,7 @@ __global__ __launch_bounds__(256) void prep_bf16_kernel(BfParams p) {
 // Running softmax state of one 32-row query tile.
 struct RowState {
   f32x16 o[4];      // O^T accumulator: d = 32 dt + 8 (e>>2) + 4 h + (e&3)
-  f32x16 negr;      // -r in every element: the score MFMA's starting accumulator
-  float r;          // reference score (log2 units): scores are taken relative to it
+  float r;          // reference score (log2 units): p = exp2(s - r)
   float l;          // this lane's share of the row sum
 };
 
@@ -339,73 +327,109 @@ __device__ __forceinline__ bool key_visible(int rel, uint64_t anc) {
   return rel < 0 || (rel < 64 && ((anc >> rel) & 1ull) != 0ull);
 }
 
-// Softmax of one 32-key score block of one query tile. x holds the scores
-// minus the row's reference r (fixed for the pass): no max, no branch.
-// Returns the probabilities packed as two B operands (keys 16 half + 8 h +
-// 0..7). rel0 = (first key of the tile) - P for masked tiles.
-template <bool MASKED>
-__device__ __forceinline__ void block_softmax(RowState& st, f32x16& x, bf16x8 (&pf)[2], int sub, int h, int rel0,
-                                              uint64_t anc) {
-  if (MASKED) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int key = 32 * sub + 16 * (e >> 3) + 8 * h + (e & 7);
-      if (!key_visible(rel0 + key, anc)) x[e] = -INFINITY;
-    }
-  }
-  float pe[16];
-#pragma unroll
-  for (int e = 0; e < 16; ++e) pe[e] = __builtin_amdgcn_exp2f(x[e]);
-  uint32_t w[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) w[j] = pack_bf16(pe[2 * j], pe[2 * j + 1]);
-  const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    st.l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[j]), ones, st.l, false);
-  pf[0] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
-  pf[1] = __builtin_bit_cast(bf16x8, make_uint4(w[4], w[5], w[6], w[7]));
+// Score MFMAs with the accumulator in vector registers. The accumulation
+// registers hold the output (128 per wavefront), so scores that the vector
+// ALU must read would otherwise be shuttled between the two register files;
+// issuing these from assembly pins the vector-register form. The compiler
+// does not see them as MFMAs, so hazard_wait() must separate the last one
+// writing a score block from the first vector-ALU read of it.
+__device__ __forceinline__ f32x16 mfma_s_first(const bf16x8& a, const bf16x8& b) {
+  f32x16 d;
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
+               : "=&v"(d)
+               : "v"(__builtin_bit_cast(u32x4, a)), "v"(__builtin_bit_cast(u32x4, b)));
+  return d;
+}
+__device__ __forceinline__ void mfma_s_acc(f32x16& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+               : "+v"(d)
+               : "v"(__builtin_bit_cast(u32x4, a)), "v"(__builtin_bit_cast(u32x4, b)));
+}
+// 32 wait states: more than the MFMA-write -> VALU-read distance required
+// for the longest (16-pass) matrix instruction. The score blocks pass through
+// the statement, so no read of them can be scheduled above it.
+template <int QT>
+__device__ __forceinline__ void hazard_wait(f32x16 (&x)[QT]) {
+  if constexpr (QT == 1)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x[0]));
+  else
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x[0]), "+v"(x[1]));
 }
 
-// One staged 64-key tile times the QT query tiles of a wavefront, in two
-// 32-key halves. Each K and V fragment read from LDS feeds QT MFMAs.
-template <int QT, bool MASKED>
+// Probabilities of elements 2c, 2c+1 of a 32-key score block (masked to 0
+// where invisible): exp2 of the score (minus the row's reference r on the
+// fallback pass; the fast pass takes r = 0), packed to bf16, and added to the
+// lane's row sum exactly as the PV product will weight them.
+template <bool MASKED, bool SHIFT>
+__device__ __forceinline__ uint32_t prob_pair(RowState& st, const f32x16& x, int c, int sub, int h, int rel0,
+                                              uint64_t anc) {
+  float a = SHIFT ? x[2 * c] - st.r : x[2 * c], b = SHIFT ? x[2 * c + 1] - st.r : x[2 * c + 1];
+  if (MASKED) {
+    const int key = 32 * sub + 16 * ((2 * c) >> 3) + 8 * h + ((2 * c) & 7);
+    if (!key_visible(rel0 + key, anc)) a = -INFINITY;
+    if (!key_visible(rel0 + key + 1, anc)) b = -INFINITY;
+  }
+  const uint32_t w = pack_bf16(__builtin_amdgcn_exp2f(a), __builtin_amdgcn_exp2f(b));
+  const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
+  st.l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, st.l, false);
+  return w;
+}
+
+// One staged 64-key tile times the QT query tiles of a wavefront, as 32
+// steps of QT MFMAs each, software-pipelined so that the matrix cores always
+// have work while the vector ALU computes probabilities:
+//   steps  0- 7  S(half 0)
+//   steps  8-15  S(half 1)   + softmax of half 0, two elements per step
+//   steps 16-23  PV(half 0)  + softmax of half 1
+//   steps 24-31  PV(half 1)
+// Step i consumes LDS fragment i (K rows, then V rows) and issues the read
+// of fragment i + kLook, so few fragments are live at once. Each fragment
+// feeds QT MFMAs. sched_barrier pins the order (the scheduler would
+// otherwise group like instructions and hoist every read).
+constexpr int kLook = 4;
+template <int QT, bool MASKED, bool SHIFT>
 __device__ __forceinline__ void tile_product(RowState (&st)[QT], const uint16_t* __restrict__ ks,
                                              const uint16_t* __restrict__ vs, const bf16x8 (&qf)[QT][8],
                                              const int (&k_addr)[8], const int (&v_addr)[4], int h, int rel0,
                                              const uint64_t (&anc)[QT]) {
+  auto frag_ptr = [&](int i) -> const bf16x8* {
+    if (i < 16) return reinterpret_cast<const bf16x8*>(ks + k_addr[i & 7] + (i >> 3) * 32 * kD);
+    const int j = (i - 16) & 7, sub = (i - 16) >> 3;
+    return reinterpret_cast<const bf16x8*>(vs + v_addr[2 * sub + (j & 1)] + (j >> 1) * 32 * kKT);
+  };
+  bf16x8 fr[32];
   f32x16 x[2][QT];
+  uint32_t w[2][QT][8];
 #pragma unroll
-  for (int sub = 0; sub < 2; ++sub) {
-    bf16x8 ka[8];
+  for (int i = 0; i < kLook; ++i) fr[i] = *frag_ptr(i);
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) ka[kk] = *reinterpret_cast<const bf16x8*>(ks + k_addr[kk] + sub * 32 * kD);
+  for (int i = 0; i < 32; ++i) {
+    if (i + kLook < 32) fr[i + kLook] = *frag_ptr(i + kLook);
+    if (i < 16) {
+      const int sub = i >> 3, kk = i & 7;
 #pragma unroll
-    for (int t = 0; t < QT; ++t) {
-      x[sub][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qf[t][0], st[t].negr, 0, 0, 0);
+      for (int t = 0; t < QT; ++t) {
+        if (kk == 0)
+          x[sub][t] = mfma_s_first(fr[i], qf[t][kk]);
+        else
+          mfma_s_acc(x[sub][t], fr[i], qf[t][kk]);
+      }
+    } else {
+      const int sub = (i - 16) >> 3, j = (i - 16) & 7, dt = j >> 1, half = j & 1;
 #pragma unroll
-      for (int kk = 1; kk < 8; ++kk)
-        x[sub][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], qf[t][kk], x[sub][t], 0, 0, 0);
+      for (int t = 0; t < QT; ++t) {
+        const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(w[sub][t][4 * half], w[sub][t][4 * half + 1],
+                                                               w[sub][t][4 * half + 2], w[sub][t][4 * half + 3]));
+        st[t].o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i], pf, st[t].o[dt], 0, 0, 0);
+      }
     }
-  }
+    if (i >= 8 && i < 24) {
+      const int sub = (i - 8) >> 3, c = (i - 8) & 7;
+      if (c == 0) hazard_wait<QT>(x[sub]);
 #pragma unroll
-  for (int sub = 0; sub < 2; ++sub) {
-    bf16x8 va[8];
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int half = 0; half < 2; ++half)
-        va[2 * dt + half] = *reinterpret_cast<const bf16x8*>(vs + v_addr[2 * sub + half] + dt * 32 * kKT);
-    bf16x8 pf[QT][2];
-#pragma unroll
-    for (int t = 0; t < QT; ++t) block_softmax<MASKED>(st[t], x[sub][t], pf[t], sub, h, rel0, anc[t]);
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int half = 0; half < 2; ++half)
-#pragma unroll
-        for (int t = 0; t < QT; ++t)
-          st[t].o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[2 * dt + half], pf[t][half], st[t].o[dt], 0, 0, 0);
+      for (int t = 0; t < QT; ++t) w[sub][t][c] = prob_pair<MASKED, SHIFT>(st[t], x[sub][t], c, sub, h, rel0, anc[t]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -554,7 +578,6 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   int my_row[QT];
   bool row_live[QT];
   uint64_t my_anc[QT];
-  float r_ref[QT];
   bf16x8 qf[QT][8];   // qf[t][kk] = rotated, scaled Q[row][16kk + 8h .. +8]
   const size_t head_rows = (static_cast<size_t>(b) * p.Hkv + g) * p.rows_pad;
 #pragma unroll
@@ -563,7 +586,6 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
     row_live[t] = my_row[t] < rows_live;
     const int node = min(my_row[t] / G, p.n_max - 1);   // padding rows load a valid row
     my_anc[t] = p.anc[static_cast<size_t>(b) * p.n_max + node];
-    r_ref[t] = p.rref[head_rows + my_row[t]];
     const uint4* qsrc = p.qprep + ((head_rows + r0 + 32 * t) / 32) * 8 * 64 + lane;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) qf[t][kk] = __builtin_bit_cast(bf16x8, qsrc[kk * 64]);
@@ -571,7 +593,6 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
     touch(my_anc[t]);
-    touch(r_ref[t]);
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) touch(qf[t][kk]);
   }
@@ -580,29 +601,32 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
     if (t < n_tiles) issue_tile(k_begin + t * kKT, t);
 
   RowState st[QT];
-  auto reset_state = [&]() {
+  auto reset_state = [&](const float (&r)[QT]) {
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) st[t].o[dt] = f32x16{};
-      st[t].r = r_ref[t];
-      st[t].negr = f32x16{} - r_ref[t];
+      st[t].r = r[t];
       st[t].l = 0.0f;
     }
   };
-  reset_state();
+  float r_ref[QT];
+#pragma unroll
+  for (int t = 0; t < QT; ++t) r_ref[t] = 0.0f;
+  reset_state(r_ref);
 
   // One pass over this split's tiles (the first kStages - 1 already in
-  // flight). MAX_ONLY passes only raise mx to the row maxima of the scores.
+  // flight). MODE 0: p = exp2(s) (fast pass); 1: only raise mx to the row
+  // maxima of the scores; 2: p = exp2(s - r) with r = the row max.
   float mx[QT];
   auto run_pass = [&](auto mode_tag) {
-    constexpr bool MAX_ONLY = decltype(mode_tag)::value;
+    constexpr int MODE = decltype(mode_tag)::value;
     auto product = [&](auto masked_tag, const uint16_t* ks_, const uint16_t* vs_, int rel0) {
       constexpr bool M = decltype(masked_tag)::value;
-      if constexpr (MAX_ONLY)
+      if constexpr (MODE == 1)
         tile_max<QT, M>(mx, ks_, qf, k_addr, h, rel0, my_anc);
       else
-        tile_product<QT, M>(st, ks_, vs_, qf, k_addr, v_addr, h, rel0, my_anc);
+        tile_product<QT, M, MODE == 2>(st, ks_, vs_, qf, k_addr, v_addr, h, rel0, my_anc);
     };
     // A ring of kStages LDS stages, kStages - 1 tiles in flight; tile t lives
     // in stage t % kStages. The steady-state loop only sees prefix tiles with
@@ -643,32 +667,37 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
     }
   };
 
-  run_pass(std::false_type{});
+  run_pass(std::integral_constant<int, 0>{});
 
-  // A row whose scores rose far above its root score (p > 2^62) would lose
-  // precision or overflow on that reference: find every row's exact max in a
-  // scores-only pass, then redo the pass with r = max (all p <= 1).
-  int overflow = 0;
+  // The fast pass is exact while a row's probabilities stay inside the
+  // float range; a row whose sum left [2^-60, 2^62] (scores far above 62 or
+  // all below about -60, in log2 units) is redone: a scores-only pass finds
+  // every row's exact max, then the pass is repeated with r = max (all
+  // p <= 1, the largest = 1; exact for any score range).
+  int redo = 0;
 #pragma unroll
-  for (int t = 0; t < QT; ++t) overflow |= row_live[t] && !(row_sum2(st[t].l) <= 0x1p62f);
-  if (__syncthreads_or(overflow)) {
+  for (int t = 0; t < QT; ++t) {
+    const float l = row_sum2(st[t].l);
+    redo |= row_live[t] && !(l <= 0x1p62f && l >= 0x1p-60f);
+  }
+  if (__syncthreads_or(redo)) {
 #pragma unroll
     for (int t = 0; t < QT; ++t) mx[t] = -INFINITY;
 #pragma unroll
     for (int t = 0; t < kStages - 1; ++t)
       if (t < n_tiles) issue_tile(k_begin + t * kKT, t);
-    run_pass(std::true_type{});
+    run_pass(std::integral_constant<int, 1>{});
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
       const float m = row_max2(mx[t]);
-      r_ref[t] = (m == -INFINITY) ? r_ref[t] : m;
+      r_ref[t] = (m == -INFINITY) ? 0.0f : m;
     }
-    reset_state();
+    reset_state(r_ref);
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < kStages - 1; ++t)
       if (t < n_tiles) issue_tile(k_begin + t * kKT, t);
-    run_pass(std::false_type{});
+    run_pass(std::integral_constant<int, 2>{});
   }
 
   // ---- epilogue
@@ -774,10 +803,10 @@ const Tune& tune() {
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// Workspace layout: qprep | rref | part_ml | part_o (the last two only with
-// several splits).
+// Workspace layout: qprep | part_ml | part_o (the last two only with several
+// splits).
 struct WsLayout {
-  size_t qprep, rref, part_ml, part_o, total;
+  size_t qprep, part_ml, part_o, total;
 };
 WsLayout ws_layout(const tv_attn_args* a, const AttnPlan& pl) {
   WsLayout w;
@@ -785,8 +814,7 @@ WsLayout ws_layout(const tv_attn_args* a, const AttnPlan& pl) {
   const size_t wg_rows = static_cast<size_t>(pl.waves) * 32 * pl.qt;
   const size_t wgs = heads * pl.row_blocks * pl.splits;
   w.qprep = 0;
-  w.rref = align_up(heads * pl.rows_pad * kD * 2);
-  w.part_ml = w.rref + align_up(heads * pl.rows_pad * sizeof(float));
+  w.part_ml = align_up(heads * pl.rows_pad * kD * 2);
   w.part_o = w.part_ml + (pl.splits > 1 ? align_up(wgs * wg_rows * 2 * sizeof(float2)) : 0);
   w.total = w.part_o + (pl.splits > 1 ? wgs * wg_rows * 32 * sizeof(float4) : 0);
   return w;
@@ -852,7 +880,6 @@ hipError_t launch_attention_bf16(const tv_attn_args* a, const AttnPlan& pl, hipS
   const WsLayout w = ws_layout(a, pl);
   char* ws = static_cast<char*>(a->workspace);
   p.qprep = reinterpret_cast<uint4*>(ws + w.qprep);
-  p.rref = reinterpret_cast<float*>(ws + w.rref);
   p.part_ml = pl.splits > 1 ? reinterpret_cast<float2*>(ws + w.part_ml) : nullptr;
   p.part_o = pl.splits > 1 ? reinterpret_cast<float4*>(ws + w.part_o) : nullptr;
 
