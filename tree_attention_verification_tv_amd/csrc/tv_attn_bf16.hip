@@ -9,7 +9,8 @@
 //
 // How (this file's design, not the pages'): three kernels on one stream.
 //
-//   prep   one workgroup per (node, sequence). Rotates the node's queries at
+//   prep   one workgroup per (node, sequence), plus one per (KV head,
+//          sequence) for the value appends. Rotates the node's queries at
 //          P + depth, scales them by softmax_scale * log2(e), rounds them to
 //          bf16 and stores them in the exact register order of the score
 //          MFMA's B operand; rotates the node's keys and appends them, with
@@ -29,9 +30,11 @@
 //          not see an LDS write it cannot tell apart from the fragment reads,
 //          and does not drain every copy in flight before each tile; the
 //          kernel waits for exactly the tile it needs (s_waitcnt vmcnt) and a
-//          barrier. Vector memory operations complete in order, so the few
-//          operand loads (queries, reference scores, ancestor masks) are
-//          issued right after the first tile and consumed before the others.
+//          barrier. The workgroup's queries (64 KB at most) are staged the
+//          same way, through the last ring stage and 32 KB beyond it, so that
+//          every copy is in flight at once: vector memory operations complete
+//          in order, and a register load issued behind the tiles would wait
+//          for all of them.
 //
 //          Scores are computed transposed, S^T = K Q^T, with
 //          v_mfma_f32_32x32x16_bf16: a lane then holds 16 keys of ONE query
@@ -88,6 +91,7 @@ constexpr int kKT = 64;                 // keys per LDS stage (= V cache block)
 constexpr int kStageElems = kKT * kD;   // bf16 elements of one K (or V) stage
 constexpr int kStages = 4;              // LDS ring of key tiles (3 in flight)
 constexpr int kMaxSplits = 8;           // key splits per row block
+constexpr int kQExtra = 16384;          // LDS elements beyond the ring (32 KB)
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -205,7 +209,8 @@ __device__ __forceinline__ SeqState seq_state(const BfParams& p, int b) {
 }
 
 // ---------------------------------------------------------------------------
-// prep: grid (n_max, B), 256 threads
+// prep: grid (n_max + Hkv, B), 256 threads: node blocks (queries, keys),
+// then one value-append block per KV head
 // ---------------------------------------------------------------------------
 
 // Rotates 8 rotate-half pairs (dims 8c..8c+7 with 64+8c..64+8c+7) by the
@@ -234,12 +239,32 @@ __device__ __forceinline__ void rotate8(const uint4& lo, const uint4& hi, const 
 __global__ __launch_bounds__(256) void prep_bf16_kernel(BfParams p) {
   __shared__ float2 cs_node[kD / 2];   // angle (P + depth) f_j
   const int i = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  if (i >= p.n_max) {
+    // Value append of KV head g = i - n_max: lane = node, so one store
+    // instruction writes 64 consecutive slots of one head dim of the blocked
+    // cache; wavefront w covers dims 8c..8c+7 for c = w, w + 4, ...
+    const int g = i - p.n_max, lane = tid & 63, w = tid >> 6;
+    const int node = min(lane, p.n_max - 1);
+    uint4 v[kD / 8 / 4];
+#pragma unroll
+    for (int k = 0; k < kD / 8 / 4; ++k)
+      v[k] = *reinterpret_cast<const uint4*>(p.v_new + ((static_cast<size_t>(b) * p.n_max + node) * p.Hkv + g) * kD +
+                                             8 * (w + 4 * k));
+    const SeqState sq = seq_state(p, b);
+    if (sq.skip || lane >= sq.n) return;
+    uint16_t* vh = p.v_cache + (static_cast<size_t>(b) * p.Hkv + g) * p.cap * kD;
+#pragma unroll
+    for (int k = 0; k < kD / 8 / 4; ++k)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) vh[v_cache_off(sq.P + lane, 8 * (w + 4 * k) + u)] = u4_elem(v[k], u);
+    return;
+  }
   const size_t node_row = static_cast<size_t>(b) * p.n_max + i;
-  const int nq = p.Hq * 8, nk = p.Hkv * 8, nv = p.Hkv * 16;
+  const int nq = p.Hq * 8, nk = p.Hkv * 8;
 
   // Every load of this thread's first items goes out before anything waits:
   // their addresses do not depend on the sequence's state.
-  uint4 q_lo = make_uint4(0, 0, 0, 0), q_hi = q_lo, k_lo = q_lo, k_hi = q_lo, v_raw = q_lo;
+  uint4 q_lo = make_uint4(0, 0, 0, 0), q_hi = q_lo, k_lo = q_lo, k_hi = q_lo;
   if (tid < nq) {
     const uint16_t* src = p.q + (node_row * p.Hq + (tid >> 3)) * kD + 8 * (tid & 7);
     q_lo = *reinterpret_cast<const uint4*>(src);
@@ -250,7 +275,6 @@ __global__ __launch_bounds__(256) void prep_bf16_kernel(BfParams p) {
     k_lo = *reinterpret_cast<const uint4*>(src);
     k_hi = *reinterpret_cast<const uint4*>(src + 64);
   }
-  if (tid < nv) v_raw = *reinterpret_cast<const uint4*>(p.v_new + (node_row * p.Hkv + (tid >> 4)) * kD + 8 * (tid & 15));
   const double freq = (tid < kD / 2) ? p.inv_freq[tid] : 0.0;
   const int dep_raw = p.depth[node_row];
 
@@ -286,7 +310,7 @@ __global__ __launch_bounds__(256) void prep_bf16_kernel(BfParams p) {
   }
   if (!live) return;
 
-  // Tree keys, rotated at P + depth, and raw values go to cache slot P + i.
+  // Tree keys, rotated at P + depth, go to cache slot P + i.
   const int slot = P + i;
   for (int it = tid; it < nk; it += 256) {
     const int g = it >> 3, c = it & 7;
@@ -301,17 +325,10 @@ __global__ __launch_bounds__(256) void prep_bf16_kernel(BfParams p) {
     *reinterpret_cast<uint4*>(kdst + 8 * c) = lo;
     *reinterpret_cast<uint4*>(kdst + 64 + 8 * c) = hi;
   }
-  for (int it = tid; it < nv; it += 256) {
-    const int g = it >> 4, c = it & 15;
-    if (it != tid) v_raw = *reinterpret_cast<const uint4*>(p.v_new + (node_row * p.Hkv + g) * kD + 8 * c);
-    uint16_t* vh = p.v_cache + (static_cast<size_t>(b) * p.Hkv + g) * p.cap * kD;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) vh[v_cache_off(slot, 8 * c + u)] = u4_elem(v_raw, u);
-  }
 }
 
 // ---------------------------------------------------------------------------
-// main: grid (splits * row_blocks, Hkv, B), WAVES * 64 threads
+// main: grid (splits * row_blocks * Hkv * B), WAVES * 64 threads
 // ---------------------------------------------------------------------------
 
 // Running softmax state of one 32-row query tile.
@@ -405,31 +422,29 @@ __device__ __forceinline__ void tile_product(RowState (&st)[QT], const uint16_t*
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
     if (i + kLook < 32) fr[i + kLook] = *frag_ptr(i + kLook);
-    if (i < 16) {
-      const int sub = i >> 3, kk = i & 7;
+    const bool soft = i >= 8 && i < 24;
+    const int ssub = (i - 8) >> 3, c = (i - 8) & 7;
+    if (soft && c == 0) hazard_wait<QT>(x[ssub]);
+    // An in-order wavefront cannot issue past an MFMA that waits for the
+    // matrix pipe, so each MFMA is followed by its own share of vector work
+    // rather than by the next MFMA.
 #pragma unroll
-      for (int t = 0; t < QT; ++t) {
+    for (int t = 0; t < QT; ++t) {
+      if (i < 16) {
+        const int sub = i >> 3, kk = i & 7;
         if (kk == 0)
           x[sub][t] = mfma_s_first(fr[i], qf[t][kk]);
         else
           mfma_s_acc(x[sub][t], fr[i], qf[t][kk]);
-      }
-    } else {
-      const int sub = (i - 16) >> 3, j = (i - 16) & 7, dt = j >> 1, half = j & 1;
-#pragma unroll
-      for (int t = 0; t < QT; ++t) {
+      } else {
+        const int sub = (i - 16) >> 3, j = (i - 16) & 7, dt = j >> 1, half = j & 1;
         const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(w[sub][t][4 * half], w[sub][t][4 * half + 1],
                                                                w[sub][t][4 * half + 2], w[sub][t][4 * half + 3]));
         st[t].o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i], pf, st[t].o[dt], 0, 0, 0);
       }
+      if (soft) w[ssub][t][c] = prob_pair<MASKED, SHIFT>(st[t], x[ssub][t], c, ssub, h, rel0, anc[t]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (i >= 8 && i < 24) {
-      const int sub = (i - 8) >> 3, c = (i - 8) & 7;
-      if (c == 0) hazard_wait<QT>(x[sub]);
-#pragma unroll
-      for (int t = 0; t < QT; ++t) w[sub][t][c] = prob_pair<MASKED, SHIFT>(st[t], x[sub][t], c, sub, h, rel0, anc[t]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -489,24 +504,59 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   constexpr int NT = WAVES * 64;
   constexpr int ROWS = WAVES * 32 * QT;      // query rows of the workgroup
   constexpr int CPT = (kKT * kD / 8) / NT;   // 16-byte chunks per thread per K (or V) stage
-  static_assert(2 * CPT * (kStages - 1) <= 63, "vmcnt range");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kStages * kStageElems];  // (K, V) x stages
+  constexpr int QCPT = ROWS * kD / 8 / NT;   // 16-byte chunks per thread of the workgroup's queries
+  static_assert(QCPT + 2 * CPT * (kStages - 1) <= 63, "vmcnt range");
+  static_assert(ROWS * kD <= 2 * kStageElems + kQExtra, "query block must fit the last stage plus the extra");
+  // (K, V) x stages, then kQExtra elements; the queries are staged through
+  // the last stage and the extra before the first tile lands there
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kStages * kStageElems + kQExtra];
 
-  const int s = blockIdx.x % p.splits;
-  const int rb = blockIdx.x / p.splits;
-  const int g = blockIdx.y, b = blockIdx.z;
+  // Workgroups are handed to the eight XCDs round-robin by index; when the
+  // row blocks come in multiples of eight, the splits of one row block get
+  // indices eight apart, so they share an L2 (their query block is fetched
+  // once) and start together. (A placement hint only: any mapping is
+  // correct.)
+  const int n_groups = gridDim.x / p.splits;
+  int s, gi;
+  if (n_groups % 8 == 0) {
+    const int L = blockIdx.x, k = L >> 3;
+    s = k % p.splits;
+    gi = (k / p.splits) * 8 + (L & 7);
+  } else {
+    s = blockIdx.x % p.splits;
+    gi = blockIdx.x / p.splits;
+  }
+  const int rb = gi % p.row_blocks;
+  const int g = (gi / p.row_blocks) % p.Hkv, b = gi / (p.row_blocks * p.Hkv);
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = p.G;
 
+  const int rb0 = rb * ROWS;
+  const int r0 = rb0 + wave * 32 * QT;       // first row of this wavefront
+  const uint32_t lds_base = lds_addr(smem);
+  const uint32_t lds_q = lds_base + 2u * kStageElems * 2u * (kStages - 1);   // = last stage
+  const size_t head_rows = (static_cast<size_t>(b) * p.Hkv + g) * p.rows_pad;
+
+  // The sequence's state is read first (scalar loads, which may not follow
+  // the copies: those are opaque memory writes to the compiler).
   const SeqState sq = seq_state(p, b);
+
+  // ---- 1. every copy goes out before anything waits: the workgroup's
+  // query block (contiguous in prep's operand order) into LDS, then the
+  // first key tiles.
+  {
+    const uint16_t* qblk = reinterpret_cast<const uint16_t*>(p.qprep) + (head_rows + rb0) * kD;
+#pragma unroll
+    for (int j = 0; j < QCPT; ++j)
+      dma16(qblk, static_cast<uint32_t>(j * NT + tid) * 16u, lds_q + static_cast<uint32_t>(j * NT + wave * 64) * 16u);
+  }
   const int n = sq.n, P = sq.P;
   const int rows_live = sq.skip ? 0 : G * n;
   const int rows_all = G * p.n_max;
-  const int rb0 = rb * ROWS;
-  const int r0 = rb0 + wave * 32 * QT;       // first row of this wavefront
 
   if (rb0 >= rows_live) {
+    wait_vm<0>();   // no copy into this workgroup's LDS may outlive it
     // nothing live in this row block; with splits the merge writes the zeros
     if (p.splits == 1) {
       for (int r = rb0 + tid / 16; r < min(rb0 + ROWS, rows_all); r += NT / 16) {
@@ -530,7 +580,6 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   // stage buf: K at smem + 2 buf * kStageElems, V right after it
   auto Ks = [&](int buf) { return smem + 2 * buf * kStageElems; };
   auto Vs = [&](int buf) { return smem + (2 * buf + 1) * kStageElems; };
-  const uint32_t lds_base = lds_addr(smem);
 
   const size_t head_off = (static_cast<size_t>(b) * p.Hkv + g) * p.cap * kD;
   const uint16_t* kc = p.k_cache + head_off;
@@ -572,33 +621,40 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
     }
   };
 
-  // ---- 1. first tile, then the operands (consumed before the next tiles)
-  if (n_tiles > 0) issue_tile(k_begin, 0);
+#pragma unroll
+  for (int t = 0; t < kStages - 1; ++t)
+    if (t < n_tiles) issue_tile(k_begin + t * kKT, t);
 
+  // ---- 2. the queries have landed once only the tile copies are
+  // outstanding: read them into the B operands
+  {
+    const int issued = min(n_tiles, kStages - 1);
+    static_assert(kStages == 4, "waits below assume three tiles in flight");
+    if (issued >= 3) wait_vm<2 * CPT * 3>();
+    else if (issued == 2) wait_vm<2 * CPT * 2>();
+    else if (issued == 1) wait_vm<2 * CPT>();
+    else wait_vm<0>();
+  }
+  __syncthreads();
   int my_row[QT];
   bool row_live[QT];
-  uint64_t my_anc[QT];
-  bf16x8 qf[QT][8];   // qf[t][kk] = rotated, scaled Q[row][16kk + 8h .. +8]
-  const size_t head_rows = (static_cast<size_t>(b) * p.Hkv + g) * p.rows_pad;
+  uint64_t my_anc[QT];   // loaded before the first masked tile
+  bf16x8 qf[QT][8];      // qf[t][kk] = rotated, scaled Q[row][16kk + 8h .. +8]
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
     my_row[t] = r0 + 32 * t + (lane & 31);
     row_live[t] = my_row[t] < rows_live;
-    const int node = min(my_row[t] / G, p.n_max - 1);   // padding rows load a valid row
-    my_anc[t] = p.anc[static_cast<size_t>(b) * p.n_max + node];
-    const uint4* qsrc = p.qprep + ((head_rows + r0 + 32 * t) / 32) * 8 * 64 + lane;
+    my_anc[t] = 0;
+    const int k = wave * QT + t;   // 32-row tile of the workgroup
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) qf[t][kk] = __builtin_bit_cast(bf16x8, qsrc[kk * 64]);
+    for (int kk = 0; kk < 8; ++kk)
+      qf[t][kk] = *reinterpret_cast<const bf16x8*>(smem + 2 * kStageElems * (kStages - 1) + ((k * 8 + kk) * 64 + lane) * 8);
   }
+  auto load_anc = [&]() {
 #pragma unroll
-  for (int t = 0; t < QT; ++t) {
-    touch(my_anc[t]);
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) touch(qf[t][kk]);
-  }
-#pragma unroll
-  for (int t = 1; t < kStages - 1; ++t)
-    if (t < n_tiles) issue_tile(k_begin + t * kKT, t);
+    for (int t = 0; t < QT; ++t)
+      my_anc[t] = p.anc[static_cast<size_t>(b) * p.n_max + min(my_row[t] / G, p.n_max - 1)];
+  };
 
   RowState st[QT];
   auto reset_state = [&](const float (&r)[QT]) {
@@ -642,6 +698,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
       issue_tile(k_begin + (t + kStages - 1) * kKT, (t + kStages - 1) % kStages);
       product(std::false_type{}, Ks(cur), Vs(cur), 0);
     }
+    if (k_begin + n_tiles * kKT > P) load_anc();   // masked tiles ahead
     for (; t < n_tiles; ++t) {
       const int cur = t % kStages;
       const int later = n_tiles - 1 - t;
@@ -680,7 +737,15 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
     const float l = row_sum2(st[t].l);
     redo |= row_live[t] && !(l <= 0x1p62f && l >= 0x1p-60f);
   }
-  if (__syncthreads_or(redo)) {
+  // workgroup-wide OR through the (now idle) ring
+  __syncthreads();
+  if (tid == 0) reinterpret_cast<int*>(smem)[0] = 0;
+  __syncthreads();
+  if (redo) reinterpret_cast<int*>(smem)[0] = 1;
+  __syncthreads();
+  const bool any_redo = reinterpret_cast<const int*>(smem)[0] != 0;
+  __syncthreads();
+  if (any_redo) {
 #pragma unroll
     for (int t = 0; t < QT; ++t) mx[t] = -INFINITY;
 #pragma unroll
@@ -883,10 +948,10 @@ hipError_t launch_attention_bf16(const tv_attn_args* a, const AttnPlan& pl, hipS
   p.part_ml = pl.splits > 1 ? reinterpret_cast<float2*>(ws + w.part_ml) : nullptr;
   p.part_o = pl.splits > 1 ? reinterpret_cast<float4*>(ws + w.part_o) : nullptr;
 
-  hipLaunchKernelGGL(prep_bf16_kernel, dim3(a->n_max, a->B), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(prep_bf16_kernel, dim3(a->n_max + a->Hkv, a->B), dim3(256), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 grid(pl.splits * pl.row_blocks, a->Hkv, a->B);
+  dim3 grid(pl.splits * pl.row_blocks * a->Hkv * a->B);
   const int wg_rows = pl.waves * 32 * pl.qt;
   dim3 mgrid(pl.row_blocks * wg_rows / 8, a->Hkv, a->B);
   const int key = pl.waves * 10 + pl.qt;
