@@ -13,8 +13,9 @@ steps do identical work.
 
 Prints one JSON line. `value` = tree nodes verified per second over the timed
 steps (wall clock between two device synchronisations). `roofline` reports the
-attention kernel: algorithmic HBM bytes per launch divided by its mean
-duration, measured with HIP events on the launch stream.
+attention call (its three kernels): algorithmic HBM bytes per call divided by
+its mean duration, measured with HIP events on the launch stream; `traffic` is
+the measured HBM bytes per call from profiles/ when it matches the source.
 """
 from __future__ import annotations
 
@@ -60,10 +61,11 @@ def algorithmic_bytes(w) -> dict:
                 tree_kv_append=tree_kv_append, out=out, total=total)
 
 
-def load_traffic(cfg: int):
-    """Measured HBM bytes per attention launch (rocprofv3 FETCH_SIZE +
-    WRITE_SIZE), valid only for the kernel source they were taken on."""
-    path = os.path.join(ROOT, "profiles", f"traffic_attention_cfg{cfg}.json")
+def load_traffic(workload: str):
+    """Measured HBM bytes per tv_tree_attention call (rocprofv3 FETCH_SIZE +
+    WRITE_SIZE of its kernels, scaled by a plain copy), valid only for the
+    kernel source they were taken on."""
+    path = os.path.join(ROOT, "profiles", f"traffic_attention_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
@@ -91,10 +93,17 @@ def cpu_baseline(w, budget_s: float = 12.0) -> dict:
             if time.perf_counter() - t0 >= budget_s:
                 break
     dt = time.perf_counter() - t0
+    cpu = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu = next(l.split(":", 1)[1].strip() for l in fh if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     return {"value": nodes / dt, "unit": "tree-nodes/s", "cores": 1, "kind": "oracle",
             "sample": f"{done} of {w.B} sequences ({nodes} nodes), full verification step "
                       f"(tree set-up, attention over prefix {int(np.mean(w.prefix_len[:done]))} "
-                      f"+ ancestors, accept, commit), numpy float64, 1 BLAS thread, {dt:.1f} s"}
+                      f"+ ancestors, accept, commit), numpy float64, 1 BLAS thread of "
+                      f"{len(os.sched_getaffinity(0))} available ({cpu}), {dt:.1f} s"}
 
 
 def main() -> None:
@@ -187,7 +196,7 @@ def main() -> None:
     attn_mean_s = float(np.mean(attn_ms)) * 1e-3
     ab = algorithmic_bytes(w)
     achieved = ab["total"] / attn_mean_s / 1e9
-    traffic = load_traffic(args.config)
+    traffic = load_traffic(w.name)
     mean_accept = float(acc_len.float().mean().item())
 
     rec = {
@@ -209,7 +218,8 @@ def main() -> None:
                    "seed": args.config if args.seed is None else args.seed},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "tv_tree_attention (attn_bf16_kernel + split merge)",
+                     "kernel": "tv_tree_attention call: prep_bf16_kernel + attn_bf16_kernel + "
+                               "merge_bf16_kernel, HIP events around the call on its stream",
                      "algorithmic_bytes_per_launch": ab["total"],
                      "attention_us_mean": attn_mean_s * 1e6,
                      "attention_us_p10": float(np.percentile(attn_ms, 10)) * 1e3,
