@@ -7,34 +7,32 @@
 // P + depth. Siblings and other branches are masked out by the node's
 // ancestor bitmask.
 //
-// How (this file's design, not the pages'): three kernels on one stream.
-//
-//   prep   one workgroup per (node, sequence), plus one per (KV head,
-//          sequence) for the value appends. Rotates the node's queries at
-//          P + depth, scales them by softmax_scale * log2(e), rounds them to
-//          bf16 and stores them in the exact register order of the score
-//          MFMA's B operand; rotates the node's keys and appends them, with
-//          the raw values, to cache slots P + i. It also flags sequences
-//          whose prefix plus tree exceeds the cache.
+// How (this file's design, not the pages'): two kernels on one stream.
 //
 //   main   workgroup = (row block rb, KV split s) of (sequence b, KV head g).
 //          Its query rows are the G query heads of g for every tree node,
 //          node-major (row = node * G + head_in_group); each wavefront owns
 //          QT tiles of 32 rows, so every K or V fragment read from LDS feeds
 //          QT MFMAs. The keys of b are slots [0, P + n) of the cache: the
-//          prefix followed by the tree appended by prep, cut into 64-key
-//          tiles that the splits share out. Tiles are copied straight into
-//          LDS (global_load_lds into a ring of four stages, three tiles in
-//          flight), so the copies cost no registers and no LDS writes.
-//          The copies are issued from inline assembly: the compiler then does
-//          not see an LDS write it cannot tell apart from the fragment reads,
-//          and does not drain every copy in flight before each tile; the
-//          kernel waits for exactly the tile it needs (s_waitcnt vmcnt) and a
-//          barrier. The workgroup's queries (64 KB at most) are staged the
-//          same way, through the last ring stage and 32 KB beyond it, so that
-//          every copy is in flight at once: vector memory operations complete
-//          in order, and a register load issued behind the tiles would wait
-//          for all of them.
+//          prefix, then the tree, cut into 64-key tiles that the splits share
+//          out. Tiles are copied straight into LDS (global_load_lds into a
+//          ring of four stages, three tiles in flight), so the copies cost no
+//          registers and no LDS writes. The copies are issued from inline
+//          assembly: the compiler then does not see an LDS write it cannot
+//          tell apart from the fragment reads, and does not drain every copy
+//          in flight before each tile; the kernel waits for exactly the tile
+//          it needs (s_waitcnt vmcnt) and a barrier.
+//
+//          While the first tiles are in flight, the workgroup builds a table
+//          of RoPE (cos, sin) for the depths 0 .. deepest node in LDS, and
+//          each lane rotates its query rows at P + depth, scales them by
+//          softmax_scale * log2(e) and rounds them to bf16 in the register
+//          order of the score MFMA's B operand. In the one or two tiles that
+//          reach past P, the tree's keys are rotated the same way and written
+//          into the LDS stage with its values, straight from k_new / v_new;
+//          row block 0 also appends them to cache slots P + i. No kernel of
+//          the call reads them back from the cache, so nothing orders the
+//          workgroups.
 //
 //          Scores are computed transposed, S^T = K Q^T, with
 //          v_mfma_f32_32x32x16_bf16: a lane then holds 16 keys of ONE query
@@ -68,9 +66,8 @@
 //          unnormalised output) to the workspace in register order; the merge
 //          combines them in split order (deterministic) and writes the rows.
 //
-// RoPE angles: the host passes theta^(-2d/D) in double precision; prep forms
-// pos * inv_freq in double, reduces it to [-pi, pi] and takes a
-// single-precision sincos.
+// RoPE angles: a table entry forms pos * 2^(-2j/D log2 theta) in double
+// precision, reduces it to [-pi, pi] and takes a single-precision sincos.
 #include <math.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -91,7 +88,7 @@ constexpr int kKT = 64;                 // keys per LDS stage (= V cache block)
 constexpr int kStageElems = kKT * kD;   // bf16 elements of one K (or V) stage
 constexpr int kStages = 4;              // LDS ring of key tiles (3 in flight)
 constexpr int kMaxSplits = 8;           // key splits per row block
-constexpr int kQExtra = 16384;          // LDS elements beyond the ring (32 KB)
+constexpr int kCsElems = 64 * 64 * 4;   // LDS elements (bf16 units) of the RoPE table: 64 depths x 64 (cos, sin)
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -109,14 +106,13 @@ struct BfParams {
   const int32_t* depth;
   int32_t* err;
   uint16_t* out;
-  uint4* qprep;      // [B][Hkv][rows_pad/32][8][64] x 8 bf16: MFMA B operands
   float4* part_o;    // split partials, register order (see the main epilogue)
   float2* part_ml;   // split (reference, row sum) per lane
   int n_max, Hq, Hkv, G, cap;
-  int splits, row_blocks, rows_pad;
-  int rope;          // 0: no rotation
+  int splits, row_blocks;
   float scale_log2;  // softmax scale * log2(e)
-  double inv_freq[kD / 2];
+  int rope;          // 0: no rotation
+  double log2_theta; // log2 of the RoPE base
 };
 
 // Two floats -> packed bf16 pair (hardware round to nearest even).
@@ -160,6 +156,10 @@ __device__ __forceinline__ float2 rope_cs(int pos, double inv_freq) {
   return make_float2(c, s);
 }
 
+// Depths index the RoPE table; out-of-range values are clamped to its rows.
+static_assert(kCsElems == TV_MAX_NODES_DEV * (kD / 2) * 4, "one table row per possible depth");
+__device__ __forceinline__ int clamp_depth(int d) { return min(max(d, 0), TV_MAX_NODES_DEV - 1); }
+
 // max / sum of a value and the value of the lane 32 away (the other half of
 // the same query row), on the vector ALU
 __device__ __forceinline__ float row_max2(float v) {
@@ -183,6 +183,29 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 __device__ __forceinline__ void dma16(const uint16_t* base, uint32_t voff, uint32_t lds) {
   asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds) : "memory");
 }
+// Register loads issued from assembly: the compiler neither counts nor waits
+// for them (it would otherwise wait for every tile copy issued after them, as
+// it does not count those either). The kernel issues them before the tile
+// copies, waits for the copies' count (s_waitcnt vmcnt), and then passes each
+// value through landed(), which re-defines it after that wait, so no use can
+// be scheduled above it.
+__device__ __forceinline__ u32x4 ld_b128(const void* a) {
+  u32x4 v;
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=&v"(v) : "v"(a) : "memory");
+  return v;
+}
+__device__ __forceinline__ uint32_t ld_b32(const void* a) {
+  uint32_t v;
+  asm volatile("global_load_dword %0, %1, off" : "=&v"(v) : "v"(a) : "memory");
+  return v;
+}
+__device__ __forceinline__ uint64_t ld_b64(const void* a) {
+  uint64_t v;
+  asm volatile("global_load_dwordx2 %0, %1, off" : "=&v"(v) : "v"(a) : "memory");
+  return v;
+}
+template <typename T>
+__device__ __forceinline__ void landed(T& v) { asm volatile("" : "+v"(v)); }
 // Waits until at most N vector memory operations of this wavefront are
 // outstanding (N must be a compile-time constant).
 template <int N>
@@ -208,22 +231,18 @@ __device__ __forceinline__ SeqState seq_state(const BfParams& p, int b) {
   return q;
 }
 
-// ---------------------------------------------------------------------------
-// prep: grid (n_max + Hkv, B), 256 threads: node blocks (queries, keys),
-// then one value-append block per KV head
-// ---------------------------------------------------------------------------
-
-// Rotates 8 rotate-half pairs (dims 8c..8c+7 with 64+8c..64+8c+7) by the
-// angles cs[8c..8c+7], scales them and packs them to bf16.
-__device__ __forceinline__ void rotate8(const uint4& lo, const uint4& hi, const float2* cs, int c, float scale,
-                                        uint4& lo_out, uint4& hi_out) {
+// Rotate-half RoPE of 8 dimension pairs: lo[e] and hi[e] are dims d + e and
+// d + 64 + e, cs[e] the (cos, sin) of their angle. Results are multiplied by
+// scale and rounded to bf16.
+__device__ __forceinline__ void rope8(const uint4& lo, const uint4& hi, const float2* cs, float scale,
+                                      uint4& lo_out, uint4& hi_out) {
   uint32_t wl[4], wh[4];
 #pragma unroll
   for (int u2 = 0; u2 < 4; ++u2) {
     float rl[2], rh[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const float2 cn = cs[8 * c + 2 * u2 + u];
+      const float2 cn = cs[2 * u2 + u];
       const float xl = bf16_bits_to_f32(u4_elem(lo, 2 * u2 + u));
       const float xh = bf16_bits_to_f32(u4_elem(hi, 2 * u2 + u));
       rl[u] = (xl * cn.x - xh * cn.y) * scale;
@@ -234,97 +253,6 @@ __device__ __forceinline__ void rotate8(const uint4& lo, const uint4& hi, const 
   }
   lo_out = make_uint4(wl[0], wl[1], wl[2], wl[3]);
   hi_out = make_uint4(wh[0], wh[1], wh[2], wh[3]);
-}
-
-__global__ __launch_bounds__(256) void prep_bf16_kernel(BfParams p) {
-  __shared__ float2 cs_node[kD / 2];   // angle (P + depth) f_j
-  const int i = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  if (i >= p.n_max) {
-    // Value append of KV head g = i - n_max: lane = node, so one store
-    // instruction writes 64 consecutive slots of one head dim of the blocked
-    // cache; wavefront w covers dims 8c..8c+7 for c = w, w + 4, ...
-    const int g = i - p.n_max, lane = tid & 63, w = tid >> 6;
-    const int node = min(lane, p.n_max - 1);
-    uint4 v[kD / 8 / 4];
-#pragma unroll
-    for (int k = 0; k < kD / 8 / 4; ++k)
-      v[k] = *reinterpret_cast<const uint4*>(p.v_new + ((static_cast<size_t>(b) * p.n_max + node) * p.Hkv + g) * kD +
-                                             8 * (w + 4 * k));
-    const SeqState sq = seq_state(p, b);
-    if (sq.skip || lane >= sq.n) return;
-    uint16_t* vh = p.v_cache + (static_cast<size_t>(b) * p.Hkv + g) * p.cap * kD;
-#pragma unroll
-    for (int k = 0; k < kD / 8 / 4; ++k)
-#pragma unroll
-      for (int u = 0; u < 8; ++u) vh[v_cache_off(sq.P + lane, 8 * (w + 4 * k) + u)] = u4_elem(v[k], u);
-    return;
-  }
-  const size_t node_row = static_cast<size_t>(b) * p.n_max + i;
-  const int nq = p.Hq * 8, nk = p.Hkv * 8;
-
-  // Every load of this thread's first items goes out before anything waits:
-  // their addresses do not depend on the sequence's state.
-  uint4 q_lo = make_uint4(0, 0, 0, 0), q_hi = q_lo, k_lo = q_lo, k_hi = q_lo;
-  if (tid < nq) {
-    const uint16_t* src = p.q + (node_row * p.Hq + (tid >> 3)) * kD + 8 * (tid & 7);
-    q_lo = *reinterpret_cast<const uint4*>(src);
-    q_hi = *reinterpret_cast<const uint4*>(src + 64);
-  }
-  if (tid < nk) {
-    const uint16_t* src = p.k_new + (node_row * p.Hkv + (tid >> 3)) * kD + 8 * (tid & 7);
-    k_lo = *reinterpret_cast<const uint4*>(src);
-    k_hi = *reinterpret_cast<const uint4*>(src + 64);
-  }
-  const double freq = (tid < kD / 2) ? p.inv_freq[tid] : 0.0;
-  const int dep_raw = p.depth[node_row];
-
-  const SeqState sq = seq_state(p, b);
-  if (sq.cap_bad && i == 0 && tid == 0) p.err[b] = TV_ERR_CAPACITY;
-  if (sq.skip) return;   // the main and merge kernels zero the rows of b
-  const int P = sq.P;
-  const bool live = i < sq.n;
-  const int dep = live ? min(max(dep_raw, 0), TV_MAX_NODES_DEV - 1) : 0;
-  if (tid < kD / 2) cs_node[tid] = p.rope ? rope_cs(P + dep, freq) : make_float2(1.0f, 0.0f);
-  __syncthreads();
-
-  const int G = p.G;
-  const int row_tiles = p.rows_pad / 32;
-  // Queries: item it = (head it/8, c = it%8) covers dims 8c..8c+7 and
-  // 64+8c..; stored as the B operand of lane (row % 32) + 32 (c % 2) at
-  // k-steps c/2 and 4 + c/2 (k-step kk holds dims 16 kk + 8 h + 0..7).
-  // Nodes past n store zeros.
-  for (int it = tid; it < nq; it += 256) {
-    const int hq = it >> 3, c = it & 7;
-    const int g = hq / G, row = i * G + hq % G;
-    if (it != tid) {
-      const uint16_t* src = p.q + (node_row * p.Hq + hq) * kD + 8 * c;
-      q_lo = *reinterpret_cast<const uint4*>(src);
-      q_hi = *reinterpret_cast<const uint4*>(src + 64);
-    }
-    uint4 lo = make_uint4(0, 0, 0, 0), hi = lo;
-    if (live) rotate8(q_lo, q_hi, cs_node, c, p.scale_log2, lo, hi);
-    const size_t tile = (static_cast<size_t>(b) * p.Hkv + g) * row_tiles + (row >> 5);
-    const int lane = (row & 31) + 32 * (c & 1);
-    p.qprep[(tile * 8 + (c >> 1)) * 64 + lane] = lo;
-    p.qprep[(tile * 8 + 4 + (c >> 1)) * 64 + lane] = hi;
-  }
-  if (!live) return;
-
-  // Tree keys, rotated at P + depth, go to cache slot P + i.
-  const int slot = P + i;
-  for (int it = tid; it < nk; it += 256) {
-    const int g = it >> 3, c = it & 7;
-    if (it != tid) {
-      const uint16_t* src = p.k_new + (node_row * p.Hkv + g) * kD + 8 * c;
-      k_lo = *reinterpret_cast<const uint4*>(src);
-      k_hi = *reinterpret_cast<const uint4*>(src + 64);
-    }
-    uint4 lo, hi;
-    rotate8(k_lo, k_hi, cs_node, c, 1.0f, lo, hi);
-    uint16_t* kdst = p.k_cache + ((static_cast<size_t>(b) * p.Hkv + g) * p.cap + slot) * kD;
-    *reinterpret_cast<uint4*>(kdst + 8 * c) = lo;
-    *reinterpret_cast<uint4*>(kdst + 64 + 8 * c) = hi;
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -504,16 +432,15 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   constexpr int NT = WAVES * 64;
   constexpr int ROWS = WAVES * 32 * QT;      // query rows of the workgroup
   constexpr int CPT = (kKT * kD / 8) / NT;   // 16-byte chunks per thread per K (or V) stage
-  constexpr int QCPT = ROWS * kD / 8 / NT;   // 16-byte chunks per thread of the workgroup's queries
-  static_assert(QCPT + 2 * CPT * (kStages - 1) <= 63, "vmcnt range");
-  static_assert(ROWS * kD <= 2 * kStageElems + kQExtra, "query block must fit the last stage plus the extra");
-  // (K, V) x stages, then kQExtra elements; the queries are staged through
-  // the last stage and the extra before the first tile lands there
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kStages * kStageElems + kQExtra];
+  static_assert(2 * CPT * (kStages - 1) <= 63, "vmcnt range");
+  // (K, V) x stages, then the RoPE table: float2 (cos, sin) of angle
+  // (P + depth) f_j at [depth][j]
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kStages * kStageElems + kCsElems];
+  float2* const cs_tab = reinterpret_cast<float2*>(smem + 2 * kStages * kStageElems);
 
   // Workgroups are handed to the eight XCDs round-robin by index; when the
   // row blocks come in multiples of eight, the splits of one row block get
-  // indices eight apart, so they share an L2 (their query block is fetched
+  // indices eight apart, so they share an L2 (their query rows are fetched
   // once) and start together. (A placement hint only: any mapping is
   // correct.)
   const int n_groups = gridDim.x / p.splits;
@@ -535,28 +462,17 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   const int rb0 = rb * ROWS;
   const int r0 = rb0 + wave * 32 * QT;       // first row of this wavefront
   const uint32_t lds_base = lds_addr(smem);
-  const uint32_t lds_q = lds_base + 2u * kStageElems * 2u * (kStages - 1);   // = last stage
-  const size_t head_rows = (static_cast<size_t>(b) * p.Hkv + g) * p.rows_pad;
 
   // The sequence's state is read first (scalar loads, which may not follow
   // the copies: those are opaque memory writes to the compiler).
   const SeqState sq = seq_state(p, b);
-
-  // ---- 1. every copy goes out before anything waits: the workgroup's
-  // query block (contiguous in prep's operand order) into LDS, then the
-  // first key tiles.
-  {
-    const uint16_t* qblk = reinterpret_cast<const uint16_t*>(p.qprep) + (head_rows + rb0) * kD;
-#pragma unroll
-    for (int j = 0; j < QCPT; ++j)
-      dma16(qblk, static_cast<uint32_t>(j * NT + tid) * 16u, lds_q + static_cast<uint32_t>(j * NT + wave * 64) * 16u);
-  }
   const int n = sq.n, P = sq.P;
   const int rows_live = sq.skip ? 0 : G * n;
   const int rows_all = G * p.n_max;
+  if (sq.cap_bad && g == 0 && rb == 0 && s == 0 && tid == 0) p.err[b] = TV_ERR_CAPACITY;
+  // (every workgroup of b reads err: before or after this store, b is skipped)
 
   if (rb0 >= rows_live) {
-    wait_vm<0>();   // no copy into this workgroup's LDS may outlive it
     // nothing live in this row block; with splits the merge writes the zeros
     if (p.splits == 1) {
       for (int r = rb0 + tid / 16; r < min(rb0 + ROWS, rows_all); r += NT / 16) {
@@ -569,13 +485,74 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   }
 
   // Keys of b: slots [0, P + n), in aligned 64-key tiles shared out over the
-  // splits. Tiles ending past P are masked (they hold the tree).
+  // splits. A split takes its tiles in DESCENDING order, so the at most two
+  // tiles that reach past P (they hold the tree) come first: their tree
+  // rows are formed in LDS from data loaded with the queries, and no load
+  // waits at the end of the kernel.
   const int key_end = P + n;
   const int tiles_all = (key_end + kKT - 1) / kKT;
   const int tiles_per_split = (tiles_all + p.splits - 1) / p.splits;
   const int t_begin = min(tiles_all, s * tiles_per_split);
   const int n_tiles = min(tiles_all, t_begin + tiles_per_split) - t_begin;
   const int k_begin = t_begin * kKT;
+  auto tile_k0 = [&](int pos) { return k_begin + (n_tiles - 1 - pos) * kKT; };   // first key at position pos
+  int n_masked = 0;
+  while (n_masked < n_tiles && tile_k0(n_masked) + kKT > P) ++n_masked;
+
+  // ---- 1. register loads go out before the tile copies (vector memory
+  // operations complete in order, so a load queued behind the copies would
+  // wait for all of them): this wavefront's query rows (lane: row
+  // r0 + 32 t + l%32, dims 16 kk + 8 h + 0..7 for kk < 8), their nodes'
+  // depths and the depth of node `lane` (for the deepest node of b); with
+  // tree tiles, also node `lane`'s key and value chunks, its depth, and the
+  // ancestor masks of this wavefront's rows. Every address is valid (node
+  // indices are clamped), so the loads need no branches; dead rows and
+  // nodes are dropped once the values have landed.
+  constexpr int KC = 8 / WAVES, VC = 16 / WAVES;   // tree: 16-byte chunks per lane
+  int my_row[QT];
+  bool row_live[QT];
+  u32x4 qraw[QT][8];
+  uint32_t qdep[QT];
+  uint64_t my_anc[QT];
+#pragma unroll
+  for (int t = 0; t < QT; ++t) {
+    my_row[t] = r0 + 32 * t + (lane & 31);
+    row_live[t] = my_row[t] < rows_live;
+    my_anc[t] = 0;
+    const int node = min(my_row[t] / G, p.n_max - 1);
+    const uint16_t* src = p.q + ((static_cast<size_t>(b) * p.n_max + node) * p.Hq + g * G + my_row[t] % G) * kD + 8 * h;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) qraw[t][kk] = ld_b128(src + 16 * kk);
+    qdep[t] = ld_b32(p.depth + static_cast<size_t>(b) * p.n_max + node);
+  }
+  uint32_t dep_lane = ld_b32(p.depth + static_cast<size_t>(b) * p.n_max + min(lane, p.n_max - 1));
+  u32x4 tk_lo[KC], tk_hi[KC], tvv[VC];
+  uint32_t t_dep = 0;
+  auto load_tree = [&](auto asm_tag) __attribute__((always_inline)) {
+    constexpr bool ASM = decltype(asm_tag)::value;
+    const size_t nrow = (static_cast<size_t>(b) * p.n_max + min(lane, n - 1)) * p.Hkv + g;
+    const uint16_t* ksrc = p.k_new + nrow * kD;
+    const uint16_t* vsrc = p.v_new + nrow * kD;
+    const uint32_t* dsrc = reinterpret_cast<const uint32_t*>(p.depth) + static_cast<size_t>(b) * p.n_max + min(lane, n - 1);
+#pragma unroll
+    for (int u = 0; u < KC; ++u) {
+      const int c = wave + WAVES * u;
+      tk_lo[u] = ASM ? ld_b128(ksrc + 8 * c) : *reinterpret_cast<const u32x4*>(ksrc + 8 * c);
+      tk_hi[u] = ASM ? ld_b128(ksrc + 64 + 8 * c) : *reinterpret_cast<const u32x4*>(ksrc + 64 + 8 * c);
+    }
+#pragma unroll
+    for (int u = 0; u < VC; ++u) {
+      const uint16_t* v8 = vsrc + 8 * (wave + WAVES * u);
+      tvv[u] = ASM ? ld_b128(v8) : *reinterpret_cast<const u32x4*>(v8);
+    }
+    t_dep = ASM ? ld_b32(dsrc) : *dsrc;
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+      const uint64_t* asrc = p.anc + static_cast<size_t>(b) * p.n_max + min(my_row[t] / G, p.n_max - 1);
+      my_anc[t] = ASM ? ld_b64(asrc) : *asrc;
+    }
+  };
+  if (n_masked > 0) load_tree(std::true_type{});
 
   // stage buf: K at smem + 2 buf * kStageElems, V right after it
   auto Ks = [&](int buf) { return smem + 2 * buf * kStageElems; };
@@ -596,10 +573,10 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
     for (int u = 0; u < 4; ++u) v_addr[u] = vs_off(d, 2 * u + h);
   }
 
-  // Copies key tile [kt0, kt0+64) into stage `buf`. LDS chunk c (16 bytes)
-  // of a stage is K row c/16, position c%16 (unit swizzled by key) and V row
-  // c/8, position c%8 (unit swizzled by d); the lane that writes chunk c
-  // fetches the matching global chunk.
+  // Copies the tile at position pos into stage pos % kStages. LDS chunk c
+  // (16 bytes) of a stage is K row c/16, position c%16 (unit swizzled by
+  // key) and V row c/8, position c%8 (unit swizzled by d); the lane that
+  // writes chunk c fetches the matching global chunk.
   uint32_t k_voff[CPT], v_voff[CPT];
 #pragma unroll
   for (int j = 0; j < CPT; ++j) {
@@ -609,7 +586,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
     const int d = c >> 3, vpos = c & 7;
     v_voff[j] = static_cast<uint32_t>(d * kKT + ((vpos ^ (d & 7)) << 3)) * 2u;
   }
-  auto issue_tile = [&](int kt0, int buf) {
+  auto issue_tile = [&](int pos) {
+    const int kt0 = tile_k0(pos), buf = pos % kStages;
     const uint16_t* ktile = kc + static_cast<size_t>(kt0) * kD;
     const uint16_t* vtile = vc + static_cast<size_t>(kt0) * kD;   // kt0 is a multiple of 64
     const uint32_t kl = lds_base + static_cast<uint32_t>(2 * buf * kStageElems + wave * 64 * 8) * 2u;
@@ -623,10 +601,12 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
 
 #pragma unroll
   for (int t = 0; t < kStages - 1; ++t)
-    if (t < n_tiles) issue_tile(k_begin + t * kKT, t);
+    if (t < n_tiles) issue_tile(t);
 
-  // ---- 2. the queries have landed once only the tile copies are
-  // outstanding: read them into the B operands
+  // ---- 2. once only tile copies are outstanding the register loads have
+  // landed: the RoPE table for depths 0 .. deepest node of b, then the
+  // queries, rotated at P + depth, times softmax_scale * log2(e), in bf16:
+  // the B operands of the score MFMA
   {
     const int issued = min(n_tiles, kStages - 1);
     static_assert(kStages == 4, "waits below assume three tiles in flight");
@@ -635,25 +615,94 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
     else if (issued == 1) wait_vm<2 * CPT>();
     else wait_vm<0>();
   }
+#pragma unroll
+  for (int t = 0; t < QT; ++t) {
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) landed(qraw[t][kk]);
+    landed(qdep[t]);
+    landed(my_anc[t]);
+  }
+  landed(dep_lane);
+#pragma unroll
+  for (int u = 0; u < KC; ++u) {
+    landed(tk_lo[u]);
+    landed(tk_hi[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < VC; ++u) landed(tvv[u]);
+  landed(t_dep);
+  {
+    int dmax = lane < n ? clamp_depth(static_cast<int>(dep_lane)) : 0;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) dmax = max(dmax, __shfl_xor(dmax, off));
+    const int n_cs = (__builtin_amdgcn_readfirstlane(dmax) + 1) * (kD / 2);
+    const double freq = exp2(p.log2_theta * (-2.0 * (tid & 63) / kD));   // column tid % 64 of every row
+    for (int e = tid; e < n_cs; e += NT)
+      cs_tab[e] = p.rope ? rope_cs(P + (e >> 6), freq) : make_float2(1.0f, 0.0f);
+  }
   __syncthreads();
-  int my_row[QT];
-  bool row_live[QT];
-  uint64_t my_anc[QT];   // loaded before the first masked tile
   bf16x8 qf[QT][8];      // qf[t][kk] = rotated, scaled Q[row][16kk + 8h .. +8]
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
-    my_row[t] = r0 + 32 * t + (lane & 31);
-    row_live[t] = my_row[t] < rows_live;
-    my_anc[t] = 0;
-    const int k = wave * QT + t;   // 32-row tile of the workgroup
+    const float2* cs = cs_tab + (row_live[t] ? clamp_depth(static_cast<int>(qdep[t])) : 0) * (kD / 2) + 8 * h;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-      qf[t][kk] = *reinterpret_cast<const bf16x8*>(smem + 2 * kStageElems * (kStages - 1) + ((k * 8 + kk) * 64 + lane) * 8);
+    for (int kk = 0; kk < 4; ++kk) {
+      uint4 lo, hi;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      const u32x4 a = row_live[t] ? qraw[t][kk] : z, c = row_live[t] ? qraw[t][kk + 4] : z;
+      rope8(make_uint4(a[0], a[1], a[2], a[3]), make_uint4(c[0], c[1], c[2], c[3]), cs + 16 * kk, p.scale_log2, lo, hi);
+      qf[t][kk] = __builtin_bit_cast(bf16x8, lo);
+      qf[t][kk + 4] = __builtin_bit_cast(bf16x8, hi);
+    }
   }
-  auto load_anc = [&]() {
+
+  // Forms the tree part of the staged tile at position pos (< n_masked):
+  // slot P + i holds tree node i (lane i): its key, rotated at
+  // P + depth(i), and its value, written into the stage (and, with `store`,
+  // appended to the cache). Slots past P + n are not this call's keys and
+  // may hold anything: their scores are masked and their values zeroed (a
+  // masked probability is 0, but 0 * NaN is not).
+  auto fill_tree = [&](int pos, bool store) __attribute__((always_inline)) {
+    const int kt0 = tile_k0(pos);
+    uint16_t* kd = Ks(pos % kStages);
+    uint16_t* vd = Vs(pos % kStages);
+    if (kt0 + lane >= key_end) {
 #pragma unroll
-    for (int t = 0; t < QT; ++t)
-      my_anc[t] = p.anc[static_cast<size_t>(b) * p.n_max + min(my_row[t] / G, p.n_max - 1)];
+      for (int u = 0; u < VC; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vd[vs_off(8 * (wave + WAVES * u) + e, lane >> 3) + (lane & 7)] = 0;
+    }
+    const int slot = P + lane;
+    if (lane < n && slot >= kt0 && slot < kt0 + kKT) {
+      const int key = slot - kt0;
+      const float2* cs = cs_tab + clamp_depth(static_cast<int>(t_dep)) * (kD / 2);
+      uint16_t* kdst = p.k_cache + head_off + static_cast<size_t>(slot) * kD;
+#pragma unroll
+      for (int u = 0; u < KC; ++u) {
+        const int c = wave + WAVES * u;   // dims 8c.. pair with 64 + 8c..
+        uint4 lo, hi;
+        rope8(make_uint4(tk_lo[u][0], tk_lo[u][1], tk_lo[u][2], tk_lo[u][3]),
+              make_uint4(tk_hi[u][0], tk_hi[u][1], tk_hi[u][2], tk_hi[u][3]), cs + 8 * c, 1.0f, lo, hi);
+        *reinterpret_cast<uint4*>(kd + ks_off(key, c)) = lo;
+        *reinterpret_cast<uint4*>(kd + ks_off(key, c + 8)) = hi;
+        if (store) {
+          *reinterpret_cast<uint4*>(kdst + 8 * c) = lo;
+          *reinterpret_cast<uint4*>(kdst + 64 + 8 * c) = hi;
+        }
+      }
+      uint16_t* vh = p.v_cache + head_off;
+#pragma unroll
+      for (int u = 0; u < VC; ++u) {
+        const uint4 v4 = make_uint4(tvv[u][0], tvv[u][1], tvv[u][2], tvv[u][3]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int d = 8 * (wave + WAVES * u) + e;
+          const uint16_t x = u4_elem(v4, e);
+          vd[vs_off(d, key >> 3) + (key & 7)] = x;
+          if (store) vh[v_cache_off(slot, d)] = x;   // lanes: consecutive slots of row d
+        }
+      }
+    }
   };
 
   RowState st[QT];
@@ -677,50 +726,50 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   float mx[QT];
   auto run_pass = [&](auto mode_tag) {
     constexpr int MODE = decltype(mode_tag)::value;
-    auto product = [&](auto masked_tag, const uint16_t* ks_, const uint16_t* vs_, int rel0) {
+    auto product = [&](auto masked_tag, int pos) {
       constexpr bool M = decltype(masked_tag)::value;
+      const int buf = pos % kStages, rel0 = tile_k0(pos) - P;
       if constexpr (MODE == 1)
-        tile_max<QT, M>(mx, ks_, qf, k_addr, h, rel0, my_anc);
+        tile_max<QT, M>(mx, Ks(buf), qf, k_addr, h, rel0, my_anc);
       else
-        tile_product<QT, M, MODE == 2>(st, ks_, vs_, qf, k_addr, v_addr, h, rel0, my_anc);
+        tile_product<QT, M, MODE == 2>(st, Ks(buf), Vs(buf), qf, k_addr, v_addr, h, rel0, my_anc);
     };
-    // A ring of kStages LDS stages, kStages - 1 tiles in flight; tile t lives
-    // in stage t % kStages. The steady-state loop only sees prefix tiles with
-    // kStages - 2 later tiles outstanding, so it is one straight block; the
-    // last kStages - 1 tiles (the drain, which holds the at most two masked
-    // tiles) are peeled off below. Wavefronts whose rows are all padding
-    // compute on their (zero) queries rather than branch around the products.
-    int t = 0;
-    for (; t + kStages - 1 < n_tiles; ++t) {
-      const int cur = t % kStages;
-      wait_vm<2 * CPT * (kStages - 2)>();
-      __syncthreads();   // tile t has landed for every wave; stage (t-1) % kStages is free
-      issue_tile(k_begin + (t + kStages - 1) * kKT, (t + kStages - 1) % kStages);
-      product(std::false_type{}, Ks(cur), Vs(cur), 0);
-    }
-    if (k_begin + n_tiles * kKT > P) load_anc();   // masked tiles ahead
-    for (; t < n_tiles; ++t) {
-      const int cur = t % kStages;
-      const int later = n_tiles - 1 - t;
-      static_assert(kStages == 4, "drain waits below assume four stages");
+    // Waits until the tile at position t has landed, given how many later
+    // tiles are in flight (at most kStages - 2).
+    auto wait_tile = [&](int t) {
+      const int later = min(kStages - 2, n_tiles - 1 - t);
+      static_assert(kStages == 4, "waits below assume four stages");
       if (later >= 2) wait_vm<2 * CPT * 2>();
       else if (later == 1) wait_vm<2 * CPT>();
       else wait_vm<0>();
+    };
+    // A ring of kStages LDS stages, kStages - 1 tiles in flight; position t
+    // lives in stage t % kStages. The tree tiles come first; the steady loop
+    // then sees prefix tiles with kStages - 2 later tiles outstanding, so it
+    // is one straight block; the last kStages - 1 tiles are peeled off.
+    // Wavefronts whose rows are all padding compute on their (zero) queries
+    // rather than branch around the products.
+    int t = 0;
+    for (; t < n_masked; ++t) {
+      wait_tile(t);
+      __syncthreads();   // tile t has landed for every wave; stage (t-1) % kStages is free
+      // the tree's keys and values (appended to the cache once: by row
+      // block 0, on the first pass)
+      fill_tree(t, MODE == 0 && rb == 0);
       __syncthreads();
-      const int kt0 = k_begin + t * kKT;
-      if (kt0 + kKT <= P) {
-        product(std::false_type{}, Ks(cur), Vs(cur), 0);
-      } else {
-        // slots past P + n are not this call's keys and may hold anything:
-        // zero their values (their scores are masked)
-        const int stale0 = max(0, key_end - kt0);
-        for (int idx = tid; idx < (kKT - stale0) * kD; idx += NT) {
-          const int key = stale0 + idx / kD, d = idx % kD;
-          Vs(cur)[vs_off(d, key >> 3) + (key & 7)] = 0;
-        }
-        __syncthreads();
-        product(std::true_type{}, Ks(cur), Vs(cur), kt0 - P);
-      }
+      if (t + kStages - 1 < n_tiles) issue_tile(t + kStages - 1);
+      product(std::true_type{}, t);
+    }
+    for (; t + kStages - 1 < n_tiles; ++t) {
+      wait_vm<2 * CPT * (kStages - 2)>();
+      __syncthreads();   // tile t has landed for every wave; stage (t-1) % kStages is free
+      issue_tile(t + kStages - 1);
+      product(std::false_type{}, t);
+    }
+    for (; t < n_tiles; ++t) {
+      wait_tile(t);
+      __syncthreads();
+      product(std::false_type{}, t);
     }
   };
 
@@ -746,11 +795,13 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   const bool any_redo = reinterpret_cast<const int*>(smem)[0] != 0;
   __syncthreads();
   if (any_redo) {
+    // (rare: the tree's rows are loaded again, by ordinary loads)
 #pragma unroll
     for (int t = 0; t < QT; ++t) mx[t] = -INFINITY;
+    if (n_masked > 0) load_tree(std::false_type{});
 #pragma unroll
     for (int t = 0; t < kStages - 1; ++t)
-      if (t < n_tiles) issue_tile(k_begin + t * kKT, t);
+      if (t < n_tiles) issue_tile(t);
     run_pass(std::integral_constant<int, 1>{});
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
@@ -759,9 +810,10 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
     }
     reset_state(r_ref);
     __syncthreads();
+    if (n_masked > 0) load_tree(std::false_type{});
 #pragma unroll
     for (int t = 0; t < kStages - 1; ++t)
-      if (t < n_tiles) issue_tile(k_begin + t * kKT, t);
+      if (t < n_tiles) issue_tile(t);
     run_pass(std::integral_constant<int, 2>{});
   }
 
@@ -868,20 +920,18 @@ const Tune& tune() {
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// Workspace layout: qprep | part_ml | part_o (the last two only with several
-// splits).
+// Workspace layout: part_ml | part_o, only with several splits.
 struct WsLayout {
-  size_t qprep, part_ml, part_o, total;
+  size_t part_ml, part_o, total;
 };
 WsLayout ws_layout(const tv_attn_args* a, const AttnPlan& pl) {
-  WsLayout w;
+  WsLayout w{0, 0, 0};
+  if (pl.splits == 1) return w;
   const size_t heads = static_cast<size_t>(a->B) * a->Hkv;
   const size_t wg_rows = static_cast<size_t>(pl.waves) * 32 * pl.qt;
   const size_t wgs = heads * pl.row_blocks * pl.splits;
-  w.qprep = 0;
-  w.part_ml = align_up(heads * pl.rows_pad * kD * 2);
-  w.part_o = w.part_ml + (pl.splits > 1 ? align_up(wgs * wg_rows * 2 * sizeof(float2)) : 0);
-  w.total = w.part_o + (pl.splits > 1 ? wgs * wg_rows * 32 * sizeof(float4) : 0);
+  w.part_o = align_up(wgs * wg_rows * 2 * sizeof(float2));
+  w.total = w.part_o + wgs * wg_rows * 32 * sizeof(float4);
   return w;
 }
 
@@ -936,21 +986,15 @@ hipError_t launch_attention_bf16(const tv_attn_args* a, const AttnPlan& pl, hipS
   p.cap = a->cap;
   p.splits = pl.splits;
   p.row_blocks = pl.row_blocks;
-  p.rows_pad = pl.rows_pad;
   p.rope = a->rope_theta != 0.0f;
-  for (int d = 0; d < kD / 2; ++d)
-    p.inv_freq[d] = p.rope ? pow(static_cast<double>(a->rope_theta), -2.0 * d / kD) : 0.0;
+  p.log2_theta = p.rope ? log2(static_cast<double>(a->rope_theta)) : 0.0;
   const float scale = a->softmax_scale > 0.0f ? a->softmax_scale : 1.0f / sqrtf(static_cast<float>(kD));
   p.scale_log2 = scale * 1.4426950408889634f;
   const WsLayout w = ws_layout(a, pl);
   char* ws = static_cast<char*>(a->workspace);
-  p.qprep = reinterpret_cast<uint4*>(ws + w.qprep);
   p.part_ml = pl.splits > 1 ? reinterpret_cast<float2*>(ws + w.part_ml) : nullptr;
   p.part_o = pl.splits > 1 ? reinterpret_cast<float4*>(ws + w.part_o) : nullptr;
 
-  hipLaunchKernelGGL(prep_bf16_kernel, dim3(a->n_max + a->Hkv, a->B), dim3(256), 0, s, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   dim3 grid(pl.splits * pl.row_blocks * a->Hkv * a->B);
   const int wg_rows = pl.waves * 32 * pl.qt;
   dim3 mgrid(pl.row_blocks * wg_rows / 8, a->Hkv, a->B);
@@ -960,7 +1004,7 @@ hipError_t launch_attention_bf16(const tv_attn_args* a, const AttnPlan& pl, hipS
     case 41: hipLaunchKernelGGL((attn_bf16_kernel<4, 1>), grid, dim3(256), 0, s, p); break;
     default: hipLaunchKernelGGL((attn_bf16_kernel<4, 2>), grid, dim3(256), 0, s, p); break;
   }
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.splits == 1) return e;
   switch (key) {
     case 21: hipLaunchKernelGGL((merge_bf16_kernel<2, 1>), mgrid, dim3(256), 0, s, p); break;
