@@ -21,18 +21,17 @@
 //          assembly: the compiler then does not see an LDS write it cannot
 //          tell apart from the fragment reads, and does not drain every copy
 //          in flight before each tile; the kernel waits for exactly the tile
-//          it needs (s_waitcnt vmcnt) and a barrier.
+//          it needs (s_waitcnt vmcnt) and a barrier. A tile's copy goes out
+//          in parts between the MFMAs of the tile product before it.
 //
 //          While the first tiles are in flight, the workgroup builds a table
 //          of RoPE (cos, sin) for the depths 0 .. deepest node in LDS, and
 //          each lane rotates its query rows at P + depth, scales them by
 //          softmax_scale * log2(e) and rounds them to bf16 in the register
-//          order of the score MFMA's B operand. In the one or two tiles that
-//          reach past P, the tree's keys are rotated the same way and written
-//          into the LDS stage with its values, straight from k_new / v_new;
-//          row block 0 also appends them to cache slots P + i. No kernel of
-//          the call reads them back from the cache, so nothing orders the
-//          workgroups.
+//          order of the score MFMA's B operand. A split takes its tiles in
+//          descending order, so the one or two tiles that reach past P come
+//          first; there the tree's keys, rotated the same way, and its values
+//          are written into the LDS stage straight from k_new / v_new.
 //
 //          Scores are computed transposed, S^T = K Q^T, with
 //          v_mfma_f32_32x32x16_bf16: a lane then holds 16 keys of ONE query
@@ -65,6 +64,11 @@
 //   merge  with several splits, each writes (reference, row sum,
 //          unnormalised output) to the workspace in register order; the merge
 //          combines them in split order (deterministic) and writes the rows.
+//          It also appends the tree to cache slots P + i (keys rotated in the
+//          same rounding order as in LDS); with one split a small kernel does
+//          only that. The attention kernel never reads those slots back, and
+//          stores issued between its tile copies would delay every later
+//          wait for a tile.
 //
 // RoPE angles: a table entry forms pos * 2^(-2j/D log2 theta) in double
 // precision, reduces it to [-pi, pi] and takes a single-precision sincos.
@@ -231,6 +235,14 @@ __device__ __forceinline__ SeqState seq_state(const BfParams& p, int b) {
   return q;
 }
 
+// Rotate-half RoPE of one dimension pair (x_lo, x_hi) by the angle whose
+// (cos, sin) is cs, in one fixed rounding order (the cache append repeats it
+// bit for bit).
+__device__ __forceinline__ float rope_lo(float xl, float xh, float2 cs) { return fmaf(xl, cs.x, -(xh * cs.y)); }
+__device__ __forceinline__ float rope_hi(float xl, float xh, float2 cs) { return fmaf(xh, cs.x, xl * cs.y); }
+// RoPE frequency of pair j: theta^(-2j/D), as 2^(-2j/D log2 theta).
+__device__ __forceinline__ double rope_freq(double log2_theta, int j) { return exp2(log2_theta * (-2.0 * j / kD)); }
+
 // Rotate-half RoPE of 8 dimension pairs: lo[e] and hi[e] are dims d + e and
 // d + 64 + e, cs[e] the (cos, sin) of their angle. Results are multiplied by
 // scale and rounded to bf16.
@@ -245,8 +257,8 @@ __device__ __forceinline__ void rope8(const uint4& lo, const uint4& hi, const fl
       const float2 cn = cs[2 * u2 + u];
       const float xl = bf16_bits_to_f32(u4_elem(lo, 2 * u2 + u));
       const float xh = bf16_bits_to_f32(u4_elem(hi, 2 * u2 + u));
-      rl[u] = (xl * cn.x - xh * cn.y) * scale;
-      rh[u] = (xh * cn.x + xl * cn.y) * scale;
+      rl[u] = rope_lo(xl, xh, cn) * scale;
+      rh[u] = rope_hi(xl, xh, cn) * scale;
     }
     wl[u2] = pack_bf16(rl[0], rl[1]);
     wh[u2] = pack_bf16(rh[0], rh[1]);
@@ -330,13 +342,19 @@ __device__ __forceinline__ uint32_t prob_pair(RowState& st, const f32x16& x, int
 // Step i consumes LDS fragment i (K rows, then V rows) and issues the read
 // of fragment i + kLook, so few fragments are live at once. Each fragment
 // feeds QT MFMAs. sched_barrier pins the order (the scheduler would
-// otherwise group like instructions and hoist every read).
+// otherwise group like instructions and hoist every read). copy(j), j < 8,
+// issues slot j of a later tile's copy; it is called in the even steps that
+// carry no vector-ALU work (0-6, 24-30), where its issue overlaps the
+// matrix cores.
 constexpr int kLook = 4;
-template <int QT, bool MASKED, bool SHIFT>
+struct NoCopy {
+  __device__ __forceinline__ void operator()(int) const {}
+};
+template <int QT, bool MASKED, bool SHIFT, typename Copy>
 __device__ __forceinline__ void tile_product(RowState (&st)[QT], const uint16_t* __restrict__ ks,
                                              const uint16_t* __restrict__ vs, const bf16x8 (&qf)[QT][8],
                                              const int (&k_addr)[8], const int (&v_addr)[4], int h, int rel0,
-                                             const uint64_t (&anc)[QT]) {
+                                             const uint64_t (&anc)[QT], const Copy& copy) {
   auto frag_ptr = [&](int i) -> const bf16x8* {
     if (i < 16) return reinterpret_cast<const bf16x8*>(ks + k_addr[i & 7] + (i >> 3) * 32 * kD);
     const int j = (i - 16) & 7, sub = (i - 16) >> 3;
@@ -371,6 +389,10 @@ __device__ __forceinline__ void tile_product(RowState (&st)[QT], const uint16_t*
         st[t].o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i], pf, st[t].o[dt], 0, 0, 0);
       }
       if (soft) w[ssub][t][c] = prob_pair<MASKED, SHIFT>(st[t], x[ssub][t], c, ssub, h, rel0, anc[t]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if ((i & 1) == 0 && (i < 8 || i >= 24)) {
+      copy(i < 8 ? i / 2 : 4 + (i - 24) / 2);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -432,29 +454,31 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   constexpr int NT = WAVES * 64;
   constexpr int ROWS = WAVES * 32 * QT;      // query rows of the workgroup
   constexpr int CPT = (kKT * kD / 8) / NT;   // 16-byte chunks per thread per K (or V) stage
-  static_assert(2 * CPT * (kStages - 1) <= 63, "vmcnt range");
+  static_assert(2 * CPT * (kStages - 1) <= 63, "vmcnt range");   // (the counter's limit)
   // (K, V) x stages, then the RoPE table: float2 (cos, sin) of angle
   // (P + depth) f_j at [depth][j]
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kStages * kStageElems + kCsElems];
   float2* const cs_tab = reinterpret_cast<float2*>(smem + 2 * kStages * kStageElems);
 
-  // Workgroups are handed to the eight XCDs round-robin by index; when the
-  // row blocks come in multiples of eight, the splits of one row block get
-  // indices eight apart, so they share an L2 (their query rows are fetched
-  // once) and start together. (A placement hint only: any mapping is
-  // correct.)
-  const int n_groups = gridDim.x / p.splits;
-  int s, gi;
-  if (n_groups % 8 == 0) {
-    const int L = blockIdx.x, k = L >> 3;
-    s = k % p.splits;
-    gi = (k / p.splits) * 8 + (L & 7);
+  // Workgroups are handed to the eight XCDs round-robin by index. When the
+  // (sequence, KV head) pairs come in multiples of eight, all workgroups of
+  // one pair get indices eight apart, so they share an L2 and start
+  // together: the row blocks of one split (adjacent there) read the same key
+  // tiles, and every split reads the same query rows. (A placement hint
+  // only: any bijection is correct.)
+  const int per_head = p.row_blocks * p.splits, n_heads = gridDim.x / per_head;
+  int s, rb, hd;
+  if (n_heads % 8 == 0) {
+    const int L = blockIdx.x, k = L >> 3, w = k % per_head;
+    hd = (k / per_head) * 8 + (L & 7);
+    s = w / p.row_blocks;
+    rb = w % p.row_blocks;
   } else {
-    s = blockIdx.x % p.splits;
-    gi = blockIdx.x / p.splits;
+    hd = blockIdx.x / per_head;
+    s = (blockIdx.x % per_head) / p.row_blocks;
+    rb = blockIdx.x % p.row_blocks;
   }
-  const int rb = gi % p.row_blocks;
-  const int g = (gi / p.row_blocks) % p.Hkv, b = gi / (p.row_blocks * p.Hkv);
+  const int g = hd % p.Hkv, b = hd / p.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = p.G;
@@ -499,19 +523,36 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   int n_masked = 0;
   while (n_masked < n_tiles && tile_k0(n_masked) + kKT > P) ++n_masked;
 
-  // ---- 1. register loads go out before the tile copies (vector memory
-  // operations complete in order, so a load queued behind the copies would
-  // wait for all of them): this wavefront's query rows (lane: row
-  // r0 + 32 t + l%32, dims 16 kk + 8 h + 0..7 for kk < 8), their nodes'
-  // depths and the depth of node `lane` (for the deepest node of b); with
-  // tree tiles, also node `lane`'s key and value chunks, its depth, and the
-  // ancestor masks of this wavefront's rows. Every address is valid (node
-  // indices are clamped), so the loads need no branches; dead rows and
-  // nodes are dropped once the values have landed.
-  constexpr int KC = 8 / WAVES, VC = 16 / WAVES;   // tree: 16-byte chunks per lane
+  // ---- 1. everything the start needs goes out before the tile copies
+  // (vector memory operations complete in order, so anything queued behind
+  // the copies would wait for all of them):
+  //  * the workgroup's query rows, raw, copied straight into LDS (the last
+  //    ring stage and the RoPE table's region, both idle until the queries
+  //    are read): chunk c = row c/16, position c%16, holding the row's 16-byte
+  //    piece (c%16) ^ (row%16), so that reads in operand order (one piece of
+  //    32 consecutive rows) hit distinct banks;
+  //  * register loads: the depths of this wavefront's rows' nodes and of
+  //    node `lane` (for the deepest node of b); with tree tiles, the tree's
+  //    keys and values in 16-byte chunks (lane items: node, chunk) with their
+  //    nodes' depths, and the ancestor masks of this wavefront's rows.
+  // Every address is valid (node indices are clamped), so nothing branches;
+  // dead rows and nodes are dropped once the data has landed.
+  constexpr int QCPT = ROWS * kD / 8 / NT;              // query chunks per thread
+  constexpr int KI = 8 * 64 / NT, VI = 16 * 64 / NT;   // tree items per thread: K pairs, V chunks
+  static_assert(ROWS * kD <= 2 * kStageElems + kCsElems, "query rows must fit the last stage and the table region");
+  const uint32_t lds_q = lds_base + 2u * kStageElems * 2u * (kStages - 1);
+  {
+    const uint16_t* qb = p.q + static_cast<size_t>(b) * p.n_max * p.Hq * kD;
+#pragma unroll
+    for (int j = 0; j < QCPT; ++j) {
+      const int c = j * NT + tid, r = c >> 4, piece = (c & 15) ^ (r & 15);
+      const int row = rb0 + r, node = min(row / G, p.n_max - 1);
+      const uint32_t voff = static_cast<uint32_t>(((node * p.Hq + g * G + row % G) * kD + 8 * piece) * 2);
+      dma16(qb, voff, lds_q + static_cast<uint32_t>(j * NT + wave * 64) * 16u);
+    }
+  }
   int my_row[QT];
   bool row_live[QT];
-  u32x4 qraw[QT][8];
   uint32_t qdep[QT];
   uint64_t my_anc[QT];
 #pragma unroll
@@ -519,33 +560,28 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
     my_row[t] = r0 + 32 * t + (lane & 31);
     row_live[t] = my_row[t] < rows_live;
     my_anc[t] = 0;
-    const int node = min(my_row[t] / G, p.n_max - 1);
-    const uint16_t* src = p.q + ((static_cast<size_t>(b) * p.n_max + node) * p.Hq + g * G + my_row[t] % G) * kD + 8 * h;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) qraw[t][kk] = ld_b128(src + 16 * kk);
-    qdep[t] = ld_b32(p.depth + static_cast<size_t>(b) * p.n_max + node);
+    qdep[t] = ld_b32(p.depth + static_cast<size_t>(b) * p.n_max + min(my_row[t] / G, p.n_max - 1));
   }
   uint32_t dep_lane = ld_b32(p.depth + static_cast<size_t>(b) * p.n_max + min(lane, p.n_max - 1));
-  u32x4 tk_lo[KC], tk_hi[KC], tvv[VC];
-  uint32_t t_dep = 0;
+  u32x4 tk_lo[KI], tk_hi[KI], tvv[VI];
+  uint32_t t_dep[KI];
   auto load_tree = [&](auto asm_tag) __attribute__((always_inline)) {
     constexpr bool ASM = decltype(asm_tag)::value;
-    const size_t nrow = (static_cast<size_t>(b) * p.n_max + min(lane, n - 1)) * p.Hkv + g;
-    const uint16_t* ksrc = p.k_new + nrow * kD;
-    const uint16_t* vsrc = p.v_new + nrow * kD;
-    const uint32_t* dsrc = reinterpret_cast<const uint32_t*>(p.depth) + static_cast<size_t>(b) * p.n_max + min(lane, n - 1);
 #pragma unroll
-    for (int u = 0; u < KC; ++u) {
-      const int c = wave + WAVES * u;
-      tk_lo[u] = ASM ? ld_b128(ksrc + 8 * c) : *reinterpret_cast<const u32x4*>(ksrc + 8 * c);
-      tk_hi[u] = ASM ? ld_b128(ksrc + 64 + 8 * c) : *reinterpret_cast<const u32x4*>(ksrc + 64 + 8 * c);
+    for (int u = 0; u < KI; ++u) {
+      const int item = tid + NT * u, node = min(item >> 3, n - 1), c = item & 7;
+      const uint16_t* ksrc = p.k_new + ((static_cast<size_t>(b) * p.n_max + node) * p.Hkv + g) * kD + 8 * c;
+      tk_lo[u] = ASM ? ld_b128(ksrc) : *reinterpret_cast<const u32x4*>(ksrc);
+      tk_hi[u] = ASM ? ld_b128(ksrc + 64) : *reinterpret_cast<const u32x4*>(ksrc + 64);
+      const uint32_t* dsrc = reinterpret_cast<const uint32_t*>(p.depth) + static_cast<size_t>(b) * p.n_max + node;
+      t_dep[u] = ASM ? ld_b32(dsrc) : *dsrc;
     }
 #pragma unroll
-    for (int u = 0; u < VC; ++u) {
-      const uint16_t* v8 = vsrc + 8 * (wave + WAVES * u);
-      tvv[u] = ASM ? ld_b128(v8) : *reinterpret_cast<const u32x4*>(v8);
+    for (int u = 0; u < VI; ++u) {
+      const int item = tid + NT * u, node = min(item >> 4, n - 1), c = item & 15;
+      const uint16_t* vsrc = p.v_new + ((static_cast<size_t>(b) * p.n_max + node) * p.Hkv + g) * kD + 8 * c;
+      tvv[u] = ASM ? ld_b128(vsrc) : *reinterpret_cast<const u32x4*>(vsrc);
     }
-    t_dep = ASM ? ld_b32(dsrc) : *dsrc;
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
       const uint64_t* asrc = p.anc + static_cast<size_t>(b) * p.n_max + min(my_row[t] / G, p.n_max - 1);
@@ -586,27 +622,58 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
     const int d = c >> 3, vpos = c & 7;
     v_voff[j] = static_cast<uint32_t>(d * kKT + ((vpos ^ (d & 7)) << 3)) * 2u;
   }
-  auto issue_tile = [&](int pos) {
-    const int kt0 = tile_k0(pos), buf = pos % kStages;
-    const uint16_t* ktile = kc + static_cast<size_t>(kt0) * kD;
-    const uint16_t* vtile = vc + static_cast<size_t>(kt0) * kD;   // kt0 is a multiple of 64
-    const uint32_t kl = lds_base + static_cast<uint32_t>(2 * buf * kStageElems + wave * 64 * 8) * 2u;
-    const uint32_t vl = kl + kStageElems * 2u;
+  // A tile's copy in 8 slots of 2 * CPT / 8 instructions each (instruction
+  // 2j: K chunk j, 2j + 1: V chunk j), so that a tile product can spread
+  // them over its steps.
+  static_assert(2 * CPT % 8 == 0, "copy slots");
+  struct TileCopy {
+    const uint16_t* ktile;
+    const uint16_t* vtile;
+    uint32_t kl, vl;
+    const uint32_t* k_voff;
+    const uint32_t* v_voff;
+    __device__ __forceinline__ void operator()(int slot) const {
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-      dma16(ktile, k_voff[j], kl + j * NT * 16);
-      dma16(vtile, v_voff[j], vl + j * NT * 16);
+      for (int part = slot * (2 * CPT / 8); part < (slot + 1) * (2 * CPT / 8); ++part) {
+        const int j = part >> 1;
+        if (part & 1)
+          dma16(vtile, v_voff[j], vl + j * NT * 16);
+        else
+          dma16(ktile, k_voff[j], kl + j * NT * 16);
+      }
     }
   };
+  auto tile_copy = [&](int pos) {
+    const int kt0 = tile_k0(pos), buf = pos % kStages;
+    TileCopy c;
+    c.ktile = kc + static_cast<size_t>(kt0) * kD;
+    c.vtile = vc + static_cast<size_t>(kt0) * kD;   // kt0 is a multiple of 64
+    c.kl = lds_base + static_cast<uint32_t>(2 * buf * kStageElems + wave * 64 * 8) * 2u;
+    c.vl = c.kl + kStageElems * 2u;
+    c.k_voff = k_voff;
+    c.v_voff = v_voff;
+    return c;
+  };
+  auto issue_tile = [&](int pos) {
+    const TileCopy c = tile_copy(pos);
+#pragma unroll
+    for (int slot = 0; slot < 8; ++slot) c(slot);
+  };
 
+  // The counter of outstanding vector memory operations holds 63: with
+  // narrow workgroups (more chunks per thread) the start's operations and
+  // three tiles' copies could exceed it, so enough of the former land first.
+  constexpr int kStartOps = QCPT + 2 * QT + 1 + 3 * KI + VI;
+  if constexpr (kStartOps + 2 * CPT * (kStages - 1) > 63) wait_vm<63 - 2 * CPT * (kStages - 1)>();
 #pragma unroll
   for (int t = 0; t < kStages - 1; ++t)
     if (t < n_tiles) issue_tile(t);
 
-  // ---- 2. once only tile copies are outstanding the register loads have
-  // landed: the RoPE table for depths 0 .. deepest node of b, then the
-  // queries, rotated at P + depth, times softmax_scale * log2(e), in bf16:
-  // the B operands of the score MFMA
+  // ---- 2. once only tile copies are outstanding, the queries and register
+  // loads have landed: the raw query rows go to registers, the RoPE table
+  // for depths 0 .. deepest node of b takes their place, and the queries,
+  // rotated at P + depth, times softmax_scale * log2(e), in bf16 become the
+  // B operands of the score MFMA
   {
     const int issued = min(n_tiles, kStages - 1);
     static_assert(kStages == 4, "waits below assume three tiles in flight");
@@ -617,26 +684,40 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   }
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) landed(qraw[t][kk]);
     landed(qdep[t]);
     landed(my_anc[t]);
   }
   landed(dep_lane);
 #pragma unroll
-  for (int u = 0; u < KC; ++u) {
+  for (int u = 0; u < KI; ++u) {
     landed(tk_lo[u]);
     landed(tk_hi[u]);
+    landed(t_dep[u]);
   }
 #pragma unroll
-  for (int u = 0; u < VC; ++u) landed(tvv[u]);
-  landed(t_dep);
+  for (int u = 0; u < VI; ++u) landed(tvv[u]);
+  __syncthreads();   // every wavefront's query copies have landed
+  u32x4 qraw[QT][8];   // qraw[t][kk] = raw Q[row][16kk + 8h .. +8]
+  {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const uint16_t* qs = smem + 2 * kStageElems * (kStages - 1);
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+      const int r = wave * 32 * QT + 32 * t + (lane & 31);
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(qs + r * kD + (((2 * kk + h) ^ (r & 15)) << 3));
+        qraw[t][kk] = row_live[t] ? v : z;
+      }
+    }
+  }
+  __syncthreads();   // the query rows are read; the table may overwrite them
   {
     int dmax = lane < n ? clamp_depth(static_cast<int>(dep_lane)) : 0;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) dmax = max(dmax, __shfl_xor(dmax, off));
     const int n_cs = (__builtin_amdgcn_readfirstlane(dmax) + 1) * (kD / 2);
-    const double freq = exp2(p.log2_theta * (-2.0 * (tid & 63) / kD));   // column tid % 64 of every row
+    const double freq = rope_freq(p.log2_theta, tid & 63);   // column tid % 64 of every row
     for (int e = tid; e < n_cs; e += NT)
       cs_tab[e] = p.rope ? rope_cs(P + (e >> 6), freq) : make_float2(1.0f, 0.0f);
   }
@@ -648,8 +729,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       uint4 lo, hi;
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      const u32x4 a = row_live[t] ? qraw[t][kk] : z, c = row_live[t] ? qraw[t][kk + 4] : z;
+      const u32x4 a = qraw[t][kk], c = qraw[t][kk + 4];
       rope8(make_uint4(a[0], a[1], a[2], a[3]), make_uint4(c[0], c[1], c[2], c[3]), cs + 16 * kk, p.scale_log2, lo, hi);
       qf[t][kk] = __builtin_bit_cast(bf16x8, lo);
       qf[t][kk + 4] = __builtin_bit_cast(bf16x8, hi);
@@ -657,54 +737,46 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   }
 
   // Forms the tree part of the staged tile at position pos (< n_masked):
-  // slot P + i holds tree node i (lane i): its key, rotated at
-  // P + depth(i), and its value, written into the stage (and, with `store`,
-  // appended to the cache). Slots past P + n are not this call's keys and
-  // may hold anything: their scores are masked and their values zeroed (a
-  // masked probability is 0, but 0 * NaN is not).
-  auto fill_tree = [&](int pos, bool store) __attribute__((always_inline)) {
+  // slot P + i holds tree node i, whose key (rotated at P + depth(i)) and
+  // value the lane items carry. Slots past P + n are not this call's keys
+  // and may hold anything: their scores are masked and their values zeroed
+  // (a masked probability is 0, but 0 * NaN is not).
+  auto fill_tree = [&](int pos) __attribute__((always_inline)) {
     const int kt0 = tile_k0(pos);
     uint16_t* kd = Ks(pos % kStages);
     uint16_t* vd = Vs(pos % kStages);
     if (kt0 + lane >= key_end) {
 #pragma unroll
-      for (int u = 0; u < VC; ++u)
+      for (int u = 0; u < 16 / WAVES; ++u)
 #pragma unroll
         for (int e = 0; e < 8; ++e) vd[vs_off(8 * (wave + WAVES * u) + e, lane >> 3) + (lane & 7)] = 0;
     }
-    const int slot = P + lane;
-    if (lane < n && slot >= kt0 && slot < kt0 + kKT) {
-      const int key = slot - kt0;
-      const float2* cs = cs_tab + clamp_depth(static_cast<int>(t_dep)) * (kD / 2);
-      uint16_t* kdst = p.k_cache + head_off + static_cast<size_t>(slot) * kD;
 #pragma unroll
-      for (int u = 0; u < KC; ++u) {
-        const int c = wave + WAVES * u;   // dims 8c.. pair with 64 + 8c..
+    for (int u = 0; u < KI; ++u) {
+      const int item = tid + NT * u, node = item >> 3, c = item & 7;   // dims 8c.. pair with 64 + 8c..
+      const int slot = P + node;
+      if (node < n && slot >= kt0 && slot < kt0 + kKT) {
+        const int key = slot - kt0;
         uint4 lo, hi;
         rope8(make_uint4(tk_lo[u][0], tk_lo[u][1], tk_lo[u][2], tk_lo[u][3]),
-              make_uint4(tk_hi[u][0], tk_hi[u][1], tk_hi[u][2], tk_hi[u][3]), cs + 8 * c, 1.0f, lo, hi);
+              make_uint4(tk_hi[u][0], tk_hi[u][1], tk_hi[u][2], tk_hi[u][3]),
+              cs_tab + clamp_depth(static_cast<int>(t_dep[u])) * (kD / 2) + 8 * c, 1.0f, lo, hi);
         *reinterpret_cast<uint4*>(kd + ks_off(key, c)) = lo;
         *reinterpret_cast<uint4*>(kd + ks_off(key, c + 8)) = hi;
-        if (store) {
-          *reinterpret_cast<uint4*>(kdst + 8 * c) = lo;
-          *reinterpret_cast<uint4*>(kdst + 64 + 8 * c) = hi;
-        }
       }
-      uint16_t* vh = p.v_cache + head_off;
+    }
 #pragma unroll
-      for (int u = 0; u < VC; ++u) {
+    for (int u = 0; u < VI; ++u) {
+      const int item = tid + NT * u, node = item >> 4, c = item & 15;
+      const int slot = P + node;
+      if (node < n && slot >= kt0 && slot < kt0 + kKT) {
+        const int key = slot - kt0;
         const uint4 v4 = make_uint4(tvv[u][0], tvv[u][1], tvv[u][2], tvv[u][3]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int d = 8 * (wave + WAVES * u) + e;
-          const uint16_t x = u4_elem(v4, e);
-          vd[vs_off(d, key >> 3) + (key & 7)] = x;
-          if (store) vh[v_cache_off(slot, d)] = x;   // lanes: consecutive slots of row d
-        }
+        for (int e = 0; e < 8; ++e) vd[vs_off(8 * c + e, key >> 3) + (key & 7)] = u4_elem(v4, e);
       }
     }
   };
-
   RowState st[QT];
   auto reset_state = [&](const float (&r)[QT]) {
 #pragma unroll
@@ -726,13 +798,16 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   float mx[QT];
   auto run_pass = [&](auto mode_tag) {
     constexpr int MODE = decltype(mode_tag)::value;
-    auto product = [&](auto masked_tag, int pos) {
+    auto product = [&](auto masked_tag, int pos, const auto& copy) {
       constexpr bool M = decltype(masked_tag)::value;
       const int buf = pos % kStages, rel0 = tile_k0(pos) - P;
-      if constexpr (MODE == 1)
+      if constexpr (MODE == 1) {
         tile_max<QT, M>(mx, Ks(buf), qf, k_addr, h, rel0, my_anc);
-      else
-        tile_product<QT, M, MODE == 2>(st, Ks(buf), Vs(buf), qf, k_addr, v_addr, h, rel0, my_anc);
+#pragma unroll
+        for (int slot = 0; slot < 8; ++slot) copy(slot);
+      } else {
+        tile_product<QT, M, MODE == 2>(st, Ks(buf), Vs(buf), qf, k_addr, v_addr, h, rel0, my_anc, copy);
+      }
     };
     // Waits until the tile at position t has landed, given how many later
     // tiles are in flight (at most kStages - 2).
@@ -753,23 +828,21 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
     for (; t < n_masked; ++t) {
       wait_tile(t);
       __syncthreads();   // tile t has landed for every wave; stage (t-1) % kStages is free
-      // the tree's keys and values (appended to the cache once: by row
-      // block 0, on the first pass)
-      fill_tree(t, MODE == 0 && rb == 0);
+      fill_tree(t);
       __syncthreads();
       if (t + kStages - 1 < n_tiles) issue_tile(t + kStages - 1);
-      product(std::true_type{}, t);
+      product(std::true_type{}, t, NoCopy{});
     }
     for (; t + kStages - 1 < n_tiles; ++t) {
       wait_vm<2 * CPT * (kStages - 2)>();
       __syncthreads();   // tile t has landed for every wave; stage (t-1) % kStages is free
-      issue_tile(t + kStages - 1);
-      product(std::false_type{}, t);
+      // the copy of tile t + kStages - 1 goes out during this product
+      product(std::false_type{}, t, tile_copy(t + kStages - 1));
     }
     for (; t < n_tiles; ++t) {
       wait_tile(t);
       __syncthreads();
-      product(std::false_type{}, t);
+      product(std::false_type{}, t, NoCopy{});
     }
   };
 
@@ -850,6 +923,46 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// tree append: cache slot P + i receives node i's key, rotated at
+// P + depth(i) exactly as the attention kernel rotated it in LDS, and its
+// value. Thread it of nthreads for head (b, g) takes key pairs (node k/64,
+// dims k%64 and 64 + k%64) and value elements (dim v/64, node v%64), so
+// consecutive lanes write consecutive cache addresses. It runs after the
+// attention kernel, which never reads these slots back.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void append_tree(const BfParams& p, int b, int g, int it, int nthreads) {
+  const SeqState sq = seq_state(p, b);
+  if (sq.skip) return;
+  const int n = sq.n, P = sq.P;
+  const size_t head_off = (static_cast<size_t>(b) * p.Hkv + g) * p.cap * kD;
+  for (int k = it; k < n * 64; k += nthreads) {
+    const int i = k >> 6, j = k & 63;
+    const uint16_t* src = p.k_new + ((static_cast<size_t>(b) * p.n_max + i) * p.Hkv + g) * kD;
+    const float xl = bf16_bits_to_f32(src[j]), xh = bf16_bits_to_f32(src[64 + j]);
+    const float2 cs = p.rope ? rope_cs(P + clamp_depth(p.depth[static_cast<size_t>(b) * p.n_max + i]),
+                                       rope_freq(p.log2_theta, j))
+                             : make_float2(1.0f, 0.0f);
+    const uint32_t w = pack_bf16(rope_lo(xl, xh, cs) * 1.0f, rope_hi(xl, xh, cs) * 1.0f);
+    uint16_t* dst = p.k_cache + head_off + static_cast<size_t>(P + i) * kD;
+    dst[j] = static_cast<uint16_t>(w & 0xFFFFu);
+    dst[64 + j] = static_cast<uint16_t>(w >> 16);
+  }
+  for (int v = it; v < kD * 64; v += nthreads) {
+    const int d = v >> 6, i = v & 63;
+    if (i < n)
+      p.v_cache[head_off + v_cache_off(P + i, d)] =
+          p.v_new[((static_cast<size_t>(b) * p.n_max + i) * p.Hkv + g) * kD + d];
+  }
+}
+
+// With one split there is no merge: the append runs alone, grid
+// (kAppendBlocks, Hkv, B), 256 threads.
+constexpr int kAppendBlocks = 32;
+__global__ __launch_bounds__(256) void append_bf16_kernel(BfParams p) {
+  append_tree(p, blockIdx.z, blockIdx.y, blockIdx.x * 256 + threadIdx.x, gridDim.x * 256);
+}
+
+// ---------------------------------------------------------------------------
 // merge: grid (row_blocks * ROWS / 8, Hkv, B), 256 threads; thread = one
 // float4 of one lane's partial (same register order as the main kernel)
 // ---------------------------------------------------------------------------
@@ -858,6 +971,7 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(BfParams p) {
   constexpr int ROWS = WAVES * 32 * QT;
   const int g = blockIdx.y, b = blockIdx.z;
   const int idx = blockIdx.x * 256 + threadIdx.x;
+  append_tree(p, b, g, idx, gridDim.x * 256);
   const int rb = idx / (ROWS * 32);
   const int rem = idx % (ROWS * 32);
   const int lane = rem & 63, slot = rem >> 6;          // slot = (wave * QT + t) * 16 + dt * 4 + i4
@@ -1005,7 +1119,11 @@ hipError_t launch_attention_bf16(const tv_attn_args* a, const AttnPlan& pl, hipS
     default: hipLaunchKernelGGL((attn_bf16_kernel<4, 2>), grid, dim3(256), 0, s, p); break;
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || pl.splits == 1) return e;
+  if (e != hipSuccess) return e;
+  if (pl.splits == 1) {
+    hipLaunchKernelGGL(append_bf16_kernel, dim3(kAppendBlocks, a->Hkv, a->B), dim3(256), 0, s, p);
+    return hipGetLastError();
+  }
   switch (key) {
     case 21: hipLaunchKernelGGL((merge_bf16_kernel<2, 1>), mgrid, dim3(256), 0, s, p); break;
     case 41: hipLaunchKernelGGL((merge_bf16_kernel<4, 1>), mgrid, dim3(256), 0, s, p); break;
