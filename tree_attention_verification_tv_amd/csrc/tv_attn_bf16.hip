@@ -90,9 +90,10 @@ namespace {
 constexpr int kD = 128;                 // head dim (bf16 path)
 constexpr int kKT = 64;                 // keys per LDS stage (= V cache block)
 constexpr int kStageElems = kKT * kD;   // bf16 elements of one K (or V) stage
-constexpr int kStages = 4;              // LDS ring of key tiles (3 in flight)
+constexpr int kStages = 5;              // LDS ring of key tiles
+constexpr int kAhead = 3;               // tiles in flight
 constexpr int kMaxSplits = 8;           // key splits per row block
-constexpr int kCsElems = 64 * 64 * 4;   // LDS elements (bf16 units) of the RoPE table: 64 depths x 64 (cos, sin)
+constexpr int kCsElems = 64 * 64 * 4;   // bf16 units of the RoPE table: 64 depths x 64 (cos, sin) = one stage
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -290,17 +291,19 @@ __device__ __forceinline__ bool key_visible(int rel, uint64_t anc) {
 // issuing these from assembly pins the vector-register form. The compiler
 // does not see them as MFMAs, so hazard_wait() must separate the last one
 // writing a score block from the first vector-ALU read of it.
+// The B operand (the queries, constant over the whole kernel) is read from
+// accumulation registers, which keeps 16 x QT vector registers free.
 __device__ __forceinline__ f32x16 mfma_s_first(const bf16x8& a, const bf16x8& b) {
   f32x16 d;
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
                : "=&v"(d)
-               : "v"(__builtin_bit_cast(u32x4, a)), "v"(__builtin_bit_cast(u32x4, b)));
+               : "v"(__builtin_bit_cast(u32x4, a)), "a"(__builtin_bit_cast(u32x4, b)));
   return d;
 }
 __device__ __forceinline__ void mfma_s_acc(f32x16& d, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
                : "+v"(d)
-               : "v"(__builtin_bit_cast(u32x4, a)), "v"(__builtin_bit_cast(u32x4, b)));
+               : "v"(__builtin_bit_cast(u32x4, a)), "a"(__builtin_bit_cast(u32x4, b)));
 }
 // 32 wait states: more than the MFMA-write -> VALU-read distance required
 // for the longest (16-pass) matrix instruction. The score blocks pass through
@@ -317,19 +320,29 @@ __device__ __forceinline__ void hazard_wait(f32x16 (&x)[QT]) {
 // where invisible): exp2 of the score (minus the row's reference r on the
 // fallback pass; the fast pass takes r = 0), packed to bf16, and added to the
 // lane's row sum exactly as the PV product will weight them.
+// (In two halves, so that a pipelined step can put the exponentials behind
+// one MFMA and the rest behind the next.)
 template <bool MASKED, bool SHIFT>
-__device__ __forceinline__ uint32_t prob_pair(RowState& st, const f32x16& x, int c, int sub, int h, int rel0,
-                                              uint64_t anc) {
+__device__ __forceinline__ f32x2 prob_exp(const RowState& st, const f32x16& x, int c, int sub, int h, int rel0,
+                                          uint64_t anc) {
   float a = SHIFT ? x[2 * c] - st.r : x[2 * c], b = SHIFT ? x[2 * c + 1] - st.r : x[2 * c + 1];
   if (MASKED) {
     const int key = 32 * sub + 16 * ((2 * c) >> 3) + 8 * h + ((2 * c) & 7);
     if (!key_visible(rel0 + key, anc)) a = -INFINITY;
     if (!key_visible(rel0 + key + 1, anc)) b = -INFINITY;
   }
-  const uint32_t w = pack_bf16(__builtin_amdgcn_exp2f(a), __builtin_amdgcn_exp2f(b));
+  return f32x2{__builtin_amdgcn_exp2f(a), __builtin_amdgcn_exp2f(b)};
+}
+__device__ __forceinline__ uint32_t prob_pack(RowState& st, f32x2 e) {
+  const uint32_t w = pack_bf16(e[0], e[1]);
   const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
   st.l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, st.l, false);
   return w;
+}
+template <bool MASKED, bool SHIFT>
+__device__ __forceinline__ uint32_t prob_pair(RowState& st, const f32x16& x, int c, int sub, int h, int rel0,
+                                              uint64_t anc) {
+  return prob_pack(st, prob_exp<MASKED, SHIFT>(st, x, c, sub, h, rel0, anc));
 }
 
 // One staged 64-key tile times the QT query tiles of a wavefront, as 32
@@ -398,6 +411,105 @@ __device__ __forceinline__ void tile_product(RowState (&st)[QT], const uint16_t*
   }
 }
 
+// Cross-tile software pipeline for tiles without masked keys. Iteration t
+// issues four blocks of eight steps (QT MFMAs each), each carrying one
+// probability pair per step on the vector ALU:
+//   A  S half 0 of tile t         probabilities of tile t-1, half 1, pairs 4-7
+//   B  PV half 1 of tile t-1      probabilities of tile t,   half 0, pairs 0-3
+//   C  S half 1 of tile t         probabilities of tile t,   half 0, pairs 4-7
+//   D  PV half 0 of tile t        probabilities of tile t,   half 1, pairs 0-3
+// so no step waits on the vector ALU alone; tile t-1's values are read one
+// iteration after its keys. Without a previous tile (PREV false) block B has
+// no MFMAs and block A no probabilities; pipe_tail finishes the last tile.
+// Fragments are read kLook steps ahead, as in tile_product; copy slots go
+// out every fourth step.
+template <int QT, bool SHIFT, bool PREV, typename Copy>
+__device__ __forceinline__ void pipe_iter(RowState (&st)[QT], f32x16 (&x)[2][QT], uint32_t (&w)[2][QT][8],
+                                          const uint16_t* __restrict__ ks, const uint16_t* __restrict__ vs,
+                                          const uint16_t* __restrict__ vs_prev, const bf16x8 (&qf)[QT][8],
+                                          const int (&k_addr)[8], const int (&v_addr)[4], int h, const Copy& copy) {
+  auto frag_ptr = [&](int f) -> const bf16x8* {
+    const int blk = f >> 3, j = f & 7;
+    if (blk == 0) return reinterpret_cast<const bf16x8*>(ks + k_addr[j]);
+    if (blk == 2) return reinterpret_cast<const bf16x8*>(ks + k_addr[j] + 32 * kD);
+    if (blk == 1) return reinterpret_cast<const bf16x8*>(vs_prev + v_addr[2 + (j & 1)] + (j >> 1) * 32 * kKT);
+    return reinterpret_cast<const bf16x8*>(vs + v_addr[j & 1] + (j >> 1) * 32 * kKT);
+  };
+  auto active = [](int f) { return PREV || (f >> 3) != 1; };
+  bf16x8 fr[32];
+#pragma unroll
+  for (int f = 0; f < kLook; ++f) fr[f] = *frag_ptr(f);
+  // One probability pair per step (query tile j % QT; with QT = 1 every
+  // other step): its two exponentials go behind the step's first MFMA and its
+  // packing and row sum behind the second (with QT = 1, behind the next
+  // step's MFMA), so that neither exceeds the MFMA it overlaps.
+  f32x2 e_pend = {0.0f, 0.0f};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    if (i + kLook < 32 && active(i + kLook)) fr[i + kLook] = *frag_ptr(i + kLook);
+    const int blk = i >> 3, j = i & 7;
+    const int psub = (blk == 0 || blk == 3) ? 1 : 0;      // score half whose probabilities this block forms
+    const bool soft = PREV || blk != 0;
+    const int tq = QT == 2 ? (j & 1) : 0;                 // query tile of this step's pair
+    const int pc = ((blk == 0 || blk == 2) ? 4 : 0) + (j >> 1);
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+      if (blk == 0 || blk == 2) {
+        const int sub = blk >> 1;
+        if (j == 0)
+          x[sub][t] = mfma_s_first(fr[i], qf[t][j]);
+        else
+          mfma_s_acc(x[sub][t], fr[i], qf[t][j]);
+      } else if (blk == 3 || PREV) {
+        const int sub = blk == 1 ? 1 : 0, dt = j >> 1, half = j & 1;
+        const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(w[sub][t][4 * half], w[sub][t][4 * half + 1],
+                                                               w[sub][t][4 * half + 2], w[sub][t][4 * half + 3]));
+        st[t].o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i], pf, st[t].o[dt], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);   // the vector work below goes behind this MFMA
+      if (t == 0) {
+        // the first probabilities read from a score block follow the MFMAs
+        // that wrote it by the hazard distance (this step's first MFMA runs
+        // meanwhile)
+        if (j == 0 && blk == 1) hazard_wait<QT>(x[0]);
+        if (j == 0 && blk == 3) hazard_wait<QT>(x[1]);
+        if (QT == 1 && soft && (j & 1) == 1) w[psub][0][pc] = prob_pack(st[0], e_pend);
+        if (soft && (QT == 2 || (j & 1) == 0)) e_pend = prob_exp<false, SHIFT>(st[tq], x[psub][tq], pc, psub, h, 0, 0ull);
+      } else if (soft) {
+        w[psub][tq][pc] = prob_pack(st[tq], e_pend);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if ((i & 3) == 0) {
+      copy(i >> 2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+// The last tile's remaining work: probabilities of half 1, pairs 4-7, then
+// PV half 1.
+template <int QT, bool SHIFT>
+__device__ __forceinline__ void pipe_tail(RowState (&st)[QT], f32x16 (&x)[2][QT], uint32_t (&w)[2][QT][8],
+                                          const uint16_t* __restrict__ vs, const int (&v_addr)[4], int h) {
+  bf16x8 fr[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    fr[j] = *reinterpret_cast<const bf16x8*>(vs + v_addr[2 + (j & 1)] + (j >> 1) * 32 * kKT);
+#pragma unroll
+  for (int c = 4; c < 8; ++c)
+#pragma unroll
+    for (int t = 0; t < QT; ++t) w[1][t][c] = prob_pair<false, SHIFT>(st[t], x[1][t], c, 1, h, 0, 0ull);
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+      const int dt = j >> 1, half = j & 1;
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(w[1][t][4 * half], w[1][t][4 * half + 1],
+                                                             w[1][t][4 * half + 2], w[1][t][4 * half + 3]));
+      st[t].o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[j], pf, st[t].o[dt], 0, 0, 0);
+    }
+}
+
 // Scores only: raises mx[t] to this lane's max visible score (log2 units) of
 // one staged tile. Used by the fallback that finds each row's exact max.
 template <int QT, bool MASKED>
@@ -408,15 +520,20 @@ __device__ __forceinline__ void tile_max(float (&mx)[QT], const uint16_t* __rest
     bf16x8 ka[8];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) ka[kk] = *reinterpret_cast<const bf16x8*>(ks + k_addr[kk] + sub * 32 * kD);
+    f32x16 x[QT];
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
-      f32x16 x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qf[t][0], f32x16{}, 0, 0, 0);
+      x[t] = mfma_s_first(ka[0], qf[t][0]);
 #pragma unroll
-      for (int kk = 1; kk < 8; ++kk) x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], qf[t][kk], x, 0, 0, 0);
+      for (int kk = 1; kk < 8; ++kk) mfma_s_acc(x[t], ka[kk], qf[t][kk]);
+    }
+    hazard_wait<QT>(x);
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int key = 32 * sub + 16 * (e >> 3) + 8 * h + (e & 7);
-        if (!MASKED || key_visible(rel0 + key, anc[t])) mx[t] = fmaxf(mx[t], x[e]);
+        if (!MASKED || key_visible(rel0 + key, anc[t])) mx[t] = fmaxf(mx[t], x[t][e]);
       }
     }
   }
@@ -454,11 +571,14 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   constexpr int NT = WAVES * 64;
   constexpr int ROWS = WAVES * 32 * QT;      // query rows of the workgroup
   constexpr int CPT = (kKT * kD / 8) / NT;   // 16-byte chunks per thread per K (or V) stage
-  static_assert(2 * CPT * (kStages - 1) <= 63, "vmcnt range");   // (the counter's limit)
-  // (K, V) x stages, then the RoPE table: float2 (cos, sin) of angle
-  // (P + depth) f_j at [depth][j]
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kStages * kStageElems + kCsElems];
-  float2* const cs_tab = reinterpret_cast<float2*>(smem + 2 * kStages * kStageElems);
+  static_assert(2 * CPT * kAhead <= 63, "vmcnt range");   // (the counter's limit)
+  // (K, V) x stages. The last stage starts out as the RoPE table, float2
+  // (cos, sin) of angle (P + depth) f_j at [depth][j], until the tree tiles
+  // are formed; the raw query rows pass through the last two stages before
+  // that.
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kStages * kStageElems];
+  static_assert(kCsElems == 2 * kStageElems, "the table fills one stage");
+  float2* const cs_tab = reinterpret_cast<float2*>(smem + 2 * (kStages - 1) * kStageElems);
 
   // Workgroups are handed to the eight XCDs round-robin by index. When the
   // (sequence, KV head) pairs come in multiples of eight, all workgroups of
@@ -539,8 +659,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   // dead rows and nodes are dropped once the data has landed.
   constexpr int QCPT = ROWS * kD / 8 / NT;              // query chunks per thread
   constexpr int KI = 8 * 64 / NT, VI = 16 * 64 / NT;   // tree items per thread: K pairs, V chunks
-  static_assert(ROWS * kD <= 2 * kStageElems + kCsElems, "query rows must fit the last stage and the table region");
-  const uint32_t lds_q = lds_base + 2u * kStageElems * 2u * (kStages - 1);
+  static_assert(ROWS * kD <= 4 * kStageElems, "query rows must fit the last two stages");
+  const uint32_t lds_q = lds_base + 2u * kStageElems * 2u * (kStages - 2);
   {
     const uint16_t* qb = p.q + static_cast<size_t>(b) * p.n_max * p.Hq * kD;
 #pragma unroll
@@ -664,9 +784,9 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   // narrow workgroups (more chunks per thread) the start's operations and
   // three tiles' copies could exceed it, so enough of the former land first.
   constexpr int kStartOps = QCPT + 2 * QT + 1 + 3 * KI + VI;
-  if constexpr (kStartOps + 2 * CPT * (kStages - 1) > 63) wait_vm<63 - 2 * CPT * (kStages - 1)>();
+  if constexpr (kStartOps + 2 * CPT * kAhead > 63) wait_vm<63 - 2 * CPT * kAhead>();
 #pragma unroll
-  for (int t = 0; t < kStages - 1; ++t)
+  for (int t = 0; t < kAhead; ++t)
     if (t < n_tiles) issue_tile(t);
 
   // ---- 2. once only tile copies are outstanding, the queries and register
@@ -675,8 +795,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   // rotated at P + depth, times softmax_scale * log2(e), in bf16 become the
   // B operands of the score MFMA
   {
-    const int issued = min(n_tiles, kStages - 1);
-    static_assert(kStages == 4, "waits below assume three tiles in flight");
+    const int issued = min(n_tiles, kAhead);
+    static_assert(kAhead == 3, "waits below assume three tiles in flight");
     if (issued >= 3) wait_vm<2 * CPT * 3>();
     else if (issued == 2) wait_vm<2 * CPT * 2>();
     else if (issued == 1) wait_vm<2 * CPT>();
@@ -700,7 +820,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   u32x4 qraw[QT][8];   // qraw[t][kk] = raw Q[row][16kk + 8h .. +8]
   {
     const u32x4 z = {0u, 0u, 0u, 0u};
-    const uint16_t* qs = smem + 2 * kStageElems * (kStages - 1);
+    const uint16_t* qs = smem + 2 * kStageElems * (kStages - 2);
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
       const int r = wave * 32 * QT + 32 * t + (lane & 31);
@@ -712,15 +832,19 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
     }
   }
   __syncthreads();   // the query rows are read; the table may overwrite them
+  int n_cs;          // table entries: depths 0 .. deepest node of b
   {
     int dmax = lane < n ? clamp_depth(static_cast<int>(dep_lane)) : 0;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) dmax = max(dmax, __shfl_xor(dmax, off));
-    const int n_cs = (__builtin_amdgcn_readfirstlane(dmax) + 1) * (kD / 2);
+    n_cs = (__builtin_amdgcn_readfirstlane(dmax) + 1) * (kD / 2);
+  }
+  auto build_table = [&]() {
     const double freq = rope_freq(p.log2_theta, tid & 63);   // column tid % 64 of every row
     for (int e = tid; e < n_cs; e += NT)
       cs_tab[e] = p.rope ? rope_cs(P + (e >> 6), freq) : make_float2(1.0f, 0.0f);
-  }
+  };
+  build_table();
   __syncthreads();
   bf16x8 qf[QT][8];      // qf[t][kk] = rotated, scaled Q[row][16kk + 8h .. +8]
 #pragma unroll
@@ -733,6 +857,14 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
       rope8(make_uint4(a[0], a[1], a[2], a[3]), make_uint4(c[0], c[1], c[2], c[3]), cs + 16 * kk, p.scale_log2, lo, hi);
       qf[t][kk] = __builtin_bit_cast(bf16x8, lo);
       qf[t][kk + 4] = __builtin_bit_cast(bf16x8, hi);
+    }
+    // the operands live in accumulation registers from here on (every score
+    // MFMA reads them from there)
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      u32x4 v = __builtin_bit_cast(u32x4, qf[t][kk]);
+      asm volatile("" : "+a"(v));
+      qf[t][kk] = __builtin_bit_cast(bf16x8, v);
     }
   }
 
@@ -792,12 +924,13 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   for (int t = 0; t < QT; ++t) r_ref[t] = 0.0f;
   reset_state(r_ref);
 
-  // One pass over this split's tiles (the first kStages - 1 already in
-  // flight). MODE 0: p = exp2(s) (fast pass); 1: only raise mx to the row
-  // maxima of the scores; 2: p = exp2(s - r) with r = the row max.
+  // One pass over this split's tiles (the first kAhead already in flight).
+  // MODE 0: p = exp2(s) (fast pass); 1: only raise mx to the row maxima of
+  // the scores; 2: p = exp2(s - r) with r = the row max.
   float mx[QT];
   auto run_pass = [&](auto mode_tag) {
     constexpr int MODE = decltype(mode_tag)::value;
+    constexpr bool SHIFT = MODE == 2;
     auto product = [&](auto masked_tag, int pos, const auto& copy) {
       constexpr bool M = decltype(masked_tag)::value;
       const int buf = pos % kStages, rel0 = tile_k0(pos) - P;
@@ -806,43 +939,87 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
 #pragma unroll
         for (int slot = 0; slot < 8; ++slot) copy(slot);
       } else {
-        tile_product<QT, M, MODE == 2>(st, Ks(buf), Vs(buf), qf, k_addr, v_addr, h, rel0, my_anc, copy);
+        tile_product<QT, M, SHIFT>(st, Ks(buf), Vs(buf), qf, k_addr, v_addr, h, rel0, my_anc, copy);
       }
     };
     // Waits until the tile at position t has landed, given how many later
-    // tiles are in flight (at most kStages - 2).
+    // tiles are in flight (at most kAhead - 1).
     auto wait_tile = [&](int t) {
-      const int later = min(kStages - 2, n_tiles - 1 - t);
-      static_assert(kStages == 4, "waits below assume four stages");
+      const int later = min(kAhead - 1, n_tiles - 1 - t);
+      static_assert(kAhead == 3, "waits below assume three tiles in flight");
       if (later >= 2) wait_vm<2 * CPT * 2>();
       else if (later == 1) wait_vm<2 * CPT>();
       else wait_vm<0>();
     };
-    // A ring of kStages LDS stages, kStages - 1 tiles in flight; position t
-    // lives in stage t % kStages. The tree tiles come first; the steady loop
-    // then sees prefix tiles with kStages - 2 later tiles outstanding, so it
-    // is one straight block; the last kStages - 1 tiles are peeled off.
+    // A ring of kStages LDS stages, kAhead tiles in flight; position t lives
+    // in stage t % kStages, and the copy of position t + kAhead goes out
+    // during iteration t, into the stage of position t - 2 (the barrier at
+    // the top of iteration t has seen every wavefront finish with it). The
+    // tree tiles come first (full products, masked); the rest go through the
+    // cross-tile pipeline (the scores-only pass through plain products), whose
+    // straight steady block sees kAhead - 1 later tiles outstanding.
     // Wavefronts whose rows are all padding compute on their (zero) queries
     // rather than branch around the products.
     int t = 0;
-    for (; t < n_masked; ++t) {
-      wait_tile(t);
-      __syncthreads();   // tile t has landed for every wave; stage (t-1) % kStages is free
-      fill_tree(t);
+    if (n_masked > 0) {
+      // every tree tile is formed before the first product, so the tree's
+      // lane items are not live across a product
+      wait_tile(n_masked - 1);
       __syncthreads();
-      if (t + kStages - 1 < n_tiles) issue_tile(t + kStages - 1);
-      product(std::true_type{}, t, NoCopy{});
-    }
-    for (; t + kStages - 1 < n_tiles; ++t) {
-      wait_vm<2 * CPT * (kStages - 2)>();
-      __syncthreads();   // tile t has landed for every wave; stage (t-1) % kStages is free
-      // the copy of tile t + kStages - 1 goes out during this product
-      product(std::false_type{}, t, tile_copy(t + kStages - 1));
-    }
-    for (; t < n_tiles; ++t) {
-      wait_tile(t);
+      for (int m = 0; m < n_masked; ++m) fill_tree(m);
       __syncthreads();
-      product(std::false_type{}, t, NoCopy{});
+      for (; t < n_masked; ++t) {
+        if (t > 0) {
+          wait_tile(t);
+          __syncthreads();   // every wavefront is done with the stage the next copy takes
+        }
+        if (t + kAhead < n_tiles) issue_tile(t + kAhead);
+        product(std::true_type{}, t, NoCopy{});
+      }
+    }
+    if constexpr (MODE == 1) {
+      for (; t + kAhead < n_tiles; ++t) {
+        wait_vm<2 * CPT * (kAhead - 1)>();
+        __syncthreads();
+        product(std::false_type{}, t, tile_copy(t + kAhead));
+      }
+      for (; t < n_tiles; ++t) {
+        wait_tile(t);
+        __syncthreads();
+        product(std::false_type{}, t, NoCopy{});
+      }
+    } else if (t < n_tiles) {
+      f32x16 x[2][QT];       // score halves
+      uint32_t w[2][QT][8];  // their probabilities, bf16 pairs
+      auto iter = [&](int pos, int prev_pos, const auto& copy) {
+        pipe_iter<QT, SHIFT, true>(st, x, w, Ks(pos % kStages), Vs(pos % kStages), Vs(prev_pos % kStages), qf, k_addr,
+                                   v_addr, h, copy);
+      };
+      // Before the first tile there is no previous tile: its half-1 scores
+      // are -inf (block A turns them into probabilities 0, adding nothing to
+      // the row sums) and its pairs 0-3, normally formed by block D, are 0,
+      // so block B weights the first tile's own values (finite) by 0.
+#pragma unroll
+      for (int q = 0; q < QT; ++q) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x[1][q][e] = -INFINITY;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) w[1][q][c] = 0u;
+      }
+      int prev = t;
+      for (; t + kAhead < n_tiles; ++t) {
+        wait_tile(t);
+        __syncthreads();
+        iter(t, prev, tile_copy(t + kAhead));
+        prev = t;
+      }
+      for (; t < n_tiles; ++t) {
+        wait_tile(t);
+        __syncthreads();
+        iter(t, prev, NoCopy{});
+        prev = t;
+      }
+      pipe_tail<QT, SHIFT>(st, x, w, Vs((n_tiles - 1) % kStages), v_addr, h);
     }
   };
 
@@ -868,12 +1045,15 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   const bool any_redo = reinterpret_cast<const int*>(smem)[0] != 0;
   __syncthreads();
   if (any_redo) {
-    // (rare: the tree's rows are loaded again, by ordinary loads)
+    // (rare: the tree's rows are loaded again, by ordinary loads, and the
+    // RoPE table, overwritten by tiles, is built again)
 #pragma unroll
     for (int t = 0; t < QT; ++t) mx[t] = -INFINITY;
     if (n_masked > 0) load_tree(std::false_type{});
+    build_table();
+    __syncthreads();
 #pragma unroll
-    for (int t = 0; t < kStages - 1; ++t)
+    for (int t = 0; t < kAhead; ++t)
       if (t < n_tiles) issue_tile(t);
     run_pass(std::integral_constant<int, 1>{});
 #pragma unroll
@@ -884,8 +1064,10 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
     reset_state(r_ref);
     __syncthreads();
     if (n_masked > 0) load_tree(std::false_type{});
+    build_table();
+    __syncthreads();
 #pragma unroll
-    for (int t = 0; t < kStages - 1; ++t)
+    for (int t = 0; t < kAhead; ++t)
       if (t < n_tiles) issue_tile(t);
     run_pass(std::integral_constant<int, 2>{});
   }
