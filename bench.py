@@ -218,8 +218,8 @@ def main() -> None:
                    "seed": args.config if args.seed is None else args.seed},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "tv_tree_attention call: prep_bf16_kernel + attn_bf16_kernel + "
-                               "merge_bf16_kernel, HIP events around the call on its stream",
+                     "kernel": "tv_tree_attention call: attn_bf16_kernel + merge_bf16_kernel (split merge "
+                               "and tree append), HIP events around the call on its stream",
                      "algorithmic_bytes_per_launch": ab["total"],
                      "attention_us_mean": attn_mean_s * 1e6,
                      "attention_us_p10": float(np.percentile(attn_ms, 10)) * 1e3,
