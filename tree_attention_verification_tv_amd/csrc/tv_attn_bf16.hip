@@ -93,6 +93,7 @@ constexpr int kStageElems = kKT * kD;   // bf16 elements of one K (or V) stage
 constexpr int kStages = 5;              // LDS ring of key tiles
 constexpr int kAhead = 3;               // tiles in flight
 constexpr int kMaxSplits = 8;           // key splits per row block
+constexpr int kVtStride = 66;           // LDS row of the value transpose in the append (64 nodes + pad)
 constexpr int kCsElems = 64 * 64 * 4;   // bf16 units of the RoPE table: 64 depths x 64 (cos, sin) = one stage
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -1108,11 +1109,11 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
 // tree append: cache slot P + i receives node i's key, rotated at
 // P + depth(i) exactly as the attention kernel rotated it in LDS, and its
 // value. Thread it of nthreads for head (b, g) takes key pairs (node k/64,
-// dims k%64 and 64 + k%64) and value elements (dim v/64, node v%64), so
-// consecutive lanes write consecutive cache addresses. It runs after the
-// attention kernel, which never reads these slots back.
+// dims k%64 and 64 + k%64), so consecutive lanes write consecutive cache
+// addresses; the values go through one block of their own per head. It runs
+// after the attention kernel, which never reads these slots back.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void append_tree(const BfParams& p, int b, int g, int it, int nthreads) {
+__device__ __forceinline__ void append_keys(const BfParams& p, int b, int g, int it, int nthreads) {
   const SeqState sq = seq_state(p, b);
   if (sq.skip) return;
   const int n = sq.n, P = sq.P;
@@ -1129,45 +1130,88 @@ __device__ __forceinline__ void append_tree(const BfParams& p, int b, int g, int
     dst[j] = static_cast<uint16_t>(w & 0xFFFFu);
     dst[64 + j] = static_cast<uint16_t>(w >> 16);
   }
-  for (int v = it; v < kD * 64; v += nthreads) {
-    const int d = v >> 6, i = v & 63;
-    if (i < n)
-      p.v_cache[head_off + v_cache_off(P + i, d)] =
-          p.v_new[((static_cast<size_t>(b) * p.n_max + i) * p.Hkv + g) * kD + d];
+}
+__device__ __forceinline__ void append_values(const BfParams& p, int b, int g, uint16_t (*vt)[kVtStride]) {
+  const SeqState sq = seq_state(p, b);
+  if (sq.skip) return;
+  const int n = sq.n, P = sq.P;
+  const size_t head_off = (static_cast<size_t>(b) * p.Hkv + g) * p.cap * kD;
+  // Values (a block of their own per KV head): node rows are read as whole
+  // 16-byte chunks, transposed through LDS ([d][node]) and written as
+  // head-dim rows of consecutive slots, as the blocked cache holds them: one
+  // 16-byte store per aligned unit of 8 slots inside [P, P + n), single
+  // elements at the ends.
+  const int tid = threadIdx.x;
+  for (int item = tid; item < n * (kD / 8); item += 256) {
+    const int i = item >> 4, c = item & 15;
+    const uint4 v4 = *reinterpret_cast<const uint4*>(p.v_new + ((static_cast<size_t>(b) * p.n_max + i) * p.Hkv + g) * kD + 8 * c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vt[8 * c + e][i] = u4_elem(v4, e);
+  }
+  __syncthreads();
+  const int u0 = P >> 3, n_units = ((P + n + 7) >> 3) - u0;   // 8-slot units touching [P, P + n)
+  for (int idx = tid; idx < kD * n_units; idx += 256) {
+    const int d = idx / n_units, s0 = (u0 + idx % n_units) << 3;
+    uint16_t* dst = p.v_cache + head_off + v_cache_off(s0, d);
+    if (s0 >= P && s0 + 8 <= P + n) {
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = static_cast<uint32_t>(vt[d][s0 - P + 2 * e]) | (static_cast<uint32_t>(vt[d][s0 - P + 2 * e + 1]) << 16);
+      *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+      for (int e = 0; e < 8; ++e)
+        if (s0 + e >= P && s0 + e < P + n) dst[e] = vt[d][s0 + e - P];
+    }
   }
 }
 
 // With one split there is no merge: the append runs alone, grid
 // (kAppendBlocks, Hkv, B), 256 threads.
 constexpr int kAppendBlocks = 32;
+// Block 0 of each KV head appends the values (it is dispatched first).
 __global__ __launch_bounds__(256) void append_bf16_kernel(BfParams p) {
-  append_tree(p, blockIdx.z, blockIdx.y, blockIdx.x * 256 + threadIdx.x, gridDim.x * 256);
+  __shared__ uint16_t vt[kD][kVtStride];
+  if (blockIdx.x == 0)
+    append_values(p, blockIdx.z, blockIdx.y, vt);
+  else
+    append_keys(p, blockIdx.z, blockIdx.y, (blockIdx.x - 1) * 256 + threadIdx.x, (gridDim.x - 1) * 256);
 }
 
 // ---------------------------------------------------------------------------
-// merge: grid (row_blocks * ROWS / 8, Hkv, B), 256 threads; thread = one
-// float4 of one lane's partial (same register order as the main kernel)
+// merge: grid (1 + row_blocks * ROWS / 32, Hkv, B), 256 threads; thread =
+// the four float4 of one (32-row tile, head-dim block) of one lane's partial
+// (same register order as the main kernel); block 0 appends the values
 // ---------------------------------------------------------------------------
 template <int WAVES, int QT>
 __global__ __launch_bounds__(256) void merge_bf16_kernel(BfParams p) {
   constexpr int ROWS = WAVES * 32 * QT;
   const int g = blockIdx.y, b = blockIdx.z;
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  append_tree(p, b, g, idx, gridDim.x * 256);
-  const int rb = idx / (ROWS * 32);
-  const int rem = idx % (ROWS * 32);
-  const int lane = rem & 63, slot = rem >> 6;          // slot = (wave * QT + t) * 16 + dt * 4 + i4
-  const int wt = slot >> 4, dt = (slot >> 2) & 3, i4 = slot & 3;
+  const int idx = (blockIdx.x - 1) * 256 + threadIdx.x;
+  // block 0 of each KV head (dispatched first) appends the tree's values,
+  // the others merge and append the keys
+  __shared__ uint16_t vt[kD][kVtStride];
+  if (blockIdx.x == 0) {
+    append_values(p, b, g, vt);
+    return;
+  }
+  append_keys(p, b, g, idx, (gridDim.x - 1) * 256);
+  // thread = (row block, 32-row tile wt, head-dim block dt, lane): the four
+  // float4 of that lane's (wt, dt) block, which share the lane's (r, l)
+  const int rb = idx / (ROWS * 8);
+  const int rem = idx % (ROWS * 8);
+  const int lane = rem & 63, q = rem >> 6;             // q = wt * 4 + dt
+  const int wt = q >> 2, dt = q & 3;
   const int row = rb * ROWS + wt * 32 + (lane & 31);   // wave * 32 QT + 32 t = 32 wt
   const int rows_all = p.G * p.n_max;
   if (rb >= p.row_blocks || row >= rows_all) return;
   const SeqState sq = seq_state(p, b);
   const int rows_live = sq.skip ? 0 : p.G * sq.n;
   const int head = g * p.G + row % p.G, node = row / p.G;
-  uint16_t* dst = p.out + ((static_cast<size_t>(b) * p.n_max + node) * p.Hq + head) * kD +
-                  32 * dt + 8 * i4 + 4 * (lane >> 5);
+  uint16_t* dst = p.out + ((static_cast<size_t>(b) * p.n_max + node) * p.Hq + head) * kD + 32 * dt + 4 * (lane >> 5);
   if (row >= rows_live) {
-    *reinterpret_cast<uint2*>(dst) = make_uint2(0u, 0u);
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) *reinterpret_cast<uint2*>(dst + 8 * i4) = make_uint2(0u, 0u);
     return;
   }
   const size_t wg0 = ((static_cast<size_t>(b) * p.Hkv + g) * p.row_blocks + rb) * p.splits;
@@ -1178,23 +1222,34 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(BfParams p) {
     ml[ss] = (ss < p.splits) ? p.part_ml[(wg0 + ss) * (ROWS * 2) + wt * 64 + lane] : make_float2(-INFINITY, 0.0f);
     M = fmaxf(M, ml[ss].x);
   }
-  float4 o[kMaxSplits];
+  float4 o[kMaxSplits][4];
 #pragma unroll
   for (int ss = 0; ss < kMaxSplits; ++ss)
-    o[ss] = (ss < p.splits) ? p.part_o[(wg0 + ss) * (ROWS * 32) + slot * 64 + lane] : make_float4(0, 0, 0, 0);
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4)
+      o[ss][i4] = (ss < p.splits) ? p.part_o[(wg0 + ss) * (ROWS * 32) + (wt * 16 + dt * 4 + i4) * 64 + lane]
+                                  : make_float4(0, 0, 0, 0);
   float L = 0.0f;
-  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  float4 acc[4];
+#pragma unroll
+  for (int i4 = 0; i4 < 4; ++i4) acc[i4] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
   for (int ss = 0; ss < kMaxSplits; ++ss) {
     const float w = (ml[ss].x == -INFINITY) ? 0.0f : exp2f(ml[ss].x - M);
     L = fmaf(w, ml[ss].y, L);
-    acc.x = fmaf(w, o[ss].x, acc.x);
-    acc.y = fmaf(w, o[ss].y, acc.y);
-    acc.z = fmaf(w, o[ss].z, acc.z);
-    acc.w = fmaf(w, o[ss].w, acc.w);
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      acc[i4].x = fmaf(w, o[ss][i4].x, acc[i4].x);
+      acc[i4].y = fmaf(w, o[ss][i4].y, acc[i4].y);
+      acc[i4].z = fmaf(w, o[ss][i4].z, acc[i4].z);
+      acc[i4].w = fmaf(w, o[ss][i4].w, acc[i4].w);
+    }
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-  *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16(acc.x * inv, acc.y * inv), pack_bf16(acc.z * inv, acc.w * inv));
+#pragma unroll
+  for (int i4 = 0; i4 < 4; ++i4)
+    *reinterpret_cast<uint2*>(dst + 8 * i4) = make_uint2(pack_bf16(acc[i4].x * inv, acc[i4].y * inv),
+                                                        pack_bf16(acc[i4].z * inv, acc[i4].w * inv));
 }
 
 // Optional launch-shape override for tuning sweeps, read once:
@@ -1293,7 +1348,7 @@ hipError_t launch_attention_bf16(const tv_attn_args* a, const AttnPlan& pl, hipS
 
   dim3 grid(pl.splits * pl.row_blocks * a->Hkv * a->B);
   const int wg_rows = pl.waves * 32 * pl.qt;
-  dim3 mgrid(pl.row_blocks * wg_rows / 8, a->Hkv, a->B);
+  dim3 mgrid(pl.row_blocks * wg_rows / 32 + 1, a->Hkv, a->B);   // (+ the value-append block)
   const int key = pl.waves * 10 + pl.qt;
   switch (key) {
     case 21: hipLaunchKernelGGL((attn_bf16_kernel<2, 1>), grid, dim3(128), 0, s, p); break;
@@ -1303,7 +1358,7 @@ hipError_t launch_attention_bf16(const tv_attn_args* a, const AttnPlan& pl, hipS
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (pl.splits == 1) {
-    hipLaunchKernelGGL(append_bf16_kernel, dim3(kAppendBlocks, a->Hkv, a->B), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(append_bf16_kernel, dim3(kAppendBlocks + 1, a->Hkv, a->B), dim3(256), 0, s, p);
     return hipGetLastError();
   }
   switch (key) {
