@@ -26,10 +26,12 @@ __global__ __launch_bounds__(64) void build_tree_kernel(const int32_t* __restric
                                                         int32_t* __restrict__ err) {
   const int b = blockIdx.x;
   const int i = threadIdx.x;
+  // (the parent load does not wait for the node count: one memory round trip)
+  const int p_in = i < n_max ? parents[static_cast<size_t>(b) * n_max + i] : -1;
   const int n = n_nodes[b];
   const bool n_ok = (n >= 0) && (n <= n_max);
   const bool live = n_ok && (i < n);
-  const int p = live ? parents[static_cast<size_t>(b) * n_max + i] : -1;
+  const int p = live ? p_in : -1;
   const bool ok_i = !live || (i == 0 ? (p == -1) : (p >= 0 && p < i));
   const bool tree_ok = n_ok && __all(ok_i);
 
@@ -72,16 +74,23 @@ __global__ __launch_bounds__(64) void accept_kernel(
   const int b = blockIdx.x;
   const int i = threadIdx.x;
   const size_t row = static_cast<size_t>(b) * n_max;
+  // every load goes out at once (node data does not wait for the count)
+  const bool in_row = i < n_max;
+  const int p_in = in_row ? parents[row + i] : -1;
+  const int tk_in = in_row ? cand_tok[row + i] : 0;
+  const int tg_in = in_row ? tgt[row + i] : 0;
+  const uint64_t a_in = in_row ? anc[row + i] : 0ull;
+  const int dp_in = in_row ? depth[row + i] : 0;
   const int n = n_nodes[b];
   const int e_in = err ? err[b] : 0;
   bool active = (e_in == 0) && (n > 0) && (n <= n_max);
 
   const bool live = active && (i < n);
-  const int p = live ? parents[row + i] : -1;
-  const int tk = live ? cand_tok[row + i] : 0;
-  const int tg = live ? tgt[row + i] : 0;
-  const uint64_t a = live ? anc[row + i] : 0ull;
-  const int dp = live ? depth[row + i] : 0;
+  const int p = live ? p_in : -1;
+  const int tk = live ? tk_in : 0;
+  const int tg = live ? tg_in : 0;
+  const uint64_t a = live ? a_in : 0ull;
+  const int dp = live ? dp_in : 0;
 
   const int tg_parent = __shfl(tg, (p >= 0 && p < 64) ? p : i);
   const bool match = live && (i == 0 || tk == tg_parent);
@@ -145,6 +154,8 @@ __global__ __launch_bounds__(256) void commit_kernel(
 
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
+  // the path goes out with the lengths (one memory round trip)
+  const int src_in = tid < n_max ? path[static_cast<size_t>(b) * n_max + tid] : 0;
   if (tid == 0) {
     const int L = accept_len[b];
     const int P = prefix_len_in[b];
@@ -156,10 +167,9 @@ __global__ __launch_bounds__(256) void commit_kernel(
   __syncthreads();
   const int L = s_L, P = s_P;
   if (tid <= L && tid < n_max && s_ok) {
-    const int src = path[static_cast<size_t>(b) * n_max + tid];
-    s_path[tid] = src;
+    s_path[tid] = src_in;
     // every source must lie in [P, cap)
-    if (src < 0 || P + src >= cap) atomicAnd(&s_ok, 0);
+    if (src_in < 0 || P + src_in >= cap) atomicAnd(&s_ok, 0);
   }
   __syncthreads();
   const bool ok = s_ok;
