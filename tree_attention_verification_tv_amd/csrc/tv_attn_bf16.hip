@@ -1093,8 +1093,10 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   const size_t wg_id = ((static_cast<size_t>(b) * p.Hkv + g) * p.row_blocks + rb) * p.splits + s;
   float4* po = p.part_o + wg_id * (ROWS * 32) + wave * (QT * 16 * 64) + lane;
   float2* pm = p.part_ml + wg_id * (ROWS * 2) + wave * (QT * 64) + lane;
+  // (rows past the live ones are never read by the merge)
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
+    if (!row_live[t]) continue;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
