@@ -227,14 +227,38 @@ struct SeqState {
   int n, P;
   bool cap_bad, skip;
 };
-__device__ __forceinline__ SeqState seq_state(const BfParams& p, int b) {
+__device__ __forceinline__ SeqState make_seq_state(const BfParams& p, int n, int P, int e_in) {
   SeqState q;
-  q.n = p.n_nodes[b];
-  q.P = p.prefix_len[b];
-  const int e_in = p.err[b];
+  q.n = n;
+  q.P = P;
   q.cap_bad = (e_in == 0) && (q.n > 0) && (q.n <= p.n_max) && (q.P < 0 || q.P + q.n > p.cap);
   q.skip = (e_in != 0) || (q.n <= 0) || (q.n > p.n_max) || q.cap_bad;
   return q;
+}
+__device__ __forceinline__ SeqState seq_state(const BfParams& p, int b) {
+  return make_seq_state(p, p.n_nodes[b], p.prefix_len[b], p.err[b]);
+}
+// The same, with the three words loaded together by scalar loads and one
+// wait (the compiler would otherwise wait between them); b is uniform over
+// the workgroup, so the addresses are read from the first lane into scalar
+// registers.
+__device__ __forceinline__ const int* uniform_ptr(const int* a) {
+  const uint64_t v = reinterpret_cast<uint64_t>(a);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const int*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+__device__ __forceinline__ SeqState seq_state_scalar(const BfParams& p, int b) {
+  int n, P, e;
+  asm volatile(
+      "s_load_dword %0, %3, 0x0\n\t"
+      "s_load_dword %1, %4, 0x0\n\t"
+      "s_load_dword %2, %5, 0x0\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&s"(n), "=&s"(P), "=&s"(e)
+      : "s"(uniform_ptr(p.n_nodes + b)), "s"(uniform_ptr(p.prefix_len + b)), "s"(uniform_ptr(p.err + b))
+      : "memory");
+  return make_seq_state(p, n, P, e);
 }
 
 // Rotate-half RoPE of one dimension pair (x_lo, x_hi) by the angle whose
@@ -334,10 +358,11 @@ __device__ __forceinline__ f32x2 prob_exp(const RowState& st, const f32x16& x, i
   }
   return f32x2{__builtin_amdgcn_exp2f(a), __builtin_amdgcn_exp2f(b)};
 }
+// (The row sum adds the two bf16 halves as floats: a dot2 instruction would
+// do it in one, but between matrix instructions it stalls the wavefront.)
 __device__ __forceinline__ uint32_t prob_pack(RowState& st, f32x2 e) {
   const uint32_t w = pack_bf16(e[0], e[1]);
-  const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
-  st.l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, st.l, false);
+  st.l += bf16_lo(w) + bf16_hi(w);
   return w;
 }
 template <bool MASKED, bool SHIFT>
@@ -610,7 +635,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
 
   // The sequence's state is read first (scalar loads, which may not follow
   // the copies: those are opaque memory writes to the compiler).
-  const SeqState sq = seq_state(p, b);
+  const SeqState sq = seq_state_scalar(p, b);
   const int n = sq.n, P = sq.P;
   const int rows_live = sq.skip ? 0 : G * n;
   const int rows_all = G * p.n_max;
@@ -1110,45 +1135,84 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
 // ---------------------------------------------------------------------------
 // tree append: cache slot P + i receives node i's key, rotated at
 // P + depth(i) exactly as the attention kernel rotated it in LDS, and its
-// value. Thread it of nthreads for head (b, g) takes key pairs (node k/64,
-// dims k%64 and 64 + k%64), so consecutive lanes write consecutive cache
-// addresses; the values go through one block of their own per head. It runs
-// after the attention kernel, which never reads these slots back.
+// value. Thread it of nthreads (a multiple of 64) for head (b, g) takes key
+// pairs k = it, it + nthreads, ... (node k/64, dims k%64 and 64 + k%64), two
+// at a time with both pairs' loads issued before either is used, so
+// consecutive lanes write consecutive cache addresses; the values go through
+// one block of their own per head. It runs after the attention kernel, which
+// never reads these slots back.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void append_keys(const BfParams& p, int b, int g, int it, int nthreads) {
-  const SeqState sq = seq_state(p, b);
-  if (sq.skip) return;
-  const int n = sq.n, P = sq.P;
-  const size_t head_off = (static_cast<size_t>(b) * p.Hkv + g) * p.cap * kD;
-  for (int k = it; k < n * 64; k += nthreads) {
-    const int i = k >> 6, j = k & 63;
+struct KeyPairs {
+  uint16_t xl[2], xh[2];
+  int dep[2];
+};
+// Loads the two key pairs k0, k0 + nthreads (clamped to the n_max rows of
+// k_new, not to n, so that they need not wait for the node count).
+__device__ __forceinline__ KeyPairs load_keys(const BfParams& p, int b, int g, int k0, int nthreads) {
+  KeyPairs kp;
+  const int j = k0 & 63;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int i = min((k0 + u * nthreads) >> 6, p.n_max - 1);
     const uint16_t* src = p.k_new + ((static_cast<size_t>(b) * p.n_max + i) * p.Hkv + g) * kD;
-    const float xl = bf16_bits_to_f32(src[j]), xh = bf16_bits_to_f32(src[64 + j]);
-    const float2 cs = p.rope ? rope_cs(P + clamp_depth(p.depth[static_cast<size_t>(b) * p.n_max + i]),
-                                       rope_freq(p.log2_theta, j))
-                             : make_float2(1.0f, 0.0f);
-    const uint32_t w = pack_bf16(rope_lo(xl, xh, cs) * 1.0f, rope_hi(xl, xh, cs) * 1.0f);
-    uint16_t* dst = p.k_cache + head_off + static_cast<size_t>(P + i) * kD;
-    dst[j] = static_cast<uint16_t>(w & 0xFFFFu);
-    dst[64 + j] = static_cast<uint16_t>(w >> 16);
+    kp.xl[u] = src[j];
+    kp.xh[u] = src[64 + j];
+    kp.dep[u] = p.depth[static_cast<size_t>(b) * p.n_max + i];
+  }
+  return kp;
+}
+// Rotates and stores the loaded pairs, then loads and stores the thread's
+// further pairs (k0 += 2 nthreads) until n * 64.
+__device__ __forceinline__ void append_keys(const BfParams& p, const SeqState& sq, int b, int g, int it,
+                                            int nthreads, KeyPairs kp) {
+  if (sq.skip) return;
+  const int j = it & 63;   // the same dimension pair for every k of this thread
+  const size_t head_off = (static_cast<size_t>(b) * p.Hkv + g) * p.cap * kD;
+  const double freq = p.rope ? rope_freq(p.log2_theta, j) : 0.0;
+  for (int k0 = it; k0 < sq.n * 64; k0 += 2 * nthreads) {
+    if (k0 != it) kp = load_keys(p, b, g, k0, nthreads);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int k = k0 + u * nthreads;
+      if (k >= sq.n * 64) break;
+      const int i = k >> 6;
+      const float l = bf16_bits_to_f32(kp.xl[u]), h = bf16_bits_to_f32(kp.xh[u]);
+      const float2 cs = p.rope ? rope_cs(sq.P + clamp_depth(kp.dep[u]), freq) : make_float2(1.0f, 0.0f);
+      const uint32_t w = pack_bf16(rope_lo(l, h, cs) * 1.0f, rope_hi(l, h, cs) * 1.0f);
+      uint16_t* dst = p.k_cache + head_off + static_cast<size_t>(sq.P + i) * kD;
+      dst[j] = static_cast<uint16_t>(w & 0xFFFFu);
+      dst[64 + j] = static_cast<uint16_t>(w >> 16);
+    }
   }
 }
 __device__ __forceinline__ void append_values(const BfParams& p, int b, int g, uint16_t (*vt)[kVtStride]) {
+  // Values (a block of their own per KV head): node rows are read as whole
+  // 16-byte chunks (all of a thread's loads in flight together, clamped to
+  // the n_max rows of v_new so that they need not wait for the node count:
+  // at most TV_MAX_NODES_DEV * 16 = 4 * 256 chunks), transposed through LDS
+  // ([d][node]) and written as head-dim rows of consecutive slots, as the
+  // blocked cache holds them: one 16-byte store per aligned unit of 8 slots
+  // inside [P, P + n), single elements at the ends.
+  static_assert(TV_MAX_NODES_DEV * (kD / 8) == 4 * 256, "four value chunks per thread");
+  const int tid = threadIdx.x;
+  uint4 v4[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = min((tid + 256 * u) >> 4, p.n_max - 1), c = tid & 15;
+    v4[u] = *reinterpret_cast<const uint4*>(p.v_new + ((static_cast<size_t>(b) * p.n_max + i) * p.Hkv + g) * kD + 8 * c);
+  }
+  asm volatile("" ::: "memory");   // the sequence state is read after these loads go out
   const SeqState sq = seq_state(p, b);
   if (sq.skip) return;
   const int n = sq.n, P = sq.P;
   const size_t head_off = (static_cast<size_t>(b) * p.Hkv + g) * p.cap * kD;
-  // Values (a block of their own per KV head): node rows are read as whole
-  // 16-byte chunks, transposed through LDS ([d][node]) and written as
-  // head-dim rows of consecutive slots, as the blocked cache holds them: one
-  // 16-byte store per aligned unit of 8 slots inside [P, P + n), single
-  // elements at the ends.
-  const int tid = threadIdx.x;
-  for (int item = tid; item < n * (kD / 8); item += 256) {
-    const int i = item >> 4, c = item & 15;
-    const uint4 v4 = *reinterpret_cast<const uint4*>(p.v_new + ((static_cast<size_t>(b) * p.n_max + i) * p.Hkv + g) * kD + 8 * c);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) vt[8 * c + e][i] = u4_elem(v4, e);
+  for (int u = 0; u < 4; ++u) {
+    const int item = tid + 256 * u, i = item >> 4, c = item & 15;
+    if (i < n) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vt[8 * c + e][i] = u4_elem(v4[u], e);
+    }
   }
   __syncthreads();
   const int u0 = P >> 3, n_units = ((P + n + 7) >> 3) - u0;   // 8-slot units touching [P, P + n)
@@ -1174,18 +1238,25 @@ constexpr int kAppendBlocks = 32;
 // Block 0 of each KV head appends the values (it is dispatched first).
 __global__ __launch_bounds__(256) void append_bf16_kernel(BfParams p) {
   __shared__ uint16_t vt[kD][kVtStride];
-  if (blockIdx.x == 0)
+  if (blockIdx.x == 0) {
     append_values(p, blockIdx.z, blockIdx.y, vt);
-  else
-    append_keys(p, blockIdx.z, blockIdx.y, (blockIdx.x - 1) * 256 + threadIdx.x, (gridDim.x - 1) * 256);
+  } else {
+    const int it = (blockIdx.x - 1) * 256 + threadIdx.x, nthreads = (gridDim.x - 1) * 256;
+    const KeyPairs kp = load_keys(p, blockIdx.z, blockIdx.y, it, nthreads);
+    asm volatile("" ::: "memory");   // the sequence state is read after these loads go out
+    append_keys(p, seq_state(p, blockIdx.z), blockIdx.z, blockIdx.y, it, nthreads, kp);
+  }
 }
 
 // ---------------------------------------------------------------------------
 // merge: grid (1 + row_blocks * ROWS / 32, Hkv, B), 256 threads; thread =
 // the four float4 of one (32-row tile, head-dim block) of one lane's partial
-// (same register order as the main kernel); block 0 appends the values
+// (same register order as the main kernel); block 0 appends the values.
+// S >= splits is the number of partials a thread loads: split min(s,
+// splits - 1) for s < S, so the loads need no branches; copies past splits
+// get weight 0.
 // ---------------------------------------------------------------------------
-template <int WAVES, int QT>
+template <int WAVES, int QT, int S>
 __global__ __launch_bounds__(256) void merge_bf16_kernel(BfParams p) {
   constexpr int ROWS = WAVES * 32 * QT;
   const int g = blockIdx.y, b = blockIdx.z;
@@ -1197,7 +1268,6 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(BfParams p) {
     append_values(p, b, g, vt);
     return;
   }
-  append_keys(p, b, g, idx, (gridDim.x - 1) * 256);
   // thread = (row block, 32-row tile wt, head-dim block dt, lane): the four
   // float4 of that lane's (wt, dt) block, which share the lane's (r, l)
   const int rb = idx / (ROWS * 8);
@@ -1205,9 +1275,26 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(BfParams p) {
   const int lane = rem & 63, q = rem >> 6;             // q = wt * 4 + dt
   const int wt = q >> 2, dt = q & 3;
   const int row = rb * ROWS + wt * 32 + (lane & 31);   // wave * 32 QT + 32 t = 32 wt
-  const int rows_all = p.G * p.n_max;
-  if (rb >= p.row_blocks || row >= rows_all) return;
+  // The partials are loaded first, for every thread of the grid (the
+  // workspace holds all rows_pad rows of each split; rows the attention
+  // kernel did not write are dropped below), so that their latency overlaps
+  // the key append.
+  const size_t wg0 = ((static_cast<size_t>(b) * p.Hkv + g) * p.row_blocks + rb) * p.splits;
+  float2 ml[S];
+  float4 o[S][4];
+#pragma unroll
+  for (int ss = 0; ss < S; ++ss) {
+    const size_t wg = wg0 + min(ss, p.splits - 1);
+    ml[ss] = p.part_ml[wg * (ROWS * 2) + wt * 64 + lane];
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) o[ss][i4] = p.part_o[wg * (ROWS * 32) + (wt * 16 + dt * 4 + i4) * 64 + lane];
+  }
+  const KeyPairs kp = load_keys(p, b, g, idx, (gridDim.x - 1) * 256);
+  asm volatile("" ::: "memory");   // the sequence state is read after these loads go out
   const SeqState sq = seq_state(p, b);
+  append_keys(p, sq, b, g, idx, (gridDim.x - 1) * 256, kp);
+  const int rows_all = p.G * p.n_max;
+  if (row >= rows_all) return;
   const int rows_live = sq.skip ? 0 : p.G * sq.n;
   const int head = g * p.G + row % p.G, node = row / p.G;
   uint16_t* dst = p.out + ((static_cast<size_t>(b) * p.n_max + node) * p.Hq + head) * kD + 32 * dt + 4 * (lane >> 5);
@@ -1216,28 +1303,16 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(BfParams p) {
     for (int i4 = 0; i4 < 4; ++i4) *reinterpret_cast<uint2*>(dst + 8 * i4) = make_uint2(0u, 0u);
     return;
   }
-  const size_t wg0 = ((static_cast<size_t>(b) * p.Hkv + g) * p.row_blocks + rb) * p.splits;
-  float2 ml[kMaxSplits];
   float M = -INFINITY;
 #pragma unroll
-  for (int ss = 0; ss < kMaxSplits; ++ss) {
-    ml[ss] = (ss < p.splits) ? p.part_ml[(wg0 + ss) * (ROWS * 2) + wt * 64 + lane] : make_float2(-INFINITY, 0.0f);
-    M = fmaxf(M, ml[ss].x);
-  }
-  float4 o[kMaxSplits][4];
-#pragma unroll
-  for (int ss = 0; ss < kMaxSplits; ++ss)
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4)
-      o[ss][i4] = (ss < p.splits) ? p.part_o[(wg0 + ss) * (ROWS * 32) + (wt * 16 + dt * 4 + i4) * 64 + lane]
-                                  : make_float4(0, 0, 0, 0);
+  for (int ss = 0; ss < S; ++ss) M = fmaxf(M, ml[ss].x);   // (the copies repeat a split's value)
   float L = 0.0f;
   float4 acc[4];
 #pragma unroll
   for (int i4 = 0; i4 < 4; ++i4) acc[i4] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
-  for (int ss = 0; ss < kMaxSplits; ++ss) {
-    const float w = (ml[ss].x == -INFINITY) ? 0.0f : exp2f(ml[ss].x - M);
+  for (int ss = 0; ss < S; ++ss) {
+    const float w = (ss >= p.splits || ml[ss].x == -INFINITY) ? 0.0f : exp2f(ml[ss].x - M);
     L = fmaf(w, ml[ss].y, L);
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
@@ -1363,10 +1438,18 @@ hipError_t launch_attention_bf16(const tv_attn_args* a, const AttnPlan& pl, hipS
     hipLaunchKernelGGL(append_bf16_kernel, dim3(kAppendBlocks + 1, a->Hkv, a->B), dim3(256), 0, s, p);
     return hipGetLastError();
   }
-  switch (key) {
-    case 21: hipLaunchKernelGGL((merge_bf16_kernel<2, 1>), mgrid, dim3(256), 0, s, p); break;
-    case 41: hipLaunchKernelGGL((merge_bf16_kernel<4, 1>), mgrid, dim3(256), 0, s, p); break;
-    default: hipLaunchKernelGGL((merge_bf16_kernel<4, 2>), mgrid, dim3(256), 0, s, p); break;
+  const int sk = pl.splits <= 2 ? 2 : (pl.splits <= 4 ? 4 : 8);
+  static_assert(kMaxSplits == 8, "merge instances cover up to eight splits");
+  switch (key * 10 + sk) {
+    case 212: hipLaunchKernelGGL((merge_bf16_kernel<2, 1, 2>), mgrid, dim3(256), 0, s, p); break;
+    case 214: hipLaunchKernelGGL((merge_bf16_kernel<2, 1, 4>), mgrid, dim3(256), 0, s, p); break;
+    case 218: hipLaunchKernelGGL((merge_bf16_kernel<2, 1, 8>), mgrid, dim3(256), 0, s, p); break;
+    case 412: hipLaunchKernelGGL((merge_bf16_kernel<4, 1, 2>), mgrid, dim3(256), 0, s, p); break;
+    case 414: hipLaunchKernelGGL((merge_bf16_kernel<4, 1, 4>), mgrid, dim3(256), 0, s, p); break;
+    case 418: hipLaunchKernelGGL((merge_bf16_kernel<4, 1, 8>), mgrid, dim3(256), 0, s, p); break;
+    case 422: hipLaunchKernelGGL((merge_bf16_kernel<4, 2, 2>), mgrid, dim3(256), 0, s, p); break;
+    case 424: hipLaunchKernelGGL((merge_bf16_kernel<4, 2, 4>), mgrid, dim3(256), 0, s, p); break;
+    default: hipLaunchKernelGGL((merge_bf16_kernel<4, 2, 8>), mgrid, dim3(256), 0, s, p); break;
   }
   return hipGetLastError();
 }
