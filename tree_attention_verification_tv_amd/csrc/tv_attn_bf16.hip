@@ -216,6 +216,8 @@ __device__ __forceinline__ void landed(T& v) { asm volatile("" : "+v"(v)); }
 // outstanding (N must be a compile-time constant).
 template <int N>
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+// Keeps a value's registers allocated (unmodified) up to this point.
+__device__ __forceinline__ void keep_live(const bf16x8& v) { asm volatile("" ::"v"(__builtin_bit_cast(u32x4, v))); }
 // Forces a loaded value to have arrived here (the compiler inserts the wait).
 __device__ __forceinline__ void touch(const bf16x8& v) { asm volatile("" ::"v"(__builtin_bit_cast(u32x4, v))); }
 __device__ __forceinline__ void touch(uint64_t v) { asm volatile("" ::"v"(v)); }
@@ -330,15 +332,16 @@ __device__ __forceinline__ void mfma_s_acc(f32x16& d, const bf16x8& a, const bf1
                : "+v"(d)
                : "v"(__builtin_bit_cast(u32x4, a)), "a"(__builtin_bit_cast(u32x4, b)));
 }
-// 32 wait states: more than the MFMA-write -> VALU-read distance required
-// for the longest (16-pass) matrix instruction. The score blocks pass through
-// the statement, so no read of them can be scheduled above it.
+// 12 wait states: the distance the compiler itself keeps between this
+// matrix instruction writing vector registers and a vector-ALU read of them.
+// The score blocks pass through the statement, so no read of them can be
+// scheduled above it.
 template <int QT>
 __device__ __forceinline__ void hazard_wait(f32x16 (&x)[QT]) {
   if constexpr (QT == 1)
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x[0]));
+    asm volatile("s_nop 11" : "+v"(x[0]));
   else
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x[0]), "+v"(x[1]));
+    asm volatile("s_nop 11" : "+v"(x[0]), "+v"(x[1]));
 }
 
 // Probabilities of elements 2c, 2c+1 of a 32-key score block (masked to 0
@@ -470,6 +473,9 @@ __device__ __forceinline__ void pipe_iter(RowState (&st)[QT], f32x16 (&x)[2][QT]
   // packing and row sum behind the second (with QT = 1, behind the next
   // step's MFMA), so that neither exceeds the MFMA it overlaps.
   f32x2 e_pend = {0.0f, 0.0f};
+  bf16x8 pv_b[QT], pv_prev[QT];   // B operands of this and the previous step's PV MFMAs
+#pragma unroll
+  for (int t = 0; t < QT; ++t) pv_b[t] = pv_prev[t] = bf16x8{};
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
     if (i + kLook < 32 && active(i + kLook)) fr[i + kLook] = *frag_ptr(i + kLook);
@@ -491,6 +497,7 @@ __device__ __forceinline__ void pipe_iter(RowState (&st)[QT], f32x16 (&x)[2][QT]
         const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(w[sub][t][4 * half], w[sub][t][4 * half + 1],
                                                                w[sub][t][4 * half + 2], w[sub][t][4 * half + 3]));
         st[t].o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i], pf, st[t].o[dt], 0, 0, 0);
+        pv_b[t] = pf;
       }
       __builtin_amdgcn_sched_barrier(0);   // the vector work below goes behind this MFMA
       if (t == 0) {
@@ -509,6 +516,18 @@ __device__ __forceinline__ void pipe_iter(RowState (&st)[QT], f32x16 (&x)[2][QT]
     if ((i & 3) == 0) {
       copy(i >> 2);
       __builtin_amdgcn_sched_barrier(0);
+    }
+    // This step's MFMA operands stay allocated through the next step: a
+    // register rewritten (by an LDS read or a vector-ALU result) while an
+    // MFMA that reads it is still executing stalls the wavefront.
+    keep_live(fr[i]);
+    if (i > 0) keep_live(fr[i - 1]);
+    const bool pv_now = blk == 3 || (blk == 1 && PREV);
+    const bool pv_before = i > 0 && (((i - 1) >> 3) == 3 || (((i - 1) >> 3) == 1 && PREV));
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+      if (pv_before) keep_live(pv_prev[t]);
+      if (pv_now) pv_prev[t] = pv_b[t];
     }
   }
 }
