@@ -827,26 +827,26 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
 
   // The counter of outstanding vector memory operations holds 63: with
   // narrow workgroups (more chunks per thread) the start's operations and
-  // three tiles' copies could exceed it, so enough of the former land first.
+  // a tile's copies could exceed it, so enough of the former land first.
+  // Only the first tile goes out with them: at the start every compute unit
+  // loads at once, and a wavefront issuing more copies would stall in the
+  // issue until most of them have arrived, with its RoPE work still ahead.
+  // Tile 1 goes out once the query rows are in registers, tile 2 after the
+  // RoPE, so that work overlaps the first tiles' transfer.
   constexpr int kStartOps = QCPT + 2 * QT + 1 + 3 * KI + VI;
-  if constexpr (kStartOps + 2 * CPT * kAhead > 63) wait_vm<63 - 2 * CPT * kAhead>();
-#pragma unroll
-  for (int t = 0; t < kAhead; ++t)
-    if (t < n_tiles) issue_tile(t);
+  static_assert(kAhead == 3, "the start issues three tiles");
+  if constexpr (kStartOps + 2 * CPT > 63) wait_vm<63 - 2 * CPT>();
+  if (n_tiles > 0) issue_tile(0);
 
-  // ---- 2. once only tile copies are outstanding, the queries and register
-  // loads have landed: the raw query rows go to registers, the RoPE table
-  // for depths 0 .. deepest node of b takes their place, and the queries,
-  // rotated at P + depth, times softmax_scale * log2(e), in bf16 become the
-  // B operands of the score MFMA
-  {
-    const int issued = min(n_tiles, kAhead);
-    static_assert(kAhead == 3, "waits below assume three tiles in flight");
-    if (issued >= 3) wait_vm<2 * CPT * 3>();
-    else if (issued == 2) wait_vm<2 * CPT * 2>();
-    else if (issued == 1) wait_vm<2 * CPT>();
-    else wait_vm<0>();
-  }
+  // ---- 2. once only the first tile's copies are outstanding, the queries
+  // and register loads have landed: the raw query rows go to registers, the
+  // RoPE table for depths 0 .. deepest node of b takes their place, and the
+  // queries, rotated at P + depth, times softmax_scale * log2(e), in bf16
+  // become the B operands of the score MFMA
+  if (n_tiles > 0)
+    wait_vm<2 * CPT>();
+  else
+    wait_vm<0>();
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
     landed(qdep[t]);
@@ -876,6 +876,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
       }
     }
   }
+  if (n_tiles > 1) issue_tile(1);
   __syncthreads();   // the query rows are read; the table may overwrite them
   int n_cs;          // table entries: depths 0 .. deepest node of b
   {
@@ -912,6 +913,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
       qf[t][kk] = __builtin_bit_cast(bf16x8, v);
     }
   }
+  if (n_tiles > 2) issue_tile(2);
 
   // Forms the tree part of the staged tile at position pos (< n_masked):
   // slot P + i holds tree node i, whose key (rotated at P + depth(i)) and
