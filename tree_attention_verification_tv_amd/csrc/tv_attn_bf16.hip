@@ -617,13 +617,13 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   constexpr int ROWS = WAVES * 32 * QT;      // query rows of the workgroup
   constexpr int CPT = (kKT * kD / 8) / NT;   // 16-byte chunks per thread per K (or V) stage
   static_assert(2 * CPT * kAhead <= 63, "vmcnt range");   // (the counter's limit)
-  // (K, V) x stages. The last stage starts out as the RoPE table, float2
-  // (cos, sin) of angle (P + depth) f_j at [depth][j], until the tree tiles
-  // are formed; the raw query rows pass through the last two stages before
-  // that.
+  // (K, V) x stages. At the start, stage 2 holds the RoPE table, float2
+  // (cos, sin) of angle (P + depth) f_j at [depth][j], until tile 2 goes
+  // out, and the raw query rows pass through the last two stages.
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kStages * kStageElems];
   static_assert(kCsElems == 2 * kStageElems, "the table fills one stage");
-  float2* const cs_tab = reinterpret_cast<float2*>(smem + 2 * (kStages - 1) * kStageElems);
+  static_assert(kStages >= 5 && kAhead == 3, "the table's stage is free until tile 2 goes out");
+  float2* const cs_tab = reinterpret_cast<float2*>(smem + 2 * 2 * kStageElems);
 
   // Workgroups are handed to the eight XCDs round-robin by index. When the
   // (sequence, KV head) pairs come in multiples of eight, all workgroups of
@@ -652,8 +652,39 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   const int r0 = rb0 + wave * 32 * QT;       // first row of this wavefront
   const uint32_t lds_base = lds_addr(smem);
 
-  // The sequence's state is read first (scalar loads, which may not follow
-  // the copies: those are opaque memory writes to the compiler).
+  // ---- 1. loads that need only the launch indices go out first: the
+  // depths of this wavefront's rows' nodes and of node `lane` (for the
+  // deepest node of b), then the workgroup's query rows, raw, copied straight
+  // into LDS (the last two ring stages, idle until the queries are read):
+  // chunk c = row c/16, position c%16, holding the row's 16-byte piece
+  // (c%16) ^ (row%16), so that reads in operand order (one piece of 32
+  // consecutive rows) hit distinct banks. The sequence's state (three scalar
+  // loads) is read while they are in flight. Every address is valid (node
+  // indices are clamped to n_max), so nothing branches; dead rows and nodes
+  // are dropped once the data has landed.
+  int my_row[QT];
+  uint32_t qdep[QT];
+#pragma unroll
+  for (int t = 0; t < QT; ++t) {
+    my_row[t] = r0 + 32 * t + (lane & 31);
+    qdep[t] = ld_b32(p.depth + static_cast<size_t>(b) * p.n_max + min(my_row[t] / G, p.n_max - 1));
+  }
+  uint32_t dep_lane = ld_b32(p.depth + static_cast<size_t>(b) * p.n_max + min(lane, p.n_max - 1));
+  constexpr int kDepOps = QT + 1;
+  constexpr int QCPT = ROWS * kD / 8 / NT;              // query chunks per thread
+  static_assert(ROWS * kD <= 4 * kStageElems, "query rows must fit the last two stages");
+  const uint32_t lds_q = lds_base + 2u * kStageElems * 2u * (kStages - 2);
+  {
+    const uint16_t* qb = p.q + static_cast<size_t>(b) * p.n_max * p.Hq * kD;
+#pragma unroll
+    for (int j = 0; j < QCPT; ++j) {
+      const int c = j * NT + tid, r = c >> 4, piece = (c & 15) ^ (r & 15);
+      const int row = rb0 + r, node = min(row / G, p.n_max - 1);
+      const uint32_t voff = static_cast<uint32_t>(((node * p.Hq + g * G + row % G) * kD + 8 * piece) * 2);
+      dma16(qb, voff, lds_q + static_cast<uint32_t>(j * NT + wave * 64) * 16u);
+    }
+  }
+
   const SeqState sq = seq_state_scalar(p, b);
   const int n = sq.n, P = sq.P;
   const int rows_live = sq.skip ? 0 : G * n;
@@ -663,6 +694,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
 
   if (rb0 >= rows_live) {
     // nothing live in this row block; with splits the merge writes the zeros
+    // (the query copies land before the workgroup's LDS is given up)
+    wait_vm<0>();
     if (p.splits == 1) {
       for (int r = rb0 + tid / 16; r < min(rb0 + ROWS, rows_all); r += NT / 16) {
         const int i = r / G, head = g * G + r % G;
@@ -671,6 +704,13 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
       }
     }
     return;
+  }
+  bool row_live[QT];
+  uint64_t my_anc[QT];
+#pragma unroll
+  for (int t = 0; t < QT; ++t) {
+    row_live[t] = my_row[t] < rows_live;
+    my_anc[t] = 0;
   }
 
   // Keys of b: slots [0, P + n), in aligned 64-key tiles shared out over the
@@ -688,46 +728,13 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   int n_masked = 0;
   while (n_masked < n_tiles && tile_k0(n_masked) + kKT > P) ++n_masked;
 
-  // ---- 1. everything the start needs goes out before the tile copies
-  // (vector memory operations complete in order, so anything queued behind
-  // the copies would wait for all of them):
-  //  * the workgroup's query rows, raw, copied straight into LDS (the last
-  //    ring stage and the RoPE table's region, both idle until the queries
-  //    are read): chunk c = row c/16, position c%16, holding the row's 16-byte
-  //    piece (c%16) ^ (row%16), so that reads in operand order (one piece of
-  //    32 consecutive rows) hit distinct banks;
-  //  * register loads: the depths of this wavefront's rows' nodes and of
-  //    node `lane` (for the deepest node of b); with tree tiles, the tree's
-  //    keys and values in 16-byte chunks (lane items: node, chunk) with their
-  //    nodes' depths, and the ancestor masks of this wavefront's rows.
-  // Every address is valid (node indices are clamped), so nothing branches;
-  // dead rows and nodes are dropped once the data has landed.
-  constexpr int QCPT = ROWS * kD / 8 / NT;              // query chunks per thread
+  // With tree tiles, the tree's keys and values in 16-byte chunks (lane
+  // items: node, chunk) with their nodes' depths, and the ancestor masks of
+  // this wavefront's rows, also before the tile copies (vector memory
+  // operations complete in order, so anything queued behind the copies would
+  // wait for all of them).
   constexpr int KI = 8 * 64 / NT, VI = 16 * 64 / NT;   // tree items per thread: K pairs, V chunks
-  static_assert(ROWS * kD <= 4 * kStageElems, "query rows must fit the last two stages");
-  const uint32_t lds_q = lds_base + 2u * kStageElems * 2u * (kStages - 2);
-  {
-    const uint16_t* qb = p.q + static_cast<size_t>(b) * p.n_max * p.Hq * kD;
-#pragma unroll
-    for (int j = 0; j < QCPT; ++j) {
-      const int c = j * NT + tid, r = c >> 4, piece = (c & 15) ^ (r & 15);
-      const int row = rb0 + r, node = min(row / G, p.n_max - 1);
-      const uint32_t voff = static_cast<uint32_t>(((node * p.Hq + g * G + row % G) * kD + 8 * piece) * 2);
-      dma16(qb, voff, lds_q + static_cast<uint32_t>(j * NT + wave * 64) * 16u);
-    }
-  }
-  int my_row[QT];
-  bool row_live[QT];
-  uint32_t qdep[QT];
-  uint64_t my_anc[QT];
-#pragma unroll
-  for (int t = 0; t < QT; ++t) {
-    my_row[t] = r0 + 32 * t + (lane & 31);
-    row_live[t] = my_row[t] < rows_live;
-    my_anc[t] = 0;
-    qdep[t] = ld_b32(p.depth + static_cast<size_t>(b) * p.n_max + min(my_row[t] / G, p.n_max - 1));
-  }
-  uint32_t dep_lane = ld_b32(p.depth + static_cast<size_t>(b) * p.n_max + min(lane, p.n_max - 1));
+  constexpr int kTreeOps = 3 * KI + VI + QT;
   u32x4 tk_lo[KI], tk_hi[KI], tvv[VI];
   uint32_t t_dep[KI];
   auto load_tree = [&](auto asm_tag) __attribute__((always_inline)) {
@@ -833,26 +840,57 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   // issue until most of them have arrived, with its RoPE work still ahead.
   // Tile 1 goes out once the query rows are in registers, tile 2 after the
   // RoPE, so that work overlaps the first tiles' transfer.
-  constexpr int kStartOps = QCPT + 2 * QT + 1 + 3 * KI + VI;
+  constexpr int kStartOps = kDepOps + QCPT + kTreeOps;
   static_assert(kAhead == 3, "the start issues three tiles");
   if constexpr (kStartOps + 2 * CPT > 63) wait_vm<63 - 2 * CPT>();
   if (n_tiles > 0) issue_tile(0);
 
-  // ---- 2. once only the first tile's copies are outstanding, the queries
-  // and register loads have landed: the raw query rows go to registers, the
-  // RoPE table for depths 0 .. deepest node of b takes their place, and the
-  // queries, rotated at P + depth, times softmax_scale * log2(e), in bf16
-  // become the B operands of the score MFMA
+  // ---- 2. the RoPE table for depths 0 .. deepest node of b, float2
+  // (cos, sin) of angle (P + depth) f_j at [depth][j], is built in stage 2
+  // (idle until tile 2 goes out) as soon as the depths have landed, while
+  // the queries are still in flight.
+  if constexpr (kStartOps + 2 * CPT <= 63) {
+    if (n_masked > 0)
+      wait_vm<QCPT + kTreeOps + 2 * CPT>();
+    else if (n_tiles > 0)
+      wait_vm<QCPT + 2 * CPT>();
+    else
+      wait_vm<QCPT>();
+  } else {
+    // (the guard above left an unknown count: wait for all but tile 0)
+    if (n_tiles > 0)
+      wait_vm<2 * CPT>();
+    else
+      wait_vm<0>();
+  }
+#pragma unroll
+  for (int t = 0; t < QT; ++t) landed(qdep[t]);
+  landed(dep_lane);
+  int n_cs;          // table entries: depths 0 .. deepest node of b
+  {
+    int dmax = lane < n ? clamp_depth(static_cast<int>(dep_lane)) : 0;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) dmax = max(dmax, __shfl_xor(dmax, off));
+    n_cs = (__builtin_amdgcn_readfirstlane(dmax) + 1) * (kD / 2);
+  }
+  auto build_table = [&]() {
+    const double freq = rope_freq(p.log2_theta, tid & 63);   // column tid % 64 of every row
+    for (int e = tid; e < n_cs; e += NT)
+      cs_tab[e] = p.rope ? rope_cs(P + (e >> 6), freq) : make_float2(1.0f, 0.0f);
+  };
+  build_table();
+
+  // ---- 3. once only the first tile's copies are outstanding, the queries
+  // and the tree's register loads have landed: the raw query rows go to
+  // registers, and the queries, rotated at P + depth, times softmax_scale *
+  // log2(e), in bf16, become the B operands of the score MFMA; the tree's
+  // keys are rotated at P + depth(node) in their registers.
   if (n_tiles > 0)
     wait_vm<2 * CPT>();
   else
     wait_vm<0>();
 #pragma unroll
-  for (int t = 0; t < QT; ++t) {
-    landed(qdep[t]);
-    landed(my_anc[t]);
-  }
-  landed(dep_lane);
+  for (int t = 0; t < QT; ++t) landed(my_anc[t]);
 #pragma unroll
   for (int u = 0; u < KI; ++u) {
     landed(tk_lo[u]);
@@ -861,7 +899,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   }
 #pragma unroll
   for (int u = 0; u < VI; ++u) landed(tvv[u]);
-  __syncthreads();   // every wavefront's query copies have landed
+  __syncthreads();   // every wavefront's query copies have landed, and the table is complete
   u32x4 qraw[QT][8];   // qraw[t][kk] = raw Q[row][16kk + 8h .. +8]
   {
     const u32x4 z = {0u, 0u, 0u, 0u};
@@ -877,21 +915,6 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
     }
   }
   if (n_tiles > 1) issue_tile(1);
-  __syncthreads();   // the query rows are read; the table may overwrite them
-  int n_cs;          // table entries: depths 0 .. deepest node of b
-  {
-    int dmax = lane < n ? clamp_depth(static_cast<int>(dep_lane)) : 0;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) dmax = max(dmax, __shfl_xor(dmax, off));
-    n_cs = (__builtin_amdgcn_readfirstlane(dmax) + 1) * (kD / 2);
-  }
-  auto build_table = [&]() {
-    const double freq = rope_freq(p.log2_theta, tid & 63);   // column tid % 64 of every row
-    for (int e = tid; e < n_cs; e += NT)
-      cs_tab[e] = p.rope ? rope_cs(P + (e >> 6), freq) : make_float2(1.0f, 0.0f);
-  };
-  build_table();
-  __syncthreads();
   bf16x8 qf[QT][8];      // qf[t][kk] = rotated, scaled Q[row][16kk + 8h .. +8]
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
@@ -913,11 +936,27 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
       qf[t][kk] = __builtin_bit_cast(bf16x8, v);
     }
   }
+  // Tree keys, lane item u: dims 8c.. and 64 + 8c.. of node item / 8, rotated
+  // in place (the cache append repeats this rotation bit for bit).
+  auto rope_tree = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < KI; ++u) {
+      const int c = (tid + NT * u) & 7;
+      uint4 lo, hi;
+      rope8(make_uint4(tk_lo[u][0], tk_lo[u][1], tk_lo[u][2], tk_lo[u][3]),
+            make_uint4(tk_hi[u][0], tk_hi[u][1], tk_hi[u][2], tk_hi[u][3]),
+            cs_tab + clamp_depth(static_cast<int>(t_dep[u])) * (kD / 2) + 8 * c, 1.0f, lo, hi);
+      tk_lo[u] = u32x4{lo.x, lo.y, lo.z, lo.w};
+      tk_hi[u] = u32x4{hi.x, hi.y, hi.z, hi.w};
+    }
+  };
+  if (n_masked > 0) rope_tree();
+  __syncthreads();   // every wavefront is done with the table: tile 2 overwrites it
   if (n_tiles > 2) issue_tile(2);
 
   // Forms the tree part of the staged tile at position pos (< n_masked):
-  // slot P + i holds tree node i, whose key (rotated at P + depth(i)) and
-  // value the lane items carry. Slots past P + n are not this call's keys
+  // slot P + i holds tree node i, whose key (already rotated at P +
+  // depth(i)) and value the lane items carry. Slots past P + n are not this call's keys
   // and may hold anything: their scores are masked and their values zeroed
   // (a masked probability is 0, but 0 * NaN is not).
   auto fill_tree = [&](int pos) __attribute__((always_inline)) {
@@ -936,12 +975,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
       const int slot = P + node;
       if (node < n && slot >= kt0 && slot < kt0 + kKT) {
         const int key = slot - kt0;
-        uint4 lo, hi;
-        rope8(make_uint4(tk_lo[u][0], tk_lo[u][1], tk_lo[u][2], tk_lo[u][3]),
-              make_uint4(tk_hi[u][0], tk_hi[u][1], tk_hi[u][2], tk_hi[u][3]),
-              cs_tab + clamp_depth(static_cast<int>(t_dep[u])) * (kD / 2) + 8 * c, 1.0f, lo, hi);
-        *reinterpret_cast<uint4*>(kd + ks_off(key, c)) = lo;
-        *reinterpret_cast<uint4*>(kd + ks_off(key, c + 8)) = hi;
+        *reinterpret_cast<u32x4*>(kd + ks_off(key, c)) = tk_lo[u];
+        *reinterpret_cast<u32x4*>(kd + ks_off(key, c + 8)) = tk_hi[u];
       }
     }
 #pragma unroll
@@ -1099,6 +1134,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
     if (n_masked > 0) load_tree(std::false_type{});
     build_table();
     __syncthreads();
+    if (n_masked > 0) rope_tree();
+    __syncthreads();
 #pragma unroll
     for (int t = 0; t < kAhead; ++t)
       if (t < n_tiles) issue_tile(t);
@@ -1112,6 +1149,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
     __syncthreads();
     if (n_masked > 0) load_tree(std::false_type{});
     build_table();
+    __syncthreads();
+    if (n_masked > 0) rope_tree();
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < kAhead; ++t)
