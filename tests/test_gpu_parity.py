@@ -292,3 +292,33 @@ def test_scores_far_above_the_root_reference():
     res = run_step(w, d)
     check_step(w, res)
     check_commit(w, res, d["k_cache"], d["v_cache"])
+
+
+def test_large_values_take_the_bf16_partials():
+    """With several key splits, each split's rows are stored as the output
+    divided by the row sum in 16 bits: fp16 unless a row's largest magnitude
+    reaches 2^15, then bf16. The values of one KV head are scaled by 2^17
+    (bf16 rows) and of another by 2^11 (fp16 rows near the range limit);
+    scaling by a power of two is exact in bf16 and the attention output
+    scales with the values, so the bf16 bound applies relative to the scale."""
+    print("[gpu] large values in split partials", flush=True)
+    w = generate(3, B=2, prefix=1100)
+    G = w.Hq // w.Hkv
+    scales = {2: 2.0 ** 17, 5: 2.0 ** 11}
+    for g, sc in scales.items():
+        w.v_cache[:, g] = f32_to_bf16_bits(bf16_bits_to_f32(w.v_cache[:, g]) * np.float32(sc))
+        w.v_new[:, :, g] = f32_to_bf16_bits(bf16_bits_to_f32(w.v_new[:, :, g]) * np.float32(sc))
+    d = upload(w, DEV)
+    res = run_step(w, d)
+    ref_anc, ref_depth, ref_err = oracle.build_tree(w.parents, w.n_nodes)
+    for b in range(w.B):
+        inp = w.oracle_inputs(b)
+        out, _, _, _ = oracle.tree_attention(inp["q"], inp["k_new"], inp["v_new"], inp["k_cache"],
+                                             inp["v_cache"], inp["prefix_len"], inp["n_nodes"],
+                                             inp["parents"], w.rope_theta, 0.0, err_in=ref_err[b:b + 1])
+        for g in range(w.Hkv):
+            sl = slice(g * G, (g + 1) * G)
+            err = float(np.abs(res["out"][b, :, sl] - out[0, :, sl]).max())
+            bound = tolerance(w.dtype) * scales.get(g, 1.0)
+            assert err <= bound, (b, g, err, bound)
+    check_commit(w, res, d["k_cache"], d["v_cache"])

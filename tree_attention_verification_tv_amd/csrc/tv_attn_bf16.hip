@@ -16,7 +16,7 @@
 //          QT MFMAs. The keys of b are slots [0, P + n) of the cache: the
 //          prefix, then the tree, cut into 64-key tiles that the splits share
 //          out. Tiles are copied straight into LDS (global_load_lds into a
-//          ring of four stages, three tiles in flight), so the copies cost no
+//          ring of five stages, three tiles in flight), so the copies cost no
 //          registers and no LDS writes. The copies are issued from inline
 //          assembly: the compiler then does not see an LDS write it cannot
 //          tell apart from the fragment reads, and does not drain every copy
@@ -44,9 +44,8 @@
 //          branch in the tile loop. A row whose sum left [2^-60, 2^62] is
 //          caught at the end; the workgroup then finds every row's exact max
 //          in a scores-only pass and redoes the pass with p = exp2(s - max)
-//          (exact for any score range). Row sums are dot products of the
-//          bf16 probabilities with ones, i.e. exactly the weights the PV
-//          product used.
+//          (exact for any score range). Row sums add up the bf16
+//          probabilities, i.e. exactly the weights the PV product used.
 //
 //          The score MFMA reads K rows in a permuted order (row m of a 32-key
 //          block is key perm(m)), so each lane half holds 8 CONSECUTIVE keys
@@ -61,9 +60,11 @@
 //          key j >= P is visible to a row iff bit j - P of its node's
 //          ancestor mask is set, and value rows past P + n are zeroed.
 //
-//   merge  with several splits, each writes (reference, row sum,
-//          unnormalised output) to the workspace in register order; the merge
-//          combines them in split order (deterministic) and writes the rows.
+//   merge  with several splits, each writes (reference, row sum) in fp32
+//          and its output divided by the row sum in 16 bits (fp16, or bf16
+//          for a row beyond fp16's range) to the workspace in register order;
+//          the merge combines them in split order (deterministic) with fp32
+//          weights and sums and writes the rows.
 //          It also appends the tree to cache slots P + i (keys rotated in the
 //          same rounding order as in LDS); with one split a small kernel does
 //          only that. The attention kernel never reads those slots back, and
@@ -112,7 +113,7 @@ struct BfParams {
   const int32_t* depth;
   int32_t* err;
   uint16_t* out;
-  float4* part_o;    // split partials, register order (see the main epilogue)
+  uint4* part_o;     // split partials, 16-bit, register order (see the main epilogue)
   float2* part_ml;   // split (reference, row sum) per lane
   int n_max, Hq, Hkv, G, cap;
   int splits, row_blocks;
@@ -128,6 +129,15 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 }
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+// Two floats -> packed fp16 pair (round to nearest even), and back.
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+}
+__device__ __forceinline__ f32x2 unpack_f16(uint32_t w) {
+  return __builtin_convertvector(__builtin_bit_cast(f16x2, w), f32x2);
+}
 
 __device__ __forceinline__ uint16_t u4_elem(const uint4& v, int t) {
   const uint32_t w = (t < 2) ? v.x : (t < 4) ? v.y : (t < 6) ? v.z : v.w;
@@ -1171,24 +1181,45 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
     write_rows<QT>(p, b, g, r0, rows_live, rows_all, lane, o, l_row);
     return;
   }
-  // Split partial in register order: the float4 of (wave, t, dt, i4) for
-  // lane l sits at (((wave * QT + t) * 16 + dt * 4 + i4) * 64 + l) within
-  // this workgroup's block; the (r, l) pair of (wave, t) for lane l at
-  // ((wave * QT + t) * 64 + l). Blocks are ordered (b, g, rb, s).
+  // Split partial, per row: the output divided by the split's row sum (a
+  // convex combination of value rows, so bounded by the largest value
+  // element), as 16-bit floats: fp16 when the row's largest magnitude is
+  // below 2^15, bf16 otherwise; the sign of the stored row sum tells which.
+  // Register order: the 16 bytes of (wave, t, dt, half j) for lane l sit at
+  // (((wave * QT + t) * 8 + dt * 2 + j) * 64 + l) within this workgroup's
+  // block (elements 8j .. 8j + 7 of the lane's dt accumulator); the (r, +-l)
+  // pair of (wave, t) for lane l at ((wave * QT + t) * 64 + l). Blocks are
+  // ordered (b, g, rb, s).
   const size_t wg_id = ((static_cast<size_t>(b) * p.Hkv + g) * p.row_blocks + rb) * p.splits + s;
-  float4* po = p.part_o + wg_id * (ROWS * 32) + wave * (QT * 16 * 64) + lane;
+  uint4* po = p.part_o + wg_id * (ROWS * 16) + wave * (QT * 8 * 64) + lane;
   float2* pm = p.part_ml + wg_id * (ROWS * 2) + wave * (QT * 64) + lane;
   // (rows past the live ones are never read by the merge)
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
     if (!row_live[t]) continue;
+    const float inv = l_row[t] > 0.0f ? 1.0f / l_row[t] : 0.0f;
+    float amax = 0.0f;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4)
-        po[(t * 16 + dt * 4 + i4) * 64] = make_float4(st[t].o[dt][4 * i4 + 0], st[t].o[dt][4 * i4 + 1],
-                                                      st[t].o[dt][4 * i4 + 2], st[t].o[dt][4 * i4 + 3]);
-    pm[t * 64] = make_float2(st[t].r, l_row[t]);
+      for (int e = 0; e < 16; ++e) {
+        st[t].o[dt][e] *= inv;
+        amax = fmaxf(amax, fabsf(st[t].o[dt][e]));
+      }
+    const bool use_f16 = row_max2(amax) < 32768.0f;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        uint32_t w[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float x0 = st[t].o[dt][8 * j + 2 * u], x1 = st[t].o[dt][8 * j + 2 * u + 1];
+          w[u] = use_f16 ? pack_f16(x0, x1) : pack_bf16(x0, x1);
+        }
+        po[(t * 8 + dt * 2 + j) * 64] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    pm[t * 64] = make_float2(st[t].r, use_f16 ? l_row[t] : -l_row[t]);
   }
 }
 
@@ -1341,13 +1372,13 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(BfParams p) {
   // the key append.
   const size_t wg0 = ((static_cast<size_t>(b) * p.Hkv + g) * p.row_blocks + rb) * p.splits;
   float2 ml[S];
-  float4 o[S][4];
+  uint4 o[S][2];
 #pragma unroll
   for (int ss = 0; ss < S; ++ss) {
     const size_t wg = wg0 + min(ss, p.splits - 1);
     ml[ss] = p.part_ml[wg * (ROWS * 2) + wt * 64 + lane];
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) o[ss][i4] = p.part_o[wg * (ROWS * 32) + (wt * 16 + dt * 4 + i4) * 64 + lane];
+    for (int j = 0; j < 2; ++j) o[ss][j] = p.part_o[wg * (ROWS * 16) + (wt * 8 + dt * 2 + j) * 64 + lane];
   }
   const KeyPairs kp = load_keys(p, b, g, idx, (gridDim.x - 1) * 256);
   asm volatile("" ::: "memory");   // the sequence state is read after these loads go out
@@ -1372,14 +1403,26 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(BfParams p) {
   for (int i4 = 0; i4 < 4; ++i4) acc[i4] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
   for (int ss = 0; ss < S; ++ss) {
-    const float w = (ss >= p.splits || ml[ss].x == -INFINITY) ? 0.0f : exp2f(ml[ss].x - M);
-    L = fmaf(w, ml[ss].y, L);
+    // weight of the split's normalised rows: 2^(r_s - max r) times its row sum
+    const float ls = fabsf(ml[ss].y);
+    const bool f16 = !(ml[ss].y < 0.0f);
+    const float w = (ss >= p.splits || ml[ss].x == -INFINITY) ? 0.0f : exp2f(ml[ss].x - M) * ls;
+    L += w;
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      acc[i4].x = fmaf(w, o[ss][i4].x, acc[i4].x);
-      acc[i4].y = fmaf(w, o[ss][i4].y, acc[i4].y);
-      acc[i4].z = fmaf(w, o[ss][i4].z, acc[i4].z);
-      acc[i4].w = fmaf(w, o[ss][i4].w, acc[i4].w);
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t wd[4] = {o[ss][j].x, o[ss][j].y, o[ss][j].z, o[ss][j].w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const f32x2 v = f16 ? unpack_f16(wd[u]) : f32x2{bf16_lo(wd[u]), bf16_hi(wd[u])};
+        float4& a4 = acc[2 * j + (u >> 1)];   // elements 8j + 2u, 8j + 2u + 1
+        if ((u & 1) == 0) {
+          a4.x = fmaf(w, v[0], a4.x);
+          a4.y = fmaf(w, v[1], a4.y);
+        } else {
+          a4.z = fmaf(w, v[0], a4.z);
+          a4.w = fmaf(w, v[1], a4.w);
+        }
+      }
     }
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
@@ -1419,7 +1462,7 @@ WsLayout ws_layout(const tv_attn_args* a, const AttnPlan& pl) {
   const size_t wg_rows = static_cast<size_t>(pl.waves) * 32 * pl.qt;
   const size_t wgs = heads * pl.row_blocks * pl.splits;
   w.part_o = align_up(wgs * wg_rows * 2 * sizeof(float2));
-  w.total = w.part_o + wgs * wg_rows * 32 * sizeof(float4);
+  w.total = w.part_o + wgs * wg_rows * 16 * sizeof(uint4);
   return w;
 }
 
@@ -1481,7 +1524,7 @@ hipError_t launch_attention_bf16(const tv_attn_args* a, const AttnPlan& pl, hipS
   const WsLayout w = ws_layout(a, pl);
   char* ws = static_cast<char*>(a->workspace);
   p.part_ml = pl.splits > 1 ? reinterpret_cast<float2*>(ws + w.part_ml) : nullptr;
-  p.part_o = pl.splits > 1 ? reinterpret_cast<float4*>(ws + w.part_o) : nullptr;
+  p.part_o = pl.splits > 1 ? reinterpret_cast<uint4*>(ws + w.part_o) : nullptr;
 
   dim3 grid(pl.splits * pl.row_blocks * a->Hkv * a->B);
   const int wg_rows = pl.waves * 32 * pl.qt;
