@@ -360,16 +360,25 @@ __device__ __forceinline__ void hazard_wait(f32x16 (&x)[QT]) {
 // lane's row sum exactly as the PV product will weight them.
 // (In two halves, so that a pipelined step can put the exponentials behind
 // one MFMA and the rest behind the next.)
+// vis: the row's visibility bits for the tile's keys, shifted down by the
+// lane half's 8-key offset (see tile_visibility), so that the bit of each
+// element sits at a constant position.
 template <bool MASKED, bool SHIFT>
-__device__ __forceinline__ f32x2 prob_exp(const RowState& st, const f32x16& x, int c, int sub, int h, int rel0,
-                                          uint64_t anc) {
+__device__ __forceinline__ f32x2 prob_exp(const RowState& st, const f32x16& x, int c, int sub, uint64_t vis) {
   float a = SHIFT ? x[2 * c] - st.r : x[2 * c], b = SHIFT ? x[2 * c + 1] - st.r : x[2 * c + 1];
   if (MASKED) {
-    const int key = 32 * sub + 16 * ((2 * c) >> 3) + 8 * h + ((2 * c) & 7);
-    if (!key_visible(rel0 + key, anc)) a = -INFINITY;
-    if (!key_visible(rel0 + key + 1, anc)) b = -INFINITY;
+    const int key = 32 * sub + 16 * ((2 * c) >> 3) + ((2 * c) & 7);   // (+ 8h, folded into vis)
+    if (((vis >> key) & 1ull) == 0ull) a = -INFINITY;
+    if (((vis >> (key + 1)) & 1ull) == 0ull) b = -INFINITY;
   }
   return f32x2{__builtin_amdgcn_exp2f(a), __builtin_amdgcn_exp2f(b)};
+}
+// Bit k of the result: is key k of the tile starting at key P + rel0
+// visible to the row with ancestor mask anc (key_visible for k = 0 .. 63),
+// shifted down by 8h. A tile with tree keys has -64 < rel0 < 64.
+__device__ __forceinline__ uint64_t tile_visibility(int rel0, uint64_t anc, int h) {
+  const uint64_t v = rel0 >= 0 ? anc >> rel0 : (anc << -rel0) | ((1ull << -rel0) - 1ull);
+  return v >> (8 * h);
 }
 // (The row sum adds the two bf16 halves as floats: a dot2 instruction would
 // do it in one, but between matrix instructions it stalls the wavefront.)
@@ -379,9 +388,8 @@ __device__ __forceinline__ uint32_t prob_pack(RowState& st, f32x2 e) {
   return w;
 }
 template <bool MASKED, bool SHIFT>
-__device__ __forceinline__ uint32_t prob_pair(RowState& st, const f32x16& x, int c, int sub, int h, int rel0,
-                                              uint64_t anc) {
-  return prob_pack(st, prob_exp<MASKED, SHIFT>(st, x, c, sub, h, rel0, anc));
+__device__ __forceinline__ uint32_t prob_pair(RowState& st, const f32x16& x, int c, int sub, uint64_t vis) {
+  return prob_pack(st, prob_exp<MASKED, SHIFT>(st, x, c, sub, vis));
 }
 
 // One staged 64-key tile times the QT query tiles of a wavefront, as 32
@@ -415,6 +423,9 @@ __device__ __forceinline__ void tile_product(RowState (&st)[QT], const uint16_t*
   bf16x8 fr[32];
   f32x16 x[2][QT];
   uint32_t w[2][QT][8];
+  uint64_t vis[QT];
+#pragma unroll
+  for (int t = 0; t < QT; ++t) vis[t] = MASKED ? tile_visibility(rel0, anc[t], h) : 0ull;
 #pragma unroll
   for (int i = 0; i < kLook; ++i) fr[i] = *frag_ptr(i);
 #pragma unroll
@@ -440,7 +451,7 @@ __device__ __forceinline__ void tile_product(RowState (&st)[QT], const uint16_t*
                                                                w[sub][t][4 * half + 2], w[sub][t][4 * half + 3]));
         st[t].o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i], pf, st[t].o[dt], 0, 0, 0);
       }
-      if (soft) w[ssub][t][c] = prob_pair<MASKED, SHIFT>(st[t], x[ssub][t], c, ssub, h, rel0, anc[t]);
+      if (soft) w[ssub][t][c] = prob_pair<MASKED, SHIFT>(st[t], x[ssub][t], c, ssub, vis[t]);
       __builtin_amdgcn_sched_barrier(0);
     }
     if ((i & 1) == 0 && (i < 8 || i >= 24)) {
@@ -517,7 +528,7 @@ __device__ __forceinline__ void pipe_iter(RowState (&st)[QT], f32x16 (&x)[2][QT]
         if (j == 0 && blk == 1) hazard_wait<QT>(x[0]);
         if (j == 0 && blk == 3) hazard_wait<QT>(x[1]);
         if (QT == 1 && soft && (j & 1) == 1) w[psub][0][pc] = prob_pack(st[0], e_pend);
-        if (soft && (QT == 2 || (j & 1) == 0)) e_pend = prob_exp<false, SHIFT>(st[tq], x[psub][tq], pc, psub, h, 0, 0ull);
+        if (soft && (QT == 2 || (j & 1) == 0)) e_pend = prob_exp<false, SHIFT>(st[tq], x[psub][tq], pc, psub, 0ull);
       } else if (soft) {
         w[psub][tq][pc] = prob_pack(st[tq], e_pend);
       }
@@ -553,7 +564,7 @@ __device__ __forceinline__ void pipe_tail(RowState (&st)[QT], f32x16 (&x)[2][QT]
 #pragma unroll
   for (int c = 4; c < 8; ++c)
 #pragma unroll
-    for (int t = 0; t < QT; ++t) w[1][t][c] = prob_pair<false, SHIFT>(st[t], x[1][t], c, 1, h, 0, 0ull);
+    for (int t = 0; t < QT; ++t) w[1][t][c] = prob_pair<false, SHIFT>(st[t], x[1][t], c, 1, 0ull);
 #pragma unroll
   for (int j = 0; j < 8; ++j)
 #pragma unroll
@@ -969,15 +980,87 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   // depth(i)) and value the lane items carry. Slots past P + n are not this call's keys
   // and may hold anything: their scores are masked and their values zeroed
   // (a masked probability is 0, but 0 * NaN is not).
+  // The values reach the tree tiles through a transpose in stage 3 (idle
+  // here: the query rows have been read, and tile 3 goes out only in the
+  // first loop iteration): the lane items are written there as [node][16-byte
+  // chunk of 8 dims], chunk c of node i at position c ^ (i % 16) of the row
+  // (stage_tree_values, before the barrier that precedes the fill); then a
+  // thread takes one chunk c and KPL consecutive keys of the tile and, for
+  // each of its 8 dims, writes those keys' 2-byte elements of the dim's V
+  // row as one 8- or 16-byte piece: tree nodes from the transpose, keys past
+  // the tree zeroed, prefix keys (below P) kept (only a thread whose keys
+  // include some reads the old piece first).
+  constexpr int KPL = 64 * 16 / NT;   // tile keys per thread in the value fill
+  static_assert(KPL == 4 || KPL == 8, "value fill in 8- or 16-byte pieces");
+  static_assert(kStages > 3 && 64 * kD * 2 <= 2 * kStageElems * 2, "the value transpose fits stage 3");
+  uint4* const vtr = reinterpret_cast<uint4*>(smem + 2 * 3 * kStageElems);   // [node][chunk]
+  auto stage_tree_values = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < VI; ++u) {
+      const int item = tid + NT * u, node = item >> 4, c = item & 15;
+      vtr[node * 16 + (c ^ (node & 15))] = make_uint4(tvv[u][0], tvv[u][1], tvv[u][2], tvv[u][3]);
+    }
+  };
   auto fill_tree = [&](int pos) __attribute__((always_inline)) {
-    const int kt0 = tile_k0(pos);
+    const int kt0 = tile_k0(pos), off = P - kt0;   // tile key k holds node k - off (k >= off)
     uint16_t* kd = Ks(pos % kStages);
     uint16_t* vd = Vs(pos % kStages);
-    if (kt0 + lane >= key_end) {
+    {
+      const int c = tid / (64 / KPL), k0 = KPL * (tid % (64 / KPL));
+      uint4 src[KPL];
+      bool tree[KPL], prefix[KPL];
+      bool any_prefix = false;
 #pragma unroll
-      for (int u = 0; u < 16 / WAVES; ++u)
+      for (int k = 0; k < KPL; ++k) {
+        const int node = k0 + k - off;
+        prefix[k] = k0 + k < off;
+        tree[k] = !prefix[k] && node < n;
+        any_prefix |= prefix[k];
+        src[k] = tree[k] ? vtr[node * 16 + (c ^ (node & 15))] : make_uint4(0u, 0u, 0u, 0u);
+      }
+      uint16_t* rows[8];
+      uint32_t wo[8][KPL / 2];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) vd[vs_off(8 * (wave + WAVES * u) + e, lane >> 3) + (lane & 7)] = 0;
+      for (int dd = 0; dd < 8; ++dd) {
+        rows[dd] = vd + vs_off(8 * c + dd, k0 >> 3) + (k0 & 7);   // KPL keys inside one 16-byte unit
+#pragma unroll
+        for (int k2 = 0; k2 < KPL / 2; ++k2) wo[dd][k2] = 0u;
+      }
+      if (any_prefix) {
+#pragma unroll
+        for (int dd = 0; dd < 8; ++dd) {
+          if constexpr (KPL == 4) {
+            const uint2 o2 = *reinterpret_cast<const uint2*>(rows[dd]);
+            wo[dd][0] = o2.x;
+            wo[dd][1] = o2.y;
+          } else {
+            const uint4 o4 = *reinterpret_cast<const uint4*>(rows[dd]);
+            wo[dd][0] = o4.x;
+            wo[dd][1] = o4.y;
+            wo[dd][2] = o4.z;
+            wo[dd][3] = o4.w;
+          }
+        }
+      }
+#pragma unroll
+      for (int dd = 0; dd < 8; ++dd) {
+        uint32_t wv[KPL / 2];
+#pragma unroll
+        for (int k2 = 0; k2 < KPL / 2; ++k2) {
+          uint32_t e[2];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int k = 2 * k2 + hh;
+            const uint32_t old = hh ? (wo[dd][k2] >> 16) : (wo[dd][k2] & 0xFFFFu);
+            e[hh] = tree[k] ? u4_elem(src[k], dd) : (prefix[k] ? old : 0u);
+          }
+          wv[k2] = e[0] | (e[1] << 16);
+        }
+        if constexpr (KPL == 4)
+          *reinterpret_cast<uint2*>(rows[dd]) = make_uint2(wv[0], wv[1]);
+        else
+          *reinterpret_cast<uint4*>(rows[dd]) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+      }
     }
 #pragma unroll
     for (int u = 0; u < KI; ++u) {
@@ -987,17 +1070,6 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
         const int key = slot - kt0;
         *reinterpret_cast<u32x4*>(kd + ks_off(key, c)) = tk_lo[u];
         *reinterpret_cast<u32x4*>(kd + ks_off(key, c + 8)) = tk_hi[u];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < VI; ++u) {
-      const int item = tid + NT * u, node = item >> 4, c = item & 15;
-      const int slot = P + node;
-      if (node < n && slot >= kt0 && slot < kt0 + kKT) {
-        const int key = slot - kt0;
-        const uint4 v4 = make_uint4(tvv[u][0], tvv[u][1], tvv[u][2], tvv[u][3]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) vd[vs_off(8 * c + e, key >> 3) + (key & 7)] = u4_elem(v4, e);
       }
     }
   };
@@ -1056,6 +1128,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
     if (n_masked > 0) {
       // every tree tile is formed before the first product, so the tree's
       // lane items are not live across a product
+      stage_tree_values();
       wait_tile(n_masked - 1);
       __syncthreads();
       for (int m = 0; m < n_masked; ++m) fill_tree(m);
