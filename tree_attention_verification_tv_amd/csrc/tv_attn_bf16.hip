@@ -94,7 +94,6 @@ constexpr int kStageElems = kKT * kD;   // bf16 elements of one K (or V) stage
 constexpr int kStages = 5;              // LDS ring of key tiles
 constexpr int kAhead = 3;               // tiles in flight
 constexpr int kMaxSplits = 8;           // key splits per row block
-constexpr int kVtStride = 66;           // LDS row of the value transpose in the append (64 nodes + pad)
 constexpr int kCsElems = 64 * 64 * 4;   // bf16 units of the RoPE table: 64 depths x 64 (cos, sin) = one stage
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -1349,49 +1348,65 @@ __device__ __forceinline__ void append_keys(const BfParams& p, const SeqState& s
     }
   }
 }
-__device__ __forceinline__ void append_values(const BfParams& p, int b, int g, uint16_t (*vt)[kVtStride]) {
+__device__ __forceinline__ void append_values(const BfParams& p, int b, int g, uint4* vtr) {
   // Values (a block of their own per KV head): node rows are read as whole
   // 16-byte chunks (all of a thread's loads in flight together, clamped to
   // the n_max rows of v_new so that they need not wait for the node count:
-  // at most TV_MAX_NODES_DEV * 16 = 4 * 256 chunks), transposed through LDS
-  // ([d][node]) and written as head-dim rows of consecutive slots, as the
-  // blocked cache holds them: one 16-byte store per aligned unit of 8 slots
-  // inside [P, P + n), single elements at the ends.
+  // at most TV_MAX_NODES_DEV * 16 = 4 * 256 chunks) and staged in LDS as
+  // [node][chunk], chunk c of node i at position c ^ (i % 16) (both passes
+  // then touch every bank once per 16 lanes). A thread then takes one chunk
+  // (8 head dims) of one aligned unit of 8 slots touching [P, P + n), gathers
+  // the unit's nodes, and writes the 8 dims' rows of consecutive slots as the
+  // blocked cache holds them: one 16-byte store per dim for a unit inside
+  // [P, P + n), single elements at the ends.
   static_assert(TV_MAX_NODES_DEV * (kD / 8) == 4 * 256, "four value chunks per thread");
+  // (the loads are issued from assembly and the sequence state is read by
+  // the scalar loader after them, so neither waits for the other)
   const int tid = threadIdx.x;
-  uint4 v4[4];
+  u32x4 v4[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int i = min((tid + 256 * u) >> 4, p.n_max - 1), c = tid & 15;
-    v4[u] = *reinterpret_cast<const uint4*>(p.v_new + ((static_cast<size_t>(b) * p.n_max + i) * p.Hkv + g) * kD + 8 * c);
+    v4[u] = ld_b128(p.v_new + ((static_cast<size_t>(b) * p.n_max + i) * p.Hkv + g) * kD + 8 * c);
   }
-  asm volatile("" ::: "memory");   // the sequence state is read after these loads go out
-  const SeqState sq = seq_state(p, b);
+  const SeqState sq = seq_state_scalar(p, b);
+  wait_vm<0>();
   if (sq.skip) return;
   const int n = sq.n, P = sq.P;
   const size_t head_off = (static_cast<size_t>(b) * p.Hkv + g) * p.cap * kD;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const int item = tid + 256 * u, i = item >> 4, c = item & 15;
-    if (i < n) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vt[8 * c + e][i] = u4_elem(v4[u], e);
-    }
+    landed(v4[u]);
+    const int i = (tid >> 4) + 16 * u, c = tid & 15;   // item tid + 256 u
+    vtr[i * 16 + (c ^ (i & 15))] = make_uint4(v4[u][0], v4[u][1], v4[u][2], v4[u][3]);
   }
   __syncthreads();
   const int u0 = P >> 3, n_units = ((P + n + 7) >> 3) - u0;   // 8-slot units touching [P, P + n)
-  for (int idx = tid; idx < kD * n_units; idx += 256) {
-    const int d = idx / n_units, s0 = (u0 + idx % n_units) << 3;
-    uint16_t* dst = p.v_cache + head_off + v_cache_off(s0, d);
-    if (s0 >= P && s0 + 8 <= P + n) {
-      uint32_t w[4];
+  for (int idx = tid; idx < 16 * n_units; idx += 256) {
+    const int c = idx & 15, s0 = (u0 + (idx >> 4)) << 3;
+    uint4 src[8];
+    bool in[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        w[e] = static_cast<uint32_t>(vt[d][s0 - P + 2 * e]) | (static_cast<uint32_t>(vt[d][s0 - P + 2 * e + 1]) << 16);
-      *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
-    } else {
-      for (int e = 0; e < 8; ++e)
-        if (s0 + e >= P && s0 + e < P + n) dst[e] = vt[d][s0 + e - P];
+    for (int j = 0; j < 8; ++j) {
+      const int i = s0 + j - P;
+      in[j] = i >= 0 && i < n;
+      src[j] = in[j] ? vtr[i * 16 + (c ^ (i & 15))] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    const bool full = s0 >= P && s0 + 8 <= P + n;
+#pragma unroll
+    for (int dd = 0; dd < 8; ++dd) {
+      uint16_t* dst = p.v_cache + head_off + v_cache_off(s0, 8 * c + dd);
+      if (full) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w[e] = static_cast<uint32_t>(u4_elem(src[2 * e], dd)) | (static_cast<uint32_t>(u4_elem(src[2 * e + 1], dd)) << 16);
+        *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (in[j]) dst[j] = u4_elem(src[j], dd);
+      }
     }
   }
 }
@@ -1401,9 +1416,9 @@ __device__ __forceinline__ void append_values(const BfParams& p, int b, int g, u
 constexpr int kAppendBlocks = 32;
 // Block 0 of each KV head appends the values (it is dispatched first).
 __global__ __launch_bounds__(256) void append_bf16_kernel(BfParams p) {
-  __shared__ uint16_t vt[kD][kVtStride];
+  __shared__ uint4 vtr[TV_MAX_NODES_DEV * 16];
   if (blockIdx.x == 0) {
-    append_values(p, blockIdx.z, blockIdx.y, vt);
+    append_values(p, blockIdx.z, blockIdx.y, vtr);
   } else {
     const int it = (blockIdx.x - 1) * 256 + threadIdx.x, nthreads = (gridDim.x - 1) * 256;
     const KeyPairs kp = load_keys(p, blockIdx.z, blockIdx.y, it, nthreads);
@@ -1427,9 +1442,9 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(BfParams p) {
   const int idx = (blockIdx.x - 1) * 256 + threadIdx.x;
   // block 0 of each KV head (dispatched first) appends the tree's values,
   // the others merge and append the keys
-  __shared__ uint16_t vt[kD][kVtStride];
+  __shared__ uint4 vtr[TV_MAX_NODES_DEV * 16];
   if (blockIdx.x == 0) {
-    append_values(p, b, g, vt);
+    append_values(p, b, g, vtr);
     return;
   }
   // thread = (row block, 32-row tile wt, head-dim block dt, lane): the four
