@@ -423,13 +423,16 @@ __device__ __forceinline__ void tile_product(RowState (&st)[QT], const uint16_t*
   f32x16 x[2][QT];
   uint32_t w[2][QT][8];
   uint64_t vis[QT];
+  bf16x8 pv_b[QT], pv_prev[QT];   // B operands of this and the previous step's PV MFMAs
 #pragma unroll
-  for (int t = 0; t < QT; ++t) vis[t] = MASKED ? tile_visibility(rel0, anc[t], h) : 0ull;
+  for (int t = 0; t < QT; ++t) {
+    vis[t] = MASKED ? tile_visibility(rel0, anc[t], h) : 0ull;
+    pv_b[t] = pv_prev[t] = bf16x8{};
+  }
 #pragma unroll
   for (int i = 0; i < kLook; ++i) fr[i] = *frag_ptr(i);
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
-    if (i + kLook < 32) fr[i + kLook] = *frag_ptr(i + kLook);
     const bool soft = i >= 8 && i < 24;
     const int ssub = (i - 8) >> 3, c = (i - 8) & 7;
     if (soft && c == 0) hazard_wait<QT>(x[ssub]);
@@ -449,13 +452,24 @@ __device__ __forceinline__ void tile_product(RowState (&st)[QT], const uint16_t*
         const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(w[sub][t][4 * half], w[sub][t][4 * half + 1],
                                                                w[sub][t][4 * half + 2], w[sub][t][4 * half + 3]));
         st[t].o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i], pf, st[t].o[dt], 0, 0, 0);
+        pv_b[t] = pf;
       }
+      __builtin_amdgcn_sched_barrier(0);
+      if (t == 0 && i + kLook < 32) fr[i + kLook] = *frag_ptr(i + kLook);   // behind the step's first MFMA
       if (soft) w[ssub][t][c] = prob_pair<MASKED, SHIFT>(st[t], x[ssub][t], c, ssub, vis[t]);
       __builtin_amdgcn_sched_barrier(0);
     }
     if ((i & 1) == 0 && (i < 8 || i >= 24)) {
       copy(i < 8 ? i / 2 : 4 + (i - 24) / 2);
       __builtin_amdgcn_sched_barrier(0);
+    }
+    // operands stay allocated one step past their last read (as in pipe_iter)
+    keep_live(fr[i]);
+    if (i > 0) keep_live(fr[i - 1]);
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+      if (i > 16) keep_live(pv_prev[t]);
+      if (i >= 16) pv_prev[t] = pv_b[t];
     }
   }
 }
@@ -498,7 +512,6 @@ __device__ __forceinline__ void pipe_iter(RowState (&st)[QT], f32x16 (&x)[2][QT]
   for (int t = 0; t < QT; ++t) pv_b[t] = pv_prev[t] = bf16x8{};
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
-    if (i + kLook < 32 && active(i + kLook)) fr[i + kLook] = *frag_ptr(i + kLook);
     const int blk = i >> 3, j = i & 7;
     const int psub = (blk == 0 || blk == 3) ? 1 : 0;      // score half whose probabilities this block forms
     const bool soft = PREV || blk != 0;
@@ -521,6 +534,10 @@ __device__ __forceinline__ void pipe_iter(RowState (&st)[QT], f32x16 (&x)[2][QT]
       }
       __builtin_amdgcn_sched_barrier(0);   // the vector work below goes behind this MFMA
       if (t == 0) {
+        // the fragment read goes behind the step's first MFMA, with the
+        // exponentials; the packing and row sums go behind the second (each
+        // group then fits the 32 cycles of the MFMA it follows)
+        if (i + kLook < 32 && active(i + kLook)) fr[i + kLook] = *frag_ptr(i + kLook);
         // the first probabilities read from a score block follow the MFMAs
         // that wrote it by the hazard distance (this step's first MFMA runs
         // meanwhile)
