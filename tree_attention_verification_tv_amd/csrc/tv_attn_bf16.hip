@@ -534,9 +534,11 @@ __device__ __forceinline__ void pipe_iter(RowState (&st)[QT], f32x16 (&x)[2][QT]
       }
       __builtin_amdgcn_sched_barrier(0);   // the vector work below goes behind this MFMA
       if (t == 0) {
-        // the fragment read goes behind the step's first MFMA, with the
-        // exponentials; the packing and row sums go behind the second (each
-        // group then fits the 32 cycles of the MFMA it follows)
+        // the copy slot (every fourth step) and the fragment read go behind
+        // the step's first MFMA, with the exponentials; the packing and row
+        // sums go behind the second (each group then nearly fits the 32
+        // cycles of the MFMA it follows)
+        if ((i & 3) == 0) copy(i >> 2);
         if (i + kLook < 32 && active(i + kLook)) fr[i + kLook] = *frag_ptr(i + kLook);
         // the first probabilities read from a score block follow the MFMAs
         // that wrote it by the hazard distance (this step's first MFMA runs
@@ -548,10 +550,6 @@ __device__ __forceinline__ void pipe_iter(RowState (&st)[QT], f32x16 (&x)[2][QT]
       } else if (soft) {
         w[psub][tq][pc] = prob_pack(st[tq], e_pend);
       }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if ((i & 3) == 0) {
-      copy(i >> 2);
       __builtin_amdgcn_sched_barrier(0);
     }
     // This step's MFMA operands stay allocated through the next step: a
