@@ -1270,8 +1270,10 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   }
   // Split partial, per row: the output divided by the split's row sum (a
   // convex combination of value rows, so bounded by the largest value
-  // element), as 16-bit floats: fp16 when the row's largest magnitude is
-  // below 2^15, bf16 otherwise; the sign of the stored row sum tells which.
+  // element), as 16-bit floats: fp16 when the largest magnitude of every row
+  // of the wavefront's 32-row tile is below 2^15, bf16 otherwise (one choice
+  // per tile, so the packing does not branch per lane); the sign of each
+  // stored row sum tells which.
   // Register order: the 16 bytes of (wave, t, dt, half j) for lane l sit at
   // (((wave * QT + t) * 8 + dt * 2 + j) * 64 + l) within this workgroup's
   // block (elements 8j .. 8j + 7 of the lane's dt accumulator); the (r, +-l)
@@ -1293,19 +1295,25 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
         st[t].o[dt][e] *= inv;
         amax = fmaxf(amax, fabsf(st[t].o[dt][e]));
       }
-    const bool use_f16 = row_max2(amax) < 32768.0f;
+    const bool use_f16 = __all(row_max2(amax) < 32768.0f);   // (over the tile's live rows)
+    auto store16 = [&](auto f16_tag) __attribute__((always_inline)) {
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        uint32_t w[4];
+        for (int j = 0; j < 2; ++j) {
+          uint32_t w[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float x0 = st[t].o[dt][8 * j + 2 * u], x1 = st[t].o[dt][8 * j + 2 * u + 1];
-          w[u] = use_f16 ? pack_f16(x0, x1) : pack_bf16(x0, x1);
+          for (int u = 0; u < 4; ++u) {
+            const float x0 = st[t].o[dt][8 * j + 2 * u], x1 = st[t].o[dt][8 * j + 2 * u + 1];
+            w[u] = decltype(f16_tag)::value ? pack_f16(x0, x1) : pack_bf16(x0, x1);
+          }
+          po[(t * 8 + dt * 2 + j) * 64] = make_uint4(w[0], w[1], w[2], w[3]);
         }
-        po[(t * 8 + dt * 2 + j) * 64] = make_uint4(w[0], w[1], w[2], w[3]);
-      }
+    };
+    if (use_f16)
+      store16(std::true_type{});
+    else
+      store16(std::false_type{});
     pm[t * 64] = make_float2(st[t].r, use_f16 ? l_row[t] : -l_row[t]);
   }
 }
