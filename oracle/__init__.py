@@ -20,10 +20,12 @@ from .tv_oracle import (  # noqa: F401
     attention_row,
     build_tree,
     commit,
+    next_token_distribution,
     rope,
     tree_attention,
     tree_depth,
     tree_is_valid,
     tree_mask,
+    typical_accept,
     verify_step,
 )

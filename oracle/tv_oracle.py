@@ -14,6 +14,9 @@ Sources (web pages, cited by title and section):
                   8 and 9.2.
   [DRAFTERS]      "Drafters: draft models, Medusa, EAGLE, MTP, DFlash, DSpark"
                   (robertz.co), section "Why the answer does not change".
+  [MEDUSA-EXPL] also defines typical acceptance (section "Typical
+  acceptance"), as do [MEDUSA-EAGLE] ("Typical acceptance") and [INFRA-5.3]
+  section 9.1.
 
 Readings of points the pages leave open are listed with each function.
 
@@ -299,6 +302,92 @@ def accept(cand_tok, tgt_argmax, parents, n_nodes, err_in=None):
         toks = [int(cand_tok[b, a]) for a in p[1:]] + [bonus[b]]
         out_tokens[b, :L + 1] = toks
     return accept_len, path, bonus, out_tokens
+
+
+# ---------------------------------------------------------------------------
+# Typical acceptance: entropy-dependent probability floor instead of argmax
+# ---------------------------------------------------------------------------
+
+def next_token_distribution(logits_row):
+    """Softmax of one row of target logits, its entropy in nats, and argmax.
+
+    The distribution is the plain softmax of the logits (no temperature: a
+    caller sampling at temperature T passes logits / T). Entropy is
+    -sum p ln p over tokens with p > 0. The argmax is the lowest index among
+    equal maxima. Returns (p [V] float64, H float, argmax int).
+    """
+    x = np.asarray(logits_row, dtype=np.float64)
+    e = np.exp(x - x.max())
+    p = e / e.sum()
+    nz = p[p > 0.0]
+    H = float(-(nz * np.log(nz)).sum())
+    return p, H, int(np.argmax(x))
+
+
+def typical_accept(logits, cand_tok, parents, n_nodes, epsilon, delta, err_in=None):
+    """Typical acceptance over a draft tree, longest accepted path.
+
+    [MEDUSA-EXPL] "Typical acceptance", [MEDUSA-EAGLE] "Typical acceptance",
+    [INFRA-5.3] section 9.1: a drafted token x passes iff the target's
+    probability of it exceeds min(epsilon, delta * exp(-H)), H being the
+    entropy of the target's distribution at that point; the first token of a
+    step is always the target's own greedy choice.
+
+    Readings:
+      * the target distribution at node i is the softmax of logits[b][i]; it
+        predicts the token after i, so child c is judged under its parent's
+        distribution (the alignment of the greedy rule);
+      * H in nats; the comparison is strict;
+      * a token id outside [0, V) has probability 0 and never passes;
+      * the root is always accepted; a node is accepted iff its parent is
+        and its own token passes; the deepest accepted node wins, equal
+        depths going to the lowest index (as in greedy acceptance);
+      * the bonus token is the target's greedy argmax at that deepest node.
+
+    Returns (entropy [B,n_max] f64, p_tok [B,n_max] f64, tgt_argmax
+    [B,n_max] int32, accept_len, path, bonus, out_tokens) with the accept
+    outputs as in ``accept``. p_tok[b][c] is the probability of node c's
+    token under its parent's distribution (1 for the root). Padding nodes and
+    skipped sequences get entropy 0, p_tok 0 and argmax -1.
+    """
+    B, n_max, V = logits.shape
+    entropy = np.zeros((B, n_max), dtype=np.float64)
+    p_tok = np.zeros((B, n_max), dtype=np.float64)
+    tgt_argmax = np.full((B, n_max), -1, dtype=np.int32)
+    accept_len = np.full(B, -1, dtype=np.int32)
+    path = np.full((B, n_max), -1, dtype=np.int32)
+    bonus = np.full(B, -1, dtype=np.int32)
+    out_tokens = np.full((B, n_max), -1, dtype=np.int32)
+    for b in range(B):
+        n = int(n_nodes[b])
+        if n == 0 or (err_in is not None and int(err_in[b]) != 0):
+            continue
+        par = [int(x) for x in parents[b, :n]]
+        dists = [next_token_distribution(logits[b, i]) for i in range(n)]
+        for i in range(n):
+            entropy[b, i] = dists[i][1]
+            tgt_argmax[b, i] = dists[i][2]
+        p_tok[b, 0] = 1.0
+        for c in range(1, n):
+            t = int(cand_tok[b, c])
+            p_tok[b, c] = dists[par[c]][0][t] if 0 <= t < V else 0.0
+        ok = [False] * n
+        ok[0] = True
+        for c in range(1, n):
+            floor = min(epsilon, delta * math.exp(-entropy[b, par[c]]))
+            ok[c] = ok[par[c]] and p_tok[b, c] > floor
+        dep = tree_depth(par)
+        best = 0
+        for i in range(n):
+            if ok[i] and dep[i] > dep[best]:
+                best = i
+        p = ancestors_or_self(par, best)
+        L = dep[best]
+        accept_len[b] = L
+        path[b, :L + 1] = p
+        bonus[b] = tgt_argmax[b, best]
+        out_tokens[b, :L + 1] = [int(cand_tok[b, a]) for a in p[1:]] + [bonus[b]]
+    return entropy, p_tok, tgt_argmax, accept_len, path, bonus, out_tokens
 
 
 # ---------------------------------------------------------------------------

@@ -72,3 +72,22 @@ def test_eagle_tree_acceptance_follows_path_confidence():
         lens.append(int(acc[0]))
     m = np.mean(lens)
     assert 1.0 < m < 6.0
+
+
+def test_target_logits_seeded_and_planted():
+    from workloads import target_logits
+    w = generate(3, B=2)
+    a = target_logits(w, vocab=500)
+    assert a.shape == (2, w.n_max, 500) and a.dtype == np.uint16
+    assert (a == target_logits(w, vocab=500)).all()
+    assert not (a == target_logits(w, vocab=500, seed=99)).all()
+    x = bf16_bits_to_f32(a)
+    # planted child logits sit near ln(V) + tau^2/2 + U(-9, 3), far above
+    # most of the N(0, tau^2) base row
+    for b in range(2):
+        for c in range(1, int(w.n_nodes[b])):
+            if 0 <= w.tok[b, c] < 500:
+                v = x[b, w.parents[b, c], w.tok[b, c]]
+                assert np.log(500) - 9.1 < v < np.log(500) + 4.5 + 3.1
+    f = target_logits(w, vocab=500, dtype="f32")
+    assert f.dtype == np.float32

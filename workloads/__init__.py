@@ -12,4 +12,5 @@ from .configs import (  # noqa: F401
     bf16_bits_to_f32,
     f32_to_bf16_bits,
     generate,
+    target_logits,
 )

@@ -389,3 +389,36 @@ def generate(cfg: int, seed: Optional[int] = None, **over) -> Workload:
                     D=D, cap=cap, rope_theta=float(c["rope_theta"]), parents=parents,
                     n_nodes=n_nodes, prefix_len=prefix_len, tok=tok, tgt=tgt, q=q,
                     k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache)
+
+
+def target_logits(w: Workload, vocab: int = VOCAB, dtype: Optional[str] = None,
+                  seed: Optional[int] = None) -> np.ndarray:
+    """Synthetic target logits [B, n_max, vocab] for typical acceptance.
+
+    Row (b, i) stands for the target model's next-token logits at node i of
+    sequence b. Base logits are tau * N(0, 1) with tau ~ U(0.5, 3) per row, so
+    rows range from nearly flat to peaked. Each child c of node i gets, at its
+    own token, the planted logit ln(vocab) + tau^2 / 2 + s with s ~ U(-9, 3):
+    ln(vocab) + tau^2 / 2 is the log of the expected sum of exp over the base
+    row, so s is roughly the child's log-odds against the rest of the
+    vocabulary and children range from hopeless to near-certain. Rows of
+    padding nodes are base logits only. Drawn from a stream of its own
+    (``seed``, default the workload's config number), then rounded to bf16
+    bits when the dtype (default the workload's) is bf16.
+    """
+    dt = w.dtype if dtype is None else dtype
+    seed = w.cfg if seed is None else seed
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 0x7A])))
+    B, n_max = w.B, w.n_max
+    tau = rng.uniform(0.5, 3.0, size=(B, n_max)).astype(np.float32)
+    x = rng.standard_normal(size=(B, n_max, vocab), dtype=np.float32)
+    x *= tau[:, :, None]
+    base = np.float32(np.log(vocab)) + 0.5 * tau * tau
+    for b in range(B):
+        n = int(w.n_nodes[b])
+        for c in range(1, n):
+            p = int(w.parents[b, c])
+            t = int(w.tok[b, c])
+            if 0 <= t < vocab:
+                x[b, p, t] = base[b, p] + np.float32(rng.uniform(-9.0, 3.0))
+    return f32_to_bf16_bits(x) if dt == "bf16" else x
