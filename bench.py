@@ -12,14 +12,22 @@ tree KV into its copy and commits from the same starting prefix length, so all
 steps do identical work.
 
 Prints one JSON line. `value` = tree nodes verified per second over the timed
-steps (wall clock between two device synchronisations). `roofline` reports the
-attention call (its three kernels): algorithmic HBM bytes per call divided by
-its mean duration, measured with HIP events on the launch stream; `traffic` is
-the measured HBM bytes per call from profiles/ when it matches the source.
+steps (wall clock between two device synchronisations; the timed loop calls
+the C ABI with arguments built once, as a native caller would). `roofline`
+reports the attention call (its two kernels): algorithmic HBM bytes per call
+divided by its mean duration, from HIP events on the launch stream around the
+call in K further steps (an event pair adds a few microseconds to a step, so
+the timed steps carry none); `traffic` is the measured HBM bytes per call from
+profiles/ when it matches the source.
+
+`--workload typical` measures typical acceptance instead (tv_accept_typical on
+the same trees, bf16 target logits over a 32000-token vocabulary by default):
+its roofline counts the live rows of logits, read once.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -106,6 +114,144 @@ def cpu_baseline(w, budget_s: float = 12.0) -> dict:
                       f"{len(os.sched_getaffinity(0))} available ({cpu}), {dt:.1f} s"}
 
 
+TYPICAL_EPS, TYPICAL_DELTA = 0.09, 0.3
+TYPICAL_SOURCES = ["tv_typical.hip", "tv_tree.hip", "tv_device.h"]
+
+
+def typical_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in TYPICAL_SOURCES:
+        with open(os.path.join(ROOT, "tree_attention_verification_tv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_typical_traffic(workload: str):
+    """Measured HBM bytes per tv_accept_typical call (as load_traffic)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_typical_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_source_hash") != typical_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def typical_cpu_baseline(w, x64, budget_s: float = 8.0) -> dict:
+    """The oracle's typical acceptance, as it is, on the whole batch, repeated
+    for about budget_s seconds; one thread."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    runs = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while True:
+            oracle.typical_accept(x64, w.tok, w.parents, w.n_nodes, TYPICAL_EPS, TYPICAL_DELTA)
+            runs += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    dt = time.perf_counter() - t0
+    return {"value": runs * w.total_nodes / dt, "unit": "tree-nodes/s", "cores": 1, "kind": "oracle",
+            "sample": f"{runs} passes over the whole batch ({w.total_nodes} nodes, vocabulary "
+                      f"{x64.shape[2]}), numpy float64 softmax / entropy / tree scan, 1 thread, "
+                      f"{dt:.1f} s"}
+
+
+def bench_typical(args) -> None:
+    """Typical acceptance from the target's logits on the headline trees:
+    one tv_accept_typical call (statistics kernel + tree scan) per step."""
+    import numpy as np
+    import torch
+
+    import tree_attention_verification_tv_amd as tv
+    from workloads import bf16_bits_to_f32, generate, target_logits
+
+    dev = torch.device("cuda:0")
+    w = generate(args.config, seed=args.seed)
+    L = target_logits(w, vocab=args.vocab, dtype="bf16")
+    x = torch.from_numpy(L).view(torch.int16).view(torch.bfloat16).to(dev)
+    row_bytes = args.vocab * 2
+    logits_bytes = w.total_nodes * row_bytes            # live rows, read once
+    copies = args.copies or max(2, -(-4 * INFINITY_CACHE_BYTES // x.numel() // 2))
+    sets = [x] + [x.clone() for _ in range(copies - 1)]
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    parents, n_nodes, tok = up(w.parents), up(w.n_nodes), up(w.tok)
+    anc, depth, err = tv.build_tree(parents, n_nodes)
+    stream = torch.cuda.current_stream()
+    # one checked call through the binding, then the C ABI with fixed arguments
+    r = tv.accept_typical(sets[0], tok, parents, anc, depth, n_nodes, err, epsilon=TYPICAL_EPS,
+                          delta=TYPICAL_DELTA)
+    acc_len, path, bonus, toks, ent, p_tok, am = r
+    lib = tv._lib.load()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def P(t):
+        return ctypes.c_void_p(t.data_ptr())
+
+    tail = (P(tok), P(parents), P(anc), P(depth), P(n_nodes), P(err), w.B, w.n_max,
+            ctypes.c_float(TYPICAL_EPS), ctypes.c_float(TYPICAL_DELTA), P(ent), P(p_tok), P(am),
+            P(acc_len), P(path), P(bonus), P(toks), sp)
+    heads = [(P(x_k), tv._lib.TV_BF16, args.vocab) for x_k in sets]
+
+    def step(k):
+        if lib.tv_accept_typical(*heads[k % copies], *tail):
+            raise RuntimeError("tv_accept_typical failed")
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(args.warmup + k)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    # the call alone, K calls back to back between one pair of HIP events
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for k in range(args.steps):
+        step(k)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    call_s = e0.elapsed_time(e1) * 1e-3 / args.steps
+    achieved = logits_bytes / call_s / 1e9
+    rec = {
+        "metric": "typical acceptance: tree nodes/s and logits GB/s (% of HBM peak), "
+                  "8B-shaped batch 8 trees",
+        "value": w.total_nodes / ((t1 - t0) / args.steps),
+        "unit": "tree-nodes/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": (t1 - t0) * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"typical-accept-{w.name}-v{args.vocab}", "batch": w.B,
+                   "tree_nodes": int(w.n_nodes.max()), "vocab": args.vocab,
+                   "epsilon": TYPICAL_EPS, "delta": TYPICAL_DELTA, "input_copies_rotated": copies,
+                   "seed": args.config if args.seed is None else args.seed},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": load_typical_traffic(f"{w.name}-v{args.vocab}"),
+                     "kernel": "tv_accept_typical call: typical_stats_kernel + accept_kernel<true>; "
+                               "HIP events on its stream around K calls back to back",
+                     "algorithmic_bytes_per_launch": logits_bytes,
+                     "call_us_mean": call_s * 1e6},
+        "mean_accept_len": float(acc_len.float().mean().item()),
+        "kernel_source_hash": typical_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = typical_cpu_baseline(w, bf16_bits_to_f32(L).astype(np.float64))
+    print(json.dumps(rec), flush=True)
+
+
 def main() -> None:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -115,6 +261,10 @@ def main() -> None:
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated per step (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--workload", choices=("step", "typical"), default="step",
+                    help="step: the verification step (default); typical: typical acceptance "
+                         "from target logits on the same trees")
+    ap.add_argument("--vocab", type=int, default=32000, help="vocabulary of --workload typical")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -122,6 +272,10 @@ def main() -> None:
               "path has no multi-GPU form in this library; see DESIGN.md for how it would shard)",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == "typical":
+        bench_typical(args)
+        return
 
     import numpy as np
     import torch
@@ -163,41 +317,79 @@ def main() -> None:
     workspace = tv.new_workspace(ws_bytes, dev)
 
     stream = torch.cuda.current_stream()
+    # The timed loop calls the C ABI with arguments built once per input
+    # copy (as a native caller would); the binding's checks run here, once.
+    lib = tv._lib.load()
+    sp = ctypes.c_void_p(stream.cuda_stream)
 
-    def step(k: int, ev=None):
-        s = sets[k % copies]
-        tv.build_tree(parents, n_nodes, anc, depth, err)
-        if ev is not None:
-            ev[0].record(stream)
-        tv.tree_attention(s["q"], s["k_new"], s["v_new"], s["k_cache"], s["v_cache"], plen, n_nodes,
-                          anc, depth, err, rope_theta=w.rope_theta, out=out, workspace=workspace)
-        if ev is not None:
-            ev[1].record(stream)
-        tv.accept(tok, tgt, parents, anc, depth, n_nodes, err, acc_len, path, bonus, toks)
-        tv.commit(s["k_cache"], s["v_cache"], plen, acc_len, path, plen_out)
+    def P(t):
+        return ctypes.c_void_p(t.data_ptr())
+
+    calls = []
+    for s in sets:
+        a = tv.attn_args(s["q"], s["k_new"], s["v_new"], s["k_cache"], s["v_cache"], plen, n_nodes,
+                         anc, depth, err, out, w.rope_theta, workspace=workspace)
+        cm = (P(s["k_cache"]), P(s["v_cache"]), B, w.Hkv, w.cap, w.D, a.dtype, P(plen), P(acc_len),
+              P(path), n_max, P(plen_out), sp)
+        calls.append((a, cm))
+    bt = (P(parents), P(n_nodes), B, n_max, P(anc), P(depth), P(err), sp)
+    ac = (P(tok), P(tgt), P(parents), P(anc), P(depth), P(n_nodes), P(err), B, n_max, P(acc_len),
+          P(path), P(bonus), P(toks), sp)
+
+    def attention(k: int) -> int:
+        return lib.tv_tree_attention(ctypes.byref(calls[k % copies][0]), sp)
+
+    def step(k: int) -> None:
+        st = lib.tv_build_tree(*bt)
+        st |= attention(k)
+        st |= lib.tv_accept(*ac)
+        st |= lib.tv_commit(*calls[k % copies][1])
+        if st:
+            raise RuntimeError(f"library call failed with status {st}")
 
     for k in range(args.warmup):
         step(k)
     torch.cuda.synchronize()
-
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        step(args.warmup + k, events[k])
+        step(args.warmup + k)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
 
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     nodes = w.total_nodes
     value = nodes / ((t1 - t0) / args.steps)
-    attn_ms = [e0.elapsed_time(e1) for e0, e1 in events]
+    mean_accept = float(acc_len.float().mean().item())
+
+    # The attention call in its step: K more steps, each with a pair of HIP
+    # events on the launch stream around the call (outside the timed loop,
+    # since each event pair adds a few microseconds to its step). Then the
+    # call alone, K calls back to back between one pair of events (each call
+    # re-appends the tree KV into its copy, so all do the same work).
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for k in range(args.steps):
+        st = lib.tv_build_tree(*bt)
+        events[k][0].record(stream)
+        st |= attention(k)
+        events[k][1].record(stream)
+        st |= lib.tv_accept(*ac) | lib.tv_commit(*calls[k % copies][1])
+        if st:
+            raise RuntimeError(f"library call failed with status {st}")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for k in range(args.steps):
+        if attention(k):
+            raise RuntimeError("tv_tree_attention failed")
+    e1.record(stream)
+    torch.cuda.synchronize()
+    attn_ms = [a.elapsed_time(b) for a, b in events]
     attn_mean_s = float(np.mean(attn_ms)) * 1e-3
+    attn_b2b_s = e0.elapsed_time(e1) * 1e-3 / args.steps
     ab = algorithmic_bytes(w)
     achieved = ab["total"] / attn_mean_s / 1e9
     traffic = load_traffic(w.name)
-    mean_accept = float(acc_len.float().mean().item())
 
     rec = {
         "metric": METRIC,
@@ -219,11 +411,12 @@ def main() -> None:
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "tv_tree_attention call: attn_bf16_kernel + merge_bf16_kernel (split merge "
-                               "and tree append), HIP events around the call on its stream",
+                               "and tree append); HIP events on its stream around each call, in the step",
                      "algorithmic_bytes_per_launch": ab["total"],
                      "attention_us_mean": attn_mean_s * 1e6,
                      "attention_us_p10": float(np.percentile(attn_ms, 10)) * 1e3,
-                     "attention_us_p90": float(np.percentile(attn_ms, 90)) * 1e3},
+                     "attention_us_p90": float(np.percentile(attn_ms, 90)) * 1e3,
+                     "attention_us_back_to_back": attn_b2b_s * 1e6},
         "attention_only_nodes_per_s": nodes / attn_mean_s,
         "mean_accept_len": mean_accept,
         "kernel_source_hash": kernel_source_hash(),

@@ -8,9 +8,10 @@
  * Sources (web pages, cited by title and section):
  *   [MEDUSA-EAGLE] "Medusa and EAGLE: self-speculative decoding heads,
  *                  explained" (pofe.ai), "Medusa: heads, losses and trees".
- *   [MEDUSA-EXPL]  "Medusa, explained" (vibeengines.com), steps 6 and 7.
+ *   [MEDUSA-EXPL]  "Medusa, explained" (vibeengines.com), steps 6 and 7,
+ *                  "Typical acceptance".
  *   [INFRA-5.3]    "5.3 Medusa、EAGLE 与 MTP" (infra-guide), sections 3.1,
- *                  3.2, 8 and 9.2.
+ *                  3.2, 8, 9.1 and 9.2.
  *   [DRAFTERS]     "Drafters: draft models, Medusa, EAGLE, MTP, DFlash,
  *                  DSpark" (robertz.co), "Why the answer does not change".
  *
@@ -180,6 +181,50 @@ tv_status tv_accept(const int32_t* cand_tok, const int32_t* tgt_argmax,
                     const int32_t* n_nodes, const int32_t* err, int32_t B, int32_t n_max,
                     int32_t* accept_len, int32_t* path, int32_t* bonus_tok,
                     int32_t* out_tokens, hipStream_t stream);
+
+/*
+ * tv_accept_typical -- typical acceptance, longest accepted path.
+ *
+ * A drafted token passes iff the target gives it probability above
+ * min(epsilon, delta * exp(-H)), H being the entropy of the target's
+ * distribution at that point ([MEDUSA-EXPL] "Typical acceptance",
+ * [MEDUSA-EAGLE] "Typical acceptance", [INFRA-5.3] section 9.1); the first
+ * token of a step is the target's own greedy choice. Readings fixed here:
+ *   - logits[b][i] are the target's next-token logits AT node i; the
+ *     distribution is their plain softmax (a caller sampling at temperature
+ *     T passes logits / T); node c >= 1 is judged under its parent's
+ *     distribution, H in nats, the comparison strict;
+ *   - a node is accepted iff its parent is and its token passes; the root
+ *     always is; the deepest accepted node e wins, equal depths going to the
+ *     lower index; accept_len = depth(e); the bonus token is the target's
+ *     argmax at e (lowest token id among equal maxima);
+ *   - a token id outside [0, vocab) has probability 0 and never passes.
+ *
+ *   logits     [B][n_max][vocab] of dtype (TV_BF16 or TV_F32), finite; read
+ *              once (rows of padding nodes and skipped sequences are not
+ *              read). 16-byte aligned rows (vocab * element size a multiple
+ *              of 16, aligned base) take the vector path; others work too.
+ *   cand_tok, parents, anc, depth, n_nodes, err as for tv_accept
+ *   epsilon, delta  the two thresholds (not NaN)
+ *   entropy    [B][n_max] float out: H at node i (nats)
+ *   p_tok      [B][n_max] float out: probability of node i's token under its
+ *              parent's distribution; 1 for the root
+ *   tgt_argmax [B][n_max] out: the target's argmax at node i
+ *              (padding nodes and skipped sequences: entropy 0, p_tok 0,
+ *              tgt_argmax -1; with err == NULL and a tree that is not laid
+ *              out parents-first, p_tok entries are unspecified)
+ *   accept_len, path, bonus_tok, out_tokens  as for tv_accept
+ * Two kernels on the stream: per-node statistics, then the tree scan.
+ * Host checks: pointers non-null (err and out_tokens may be NULL) unless
+ * B == 0, 0 <= B <= 65535, 1 <= n_max <= TV_MAX_NODES, vocab >= 1, dtype
+ * valid. B == 0 is a no-op.
+ */
+tv_status tv_accept_typical(const void* logits, int32_t dtype, int32_t vocab,
+                            const int32_t* cand_tok, const int32_t* parents, const uint64_t* anc,
+                            const int32_t* depth, const int32_t* n_nodes, const int32_t* err,
+                            int32_t B, int32_t n_max, float epsilon, float delta, float* entropy,
+                            float* p_tok, int32_t* tgt_argmax, int32_t* accept_len, int32_t* path,
+                            int32_t* bonus_tok, int32_t* out_tokens, hipStream_t stream);
 
 /*
  * tv_commit -- keep the accepted path's KV in place, drop the other branches.

@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_header_declares_expected_calls():
     names = declared_functions()
-    for must in ("tv_build_tree", "tv_tree_attention", "tv_accept", "tv_commit"):
+    for must in ("tv_build_tree", "tv_tree_attention", "tv_accept", "tv_commit", "tv_accept_typical"):
         assert must in names
 
 
@@ -67,6 +67,21 @@ def test_host_validation_without_device():
                          null) == _lib.TV_ERR_INVALID_ARG
     assert lib.tv_accept(null, null, null, null, null, null, null, 0, 5, null, null, null, null,
                          null) == _lib.TV_OK
+    # typical acceptance: B, n_max, vocab, dtype, thresholds, pointers
+    def typ(B=1, n_max=5, V=32000, dtype=_lib.TV_BF16, eps=0.09, delta=0.3, logits=fake, ent=fake):
+        return lib.tv_accept_typical(logits, dtype, V, fake, fake, fake, fake, fake, null, B, n_max,
+                                     eps, delta, ent, fake, fake, fake, fake, fake, null, null)
+    assert typ(B=-1) == _lib.TV_ERR_INVALID_ARG
+    assert typ(B=70000) == _lib.TV_ERR_INVALID_ARG
+    assert typ(n_max=0) == _lib.TV_ERR_INVALID_ARG
+    assert typ(n_max=65) == _lib.TV_ERR_INVALID_ARG
+    assert typ(V=0) == _lib.TV_ERR_INVALID_ARG
+    assert typ(dtype=3) == _lib.TV_ERR_INVALID_ARG
+    assert typ(eps=float("nan")) == _lib.TV_ERR_INVALID_ARG
+    assert typ(delta=float("nan")) == _lib.TV_ERR_INVALID_ARG
+    assert typ(logits=null) == _lib.TV_ERR_INVALID_ARG
+    assert typ(ent=null) == _lib.TV_ERR_INVALID_ARG
+    assert typ(B=0, logits=null, ent=null) == _lib.TV_OK
     # commit
     assert lib.tv_commit(fake, fake, 1, 0, 10, 128, 1, fake, fake, fake, 5, fake, null) == _lib.TV_ERR_INVALID_ARG
     assert lib.tv_commit(fake, fake, 1, 2, 4, 128, 1, fake, fake, fake, 5, fake, null) == _lib.TV_ERR_INVALID_ARG

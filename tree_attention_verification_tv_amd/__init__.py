@@ -11,6 +11,8 @@ Step order for one verification pass of one layer:
                          n_nodes, anc, depth, err)
     accept_len, path, bonus, tokens = accept(cand_tok, tgt_argmax, parents,
                                              anc, depth, n_nodes, err)
+      (or, from the target's logits: accept_typical(logits, cand_tok, parents,
+       anc, depth, n_nodes, err, epsilon=..., delta=...))
     new_prefix_len = commit(k_cache, v_cache, prefix_len, accept_len, path)
 """
 from __future__ import annotations
@@ -24,7 +26,8 @@ from . import _lib
 from ._lib import (TV_BF16, TV_ERR_BAD_TREE, TV_ERR_CAPACITY, TV_F32, TV_MAX_NODES,  # noqa: F401
                    TvAttnArgs, TvError)
 
-__all__ = ["build_tree", "tree_attention", "tree_attention_workspace_size", "new_workspace", "accept", "commit",
+__all__ = ["build_tree", "tree_attention", "tree_attention_workspace_size", "new_workspace", "accept",
+           "accept_typical", "commit",
            "version", "TvError", "TV_ERR_BAD_TREE", "TV_ERR_CAPACITY", "attn_args",
            "v_cache_blocked", "v_cache_rows", "V_BLOCK"]
 
@@ -203,6 +206,42 @@ def accept(cand_tok, tgt_argmax, parents, anc, depth, n_nodes, err=None, accept_
                                           _ptr(accept_len), _ptr(path), _ptr(bonus), _ptr(out_tokens),
                                           _stream(stream)))
     return accept_len, path, bonus, out_tokens
+
+
+def accept_typical(logits, cand_tok, parents, anc, depth, n_nodes, err=None, *, epsilon: float,
+                   delta: float, want_tokens=True, stream=None):
+    """Typical acceptance from the target's logits [B, n_max, V] (float32 or
+    bfloat16): a drafted token passes iff its probability under its parent's
+    distribution exceeds min(epsilon, delta * exp(-H(parent))).
+
+    Returns (accept_len [B], path [B, n_max], bonus [B], out_tokens [B, n_max]
+    or None, entropy [B, n_max] float32, p_tok [B, n_max] float32,
+    tgt_argmax [B, n_max] int32)."""
+    lib = _lib.load()
+    if logits.dtype not in _DTYPES:
+        raise ValueError(f"logits must be float32 or bfloat16 (got {logits.dtype})")
+    _dev(logits, "logits", logits.dtype)
+    for name, t in (("cand_tok", cand_tok), ("parents", parents), ("depth", depth), ("n_nodes", n_nodes)):
+        _dev(t, name, torch.int32)
+    _dev(anc, "anc", torch.int64)
+    if err is not None:
+        _dev(err, "err", torch.int32)
+    B, n_max = parents.shape
+    if logits.dim() != 3 or tuple(logits.shape[:2]) != (B, n_max):
+        raise ValueError("logits must be [B, n_max, V]")
+    V = logits.shape[2]
+    dev = parents.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    accept_len, bonus = torch.empty(B, **i32), torch.empty(B, **i32)
+    path, tgt_argmax = torch.empty((B, n_max), **i32), torch.empty((B, n_max), **i32)
+    entropy, p_tok = torch.empty((B, n_max), **f32), torch.empty((B, n_max), **f32)
+    out_tokens = torch.empty((B, n_max), **i32) if want_tokens else None
+    _lib.check("tv_accept_typical", lib.tv_accept_typical(
+        _ptr(logits), _DTYPES[logits.dtype], V, _ptr(cand_tok), _ptr(parents), _ptr(anc), _ptr(depth),
+        _ptr(n_nodes), _ptr(err), B, n_max, float(epsilon), float(delta), _ptr(entropy), _ptr(p_tok),
+        _ptr(tgt_argmax), _ptr(accept_len), _ptr(path), _ptr(bonus), _ptr(out_tokens), _stream(stream)))
+    return accept_len, path, bonus, out_tokens, entropy, p_tok, tgt_argmax
 
 
 def commit(k_cache, v_cache, prefix_len_in, accept_len, path, prefix_len_out=None, stream=None):

@@ -40,6 +40,8 @@ SIGNATURES = {
     "tv_tree_attention_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(TvAttnArgs)]),
     "tv_tree_attention": (_I, [ctypes.POINTER(TvAttnArgs), _P]),
     "tv_accept": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P]),
+    "tv_accept_typical": (_I, [_P, _I, _I, _P, _P, _P, _P, _P, _P, _I, _I, ctypes.c_float,
+                               ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P]),
     "tv_commit": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _I, _P, _P]),
 }
 

@@ -84,6 +84,30 @@ tv_status tv_accept(const int32_t* cand_tok, const int32_t* tgt_argmax, const in
                                     n_max, accept_len, path, bonus_tok, out_tokens, stream));
 }
 
+tv_status tv_accept_typical(const void* logits, int32_t dtype, int32_t vocab,
+                            const int32_t* cand_tok, const int32_t* parents, const uint64_t* anc,
+                            const int32_t* depth, const int32_t* n_nodes, const int32_t* err,
+                            int32_t B, int32_t n_max, float epsilon, float delta, float* entropy,
+                            float* p_tok, int32_t* tgt_argmax, int32_t* accept_len, int32_t* path,
+                            int32_t* bonus_tok, int32_t* out_tokens, hipStream_t stream) {
+  if (B < 0 || B > 65535 || n_max < 1 || n_max > TV_MAX_NODES || vocab < 1)
+    return TV_ERR_INVALID_ARG;
+  if (!dtype_ok(dtype)) return TV_ERR_INVALID_ARG;
+  // NaN thresholds fail both comparisons; negative ones mean "no floor"
+  if (!(epsilon == epsilon) || !(delta == delta)) return TV_ERR_INVALID_ARG;
+  if (B == 0) return TV_OK;
+  if (!logits || !cand_tok || !parents || !anc || !depth || !n_nodes || !entropy || !p_tok ||
+      !tgt_argmax || !accept_len || !path || !bonus_tok)
+    return TV_ERR_INVALID_ARG;
+  const hipError_t e = tv::launch_typical_stats(logits, elem_bytes(dtype), vocab, cand_tok, parents,
+                                                n_nodes, err, B, n_max, entropy, p_tok, tgt_argmax,
+                                                stream);
+  if (e != hipSuccess) return TV_ERR_HIP;
+  return from_hip(tv::launch_accept_typical(cand_tok, tgt_argmax, p_tok, entropy, epsilon, delta,
+                                            parents, anc, depth, n_nodes, err, B, n_max,
+                                            accept_len, path, bonus_tok, out_tokens, stream));
+}
+
 tv_status tv_commit(void* k_cache, void* v_cache, int32_t B, int32_t Hkv, int32_t cap, int32_t D,
                     int32_t dtype, const int32_t* prefix_len_in, const int32_t* accept_len,
                     const int32_t* path, int32_t n_max, int32_t* prefix_len_out,

@@ -19,6 +19,18 @@ hipError_t launch_accept(const int32_t* cand_tok, const int32_t* tgt, const int3
                          const int32_t* err, int B, int n_max, int32_t* accept_len,
                          int32_t* path, int32_t* bonus, int32_t* out_tokens, hipStream_t s);
 
+hipError_t launch_accept_typical(const int32_t* cand_tok, const int32_t* tgt_argmax,
+                                 const float* p_tok, const float* entropy, float eps, float delta,
+                                 const int32_t* parents, const uint64_t* anc, const int32_t* depth,
+                                 const int32_t* n_nodes, const int32_t* err, int B, int n_max,
+                                 int32_t* accept_len, int32_t* path, int32_t* bonus,
+                                 int32_t* out_tokens, hipStream_t s);
+
+hipError_t launch_typical_stats(const void* logits, int elem_bytes, int V, const int32_t* cand_tok,
+                                const int32_t* parents, const int32_t* n_nodes, const int32_t* err,
+                                int B, int n_max, float* entropy, float* p_tok, int32_t* argmax,
+                                hipStream_t s);
+
 hipError_t launch_commit(void* k_cache, void* v_cache, int B, int Hkv, int cap, int D,
                          int elem_bytes, const int32_t* prefix_len_in, const int32_t* accept_len,
                          const int32_t* path, int n_max, int32_t* prefix_len_out, hipStream_t s);

@@ -1,10 +1,11 @@
-// Tree set-up, greedy acceptance and KV commit: the integer side of a
-// verification step. One 64-lane wavefront per sequence; lane i is node i.
+// Tree set-up, acceptance and KV commit: the integer side of a verification
+// step. One 64-lane wavefront per sequence; lane i is node i.
 //
 // Tree mask and depth positions: infra-guide "5.3 Medusa、EAGLE 与 MTP",
 // sections 3.1, 3.2 and 8. Acceptance: pofe.ai "Medusa and EAGLE ...",
 // greedy case of "Typical acceptance"; vibeengines.com "Medusa, explained",
-// step 7; infra-guide section 9.2. Commit: infra-guide section 3.2 and summary.
+// step 7 and "Typical acceptance"; infra-guide sections 9.1 and 9.2. Commit:
+// infra-guide section 3.2 and summary.
 #include "tv_device.h"
 #include "tv_internal.h"
 
@@ -59,18 +60,23 @@ __global__ __launch_bounds__(64) void build_tree_kernel(const int32_t* __restric
 }
 
 // ---------------------------------------------------------------------------
-// accept: node c >= 1 matches iff its token equals the target's choice at its
-// parent; the root always matches. A node is accepted iff every node in its
-// ancestors-or-self mask matches, i.e. (anc & ~match_mask) == 0. The deepest
-// accepted node wins (ties: lowest index); its mask, read bit by bit in
-// ascending order, is the path.
+// accept: the root always matches. Greedy rule: node c >= 1 matches iff its
+// token equals the target's choice at its parent. Typical rule: node c >= 1
+// matches iff the target's probability of its token at its parent, p_tok[c],
+// exceeds min(eps, delta * exp(-H(parent))). A node is accepted iff every
+// node in its ancestors-or-self mask matches, i.e. (anc & ~match_mask) == 0.
+// The deepest accepted node wins (ties: lowest index); its mask, read bit by
+// bit in ascending order, is the path. The bonus token is tgt at that node
+// (the target's argmax there, for both rules).
 // ---------------------------------------------------------------------------
+template <bool TYPICAL>
 __global__ __launch_bounds__(64) void accept_kernel(
     const int32_t* __restrict__ cand_tok, const int32_t* __restrict__ tgt,
     const int32_t* __restrict__ parents, const uint64_t* __restrict__ anc,
     const int32_t* __restrict__ depth, const int32_t* __restrict__ n_nodes,
     const int32_t* __restrict__ err, int n_max, int32_t* __restrict__ accept_len,
-    int32_t* __restrict__ path, int32_t* __restrict__ bonus, int32_t* __restrict__ out_tokens) {
+    int32_t* __restrict__ path, int32_t* __restrict__ bonus, int32_t* __restrict__ out_tokens,
+    const float* __restrict__ p_tok, const float* __restrict__ entropy, float eps, float delta) {
   const int b = blockIdx.x;
   const int i = threadIdx.x;
   const size_t row = static_cast<size_t>(b) * n_max;
@@ -81,6 +87,11 @@ __global__ __launch_bounds__(64) void accept_kernel(
   const int tg_in = in_row ? tgt[row + i] : 0;
   const uint64_t a_in = in_row ? anc[row + i] : 0ull;
   const int dp_in = in_row ? depth[row + i] : 0;
+  float pt_in = 0.f, h_in = 0.f;
+  if constexpr (TYPICAL) {
+    pt_in = in_row ? p_tok[row + i] : 0.f;
+    h_in = in_row ? entropy[row + i] : 0.f;
+  }
   const int n = n_nodes[b];
   const int e_in = err ? err[b] : 0;
   bool active = (e_in == 0) && (n > 0) && (n <= n_max);
@@ -92,8 +103,16 @@ __global__ __launch_bounds__(64) void accept_kernel(
   const uint64_t a = live ? a_in : 0ull;
   const int dp = live ? dp_in : 0;
 
-  const int tg_parent = __shfl(tg, (p >= 0 && p < 64) ? p : i);
-  const bool match = live && (i == 0 || tk == tg_parent);
+  // every lane takes part in the shuffles (none sits behind a branch)
+  const int src = (p >= 0 && p < 64) ? p : i;
+  const int tg_parent = __shfl(tg, src);
+  const float h_parent = TYPICAL ? __shfl(h_in, src) : 0.f;
+  bool match;
+  if constexpr (TYPICAL) {
+    match = live && (i == 0 || pt_in > fminf(eps, delta * expf(-h_parent)));
+  } else {
+    match = live && (i == 0 || tk == tg_parent);
+  }
   const uint64_t M = __ballot(match);
   const bool accepted = live && (a != 0ull) && ((a & ~M) == 0ull);
   int key = accepted ? ((dp << 8) | (255 - i)) : -1;
@@ -212,8 +231,21 @@ hipError_t launch_accept(const int32_t* cand_tok, const int32_t* tgt, const int3
                          const uint64_t* anc, const int32_t* depth, const int32_t* n_nodes,
                          const int32_t* err, int B, int n_max, int32_t* accept_len,
                          int32_t* path, int32_t* bonus, int32_t* out_tokens, hipStream_t s) {
-  hipLaunchKernelGGL(accept_kernel, dim3(B), dim3(64), 0, s, cand_tok, tgt, parents, anc, depth,
-                     n_nodes, err, n_max, accept_len, path, bonus, out_tokens);
+  hipLaunchKernelGGL(accept_kernel<false>, dim3(B), dim3(64), 0, s, cand_tok, tgt, parents, anc,
+                     depth, n_nodes, err, n_max, accept_len, path, bonus, out_tokens, nullptr,
+                     nullptr, 0.f, 0.f);
+  return hipGetLastError();
+}
+
+hipError_t launch_accept_typical(const int32_t* cand_tok, const int32_t* tgt_argmax,
+                                 const float* p_tok, const float* entropy, float eps, float delta,
+                                 const int32_t* parents, const uint64_t* anc, const int32_t* depth,
+                                 const int32_t* n_nodes, const int32_t* err, int B, int n_max,
+                                 int32_t* accept_len, int32_t* path, int32_t* bonus,
+                                 int32_t* out_tokens, hipStream_t s) {
+  hipLaunchKernelGGL(accept_kernel<true>, dim3(B), dim3(64), 0, s, cand_tok, tgt_argmax, parents,
+                     anc, depth, n_nodes, err, n_max, accept_len, path, bonus, out_tokens, p_tok,
+                     entropy, eps, delta);
   return hipGetLastError();
 }
 
