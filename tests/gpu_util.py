@@ -51,6 +51,10 @@ def run_step(w, d: dict, parents_override=None, n_nodes_override=None, prefix_ov
 
 
 def attention_error(dtype: str, got: np.ndarray, ref: np.ndarray) -> float:
+    """Max abs error (bf16) or max row-relative error (fp32); a non-finite
+    output counts as an infinite error."""
+    if not np.isfinite(got).all():
+        return float("inf")
     if dtype == "f32":
         num = np.abs(got - ref).max(axis=-1)
         den = np.maximum(np.abs(ref).max(axis=-1), 1e-30)

@@ -1141,9 +1141,15 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
     int t = 0;
     if (n_masked > 0) {
       // every tree tile is formed before the first product, so the tree's
-      // lane items are not live across a product
+      // lane items are not live across a product. Only tiles 0 .. kAhead - 1
+      // are in flight here (tile kAhead goes out in the first iteration), so
+      // after the last tree tile come min(kAhead, n_tiles) - n_masked tiles
+      // (one fewer than wait_tile assumes when the tree spans two tiles).
       stage_tree_values();
-      wait_tile(n_masked - 1);
+      const int after = min(kAhead, n_tiles) - n_masked;
+      if (after >= 2) wait_vm<2 * CPT * 2>();
+      else if (after == 1) wait_vm<2 * CPT>();
+      else wait_vm<0>();
       __syncthreads();
       for (int m = 0; m < n_masked; ++m) fill_tree(m);
       __syncthreads();
