@@ -200,10 +200,13 @@ tv_status tv_accept(const int32_t* cand_tok, const int32_t* tgt_argmax,
  *     argmax at e (lowest token id among equal maxima);
  *   - a token id outside [0, vocab) has probability 0 and never passes.
  *
- *   logits     [B][n_max][vocab] of dtype (TV_BF16 or TV_F32), finite; read
- *              once (rows of padding nodes and skipped sequences are not
- *              read). 16-byte aligned rows (vocab * element size a multiple
- *              of 16, aligned base) take the vector path; others work too.
+ *   logits     [B][n_max][vocab] of dtype (TV_BF16 or TV_F32), finite, all of
+ *              it readable; each live row is read once. A row's first
+ *              64 KiB go out before the node count is known, so rows of
+ *              padding nodes and skipped sequences may be read that far,
+ *              never further, and are otherwise ignored. 16-byte aligned
+ *              rows (vocab * element size a multiple of 16, aligned base)
+ *              take the vector path; others work too.
  *   cand_tok, parents, anc, depth, n_nodes, err as for tv_accept
  *   epsilon, delta  the two thresholds (not NaN)
  *   entropy    [B][n_max] float out: H at node i (nats)

@@ -10,14 +10,18 @@
 // child c of i the probability of c's token under i's distribution; the
 // tree scan that follows (tv_tree.hip) applies the rule.
 //
-// One workgroup of 256 threads per (node, sequence) reads that node's logits
-// row once, in 16-byte chunks, eight chunks in flight per thread. Each thread
-// keeps, in base-2 units, the largest logit mx, m = mx * log2(e),
-// z = sum 2^u and s = sum u * 2^u over u = x * log2(e) - m; partial
-// statistics combine by rescaling to the larger maximum. Then
-// H = ln 2 * (log2 z - s / z) nats and p(t) = 2^(x_t * log2(e) - m) / z.
-// The row is HBM traffic read exactly once; the child tokens' logits are
-// fetched after the first batch, while the rest of the row streams in.
+// One workgroup of 512 threads per (node, sequence) reads that node's logits
+// row once, in 16-byte chunks, eight chunks in flight per thread (a whole
+// 32000-entry bf16 row in one round trip). Each thread keeps the largest
+// logit and its first index, and, in base-2 units, z = sum 2^u and
+// s = sum u * 2^u over u = x * log2(e) - ref for a reference ref that trails
+// its maximum; partial statistics combine by moving to the larger reference.
+// Then H = ln 2 * (log2 z - s / z) nats and p(t) = 2^(x_t * log2(e) - ref) / z.
+// The row is HBM traffic read exactly once. Its first batch goes out before
+// the node count is known (so a padding row's first batch may be read and
+// dropped), and the candidate tokens' logits are gathered while the row
+// streams in: lane t reads node t's token and then row i at that token
+// before it is known whether t is a child of i.
 #include <climits>
 
 #include "tv_device.h"
@@ -26,24 +30,35 @@
 namespace tv {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kBatch = 8;   // chunks per thread in flight
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// 2^u for u <= 0 by the bare hardware instruction: results below 2^-126
+// flush to 0, which changes no sum here (every row's sum is at least 1).
+__device__ __forceinline__ float exp2_sum_term(float u) { return __builtin_amdgcn_exp2f(u); }
+
+// The sums are kept relative to a reference ref (log2 units) that trails
+// the running maximum: u = x * log2(e) - ref stays below kSlack, and ref is
+// raised (the sums rescaled) only when a chunk's maximum would exceed that.
+// Any reference gives the same p and H, since both are ratios of the sums.
+constexpr float kSlack = 8.0f;
+
 struct RowStat {
   float mx;   // largest logit seen, -inf if none
   int idx;    // lowest index holding mx
-  float z;    // sum of 2^u, u relative to mx * log2(e)
+  float ref;  // reference of the sums, -inf if none
+  float z;    // sum of 2^u, u = x * log2(e) - ref
   float s;    // sum of u * 2^u
 };
 
-// Rescales a's sums from its own maximum to the larger maximum mx.
-__device__ __forceinline__ void rescaled(const RowStat& a, float m, float& z, float& s) {
+// Adds a's sums, moved from a.ref to the reference ref >= a.ref.
+__device__ __forceinline__ void rescaled(const RowStat& a, float ref, float& z, float& s) {
   if (a.z > 0.f) {
-    const float d = a.mx * kLog2e - m;   // <= 0
-    const float f = exp2f(d);
+    const float d = a.ref - ref;   // <= 0
+    const float f = exp2_sum_term(d);
     z += f * a.z;
     s += f * fmaf(d, a.z, a.s);
   }
@@ -55,11 +70,11 @@ __device__ __forceinline__ RowStat combine(RowStat a, RowStat b) {
   const int ia = a.idx, ib = b.idx;
   const bool take_b = (b.mx > a.mx) || (b.mx == a.mx && ib < ia);
   r.idx = take_b ? ib : ia;
-  const float m = r.mx * kLog2e;
+  r.ref = fmaxf(a.ref, b.ref);
   r.z = 0.f;
   r.s = 0.f;
-  rescaled(a, m, r.z, r.s);
-  rescaled(b, m, r.z, r.s);
+  rescaled(a, r.ref, r.z, r.s);
+  rescaled(b, r.ref, r.z, r.s);
   return r;
 }
 
@@ -102,7 +117,64 @@ __device__ __forceinline__ float load_elem(const T* row, int t) {
   else return reinterpret_cast<const float*>(row)[t];
 }
 
-// Grid (n_max, B), 256 threads. T is uint16_t (bf16 bits) or float; E the
+// c ? a : b on values, component by component (a select of whole
+// aggregates becomes a select of their addresses and sends them to scratch)
+__device__ __forceinline__ uint4 pick(bool c, uint4 a, uint4 b) {
+  return make_uint4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
+}
+__device__ __forceinline__ uint32_t pick(bool c, uint32_t a, uint32_t b) { return c ? a : b; }
+
+// Every load is unconditional (indices clamped into the row; out-of-range
+// chunks are loaded again and skipped by the arithmetic), so that the wait
+// before each chunk's use counts exactly the loads still in flight behind it.
+template <typename T, int E>
+__device__ __forceinline__ void load_batch(typename ChunkOf<T, E>::type (&v)[kBatch], const T* row, int base,
+                                           int nchunks, int tid) {
+#pragma unroll
+  for (int k = 0; k < kBatch; ++k) v[k] = load_chunk<T, E>(row, min(base + k * kThreads + tid, nchunks - 1));
+}
+
+// Folds a batch into the running statistics, chunk by chunk as they land: a
+// chunk whose maximum would put u above kSlack first raises the reference
+// (rare after the first chunk), and the chunk holding the maximum is kept,
+// so that the index is found once at the end (chunks ascend, and only a
+// strictly larger maximum replaces it, so the first index wins).
+template <typename T, int E>
+__device__ __forceinline__ void fold_batch(const typename ChunkOf<T, E>::type (&v)[kBatch], int base, int nchunks,
+                                           int tid, RowStat& st, typename ChunkOf<T, E>::type& vmax,
+                                           int& cmax_at) {
+#pragma unroll
+  for (int k = 0; k < kBatch; ++k) {
+    const int c = base + k * kThreads + tid;
+    if (c < nchunks) {
+      float cm = chunk_elem<T, E>(v[k], 0);
+#pragma unroll
+      for (int j = 1; j < E; ++j) cm = fmaxf(cm, chunk_elem<T, E>(v[k], j));
+      const float cref = cm * kLog2e;
+      if (cref > st.ref + kSlack) {
+        float z = 0.f, s = 0.f;
+        rescaled(st, cref, z, s);
+        st.ref = cref;
+        st.z = z;
+        st.s = s;
+      }
+      const bool raised = cm > st.mx;
+      vmax = pick(raised, v[k], vmax);
+      cmax_at = raised ? c : cmax_at;
+      st.mx = fmaxf(st.mx, cm);
+      const float m = st.ref;
+#pragma unroll
+      for (int j = 0; j < E; ++j) {
+        const float u = fmaf(chunk_elem<T, E>(v[k], j), kLog2e, -m);
+        const float w = exp2_sum_term(u);
+        st.z += w;
+        st.s = fmaf(u, w, st.s);
+      }
+    }
+  }
+}
+
+// Grid (n_max, B), 512 threads. T is uint16_t (bf16 bits) or float; E the
 // elements per chunk (V must be a multiple of E on the vector paths).
 template <typename T, int E>
 __global__ __launch_bounds__(kThreads) void typical_stats_kernel(
@@ -117,11 +189,28 @@ __global__ __launch_bounds__(kThreads) void typical_stats_kernel(
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
   const size_t seq = static_cast<size_t>(b) * n_max;
+  const T* row = logits + (seq + i) * static_cast<size_t>(V);
+
+  // wave 0, lane t = node t: its parent, its token and row i's logit at that
+  // token, gathered without waiting for the node count
+  const bool lane_node = tid >= 1 && tid < n_max;
+  const int node_c = min(tid, n_max - 1);
+  const int par = parents[seq + node_c];
+  const int tok = cand_tok[seq + node_c];
+
+  // the row's first batch goes out before the node count is known (a padding
+  // row's batch is then dropped unread)
+  const int nchunks = V / E;
+  Chunk v0[kBatch];
+  load_batch<T, E>(v0, row, 0, nchunks, tid);
+  const bool tok_in = lane_node && tok >= 0 && tok < V;
+  const float x_tok = load_elem<T>(row, tok_in ? tok : 0);
+
   const int n = n_nodes[b];
   const int e_in = err ? err[b] : 0;
   const bool active = (e_in == 0) && (n > 0) && (n <= n_max);
   if (!active || i >= n) {
-    // padding node or skipped sequence: nothing reads this row
+    // padding node or skipped sequence
     if (tid == 0) {
       entropy[seq + i] = 0.f;
       argmax[seq + i] = -1;
@@ -129,61 +218,21 @@ __global__ __launch_bounds__(kThreads) void typical_stats_kernel(
     }
     return;
   }
+  const bool child = lane_node && tid < n && par == i;
 
-  // children of i and their tokens (lanes of wave 0; node t is lane t)
-  const bool child = (tid >= 1) && (tid < n) && (parents[seq + tid] == i);
-  const int tok = child ? cand_tok[seq + tid] : -1;
-  const bool in_vocab = child && tok >= 0 && tok < V;
-
-  const T* row = logits + (seq + i) * static_cast<size_t>(V);
-  const int nchunks = V / E;
-  RowStat st{-INFINITY, INT_MAX, 0.f, 0.f};
-  float x_tok = 0.f;
-  for (int base = 0; base < nchunks; base += kThreads * kBatch) {
+  RowStat st{-INFINITY, INT_MAX, -INFINITY, 0.f, 0.f};
+  Chunk vmax{};
+  int cmax_at = -1;
+  fold_batch<T, E>(v0, 0, nchunks, tid, st, vmax, cmax_at);
+  for (int base = kThreads * kBatch; base < nchunks; base += kThreads * kBatch) {
     Chunk v[kBatch];
+    load_batch<T, E>(v, row, base, nchunks, tid);
+    fold_batch<T, E>(v, base, nchunks, tid, st, vmax, cmax_at);
+  }
+  if (cmax_at >= 0) {
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const int c = base + k * kThreads + tid;
-      if (c < nchunks) v[k] = load_chunk<T, E>(row, c);
-    }
-    // batch maximum; chunks and elements ascend, so ">" keeps the first index
-    float bmx = -INFINITY;
-    int bidx = INT_MAX;
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const int c = base + k * kThreads + tid;
-      if (c < nchunks) {
-#pragma unroll
-        for (int j = 0; j < E; ++j) {
-          const float x = chunk_elem<T, E>(v[k], j);
-          if (x > bmx) {
-            bmx = x;
-            bidx = c * E + j;
-          }
-        }
-      }
-    }
-    if (bmx > st.mx) {
-      float z = 0.f, s = 0.f;
-      rescaled(st, bmx * kLog2e, z, s);
-      st = RowStat{bmx, bidx, z, s};
-    }
-    const float m = st.mx * kLog2e;
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const int c = base + k * kThreads + tid;
-      if (c < nchunks) {
-#pragma unroll
-        for (int j = 0; j < E; ++j) {
-          const float u = fmaf(chunk_elem<T, E>(v[k], j), kLog2e, -m);
-          const float w = exp2f(u);
-          st.z += w;
-          st.s = fmaf(u, w, st.s);
-        }
-      }
-    }
-    // the child tokens' logits go out behind the first batch
-    if (base == 0 && in_vocab) x_tok = load_elem<T>(row, tok);
+    for (int j = E - 1; j >= 0; --j)
+      if (chunk_elem<T, E>(vmax, j) == st.mx) st.idx = cmax_at * E + j;
   }
 
   // wave, then workgroup
@@ -192,6 +241,7 @@ __global__ __launch_bounds__(kThreads) void typical_stats_kernel(
     RowStat o;
     o.mx = __shfl_xor(st.mx, off);
     o.idx = __shfl_xor(st.idx, off);
+    o.ref = __shfl_xor(st.ref, off);
     o.z = __shfl_xor(st.z, off);
     o.s = __shfl_xor(st.s, off);
     st = combine(st, o);
@@ -206,8 +256,7 @@ __global__ __launch_bounds__(kThreads) void typical_stats_kernel(
 #pragma unroll
   for (int w = 1; w < kWaves; ++w) r = combine(r, part[w]);
 
-  const float m = r.mx * kLog2e;
-  if (child) p_tok[seq + tid] = in_vocab ? exp2f(fmaf(x_tok, kLog2e, -m)) / r.z : 0.f;
+  if (child) p_tok[seq + tid] = tok_in ? exp2f(fmaf(x_tok, kLog2e, -r.ref)) / r.z : 0.f;
   if (tid == 0) {
     entropy[seq + i] = kLn2 * (log2f(r.z) - r.s / r.z);
     argmax[seq + i] = r.idx;
