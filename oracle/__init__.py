@@ -19,7 +19,10 @@ from .tv_oracle import (  # noqa: F401
     ancestors_or_self,
     attention_row,
     build_tree,
+    PAGE,
     commit,
+    gather_pages,
+    scatter_pages,
     next_token_distribution,
     rope,
     tree_attention,

@@ -426,6 +426,50 @@ def commit(k_cache, v_cache, prefix_len, accept_len, path):
     return k_new, v_new, plen
 
 
+# ---------------------------------------------------------------------------
+# Paged KV: the cache of each sequence as a list of fixed-size pages
+# ---------------------------------------------------------------------------
+
+PAGE = 64   # slots per page
+
+
+def gather_pages(k_pool, v_pool, block_table):
+    """The dense per-sequence cache that a paged cache stands for.
+
+    [INFRA-5.3] section 8 names the block table of a paged KV cache as what a
+    real implementation adds: logical slot s of sequence b lives in page
+    block_table[b][s // PAGE], at offset s % PAGE. Pools are slot-major here:
+    k_pool and v_pool [num_pages][Hkv][PAGE][D]. Returns k, v
+    [B][Hkv][max_pages * PAGE][D] (a copy).
+    """
+    B, max_pages = block_table.shape
+    _, Hkv, page, D = k_pool.shape
+    k = np.zeros((B, Hkv, max_pages * page, D), dtype=k_pool.dtype)
+    v = np.zeros((B, Hkv, max_pages * page, D), dtype=v_pool.dtype)
+    for b in range(B):
+        for j in range(max_pages):
+            pg = int(block_table[b, j])
+            k[b, :, j * page:(j + 1) * page] = k_pool[pg]
+            v[b, :, j * page:(j + 1) * page] = v_pool[pg]
+    return k, v
+
+
+def scatter_pages(k, v, block_table, k_pool, v_pool):
+    """Writes a dense per-sequence cache back into (copies of) the pools: the
+    inverse of gather_pages on the pages the table references. Pages that no
+    sequence references keep their contents. Returns (k_pool, v_pool)."""
+    kp = np.array(k_pool, copy=True)
+    vp = np.array(v_pool, copy=True)
+    B, max_pages = block_table.shape
+    page = kp.shape[2]
+    for b in range(B):
+        for j in range(max_pages):
+            pg = int(block_table[b, j])
+            kp[pg] = k[b, :, j * page:(j + 1) * page]
+            vp[pg] = v[b, :, j * page:(j + 1) * page]
+    return kp, vp
+
+
 def verify_step(inputs: dict, rows=None) -> dict:
     """One whole verification step: tree set-up, attention, acceptance, commit.
 
