@@ -24,8 +24,8 @@
  *     and never synchronises. The return value reports host-side argument
  *     checks and launch errors only.
  *   - Data-dependent problems are reported per sequence in a device array
- *     `err[B]` (0 = ok, TV_ERR_BAD_TREE, TV_ERR_CAPACITY). Later calls treat
- *     a sequence with err != 0 as inactive.
+ *     `err[B]` (0 = ok, TV_ERR_BAD_TREE, TV_ERR_CAPACITY, TV_ERR_BAD_PAGE).
+ *     Later calls treat a sequence with err != 0 as inactive.
  *   - Trees: node 0 is the root (the last verified token), parents[b][0] ==
  *     -1 and 0 <= parents[b][i] < i for 1 <= i < n_nodes[b]; nodes
  *     n_nodes[b] .. n_max-1 are padding and ignored. n_nodes[b] == 0 marks an
@@ -53,7 +53,9 @@ typedef enum tv_status {
   TV_ERR_BAD_TREE = 2,      /* per-sequence only: parents not a tree        */
   TV_ERR_CAPACITY = 3,      /* per-sequence only: prefix + tree > cache     */
   TV_ERR_UNSUPPORTED = 4,   /* valid but not implemented (e.g. head dim)    */
-  TV_ERR_HIP = 5            /* a HIP launch or runtime call failed          */
+  TV_ERR_HIP = 5,           /* a HIP launch or runtime call failed          */
+  TV_ERR_BAD_PAGE = 6       /* per-sequence only: a block-table entry names
+                               a page outside the pools                     */
 } tv_status;
 
 typedef enum tv_dtype { TV_F32 = 0, TV_BF16 = 1 } tv_dtype;
@@ -148,6 +150,44 @@ size_t tv_tree_attention_workspace_size(const tv_attn_args* a);
  * B == 0 is a no-op.
  */
 tv_status tv_tree_attention(const tv_attn_args* a, hipStream_t stream);
+
+/*
+ * Paged KV cache ([INFRA-5.3] section 8 names the block table of a paged KV
+ * cache as what a real implementation adds to the dense sketch).
+ *
+ * The cache is a pool of pages of 64 slots (the V block size): K pages
+ * [num_pages][Hkv][64][D] (slot-major within a page) and V pages
+ * [num_pages][Hkv][D][64] (head-dim-major, as one block of the dense V
+ * layout). Logical slot s of sequence b is slot s % 64 of page
+ * block_table[b * max_pages + s / 64]. A sequence's capacity is
+ * 64 * max_pages slots. Pages that only hold prefix slots (below P) are read
+ * only and may be shared by several sequences; the pages holding slots
+ * [P, P + n_nodes) are written (tree append, commit) and must belong to one
+ * sequence. Entries past a sequence's P + n_nodes slots are never read.
+ */
+#define TV_MAX_PAGES_PER_SEQ 256
+
+typedef struct tv_paged_kv {
+  const int32_t* block_table;  /* [B][max_pages] page ids, device memory     */
+  int32_t max_pages;           /* 1 .. TV_MAX_PAGES_PER_SEQ (attention)      */
+  int32_t num_pages;           /* pages in each pool                         */
+} tv_paged_kv;
+
+/*
+ * tv_tree_attention_paged -- tv_tree_attention over a paged cache.
+ *
+ * Same computation, arguments and side effect as tv_tree_attention, except
+ * that a->k_cache and a->v_cache are the K and V page pools and a->cap must
+ * equal 64 * pk->max_pages; the workspace is tv_tree_attention_workspace_size
+ * of the same arguments. A sequence whose blocks [0, (P + n) / 64] name a page
+ * outside [0, num_pages) gets err = TV_ERR_BAD_PAGE and zero output rows;
+ * no page outside the pools is read or written.
+ * Host checks as tv_tree_attention, plus pk non-null with a non-null table,
+ * max_pages >= 1, num_pages >= 1, a->cap == 64 * max_pages; TV_BF16 only and
+ * max_pages <= TV_MAX_PAGES_PER_SEQ, else TV_ERR_UNSUPPORTED.
+ */
+tv_status tv_tree_attention_paged(const tv_attn_args* a, const tv_paged_kv* pk,
+                                  hipStream_t stream);
 
 /*
  * tv_accept -- greedy longest-accepted-path selection.
@@ -253,6 +293,19 @@ tv_status tv_commit(void* k_cache, void* v_cache, int32_t B, int32_t Hkv, int32_
                     int32_t D, int32_t dtype, const int32_t* prefix_len_in,
                     const int32_t* accept_len, const int32_t* path, int32_t n_max,
                     int32_t* prefix_len_out, hipStream_t stream);
+
+/*
+ * tv_commit_paged -- tv_commit over a paged cache (see tv_tree_attention_paged
+ * for the layout): slot P + d <- slot P + path[b][d], d = 0..L, through the
+ * block table. A move touching a page outside the pools leaves that sequence
+ * unchanged (prefix_len_out = prefix_len_in). Host checks as tv_commit with
+ * cap = 64 * pk->max_pages, plus pk non-null with a non-null table,
+ * max_pages >= 1, num_pages >= 1.
+ */
+tv_status tv_commit_paged(void* k_pool, void* v_pool, const tv_paged_kv* pk, int32_t B,
+                          int32_t Hkv, int32_t D, int32_t dtype, const int32_t* prefix_len_in,
+                          const int32_t* accept_len, const int32_t* path, int32_t n_max,
+                          int32_t* prefix_len_out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

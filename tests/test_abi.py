@@ -23,7 +23,8 @@ def declared_functions():
 
 def test_header_declares_expected_calls():
     names = declared_functions()
-    for must in ("tv_build_tree", "tv_tree_attention", "tv_accept", "tv_commit", "tv_accept_typical"):
+    for must in ("tv_build_tree", "tv_tree_attention", "tv_accept", "tv_commit", "tv_accept_typical",
+                 "tv_tree_attention_paged", "tv_commit_paged"):
         assert must in names
 
 
@@ -38,8 +39,9 @@ def test_every_declared_symbol_is_exported_and_bound():
 def test_status_strings_and_version():
     lib = _lib.load()
     assert lib.tv_version().decode().startswith("tv ")
-    for code in range(6):
+    for code in range(7):
         assert lib.tv_status_string(code)
+    assert lib.tv_status_string(_lib.TV_ERR_BAD_PAGE).decode().startswith("block table")
     assert lib.tv_status_string(_lib.TV_ERR_CAPACITY).decode().startswith("prefix")
 
 
@@ -122,3 +124,36 @@ def test_attention_host_validation_and_workspace():
     assert run(attn(workspace=0x1000, workspace_bytes=need - 1)) == _lib.TV_ERR_INVALID_ARG
     assert lib.tv_tree_attention_workspace_size(ctypes.byref(attn(dtype=_lib.TV_F32))) == 0
     assert lib.tv_tree_attention_workspace_size(ctypes.byref(attn(Hq=30))) == 0
+
+
+def test_paged_host_validation():
+    lib = _lib.load()
+    null = None
+
+    def pk(max_pages=65, num_pages=100, table=0x2000):
+        p = _lib.TvPagedKv()
+        p.block_table, p.max_pages, p.num_pages = table, max_pages, num_pages
+        return p
+
+    def call(a, p):
+        return lib.tv_tree_attention_paged(ctypes.byref(a), None if p is None else ctypes.byref(p), null)
+    ok_args = attn(cap=65 * 64, workspace=0x3000, workspace_bytes=1 << 40)
+    assert call(ok_args, None) == _lib.TV_ERR_INVALID_ARG                    # no table struct
+    assert call(ok_args, pk(table=0)) == _lib.TV_ERR_INVALID_ARG            # null table
+    assert call(ok_args, pk(max_pages=0)) == _lib.TV_ERR_INVALID_ARG
+    assert call(ok_args, pk(num_pages=0)) == _lib.TV_ERR_INVALID_ARG
+    assert call(attn(cap=64 * 64), pk()) == _lib.TV_ERR_INVALID_ARG        # cap != 64 max_pages
+    assert call(attn(cap=300 * 64), pk(max_pages=300)) == _lib.TV_ERR_UNSUPPORTED   # > 256 pages
+    assert call(attn(cap=65 * 64, dtype=_lib.TV_F32, D=64), pk()) == _lib.TV_ERR_UNSUPPORTED
+    assert call(attn(cap=65 * 64, B=0), pk()) == _lib.TV_OK
+    fake = ctypes.c_void_p(0x1000)
+    p = pk()
+    assert lib.tv_commit_paged(fake, fake, None, 1, 2, 128, 1, fake, fake, fake, 5, fake, null) == _lib.TV_ERR_INVALID_ARG
+    assert lib.tv_commit_paged(fake, fake, ctypes.byref(pk(table=0)), 1, 2, 128, 1, fake, fake, fake, 5, fake,
+                               null) == _lib.TV_ERR_INVALID_ARG
+    assert lib.tv_commit_paged(fake, fake, ctypes.byref(p), 1, 2, 96, 1, fake, fake, fake, 5, fake,
+                               null) == _lib.TV_ERR_UNSUPPORTED
+    assert lib.tv_commit_paged(null, fake, ctypes.byref(p), 1, 2, 128, 1, fake, fake, fake, 5, fake,
+                               null) == _lib.TV_ERR_INVALID_ARG
+    assert lib.tv_commit_paged(null, null, ctypes.byref(p), 0, 2, 128, 1, null, null, null, 5, null,
+                               null) == _lib.TV_OK

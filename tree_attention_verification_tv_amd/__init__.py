@@ -23,11 +23,12 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import (TV_BF16, TV_ERR_BAD_TREE, TV_ERR_CAPACITY, TV_F32, TV_MAX_NODES,  # noqa: F401
-                   TvAttnArgs, TvError)
+from ._lib import (PAGE, TV_BF16, TV_ERR_BAD_PAGE, TV_ERR_BAD_TREE, TV_ERR_CAPACITY, TV_F32,  # noqa: F401
+                   TV_MAX_NODES, TvAttnArgs, TvError, TvPagedKv)
 
 __all__ = ["build_tree", "tree_attention", "tree_attention_workspace_size", "new_workspace", "accept",
-           "accept_typical", "commit",
+           "accept_typical", "commit", "tree_attention_paged", "commit_paged", "pages_from_dense",
+           "dense_from_pages", "TV_ERR_BAD_PAGE", "PAGE",
            "version", "TvError", "TV_ERR_BAD_TREE", "TV_ERR_CAPACITY", "attn_args",
            "v_cache_blocked", "v_cache_rows", "V_BLOCK"]
 
@@ -47,6 +48,37 @@ def v_cache_rows(v_blocked: torch.Tensor) -> torch.Tensor:
     """Inverse of v_cache_blocked: [B, Hkv, cap/64, D, 64] -> [B, Hkv, cap, D]."""
     B, H, nb, D, blk = v_blocked.shape
     return v_blocked.transpose(-1, -2).reshape(B, H, nb * blk, D).contiguous()
+
+
+def pages_from_dense(k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                     num_pages: int, k_pool=None, v_pool=None):
+    """Layout helper: writes dense caches (K [B, Hkv, cap, D], V blocked
+    [B, Hkv, cap/64, D, 64]) into page pools K [num_pages, Hkv, 64, D] and
+    V [num_pages, Hkv, D, 64] at the pages block_table [B, cap/64] names;
+    pages no entry names are zero (or keep k_pool / v_pool's contents)."""
+    B, H, cap, D = k_cache.shape
+    mp = cap // PAGE
+    if tuple(block_table.shape) != (B, mp):
+        raise ValueError("block_table must be [B, cap/64]")
+    if k_pool is None:
+        k_pool = torch.zeros((num_pages, H, PAGE, D), dtype=k_cache.dtype, device=k_cache.device)
+    if v_pool is None:
+        v_pool = torch.zeros((num_pages, H, D, PAGE), dtype=v_cache.dtype, device=v_cache.device)
+    idx = block_table.reshape(-1).long()
+    k_pool.index_copy_(0, idx, k_cache.reshape(B, H, mp, PAGE, D).permute(0, 2, 1, 3, 4).reshape(B * mp, H, PAGE, D))
+    v_pool.index_copy_(0, idx, v_cache.permute(0, 2, 1, 3, 4).reshape(B * mp, H, D, PAGE))
+    return k_pool, v_pool
+
+
+def dense_from_pages(k_pool: torch.Tensor, v_pool: torch.Tensor, block_table: torch.Tensor):
+    """Inverse of pages_from_dense: the dense caches (K [B, Hkv, cap, D], V
+    blocked [B, Hkv, cap/64, D, 64]) that the pools and table stand for."""
+    B, mp = block_table.shape
+    idx = block_table.reshape(-1).long()
+    _, H, _, D = k_pool.shape
+    k = k_pool[idx].reshape(B, mp, H, PAGE, D).permute(0, 2, 1, 3, 4).reshape(B, H, mp * PAGE, D)
+    v = v_pool[idx].reshape(B, mp, H, D, PAGE).permute(0, 2, 1, 3, 4).contiguous()
+    return k.contiguous(), v
 
 
 def version() -> str:
@@ -95,8 +127,9 @@ def build_tree(parents: torch.Tensor, n_nodes: torch.Tensor, anc=None, depth=Non
 
 
 def attn_args(q, k_new, v_new, k_cache, v_cache, prefix_len, n_nodes, anc, depth, err, out,
-              rope_theta=10000.0, softmax_scale=0.0, workspace=None) -> TvAttnArgs:
-    """Checks the tensors of one tree_attention call and fills tv_attn_args."""
+              rope_theta=10000.0, softmax_scale=0.0, workspace=None, block_table=None) -> TvAttnArgs:
+    """Checks the tensors of one tree_attention call and fills tv_attn_args
+    (with block_table, k_cache and v_cache are the page pools)."""
     if q.dtype not in _DTYPES:
         raise ValueError(f"q must be float32 or bfloat16 (got {q.dtype})")
     dt = q.dtype
@@ -108,15 +141,26 @@ def attn_args(q, k_new, v_new, k_cache, v_cache, prefix_len, n_nodes, anc, depth
     _dev(anc, "anc", torch.int64)
     B, n_max, Hq, D = q.shape
     Hkv = k_new.shape[2]
-    cap = k_cache.shape[2]
     if tuple(k_new.shape) != (B, n_max, Hkv, D) or tuple(v_new.shape) != (B, n_max, Hkv, D):
         raise ValueError("k_new / v_new must be [B, n_max, Hkv, D]")
-    if cap % V_BLOCK:
-        raise ValueError("cache capacity must be a multiple of 64")
-    if tuple(k_cache.shape) != (B, Hkv, cap, D):
-        raise ValueError("k_cache must be [B, Hkv, cap, D]")
-    if tuple(v_cache.shape) != (B, Hkv, cap // V_BLOCK, D, V_BLOCK):
-        raise ValueError("v_cache must be [B, Hkv, cap/64, D, 64] (see v_cache_blocked)")
+    if block_table is None:
+        cap = k_cache.shape[2]
+        if cap % V_BLOCK:
+            raise ValueError("cache capacity must be a multiple of 64")
+        if tuple(k_cache.shape) != (B, Hkv, cap, D):
+            raise ValueError("k_cache must be [B, Hkv, cap, D]")
+        if tuple(v_cache.shape) != (B, Hkv, cap // V_BLOCK, D, V_BLOCK):
+            raise ValueError("v_cache must be [B, Hkv, cap/64, D, 64] (see v_cache_blocked)")
+    else:
+        _dev(block_table, "block_table", torch.int32)
+        if block_table.dim() != 2 or block_table.shape[0] != B:
+            raise ValueError("block_table must be [B, max_pages]")
+        cap = block_table.shape[1] * PAGE
+        n_pages = k_cache.shape[0]
+        if tuple(k_cache.shape) != (n_pages, Hkv, PAGE, D):
+            raise ValueError("k_pool must be [num_pages, Hkv, 64, D]")
+        if tuple(v_cache.shape) != (n_pages, Hkv, D, PAGE):
+            raise ValueError("v_pool must be [num_pages, Hkv, D, 64]")
     if tuple(out.shape) != (B, n_max, Hq, D):
         raise ValueError("out must be [B, n_max, Hq, D]")
     if tuple(anc.shape) != (B, n_max) or tuple(depth.shape) != (B, n_max):
@@ -181,6 +225,65 @@ def tree_attention(q, k_new, v_new, k_cache, v_cache, prefix_len, n_nodes, anc, 
         a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
     _lib.check("tv_tree_attention", lib.tv_tree_attention(ctypes.byref(a), _stream(stream)))
     return out
+
+
+def paged_kv(block_table: torch.Tensor, k_pool: torch.Tensor) -> TvPagedKv:
+    """tv_paged_kv for a block table [B, max_pages] over pools of k_pool's size."""
+    _dev(block_table, "block_table", torch.int32)
+    pk = TvPagedKv()
+    pk.block_table = block_table.data_ptr()
+    pk.max_pages = block_table.shape[1]
+    pk.num_pages = k_pool.shape[0]
+    return pk
+
+
+def tree_attention_paged(q, k_new, v_new, k_pool, v_pool, block_table, prefix_len, n_nodes, anc, depth,
+                         err, rope_theta=10000.0, softmax_scale=0.0, out=None, workspace=None,
+                         stream=None):
+    """tree_attention over a paged cache: k_pool [num_pages, Hkv, 64, D],
+    v_pool [num_pages, Hkv, D, 64], block_table [B, max_pages] int32 (logical
+    slot s of sequence b is slot s % 64 of page block_table[b, s // 64]).
+    Appends the tree KV through the table; returns out [B, n_max, Hq, D]."""
+    lib = _lib.load()
+    if out is None:
+        out = torch.empty_like(q)
+    a = attn_args(q, k_new, v_new, k_pool, v_pool, prefix_len, n_nodes, anc, depth, err, out,
+                  rope_theta, softmax_scale, workspace, block_table=block_table)
+    pk = paged_kv(block_table, k_pool)
+    need = tree_attention_workspace_size(a)
+    if need > a.workspace_bytes:
+        if workspace is not None:
+            raise ValueError(f"workspace holds {a.workspace_bytes} bytes, {need} needed")
+        workspace = _default_workspace(q.device, need)
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
+    _lib.check("tv_tree_attention_paged",
+               lib.tv_tree_attention_paged(ctypes.byref(a), ctypes.byref(pk), _stream(stream)))
+    return out
+
+
+def commit_paged(k_pool, v_pool, block_table, prefix_len_in, accept_len, path, prefix_len_out=None,
+                 stream=None):
+    """commit over a paged cache (layout as tree_attention_paged)."""
+    lib = _lib.load()
+    if k_pool.dtype not in _DTYPES:
+        raise ValueError("pools must be float32 or bfloat16")
+    _dev(k_pool, "k_pool", k_pool.dtype)
+    _dev(v_pool, "v_pool", k_pool.dtype)
+    for name, t in (("prefix_len_in", prefix_len_in), ("accept_len", accept_len), ("path", path)):
+        _dev(t, name, torch.int32)
+    n_pages, Hkv, _, D = k_pool.shape
+    if tuple(v_pool.shape) != (n_pages, Hkv, D, PAGE):
+        raise ValueError("v_pool must be [num_pages, Hkv, D, 64]")
+    pk = paged_kv(block_table, k_pool)
+    B, n_max = path.shape
+    if prefix_len_out is None:
+        prefix_len_out = torch.empty_like(prefix_len_in)
+    _dev(prefix_len_out, "prefix_len_out", torch.int32)
+    _lib.check("tv_commit_paged", lib.tv_commit_paged(_ptr(k_pool), _ptr(v_pool), ctypes.byref(pk), B, Hkv, D,
+                                                      _DTYPES[k_pool.dtype], _ptr(prefix_len_in),
+                                                      _ptr(accept_len), _ptr(path), n_max,
+                                                      _ptr(prefix_len_out), _stream(stream)))
+    return prefix_len_out
 
 
 def accept(cand_tok, tgt_argmax, parents, anc, depth, n_nodes, err=None, accept_len=None, path=None,

@@ -12,10 +12,13 @@ TV_ERR_BAD_TREE = 2
 TV_ERR_CAPACITY = 3
 TV_ERR_UNSUPPORTED = 4
 TV_ERR_HIP = 5
+TV_ERR_BAD_PAGE = 6
 
 TV_F32 = 0
 TV_BF16 = 1
 TV_MAX_NODES = 64
+TV_MAX_PAGES_PER_SEQ = 256
+PAGE = 64
 
 # every function the header declares, with (restype, argtypes)
 _P = ctypes.c_void_p
@@ -33,16 +36,23 @@ class TvAttnArgs(ctypes.Structure):
     ]
 
 
+class TvPagedKv(ctypes.Structure):
+    """Mirror of tv_paged_kv."""
+    _fields_ = [("block_table", _P), ("max_pages", _I), ("num_pages", _I)]
+
+
 SIGNATURES = {
     "tv_status_string": (ctypes.c_char_p, [_I]),
     "tv_version": (ctypes.c_char_p, []),
     "tv_build_tree": (_I, [_P, _P, _I, _I, _P, _P, _P, _P]),
     "tv_tree_attention_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(TvAttnArgs)]),
     "tv_tree_attention": (_I, [ctypes.POINTER(TvAttnArgs), _P]),
+    "tv_tree_attention_paged": (_I, [ctypes.POINTER(TvAttnArgs), ctypes.POINTER(TvPagedKv), _P]),
     "tv_accept": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P]),
     "tv_accept_typical": (_I, [_P, _I, _I, _P, _P, _P, _P, _P, _P, _I, _I, ctypes.c_float,
                                ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P]),
     "tv_commit": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _I, _P, _P]),
+    "tv_commit_paged": (_I, [_P, _P, ctypes.POINTER(TvPagedKv), _I, _I, _I, _I, _P, _P, _P, _I, _P, _P]),
 }
 
 _lib = None

@@ -37,6 +37,7 @@ const char* tv_status_string(tv_status s) {
     case TV_ERR_CAPACITY: return "prefix plus tree exceeds the cache capacity";
     case TV_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case TV_ERR_HIP: return "HIP runtime or launch error";
+    case TV_ERR_BAD_PAGE: return "block table names a page outside the pools";
   }
   return "unknown status";
 }
@@ -68,7 +69,23 @@ tv_status tv_tree_attention(const tv_attn_args* a, hipStream_t stream) {
   const tv::AttnPlan plan = tv::plan_attention_bf16(a);
   if (plan.workspace_bytes > 0 && (a->workspace == nullptr || a->workspace_bytes < plan.workspace_bytes))
     return TV_ERR_INVALID_ARG;
-  return from_hip(tv::launch_attention_bf16(a, plan, stream));
+  return from_hip(tv::launch_attention_bf16(a, plan, nullptr, stream));
+}
+
+tv_status tv_tree_attention_paged(const tv_attn_args* a, const tv_paged_kv* pk, hipStream_t stream) {
+  const tv_status st = check_attn_shapes(a);
+  if (st != TV_OK) return st;
+  if (pk == nullptr || pk->max_pages < 1 || pk->num_pages < 1) return TV_ERR_INVALID_ARG;
+  if (a->cap != 64 * pk->max_pages) return TV_ERR_INVALID_ARG;
+  if (a->dtype != TV_BF16 || pk->max_pages > TV_MAX_PAGES_PER_SEQ) return TV_ERR_UNSUPPORTED;
+  if (a->B == 0) return TV_OK;
+  if (!a->q || !a->k_new || !a->v_new || !a->k_cache || !a->v_cache || !a->prefix_len ||
+      !a->n_nodes || !a->anc || !a->depth || !a->err || !a->out || !pk->block_table)
+    return TV_ERR_INVALID_ARG;
+  const tv::AttnPlan plan = tv::plan_attention_bf16(a);
+  if (plan.workspace_bytes > 0 && (a->workspace == nullptr || a->workspace_bytes < plan.workspace_bytes))
+    return TV_ERR_INVALID_ARG;
+  return from_hip(tv::launch_attention_bf16(a, plan, pk, stream));
 }
 
 tv_status tv_accept(const int32_t* cand_tok, const int32_t* tgt_argmax, const int32_t* parents,
@@ -120,7 +137,26 @@ tv_status tv_commit(void* k_cache, void* v_cache, int32_t B, int32_t Hkv, int32_
   if (!k_cache || !v_cache || !prefix_len_in || !accept_len || !path || !prefix_len_out)
     return TV_ERR_INVALID_ARG;
   return from_hip(tv::launch_commit(k_cache, v_cache, B, Hkv, cap, D, elem_bytes(dtype),
-                                    prefix_len_in, accept_len, path, n_max, prefix_len_out, stream));
+                                    prefix_len_in, accept_len, path, n_max, prefix_len_out, nullptr,
+                                    stream));
+}
+
+tv_status tv_commit_paged(void* k_pool, void* v_pool, const tv_paged_kv* pk, int32_t B, int32_t Hkv,
+                          int32_t D, int32_t dtype, const int32_t* prefix_len_in,
+                          const int32_t* accept_len, const int32_t* path, int32_t n_max,
+                          int32_t* prefix_len_out, hipStream_t stream) {
+  if (pk == nullptr || pk->max_pages < 1 || pk->num_pages < 1) return TV_ERR_INVALID_ARG;
+  if (B < 0 || Hkv < 1 || n_max < 1 || n_max > TV_MAX_NODES || 64 * pk->max_pages < n_max)
+    return TV_ERR_INVALID_ARG;
+  if (!dtype_ok(dtype)) return TV_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return TV_ERR_UNSUPPORTED;
+  if (B == 0) return TV_OK;
+  if (!k_pool || !v_pool || !pk->block_table || !prefix_len_in || !accept_len || !path ||
+      !prefix_len_out)
+    return TV_ERR_INVALID_ARG;
+  return from_hip(tv::launch_commit(k_pool, v_pool, B, Hkv, 64 * pk->max_pages, D, elem_bytes(dtype),
+                                    prefix_len_in, accept_len, path, n_max, prefix_len_out, pk,
+                                    stream));
 }
 
 }  // extern "C"

@@ -119,6 +119,11 @@ struct BfParams {
   float scale_log2;  // softmax scale * log2(e)
   int rope;          // 0: no rotation
   double log2_theta; // log2 of the RoPE base
+  // paged cache (block_table non-null): k_cache / v_cache are pools of
+  // pages [num_pages][Hkv][64][D] / [num_pages][Hkv][D][64], and 64-slot block
+  // j of sequence b is page block_table[b * max_pages + j]; cap = 64 max_pages
+  const int32_t* block_table;
+  int max_pages, num_pages;
 };
 
 // Two floats -> packed bf16 pair (hardware round to nearest even).
@@ -156,10 +161,6 @@ __device__ __forceinline__ int k_swz(int key) { return (key & 7) ^ (((key >> 3) 
 // element offsets in LDS
 __device__ __forceinline__ int ks_off(int key, int unit) { return key * kD + ((unit ^ k_swz(key)) << 3); }
 __device__ __forceinline__ int vs_off(int d, int unit) { return d * kKT + ((unit ^ (d & 7)) << 3); }
-// element offset of (slot, d) in one head's blocked V cache
-__device__ __forceinline__ size_t v_cache_off(int slot, int d) {
-  return (static_cast<size_t>(slot >> 6) * kD + d) * kKT + (slot & 63);
-}
 
 // cos/sin of pos * inv_freq: angle in double precision, reduced to [-pi, pi],
 // then single-precision sincos.
@@ -646,7 +647,7 @@ __device__ __forceinline__ void write_rows(const BfParams& p, int b, int g, int 
   }
 }
 
-template <int WAVES, int QT>
+template <int WAVES, int QT, bool PAGED>
 __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   constexpr int NT = WAVES * 64;
   constexpr int ROWS = WAVES * 32 * QT;      // query rows of the workgroup
@@ -697,6 +698,15 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   // loads) is read while they are in flight. Every address is valid (node
   // indices are clamped to n_max), so nothing branches; dead rows and nodes
   // are dropped once the data has landed.
+  // With a paged cache the sequence's page ids go out first: lane l of
+  // pg[u] holds block l + 64 u (clamped to the table; at most 256 blocks).
+  constexpr int kPageOps = PAGED ? 4 : 0;
+  uint32_t pg[4] = {0u, 0u, 0u, 0u};
+  if constexpr (PAGED) {
+    const int32_t* bt = p.block_table + static_cast<size_t>(b) * p.max_pages;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) pg[u] = ld_b32(bt + min(lane + 64 * u, p.max_pages - 1));
+  }
   int my_row[QT];
   uint32_t qdep[QT];
 #pragma unroll
@@ -727,17 +737,20 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   if (sq.cap_bad && g == 0 && rb == 0 && s == 0 && tid == 0) p.err[b] = TV_ERR_CAPACITY;
   // (every workgroup of b reads err: before or after this store, b is skipped)
 
-  if (rb0 >= rows_live) {
-    // nothing live in this row block; with splits the merge writes the zeros
-    // (the query copies land before the workgroup's LDS is given up)
+  // A workgroup with nothing to compute: its loads land before its LDS is
+  // given up; with splits the merge writes the zero rows, else it does.
+  auto retire = [&](int first_row) __attribute__((always_inline)) {
     wait_vm<0>();
     if (p.splits == 1) {
-      for (int r = rb0 + tid / 16; r < min(rb0 + ROWS, rows_all); r += NT / 16) {
+      for (int r = first_row + tid / 16; r < min(rb0 + ROWS, rows_all); r += NT / 16) {
         const int i = r / G, head = g * G + r % G;
         uint16_t* orow = p.out + ((static_cast<size_t>(b) * p.n_max + i) * p.Hq + head) * kD;
         reinterpret_cast<uint4*>(orow)[tid % 16] = make_uint4(0, 0, 0, 0);
       }
     }
+  };
+  if (rb0 >= rows_live) {
+    retire(rb0);   // nothing live in this row block
     return;
   }
   bool row_live[QT];
@@ -853,8 +866,16 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   auto tile_copy = [&](int pos) {
     const int kt0 = tile_k0(pos), buf = pos % kStages;
     TileCopy c;
-    c.ktile = kc + static_cast<size_t>(kt0) * kD;
-    c.vtile = vc + static_cast<size_t>(kt0) * kD;   // kt0 is a multiple of 64
+    if constexpr (PAGED) {
+      const int blk = kt0 >> 6;   // < 256
+      const uint32_t reg = blk < 64 ? pg[0] : blk < 128 ? pg[1] : blk < 192 ? pg[2] : pg[3];
+      const size_t off = (static_cast<size_t>(__builtin_amdgcn_readlane(reg, blk & 63)) * p.Hkv + g) * kKT * kD;
+      c.ktile = p.k_cache + off;
+      c.vtile = p.v_cache + off;
+    } else {
+      c.ktile = kc + static_cast<size_t>(kt0) * kD;
+      c.vtile = vc + static_cast<size_t>(kt0) * kD;   // kt0 is a multiple of 64
+    }
     c.kl = lds_base + static_cast<uint32_t>(2 * buf * kStageElems + wave * 64 * 8) * 2u;
     c.vl = c.kl + kStageElems * 2u;
     c.k_voff = k_voff;
@@ -875,9 +896,30 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   // issue until most of them have arrived, with its RoPE work still ahead.
   // Tile 1 goes out once the query rows are in registers, tile 2 after the
   // RoPE, so that work overlaps the first tiles' transfer.
-  constexpr int kStartOps = kDepOps + QCPT + kTreeOps;
+  constexpr int kStartOps = kPageOps + kDepOps + QCPT + kTreeOps;
   static_assert(kAhead == 3, "the start issues three tiles");
   if constexpr (kStartOps + 2 * CPT > 63) wait_vm<63 - 2 * CPT>();
+  if constexpr (PAGED) {
+    // the page ids (the oldest loads) land; every block of slots [0, P + n)
+    // must name a page of the pools (all workgroups of b check alike), else
+    // b is flagged and skipped
+    if (n_masked > 0)
+      wait_vm<kDepOps + QCPT + kTreeOps>();
+    else
+      wait_vm<kDepOps + QCPT>();
+    bool bad = false;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      landed(pg[u]);
+      const int page = static_cast<int>(pg[u]);
+      bad |= lane + 64 * u < tiles_all && (page < 0 || page >= p.num_pages);
+    }
+    if (__any(bad)) {
+      if (g == 0 && rb == 0 && s == 0 && tid == 0) p.err[b] = TV_ERR_BAD_PAGE;
+      retire(rb0);
+      return;
+    }
+  }
   if (n_tiles > 0) issue_tile(0);
 
   // ---- 2. the RoPE table for depths 0 .. deepest node of b, float2
@@ -1334,6 +1376,33 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
 // one block of their own per head. It runs after the attention kernel, which
 // never reads these slots back.
 // ---------------------------------------------------------------------------
+// Element offsets of the (at most two) 64-slot blocks that hold a tree's
+// slots [P, P + n) for KV head (b, g), n <= 64: the dense cache's blocks, or
+// the pages the block table names (clamped into the pools; a sequence with
+// a page outside them is flagged and skipped by the attention kernel).
+struct TreeBlocks {
+  int blk0;
+  size_t off0, off1;
+  __device__ __forceinline__ size_t of(int slot) const { return (slot >> 6) == blk0 ? off0 : off1; }
+};
+__device__ __forceinline__ size_t page_off(const BfParams& p, int b, int g, int blk) {
+  const int32_t e = p.block_table[static_cast<size_t>(b) * p.max_pages + min(blk, p.max_pages - 1)];
+  const int page = min(max(e, 0), p.num_pages - 1);
+  return (static_cast<size_t>(page) * p.Hkv + g) * kKT * kD;
+}
+__device__ __forceinline__ TreeBlocks tree_blocks(const BfParams& p, int b, int g, int P) {
+  TreeBlocks t;
+  t.blk0 = P >> 6;
+  if (p.block_table) {
+    t.off0 = page_off(p, b, g, t.blk0);
+    t.off1 = page_off(p, b, g, t.blk0 + 1);
+  } else {
+    t.off0 = ((static_cast<size_t>(b) * p.Hkv + g) * p.cap + static_cast<size_t>(t.blk0) * kKT) * kD;
+    t.off1 = t.off0 + kKT * kD;
+  }
+  return t;
+}
+
 struct KeyPairs {
   uint16_t xl[2], xh[2];
   int dep[2];
@@ -1359,7 +1428,7 @@ __device__ __forceinline__ void append_keys(const BfParams& p, const SeqState& s
                                             int nthreads, KeyPairs kp) {
   if (sq.skip) return;
   const int j = it & 63;   // the same dimension pair for every k of this thread
-  const size_t head_off = (static_cast<size_t>(b) * p.Hkv + g) * p.cap * kD;
+  const TreeBlocks tb = tree_blocks(p, b, g, sq.P);
   const double freq = p.rope ? rope_freq(p.log2_theta, j) : 0.0;
   for (int k0 = it; k0 < sq.n * 64; k0 += 2 * nthreads) {
     if (k0 != it) kp = load_keys(p, b, g, k0, nthreads);
@@ -1371,7 +1440,8 @@ __device__ __forceinline__ void append_keys(const BfParams& p, const SeqState& s
       const float l = bf16_bits_to_f32(kp.xl[u]), h = bf16_bits_to_f32(kp.xh[u]);
       const float2 cs = p.rope ? rope_cs(sq.P + clamp_depth(kp.dep[u]), freq) : make_float2(1.0f, 0.0f);
       const uint32_t w = pack_bf16(rope_lo(l, h, cs) * 1.0f, rope_hi(l, h, cs) * 1.0f);
-      uint16_t* dst = p.k_cache + head_off + static_cast<size_t>(sq.P + i) * kD;
+      const int slot = sq.P + i;
+      uint16_t* dst = p.k_cache + tb.of(slot) + static_cast<size_t>(slot & 63) * kD;
       dst[j] = static_cast<uint16_t>(w & 0xFFFFu);
       dst[64 + j] = static_cast<uint16_t>(w >> 16);
     }
@@ -1402,7 +1472,7 @@ __device__ __forceinline__ void append_values(const BfParams& p, int b, int g, u
   wait_vm<0>();
   if (sq.skip) return;
   const int n = sq.n, P = sq.P;
-  const size_t head_off = (static_cast<size_t>(b) * p.Hkv + g) * p.cap * kD;
+  const TreeBlocks tb = tree_blocks(p, b, g, P);
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     landed(v4[u]);
@@ -1424,7 +1494,7 @@ __device__ __forceinline__ void append_values(const BfParams& p, int b, int g, u
     const bool full = s0 >= P && s0 + 8 <= P + n;
 #pragma unroll
     for (int dd = 0; dd < 8; ++dd) {
-      uint16_t* dst = p.v_cache + head_off + v_cache_off(s0, 8 * c + dd);
+      uint16_t* dst = p.v_cache + tb.of(s0) + (8 * c + dd) * kKT + (s0 & 63);   // (8-slot units stay in one block)
       if (full) {
         uint32_t w[4];
 #pragma unroll
@@ -1614,7 +1684,8 @@ AttnPlan plan_attention_bf16(const tv_attn_args* a) {
   return pl;
 }
 
-hipError_t launch_attention_bf16(const tv_attn_args* a, const AttnPlan& pl, hipStream_t s) {
+hipError_t launch_attention_bf16(const tv_attn_args* a, const AttnPlan& pl, const tv_paged_kv* pk,
+                                 hipStream_t s) {
   BfParams p;
   p.q = static_cast<const uint16_t*>(a->q);
   p.k_new = static_cast<const uint16_t*>(a->k_new);
@@ -1632,6 +1703,9 @@ hipError_t launch_attention_bf16(const tv_attn_args* a, const AttnPlan& pl, hipS
   p.Hkv = a->Hkv;
   p.G = a->Hq / a->Hkv;
   p.cap = a->cap;
+  p.block_table = pk ? pk->block_table : nullptr;
+  p.max_pages = pk ? pk->max_pages : 0;
+  p.num_pages = pk ? pk->num_pages : 0;
   p.splits = pl.splits;
   p.row_blocks = pl.row_blocks;
   p.rope = a->rope_theta != 0.0f;
@@ -1647,10 +1721,13 @@ hipError_t launch_attention_bf16(const tv_attn_args* a, const AttnPlan& pl, hipS
   const int wg_rows = pl.waves * 32 * pl.qt;
   dim3 mgrid(pl.row_blocks * wg_rows / 32 + 1, a->Hkv, a->B);   // (+ the value-append block)
   const int key = pl.waves * 10 + pl.qt;
-  switch (key) {
-    case 21: hipLaunchKernelGGL((attn_bf16_kernel<2, 1>), grid, dim3(128), 0, s, p); break;
-    case 41: hipLaunchKernelGGL((attn_bf16_kernel<4, 1>), grid, dim3(256), 0, s, p); break;
-    default: hipLaunchKernelGGL((attn_bf16_kernel<4, 2>), grid, dim3(256), 0, s, p); break;
+  switch (key + (pk ? 100 : 0)) {
+    case 21: hipLaunchKernelGGL((attn_bf16_kernel<2, 1, false>), grid, dim3(128), 0, s, p); break;
+    case 41: hipLaunchKernelGGL((attn_bf16_kernel<4, 1, false>), grid, dim3(256), 0, s, p); break;
+    case 42: hipLaunchKernelGGL((attn_bf16_kernel<4, 2, false>), grid, dim3(256), 0, s, p); break;
+    case 121: hipLaunchKernelGGL((attn_bf16_kernel<2, 1, true>), grid, dim3(128), 0, s, p); break;
+    case 141: hipLaunchKernelGGL((attn_bf16_kernel<4, 1, true>), grid, dim3(256), 0, s, p); break;
+    default: hipLaunchKernelGGL((attn_bf16_kernel<4, 2, true>), grid, dim3(256), 0, s, p); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -31,9 +31,11 @@ hipError_t launch_typical_stats(const void* logits, int elem_bytes, int V, const
                                 int B, int n_max, float* entropy, float* p_tok, int32_t* argmax,
                                 hipStream_t s);
 
+// pk: paged cache (nullptr: the dense layout)
 hipError_t launch_commit(void* k_cache, void* v_cache, int B, int Hkv, int cap, int D,
                          int elem_bytes, const int32_t* prefix_len_in, const int32_t* accept_len,
-                         const int32_t* path, int n_max, int32_t* prefix_len_out, hipStream_t s);
+                         const int32_t* path, int n_max, int32_t* prefix_len_out,
+                         const tv_paged_kv* pk, hipStream_t s);
 
 // Launch plan of the bf16 attention: waves per workgroup, row blocks, KV
 // splits and the workspace they need.
@@ -48,7 +50,9 @@ struct AttnPlan {
 
 AttnPlan plan_attention_bf16(const tv_attn_args* a);
 
-hipError_t launch_attention_bf16(const tv_attn_args* a, const AttnPlan& plan, hipStream_t s);
+// pk: paged cache (nullptr: the dense layout)
+hipError_t launch_attention_bf16(const tv_attn_args* a, const AttnPlan& plan, const tv_paged_kv* pk,
+                                 hipStream_t s);
 hipError_t launch_attention_f32(const tv_attn_args* a, hipStream_t s);
 
 }  // namespace tv

@@ -155,7 +155,11 @@ __global__ __launch_bounds__(64) void accept_kernel(
 // commit: slot P+d <- slot P+path[d] for d = 0..L. path is strictly increasing
 // with path[d] >= d, so a source slot may be another lane's destination; all
 // sources of one KV head are staged in LDS before any slot is written.
-// K is [cap][D] per head; V is blocked [cap/64][D][64] per head.
+// K is [cap][D] per head; V is blocked [cap/64][D][64] per head. With a
+// paged cache (bt non-null) the 64-slot block j of sequence b is page
+// bt[b * max_pages + j] of pools [num_pages][Hkv][64][D] (K) and
+// [num_pages][Hkv][D][64] (V). The moved slots lie in [P, P + n_max), at most
+// two blocks, whose offsets are found once per head.
 // Grid: (Hkv / heads_per_block, B). The block of head 0 writes prefix_len_out;
 // when that array is also prefix_len_in, one block per sequence walks every
 // head, so no block can read a length another block has already replaced.
@@ -164,12 +168,14 @@ template <typename T>
 __global__ __launch_bounds__(256) void commit_kernel(
     T* __restrict__ k_cache, T* __restrict__ v_cache, int Hkv, int cap, int D,
     const int32_t* prefix_len_in, const int32_t* __restrict__ accept_len,
-    const int32_t* __restrict__ path, int n_max, int32_t* prefix_len_out, int heads_per_block) {
+    const int32_t* __restrict__ path, int n_max, int32_t* prefix_len_out, int heads_per_block,
+    const int32_t* __restrict__ bt, int max_pages, int num_pages) {
   constexpr int kStage = TV_MAX_NODES_DEV * 128 * 4 / sizeof(T);   // elements
   __shared__ T k_stage[kStage];
   __shared__ T v_stage[kStage];
   __shared__ int s_path[TV_MAX_NODES_DEV];
   __shared__ int s_L, s_P, s_ok;
+  __shared__ int s_page[2];
 
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
@@ -178,7 +184,12 @@ __global__ __launch_bounds__(256) void commit_kernel(
   if (tid == 0) {
     const int L = accept_len[b];
     const int P = prefix_len_in[b];
-    int ok = (L >= 0) && (L < n_max) && (P >= 0) && (P + L < cap);
+    const int ok = (L >= 0) && (L < n_max) && (P >= 0) && (P + L < cap);
+    if (bt && ok) {
+      // the table entries of the (at most two) blocks from P on
+      for (int u = 0; u < 2; ++u)
+        s_page[u] = bt[static_cast<size_t>(b) * max_pages + min((P >> 6) + u, max_pages - 1)];
+    }
     s_L = L;
     s_P = P;
     s_ok = ok;
@@ -191,28 +202,51 @@ __global__ __launch_bounds__(256) void commit_kernel(
     if (src_in < 0 || P + src_in >= cap) atomicAnd(&s_ok, 0);
   }
   __syncthreads();
+  if (bt && tid == 0 && s_ok) {
+    // the pages the move touches (the largest slot is P + path[L]) must be
+    // pages of the pools, else the sequence is left unchanged
+    const int blocks = ((P + s_path[L]) >> 6) - (P >> 6) + 1;
+    for (int u = 0; u < 2; ++u) {
+      const int e = s_page[u];
+      if (u < blocks && (e < 0 || e >= num_pages)) s_ok = 0;
+      s_page[u] = min(max(e, 0), num_pages - 1);
+    }
+  }
+  if (bt) __syncthreads();
   const bool ok = s_ok;
   if ((heads_per_block == Hkv || blockIdx.x == 0) && tid == 0) prefix_len_out[b] = ok ? P + L + 1 : P;
   if (!ok) return;
 
   const int g0 = (heads_per_block == Hkv) ? 0 : blockIdx.x;
   const int total = (L + 1) * D;
+  const int blk0 = P >> 6;
   for (int gg = 0; gg < heads_per_block; ++gg) {
-    const size_t head = (static_cast<size_t>(b) * Hkv + g0 + gg) * cap * D;
+    const int g = g0 + gg;
+    // element offsets of blocks blk0 and blk0 + 1 of this head
+    size_t off[2];
+    if (bt) {
+      off[0] = (static_cast<size_t>(s_page[0]) * Hkv + g) * 64 * D;
+      off[1] = (static_cast<size_t>(s_page[1]) * Hkv + g) * 64 * D;
+    } else {
+      off[0] = ((static_cast<size_t>(b) * Hkv + g) * cap + static_cast<size_t>(blk0) * 64) * D;
+      off[1] = off[0] + static_cast<size_t>(64) * D;
+    }
+    auto k_at = [&](int slot, int c) { return off[(slot >> 6) - blk0] + static_cast<size_t>(slot & 63) * D + c; };
+    auto v_at = [&](int slot, int c) { return off[(slot >> 6) - blk0] + static_cast<size_t>(c) * 64 + (slot & 63); };
     for (int idx = tid; idx < total; idx += blockDim.x) {
       const int d = idx / D, c = idx % D;
       const int src = P + s_path[d];
       if (src == P + d) continue;
-      k_stage[idx] = k_cache[head + static_cast<size_t>(src) * D + c];
-      v_stage[idx] = v_cache[head + (static_cast<size_t>(src >> 6) * D + c) * 64 + (src & 63)];
+      k_stage[idx] = k_cache[k_at(src, c)];
+      v_stage[idx] = v_cache[v_at(src, c)];
     }
     __syncthreads();
     for (int idx = tid; idx < total; idx += blockDim.x) {
       const int d = idx / D, c = idx % D;
       if (s_path[d] == d) continue;
       const int dst = P + d;
-      k_cache[head + static_cast<size_t>(dst) * D + c] = k_stage[idx];
-      v_cache[head + (static_cast<size_t>(dst >> 6) * D + c) * 64 + (dst & 63)] = v_stage[idx];
+      k_cache[k_at(dst, c)] = k_stage[idx];
+      v_cache[v_at(dst, c)] = v_stage[idx];
     }
     __syncthreads();
   }
@@ -251,7 +285,10 @@ hipError_t launch_accept_typical(const int32_t* cand_tok, const int32_t* tgt_arg
 
 hipError_t launch_commit(void* k_cache, void* v_cache, int B, int Hkv, int cap, int D,
                          int elem_bytes, const int32_t* prefix_len_in, const int32_t* accept_len,
-                         const int32_t* path, int n_max, int32_t* prefix_len_out, hipStream_t s) {
+                         const int32_t* path, int n_max, int32_t* prefix_len_out,
+                         const tv_paged_kv* pk, hipStream_t s) {
+  const int32_t* bt = pk ? pk->block_table : nullptr;
+  const int max_pages = pk ? pk->max_pages : 0, num_pages = pk ? pk->num_pages : 0;
   // One block per (kv head, sequence) unless the new prefix lengths overwrite
   // the old ones, in which case one block per sequence walks every head so
   // that no block reads a length another block has already replaced.
@@ -261,11 +298,11 @@ hipError_t launch_commit(void* k_cache, void* v_cache, int B, int Hkv, int cap, 
   if (elem_bytes == 2) {
     hipLaunchKernelGGL(commit_kernel<uint16_t>, grid, dim3(256), 0, s, static_cast<uint16_t*>(k_cache),
                        static_cast<uint16_t*>(v_cache), Hkv, cap, D, prefix_len_in, accept_len,
-                       path, n_max, prefix_len_out, hpb);
+                       path, n_max, prefix_len_out, hpb, bt, max_pages, num_pages);
   } else {
     hipLaunchKernelGGL(commit_kernel<uint32_t>, grid, dim3(256), 0, s, static_cast<uint32_t*>(k_cache),
                        static_cast<uint32_t*>(v_cache), Hkv, cap, D, prefix_len_in, accept_len,
-                       path, n_max, prefix_len_out, hpb);
+                       path, n_max, prefix_len_out, hpb, bt, max_pages, num_pages);
   }
   return hipGetLastError();
 }
