@@ -83,9 +83,11 @@ def load_traffic(workload: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, budget_s: float = 12.0) -> dict:
+def cpu_baseline(w, budget_s: float = 12.0, paged: bool = False) -> dict:
     """The oracle, as it is, on whole sequences of the same workload until
-    about budget_s seconds of CPU work; one BLAS thread."""
+    about budget_s seconds of CPU work; one BLAS thread. paged: each
+    sequence's cache first goes to shuffled pages and back through the block
+    table (oracle.scatter_pages / gather_pages), inside the timed region."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -94,8 +96,16 @@ def cpu_baseline(w, budget_s: float = 12.0) -> dict:
     done = 0
     t0 = time.perf_counter()
     with threadpool_limits(limits=1):
+        rng = np.random.default_rng(0)
         for b in range(w.B):
-            oracle.verify_step(w.oracle_inputs(b))
+            inp = w.oracle_inputs(b)
+            if paged:
+                mp = w.cap // oracle.PAGE
+                bt = rng.permutation(mp)[None, :].astype(np.int32)
+                shape = (mp, w.Hkv, oracle.PAGE, w.D)
+                kp, vp = oracle.scatter_pages(inp["k_cache"], inp["v_cache"], bt, np.zeros(shape), np.zeros(shape))
+                inp["k_cache"], inp["v_cache"] = oracle.gather_pages(kp, vp, bt)
+            oracle.verify_step(inp)
             nodes += int(w.n_nodes[b])
             done += 1
             if time.perf_counter() - t0 >= budget_s:
@@ -110,7 +120,8 @@ def cpu_baseline(w, budget_s: float = 12.0) -> dict:
     return {"value": nodes / dt, "unit": "tree-nodes/s", "cores": 1, "kind": "oracle",
             "sample": f"{done} of {w.B} sequences ({nodes} nodes), full verification step "
                       f"(tree set-up, attention over prefix {int(np.mean(w.prefix_len[:done]))} "
-                      f"+ ancestors, accept, commit), numpy float64, 1 BLAS thread of "
+                      f"+ ancestors, accept, commit{', through a shuffled block table' if paged else ''}), "
+                      f"numpy float64, 1 BLAS thread of "
                       f"{len(os.sched_getaffinity(0))} available ({cpu}), {dt:.1f} s"}
 
 
@@ -261,9 +272,10 @@ def main() -> None:
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated per step (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=None)
-    ap.add_argument("--workload", choices=("step", "typical"), default="step",
+    ap.add_argument("--workload", choices=("step", "typical", "paged"), default="step",
                     help="step: the verification step (default); typical: typical acceptance "
-                         "from target logits on the same trees")
+                         "from target logits on the same trees; paged: the step over a paged "
+                         "KV cache (shuffled 64-slot pages)")
     ap.add_argument("--vocab", type=int, default=32000, help="vocabulary of --workload typical")
     args = ap.parse_args()
 
@@ -300,6 +312,20 @@ def main() -> None:
     per_copy = sum(t.numel() * t.element_size() for t in base.values())
     copies = args.copies or max(2, -(-4 * INFINITY_CACHE_BYTES // per_copy))
     sets = [base] + [{k: t.clone() for k, t in base.items()} for _ in range(copies - 1)]
+    paged = args.workload == "paged"
+    if paged:
+        # each copy's cache moves to page pools under its own random table
+        # (every 64-slot block of every sequence on a page drawn without
+        # replacement); the dense copy is dropped
+        mp = w.cap // tv.PAGE
+        n_pages = B_pages = w.B * mp
+        rng = np.random.default_rng(7)
+        for s in sets:
+            s["bt"] = torch.from_numpy(rng.permutation(B_pages).reshape(w.B, mp).astype(np.int32)).to(dev)
+            s["k_cache"], s["v_cache"] = tv.pages_from_dense(s["k_cache"], s["v_cache"], s["bt"], n_pages)
+            s["pk"] = tv._lib.TvPagedKv()
+            s["pk"].block_table, s["pk"].max_pages, s["pk"].num_pages = s["bt"].data_ptr(), mp, n_pages
+        torch.cuda.synchronize()
 
     B, n_max = w.B, w.n_max
     anc = torch.empty((B, n_max), dtype=torch.int64, device=dev)
@@ -312,7 +338,8 @@ def main() -> None:
     toks = torch.empty((B, n_max), dtype=torch.int32, device=dev)
     plen_out = torch.empty_like(plen)
     a0 = tv.attn_args(base["q"], base["k_new"], base["v_new"], base["k_cache"], base["v_cache"],
-                      plen, n_nodes, anc, depth, err, out, w.rope_theta)
+                      plen, n_nodes, anc, depth, err, out, w.rope_theta,
+                      block_table=base["bt"] if paged else None)
     ws_bytes = tv.tree_attention_workspace_size(a0)
     workspace = tv.new_workspace(ws_bytes, dev)
 
@@ -328,22 +355,31 @@ def main() -> None:
     calls = []
     for s in sets:
         a = tv.attn_args(s["q"], s["k_new"], s["v_new"], s["k_cache"], s["v_cache"], plen, n_nodes,
-                         anc, depth, err, out, w.rope_theta, workspace=workspace)
-        cm = (P(s["k_cache"]), P(s["v_cache"]), B, w.Hkv, w.cap, w.D, a.dtype, P(plen), P(acc_len),
-              P(path), n_max, P(plen_out), sp)
+                         anc, depth, err, out, w.rope_theta, workspace=workspace,
+                         block_table=s["bt"] if paged else None)
+        if paged:
+            cm = (P(s["k_cache"]), P(s["v_cache"]), ctypes.byref(s["pk"]), B, w.Hkv, w.D, a.dtype, P(plen),
+                  P(acc_len), P(path), n_max, P(plen_out), sp)
+        else:
+            cm = (P(s["k_cache"]), P(s["v_cache"]), B, w.Hkv, w.cap, w.D, a.dtype, P(plen), P(acc_len),
+                  P(path), n_max, P(plen_out), sp)
         calls.append((a, cm))
+    commit_fn = lib.tv_commit_paged if paged else lib.tv_commit
     bt = (P(parents), P(n_nodes), B, n_max, P(anc), P(depth), P(err), sp)
     ac = (P(tok), P(tgt), P(parents), P(anc), P(depth), P(n_nodes), P(err), B, n_max, P(acc_len),
           P(path), P(bonus), P(toks), sp)
 
     def attention(k: int) -> int:
+        if paged:
+            return lib.tv_tree_attention_paged(ctypes.byref(calls[k % copies][0]),
+                                               ctypes.byref(sets[k % copies]["pk"]), sp)
         return lib.tv_tree_attention(ctypes.byref(calls[k % copies][0]), sp)
 
     def step(k: int) -> None:
         st = lib.tv_build_tree(*bt)
         st |= attention(k)
         st |= lib.tv_accept(*ac)
-        st |= lib.tv_commit(*calls[k % copies][1])
+        st |= commit_fn(*calls[k % copies][1])
         if st:
             raise RuntimeError(f"library call failed with status {st}")
 
@@ -374,7 +410,7 @@ def main() -> None:
         events[k][0].record(stream)
         st |= attention(k)
         events[k][1].record(stream)
-        st |= lib.tv_accept(*ac) | lib.tv_commit(*calls[k % copies][1])
+        st |= lib.tv_accept(*ac) | commit_fn(*calls[k % copies][1])
         if st:
             raise RuntimeError(f"library call failed with status {st}")
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -389,7 +425,8 @@ def main() -> None:
     attn_b2b_s = e0.elapsed_time(e1) * 1e-3 / args.steps
     ab = algorithmic_bytes(w)
     achieved = ab["total"] / attn_mean_s / 1e9
-    traffic = load_traffic(w.name)
+    wname = f"{w.name}-paged" if paged else w.name
+    traffic = load_traffic(wname)
 
     rec = {
         "metric": METRIC,
@@ -404,7 +441,7 @@ def main() -> None:
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": w.name, "batch": B, "q_heads": w.Hq, "kv_heads": w.Hkv,
+        "config": {"workload": wname, "batch": B, "q_heads": w.Hq, "kv_heads": w.Hkv,
                    "head_dim": w.D, "prefix_len_mean": float(np.mean(w.prefix_len)),
                    "tree_nodes": int(w.n_nodes.max()), "input_copies_rotated": copies,
                    "seed": args.config if args.seed is None else args.seed},
@@ -422,7 +459,7 @@ def main() -> None:
         "kernel_source_hash": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w)
+        rec["cpu_baseline"] = cpu_baseline(w, paged=paged)
     print(json.dumps(rec), flush=True)
 
 
