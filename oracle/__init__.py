@@ -21,6 +21,7 @@ from .tv_oracle import (  # noqa: F401
     build_tree,
     PAGE,
     commit,
+    eagle2_tree,
     gather_pages,
     scatter_pages,
     next_token_distribution,

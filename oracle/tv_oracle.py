@@ -427,6 +427,66 @@ def commit(k_cache, v_cache, prefix_len, accept_len, path):
 
 
 # ---------------------------------------------------------------------------
+# EAGLE-2 dynamic draft tree: expansion by path value, rerank, flatten
+# ---------------------------------------------------------------------------
+
+def eagle2_tree(conf, cand, root_tok, n_max):
+    """Builds one dynamic draft tree ([INFRA-5.3] section 5.2).
+
+    A node's value is the product of the draft's confidences along its path
+    from the root (the root, the last verified token, has value 1). The
+    expansion phase grows, at each of S steps, the K highest-valued nodes of
+    the newest layer, each by the M children the draft proposes for it; the
+    rerank phase keeps the n_max - 1 highest-valued nodes of all created
+    ones, plus the root, for verification.
+
+    Inputs (the draft's proposals, given rather than computed):
+      conf [S][K][M] float32: confidence of child c of the k-th expanded node
+        (in value order) at step s; cand [S][K][M] int32: that child's token.
+    Readings: values are float32 products v(parent) * c, rounded once per
+    node; confidences are clamped into [0, 1] (NaN counts as 0), so values
+    never grow along a path; ties in value go to the node created first
+    (at a step, children in (k, c) order), in both phases; a layer with
+    fewer than K nodes expands all of them; the kept nodes are flattened in
+    creation order, which is depth order, so every parent precedes its
+    children. With conf in [0, 1] the kept set is closed under ancestors (a
+    parent is worth at least as much as its child and was created first).
+
+    Returns (parents [n_max] int32, tokens [n_max] int32, values [n_max]
+    float32, n) with n kept nodes and -1 / -1 / 0 padding.
+    """
+    S, K, M = conf.shape
+    val = [np.float32(1.0)]
+    par = [-1]
+    tok = [int(root_tok)]
+    layer = [0]
+    for s in range(S):
+        grow = sorted(layer, key=lambda i: (-val[i], i))[:K]
+        new = []
+        for k, p in enumerate(grow):
+            for c in range(M):
+                x = np.float32(conf[s, k, c])
+                x = np.float32(0.0) if np.isnan(x) else min(max(x, np.float32(0.0)), np.float32(1.0))
+                val.append(np.float32(val[p] * x))
+                par.append(p)
+                tok.append(int(cand[s, k, c]))
+                new.append(len(val) - 1)
+        layer = new
+    kept = sorted(range(1, len(val)), key=lambda i: (-val[i], i))[:n_max - 1]
+    order = [0] + sorted(kept)
+    index = {old: new for new, old in enumerate(order)}
+    n = len(order)
+    parents = np.full(n_max, -1, dtype=np.int32)
+    tokens = np.full(n_max, -1, dtype=np.int32)
+    values = np.zeros(n_max, dtype=np.float32)
+    for new_i, old in enumerate(order):
+        parents[new_i] = -1 if old == 0 else index[par[old]]
+        tokens[new_i] = tok[old]
+        values[new_i] = val[old]
+    return parents, tokens, values, n
+
+
+# ---------------------------------------------------------------------------
 # Paged KV: the cache of each sequence as a list of fixed-size pages
 # ---------------------------------------------------------------------------
 

@@ -11,6 +11,7 @@ from .configs import (  # noqa: F401
     Workload,
     bf16_bits_to_f32,
     f32_to_bf16_bits,
+    draft_proposals,
     generate,
     target_logits,
 )

@@ -422,3 +422,21 @@ def target_logits(w: Workload, vocab: int = VOCAB, dtype: Optional[str] = None,
             if 0 <= t < vocab:
                 x[b, p, t] = base[b, p] + np.float32(rng.uniform(-9.0, 3.0))
     return f32_to_bf16_bits(x) if dt == "bf16" else x
+
+
+def draft_proposals(B: int, S: int, K: int, M: int, seed: int = 0):
+    """Synthetic draft proposals for building EAGLE-2 trees: for each sequence,
+    expansion step s and expanded node k, M children with confidences drawn by
+    stick-breaking (fraction ~ Beta(2, 2) of the mass left, so siblings sum
+    to at most 1 like a draft softmax), sorted best first as a top-M would be,
+    and M distinct token ids. Returns (conf [B][S][K][M] float32,
+    cand [B][S][K][M] int32, root_tok [B] int32)."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 0xE2])))
+    frac = rng.beta(2.0, 2.0, size=(B, S, K, M))
+    left = np.cumprod(np.concatenate([np.ones((B, S, K, 1)), 1.0 - frac[..., :-1]], axis=-1), axis=-1)
+    conf = -np.sort(-(left * frac), axis=-1)
+    cand = np.empty((B, S, K, M), dtype=np.int32)
+    for idx in np.ndindex(B, S, K):
+        cand[idx] = rng.choice(VOCAB, size=M, replace=False)
+    root = rng.integers(0, VOCAB, size=B).astype(np.int32)
+    return conf.astype(np.float32), cand, root
