@@ -11,7 +11,7 @@
  *   [MEDUSA-EXPL]  "Medusa, explained" (vibeengines.com), steps 6 and 7,
  *                  "Typical acceptance".
  *   [INFRA-5.3]    "5.3 Medusa、EAGLE 与 MTP" (infra-guide), sections 3.1,
- *                  3.2, 8, 9.1 and 9.2.
+ *                  3.2, 5.2, 8, 9.1 and 9.2.
  *   [DRAFTERS]     "Drafters: draft models, Medusa, EAGLE, MTP, DFlash,
  *                  DSpark" (robertz.co), "Why the answer does not change".
  *
@@ -87,6 +87,39 @@ const char* tv_version(void);
 tv_status tv_build_tree(const int32_t* parents, const int32_t* n_nodes, int32_t B,
                         int32_t n_max, uint64_t* anc, int32_t* depth, int32_t* err,
                         hipStream_t stream);
+
+/*
+ * tv_eagle2_tree -- an EAGLE-2 dynamic draft tree from the draft's proposals.
+ *
+ * [INFRA-5.3] section 5.2: a node's value is the product of the draft's
+ * confidences along its path from the root (the root, the last verified
+ * token, is worth 1); the expansion grows, at each of S steps, the K best
+ * nodes of the newest layer by the M children the draft proposes for each;
+ * the rerank keeps the n_max - 1 best of all created nodes, plus the root,
+ * for verification. Readings fixed here: values are float32 products
+ * v(parent) * c, c the confidence clamped into [0, 1] (NaN counts as 0);
+ * ties in value go to the node created first (a step creates its children
+ * in (k, c) order), in both phases; a layer with fewer than K nodes grows
+ * all of them. The kept nodes are numbered in creation order (= depth
+ * order), so the output is a parents-first tree for tv_build_tree.
+ *
+ *   conf     [B][S][K][M] float  confidence of child c of the k-th best node
+ *                                of the newest layer at step s
+ *   cand     [B][S][K][M]        that child's token
+ *   root_tok [B]                 token of the root
+ *   parents  [B][n_max] out      parent of each kept node (-1 for the root),
+ *                                -1 padding
+ *   tokens   [B][n_max] out      token of each kept node, -1 padding
+ *   values   [B][n_max] float out  its path value, 0 padding
+ *   n_nodes  [B] out             kept nodes, min(n_max, nodes created)
+ * Host checks: pointers non-null unless B == 0, B >= 0, S, K, M >= 1,
+ * 1 <= n_max <= TV_MAX_NODES; S * K * M <= TV_MAX_DRAFT_PROPOSALS, else
+ * TV_ERR_UNSUPPORTED. B == 0 is a no-op.
+ */
+#define TV_MAX_DRAFT_PROPOSALS 512
+tv_status tv_eagle2_tree(const float* conf, const int32_t* cand, const int32_t* root_tok, int32_t B,
+                         int32_t S, int32_t K, int32_t M, int32_t n_max, int32_t* parents,
+                         int32_t* tokens, float* values, int32_t* n_nodes, hipStream_t stream);
 
 /*
  * tv_tree_attention -- tree-masked GQA attention of every tree node over the

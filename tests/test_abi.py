@@ -18,13 +18,13 @@ pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(tv_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(tv_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_expected_calls():
     names = declared_functions()
     for must in ("tv_build_tree", "tv_tree_attention", "tv_accept", "tv_commit", "tv_accept_typical",
-                 "tv_tree_attention_paged", "tv_commit_paged"):
+                 "tv_tree_attention_paged", "tv_commit_paged", "tv_eagle2_tree"):
         assert must in names
 
 
@@ -157,3 +157,20 @@ def test_paged_host_validation():
                                null) == _lib.TV_ERR_INVALID_ARG
     assert lib.tv_commit_paged(null, null, ctypes.byref(p), 0, 2, 128, 1, null, null, null, 5, null,
                                null) == _lib.TV_OK
+
+
+def test_eagle2_tree_host_validation():
+    lib = _lib.load()
+    f, null = ctypes.c_void_p(0x1000), None
+
+    def call(B=2, S=6, K=8, M=8, n=60, conf=f):
+        return lib.tv_eagle2_tree(conf, f, f, B, S, K, M, n, f, f, f, f, null)
+    assert call(B=-1) == _lib.TV_ERR_INVALID_ARG
+    assert call(S=0) == _lib.TV_ERR_INVALID_ARG
+    assert call(K=0) == _lib.TV_ERR_INVALID_ARG
+    assert call(M=0) == _lib.TV_ERR_INVALID_ARG
+    assert call(n=0) == _lib.TV_ERR_INVALID_ARG
+    assert call(n=65) == _lib.TV_ERR_INVALID_ARG
+    assert call(S=7, K=8, M=10) == _lib.TV_ERR_UNSUPPORTED      # 560 proposals > 512
+    assert call(conf=null) == _lib.TV_ERR_INVALID_ARG
+    assert call(B=0, conf=null) == _lib.TV_OK

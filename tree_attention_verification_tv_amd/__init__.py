@@ -27,7 +27,7 @@ from ._lib import (PAGE, TV_BF16, TV_ERR_BAD_PAGE, TV_ERR_BAD_TREE, TV_ERR_CAPAC
                    TV_MAX_NODES, TvAttnArgs, TvError, TvPagedKv)
 
 __all__ = ["build_tree", "tree_attention", "tree_attention_workspace_size", "new_workspace", "accept",
-           "accept_typical", "commit", "tree_attention_paged", "commit_paged", "pages_from_dense",
+           "accept_typical", "commit", "eagle2_tree", "tree_attention_paged", "commit_paged", "pages_from_dense",
            "dense_from_pages", "TV_ERR_BAD_PAGE", "PAGE",
            "version", "TvError", "TV_ERR_BAD_TREE", "TV_ERR_CAPACITY", "attn_args",
            "v_cache_blocked", "v_cache_rows", "V_BLOCK"]
@@ -309,6 +309,31 @@ def accept(cand_tok, tgt_argmax, parents, anc, depth, n_nodes, err=None, accept_
                                           _ptr(accept_len), _ptr(path), _ptr(bonus), _ptr(out_tokens),
                                           _stream(stream)))
     return accept_len, path, bonus, out_tokens
+
+
+def eagle2_tree(conf, cand, root_tok, n_max: int, stream=None):
+    """EAGLE-2 dynamic draft tree from the draft's proposals: conf [B, S, K, M]
+    float32, cand [B, S, K, M] int32, root_tok [B] int32 -> (parents, tokens
+    [B, n_max] int32, values [B, n_max] float32, n_nodes [B] int32), the
+    parents-first tree that build_tree takes."""
+    lib = _lib.load()
+    _dev(conf, "conf", torch.float32)
+    _dev(cand, "cand", torch.int32)
+    _dev(root_tok, "root_tok", torch.int32)
+    if conf.dim() != 4 or tuple(cand.shape) != tuple(conf.shape):
+        raise ValueError("conf and cand must be [B, S, K, M]")
+    B, S, K, M = conf.shape
+    if root_tok.numel() != B:
+        raise ValueError("root_tok must have B entries")
+    dev = conf.device
+    parents = torch.empty((B, n_max), dtype=torch.int32, device=dev)
+    tokens = torch.empty((B, n_max), dtype=torch.int32, device=dev)
+    values = torch.empty((B, n_max), dtype=torch.float32, device=dev)
+    n_nodes = torch.empty(B, dtype=torch.int32, device=dev)
+    _lib.check("tv_eagle2_tree", lib.tv_eagle2_tree(_ptr(conf), _ptr(cand), _ptr(root_tok), B, S, K, M, n_max,
+                                                    _ptr(parents), _ptr(tokens), _ptr(values), _ptr(n_nodes),
+                                                    _stream(stream)))
+    return parents, tokens, values, n_nodes
 
 
 def accept_typical(logits, cand_tok, parents, anc, depth, n_nodes, err=None, *, epsilon: float,

@@ -49,6 +49,7 @@ SIGNATURES = {
     "tv_tree_attention": (_I, [ctypes.POINTER(TvAttnArgs), _P]),
     "tv_tree_attention_paged": (_I, [ctypes.POINTER(TvAttnArgs), ctypes.POINTER(TvPagedKv), _P]),
     "tv_accept": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P]),
+    "tv_eagle2_tree": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
     "tv_accept_typical": (_I, [_P, _I, _I, _P, _P, _P, _P, _P, _P, _I, _I, ctypes.c_float,
                                ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P]),
     "tv_commit": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _I, _P, _P]),

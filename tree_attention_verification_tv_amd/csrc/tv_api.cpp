@@ -101,6 +101,17 @@ tv_status tv_accept(const int32_t* cand_tok, const int32_t* tgt_argmax, const in
                                     n_max, accept_len, path, bonus_tok, out_tokens, stream));
 }
 
+tv_status tv_eagle2_tree(const float* conf, const int32_t* cand, const int32_t* root_tok, int32_t B,
+                         int32_t S, int32_t K, int32_t M, int32_t n_max, int32_t* parents,
+                         int32_t* tokens, float* values, int32_t* n_nodes, hipStream_t stream) {
+  if (B < 0 || S < 1 || K < 1 || M < 1 || n_max < 1 || n_max > TV_MAX_NODES) return TV_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(S) * K * M > TV_MAX_DRAFT_PROPOSALS) return TV_ERR_UNSUPPORTED;
+  if (B == 0) return TV_OK;
+  if (!conf || !cand || !root_tok || !parents || !tokens || !values || !n_nodes) return TV_ERR_INVALID_ARG;
+  return from_hip(tv::launch_eagle2_tree(conf, cand, root_tok, B, S, K, M, n_max, parents, tokens, values,
+                                         n_nodes, stream));
+}
+
 tv_status tv_accept_typical(const void* logits, int32_t dtype, int32_t vocab,
                             const int32_t* cand_tok, const int32_t* parents, const uint64_t* anc,
                             const int32_t* depth, const int32_t* n_nodes, const int32_t* err,

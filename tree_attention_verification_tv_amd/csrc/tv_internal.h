@@ -26,6 +26,10 @@ hipError_t launch_accept_typical(const int32_t* cand_tok, const int32_t* tgt_arg
                                  int32_t* accept_len, int32_t* path, int32_t* bonus,
                                  int32_t* out_tokens, hipStream_t s);
 
+hipError_t launch_eagle2_tree(const float* conf, const int32_t* cand, const int32_t* root_tok, int B, int S,
+                              int K, int M, int n_max, int32_t* parents, int32_t* tokens, float* values,
+                              int32_t* n_nodes, hipStream_t s);
+
 hipError_t launch_typical_stats(const void* logits, int elem_bytes, int V, const int32_t* cand_tok,
                                 const int32_t* parents, const int32_t* n_nodes, const int32_t* err,
                                 int B, int n_max, float* entropy, float* p_tok, int32_t* argmax,
