@@ -129,6 +129,14 @@ TYPICAL_EPS, TYPICAL_DELTA = 0.09, 0.3
 TYPICAL_SOURCES = ["tv_typical.hip", "tv_tree.hip", "tv_device.h"]
 
 
+def source_hash(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "tree_attention_verification_tv_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
 def typical_source_hash() -> str:
     h = hashlib.sha256()
     for f in TYPICAL_SOURCES:
@@ -263,6 +271,95 @@ def bench_typical(args) -> None:
     print(json.dumps(rec), flush=True)
 
 
+DRAFT_SHAPES = {3: (8, 6, 8, 8, 60), 5: (64, 7, 4, 3, 32)}   # B, S, K, M, n per workload
+
+
+def bench_draft_tree(args) -> None:
+    """EAGLE-2 tree construction (tv_eagle2_tree) for the batch of the
+    headline workload (8 trees: 6 steps, top-8 of each layer grown by 8
+    children, 60 nodes kept) or, with --config 5, the ragged serving batch
+    (64 trees: 7 steps, top-4 by 3, 32 nodes)."""
+    import numpy as np
+    import torch
+
+    import tree_attention_verification_tv_amd as tv
+    from workloads import draft_proposals
+
+    dev = torch.device("cuda:0")
+    B, S, K, M, n = DRAFT_SHAPES[args.config]
+    conf, cand, root = draft_proposals(B, S, K, M, seed=args.config if args.seed is None else args.seed)
+    c_d, k_d, r_d = (torch.from_numpy(x).to(dev) for x in (conf, cand, root))
+    parents, tokens, values, n_nodes = tv.eagle2_tree(c_d, k_d, r_d, n)
+    lib = tv._lib.load()
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())   # noqa: E731
+    call = (P(c_d), P(k_d), P(r_d), B, S, K, M, n, P(parents), P(tokens), P(values), P(n_nodes), sp)
+
+    def step():
+        if lib.tv_eagle2_tree(*call):
+            raise RuntimeError("tv_eagle2_tree failed")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    call_s = e0.elapsed_time(e1) * 1e-3 / args.steps
+    # work: the rank comparisons (each layer node against its layer, each
+    # created node against all created nodes, each against those before it)
+    created, layer, comps = 1, 1, 0
+    for _ in range(S):
+        comps += layer * layer
+        layer = min(K, layer) * M
+        created += layer
+    comps += 2 * created * created
+    comps *= B
+    achieved = comps / call_s / 1e12
+    rec = {
+        "metric": "EAGLE-2 draft trees built per second (tree construction before verification)",
+        "value": B / ((t1 - t0) / args.steps),
+        "unit": "trees/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": (t1 - t0) * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"eagle2-draft-tree-b{B}-s{S}-k{K}-m{M}-n{n}", "batch": B, "steps": S,
+                   "grown_per_layer": K, "children": M, "nodes_kept": n},
+        "roofline": {"bound": "alu", "achieved": achieved, "peak": 157.3, "unit": "Tcompare/s",
+                     "frac": achieved / 157.3, "traffic": None,
+                     "kernel": "eagle2_tree_kernel (one workgroup per tree); HIP events around K calls "
+                               "back to back; work = rank comparisons, peak = fp32 vector rate",
+                     "comparisons_per_launch": comps, "call_us_mean": call_s * 1e6},
+        "kernel_source_hash": source_hash(["tv_draft.hip"]),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        runs, t2 = 0, time.perf_counter()
+        while time.perf_counter() - t2 < 5.0:
+            for b in range(B):
+                oracle.eagle2_tree(conf[b], cand[b], root[b], n)
+            runs += 1
+        dt = time.perf_counter() - t2
+        rec["cpu_baseline"] = {"value": runs * B / dt, "unit": "trees/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{runs} passes over the {B} trees, Python/NumPy, 1 thread, {dt:.1f} s"}
+    print(json.dumps(rec), flush=True)
+
+
 def main() -> None:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -272,10 +369,11 @@ def main() -> None:
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated per step (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=None)
-    ap.add_argument("--workload", choices=("step", "typical", "paged"), default="step",
+    ap.add_argument("--workload", choices=("step", "typical", "paged", "draft-tree"), default="step",
                     help="step: the verification step (default); typical: typical acceptance "
                          "from target logits on the same trees; paged: the step over a paged "
-                         "KV cache (shuffled 64-slot pages)")
+                         "KV cache (shuffled 64-slot pages); draft-tree: EAGLE-2 tree "
+                         "construction from draft proposals")
     ap.add_argument("--vocab", type=int, default=32000, help="vocabulary of --workload typical")
     args = ap.parse_args()
 
@@ -287,6 +385,9 @@ def main() -> None:
 
     if args.workload == "typical":
         bench_typical(args)
+        return
+    if args.workload == "draft-tree":
+        bench_draft_tree(args)
         return
 
     import numpy as np

@@ -4,12 +4,13 @@
 // expansion grows the best nodes of the newest layer, the rerank keeps the
 // best nodes of all for verification).
 //
-// One workgroup per sequence. The proposal table (at most 512 confidences
-// and tokens) is staged in LDS with one round trip; the tree of created
-// nodes (at most 513 with the root) lives in LDS. Every selection is a rank
-// count: a node's rank is the number of nodes ahead of it in (value
-// descending, creation ascending) order, so no sort and no atomics, and the
-// same total order as the oracle's. Values are float32 products
+// One workgroup of 1024 threads per sequence. The proposal table (at most
+// 512 confidences and tokens) is staged in LDS with one round trip; the tree
+// of created nodes (at most 513 with the root) lives in LDS. Every selection
+// is a rank count: a node's rank is the number of nodes ahead of it in
+// (value descending, creation ascending) order, counted by several lanes at
+// once, so no sort and no atomics, and the same total order as the
+// oracle's; each child of a step is created by a thread of its own. Values are float32 products
 // v(parent) * clamp(conf, 0, 1), rounded once per node, so both sides rank
 // identical numbers. The kept nodes are numbered in creation order (which is
 // depth order), so parents come first.
@@ -19,8 +20,47 @@
 namespace tv {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 1024;
 constexpr int kMaxCreated = 1 + TV_MAX_DRAFT_PROPOSALS;
+
+// Number of j in [a, b) with vals[j] >= v (GE) or vals[j] > v: aligned runs
+// of four values per LDS access, single values at the ragged ends.
+template <bool GE>
+__device__ __forceinline__ int count_from(const float* vals, int a, int b, float v) {
+  auto ahead = [&](float u) { return GE ? (u >= v) : (u > v); };
+  int r = 0, j = a;
+  for (; j < b && (j & 3); ++j) r += ahead(vals[j]);
+#pragma unroll 4
+  for (; j + 4 <= b; j += 4) {
+    const float4 u = *reinterpret_cast<const float4*>(vals + j);
+    r += ahead(u.x) + ahead(u.y) + ahead(u.z) + ahead(u.w);
+  }
+  for (; j < b; ++j) r += ahead(vals[j]);
+  return r;
+}
+
+// rank[i - j0] for every node i of [j0, j1) (at most kThreads nodes): the
+// nodes of [j0, j1) ahead of i in (value descending, creation ascending)
+// order, i.e. the earlier ones worth at least v(i) and the later ones worth
+// more. Each node's count is split over `segs` consecutive lanes (a power
+// of two dividing 64), summed with shuffles.
+__device__ __forceinline__ void rank_all(const float* vals, int j0, int j1, int* rank, int tid) {
+  const int L = j1 - j0;
+  int segs = 1;
+  while (segs < 16 && 2 * segs * L <= kThreads) segs *= 2;
+  const int seg_len = ((L + segs - 1) / segs + 3) & ~3;
+  const int node = tid / segs, seg = tid % segs;
+  int r = 0;
+  float v = 0.0f;
+  const int i = j0 + node;
+  if (node < L) {
+    v = vals[i];
+    const int a = j0 + seg * seg_len, b = min(j1, a + seg_len);
+    r = count_from<true>(vals, a, min(b, i), v) + count_from<false>(vals, max(a, i + 1), b, v);
+  }
+  for (int off = 1; off < segs; off <<= 1) r += __shfl_xor(r, off);
+  if (node < L && seg == 0) rank[node] = r;
+}
 
 __global__ __launch_bounds__(kThreads) void eagle2_tree_kernel(
     const float* __restrict__ conf, const int32_t* __restrict__ cand, const int32_t* __restrict__ root_tok,
@@ -28,11 +68,13 @@ __global__ __launch_bounds__(kThreads) void eagle2_tree_kernel(
     float* __restrict__ values, int32_t* __restrict__ n_nodes) {
   __shared__ float s_conf[TV_MAX_DRAFT_PROPOSALS];
   __shared__ int s_cand[TV_MAX_DRAFT_PROPOSALS];
-  __shared__ float s_val[kMaxCreated];
+  __shared__ __attribute__((aligned(16))) float s_val[kMaxCreated];
   __shared__ int s_par[kMaxCreated];
   __shared__ int s_tok[kMaxCreated];
-  __shared__ int s_keep[kMaxCreated];
+  __shared__ int s_rank[kMaxCreated];
   __shared__ int s_new[kMaxCreated];
+  __shared__ int s_grow[TV_MAX_DRAFT_PROPOSALS];   // node of each rank < K in the layer
+  __shared__ int s_count[(kMaxCreated + 63) / 64];
 
   const int b = blockIdx.x, tid = threadIdx.x;
   const int n_prop = S * K * M;
@@ -49,26 +91,22 @@ __global__ __launch_bounds__(kThreads) void eagle2_tree_kernel(
   }
   __syncthreads();
 
-  // expansion: the newest layer is created nodes [f0, f1)
+  // expansion: the newest layer is created nodes [f0, f1); its nodes of rank
+  // r < K each get M children, child c of rank r at f1 + r M + c (one thread
+  // per child)
   int f0 = 0, f1 = 1;
   for (int s = 0; s < S; ++s) {
     const int grown = min(K, f1 - f0);
-    for (int i = f0 + tid; i < f1; i += kThreads) {
-      const float v = s_val[i];
-      int r = 0;
-      for (int j = f0; j < f1; ++j) {
-        const float u = s_val[j];
-        r += (u > v) || (u == v && j < i);
-      }
-      if (r < grown) {
-        for (int c = 0; c < M; ++c) {
-          const int e = (s * K + r) * M + c;
-          const int child = f1 + r * M + c;
-          s_val[child] = v * s_conf[e];
-          s_par[child] = i;
-          s_tok[child] = s_cand[e];
-        }
-      }
+    rank_all(s_val, f0, f1, s_rank, tid);
+    __syncthreads();
+    for (int i = tid; i < f1 - f0; i += kThreads)
+      if (s_rank[i] < grown) s_grow[s_rank[i]] = f0 + i;
+    __syncthreads();
+    for (int t = tid; t < grown * M; t += kThreads) {
+      const int r = t / M, e = s * K * M + t, child = f1 + t, p = s_grow[r];
+      s_val[child] = s_val[p] * s_conf[e];
+      s_par[child] = p;
+      s_tok[child] = s_cand[e];
     }
     __syncthreads();
     f0 = f1;
@@ -76,26 +114,27 @@ __global__ __launch_bounds__(kThreads) void eagle2_tree_kernel(
   }
   const int T = f1;   // created nodes, the root included
 
-  // rerank: the root and the n_max - 1 best other nodes are kept
-  for (int i = tid; i < T; i += kThreads) {
-    int keep = 1;
-    if (i > 0) {
-      const float v = s_val[i];
-      int r = 0;
-      for (int j = 1; j < T; ++j) {
-        const float u = s_val[j];
-        r += (u > v) || (u == v && j < i);
-      }
-      keep = r < n_max - 1;
-    }
-    s_keep[i] = keep;
+  // rerank: the n_max best of all created nodes are kept; the root (worth
+  // 1, the largest value, and created first) is always among them
+  rank_all(s_val, 0, T, s_rank, tid);
+  __syncthreads();
+  // flattened index of a kept node = kept nodes created before it: a ballot
+  // per 64 nodes, then the counts of the earlier groups
+  const int lane = tid & 63, wave = tid >> 6;
+  const int groups = (T + 63) / 64;
+  for (int q = wave; q < groups; q += kThreads / 64) {
+    const int i = 64 * q + lane;
+    const uint64_t bal = __ballot(i < T && s_rank[i] < n_max);
+    if (lane == 0) s_count[q] = __popcll(bal);
   }
   __syncthreads();
-  // flattened index of a kept node: kept nodes created before it
-  for (int i = tid; i < T; i += kThreads) {
-    int idx = 0;
-    for (int j = 0; j < i; ++j) idx += s_keep[j];
-    s_new[i] = s_keep[i] ? idx : -1;
+  for (int q = wave; q < groups; q += kThreads / 64) {
+    const int i = 64 * q + lane;
+    const bool k = i < T && s_rank[i] < n_max;
+    const uint64_t bal = __ballot(k);
+    int base = 0;
+    for (int qq = 0; qq < q; ++qq) base += s_count[qq];
+    if (i < T) s_new[i] = k ? base + __popcll(bal & ((1ull << lane) - 1ull)) : -1;
   }
   __syncthreads();
 
