@@ -25,7 +25,10 @@ from .tv_oracle import (  # noqa: F401
     gather_pages,
     scatter_pages,
     next_token_distribution,
+    inverse_cdf,
     rope,
+    softmax64,
+    speculative_sample,
     tree_attention,
     tree_depth,
     tree_is_valid,

@@ -427,6 +427,68 @@ def commit(k_cache, v_cache, prefix_len, accept_len, path):
 
 
 # ---------------------------------------------------------------------------
+# Chain speculative sampling: keep with probability min(1, p/q), else resample
+# ---------------------------------------------------------------------------
+
+def softmax64(logits_row):
+    """Plain float64 softmax of one row of logits."""
+    x = np.asarray(logits_row, dtype=np.float64)
+    e = np.exp(x - x.max())
+    return e / e.sum()
+
+
+def inverse_cdf(weights, u):
+    """The first index whose running sum of weights exceeds u * total: a draw
+    from the distribution proportional to weights, for u uniform in [0, 1)."""
+    c = np.cumsum(np.asarray(weights, dtype=np.float64))
+    t = u * c[-1]
+    return int(min(np.searchsorted(c, t, side="right"), len(c) - 1))
+
+
+def speculative_sample(p_logits, q_logits, draft, u_acc, u_res):
+    """Chain speculative sampling of one draft ([DRAFTERS] "Why the answer does
+    not change"; [MEDUSA-EAGLE] on lossless verification).
+
+    Drafted token x_i (i < L) is kept with probability min(1, p_i(x_i) /
+    q_i(x_i)), p_i the target's and q_i the draft's distribution at position
+    i; checking stops at the first rejection j. The step then emits a token
+    drawn from the target's distribution with the draft's subtracted,
+    max(0, p_j - q_j) normalised, or, when all L are kept, from p_L.
+
+    Readings: distributions are plain softmaxes of the logits; the draws are
+    inputs (u_acc[i] for position i: keep iff u_acc[i] * q_i(x_i) < p_i(x_i),
+    which is u < min(1, p/q) for u in [0, 1); u_res for the final draw, by
+    inverse CDF over token ids in ascending order).
+
+    p_logits [L+1][V], q_logits [L][V], draft [L], u_acc [L], u_res scalar.
+    Returns (accepted, tokens [L+1] (-1 padded), p_tok [L], q_tok [L]).
+    """
+    L = len(draft)
+    p_tok = np.zeros(L)
+    q_tok = np.zeros(L)
+    j = L
+    for i in range(L):
+        p = softmax64(p_logits[i])
+        q = softmax64(q_logits[i])
+        x = int(draft[i])
+        p_tok[i], q_tok[i] = p[x], q[x]
+        if not u_acc[i] * q[x] < p[x]:
+            j = i
+            break
+    for i in range(j + 1, L):      # (not checked, reported for completeness)
+        p_tok[i] = softmax64(p_logits[i])[int(draft[i])]
+        q_tok[i] = softmax64(q_logits[i])[int(draft[i])]
+    if j < L:
+        w = np.maximum(softmax64(p_logits[j]) - softmax64(q_logits[j]), 0.0)
+    else:
+        w = softmax64(p_logits[L])
+    tokens = np.full(L + 1, -1, dtype=np.int32)
+    tokens[:j] = draft[:j]
+    tokens[j] = inverse_cdf(w, u_res)
+    return j, tokens, p_tok, q_tok
+
+
+# ---------------------------------------------------------------------------
 # EAGLE-2 dynamic draft tree: expansion by path value, rerank, flatten
 # ---------------------------------------------------------------------------
 
