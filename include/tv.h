@@ -303,6 +303,44 @@ tv_status tv_accept_typical(const void* logits, int32_t dtype, int32_t vocab,
                             int32_t* bonus_tok, int32_t* out_tokens, hipStream_t stream);
 
 /*
+ * tv_speculative_sample -- chain speculative sampling of L drafted tokens.
+ *
+ * [DRAFTERS] "Why the answer does not change": drafted token x_i is kept with
+ * probability min(1, p_i(x_i) / q_i(x_i)), p the target's and q the draft's
+ * distribution at position i; at the first rejection j the step emits a
+ * token drawn from the target's distribution with the draft's subtracted,
+ * max(0, p_j - q_j) normalised, or, when all L are kept, from p_L. The
+ * output is then distributed as sampling from the target alone. Readings
+ * fixed here: distributions are plain softmaxes of the logits (a caller
+ * sampling at temperature T passes logits / T); the uniform draws are
+ * inputs: token i is kept iff u_acc[i] * q_i(x_i) < p_i(x_i) (u in [0, 1)),
+ * and the final token is the first id (ascending) whose running weight
+ * exceeds u_res * total weight; a drafted id outside [0, vocab) has
+ * probability 0 under both.
+ *
+ *   p_logits  [B][L + 1][vocab]  target logits at the L drafted positions and
+ *                                after them; dtype TV_BF16 or TV_F32, finite
+ *   q_logits  [B][L][vocab]      draft logits at the L drafted positions
+ *   draft     [B][L]             drafted tokens
+ *   u_acc     [B][L] float, u_res [B] float   uniform draws in [0, 1)
+ *   p_tok, q_tok [B][L] float out  p_i(x_i) and q_i(x_i)
+ *   accept_len [B] out           kept drafted tokens j (0 .. L)
+ *   tokens    [B][L + 1] out     the j kept tokens, the drawn token, then -1
+ *   workspace                    >= tv_speculative_sample_workspace_size(B, L)
+ *                                bytes of device scratch (row statistics)
+ * Two kernels: per-row statistics (grid (L + 1, B)), then one workgroup per
+ * sequence for the decisions and the draw. Host checks: pointers non-null
+ * unless B == 0, 0 <= B <= 65535, 1 <= L <= TV_MAX_NODES, vocab >= 1, dtype
+ * valid, workspace large enough. B == 0 is a no-op.
+ */
+size_t tv_speculative_sample_workspace_size(int32_t B, int32_t L);
+tv_status tv_speculative_sample(const void* p_logits, const void* q_logits, int32_t dtype, int32_t vocab,
+                                const int32_t* draft, const float* u_acc, const float* u_res, int32_t B,
+                                int32_t L, float* p_tok, float* q_tok, int32_t* accept_len,
+                                int32_t* tokens, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+/*
  * tv_commit -- keep the accepted path's KV in place, drop the other branches.
  *
  * [INFRA-5.3] section 3.2 and summary: only the accepted path is committed.

@@ -24,7 +24,7 @@ def declared_functions():
 def test_header_declares_expected_calls():
     names = declared_functions()
     for must in ("tv_build_tree", "tv_tree_attention", "tv_accept", "tv_commit", "tv_accept_typical",
-                 "tv_tree_attention_paged", "tv_commit_paged", "tv_eagle2_tree"):
+                 "tv_tree_attention_paged", "tv_commit_paged", "tv_eagle2_tree", "tv_speculative_sample"):
         assert must in names
 
 
@@ -174,3 +174,22 @@ def test_eagle2_tree_host_validation():
     assert call(S=7, K=8, M=10) == _lib.TV_ERR_UNSUPPORTED      # 560 proposals > 512
     assert call(conf=null) == _lib.TV_ERR_INVALID_ARG
     assert call(B=0, conf=null) == _lib.TV_OK
+
+
+def test_speculative_sample_host_validation():
+    lib = _lib.load()
+    f, null = ctypes.c_void_p(0x1000), None
+    ws = lib.tv_speculative_sample_workspace_size(8, 5)
+    assert ws == 8 * 11 * 2 * 4
+    assert lib.tv_speculative_sample_workspace_size(0, 5) == 0
+
+    def call(B=8, L=5, V=32000, dtype=_lib.TV_BF16, p=f, wsb=ws):
+        return lib.tv_speculative_sample(p, f, dtype, V, f, f, f, B, L, f, f, f, f, f, wsb, null)
+    assert call(B=-1) == _lib.TV_ERR_INVALID_ARG
+    assert call(L=0) == _lib.TV_ERR_INVALID_ARG
+    assert call(L=65) == _lib.TV_ERR_INVALID_ARG
+    assert call(V=0) == _lib.TV_ERR_INVALID_ARG
+    assert call(dtype=9) == _lib.TV_ERR_INVALID_ARG
+    assert call(p=null) == _lib.TV_ERR_INVALID_ARG
+    assert call(wsb=ws - 1) == _lib.TV_ERR_INVALID_ARG
+    assert call(B=0, p=null) == _lib.TV_OK

@@ -27,7 +27,7 @@ from ._lib import (PAGE, TV_BF16, TV_ERR_BAD_PAGE, TV_ERR_BAD_TREE, TV_ERR_CAPAC
                    TV_MAX_NODES, TvAttnArgs, TvError, TvPagedKv)
 
 __all__ = ["build_tree", "tree_attention", "tree_attention_workspace_size", "new_workspace", "accept",
-           "accept_typical", "commit", "eagle2_tree", "tree_attention_paged", "commit_paged", "pages_from_dense",
+           "accept_typical", "commit", "eagle2_tree", "speculative_sample", "tree_attention_paged", "commit_paged", "pages_from_dense",
            "dense_from_pages", "TV_ERR_BAD_PAGE", "PAGE",
            "version", "TvError", "TV_ERR_BAD_TREE", "TV_ERR_CAPACITY", "attn_args",
            "v_cache_blocked", "v_cache_rows", "V_BLOCK"]
@@ -334,6 +334,37 @@ def eagle2_tree(conf, cand, root_tok, n_max: int, stream=None):
                                                     _ptr(parents), _ptr(tokens), _ptr(values), _ptr(n_nodes),
                                                     _stream(stream)))
     return parents, tokens, values, n_nodes
+
+
+def speculative_sample(p_logits, q_logits, draft, u_acc, u_res, stream=None):
+    """Chain speculative sampling: p_logits [B, L+1, V], q_logits [B, L, V]
+    (float32 or bfloat16, same dtype), draft [B, L] int32, u_acc [B, L] and
+    u_res [B] float32 uniform draws -> (accept_len [B], tokens [B, L+1],
+    p_tok [B, L], q_tok [B, L])."""
+    lib = _lib.load()
+    if p_logits.dtype not in _DTYPES:
+        raise ValueError("logits must be float32 or bfloat16")
+    _dev(p_logits, "p_logits", p_logits.dtype)
+    _dev(q_logits, "q_logits", p_logits.dtype)
+    _dev(draft, "draft", torch.int32)
+    _dev(u_acc, "u_acc", torch.float32)
+    _dev(u_res, "u_res", torch.float32)
+    B, L = draft.shape
+    V = p_logits.shape[-1]
+    if tuple(p_logits.shape) != (B, L + 1, V) or tuple(q_logits.shape) != (B, L, V):
+        raise ValueError("p_logits must be [B, L+1, V] and q_logits [B, L, V]")
+    if tuple(u_acc.shape) != (B, L) or u_res.numel() != B:
+        raise ValueError("u_acc must be [B, L] and u_res [B]")
+    dev = draft.device
+    ws = torch.empty(max(1, int(lib.tv_speculative_sample_workspace_size(B, L))), dtype=torch.uint8, device=dev)
+    accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    tokens = torch.empty((B, L + 1), dtype=torch.int32, device=dev)
+    p_tok = torch.empty((B, L), dtype=torch.float32, device=dev)
+    q_tok = torch.empty((B, L), dtype=torch.float32, device=dev)
+    _lib.check("tv_speculative_sample", lib.tv_speculative_sample(
+        _ptr(p_logits), _ptr(q_logits), _DTYPES[p_logits.dtype], V, _ptr(draft), _ptr(u_acc), _ptr(u_res), B, L,
+        _ptr(p_tok), _ptr(q_tok), _ptr(accept_len), _ptr(tokens), _ptr(ws), ws.numel(), _stream(stream)))
+    return accept_len, tokens, p_tok, q_tok
 
 
 def accept_typical(logits, cand_tok, parents, anc, depth, n_nodes, err=None, *, epsilon: float,

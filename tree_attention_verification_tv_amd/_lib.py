@@ -50,6 +50,8 @@ SIGNATURES = {
     "tv_tree_attention_paged": (_I, [ctypes.POINTER(TvAttnArgs), ctypes.POINTER(TvPagedKv), _P]),
     "tv_accept": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P]),
     "tv_eagle2_tree": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
+    "tv_speculative_sample_workspace_size": (ctypes.c_size_t, [_I, _I]),
+    "tv_speculative_sample": (_I, [_P, _P, _I, _I, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "tv_accept_typical": (_I, [_P, _I, _I, _P, _P, _P, _P, _P, _P, _I, _I, ctypes.c_float,
                                ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P]),
     "tv_commit": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _I, _P, _P]),

@@ -112,6 +112,26 @@ tv_status tv_eagle2_tree(const float* conf, const int32_t* cand, const int32_t* 
                                          n_nodes, stream));
 }
 
+size_t tv_speculative_sample_workspace_size(int32_t B, int32_t L) {
+  if (B < 1 || L < 1 || L > TV_MAX_NODES) return 0;
+  return static_cast<size_t>(B) * (2 * L + 1) * 2 * sizeof(float);
+}
+
+tv_status tv_speculative_sample(const void* p_logits, const void* q_logits, int32_t dtype, int32_t vocab,
+                                const int32_t* draft, const float* u_acc, const float* u_res, int32_t B,
+                                int32_t L, float* p_tok, float* q_tok, int32_t* accept_len, int32_t* tokens,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (B < 0 || B > 65535 || L < 1 || L > TV_MAX_NODES || vocab < 1) return TV_ERR_INVALID_ARG;
+  if (!dtype_ok(dtype)) return TV_ERR_INVALID_ARG;
+  if (B == 0) return TV_OK;
+  if (!p_logits || !q_logits || !draft || !u_acc || !u_res || !p_tok || !q_tok || !accept_len || !tokens ||
+      !workspace || workspace_bytes < tv_speculative_sample_workspace_size(B, L))
+    return TV_ERR_INVALID_ARG;
+  return from_hip(tv::launch_speculative_sample(p_logits, q_logits, elem_bytes(dtype), vocab, draft, u_acc,
+                                                u_res, B, L, p_tok, q_tok, accept_len, tokens,
+                                                static_cast<float*>(workspace), stream));
+}
+
 tv_status tv_accept_typical(const void* logits, int32_t dtype, int32_t vocab,
                             const int32_t* cand_tok, const int32_t* parents, const uint64_t* anc,
                             const int32_t* depth, const int32_t* n_nodes, const int32_t* err,

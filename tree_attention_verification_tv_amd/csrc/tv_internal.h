@@ -30,6 +30,11 @@ hipError_t launch_eagle2_tree(const float* conf, const int32_t* cand, const int3
                               int K, int M, int n_max, int32_t* parents, int32_t* tokens, float* values,
                               int32_t* n_nodes, hipStream_t s);
 
+hipError_t launch_speculative_sample(const void* p_logits, const void* q_logits, int elem_bytes, int V,
+                                     const int32_t* draft, const float* u_acc, const float* u_res, int B, int L,
+                                     float* p_tok, float* q_tok, int32_t* accept_len, int32_t* tokens,
+                                     float* stats, hipStream_t s);
+
 hipError_t launch_typical_stats(const void* logits, int elem_bytes, int V, const int32_t* cand_tok,
                                 const int32_t* parents, const int32_t* n_nodes, const int32_t* err,
                                 int B, int n_max, float* entropy, float* p_tok, int32_t* argmax,

@@ -264,6 +264,192 @@ __global__ __launch_bounds__(kThreads) void typical_stats_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Chain speculative sampling (robertz.co "Drafters ...", section "Why the
+// answer does not change"): drafted token x_i is kept with probability
+// min(1, p_i(x_i) / q_i(x_i)), p the target's and q the draft's
+// distribution; at the first rejection j the step draws from
+// max(0, p_j - q_j) normalised, or from p_L when all L tokens are kept.
+// The uniform draws are inputs (keep iff u_i q_i(x_i) < p_i(x_i); the final
+// draw by inverse CDF over ascending token ids).
+// ---------------------------------------------------------------------------
+
+// (ref, z) of one logits row over the workgroup, z = sum 2^(x log2(e) - ref),
+// handed to every thread; s_part is reusable once every thread has it.
+template <typename T, int E>
+__device__ __forceinline__ void row_ref_z(const T* row, int V, int tid, RowStat* s_part, float& ref, float& z) {
+  using Chunk = typename ChunkOf<T, E>::type;
+  const int nchunks = V / E;
+  RowStat st{-INFINITY, INT_MAX, -INFINITY, 0.f, 0.f};
+  for (int base = 0; base < nchunks; base += kThreads * kBatch) {
+    Chunk v[kBatch];
+    load_batch<T, E>(v, row, base, nchunks, tid);
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int c = base + k * kThreads + tid;
+      if (c < nchunks) {
+        float cm = chunk_elem<T, E>(v[k], 0);
+#pragma unroll
+        for (int j = 1; j < E; ++j) cm = fmaxf(cm, chunk_elem<T, E>(v[k], j));
+        const float cref = cm * kLog2e;
+        if (cref > st.ref + kSlack) {
+          float zz = 0.f, ss = 0.f;
+          rescaled(st, cref, zz, ss);
+          st.ref = cref;
+          st.z = zz;
+        }
+#pragma unroll
+        for (int j = 0; j < E; ++j) st.z += exp2_sum_term(fmaf(chunk_elem<T, E>(v[k], j), kLog2e, -st.ref));
+      }
+    }
+  }
+#pragma unroll
+  for (int off = kWave / 2; off >= 1; off >>= 1) {
+    RowStat o;
+    o.mx = -INFINITY;
+    o.idx = INT_MAX;
+    o.ref = __shfl_xor(st.ref, off);
+    o.z = __shfl_xor(st.z, off);
+    o.s = 0.f;
+    st = combine(st, o);
+  }
+  if ((tid & (kWave - 1)) == 0) s_part[tid / kWave] = st;
+  __syncthreads();
+  RowStat r = s_part[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) r = combine(r, s_part[w]);
+  ref = r.ref;
+  z = r.z;
+  __syncthreads();
+}
+
+// Grid (L + 1, B), 512 threads: target row i and, for i < L, draft row i:
+// (ref, z) of each into stats [B][2L + 1][2] (target rows first), and the
+// drafted token's probability under each (0 for an id outside [0, V)).
+template <typename T, int E>
+__global__ __launch_bounds__(kThreads) void spec_stats_kernel(
+    const T* __restrict__ p_logits, const T* __restrict__ q_logits, int V, int L,
+    const int32_t* __restrict__ draft, float* __restrict__ stats, float* __restrict__ p_tok,
+    float* __restrict__ q_tok) {
+  __shared__ RowStat s_part[kWaves];
+  const int i = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int x = i < L ? draft[static_cast<size_t>(b) * L + i] : 0;
+  const bool x_in = x >= 0 && x < V;
+  float* st = stats + static_cast<size_t>(b) * (2 * L + 1) * 2;
+  float ref, z;
+  const T* prow = p_logits + (static_cast<size_t>(b) * (L + 1) + i) * V;
+  row_ref_z<T, E>(prow, V, tid, s_part, ref, z);
+  if (tid == 0) {
+    st[2 * i] = ref;
+    st[2 * i + 1] = z;
+    if (i < L) p_tok[static_cast<size_t>(b) * L + i] = x_in ? exp2f(fmaf(load_elem<T>(prow, x), kLog2e, -ref)) / z : 0.f;
+  }
+  if (i >= L) return;
+  const T* qrow = q_logits + (static_cast<size_t>(b) * L + i) * V;
+  row_ref_z<T, E>(qrow, V, tid, s_part, ref, z);
+  if (tid == 0) {
+    st[2 * (L + 1 + i)] = ref;
+    st[2 * (L + 1 + i) + 1] = z;
+    q_tok[static_cast<size_t>(b) * L + i] = x_in ? exp2f(fmaf(load_elem<T>(qrow, x), kLog2e, -ref)) / z : 0.f;
+  }
+}
+
+constexpr int kSampleThreads = 1024;
+
+// Grid B, 1024 threads: the keep decisions, then one pass over the row to
+// draw from. Thread t sums the weights of a contiguous run of token ids; a
+// block scan of those sums gives every run's place in the running total, and
+// the one thread whose run holds u * total finds the token by summing its
+// run again in the same order (the runs meet exactly: each starts where the
+// scan ended the one before). If rounding leaves u * total past every run,
+// the last token of positive weight is drawn.
+template <typename T>
+__global__ __launch_bounds__(kSampleThreads) void spec_sample_kernel(
+    const T* __restrict__ p_logits, const T* __restrict__ q_logits, int V, int L,
+    const int32_t* __restrict__ draft, const float* __restrict__ u_acc, const float* __restrict__ u_res,
+    const float* __restrict__ stats, const float* __restrict__ p_tok, const float* __restrict__ q_tok,
+    int32_t* __restrict__ accept_len, int32_t* __restrict__ tokens) {
+  constexpr int kW = kSampleThreads / kWave;
+  __shared__ int s_j, s_y;
+  __shared__ float s_wsum[kW];
+  __shared__ int s_last[kW];
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  if (wave == 0) {
+    bool rej = false;
+    if (lane < L) {
+      const size_t e = static_cast<size_t>(b) * L + lane;
+      rej = !(u_acc[e] * q_tok[e] < p_tok[e]);
+    }
+    const uint64_t m = __ballot(rej);
+    if (lane == 0) {
+      s_j = m ? __ffsll(static_cast<long long>(m)) - 1 : L;
+      s_y = -1;
+    }
+  }
+  __syncthreads();
+  const int j = s_j;
+  const bool resid = j < L;
+  const float* st = stats + static_cast<size_t>(b) * (2 * L + 1) * 2;
+  const float pref = st[2 * j], pinv = 1.0f / st[2 * j + 1];
+  const float qref = resid ? st[2 * (L + 1 + j)] : 0.f, qinv = resid ? 1.0f / st[2 * (L + 1 + j) + 1] : 0.f;
+  const T* prow = p_logits + (static_cast<size_t>(b) * (L + 1) + j) * V;
+  const T* qrow = q_logits + (static_cast<size_t>(b) * L + (resid ? j : 0)) * V;
+  auto weight = [&](int y) {
+    float w = exp2f(fmaf(load_elem<T>(prow, y), kLog2e, -pref)) * pinv;
+    if (resid) w = fmaxf(w - exp2f(fmaf(load_elem<T>(qrow, y), kLog2e, -qref)) * qinv, 0.0f);
+    return w;
+  };
+  const int seg = (V + kSampleThreads - 1) / kSampleThreads;
+  const int y0 = min(V, tid * seg), y1 = min(V, y0 + seg);
+  float S = 0.f;
+  int last = -1;
+  for (int y = y0; y < y1; ++y) {
+    const float w = weight(y);
+    S += w;
+    if (w > 0.f) last = y;
+  }
+  // inclusive scan of the run sums: within the wave, then over the waves
+  float inc = S;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const float o = __shfl_up(inc, off);
+    if (lane >= off) inc += o;
+  }
+  int lmax = last;
+#pragma unroll
+  for (int off = kWave / 2; off >= 1; off >>= 1) lmax = max(lmax, __shfl_xor(lmax, off));
+  if (lane == kWave - 1) s_wsum[wave] = inc;
+  if (lane == 0) s_last[wave] = lmax;
+  __syncthreads();
+  float before = 0.f, total = 0.f;
+  int last_all = -1;
+  for (int w = 0; w < kW; ++w) {
+    if (w < wave) before += s_wsum[w];
+    total += s_wsum[w];
+    last_all = max(last_all, s_last[w]);
+  }
+  const float hi = before + inc, lo = hi - S;   // this run's place
+  const float t = u_res[b] * total;
+  if (S > 0.f && lo <= t && t < hi) {
+    float acc = lo;
+    int pick = last;
+    for (int y = y0; y < y1; ++y) {
+      acc += weight(y);
+      if (acc > t) {
+        pick = y;
+        break;
+      }
+    }
+    s_y = pick;
+  }
+  __syncthreads();
+  const int y = s_y >= 0 ? s_y : last_all;
+  const size_t row = static_cast<size_t>(b) * (L + 1);
+  for (int k = tid; k <= L; k += kSampleThreads)
+    tokens[row + k] = k < j ? draft[static_cast<size_t>(b) * L + k] : (k == j ? y : -1);
+  if (tid == 0) accept_len[b] = j;
+}
+
 }  // namespace
 
 hipError_t launch_typical_stats(const void* logits, int elem_bytes, int V, const int32_t* cand_tok,
@@ -289,6 +475,48 @@ hipError_t launch_typical_stats(const void* logits, int elem_bytes, int V, const
     else
       hipLaunchKernelGGL((typical_stats_kernel<float, 1>), grid, dim3(kThreads), 0, s, p, V,
                          cand_tok, parents, n_nodes, err, n_max, entropy, p_tok, argmax);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace tv
+
+namespace tv {
+
+hipError_t launch_speculative_sample(const void* p_logits, const void* q_logits, int elem_bytes, int V,
+                                     const int32_t* draft, const float* u_acc, const float* u_res, int B, int L,
+                                     float* p_tok, float* q_tok, int32_t* accept_len, int32_t* tokens,
+                                     float* stats, hipStream_t s) {
+  const dim3 grid(L + 1, B);
+  const bool aligned = (reinterpret_cast<uintptr_t>(p_logits) % 16 == 0) &&
+                       (reinterpret_cast<uintptr_t>(q_logits) % 16 == 0) &&
+                       ((static_cast<size_t>(V) * elem_bytes) % 16 == 0);
+  if (elem_bytes == 2) {
+    const auto* p = static_cast<const uint16_t*>(p_logits);
+    const auto* q = static_cast<const uint16_t*>(q_logits);
+    if (aligned)
+      hipLaunchKernelGGL((spec_stats_kernel<uint16_t, 8>), grid, dim3(kThreads), 0, s, p, q, V, L, draft, stats,
+                         p_tok, q_tok);
+    else
+      hipLaunchKernelGGL((spec_stats_kernel<uint16_t, 1>), grid, dim3(kThreads), 0, s, p, q, V, L, draft, stats,
+                         p_tok, q_tok);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((spec_sample_kernel<uint16_t>), dim3(B), dim3(kSampleThreads), 0, s, p, q, V, L, draft,
+                       u_acc, u_res, stats, p_tok, q_tok, accept_len, tokens);
+  } else {
+    const auto* p = static_cast<const float*>(p_logits);
+    const auto* q = static_cast<const float*>(q_logits);
+    if (aligned)
+      hipLaunchKernelGGL((spec_stats_kernel<float, 4>), grid, dim3(kThreads), 0, s, p, q, V, L, draft, stats,
+                         p_tok, q_tok);
+    else
+      hipLaunchKernelGGL((spec_stats_kernel<float, 1>), grid, dim3(kThreads), 0, s, p, q, V, L, draft, stats,
+                         p_tok, q_tok);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((spec_sample_kernel<float>), dim3(B), dim3(kSampleThreads), 0, s, p, q, V, L, draft, u_acc,
+                       u_res, stats, p_tok, q_tok, accept_len, tokens);
   }
   return hipGetLastError();
 }

@@ -13,5 +13,6 @@ from .configs import (  # noqa: F401
     f32_to_bf16_bits,
     draft_proposals,
     generate,
+    speculative_inputs,
     target_logits,
 )

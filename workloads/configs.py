@@ -440,3 +440,33 @@ def draft_proposals(B: int, S: int, K: int, M: int, seed: int = 0):
         cand[idx] = rng.choice(VOCAB, size=M, replace=False)
     root = rng.integers(0, VOCAB, size=B).astype(np.int32)
     return conf.astype(np.float32), cand, root
+
+
+def speculative_inputs(B: int, L: int, V: int = VOCAB, dtype: str = "bf16", seed: int = 0):
+    """Synthetic inputs for chain speculative sampling: target logits
+    [B][L+1][V] (tau * N(0, 1), tau ~ U(0.5, 3) per row, plus a few boosted
+    tokens so rows range from flat to peaked), draft logits [B][L][V] (the
+    target's row plus N(0, sigma^2) noise, sigma ~ U(0.2, 1.5) per row: a
+    drafter that mostly agrees), drafted tokens (the draft row's top token,
+    or with probability 0.3 one of its next seven, ranked by logit), and the
+    uniform draws u_acc [B][L], u_res [B]. Logits rounded to bf16 bits when
+    dtype is bf16."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 0x5B])))
+    tau = rng.uniform(0.5, 3.0, size=(B, L + 1, 1)).astype(np.float32)
+    p = rng.standard_normal((B, L + 1, V), dtype=np.float32) * tau
+    for idx in np.ndindex(B, L + 1):
+        hot = rng.choice(V, size=4, replace=False)
+        p[idx][hot] += rng.uniform(2.0, 8.0, size=4).astype(np.float32) * tau[idx][0]
+    sig = rng.uniform(0.2, 1.5, size=(B, L, 1)).astype(np.float32)
+    q = p[:, :L] + rng.standard_normal((B, L, V), dtype=np.float32) * sig
+    if dtype == "bf16":
+        p, q = bf16_bits_to_f32(f32_to_bf16_bits(p)), bf16_bits_to_f32(f32_to_bf16_bits(q))
+    draft = np.empty((B, L), dtype=np.int32)
+    for idx in np.ndindex(B, L):
+        order = np.argsort(-q[idx], kind="stable")[:8]
+        draft[idx] = order[0] if rng.random() >= 0.3 else order[rng.integers(1, 8)]
+    u_acc = rng.random((B, L)).astype(np.float32)
+    u_res = rng.random(B).astype(np.float32)
+    if dtype == "bf16":
+        p, q = f32_to_bf16_bits(p), f32_to_bf16_bits(q)
+    return p, q, draft, u_acc, u_res
