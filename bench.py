@@ -360,6 +360,94 @@ def bench_draft_tree(args) -> None:
     print(json.dumps(rec), flush=True)
 
 
+def bench_spec_sample(args) -> None:
+    """Chain speculative sampling (tv_speculative_sample): batch 8, 5 drafted
+    tokens per sequence, bf16 target and draft logits over a 32000-entry
+    vocabulary (the headline batch and vocabulary)."""
+    import numpy as np
+    import torch
+
+    import tree_attention_verification_tv_amd as tv
+    from workloads import bf16_bits_to_f32, speculative_inputs
+
+    dev = torch.device("cuda:0")
+    B, L, V = 8, 5, args.vocab
+    p, q, draft, u_acc, u_res = speculative_inputs(B, L, V=V, seed=args.config if args.seed is None else args.seed)
+    bf = lambda a: torch.from_numpy(a).view(torch.int16).view(torch.bfloat16)   # noqa: E731
+    row_bytes = V * 2
+    copies = args.copies or max(2, -(-4 * INFINITY_CACHE_BYTES // ((p.size + q.size) * 2)))
+    sets = [(bf(p).to(dev), bf(q).to(dev)) for _ in range(copies)]
+    d_draft, d_ua, d_ur = (torch.from_numpy(x).to(dev) for x in (draft, u_acc, u_res))
+    acc, toks, pt, qt = tv.speculative_sample(sets[0][0], sets[0][1], d_draft, d_ua, d_ur)
+    lib = tv._lib.load()
+    ws_n = int(lib.tv_speculative_sample_workspace_size(B, L))
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())   # noqa: E731
+    tail = (P(d_draft), P(d_ua), P(d_ur), B, L, P(pt), P(qt), P(acc), P(toks), P(ws), ws_n, sp)
+
+    def step(k):
+        pp, qq = sets[k % copies]
+        if lib.tv_speculative_sample(P(pp), P(qq), tv._lib.TV_BF16, V, *tail):
+            raise RuntimeError("tv_speculative_sample failed")
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(k)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for k in range(args.steps):
+        step(k)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    call_s = e0.elapsed_time(e1) * 1e-3 / args.steps
+    # every target and draft row is read once; the row drawn from is read again
+    algo = (B * (L + 1) + B * L) * row_bytes + 2 * B * row_bytes
+    achieved = algo / call_s / 1e9
+    rec = {
+        "metric": "chain speculative sampling: drafted tokens verified per second, 8 sequences x 5 tokens",
+        "value": B * L / ((t1 - t0) / args.steps),
+        "unit": "drafted-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": (t1 - t0) * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"spec-sample-b{B}-l{L}-v{V}", "batch": B, "drafted": L, "vocab": V,
+                   "input_copies_rotated": copies},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "tv_speculative_sample call: spec_stats_kernel + spec_sample_kernel; HIP events "
+                               "around K calls back to back",
+                     "algorithmic_bytes_per_launch": algo, "call_us_mean": call_s * 1e6},
+        "mean_accept_len": float(acc.float().mean().item()),
+        "kernel_source_hash": source_hash(["tv_typical.hip"]),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        pf, qf = bf16_bits_to_f32(p).astype(np.float64), bf16_bits_to_f32(q).astype(np.float64)
+        runs, t2 = 0, time.perf_counter()
+        while time.perf_counter() - t2 < 5.0:
+            for b in range(B):
+                oracle.speculative_sample(pf[b], qf[b], draft[b], u_acc[b].astype(np.float64), float(u_res[b]))
+            runs += 1
+        dt = time.perf_counter() - t2
+        rec["cpu_baseline"] = {"value": runs * B * L / dt, "unit": "drafted-tokens/s", "cores": 1,
+                               "kind": "oracle", "sample": f"{runs} passes over the {B} sequences, NumPy float64, "
+                                                           f"1 thread, {dt:.1f} s"}
+    print(json.dumps(rec), flush=True)
+
+
 def main() -> None:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -369,11 +457,12 @@ def main() -> None:
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated per step (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=None)
-    ap.add_argument("--workload", choices=("step", "typical", "paged", "draft-tree"), default="step",
+    ap.add_argument("--workload", choices=("step", "typical", "paged", "draft-tree", "spec-sample"), default="step",
                     help="step: the verification step (default); typical: typical acceptance "
                          "from target logits on the same trees; paged: the step over a paged "
                          "KV cache (shuffled 64-slot pages); draft-tree: EAGLE-2 tree "
-                         "construction from draft proposals")
+                         "construction from draft proposals; spec-sample: chain speculative "
+                         "sampling of 5 drafted tokens per sequence")
     ap.add_argument("--vocab", type=int, default=32000, help="vocabulary of --workload typical")
     args = ap.parse_args()
 
@@ -388,6 +477,9 @@ def main() -> None:
         return
     if args.workload == "draft-tree":
         bench_draft_tree(args)
+        return
+    if args.workload == "spec-sample":
+        bench_spec_sample(args)
         return
 
     import numpy as np

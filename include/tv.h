@@ -328,7 +328,7 @@ tv_status tv_accept_typical(const void* logits, int32_t dtype, int32_t vocab,
  *   tokens    [B][L + 1] out     the j kept tokens, the drawn token, then -1
  *   workspace                    >= tv_speculative_sample_workspace_size(B, L)
  *                                bytes of device scratch (row statistics)
- * Two kernels: per-row statistics (grid (L + 1, B)), then one workgroup per
+ * Two kernels: per-row statistics (grid (2L + 1, B)), then one workgroup per
  * sequence for the decisions and the draw. Host checks: pointers non-null
  * unless B == 0, 0 <= B <= 65535, 1 <= L <= TV_MAX_NODES, vocab >= 1, dtype
  * valid, workspace large enough. B == 0 is a no-op.

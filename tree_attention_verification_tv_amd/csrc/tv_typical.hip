@@ -323,47 +323,75 @@ __device__ __forceinline__ void row_ref_z(const T* row, int V, int tid, RowStat*
   __syncthreads();
 }
 
-// Grid (L + 1, B), 512 threads: target row i and, for i < L, draft row i:
-// (ref, z) of each into stats [B][2L + 1][2] (target rows first), and the
-// drafted token's probability under each (0 for an id outside [0, V)).
+// Grid (2L + 1, B), 512 threads, one logits row each: rows r <= L are the
+// target's rows r, rows L + 1 + i the draft's rows i. (ref, z) of each row
+// into stats [B][2L + 1][2], and the drafted token's probability under it
+// (0 for an id outside [0, V)) into p_tok / q_tok.
 template <typename T, int E>
 __global__ __launch_bounds__(kThreads) void spec_stats_kernel(
     const T* __restrict__ p_logits, const T* __restrict__ q_logits, int V, int L,
     const int32_t* __restrict__ draft, float* __restrict__ stats, float* __restrict__ p_tok,
     float* __restrict__ q_tok) {
   __shared__ RowStat s_part[kWaves];
-  const int i = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int x = i < L ? draft[static_cast<size_t>(b) * L + i] : 0;
-  const bool x_in = x >= 0 && x < V;
-  float* st = stats + static_cast<size_t>(b) * (2 * L + 1) * 2;
+  const int r = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const bool target = r <= L;
+  const int i = target ? r : r - (L + 1);
+  const T* row = target ? p_logits + (static_cast<size_t>(b) * (L + 1) + i) * V
+                        : q_logits + (static_cast<size_t>(b) * L + i) * V;
   float ref, z;
-  const T* prow = p_logits + (static_cast<size_t>(b) * (L + 1) + i) * V;
-  row_ref_z<T, E>(prow, V, tid, s_part, ref, z);
+  row_ref_z<T, E>(row, V, tid, s_part, ref, z);
   if (tid == 0) {
-    st[2 * i] = ref;
-    st[2 * i + 1] = z;
-    if (i < L) p_tok[static_cast<size_t>(b) * L + i] = x_in ? exp2f(fmaf(load_elem<T>(prow, x), kLog2e, -ref)) / z : 0.f;
-  }
-  if (i >= L) return;
-  const T* qrow = q_logits + (static_cast<size_t>(b) * L + i) * V;
-  row_ref_z<T, E>(qrow, V, tid, s_part, ref, z);
-  if (tid == 0) {
-    st[2 * (L + 1 + i)] = ref;
-    st[2 * (L + 1 + i) + 1] = z;
-    q_tok[static_cast<size_t>(b) * L + i] = x_in ? exp2f(fmaf(load_elem<T>(qrow, x), kLog2e, -ref)) / z : 0.f;
+    float* st = stats + (static_cast<size_t>(b) * (2 * L + 1) + r) * 2;
+    st[0] = ref;
+    st[1] = z;
+    if (i < L) {
+      const int x = draft[static_cast<size_t>(b) * L + i];
+      const float pr = (x >= 0 && x < V) ? exp2f(fmaf(load_elem<T>(row, x), kLog2e, -ref)) / z : 0.f;
+      (target ? p_tok : q_tok)[static_cast<size_t>(b) * L + i] = pr;
+    }
   }
 }
 
 constexpr int kSampleThreads = 1024;
+constexpr int kRun = 32;   // token ids per thread per round
 
-// Grid B, 1024 threads: the keep decisions, then one pass over the row to
-// draw from. Thread t sums the weights of a contiguous run of token ids; a
-// block scan of those sums gives every run's place in the running total, and
-// the one thread whose run holds u * total finds the token by summing its
-// run again in the same order (the runs meet exactly: each starts where the
-// scan ended the one before). If rounding leaves u * total past every run,
-// the last token of positive weight is drawn.
-template <typename T>
+// The weights of one thread's run of kRun token ids from y0 (ids past V
+// weigh 0): p(y) or max(0, p(y) - q(y)), p(y) = 2^(x log2(e) - ref) / z.
+// Whole runs of a 16-byte-aligned row are read as 16-byte vectors.
+template <typename T, int E>
+__device__ __forceinline__ void run_weights(const T* prow, const T* qrow, bool resid, int V, int y0, float pref,
+                                            float pinv, float qref, float qinv, float (&w)[kRun]) {
+  auto one = [&](float xp, float xq) {
+    const float a = exp2_sum_term(fmaf(xp, kLog2e, -pref)) * pinv;
+    return resid ? fmaxf(a - exp2_sum_term(fmaf(xq, kLog2e, -qref)) * qinv, 0.0f) : a;
+  };
+  if (E > 1 && y0 + kRun <= V) {
+    using Chunk = typename ChunkOf<T, E>::type;
+#pragma unroll
+    for (int k = 0; k < kRun / E; ++k) {
+      const Chunk cp = load_chunk<T, E>(prow, y0 / E + k);
+      const Chunk cq = resid ? load_chunk<T, E>(qrow, y0 / E + k) : cp;
+#pragma unroll
+      for (int e = 0; e < E; ++e) w[k * E + e] = one(chunk_elem<T, E>(cp, e), chunk_elem<T, E>(cq, e));
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kRun; ++k) {
+      const int y = y0 + k;
+      w[k] = y < V ? one(load_elem<T>(prow, y), resid ? load_elem<T>(qrow, y) : 0.0f) : 0.0f;
+    }
+  }
+}
+
+// Grid B, 1024 threads: the keep decisions, then the draw. The row is cut
+// into rounds of 1024 runs of kRun ids (round r, thread t: ids from
+// (r * 1024 + t) * kRun); in id order a thread sums its run's weights, and a
+// block scan of those sums places every run in the running total. A first
+// pass over the rounds gives the total W; the second repeats the same sums
+// in the same order, so the runs tile [0, W) exactly, and the one thread
+// whose run holds u * W finds the token in its run. If rounding leaves
+// u * W past every run, the last token of positive weight is drawn.
+template <typename T, int E>
 __global__ __launch_bounds__(kSampleThreads) void spec_sample_kernel(
     const T* __restrict__ p_logits, const T* __restrict__ q_logits, int V, int L,
     const int32_t* __restrict__ draft, const float* __restrict__ u_acc, const float* __restrict__ u_res,
@@ -394,55 +422,79 @@ __global__ __launch_bounds__(kSampleThreads) void spec_sample_kernel(
   const float qref = resid ? st[2 * (L + 1 + j)] : 0.f, qinv = resid ? 1.0f / st[2 * (L + 1 + j) + 1] : 0.f;
   const T* prow = p_logits + (static_cast<size_t>(b) * (L + 1) + j) * V;
   const T* qrow = q_logits + (static_cast<size_t>(b) * L + (resid ? j : 0)) * V;
-  auto weight = [&](int y) {
-    float w = exp2f(fmaf(load_elem<T>(prow, y), kLog2e, -pref)) * pinv;
-    if (resid) w = fmaxf(w - exp2f(fmaf(load_elem<T>(qrow, y), kLog2e, -qref)) * qinv, 0.0f);
-    return w;
-  };
-  const int seg = (V + kSampleThreads - 1) / kSampleThreads;
-  const int y0 = min(V, tid * seg), y1 = min(V, y0 + seg);
-  float S = 0.f;
-  int last = -1;
-  for (int y = y0; y < y1; ++y) {
-    const float w = weight(y);
-    S += w;
-    if (w > 0.f) last = y;
-  }
-  // inclusive scan of the run sums: within the wave, then over the waves
-  float inc = S;
+  const int rounds = (V + kSampleThreads * kRun - 1) / (kSampleThreads * kRun);
+
+  // Block scan of one value per thread: the running sums before (exc) and
+  // after (inc) this thread's value, and the block's total. A thread's exc
+  // is bit for bit the previous thread's inc (the same additions in the
+  // same order), so the runs' intervals meet exactly.
+  auto block_scan = [&](float S, float& exc, float& inc, float& total) {
+    float x = S;
 #pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const float o = __shfl_up(inc, off);
-    if (lane >= off) inc += o;
+    for (int off = 1; off < kWave; off <<= 1) {
+      const float o = __shfl_up(x, off);
+      if (lane >= off) x += o;
+    }
+    float xe = __shfl_up(x, 1);
+    if (lane == 0) xe = 0.f;
+    if (lane == kWave - 1) s_wsum[wave] = x;
+    __syncthreads();
+    float before = 0.f;
+    total = 0.f;
+    for (int w = 0; w < kW; ++w) {
+      if (w < wave) before += s_wsum[w];
+      total += s_wsum[w];
+    }
+    __syncthreads();
+    exc = lane == 0 ? before : before + xe;
+    inc = before + x;
+  };
+
+  float w[kRun];
+  float W = 0.f;
+  int last = -1;
+  for (int pass = 0; pass < 2; ++pass) {
+    const float t = pass ? u_res[b] * W : 0.f;
+    float base = 0.f;
+    for (int r = 0; r < rounds; ++r) {
+      const int y0 = (r * kSampleThreads + tid) * kRun;
+      if (pass == 0 || rounds > 1) run_weights<T, E>(prow, qrow, resid, V, y0, pref, pinv, qref, qinv, w);
+      float S = 0.f;
+#pragma unroll
+      for (int k = 0; k < kRun; ++k) {
+        S += w[k];
+        if (pass == 0 && w[k] > 0.f) last = y0 + k;
+      }
+      float exc, inc, total;
+      block_scan(S, exc, inc, total);
+      const float lo = base + exc, hi = base + inc;
+      if (pass == 1 && S > 0.f && lo <= t && t < hi) {
+        float acc = lo;
+        int pick = -1;
+#pragma unroll
+        for (int k = 0; k < kRun; ++k) {
+          acc += w[k];
+          if (pick < 0 && w[k] > 0.f && acc > t) pick = y0 + k;
+        }
+        if (pick < 0)
+          for (int k = kRun - 1; k >= 0; --k)
+            if (w[k] > 0.f) {
+              pick = y0 + k;
+              break;
+            }
+        s_y = pick;
+      }
+      base += total;
+    }
+    if (pass == 0) W = base;
   }
   int lmax = last;
 #pragma unroll
   for (int off = kWave / 2; off >= 1; off >>= 1) lmax = max(lmax, __shfl_xor(lmax, off));
-  if (lane == kWave - 1) s_wsum[wave] = inc;
   if (lane == 0) s_last[wave] = lmax;
   __syncthreads();
-  float before = 0.f, total = 0.f;
   int last_all = -1;
-  for (int w = 0; w < kW; ++w) {
-    if (w < wave) before += s_wsum[w];
-    total += s_wsum[w];
-    last_all = max(last_all, s_last[w]);
-  }
-  const float hi = before + inc, lo = hi - S;   // this run's place
-  const float t = u_res[b] * total;
-  if (S > 0.f && lo <= t && t < hi) {
-    float acc = lo;
-    int pick = last;
-    for (int y = y0; y < y1; ++y) {
-      acc += weight(y);
-      if (acc > t) {
-        pick = y;
-        break;
-      }
-    }
-    s_y = pick;
-  }
-  __syncthreads();
+  for (int q = 0; q < kW; ++q) last_all = max(last_all, s_last[q]);
   const int y = s_y >= 0 ? s_y : last_all;
   const size_t row = static_cast<size_t>(b) * (L + 1);
   for (int k = tid; k <= L; k += kSampleThreads)
@@ -487,7 +539,7 @@ hipError_t launch_speculative_sample(const void* p_logits, const void* q_logits,
                                      const int32_t* draft, const float* u_acc, const float* u_res, int B, int L,
                                      float* p_tok, float* q_tok, int32_t* accept_len, int32_t* tokens,
                                      float* stats, hipStream_t s) {
-  const dim3 grid(L + 1, B);
+  const dim3 grid(2 * L + 1, B);
   const bool aligned = (reinterpret_cast<uintptr_t>(p_logits) % 16 == 0) &&
                        (reinterpret_cast<uintptr_t>(q_logits) % 16 == 0) &&
                        ((static_cast<size_t>(V) * elem_bytes) % 16 == 0);
@@ -502,8 +554,12 @@ hipError_t launch_speculative_sample(const void* p_logits, const void* q_logits,
                          p_tok, q_tok);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((spec_sample_kernel<uint16_t>), dim3(B), dim3(kSampleThreads), 0, s, p, q, V, L, draft,
-                       u_acc, u_res, stats, p_tok, q_tok, accept_len, tokens);
+    if (aligned)
+      hipLaunchKernelGGL((spec_sample_kernel<uint16_t, 8>), dim3(B), dim3(kSampleThreads), 0, s, p, q, V, L,
+                         draft, u_acc, u_res, stats, p_tok, q_tok, accept_len, tokens);
+    else
+      hipLaunchKernelGGL((spec_sample_kernel<uint16_t, 1>), dim3(B), dim3(kSampleThreads), 0, s, p, q, V, L,
+                         draft, u_acc, u_res, stats, p_tok, q_tok, accept_len, tokens);
   } else {
     const auto* p = static_cast<const float*>(p_logits);
     const auto* q = static_cast<const float*>(q_logits);
@@ -515,8 +571,12 @@ hipError_t launch_speculative_sample(const void* p_logits, const void* q_logits,
                          p_tok, q_tok);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((spec_sample_kernel<float>), dim3(B), dim3(kSampleThreads), 0, s, p, q, V, L, draft, u_acc,
-                       u_res, stats, p_tok, q_tok, accept_len, tokens);
+    if (aligned)
+      hipLaunchKernelGGL((spec_sample_kernel<float, 4>), dim3(B), dim3(kSampleThreads), 0, s, p, q, V, L, draft,
+                         u_acc, u_res, stats, p_tok, q_tok, accept_len, tokens);
+    else
+      hipLaunchKernelGGL((spec_sample_kernel<float, 1>), dim3(B), dim3(kSampleThreads), 0, s, p, q, V, L, draft,
+                         u_acc, u_res, stats, p_tok, q_tok, accept_len, tokens);
   }
   return hipGetLastError();
 }
