@@ -32,6 +32,11 @@
  *     inactive sequence. At most TV_MAX_NODES nodes per tree.
  *   - Integer arrays are int32 unless noted; tensors are row-major in the
  *     shapes given, all of one dtype (TV_F32 or TV_BF16).
+ *   - Environment: TV_ATTN_TUNE="waves=W qt=Q splits=S" (any subset) overrides
+ *     the bf16 attention's launch plan (wavefronts per workgroup 2 or 4, query
+ *     tiles per wavefront 1 or 2, key splits 1..8), read once per process,
+ *     for tuning sweeps; tv_tree_attention_workspace_size follows the same
+ *     plan. Results do not depend on it beyond rounding order.
  */
 #ifndef TV_H
 #define TV_H
