@@ -69,6 +69,33 @@ def algorithmic_bytes(w) -> dict:
                 tree_kv_append=tree_kv_append, out=out, total=total)
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak of one MI355X
+
+
+def algorithmic_flops(w) -> int:
+    """Multiply-add flops of the attention (live nodes only): per query row,
+    2 D for each score and 2 D for each value row it weighs, over the prefix
+    and the node's ancestors-or-self (depth + 1 keys)."""
+    import numpy as np
+    total = 0
+    for b in range(w.B):
+        n = int(w.n_nodes[b])
+        depth = np.zeros(n, dtype=np.int64)
+        for i in range(1, n):
+            depth[i] = depth[w.parents[b, i]] + 1
+        keys = int(w.prefix_len[b]) * n + int((depth + 1).sum())
+        total += 4 * w.D * w.Hq * keys
+    return total
+
+
+def roofline_bound(w, bytes_: int, flops: int) -> str:
+    """The bound of a bf16 call is the matrix cores when its arithmetic
+    intensity exceeds the chip's ridge (peak flops / peak bytes), else HBM;
+    fp32 calls run on the vector ALU at about one flop per byte (HBM)."""
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    return "mfma" if w.dtype == "bf16" and flops > ridge * bytes_ else "hbm"
+
+
 def load_traffic(workload: str):
     """Measured HBM bytes per tv_tree_attention call (rocprofv3 FETCH_SIZE +
     WRITE_SIZE of its kernels, scaled by a plain copy), valid only for the
@@ -617,7 +644,12 @@ def main() -> None:
     attn_mean_s = float(np.mean(attn_ms)) * 1e-3
     attn_b2b_s = e0.elapsed_time(e1) * 1e-3 / args.steps
     ab = algorithmic_bytes(w)
-    achieved = ab["total"] / attn_mean_s / 1e9
+    flops = algorithmic_flops(w)
+    bound = roofline_bound(w, ab["total"], flops)
+    if bound == "mfma":
+        achieved, peak, unit = flops / attn_mean_s / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+    else:
+        achieved, peak, unit = ab["total"] / attn_mean_s / 1e9, HBM_PEAK_GBS, "GB/s"
     wname = f"{w.name}-paged" if paged else w.name
     traffic = load_traffic(wname)
 
@@ -638,11 +670,14 @@ def main() -> None:
                    "head_dim": w.D, "prefix_len_mean": float(np.mean(w.prefix_len)),
                    "tree_nodes": int(w.n_nodes.max()), "input_copies_rotated": copies,
                    "seed": args.config if args.seed is None else args.seed},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+        "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+                     "frac": achieved / peak, "traffic": traffic,
                      "kernel": "tv_tree_attention call: attn_bf16_kernel + merge_bf16_kernel (split merge "
                                "and tree append); HIP events on its stream around each call, in the step",
                      "algorithmic_bytes_per_launch": ab["total"],
+                     "algorithmic_flops_per_launch": flops,
+                     "hbm_frac": ab["total"] / attn_mean_s / 1e9 / HBM_PEAK_GBS,
+                     "mfma_frac": flops / attn_mean_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                      "attention_us_mean": attn_mean_s * 1e6,
                      "attention_us_p10": float(np.percentile(attn_ms, 10)) * 1e3,
                      "attention_us_p90": float(np.percentile(attn_ms, 90)) * 1e3,
