@@ -1,0 +1,44 @@
+"""GPU parity of the bf16 attention under launch plans the automatic choice
+does not take on the test workloads (TV_ATTN_TUNE: wavefronts per workgroup,
+query tiles per wavefront, key splits). The library reads the override once
+per process, so each plan runs in a child process of its own, one at a
+time, on the same small cases as the full-parity tests, against the oracle
+at the same tolerance. Results do not depend on the plan beyond rounding
+order."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# (cfg, overrides) from the full-parity list: 64, 240 and 512 rows per KV
+# head, a ragged tail and ragged prefixes
+CASES = [(2, dict(prefix=300)), (3, dict(B=2, prefix=1100)), (4, dict(B=2, prefix=200)),
+         (5, dict(B=6, prefix=(16, 300)))]
+PLANS = ["waves=2,qt=1", "waves=2,qt=1,splits=1", "waves=4,qt=1,splits=8", "qt=2,splits=2", "splits=1"]
+
+
+def child_main(plan: str) -> None:
+    sys.path.insert(0, ROOT)
+    from tests.test_gpu_parity import test_small_workloads_full_parity
+    for cfg, over in CASES:
+        test_small_workloads_full_parity(cfg, over)
+        print(f"ok plan={plan} cfg={cfg} {over}", flush=True)
+
+
+@pytest.mark.parametrize("plan", PLANS)
+def test_plan_parity(plan):
+    print(f"[gpu] attention plan {plan}", flush=True)
+    env = dict(os.environ, TV_ATTN_TUNE=plan)
+    r = subprocess.run([sys.executable, "-u", "-m", "tests.test_gpu_tune", plan], cwd=ROOT, env=env,
+                       capture_output=True, text=True, timeout=110)
+    print(r.stdout[-2000:], flush=True)
+    assert r.returncode == 0, r.stderr[-3000:]
+    assert r.stdout.count("ok plan=") == len(CASES)
+
+
+if __name__ == "__main__":
+    child_main(sys.argv[1])
