@@ -172,6 +172,22 @@ def test_full_size_workloads_sampled(cfg):
     print(f"  attention error {worst:.3g}; mean accepted {res['accept_len'].mean():.2f}", flush=True)
 
 
+@pytest.mark.parametrize("B,prefix", [(1, 32768), (2, 16000)])
+def test_long_prefix_eight_splits(B, prefix):
+    """Long-context verification: with one or two sequences the automatic
+    plan splits each KV head's keys eight ways (64 or 65 tiles per split);
+    attention on sampled rows, integer results and the commit in full."""
+    print(f"[gpu] long prefix B={B} P={prefix}", flush=True)
+    w = generate(3, B=B, prefix=prefix)
+    d = upload(w, DEV)
+    res = run_step(w, d)
+    worst = check_step(w, res, rows=sample_rows(w, per_seq=5, seed=B), untouched=False)
+    for b in range(w.B):
+        P, L = int(w.prefix_len[b]), int(res["accept_len"][b])
+        assert res["prefix_len_out"][b] == P + L + 1
+    print(f"  attention error {worst:.3g}", flush=True)
+
+
 @pytest.mark.parametrize("cfg", [3, 5])
 def test_attention_is_deterministic(cfg):
     """Repeated calls on the same inputs give the same bits (each call
