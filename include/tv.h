@@ -34,7 +34,7 @@
  *     shapes given, all of one dtype (TV_F32 or TV_BF16).
  *   - Environment: TV_ATTN_TUNE="waves=W qt=Q splits=S" (any subset) overrides
  *     the bf16 attention's launch plan (wavefronts per workgroup 2 or 4, query
- *     tiles per wavefront 1 or 2, key splits 1..8), read once per process,
+ *     tiles per wavefront 1 or 2, key splits 1..16), read once per process,
  *     for tuning sweeps; tv_tree_attention_workspace_size follows the same
  *     plan. Results do not depend on it beyond rounding order.
  */

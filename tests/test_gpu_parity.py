@@ -173,10 +173,11 @@ def test_full_size_workloads_sampled(cfg):
 
 
 @pytest.mark.parametrize("B,prefix", [(1, 32768), (2, 16000)])
-def test_long_prefix_eight_splits(B, prefix):
+def test_long_prefix_sixteen_splits(B, prefix):
     """Long-context verification: with one or two sequences the automatic
-    plan splits each KV head's keys eight ways (64 or 65 tiles per split);
-    attention on sampled rows, integer results and the commit in full."""
+    plan splits each KV head's keys sixteen ways (33 or 16 tiles per split,
+    the merge's largest instance); attention on sampled rows, integer
+    results and the commit in full."""
     print(f"[gpu] long prefix B={B} P={prefix}", flush=True)
     w = generate(3, B=B, prefix=prefix)
     d = upload(w, DEV)

@@ -18,7 +18,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 # head, a ragged tail and ragged prefixes
 CASES = [(2, dict(prefix=300)), (3, dict(B=2, prefix=1100)), (4, dict(B=2, prefix=200)),
          (5, dict(B=6, prefix=(16, 300)))]
-PLANS = ["waves=2,qt=1", "waves=2,qt=1,splits=1", "waves=4,qt=1,splits=8", "qt=2,splits=2", "splits=1"]
+PLANS = ["waves=2,qt=1", "waves=2,qt=1,splits=1", "waves=4,qt=1,splits=8", "qt=2,splits=2", "splits=1",
+         "splits=16"]
 
 
 def child_main(plan: str) -> None:

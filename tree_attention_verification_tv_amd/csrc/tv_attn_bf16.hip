@@ -93,7 +93,7 @@ constexpr int kKT = 64;                 // keys per LDS stage (= V cache block)
 constexpr int kStageElems = kKT * kD;   // bf16 elements of one K (or V) stage
 constexpr int kStages = 5;              // LDS ring of key tiles
 constexpr int kAhead = 3;               // tiles in flight
-constexpr int kMaxSplits = 8;           // key splits per row block
+constexpr int kMaxSplits = 16;          // key splits per row block
 constexpr int kCsElems = 64 * 64 * 4;   // bf16 units of the RoPE table: 64 depths x 64 (cos, sin) = one stage
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -1747,18 +1747,21 @@ hipError_t launch_attention_bf16(const tv_attn_args* a, const AttnPlan& pl, cons
     hipLaunchKernelGGL(append_bf16_kernel, dim3(kAppendBlocks + 1, a->Hkv, a->B), dim3(256), 0, s, p);
     return hipGetLastError();
   }
-  const int sk = pl.splits <= 2 ? 2 : (pl.splits <= 4 ? 4 : 8);
-  static_assert(kMaxSplits == 8, "merge instances cover up to eight splits");
-  switch (key * 10 + sk) {
-    case 212: hipLaunchKernelGGL((merge_bf16_kernel<2, 1, 2>), mgrid, dim3(256), 0, s, p); break;
-    case 214: hipLaunchKernelGGL((merge_bf16_kernel<2, 1, 4>), mgrid, dim3(256), 0, s, p); break;
-    case 218: hipLaunchKernelGGL((merge_bf16_kernel<2, 1, 8>), mgrid, dim3(256), 0, s, p); break;
-    case 412: hipLaunchKernelGGL((merge_bf16_kernel<4, 1, 2>), mgrid, dim3(256), 0, s, p); break;
-    case 414: hipLaunchKernelGGL((merge_bf16_kernel<4, 1, 4>), mgrid, dim3(256), 0, s, p); break;
-    case 418: hipLaunchKernelGGL((merge_bf16_kernel<4, 1, 8>), mgrid, dim3(256), 0, s, p); break;
-    case 422: hipLaunchKernelGGL((merge_bf16_kernel<4, 2, 2>), mgrid, dim3(256), 0, s, p); break;
-    case 424: hipLaunchKernelGGL((merge_bf16_kernel<4, 2, 4>), mgrid, dim3(256), 0, s, p); break;
-    default: hipLaunchKernelGGL((merge_bf16_kernel<4, 2, 8>), mgrid, dim3(256), 0, s, p); break;
+  const int sk = pl.splits <= 2 ? 2 : pl.splits <= 4 ? 4 : pl.splits <= 8 ? 8 : 16;
+  static_assert(kMaxSplits == 16, "merge instances cover up to sixteen splits");
+  switch (key * 100 + sk) {
+    case 2102: hipLaunchKernelGGL((merge_bf16_kernel<2, 1, 2>), mgrid, dim3(256), 0, s, p); break;
+    case 2104: hipLaunchKernelGGL((merge_bf16_kernel<2, 1, 4>), mgrid, dim3(256), 0, s, p); break;
+    case 2108: hipLaunchKernelGGL((merge_bf16_kernel<2, 1, 8>), mgrid, dim3(256), 0, s, p); break;
+    case 2116: hipLaunchKernelGGL((merge_bf16_kernel<2, 1, 16>), mgrid, dim3(256), 0, s, p); break;
+    case 4102: hipLaunchKernelGGL((merge_bf16_kernel<4, 1, 2>), mgrid, dim3(256), 0, s, p); break;
+    case 4104: hipLaunchKernelGGL((merge_bf16_kernel<4, 1, 4>), mgrid, dim3(256), 0, s, p); break;
+    case 4108: hipLaunchKernelGGL((merge_bf16_kernel<4, 1, 8>), mgrid, dim3(256), 0, s, p); break;
+    case 4116: hipLaunchKernelGGL((merge_bf16_kernel<4, 1, 16>), mgrid, dim3(256), 0, s, p); break;
+    case 4202: hipLaunchKernelGGL((merge_bf16_kernel<4, 2, 2>), mgrid, dim3(256), 0, s, p); break;
+    case 4204: hipLaunchKernelGGL((merge_bf16_kernel<4, 2, 4>), mgrid, dim3(256), 0, s, p); break;
+    case 4208: hipLaunchKernelGGL((merge_bf16_kernel<4, 2, 8>), mgrid, dim3(256), 0, s, p); break;
+    default: hipLaunchKernelGGL((merge_bf16_kernel<4, 2, 16>), mgrid, dim3(256), 0, s, p); break;
   }
   return hipGetLastError();
 }
