@@ -22,20 +22,31 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kMaxCreated = 1 + TV_MAX_DRAFT_PROPOSALS;
+constexpr int kValSlots = (kMaxCreated + 3) & ~3;   // whole four-value runs past the last node
 
 // Number of j in [a, b) with vals[j] >= v (GE) or vals[j] > v: aligned runs
-// of four values per LDS access, single values at the ragged ends.
+// of four values per LDS access; a ragged first or last run is one aligned
+// read with its values outside [a, b) masked (vals holds whole runs).
 template <bool GE>
 __device__ __forceinline__ int count_from(const float* vals, int a, int b, float v) {
   auto ahead = [&](float u) { return GE ? (u >= v) : (u > v); };
-  int r = 0, j = a;
-  for (; j < b && (j & 3); ++j) r += ahead(vals[j]);
+  auto masked_run = [&](int j) {
+    const float4 u = *reinterpret_cast<const float4*>(vals + j);
+    return (j >= a && j < b && ahead(u.x)) + (j + 1 >= a && j + 1 < b && ahead(u.y)) +
+           (j + 2 >= a && j + 2 < b && ahead(u.z)) + (j + 3 >= a && j + 3 < b && ahead(u.w));
+  };
+  if (a >= b) return 0;
+  int r = 0, j = a & ~3;
+  if (j < a) {
+    r += masked_run(j);
+    j += 4;
+  }
 #pragma unroll 4
   for (; j + 4 <= b; j += 4) {
     const float4 u = *reinterpret_cast<const float4*>(vals + j);
     r += ahead(u.x) + ahead(u.y) + ahead(u.z) + ahead(u.w);
   }
-  for (; j < b; ++j) r += ahead(vals[j]);
+  if (j < b) r += masked_run(j);
   return r;
 }
 
@@ -68,7 +79,7 @@ __global__ __launch_bounds__(kThreads) void eagle2_tree_kernel(
     float* __restrict__ values, int32_t* __restrict__ n_nodes) {
   __shared__ float s_conf[TV_MAX_DRAFT_PROPOSALS];
   __shared__ int s_cand[TV_MAX_DRAFT_PROPOSALS];
-  __shared__ __attribute__((aligned(16))) float s_val[kMaxCreated];
+  __shared__ __attribute__((aligned(16))) float s_val[kValSlots];
   __shared__ int s_par[kMaxCreated];
   __shared__ int s_tok[kMaxCreated];
   __shared__ int s_rank[kMaxCreated];
