@@ -70,6 +70,10 @@ def algorithmic_bytes(w) -> dict:
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak of one MI355X
+# one vector-ALU operation per lane per cycle: 256 CUs x 4 SIMDs x 32 lanes'
+# worth of fp32 FMAs at 2.4 GHz is 157.3 TFLOP/s counted as two flops each,
+# so 78.6 T single operations (a compare) per second
+ALU_OPS_PEAK_T = 157.3 / 2
 
 
 def algorithmic_flops(w) -> int:
@@ -367,10 +371,12 @@ def bench_draft_tree(args) -> None:
         "data": "synthetic",
         "config": {"workload": f"eagle2-draft-tree-b{B}-s{S}-k{K}-m{M}-n{n}", "batch": B, "steps": S,
                    "grown_per_layer": K, "children": M, "nodes_kept": n},
-        "roofline": {"bound": "alu", "achieved": achieved, "peak": 157.3, "unit": "Tcompare/s",
-                     "frac": achieved / 157.3, "traffic": None,
+        "roofline": {"bound": "alu", "achieved": achieved, "peak": ALU_OPS_PEAK_T, "unit": "Tcompare/s",
+                     "frac": achieved / ALU_OPS_PEAK_T, "traffic": None,
                      "kernel": "eagle2_tree_kernel (one workgroup per tree); HIP events around K calls "
-                               "back to back; work = rank comparisons, peak = fp32 vector rate",
+                               "back to back; work = rank comparisons, peak = one vector-ALU operation "
+                               "per lane per cycle (the fp32 FMA rate 157.3 TFLOP/s counts two flops "
+                               "per FMA)",
                      "comparisons_per_launch": comps, "call_us_mean": call_s * 1e6},
         "kernel_source_hash": source_hash(["tv_draft.hip"]),
     }

@@ -32,11 +32,12 @@
  *     inactive sequence. At most TV_MAX_NODES nodes per tree.
  *   - Integer arrays are int32 unless noted; tensors are row-major in the
  *     shapes given, all of one dtype (TV_F32 or TV_BF16).
- *   - Environment: TV_ATTN_TUNE="waves=W qt=Q splits=S" (any subset) overrides
- *     the bf16 attention's launch plan (wavefronts per workgroup 2 or 4, query
- *     tiles per wavefront 1 or 2, key splits 1..16), read once per process,
- *     for tuning sweeps; tv_tree_attention_workspace_size follows the same
- *     plan. Results do not depend on it beyond rounding order.
+ *   - Environment: TV_ATTN_TUNE="waves=W qt=Q splits=S fused=F" (any subset)
+ *     overrides the bf16 attention's launch plan (wavefronts per workgroup 2
+ *     or 4, query tiles per wavefront 1 or 2, key splits 1..16; fused=0 makes
+ *     a separate kernel merge the key splits), read once per process, for
+ *     tuning sweeps; tv_tree_attention_workspace_size follows the same plan.
+ *     Results do not depend on it beyond rounding order.
  */
 #ifndef TV_H
 #define TV_H
@@ -164,9 +165,13 @@ typedef struct tv_attn_args {
   void* out;              /* [B][n_max][Hq][D]   attention output; rows of
                              padding nodes and skipped sequences are zero    */
   void* workspace;        /* device scratch, >= tv_tree_attention_workspace_size
-                             bytes (may be NULL when that size is 0); no
-                             initial contents needed. Calls that may run at
-                             the same time need separate workspaces.        */
+                             bytes (may be NULL when that size is 0). Its
+                             first 16 KiB (when the size is not 0) hold
+                             synchronisation words of the split merge: zero
+                             them before the first use; every call leaves
+                             them zero again (the rest needs no initial
+                             contents). Calls that may run at the same time
+                             need separate workspaces.                      */
   size_t workspace_bytes;
   int32_t B, n_max, Hq, Hkv, D, cap;
   int32_t dtype;          /* tv_dtype                                        */
@@ -362,8 +367,11 @@ tv_status tv_speculative_sample(const void* p_logits, const void* q_logits, int3
  *   prefix_len_out   [B] out; may be the same array as prefix_len_in
  * Host checks: pointers non-null unless B == 0, Hkv >= 1, D in {64, 128},
  * 1 <= n_max <= TV_MAX_NODES, cap >= n_max, cap % 64 == 0, dtype valid. Device side,
- * a path that would read or write outside [P, cap) leaves that sequence
- * unchanged.
+ * a path entry outside [0, n_max), accept_len outside [0, n_max), or a move
+ * that would read or write outside [P, cap) leaves that sequence unchanged
+ * (prefix_len_out = prefix_len_in). Any path with entries in [0, n_max) is
+ * moved as the simultaneous copy above (tv_accept's paths are strictly
+ * increasing, but the copy does not rely on it).
  */
 tv_status tv_commit(void* k_cache, void* v_cache, int32_t B, int32_t Hkv, int32_t cap,
                     int32_t D, int32_t dtype, const int32_t* prefix_len_in,

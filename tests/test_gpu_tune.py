@@ -18,16 +18,20 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 # head, a ragged tail and ragged prefixes
 CASES = [(2, dict(prefix=300)), (3, dict(B=2, prefix=1100)), (4, dict(B=2, prefix=200)),
          (5, dict(B=6, prefix=(16, 300)))]
+# fused=0: the separate merge kernel on plans the automatic choice merges in
+# the kernel; splits=2 / 4: the fused merge with two and four splits
 PLANS = ["waves=2,qt=1", "waves=2,qt=1,splits=1", "waves=4,qt=1,splits=8", "qt=2,splits=2", "splits=1",
-         "splits=16"]
+         "splits=16", "fused=0", "splits=2", "waves=4,qt=1,splits=4", "splits=4,fused=0"]
 
 
 def child_main(plan: str) -> None:
     sys.path.insert(0, ROOT)
-    from tests.test_gpu_parity import test_small_workloads_full_parity
+    from tests.test_gpu_parity import test_small_workloads_full_parity, test_uniformly_low_scores_with_empty_splits
     for cfg, over in CASES:
         test_small_workloads_full_parity(cfg, over)
         print(f"ok plan={plan} cfg={cfg} {over}", flush=True)
+    test_uniformly_low_scores_with_empty_splits()
+    print(f"ok plan={plan} low scores", flush=True)
 
 
 @pytest.mark.parametrize("plan", PLANS)
@@ -38,7 +42,7 @@ def test_plan_parity(plan):
                        capture_output=True, text=True, timeout=110)
     print(r.stdout[-2000:], flush=True)
     assert r.returncode == 0, r.stderr[-3000:]
-    assert r.stdout.count("ok plan=") == len(CASES)
+    assert r.stdout.count("ok plan=") == len(CASES) + 1
 
 
 if __name__ == "__main__":

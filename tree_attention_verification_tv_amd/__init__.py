@@ -189,21 +189,27 @@ def tree_attention_workspace_size(args: TvAttnArgs) -> int:
 
 
 def new_workspace(nbytes: int, device) -> torch.Tensor:
-    """A workspace for tree_attention (its contents need no initialisation)."""
-    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    """A workspace for tree_attention: zero-filled, as the library requires
+    before its first use (the calls leave its synchronisation words zero)."""
+    return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
 _WORKSPACES: dict = {}
 
 
-def _default_workspace(device, need: int) -> torch.Tensor:
+def _default_workspace(device, need: int, stream=None) -> torch.Tensor:
     """Per-device workspace shared by calls that pass none (calls on one
-    device must then not overlap on different streams)."""
+    device must then not overlap on different streams). When the kernels
+    run on a stream other than the current one, the tensor is recorded on
+    that stream, so that replacing it by a larger one cannot hand its memory
+    to other work while the kernels still use it."""
     key = torch.device(device).index
     ws = _WORKSPACES.get(key)
     if ws is None or ws.numel() < need:
         ws = new_workspace(need, device)
         _WORKSPACES[key] = ws
+    if stream is not None and stream != torch.cuda.current_stream(ws.device):
+        ws.record_stream(stream)
     return ws
 
 
@@ -221,7 +227,7 @@ def tree_attention(q, k_new, v_new, k_cache, v_cache, prefix_len, n_nodes, anc, 
     if need > a.workspace_bytes:
         if workspace is not None:
             raise ValueError(f"workspace holds {a.workspace_bytes} bytes, {need} needed")
-        workspace = _default_workspace(q.device, need)
+        workspace = _default_workspace(q.device, need, stream)
         a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
     _lib.check("tv_tree_attention", lib.tv_tree_attention(ctypes.byref(a), _stream(stream)))
     return out
@@ -254,7 +260,7 @@ def tree_attention_paged(q, k_new, v_new, k_pool, v_pool, block_table, prefix_le
     if need > a.workspace_bytes:
         if workspace is not None:
             raise ValueError(f"workspace holds {a.workspace_bytes} bytes, {need} needed")
-        workspace = _default_workspace(q.device, need)
+        workspace = _default_workspace(q.device, need, stream)
         a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
     _lib.check("tv_tree_attention_paged",
                lib.tv_tree_attention_paged(ctypes.byref(a), ctypes.byref(pk), _stream(stream)))

@@ -44,8 +44,8 @@
 //          branch in the tile loop. A row whose sum left [2^-60, 2^62] is
 //          caught at the end; the workgroup then finds every row's exact max
 //          in a scores-only pass and redoes the pass with p = exp2(s - max)
-//          (exact for any score range). Row sums add up the bf16
-//          probabilities, i.e. exactly the weights the PV product used.
+//          (exact for any score range). Row sums add up the fp32
+//          probabilities (the PV product weights their bf16 roundings).
 //
 //          The score MFMA reads K rows in a permuted order (row m of a 32-key
 //          block is key perm(m)), so each lane half holds 8 CONSECUTIVE keys
@@ -124,6 +124,12 @@ struct BfParams {
   // j of sequence b is page block_table[b * max_pages + j]; cap = 64 max_pages
   const int32_t* block_table;
   int max_pages, num_pages;
+  // fused split merge (see merge_in_kernel): the partials are published with
+  // agent-coherent stores and merged by the workgroups themselves; sync holds
+  // four words per (sequence, KV head, row block), zero between calls
+  int fused;
+  uint32_t* sync;
+  size_t ws_bytes;   // workspace bytes (buffer-resource range of the partials)
 };
 
 // Two floats -> packed bf16 pair (hardware round to nearest even).
@@ -190,6 +196,17 @@ __device__ __forceinline__ float row_sum2(float v) {
 // LDS byte address of a shared-memory pointer.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
+}
+
+// Agent-coherent access to the split partials (the sc1 cache policy: the
+// store is performed where every compute unit of the device sees it, and the
+// load reads from there), through a buffer resource over the workspace. The
+// accesses are compiler-tracked (no inline assembly), so the waits for the
+// loads are the compiler's.
+constexpr int kCoherent = 16;   // cache-policy operand: sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ws_rsrc(const void* base, size_t bytes) {
+  const int n = static_cast<int>(bytes < 0x7fffffffull ? bytes : 0x7fffffffull);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
 }
 
 // Direct global -> LDS copy of 16 bytes per lane: lane i reads base + voff
@@ -357,7 +374,7 @@ __device__ __forceinline__ void hazard_wait(f32x16 (&x)[QT]) {
 // Probabilities of elements 2c, 2c+1 of a 32-key score block (masked to 0
 // where invisible): exp2 of the score (minus the row's reference r on the
 // fallback pass; the fast pass takes r = 0), packed to bf16, and added to the
-// lane's row sum exactly as the PV product will weight them.
+// lane's row sum.
 // (In two halves, so that a pipelined step can put the exponentials behind
 // one MFMA and the rest behind the next.)
 // vis: the row's visibility bits for the tile's keys, shifted down by the
@@ -380,12 +397,14 @@ __device__ __forceinline__ uint64_t tile_visibility(int rel0, uint64_t anc, int 
   const uint64_t v = rel0 >= 0 ? anc >> rel0 : (anc << -rel0) | ((1ull << -rel0) - 1ull);
   return v >> (8 * h);
 }
-// (The row sum adds the two bf16 halves as floats: a dot2 instruction would
-// do it in one, but between matrix instructions it stalls the wavefront.)
+// The row sum adds the fp32 probabilities before their rounding to bf16:
+// two adds per pair (the rounded halves would cost two more instructions
+// to unpack, and the wavefront's issue, not the matrix cores, bounds the
+// pipelined step). The rounding is to nearest, unbiased, so the sum of the
+// rounded weights differs from this one by about 2^-9 / sqrt(keys) of it.
 __device__ __forceinline__ uint32_t prob_pack(RowState& st, f32x2 e) {
-  const uint32_t w = pack_bf16(e[0], e[1]);
-  st.l += bf16_lo(w) + bf16_hi(w);
-  return w;
+  st.l += e[0] + e[1];
+  return pack_bf16(e[0], e[1]);
 }
 template <bool MASKED, bool SHIFT>
 __device__ __forceinline__ uint32_t prob_pair(RowState& st, const f32x16& x, int c, int sub, uint64_t vis) {
@@ -647,6 +666,351 @@ __device__ __forceinline__ void write_rows(const BfParams& p, int b, int g, int 
   }
 }
 
+// ---------------------------------------------------------------------------
+// tree append: cache slot P + i receives node i's key, rotated at
+// P + depth(i) exactly as the attention kernel rotated it in LDS, and its
+// value. Thread it of nthreads (a multiple of 64) for head (b, g) takes key
+// pairs k = it, it + nthreads, ... (node k/64, dims k%64 and 64 + k%64), two
+// at a time with both pairs' loads issued before either is used, so
+// consecutive lanes write consecutive cache addresses; the values go through
+// one block of their own per head. It runs after the attention kernel, which
+// never reads these slots back.
+// ---------------------------------------------------------------------------
+// Element offsets of the (at most two) 64-slot blocks that hold a tree's
+// slots [P, P + n) for KV head (b, g), n <= 64: the dense cache's blocks, or
+// the pages the block table names (clamped into the pools; a sequence with
+// a page outside them is flagged and skipped by the attention kernel).
+struct TreeBlocks {
+  int blk0;
+  size_t off0, off1;
+  __device__ __forceinline__ size_t of(int slot) const { return (slot >> 6) == blk0 ? off0 : off1; }
+};
+__device__ __forceinline__ size_t page_off(const BfParams& p, int b, int g, int blk) {
+  const int32_t e = p.block_table[static_cast<size_t>(b) * p.max_pages + min(blk, p.max_pages - 1)];
+  const int page = min(max(e, 0), p.num_pages - 1);
+  return (static_cast<size_t>(page) * p.Hkv + g) * kKT * kD;
+}
+__device__ __forceinline__ TreeBlocks tree_blocks(const BfParams& p, int b, int g, int P) {
+  TreeBlocks t;
+  t.blk0 = P >> 6;
+  if (p.block_table) {
+    t.off0 = page_off(p, b, g, t.blk0);
+    t.off1 = page_off(p, b, g, t.blk0 + 1);
+  } else {
+    t.off0 = ((static_cast<size_t>(b) * p.Hkv + g) * p.cap + static_cast<size_t>(t.blk0) * kKT) * kD;
+    t.off1 = t.off0 + kKT * kD;
+  }
+  return t;
+}
+
+struct KeyPairs {
+  uint16_t xl[2], xh[2];
+  int dep[2];
+};
+// Loads the two key pairs k0, k0 + nthreads (clamped to the n_max rows of
+// k_new, not to n, so that they need not wait for the node count).
+__device__ __forceinline__ KeyPairs load_keys(const BfParams& p, int b, int g, int k0, int nthreads) {
+  KeyPairs kp;
+  const int j = k0 & 63;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int i = min((k0 + u * nthreads) >> 6, p.n_max - 1);
+    const uint16_t* src = p.k_new + ((static_cast<size_t>(b) * p.n_max + i) * p.Hkv + g) * kD;
+    kp.xl[u] = src[j];
+    kp.xh[u] = src[64 + j];
+    kp.dep[u] = p.depth[static_cast<size_t>(b) * p.n_max + i];
+  }
+  return kp;
+}
+// Rotates and stores the loaded pairs, then loads and stores the thread's
+// further pairs (k0 += 2 nthreads) until n * 64.
+__device__ __forceinline__ void append_keys(const BfParams& p, const SeqState& sq, int b, int g, int it,
+                                            int nthreads, KeyPairs kp) {
+  if (sq.skip) return;
+  const int j = it & 63;   // the same dimension pair for every k of this thread
+  const TreeBlocks tb = tree_blocks(p, b, g, sq.P);
+  const double freq = p.rope ? rope_freq(p.log2_theta, j) : 0.0;
+  for (int k0 = it; k0 < sq.n * 64; k0 += 2 * nthreads) {
+    if (k0 != it) kp = load_keys(p, b, g, k0, nthreads);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int k = k0 + u * nthreads;
+      if (k >= sq.n * 64) break;
+      const int i = k >> 6;
+      const float l = bf16_bits_to_f32(kp.xl[u]), h = bf16_bits_to_f32(kp.xh[u]);
+      const float2 cs = p.rope ? rope_cs(sq.P + clamp_depth(kp.dep[u]), freq) : make_float2(1.0f, 0.0f);
+      const uint32_t w = pack_bf16(rope_lo(l, h, cs) * 1.0f, rope_hi(l, h, cs) * 1.0f);
+      const int slot = sq.P + i;
+      uint16_t* dst = p.k_cache + tb.of(slot) + static_cast<size_t>(slot & 63) * kD;
+      dst[j] = static_cast<uint16_t>(w & 0xFFFFu);
+      dst[64 + j] = static_cast<uint16_t>(w >> 16);
+    }
+  }
+}
+__device__ __forceinline__ void write_tree_values(const BfParams& p, int P, int n, const TreeBlocks& tb,
+                                                  const uint4* vtr, int tid, int nthreads);
+__device__ __forceinline__ void append_values(const BfParams& p, int b, int g, uint4* vtr) {
+  // Values (a block of their own per KV head): node rows are read as whole
+  // 16-byte chunks (all of a thread's loads in flight together, clamped to
+  // the n_max rows of v_new so that they need not wait for the node count:
+  // at most TV_MAX_NODES_DEV * 16 = 4 * 256 chunks) and staged in LDS as
+  // [node][chunk], chunk c of node i at position c ^ (i % 16) (both passes
+  // then touch every bank once per 16 lanes). A thread then takes one chunk
+  // (8 head dims) of one aligned unit of 8 slots touching [P, P + n), gathers
+  // the unit's nodes, and writes the 8 dims' rows of consecutive slots as the
+  // blocked cache holds them: one 16-byte store per dim for a unit inside
+  // [P, P + n), single elements at the ends.
+  static_assert(TV_MAX_NODES_DEV * (kD / 8) == 4 * 256, "four value chunks per thread");
+  // (the loads are issued from assembly and the sequence state is read by
+  // the scalar loader after them, so neither waits for the other)
+  const int tid = threadIdx.x;
+  u32x4 v4[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = min((tid + 256 * u) >> 4, p.n_max - 1), c = tid & 15;
+    v4[u] = ld_b128(p.v_new + ((static_cast<size_t>(b) * p.n_max + i) * p.Hkv + g) * kD + 8 * c);
+  }
+  const SeqState sq = seq_state_scalar(p, b);
+  wait_vm<0>();
+  if (sq.skip) return;
+  const int n = sq.n, P = sq.P;
+  const TreeBlocks tb = tree_blocks(p, b, g, P);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    landed(v4[u]);
+    const int i = (tid >> 4) + 16 * u, c = tid & 15;   // item tid + 256 u
+    vtr[i * 16 + (c ^ (i & 15))] = make_uint4(v4[u][0], v4[u][1], v4[u][2], v4[u][3]);
+  }
+  __syncthreads();
+  write_tree_values(p, P, n, tb, vtr, tid, 256);
+}
+// The write half of the value append: vtr holds the tree's value chunks as
+// [node][chunk] (chunk c of node i at position c ^ (i % 16)); thread it of
+// nthreads takes (chunk, 8-slot unit) pairs and writes the unit's 8 head-dim
+// rows as the blocked cache holds them.
+__device__ __forceinline__ void write_tree_values(const BfParams& p, int P, int n, const TreeBlocks& tb,
+                                                  const uint4* vtr, int tid, int nthreads) {
+  const int u0 = P >> 3, n_units = ((P + n + 7) >> 3) - u0;   // 8-slot units touching [P, P + n)
+  for (int idx = tid; idx < 16 * n_units; idx += nthreads) {
+    const int c = idx & 15, s0 = (u0 + (idx >> 4)) << 3;
+    uint4 src[8];
+    bool in[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = s0 + j - P;
+      in[j] = i >= 0 && i < n;
+      src[j] = in[j] ? vtr[i * 16 + (c ^ (i & 15))] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    const bool full = s0 >= P && s0 + 8 <= P + n;
+#pragma unroll
+    for (int dd = 0; dd < 8; ++dd) {
+      uint16_t* dst = p.v_cache + tb.of(s0) + (8 * c + dd) * kKT + (s0 & 63);   // (8-slot units stay in one block)
+      if (full) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w[e] = static_cast<uint32_t>(u4_elem(src[2 * e], dd)) | (static_cast<uint32_t>(u4_elem(src[2 * e + 1], dd)) << 16);
+        *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (in[j]) dst[j] = u4_elem(src[j], dd);
+      }
+    }
+  }
+}
+
+
+// ---------------------------------------------------------------------------
+// Fused split merge. With a few key splits and a grid that fits the device at
+// once, the splits of a (sequence, KV head, row block) group merge their
+// partials themselves instead of a second kernel:
+//   publish  every split stores its partial with agent-coherent stores and
+//            waits until they are performed;
+//   arrive   one atomic increment of the group's arrival count (word 0);
+//   claim    the row block's items are dealt out in `splits` equal ranges;
+//            a split that has seen every split arrive claims its own range
+//            (atomic OR of its bit into word 1) and merges it if the bit was
+//            still clear. The last split to arrive never waits: after its own
+//            range it claims every range still unclaimed and merges those.
+//            The others wait for the count with a bounded spin (no workgroup
+//            ever waits on another without a time limit, so the scheme cannot
+//            deadlock whatever the dispatch order; one that gives up leaves
+//            its range to the last arrival);
+//   reset    each split increments word 2 as its last access to the words;
+//            the one that completes the count zeroes all three, so the words
+//            are zero between calls (also across graph replays).
+// Agent-coherent (sc1) stores are performed where every compute unit sees
+// them and sc1 loads read from there, so no cache flush or invalidation is
+// needed; the partials may be on another XCD's side.
+// ---------------------------------------------------------------------------
+constexpr uint64_t kSpinTicks = 20000;   // 200 us of the 100 MHz real-time clock
+
+__device__ __forceinline__ uint32_t* group_words(const BfParams& p, int grp) { return p.sync + 4 * static_cast<size_t>(grp); }
+
+// Thread 0 counts this split in; words[0] gets the count it saw (1 .. splits).
+__device__ __forceinline__ void merge_arrive(const BfParams& p, int grp, uint32_t* words) {
+  if (threadIdx.x == 0) {
+    uint32_t* w = group_words(p, grp);
+    words[0] = __hip_atomic_fetch_add(&w[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+  }
+}
+
+// Combines one item (32-row tile wt, head-dim block dt, lane) of S split
+// partials: fp32 weights 2^(r_s - max r) * l_s over the splits that saw a
+// key, fp32 sums, one division; writes the row's 16 values (4 x 8 bytes).
+// Partials of copies ss >= splits have weight 0.
+// Every caller gives the 64 lanes of a wavefront the items of one (tile,
+// head-dim block), lane = item lane, so lane 0 holds the tile's lowest row,
+// which is live whenever any row of the tile is: the 16-bit format of each
+// split's partial (one per tile, the sign bit of the stored row sum, -0.0
+// included) is read from lane 0 and the conversion branches uniformly.
+template <int S>
+__device__ __forceinline__ void merge_item(int splits, const float2 (&ml)[S], const uint4 (&o)[S][2], uint16_t* dst) {
+  float M = -INFINITY;
+#pragma unroll
+  for (int ss = 0; ss < S; ++ss) M = fmaxf(M, ml[ss].x);   // (the copies repeat a split's value)
+  float L = 0.0f;
+  float4 acc[4];
+#pragma unroll
+  for (int i4 = 0; i4 < 4; ++i4) acc[i4] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+  for (int ss = 0; ss < S; ++ss) {
+    // weight of the split's normalised rows: 2^(r_s - max r) times its row sum
+    const float ls = fabsf(ml[ss].y);
+    const bool f16 = (__builtin_amdgcn_readfirstlane(__float_as_uint(ml[ss].y)) >> 31) == 0u;
+    const float w = (ss >= splits || ml[ss].x == -INFINITY) ? 0.0f : exp2f(ml[ss].x - M) * ls;
+    L += w;
+    auto accumulate = [&](auto f16_tag) __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t wd[4] = {o[ss][j].x, o[ss][j].y, o[ss][j].z, o[ss][j].w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const f32x2 v = decltype(f16_tag)::value ? unpack_f16(wd[u]) : f32x2{bf16_lo(wd[u]), bf16_hi(wd[u])};
+          float4& a4 = acc[2 * j + (u >> 1)];   // elements 8j + 2u, 8j + 2u + 1
+          if ((u & 1) == 0) {
+            a4.x = fmaf(w, v[0], a4.x);
+            a4.y = fmaf(w, v[1], a4.y);
+          } else {
+            a4.z = fmaf(w, v[0], a4.z);
+            a4.w = fmaf(w, v[1], a4.w);
+          }
+        }
+      }
+    };
+    if (f16)
+      accumulate(std::true_type{});
+    else
+      accumulate(std::false_type{});
+  }
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+#pragma unroll
+  for (int i4 = 0; i4 < 4; ++i4)
+    *reinterpret_cast<uint2*>(dst + 8 * i4) = make_uint2(pack_bf16(acc[i4].x * inv, acc[i4].y * inv),
+                                                        pack_bf16(acc[i4].z * inv, acc[i4].w * inv));
+}
+
+// Merges range r of the row block's items (item = (wt, dt, lane) in the
+// partials' register order, 256 per 32-row tile), two items per thread with
+// all their coherent loads in flight together. S >= splits.
+template <int WAVES, int QT, int S>
+__device__ __forceinline__ void merge_range(const BfParams& p, int b, int g, int rb, int r, int rows_live,
+                                            __amdgpu_buffer_rsrc_t rml, __amdgpu_buffer_rsrc_t ro) {
+  constexpr int ROWS = WAVES * 32 * QT, NT = WAVES * 64, ITEMS = ROWS / 32 * 256;
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const int per = ITEMS / p.splits, lo = r * per, hi = lo + per;
+  const int rows_all = p.G * p.n_max;
+  const int wg0 = ((b * p.Hkv + g) * p.row_blocks + rb) * p.splits;
+  for (int base = lo; base < hi; base += 2 * NT) {
+    float2 ml[2][S];
+    uint4 o[2][S][2];
+    int it[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      it[k] = base + k * NT + static_cast<int>(threadIdx.x);
+      const int ic = it[k] < hi ? it[k] : lo;   // (loads without branches)
+      const int wt = ic >> 8, dt = (ic >> 6) & 3, lane = ic & 63;
+#pragma unroll
+      for (int ss = 0; ss < S; ++ss) {
+        const int wg = wg0 + min(ss, p.splits - 1);
+        ml[k][ss] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                   rml, (wg * (ROWS * 2) + wt * 64 + lane) * 8, 0, kCoherent));
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          o[k][ss][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      ro, (wg * (ROWS * 16) + (wt * 8 + dt * 2 + j) * 64 + lane) * 16, 0,
+                                                      kCoherent));
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      if (it[k] >= hi) continue;
+      const int wt = it[k] >> 8, dt = (it[k] >> 6) & 3, lane = it[k] & 63;
+      const int row = rb * ROWS + wt * 32 + (lane & 31);
+      if (row >= rows_all) continue;
+      const int head = g * p.G + row % p.G, node = row / p.G;
+      uint16_t* dst = p.out + ((static_cast<size_t>(b) * p.n_max + node) * p.Hq + head) * kD + 32 * dt + 4 * (lane >> 5);
+      if (row >= rows_live) {
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) *reinterpret_cast<uint2*>(dst + 8 * i4) = make_uint2(0u, 0u);
+        continue;
+      }
+      merge_item<S>(p.splits, ml[k], o[k], dst);
+    }
+  }
+}
+
+// Waits (bounded) until every split has arrived, claims and merges this
+// split's range; the last arrival also claims and merges every range still
+// unclaimed. Then counts this split out (and the last one out zeroes the
+// words). words: three LDS words, words[0] = the arrival count this split saw.
+template <int WAVES, int QT>
+__device__ __forceinline__ void merge_claim_and_run(const BfParams& p, int grp, int s, int b, int g, int rb,
+                                                    int rows_live, uint32_t* words, __amdgpu_buffer_rsrc_t rml,
+                                                    __amdgpu_buffer_rsrc_t ro) {
+  constexpr int S = 4;   // the fused merge serves up to four splits
+  const uint32_t splits = static_cast<uint32_t>(p.splits);
+  const uint32_t full = (1u << splits) - 1u, mine = 1u << s;
+  uint32_t* w = group_words(p, grp);
+  const bool last = words[0] == splits;   // (uniform: read after a barrier)
+  if (threadIdx.x == 0) {
+    bool all = last;
+    if (!all) {
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      while (true) {
+        if (__hip_atomic_load(&w[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= splits) {
+          all = true;
+          break;
+        }
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    uint32_t got = 0;
+    if (all) got = mine & ~__hip_atomic_fetch_or(&w[1], mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    words[1] = got;
+  }
+  __syncthreads();
+  if (words[1] != 0u) merge_range<WAVES, QT, S>(p, b, g, rb, s, rows_live, rml, ro);
+  if (last) {
+    __syncthreads();
+    if (threadIdx.x == 0)
+      words[2] = (full & ~mine) & ~__hip_atomic_fetch_or(&w[1], full & ~mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const uint32_t todo = words[2];
+    for (int r = 0; r < static_cast<int>(splits); ++r)
+      if ((todo >> r) & 1u) merge_range<WAVES, QT, S>(p, b, g, rb, r, rows_live, rml, ro);
+  }
+  if (threadIdx.x == 0) {
+    if (__hip_atomic_fetch_add(&w[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u == splits) {
+      __hip_atomic_store(&w[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&w[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&w[2], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 template <int WAVES, int QT, bool PAGED>
 __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   constexpr int NT = WAVES * 64;
@@ -738,10 +1102,11 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   // (every workgroup of b reads err: before or after this store, b is skipped)
 
   // A workgroup with nothing to compute: its loads land before its LDS is
-  // given up; with splits the merge writes the zero rows, else it does.
+  // given up; with separate split merging the merge kernel writes the zero
+  // rows, else (one split, or the fused merge: split 0) it does.
   auto retire = [&](int first_row) __attribute__((always_inline)) {
     wait_vm<0>();
-    if (p.splits == 1) {
+    if (p.splits == 1 || (p.fused && s == 0)) {
       for (int r = first_row + tid / 16; r < min(rb0 + ROWS, rows_all); r += NT / 16) {
         const int i = r / G, head = g * G + r % G;
         uint16_t* orow = p.out + ((static_cast<size_t>(b) * p.n_max + i) * p.Hq + head) * kD;
@@ -1257,11 +1622,12 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   // all below about -60, in log2 units) is redone: a scores-only pass finds
   // every row's exact max, then the pass is repeated with r = max (all
   // p <= 1, the largest = 1; exact for any score range).
+  // (a split without tiles has nothing to redo: its rows stay empty)
   int redo = 0;
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
     const float l = row_sum2(st[t].l);
-    redo |= row_live[t] && !(l <= 0x1p62f && l >= 0x1p-60f);
+    redo |= row_live[t] && n_tiles > 0 && !(l <= 0x1p62f && l >= 0x1p-60f);
   }
   // workgroup-wide OR through the (now idle) ring
   __syncthreads();
@@ -1328,12 +1694,15 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   // pair of (wave, t) for lane l at ((wave * QT + t) * 64 + l). Blocks are
   // ordered (b, g, rb, s).
   const size_t wg_id = ((static_cast<size_t>(b) * p.Hkv + g) * p.row_blocks + rb) * p.splits + s;
+  const __amdgpu_buffer_rsrc_t rml = ws_rsrc(p.part_ml, p.ws_bytes), ro = ws_rsrc(p.part_o, p.ws_bytes);
   uint4* po = p.part_o + wg_id * (ROWS * 16) + wave * (QT * 8 * 64) + lane;
   float2* pm = p.part_ml + wg_id * (ROWS * 2) + wave * (QT * 64) + lane;
-  // (rows past the live ones are never read by the merge). The partials are
-  // stored non-temporally: each is read once, by the merge, and keeping them
-  // out of the way in L2 shortens the whole call by about 3% on the
-  // 8-sequence, 4096-token workload.
+  // (rows past the live ones are never read by the merge). For the merge
+  // kernel the partials are stored non-temporally: each is read once, by the
+  // merge, and keeping them out of the way in L2 shortens the whole call by
+  // about 3% on the 8-sequence, 4096-token workload. For the fused merge they
+  // are stored agent-coherently: another compute unit, possibly on another
+  // XCD, reads them while this kernel runs.
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
     if (!row_live[t]) continue;
@@ -1359,160 +1728,58 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
             w[u] = decltype(f16_tag)::value ? pack_f16(x0, x1) : pack_bf16(x0, x1);
           }
           const u32x4 x = {w[0], w[1], w[2], w[3]};
-          __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(po + (t * 8 + dt * 2 + j) * 64));
+          uint4* dst = po + (t * 8 + dt * 2 + j) * 64;
+          if (p.fused)
+            __builtin_amdgcn_raw_buffer_store_b128(x, ro, static_cast<int>((dst - p.part_o) * 16), 0, kCoherent);
+          else
+            __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(dst));
         }
     };
     if (use_f16)
       store16(std::true_type{});
     else
       store16(std::false_type{});
-    const f32x2 m = {st[t].r, use_f16 ? l_row[t] : -l_row[t]};
-    __builtin_nontemporal_store(m, reinterpret_cast<f32x2*>(pm + t * 64));
-  }
-}
-
-// ---------------------------------------------------------------------------
-// tree append: cache slot P + i receives node i's key, rotated at
-// P + depth(i) exactly as the attention kernel rotated it in LDS, and its
-// value. Thread it of nthreads (a multiple of 64) for head (b, g) takes key
-// pairs k = it, it + nthreads, ... (node k/64, dims k%64 and 64 + k%64), two
-// at a time with both pairs' loads issued before either is used, so
-// consecutive lanes write consecutive cache addresses; the values go through
-// one block of their own per head. It runs after the attention kernel, which
-// never reads these slots back.
-// ---------------------------------------------------------------------------
-// Element offsets of the (at most two) 64-slot blocks that hold a tree's
-// slots [P, P + n) for KV head (b, g), n <= 64: the dense cache's blocks, or
-// the pages the block table names (clamped into the pools; a sequence with
-// a page outside them is flagged and skipped by the attention kernel).
-struct TreeBlocks {
-  int blk0;
-  size_t off0, off1;
-  __device__ __forceinline__ size_t of(int slot) const { return (slot >> 6) == blk0 ? off0 : off1; }
-};
-__device__ __forceinline__ size_t page_off(const BfParams& p, int b, int g, int blk) {
-  const int32_t e = p.block_table[static_cast<size_t>(b) * p.max_pages + min(blk, p.max_pages - 1)];
-  const int page = min(max(e, 0), p.num_pages - 1);
-  return (static_cast<size_t>(page) * p.Hkv + g) * kKT * kD;
-}
-__device__ __forceinline__ TreeBlocks tree_blocks(const BfParams& p, int b, int g, int P) {
-  TreeBlocks t;
-  t.blk0 = P >> 6;
-  if (p.block_table) {
-    t.off0 = page_off(p, b, g, t.blk0);
-    t.off1 = page_off(p, b, g, t.blk0 + 1);
-  } else {
-    t.off0 = ((static_cast<size_t>(b) * p.Hkv + g) * p.cap + static_cast<size_t>(t.blk0) * kKT) * kD;
-    t.off1 = t.off0 + kKT * kD;
-  }
-  return t;
-}
-
-struct KeyPairs {
-  uint16_t xl[2], xh[2];
-  int dep[2];
-};
-// Loads the two key pairs k0, k0 + nthreads (clamped to the n_max rows of
-// k_new, not to n, so that they need not wait for the node count).
-__device__ __forceinline__ KeyPairs load_keys(const BfParams& p, int b, int g, int k0, int nthreads) {
-  KeyPairs kp;
-  const int j = k0 & 63;
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int i = min((k0 + u * nthreads) >> 6, p.n_max - 1);
-    const uint16_t* src = p.k_new + ((static_cast<size_t>(b) * p.n_max + i) * p.Hkv + g) * kD;
-    kp.xl[u] = src[j];
-    kp.xh[u] = src[64 + j];
-    kp.dep[u] = p.depth[static_cast<size_t>(b) * p.n_max + i];
-  }
-  return kp;
-}
-// Rotates and stores the loaded pairs, then loads and stores the thread's
-// further pairs (k0 += 2 nthreads) until n * 64.
-__device__ __forceinline__ void append_keys(const BfParams& p, const SeqState& sq, int b, int g, int it,
-                                            int nthreads, KeyPairs kp) {
-  if (sq.skip) return;
-  const int j = it & 63;   // the same dimension pair for every k of this thread
-  const TreeBlocks tb = tree_blocks(p, b, g, sq.P);
-  const double freq = p.rope ? rope_freq(p.log2_theta, j) : 0.0;
-  for (int k0 = it; k0 < sq.n * 64; k0 += 2 * nthreads) {
-    if (k0 != it) kp = load_keys(p, b, g, k0, nthreads);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int k = k0 + u * nthreads;
-      if (k >= sq.n * 64) break;
-      const int i = k >> 6;
-      const float l = bf16_bits_to_f32(kp.xl[u]), h = bf16_bits_to_f32(kp.xh[u]);
-      const float2 cs = p.rope ? rope_cs(sq.P + clamp_depth(kp.dep[u]), freq) : make_float2(1.0f, 0.0f);
-      const uint32_t w = pack_bf16(rope_lo(l, h, cs) * 1.0f, rope_hi(l, h, cs) * 1.0f);
-      const int slot = sq.P + i;
-      uint16_t* dst = p.k_cache + tb.of(slot) + static_cast<size_t>(slot & 63) * kD;
-      dst[j] = static_cast<uint16_t>(w & 0xFFFFu);
-      dst[64 + j] = static_cast<uint16_t>(w >> 16);
+    // A row that saw no key in this split (an empty split, or one whose
+    // keys are all invisible to it) has row sum 0 and stores the reference
+    // -inf, so that the merge leaves it out of the largest reference.
+    const f32x2 m = {l_row[t] > 0.0f ? st[t].r : -INFINITY, use_f16 ? l_row[t] : -l_row[t]};
+    if (p.fused) {
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, m), rml,
+                                            static_cast<int>((pm + t * 64 - p.part_ml) * 8), 0, kCoherent);
+    } else {
+      __builtin_nontemporal_store(m, reinterpret_cast<f32x2*>(pm + t * 64));
     }
   }
-}
-__device__ __forceinline__ void append_values(const BfParams& p, int b, int g, uint4* vtr) {
-  // Values (a block of their own per KV head): node rows are read as whole
-  // 16-byte chunks (all of a thread's loads in flight together, clamped to
-  // the n_max rows of v_new so that they need not wait for the node count:
-  // at most TV_MAX_NODES_DEV * 16 = 4 * 256 chunks) and staged in LDS as
-  // [node][chunk], chunk c of node i at position c ^ (i % 16) (both passes
-  // then touch every bank once per 16 lanes). A thread then takes one chunk
-  // (8 head dims) of one aligned unit of 8 slots touching [P, P + n), gathers
-  // the unit's nodes, and writes the 8 dims' rows of consecutive slots as the
-  // blocked cache holds them: one 16-byte store per dim for a unit inside
-  // [P, P + n), single elements at the ends.
-  static_assert(TV_MAX_NODES_DEV * (kD / 8) == 4 * 256, "four value chunks per thread");
-  // (the loads are issued from assembly and the sequence state is read by
-  // the scalar loader after them, so neither waits for the other)
-  const int tid = threadIdx.x;
-  u32x4 v4[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int i = min((tid + 256 * u) >> 4, p.n_max - 1), c = tid & 15;
-    v4[u] = ld_b128(p.v_new + ((static_cast<size_t>(b) * p.n_max + i) * p.Hkv + g) * kD + 8 * c);
-  }
-  const SeqState sq = seq_state_scalar(p, b);
-  wait_vm<0>();
-  if (sq.skip) return;
-  const int n = sq.n, P = sq.P;
-  const TreeBlocks tb = tree_blocks(p, b, g, P);
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    landed(v4[u]);
-    const int i = (tid >> 4) + 16 * u, c = tid & 15;   // item tid + 256 u
-    vtr[i * 16 + (c ^ (i & 15))] = make_uint4(v4[u][0], v4[u][1], v4[u][2], v4[u][3]);
-  }
+  if (!p.fused) return;   // the merge kernel follows
+
+  // ---- fused merge (merge_in_kernel): publish, arrive, claim, merge; the
+  // workgroup holding the tree appends it to the cache meanwhile
+  wait_vm<0>();          // this wavefront's partials are performed
   __syncthreads();
-  const int u0 = P >> 3, n_units = ((P + n + 7) >> 3) - u0;   // 8-slot units touching [P, P + n)
-  for (int idx = tid; idx < 16 * n_units; idx += 256) {
-    const int c = idx & 15, s0 = (u0 + (idx >> 4)) << 3;
-    uint4 src[8];
-    bool in[8];
+  uint32_t* const words = reinterpret_cast<uint32_t*>(smem);   // (the ring is idle now)
+  const int grp = (b * p.Hkv + g) * p.row_blocks + rb;
+  merge_arrive(p, grp, words);
+  if (n_masked > 0 && !sq.skip) {
+    // rotated tree keys straight from the lane items; values through the
+    // [node][chunk] transpose in stage 3 (as the merge kernel's append)
+    const TreeBlocks tb = tree_blocks(p, b, g, P);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int i = s0 + j - P;
-      in[j] = i >= 0 && i < n;
-      src[j] = in[j] ? vtr[i * 16 + (c ^ (i & 15))] : make_uint4(0u, 0u, 0u, 0u);
-    }
-    const bool full = s0 >= P && s0 + 8 <= P + n;
-#pragma unroll
-    for (int dd = 0; dd < 8; ++dd) {
-      uint16_t* dst = p.v_cache + tb.of(s0) + (8 * c + dd) * kKT + (s0 & 63);   // (8-slot units stay in one block)
-      if (full) {
-        uint32_t w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          w[e] = static_cast<uint32_t>(u4_elem(src[2 * e], dd)) | (static_cast<uint32_t>(u4_elem(src[2 * e + 1], dd)) << 16);
-        *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (in[j]) dst[j] = u4_elem(src[j], dd);
+    for (int u = 0; u < KI; ++u) {
+      const int item = tid + NT * u, node = item >> 3, c = item & 7;
+      if (node < n) {
+        const int slot = P + node;
+        uint16_t* dst = p.k_cache + tb.of(slot) + static_cast<size_t>(slot & 63) * kD + 8 * c;
+        *reinterpret_cast<u32x4*>(dst) = tk_lo[u];
+        *reinterpret_cast<u32x4*>(dst + 64) = tk_hi[u];
       }
     }
+    stage_tree_values();
+    __syncthreads();
+    write_tree_values(p, P, n, tb, vtr, tid, NT);
   }
+  __syncthreads();
+  merge_claim_and_run<WAVES, QT>(p, grp, s, b, g, rb, rows_live, words, rml, ro);
 }
 
 // With one split there is no merge: the append runs alone, grid
@@ -1586,47 +1853,13 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(BfParams p) {
     for (int i4 = 0; i4 < 4; ++i4) *reinterpret_cast<uint2*>(dst + 8 * i4) = make_uint2(0u, 0u);
     return;
   }
-  float M = -INFINITY;
-#pragma unroll
-  for (int ss = 0; ss < S; ++ss) M = fmaxf(M, ml[ss].x);   // (the copies repeat a split's value)
-  float L = 0.0f;
-  float4 acc[4];
-#pragma unroll
-  for (int i4 = 0; i4 < 4; ++i4) acc[i4] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-#pragma unroll
-  for (int ss = 0; ss < S; ++ss) {
-    // weight of the split's normalised rows: 2^(r_s - max r) times its row sum
-    const float ls = fabsf(ml[ss].y);
-    const bool f16 = !(ml[ss].y < 0.0f);
-    const float w = (ss >= p.splits || ml[ss].x == -INFINITY) ? 0.0f : exp2f(ml[ss].x - M) * ls;
-    L += w;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint32_t wd[4] = {o[ss][j].x, o[ss][j].y, o[ss][j].z, o[ss][j].w};
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const f32x2 v = f16 ? unpack_f16(wd[u]) : f32x2{bf16_lo(wd[u]), bf16_hi(wd[u])};
-        float4& a4 = acc[2 * j + (u >> 1)];   // elements 8j + 2u, 8j + 2u + 1
-        if ((u & 1) == 0) {
-          a4.x = fmaf(w, v[0], a4.x);
-          a4.y = fmaf(w, v[1], a4.y);
-        } else {
-          a4.z = fmaf(w, v[0], a4.z);
-          a4.w = fmaf(w, v[1], a4.w);
-        }
-      }
-    }
-  }
-  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-#pragma unroll
-  for (int i4 = 0; i4 < 4; ++i4)
-    *reinterpret_cast<uint2*>(dst + 8 * i4) = make_uint2(pack_bf16(acc[i4].x * inv, acc[i4].y * inv),
-                                                        pack_bf16(acc[i4].z * inv, acc[i4].w * inv));
+  merge_item<S>(p.splits, ml, o, dst);
 }
 
 // Optional launch-shape override for tuning sweeps, read once:
-// TV_ATTN_TUNE="waves=4,qt=2,splits=4" (any subset; 0 = automatic).
-struct Tune { int waves = 0, qt = 0, splits = 0; };
+// TV_ATTN_TUNE="waves=4,qt=2,splits=4,fused=0" (any subset; 0 = automatic,
+// except fused: 0 = the merge kernel, 1 = automatic).
+struct Tune { int waves = 0, qt = 0, splits = 0, fused = 1; };
 const Tune& tune() {
   static const Tune t = [] {
     Tune r;
@@ -1634,6 +1867,7 @@ const Tune& tune() {
       if (const char* w = strstr(e, "waves=")) sscanf(w, "waves=%d", &r.waves);
       if (const char* q = strstr(e, "qt=")) sscanf(q, "qt=%d", &r.qt);
       if (const char* s = strstr(e, "splits=")) sscanf(s, "splits=%d", &r.splits);
+      if (const char* f = strstr(e, "fused=")) sscanf(f, "fused=%d", &r.fused);
     }
     return r;
   }();
@@ -1643,19 +1877,40 @@ const Tune& tune() {
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// Workspace layout: part_ml | part_o, only with several splits.
+// Workspace layout, only with several splits: sync | part_ml | part_o. sync
+// holds four 32-bit words per (sequence, KV head, row block) for the fused
+// merge, zero between calls. It is one fixed-size region at the start of
+// every workspace with splits, whatever the shapes, so that a call with
+// other shapes (whose partials start right after it) never writes over the
+// words of a later call sharing the workspace.
+constexpr size_t kSyncBytes = 16384;
+constexpr long kMaxFusedGroups = kSyncBytes / (4 * sizeof(uint32_t));
 struct WsLayout {
-  size_t part_ml, part_o, total;
+  size_t sync, part_ml, part_o, total;
 };
 WsLayout ws_layout(const tv_attn_args* a, const AttnPlan& pl) {
-  WsLayout w{0, 0, 0};
+  WsLayout w{0, 0, 0, 0};
   if (pl.splits == 1) return w;
   const size_t heads = static_cast<size_t>(a->B) * a->Hkv;
   const size_t wg_rows = static_cast<size_t>(pl.waves) * 32 * pl.qt;
   const size_t wgs = heads * pl.row_blocks * pl.splits;
-  w.part_o = align_up(wgs * wg_rows * 2 * sizeof(float2));
+  w.part_ml = kSyncBytes;
+  w.part_o = w.part_ml + align_up(wgs * wg_rows * 2 * sizeof(float2));
   w.total = w.part_o + wgs * wg_rows * 16 * sizeof(uint4);
   return w;
+}
+
+// Compute units of the current device, queried once per device.
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
 }
 
 }  // namespace
@@ -1686,12 +1941,17 @@ AttnPlan plan_attention_bf16(const tv_attn_args* a) {
   // A grid that already needs more than one round of workgroups is split
   // once, so that the last round's tail is shorter when the prefixes are
   // ragged (64 sequences of 512 to 4096 tokens: 170.8 to 166.7 us).
+  const long cus = device_cus();
   int splits = 1;
-  while (units * splits < 256 && splits < kMaxSplits && (max_tiles / (splits * 2)) >= 4) splits *= 2;
-  if (units > 256 && units <= 512 && max_tiles / 2 >= 4) splits = 2;
+  while (units * splits < cus && splits < kMaxSplits && (max_tiles / (splits * 2)) >= 4) splits *= 2;
+  if (units > cus && units <= 2 * cus && max_tiles / 2 >= 4) splits = 2;
   if (tn.splits > 0) splits = std::min(std::min(tn.splits, kMaxSplits), std::max(1, max_tiles));
   pl.splits = splits;
   pl.rows_pad = pl.row_blocks * wg_rows;
+  // The splits merge in the kernel (no second launch, partials read while
+  // still near) when there are at most four and the whole grid runs at once
+  // (one workgroup per compute unit); otherwise the merge kernel follows.
+  pl.fused = splits > 1 && splits <= 4 && units * splits <= cus && units <= kMaxFusedGroups && tn.fused != 0;
   pl.workspace_bytes = ws_layout(a, pl).total;
   return pl;
 }
@@ -1728,6 +1988,9 @@ hipError_t launch_attention_bf16(const tv_attn_args* a, const AttnPlan& pl, cons
   char* ws = static_cast<char*>(a->workspace);
   p.part_ml = pl.splits > 1 ? reinterpret_cast<float2*>(ws + w.part_ml) : nullptr;
   p.part_o = pl.splits > 1 ? reinterpret_cast<uint4*>(ws + w.part_o) : nullptr;
+  p.sync = pl.splits > 1 ? reinterpret_cast<uint32_t*>(ws + w.sync) : nullptr;
+  p.fused = pl.fused ? 1 : 0;
+  p.ws_bytes = pl.workspace_bytes;
 
   dim3 grid(pl.splits * pl.row_blocks * a->Hkv * a->B);
   const int wg_rows = pl.waves * 32 * pl.qt;
@@ -1747,6 +2010,7 @@ hipError_t launch_attention_bf16(const tv_attn_args* a, const AttnPlan& pl, cons
     hipLaunchKernelGGL(append_bf16_kernel, dim3(kAppendBlocks + 1, a->Hkv, a->B), dim3(256), 0, s, p);
     return hipGetLastError();
   }
+  if (pl.fused) return hipSuccess;   // the main kernel merged and appended
   const int sk = pl.splits <= 2 ? 2 : pl.splits <= 4 ? 4 : pl.splits <= 8 ? 8 : 16;
   static_assert(kMaxSplits == 16, "merge instances cover up to sixteen splits");
   switch (key * 100 + sk) {

@@ -54,6 +54,7 @@ struct AttnPlan {
   int row_blocks;  // workgroups along the (node, head-in-group) rows
   int splits;      // workgroups along the prefix keys
   int rows_pad;    // row_blocks * waves * 32
+  bool fused;      // the splits merge inside the main kernel (no merge kernel)
   size_t workspace_bytes;
 };
 

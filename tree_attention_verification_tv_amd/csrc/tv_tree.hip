@@ -152,9 +152,11 @@ __global__ __launch_bounds__(64) void accept_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// commit: slot P+d <- slot P+path[d] for d = 0..L. path is strictly increasing
-// with path[d] >= d, so a source slot may be another lane's destination; all
-// sources of one KV head are staged in LDS before any slot is written.
+// commit: slot P+d <- slot P+path[d] for d = 0..L. A path from accept is
+// strictly increasing with path[d] >= d, so a source slot may be another
+// lane's destination; all sources of one KV head are staged in LDS before any
+// slot is written, which makes any path with entries in [0, n_max) a plain
+// simultaneous copy.
 // K is [cap][D] per head; V is blocked [cap/64][D][64] per head. With a
 // paged cache (bt non-null) the 64-slot block j of sequence b is page
 // bt[b * max_pages + j] of pools [num_pages][Hkv][64][D] (K) and
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(256) void commit_kernel(
   __shared__ T k_stage[kStage];
   __shared__ T v_stage[kStage];
   __shared__ int s_path[TV_MAX_NODES_DEV];
-  __shared__ int s_L, s_P, s_ok;
+  __shared__ int s_L, s_P, s_ok, s_top;
   __shared__ int s_page[2];
 
   const int b = blockIdx.y;
@@ -193,19 +195,22 @@ __global__ __launch_bounds__(256) void commit_kernel(
     s_L = L;
     s_P = P;
     s_ok = ok;
+    s_top = L;
   }
   __syncthreads();
   const int L = s_L, P = s_P;
   if (tid <= L && tid < n_max && s_ok) {
     s_path[tid] = src_in;
-    // every source must lie in [P, cap)
-    if (src_in < 0 || P + src_in >= cap) atomicAnd(&s_ok, 0);
+    // every source must be a tree node, 0 <= path[d] < n_max (so all moved
+    // slots lie in [P, P + 64): the two blocks from P >> 6), inside the cache
+    if (src_in < 0 || src_in >= n_max || P + src_in >= cap) atomicAnd(&s_ok, 0);
+    atomicMax(&s_top, src_in);
   }
   __syncthreads();
   if (bt && tid == 0 && s_ok) {
-    // the pages the move touches (the largest slot is P + path[L]) must be
-    // pages of the pools, else the sequence is left unchanged
-    const int blocks = ((P + s_path[L]) >> 6) - (P >> 6) + 1;
+    // the pages the move touches (slots P .. P + max(L, largest path entry))
+    // must be pages of the pools, else the sequence is left unchanged
+    const int blocks = ((P + s_top) >> 6) - (P >> 6) + 1;
     for (int u = 0; u < 2; ++u) {
       const int e = s_page[u];
       if (u < blocks && (e < 0 || e >= num_pages)) s_ok = 0;
