@@ -60,8 +60,10 @@ typedef enum tv_status {
   TV_ERR_CAPACITY = 3,      /* per-sequence only: prefix + tree > cache     */
   TV_ERR_UNSUPPORTED = 4,   /* valid but not implemented (e.g. head dim)    */
   TV_ERR_HIP = 5,           /* a HIP launch or runtime call failed          */
-  TV_ERR_BAD_PAGE = 6       /* per-sequence only: a block-table entry names
+  TV_ERR_BAD_PAGE = 6,      /* per-sequence only: a block-table entry names
                                a page outside the pools                     */
+  TV_ERR_SCRATCH = 7        /* tv_tree_attention_noalloc only: the shapes
+                               need more scratch than its static buffer     */
 } tv_status;
 
 typedef enum tv_dtype { TV_F32 = 0, TV_BF16 = 1 } tv_dtype;
@@ -193,6 +195,25 @@ size_t tv_tree_attention_workspace_size(const tv_attn_args* a);
  * B == 0 is a no-op.
  */
 tv_status tv_tree_attention(const tv_attn_args* a, hipStream_t stream);
+
+/*
+ * tv_tree_attention_noalloc -- tv_tree_attention for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. Same arguments, computation, outputs and
+ * host checks as tv_tree_attention, except that a->workspace and
+ * a->workspace_bytes are ignored: the workspace is a static device buffer of
+ * the library (48 MiB per device, zero when the library's module loads,
+ * held until the process ends; its address is looked up once per device on
+ * the first call with that device current). The call allocates nothing.
+ * Shapes whose workspace (tv_tree_attention_workspace_size) exceeds 48 MiB
+ * return TV_ERR_SCRATCH before any device work; the workloads of this
+ * library need at most about 35 MB. All calls on one device share that
+ * device's buffer, which keeps the last call's contents: calls that may
+ * overlap on one device (other streams, other host threads) race and must
+ * not be issued. Kernels and launch plan are those of tv_tree_attention, so
+ * the results are the same bit for bit.
+ */
+tv_status tv_tree_attention_noalloc(const tv_attn_args* a, hipStream_t stream);
 
 /*
  * Paged KV cache ([INFRA-5.3] section 8 names the block table of a paged KV

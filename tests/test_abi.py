@@ -39,8 +39,9 @@ def test_every_declared_symbol_is_exported_and_bound():
 def test_status_strings_and_version():
     lib = _lib.load()
     assert lib.tv_version().decode().startswith("tv ")
-    for code in range(7):
+    for code in range(8):
         assert lib.tv_status_string(code)
+    assert lib.tv_status_string(_lib.TV_ERR_SCRATCH).decode().startswith("shapes need more scratch")
     assert lib.tv_status_string(_lib.TV_ERR_BAD_PAGE).decode().startswith("block table")
     assert lib.tv_status_string(_lib.TV_ERR_CAPACITY).decode().startswith("prefix")
 
@@ -193,3 +194,33 @@ def test_speculative_sample_host_validation():
     assert call(p=null) == _lib.TV_ERR_INVALID_ARG
     assert call(wsb=ws - 1) == _lib.TV_ERR_INVALID_ARG
     assert call(B=0, p=null) == _lib.TV_OK
+
+
+def test_noalloc_host_validation_without_device():
+    """The allocation-free attention entry point checks like tv_tree_attention
+    and refuses, before any device call, shapes whose workspace exceeds its
+    static scratch."""
+    lib = _lib.load()
+    fake = ctypes.c_void_p(0x1000)
+
+    def args(**kw):
+        a = _lib.TvAttnArgs()
+        for name in ("q", "k_new", "v_new", "k_cache", "v_cache", "prefix_len", "n_nodes", "anc", "depth",
+                     "err", "out"):
+            setattr(a, name, fake.value)
+        a.B, a.n_max, a.Hq, a.Hkv, a.D, a.cap, a.dtype = 8, 60, 32, 8, 128, 4160, _lib.TV_BF16
+        a.rope_theta, a.softmax_scale = 10000.0, 0.0
+        for k, v in kw.items():
+            setattr(a, k, v)
+        return a
+
+    assert lib.tv_tree_attention_noalloc(None, None) == _lib.TV_ERR_INVALID_ARG
+    assert lib.tv_tree_attention_noalloc(ctypes.byref(args(n_max=0)), None) == _lib.TV_ERR_INVALID_ARG
+    assert lib.tv_tree_attention_noalloc(ctypes.byref(args(Hq=30)), None) == _lib.TV_ERR_INVALID_ARG
+    assert lib.tv_tree_attention_noalloc(ctypes.byref(args(cap=4100)), None) == _lib.TV_ERR_INVALID_ARG
+    assert lib.tv_tree_attention_noalloc(ctypes.byref(args(q=None)), None) == _lib.TV_ERR_INVALID_ARG
+    assert lib.tv_tree_attention_noalloc(ctypes.byref(args(B=0, q=None)), None) == _lib.TV_OK
+    # 32 sequences x 8 KV heads x two row blocks, two key splits: about 68 MiB
+    big = args(B=32, n_max=64, Hq=64, cap=4096)
+    assert lib.tv_tree_attention_workspace_size(ctypes.byref(big)) > 48 << 20
+    assert lib.tv_tree_attention_noalloc(ctypes.byref(big), None) == _lib.TV_ERR_SCRATCH

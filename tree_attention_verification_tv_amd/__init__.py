@@ -26,7 +26,7 @@ from . import _lib
 from ._lib import (PAGE, TV_BF16, TV_ERR_BAD_PAGE, TV_ERR_BAD_TREE, TV_ERR_CAPACITY, TV_F32,  # noqa: F401
                    TV_MAX_NODES, TvAttnArgs, TvError, TvPagedKv)
 
-__all__ = ["build_tree", "tree_attention", "tree_attention_workspace_size", "new_workspace", "accept",
+__all__ = ["build_tree", "tree_attention", "tree_attention_noalloc", "tree_attention_workspace_size", "new_workspace", "accept",
            "accept_typical", "commit", "eagle2_tree", "speculative_sample", "tree_attention_paged", "commit_paged", "pages_from_dense",
            "dense_from_pages", "TV_ERR_BAD_PAGE", "PAGE",
            "version", "TvError", "TV_ERR_BAD_TREE", "TV_ERR_CAPACITY", "attn_args",
@@ -230,6 +230,18 @@ def tree_attention(q, k_new, v_new, k_cache, v_cache, prefix_len, n_nodes, anc, 
         workspace = _default_workspace(q.device, need, stream)
         a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
     _lib.check("tv_tree_attention", lib.tv_tree_attention(ctypes.byref(a), _stream(stream)))
+    return out
+
+
+def tree_attention_noalloc(q, k_new, v_new, k_cache, v_cache, prefix_len, n_nodes, anc, depth, err, out,
+                           rope_theta=10000.0, softmax_scale=0.0, stream=None):
+    """tree_attention through the allocation-free entry point: the library's
+    static per-device scratch replaces the workspace, and out must be given
+    (nothing is allocated). Calls on one device must not overlap."""
+    lib = _lib.load()
+    a = attn_args(q, k_new, v_new, k_cache, v_cache, prefix_len, n_nodes, anc, depth, err, out,
+                  rope_theta, softmax_scale)
+    _lib.check("tv_tree_attention_noalloc", lib.tv_tree_attention_noalloc(ctypes.byref(a), _stream(stream)))
     return out
 
 

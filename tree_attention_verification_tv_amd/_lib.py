@@ -13,6 +13,7 @@ TV_ERR_CAPACITY = 3
 TV_ERR_UNSUPPORTED = 4
 TV_ERR_HIP = 5
 TV_ERR_BAD_PAGE = 6
+TV_ERR_SCRATCH = 7
 
 TV_F32 = 0
 TV_BF16 = 1
@@ -47,6 +48,7 @@ SIGNATURES = {
     "tv_build_tree": (_I, [_P, _P, _I, _I, _P, _P, _P, _P]),
     "tv_tree_attention_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(TvAttnArgs)]),
     "tv_tree_attention": (_I, [ctypes.POINTER(TvAttnArgs), _P]),
+    "tv_tree_attention_noalloc": (_I, [ctypes.POINTER(TvAttnArgs), _P]),
     "tv_tree_attention_paged": (_I, [ctypes.POINTER(TvAttnArgs), ctypes.POINTER(TvPagedKv), _P]),
     "tv_accept": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P]),
     "tv_eagle2_tree": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]),

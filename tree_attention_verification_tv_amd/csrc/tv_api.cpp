@@ -38,6 +38,7 @@ const char* tv_status_string(tv_status s) {
     case TV_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case TV_ERR_HIP: return "HIP runtime or launch error";
     case TV_ERR_BAD_PAGE: return "block table names a page outside the pools";
+    case TV_ERR_SCRATCH: return "shapes need more scratch than the allocation-free entry point holds";
   }
   return "unknown status";
 }
@@ -70,6 +71,26 @@ tv_status tv_tree_attention(const tv_attn_args* a, hipStream_t stream) {
   if (plan.workspace_bytes > 0 && (a->workspace == nullptr || a->workspace_bytes < plan.workspace_bytes))
     return TV_ERR_INVALID_ARG;
   return from_hip(tv::launch_attention_bf16(a, plan, nullptr, stream));
+}
+
+tv_status tv_tree_attention_noalloc(const tv_attn_args* a, hipStream_t stream) {
+  const tv_status st = check_attn_shapes(a);
+  if (st != TV_OK) return st;
+  if (a->B == 0) return TV_OK;
+  if (!a->q || !a->k_new || !a->v_new || !a->k_cache || !a->v_cache || !a->prefix_len ||
+      !a->n_nodes || !a->anc || !a->depth || !a->err || !a->out)
+    return TV_ERR_INVALID_ARG;
+  if (a->dtype == TV_F32) return from_hip(tv::launch_attention_f32(a, stream));   // (no workspace)
+  const tv::AttnPlan plan = tv::plan_attention_bf16(a);
+  if (plan.workspace_bytes > tv::kScratchBytes) return TV_ERR_SCRATCH;
+  tv_attn_args b = *a;
+  b.workspace = nullptr;
+  b.workspace_bytes = 0;
+  if (plan.workspace_bytes > 0) {
+    if (tv::scratch_workspace(&b.workspace) != hipSuccess) return TV_ERR_HIP;
+    b.workspace_bytes = tv::kScratchBytes;
+  }
+  return from_hip(tv::launch_attention_bf16(&b, plan, nullptr, stream));
 }
 
 tv_status tv_tree_attention_paged(const tv_attn_args* a, const tv_paged_kv* pk, hipStream_t stream) {

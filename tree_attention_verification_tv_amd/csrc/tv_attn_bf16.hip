@@ -79,6 +79,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "tv_device.h"
@@ -1954,6 +1955,37 @@ AttnPlan plan_attention_bf16(const tv_attn_args* a) {
   pl.fused = splits > 1 && splits <= 4 && units * splits <= cus && units <= kMaxFusedGroups && tn.fused != 0;
   pl.workspace_bytes = ws_layout(a, pl).total;
   return pl;
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free entry point: the bf16 attention's workspace
+// (split partials and the fused merge's synchronisation words) as one
+// file-scope device array. Each device the library runs on holds its own
+// copy, zero when the module loads (so the synchronisation words start at
+// zero; every call leaves them zero), from first use until the process ends.
+// Host code never passes the array's name to a kernel (on the host it only
+// stands for the symbol); the device address comes from hipGetSymbolAddress
+// once per device, with that device current, and is kept per device.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+hipError_t scratch_workspace(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {nullptr};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_attention_bf16(const tv_attn_args* a, const AttnPlan& pl, const tv_paged_kv* pk,

@@ -65,4 +65,10 @@ hipError_t launch_attention_bf16(const tv_attn_args* a, const AttnPlan& plan, co
                                  hipStream_t s);
 hipError_t launch_attention_f32(const tv_attn_args* a, hipStream_t s);
 
+// Bytes of the static device scratch behind tv_tree_attention_noalloc (every
+// workload of this library needs at most about 35 MB), and its device address
+// on the current device (looked up once per device).
+constexpr size_t kScratchBytes = size_t(48) << 20;
+hipError_t scratch_workspace(void** ptr);
+
 }  // namespace tv
