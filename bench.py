@@ -1,8 +1,9 @@
 """Throughput of one draft-tree verification step on one MI355X.
 
 A step is the whole verification path for one attention layer over one batch:
-tv_build_tree -> tv_tree_attention -> tv_accept -> tv_commit, all through the
-C ABI. The headline workload is the Llama-3-8B-shaped GQA batch (32 q / 8 kv
+tv_build_tree -> tv_tree_attention -> tv_accept_commit (greedy accept and the
+in-place KV commit in one launch; the paged step calls tv_accept and
+tv_commit_paged), all through the C ABI. The headline workload is the Llama-3-8B-shaped GQA batch (32 q / 8 kv
 heads, head dim 128, batch 8, prefix 4096, 60-node EAGLE-2-style trees, bf16).
 
 Inputs are generated once on the host, copied to HBM, and replicated into
@@ -589,7 +590,10 @@ def main() -> None:
         else:
             cm = (P(s["k_cache"]), P(s["v_cache"]), B, w.Hkv, w.cap, w.D, a.dtype, P(plen), P(acc_len),
                   P(path), n_max, P(plen_out), sp)
-        calls.append((a, cm))
+        acm = (P(tok), P(tgt), P(parents), P(anc), P(depth), P(n_nodes), P(err), B, n_max, P(acc_len), P(path),
+               P(bonus), P(toks), P(s["k_cache"]), P(s["v_cache"]), w.Hkv, w.cap, w.D, a.dtype, P(plen), P(plen_out),
+               sp)
+        calls.append((a, cm, acm))
     commit_fn = lib.tv_commit_paged if paged else lib.tv_commit
     bt = (P(parents), P(n_nodes), B, n_max, P(anc), P(depth), P(err), sp)
     ac = (P(tok), P(tgt), P(parents), P(anc), P(depth), P(n_nodes), P(err), B, n_max, P(acc_len),
@@ -601,11 +605,15 @@ def main() -> None:
                                                ctypes.byref(sets[k % copies]["pk"]), sp)
         return lib.tv_tree_attention(ctypes.byref(calls[k % copies][0]), sp)
 
+    def accept_commit(k: int) -> int:
+        if paged:
+            return lib.tv_accept(*ac) | commit_fn(*calls[k % copies][1])
+        return lib.tv_accept_commit(*calls[k % copies][2])
+
     def step(k: int) -> None:
         st = lib.tv_build_tree(*bt)
         st |= attention(k)
-        st |= lib.tv_accept(*ac)
-        st |= commit_fn(*calls[k % copies][1])
+        st |= accept_commit(k)
         if st:
             raise RuntimeError(f"library call failed with status {st}")
 
@@ -636,7 +644,7 @@ def main() -> None:
         events[k][0].record(stream)
         st |= attention(k)
         events[k][1].record(stream)
-        st |= lib.tv_accept(*ac) | commit_fn(*calls[k % copies][1])
+        st |= accept_commit(k)
         if st:
             raise RuntimeError(f"library call failed with status {st}")
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -678,8 +686,9 @@ def main() -> None:
                    "seed": args.config if args.seed is None else args.seed},
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": traffic,
-                     "kernel": "tv_tree_attention call: attn_bf16_kernel + merge_bf16_kernel (split merge "
-                               "and tree append); HIP events on its stream around each call, in the step",
+                     "kernel": "tv_tree_attention call: attn_bf16_kernel (key splits merged and tree appended "
+                               "inside the kernel on the automatic plan; merge_bf16_kernel otherwise); HIP events "
+                               "on its stream around each call, in the step",
                      "algorithmic_bytes_per_launch": ab["total"],
                      "algorithmic_flops_per_launch": flops,
                      "hbm_frac": ab["total"] / attn_mean_s / 1e9 / HBM_PEAK_GBS,

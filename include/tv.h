@@ -400,6 +400,29 @@ tv_status tv_commit(void* k_cache, void* v_cache, int32_t B, int32_t Hkv, int32_
                     int32_t* prefix_len_out, hipStream_t stream);
 
 /*
+ * tv_accept_commit -- tv_accept followed by tv_commit, in one launch.
+ *
+ * The greedy selection of tv_accept ([MEDUSA-EAGLE] "Typical acceptance",
+ * [MEDUSA-EXPL] step 7) and the in-place commit of the accepted path's KV of
+ * tv_commit ([INFRA-5.3] section 3.2 and summary) for the dense cache, with
+ * the arguments of both: the accept outputs are the same, and for each
+ * sequence with accept_len = L >= 0 slot P + d <- slot P + path[d] (d = 0..L,
+ * every KV head, K and V, all sources read before any slot is written),
+ * prefix_len_out[b] = P + L + 1. Sequences tv_accept skips (accept_len -1),
+ * or whose path would move a slot outside [P, cap), keep their cache and
+ * prefix length. prefix_len_out may be the same array as prefix_len_in
+ * (then one workgroup per sequence walks every KV head; otherwise one per
+ * KV head and sequence). Host checks as tv_accept and tv_commit.
+ * B == 0 is a no-op.
+ */
+tv_status tv_accept_commit(const int32_t* cand_tok, const int32_t* tgt_argmax, const int32_t* parents,
+                           const uint64_t* anc, const int32_t* depth, const int32_t* n_nodes,
+                           const int32_t* err, int32_t B, int32_t n_max, int32_t* accept_len, int32_t* path,
+                           int32_t* bonus_tok, int32_t* out_tokens, void* k_cache, void* v_cache, int32_t Hkv,
+                           int32_t cap, int32_t D, int32_t dtype, const int32_t* prefix_len_in,
+                           int32_t* prefix_len_out, hipStream_t stream);
+
+/*
  * tv_commit_paged -- tv_commit over a paged cache (see tv_tree_attention_paged
  * for the layout): slot P + d <- slot P + path[b][d], d = 0..L, through the
  * block table. A move touching a page outside the pools leaves that sequence

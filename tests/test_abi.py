@@ -224,3 +224,24 @@ def test_noalloc_host_validation_without_device():
     big = args(B=32, n_max=64, Hq=64, cap=4096)
     assert lib.tv_tree_attention_workspace_size(ctypes.byref(big)) > 48 << 20
     assert lib.tv_tree_attention_noalloc(ctypes.byref(big), None) == _lib.TV_ERR_SCRATCH
+
+
+def test_accept_commit_host_validation_without_device():
+    lib = _lib.load()
+    fake = ctypes.c_void_p(0x1000)
+    null = None
+
+    def call(B=1, n_max=5, Hkv=8, cap=128, D=128, dtype=_lib.TV_BF16, k=fake, plen_out=fake):
+        return lib.tv_accept_commit(fake, fake, fake, fake, fake, fake, null, B, n_max, fake, fake, fake, null, k,
+                                    fake, Hkv, cap, D, dtype, fake, plen_out, null)
+    assert call(B=-1) == _lib.TV_ERR_INVALID_ARG
+    assert call(n_max=0) == _lib.TV_ERR_INVALID_ARG
+    assert call(n_max=65) == _lib.TV_ERR_INVALID_ARG
+    assert call(Hkv=0) == _lib.TV_ERR_INVALID_ARG
+    assert call(cap=100) == _lib.TV_ERR_INVALID_ARG
+    assert call(cap=4) == _lib.TV_ERR_INVALID_ARG
+    assert call(dtype=7) == _lib.TV_ERR_INVALID_ARG
+    assert call(D=96) == _lib.TV_ERR_UNSUPPORTED
+    assert call(k=None) == _lib.TV_ERR_INVALID_ARG
+    assert call(plen_out=None) == _lib.TV_ERR_INVALID_ARG
+    assert call(B=0, k=None) == _lib.TV_OK

@@ -26,7 +26,7 @@ from . import _lib
 from ._lib import (PAGE, TV_BF16, TV_ERR_BAD_PAGE, TV_ERR_BAD_TREE, TV_ERR_CAPACITY, TV_F32,  # noqa: F401
                    TV_MAX_NODES, TvAttnArgs, TvError, TvPagedKv)
 
-__all__ = ["build_tree", "tree_attention", "tree_attention_noalloc", "tree_attention_workspace_size", "new_workspace", "accept",
+__all__ = ["build_tree", "tree_attention", "tree_attention_noalloc", "accept_commit", "tree_attention_workspace_size", "new_workspace", "accept",
            "accept_typical", "commit", "eagle2_tree", "speculative_sample", "tree_attention_paged", "commit_paged", "pages_from_dense",
            "dense_from_pages", "TV_ERR_BAD_PAGE", "PAGE",
            "version", "TvError", "TV_ERR_BAD_TREE", "TV_ERR_CAPACITY", "attn_args",
@@ -443,3 +443,37 @@ def commit(k_cache, v_cache, prefix_len_in, accept_len, path, prefix_len_out=Non
                                           _DTYPES[k_cache.dtype], _ptr(prefix_len_in), _ptr(accept_len),
                                           _ptr(path), n_max, _ptr(prefix_len_out), _stream(stream)))
     return prefix_len_out
+
+
+def accept_commit(cand_tok, tgt_argmax, parents, anc, depth, n_nodes, err, k_cache, v_cache, prefix_len_in,
+                  prefix_len_out=None, want_tokens=True, stream=None):
+    """accept followed by commit in one launch (dense cache): returns
+    (accept_len, path, bonus, out_tokens or None, prefix_len_out)."""
+    lib = _lib.load()
+    for name, t in (("cand_tok", cand_tok), ("tgt_argmax", tgt_argmax), ("parents", parents),
+                    ("depth", depth), ("n_nodes", n_nodes), ("prefix_len_in", prefix_len_in)):
+        _dev(t, name, torch.int32)
+    _dev(anc, "anc", torch.int64)
+    if err is not None:
+        _dev(err, "err", torch.int32)
+    if k_cache.dtype not in _DTYPES:
+        raise ValueError("cache must be float32 or bfloat16")
+    _dev(k_cache, "k_cache", k_cache.dtype)
+    _dev(v_cache, "v_cache", k_cache.dtype)
+    B, n_max = parents.shape
+    Bc, Hkv, cap, D = k_cache.shape
+    if Bc != B or tuple(v_cache.shape) != (B, Hkv, cap // V_BLOCK, D, V_BLOCK):
+        raise ValueError("k_cache must be [B, Hkv, cap, D] and v_cache [B, Hkv, cap/64, D, 64]")
+    dev = parents.device
+    accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    path = torch.empty((B, n_max), dtype=torch.int32, device=dev)
+    bonus = torch.empty(B, dtype=torch.int32, device=dev)
+    out_tokens = torch.empty((B, n_max), dtype=torch.int32, device=dev) if want_tokens else None
+    if prefix_len_out is None:
+        prefix_len_out = torch.empty_like(prefix_len_in)
+    _dev(prefix_len_out, "prefix_len_out", torch.int32)
+    _lib.check("tv_accept_commit", lib.tv_accept_commit(
+        _ptr(cand_tok), _ptr(tgt_argmax), _ptr(parents), _ptr(anc), _ptr(depth), _ptr(n_nodes), _ptr(err), B, n_max,
+        _ptr(accept_len), _ptr(path), _ptr(bonus), _ptr(out_tokens), _ptr(k_cache), _ptr(v_cache), Hkv, cap, D,
+        _DTYPES[k_cache.dtype], _ptr(prefix_len_in), _ptr(prefix_len_out), _stream(stream)))
+    return accept_len, path, bonus, out_tokens, prefix_len_out

@@ -57,6 +57,8 @@ SIGNATURES = {
     "tv_accept_typical": (_I, [_P, _I, _I, _P, _P, _P, _P, _P, _P, _I, _I, ctypes.c_float,
                                ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P]),
     "tv_commit": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _I, _P, _P]),
+    "tv_accept_commit": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P,
+                              _P]),
     "tv_commit_paged": (_I, [_P, _P, ctypes.POINTER(TvPagedKv), _I, _I, _I, _I, _P, _P, _P, _I, _P, _P]),
 }
 

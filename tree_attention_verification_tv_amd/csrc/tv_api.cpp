@@ -122,6 +122,25 @@ tv_status tv_accept(const int32_t* cand_tok, const int32_t* tgt_argmax, const in
                                     n_max, accept_len, path, bonus_tok, out_tokens, stream));
 }
 
+tv_status tv_accept_commit(const int32_t* cand_tok, const int32_t* tgt_argmax, const int32_t* parents,
+                           const uint64_t* anc, const int32_t* depth, const int32_t* n_nodes,
+                           const int32_t* err, int32_t B, int32_t n_max, int32_t* accept_len, int32_t* path,
+                           int32_t* bonus_tok, int32_t* out_tokens, void* k_cache, void* v_cache, int32_t Hkv,
+                           int32_t cap, int32_t D, int32_t dtype, const int32_t* prefix_len_in,
+                           int32_t* prefix_len_out, hipStream_t stream) {
+  if (B < 0 || n_max < 1 || n_max > TV_MAX_NODES || Hkv < 1 || cap < n_max || cap % 64 != 0)
+    return TV_ERR_INVALID_ARG;
+  if (!dtype_ok(dtype)) return TV_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return TV_ERR_UNSUPPORTED;
+  if (B == 0) return TV_OK;
+  if (!cand_tok || !tgt_argmax || !parents || !anc || !depth || !n_nodes || !accept_len || !path ||
+      !bonus_tok || !k_cache || !v_cache || !prefix_len_in || !prefix_len_out)
+    return TV_ERR_INVALID_ARG;
+  return from_hip(tv::launch_accept_commit(cand_tok, tgt_argmax, parents, anc, depth, n_nodes, err, B, n_max,
+                                           accept_len, path, bonus_tok, out_tokens, k_cache, v_cache, Hkv, cap, D,
+                                           elem_bytes(dtype), prefix_len_in, prefix_len_out, stream));
+}
+
 tv_status tv_eagle2_tree(const float* conf, const int32_t* cand, const int32_t* root_tok, int32_t B,
                          int32_t S, int32_t K, int32_t M, int32_t n_max, int32_t* parents,
                          int32_t* tokens, float* values, int32_t* n_nodes, hipStream_t stream) {

@@ -879,7 +879,8 @@ __device__ __forceinline__ void merge_item(int splits, const float2 (&ml)[S], co
   for (int ss = 0; ss < S; ++ss) {
     // weight of the split's normalised rows: 2^(r_s - max r) times its row sum
     const float ls = fabsf(ml[ss].y);
-    const bool f16 = (__builtin_amdgcn_readfirstlane(__float_as_uint(ml[ss].y)) >> 31) == 0u;
+    const uint32_t y0 = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(__float_as_uint(ml[ss].y)));
+    const bool f16 = (y0 >> 31) == 0u;
     const float w = (ss >= splits || ml[ss].x == -INFINITY) ? 0.0f : exp2f(ml[ss].x - M) * ls;
     L += w;
     auto accumulate = [&](auto f16_tag) __attribute__((always_inline)) {

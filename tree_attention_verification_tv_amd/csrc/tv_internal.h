@@ -40,6 +40,13 @@ hipError_t launch_typical_stats(const void* logits, int elem_bytes, int V, const
                                 int B, int n_max, float* entropy, float* p_tok, int32_t* argmax,
                                 hipStream_t s);
 
+hipError_t launch_accept_commit(const int32_t* cand_tok, const int32_t* tgt, const int32_t* parents,
+                                const uint64_t* anc, const int32_t* depth, const int32_t* n_nodes,
+                                const int32_t* err, int B, int n_max, int32_t* accept_len, int32_t* path,
+                                int32_t* bonus, int32_t* out_tokens, void* k_cache, void* v_cache, int Hkv,
+                                int cap, int D, int elem_bytes, const int32_t* prefix_len_in,
+                                int32_t* prefix_len_out, hipStream_t s);
+
 // pk: paged cache (nullptr: the dense layout)
 hipError_t launch_commit(void* k_cache, void* v_cache, int B, int Hkv, int cap, int D,
                          int elem_bytes, const int32_t* prefix_len_in, const int32_t* accept_len,

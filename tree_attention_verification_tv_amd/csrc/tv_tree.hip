@@ -69,16 +69,19 @@ __global__ __launch_bounds__(64) void build_tree_kernel(const int32_t* __restric
 // bit in ascending order, is the path. The bonus token is tgt at that node
 // (the target's argmax there, for both rules).
 // ---------------------------------------------------------------------------
+// Accept of sequence b by one wavefront (lane i = node i); writes the
+// outputs and returns the accepted length (-1: skipped) in every lane, and in
+// `on_pos` the path position of node i (-1 if i is not on the path).
 template <bool TYPICAL>
-__global__ __launch_bounds__(64) void accept_kernel(
+__device__ __forceinline__ int accept_sequence(
     const int32_t* __restrict__ cand_tok, const int32_t* __restrict__ tgt,
     const int32_t* __restrict__ parents, const uint64_t* __restrict__ anc,
     const int32_t* __restrict__ depth, const int32_t* __restrict__ n_nodes,
     const int32_t* __restrict__ err, int n_max, int32_t* __restrict__ accept_len,
     int32_t* __restrict__ path, int32_t* __restrict__ bonus, int32_t* __restrict__ out_tokens,
-    const float* __restrict__ p_tok, const float* __restrict__ entropy, float eps, float delta) {
-  const int b = blockIdx.x;
-  const int i = threadIdx.x;
+    const float* __restrict__ p_tok, const float* __restrict__ entropy, float eps, float delta, int b, int i,
+    int& on_pos, bool write = true) {
+  on_pos = -1;
   const size_t row = static_cast<size_t>(b) * n_max;
   // every load goes out at once (node data does not wait for the count)
   const bool in_row = i < n_max;
@@ -120,21 +123,26 @@ __global__ __launch_bounds__(64) void accept_kernel(
   if (key < 0) active = false;   // no accepted root: tree unusable
 
   if (!active) {
-    if (i < n_max) {
+    if (write && i < n_max) {
       path[row + i] = -1;
       if (out_tokens) out_tokens[row + i] = -1;
     }
-    if (i == 0) {
+    if (write && i == 0) {
       accept_len[b] = -1;
       bonus[b] = -1;
     }
-    return;
+    return -1;
   }
   const int e = 255 - (key & 255);
   const int L = key >> 8;
   const uint64_t ae = shfl_u64(a, e);
   const int bonus_tok = __shfl(tg, e);
   if (i < n_max) {
+    const bool on = (ae >> i) & 1ull;
+    const int pos = __popcll(ae & ((1ull << i) - 1ull));
+    if (on) on_pos = pos;
+  }
+  if (write && i < n_max) {
     const bool on = (ae >> i) & 1ull;
     const int pos = __popcll(ae & ((1ull << i) - 1ull));
     if (on) path[row + pos] = i;
@@ -145,10 +153,24 @@ __global__ __launch_bounds__(64) void accept_kernel(
       if (i > L) out_tokens[row + i] = -1;
     }
   }
-  if (i == 0) {
+  if (write && i == 0) {
     accept_len[b] = L;
     bonus[b] = bonus_tok;
   }
+  return L;
+}
+
+template <bool TYPICAL>
+__global__ __launch_bounds__(64) void accept_kernel(
+    const int32_t* __restrict__ cand_tok, const int32_t* __restrict__ tgt,
+    const int32_t* __restrict__ parents, const uint64_t* __restrict__ anc,
+    const int32_t* __restrict__ depth, const int32_t* __restrict__ n_nodes,
+    const int32_t* __restrict__ err, int n_max, int32_t* __restrict__ accept_len,
+    int32_t* __restrict__ path, int32_t* __restrict__ bonus, int32_t* __restrict__ out_tokens,
+    const float* __restrict__ p_tok, const float* __restrict__ entropy, float eps, float delta) {
+  int on_pos;
+  accept_sequence<TYPICAL>(cand_tok, tgt, parents, anc, depth, n_nodes, err, n_max, accept_len, path, bonus,
+                           out_tokens, p_tok, entropy, eps, delta, blockIdx.x, threadIdx.x, on_pos);
 }
 
 // ---------------------------------------------------------------------------
@@ -257,6 +279,132 @@ __global__ __launch_bounds__(256) void commit_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// accept + commit in one launch: grid (Hkv / heads_per_block, B), 256
+// threads. Wave 0 of every workgroup of sequence b runs the accept of
+// accept_kernel (a few hundred bytes of loads, repeated per KV head rather
+// than waited for across a launch); the workgroup of heads 0.. writes its
+// outputs. The length and path stay in LDS, and the workgroup moves the
+// path's K and V of its KV heads (slot P + d <- slot P + path[d]) in batches
+// whose sources fit the LDS stage: all of a batch's sources are read before
+// any slot is written. When prefix_len_out is prefix_len_in, one workgroup
+// per sequence walks every head (heads_per_block = Hkv), so no workgroup
+// reads a length another has replaced. A skipped sequence (accept length
+// -1) or a move outside [P, cap) leaves the cache and the prefix length
+// unchanged.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void accept_commit_kernel(
+    const int32_t* __restrict__ cand_tok, const int32_t* __restrict__ tgt,
+    const int32_t* __restrict__ parents, const uint64_t* __restrict__ anc,
+    const int32_t* __restrict__ depth, const int32_t* __restrict__ n_nodes,
+    const int32_t* __restrict__ err, int n_max, int32_t* __restrict__ accept_len,
+    int32_t* __restrict__ path, int32_t* __restrict__ bonus, int32_t* __restrict__ out_tokens,
+    T* __restrict__ k_cache, T* __restrict__ v_cache, int Hkv, int cap, int D,
+    const int32_t* prefix_len_in, int32_t* prefix_len_out, int heads_per_block) {
+  // the tree's slots [P, P + n) of one KV head: K rows [slot][D], V [D][slot]
+  constexpr int kRows = TV_MAX_NODES_DEV, kMaxD = 128;
+  constexpr int EPC = 16 / static_cast<int>(sizeof(T));   // elements per 16-byte chunk
+  // V rows: head dim c, slots from P rounded down to a 16-byte chunk
+  constexpr int kVSlots = kRows + EPC;
+  __shared__ uint4 k_rows[kRows * kMaxD / EPC];
+  __shared__ __attribute__((aligned(16))) T v_rows[kMaxD * kVSlots];
+  __shared__ int s_path[TV_MAX_NODES_DEV];
+  __shared__ int s_L;
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int g_first = blockIdx.x * heads_per_block, g_last = min(Hkv, g_first + heads_per_block);
+  const int P = prefix_len_in[b];
+  const int n_in = n_nodes[b];
+  // tree rows that lie in the cache (any move from outside it is refused)
+  const int nr = (P >= 0 && n_in > 0 && n_in <= n_max) ? max(0, min(n_in, cap - P)) : 0;
+  const int kpr = D / EPC;   // 16-byte chunks per K row
+  // element offset of the 64-slot block holding `slot` (head g)
+  auto base = [&](int g, int slot) {
+    return ((static_cast<size_t>(b) * Hkv + g) * cap + static_cast<size_t>(slot >> 6) * 64) * D;
+  };
+  // The tree rows of head g are loaded into registers, every load of a
+  // thread in flight together (fully unrolled, constant indices), then
+  // written to LDS: K as 16-byte chunks of its rows, V as 16-byte chunks of
+  // its head-dim rows (the tree's slots of one head dim are contiguous inside
+  // a 64-slot block, and chunks never straddle blocks).
+  // per thread: enough chunks for 64 rows of D = 128
+  constexpr int KU = kRows * kMaxD / EPC / 256, VU = (kMaxD * (kRows / EPC + 1) + 255) / 256;
+  static_assert(KU * 256 * EPC == kRows * kMaxD, "one round covers the tree's K rows");
+  const int v0 = P & ~(EPC - 1);                                       // first slot of the first V chunk
+  const int vchunks = nr > 0 ? ((P + nr - 1 - v0) / EPC + 1) : 0;     // V chunks per head-dim row
+  const int ktotal = nr * kpr, vtotal = vchunks * D;
+  uint4 kv[KU], vv[VU];
+  auto load_rows = [&](int g) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      const int idx = min(tid + u * 256, max(ktotal - 1, 0)), r = idx / kpr, c = idx % kpr;
+      const int slot = P + r;
+      kv[u] = ktotal > 0 ? *reinterpret_cast<const uint4*>(k_cache + base(g, slot) +
+                                                           static_cast<size_t>(slot & 63) * D + EPC * c)
+                         : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < VU; ++u) {
+      // consecutive lanes walk the chunks of one head-dim row
+      const int idx = min(tid + u * 256, max(vtotal - 1, 0)), c = idx / max(vchunks, 1), k = idx % max(vchunks, 1);
+      const int slot = v0 + EPC * k;
+      vv[u] = vtotal > 0 ? *reinterpret_cast<const uint4*>(v_cache + base(g, slot) + static_cast<size_t>(c) * 64 +
+                                                           (slot & 63))
+                         : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  auto put_rows = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < KU; ++u)
+      if (tid + u * 256 < ktotal) k_rows[tid + u * 256] = kv[u];
+#pragma unroll
+    for (int u = 0; u < VU; ++u) {
+      const int idx = tid + u * 256;
+      if (idx < vtotal)
+        *reinterpret_cast<uint4*>(&v_rows[(idx / vchunks) * kVSlots + EPC * (idx % vchunks)]) = vv[u];
+    }
+  };
+  // the first head's rows go out together with the accept's loads
+  load_rows(g_first);
+  if (tid < 64) {
+    int on_pos;
+    const int L = accept_sequence<false>(cand_tok, tgt, parents, anc, depth, n_nodes, err, n_max, accept_len, path,
+                                         bonus, out_tokens, nullptr, nullptr, 0.f, 0.f, b, tid, on_pos,
+                                         blockIdx.x == 0);
+    if (on_pos >= 0) s_path[on_pos] = tid;
+    if (tid == 0) s_L = L;
+  }
+  put_rows();
+  __syncthreads();
+  // the path ascends, so its end node path[L] is the largest moved slot
+  const int L = (s_L >= 0 && P >= 0 && s_path[max(s_L, 0)] < nr) ? s_L : -1;
+  if (blockIdx.x == 0 && tid == 0) prefix_len_out[b] = L >= 0 ? P + L + 1 : P;
+  if (L < 0) return;
+  for (int g = g_first; g < g_last; ++g) {
+    if (g != g_first) {
+      __syncthreads();   // (the previous head's rows are written)
+      load_rows(g);
+      put_rows();
+      __syncthreads();
+    }
+    // slot P + d <- tree row path[d], d = 0 .. L (rows on their own slot stay)
+    for (int idx = tid; idx < (L + 1) * kpr; idx += 256) {
+      const int d = idx / kpr, c = idx % kpr, src = s_path[d];
+      if (src == d) continue;
+      const int dst = P + d;
+      *reinterpret_cast<uint4*>(k_cache + base(g, dst) + static_cast<size_t>(dst & 63) * D + EPC * c) =
+          k_rows[src * kpr + c];
+    }
+    for (int idx = tid; idx < (L + 1) * D; idx += 256) {
+      const int c = idx / (L + 1), d = idx % (L + 1), src = s_path[d];
+      if (src == d) continue;
+      const int dst = P + d;
+      v_cache[base(g, dst) + static_cast<size_t>(c) * 64 + (dst & 63)] = v_rows[c * kVSlots + (P + src - v0)];
+    }
+  }
+}
+
 // ------------------------------------------------------------------ launches
 
 hipError_t launch_build_tree(const int32_t* parents, const int32_t* n_nodes, int B, int n_max,
@@ -285,6 +433,28 @@ hipError_t launch_accept_typical(const int32_t* cand_tok, const int32_t* tgt_arg
   hipLaunchKernelGGL(accept_kernel<true>, dim3(B), dim3(64), 0, s, cand_tok, tgt_argmax, parents,
                      anc, depth, n_nodes, err, n_max, accept_len, path, bonus, out_tokens, p_tok,
                      entropy, eps, delta);
+  return hipGetLastError();
+}
+
+hipError_t launch_accept_commit(const int32_t* cand_tok, const int32_t* tgt, const int32_t* parents,
+                                const uint64_t* anc, const int32_t* depth, const int32_t* n_nodes,
+                                const int32_t* err, int B, int n_max, int32_t* accept_len, int32_t* path,
+                                int32_t* bonus, int32_t* out_tokens, void* k_cache, void* v_cache, int Hkv,
+                                int cap, int D, int elem_bytes, const int32_t* prefix_len_in,
+                                int32_t* prefix_len_out, hipStream_t s) {
+  // one workgroup per (KV head, sequence), or per sequence when the new
+  // prefix lengths overwrite the old ones
+  const int hpb = (prefix_len_in == prefix_len_out) ? Hkv : 1;
+  const dim3 grid(Hkv / hpb, B);
+  if (elem_bytes == 2) {
+    hipLaunchKernelGGL(accept_commit_kernel<uint16_t>, grid, dim3(256), 0, s, cand_tok, tgt, parents, anc, depth,
+                       n_nodes, err, n_max, accept_len, path, bonus, out_tokens, static_cast<uint16_t*>(k_cache),
+                       static_cast<uint16_t*>(v_cache), Hkv, cap, D, prefix_len_in, prefix_len_out, hpb);
+  } else {
+    hipLaunchKernelGGL(accept_commit_kernel<uint32_t>, grid, dim3(256), 0, s, cand_tok, tgt, parents, anc, depth,
+                       n_nodes, err, n_max, accept_len, path, bonus, out_tokens, static_cast<uint32_t*>(k_cache),
+                       static_cast<uint32_t*>(v_cache), Hkv, cap, D, prefix_len_in, prefix_len_out, hpb);
+  }
   return hipGetLastError();
 }
 
