@@ -164,3 +164,30 @@ def test_paged_is_deterministic():
     torch.cuda.synchronize()
     for o in outs[1:]:
         assert torch.equal(o, outs[0])
+
+
+def test_paged_ragged_trees_against_oracle_and_dense():
+    """Per-request tree boundaries with a paged cache (infra-guide "5.3"
+    section 8 names both): trees of 60, 17, 1 and 0 nodes and a tree that is
+    not parents-first, in one batch over shuffled pages; paged equals dense
+    bit for bit, and every row of the live sequences matches the oracle."""
+    print("[gpu] paged ragged trees", flush=True)
+    w = generate(3, B=5, prefix=1100)
+    w.n_nodes[:] = [60, 17, 1, 0, 60]
+    for b in range(w.B):
+        w.parents[b, w.n_nodes[b]:] = -1
+    w.parents[4, 5] = 7                       # a parent after its child
+    rng = np.random.default_rng(11)
+    bt, n_pages = shuffled_table(w, rng)
+    res = run_both(w, bt, n_pages)
+    check_equal_to_dense(res, bt)
+    assert res["err_p"].cpu().tolist() == [0, 0, 0, 0, tv.TV_ERR_BAD_TREE]
+    assert res["acc_p"].cpu().tolist()[3:] == [-1, -1]
+    inp = w.oracle_inputs()
+    ref_anc, ref_depth, ref_err = oracle.build_tree(w.parents, w.n_nodes)
+    out, kc, vc, e = oracle.tree_attention(inp["q"], inp["k_new"], inp["v_new"], inp["k_cache"], inp["v_cache"],
+                                           inp["prefix_len"], inp["n_nodes"], inp["parents"], w.rope_theta, 0.0,
+                                           err_in=ref_err)
+    got = host_f64(res["out_p"])
+    assert attention_error(w.dtype, got, out) <= tolerance(w.dtype)
+    assert not got[3].any() and not got[4].any()

@@ -396,3 +396,18 @@ def test_uniformly_low_scores_with_empty_splits():
     check_commit(w, res, d["k_cache"], d["v_cache"])
     assert np.isfinite(res["out"]).all() and np.abs(res["out"]).max() > 0.0
     print(f"  attention error {worst:.3g}", flush=True)
+
+
+@pytest.mark.parametrize("over", [dict(D=128, B=3, prefix=200), dict(D=128, Hq=8, Hkv=2, B=2, prefix=90)],
+                         ids=["mha", "gqa"])
+def test_fp32_head_dim_128(over):
+    """The fp32 path at head dim 128 (the tiny workload's own head dim is 64),
+    with and without grouped query heads: every row within the fp32 bound."""
+    print(f"[gpu] fp32 head dim 128 {over}", flush=True)
+    w = generate(1, **over)
+    assert w.dtype == "f32" and w.D == 128
+    d = upload(w, DEV)
+    res = run_step(w, d)
+    worst = check_step(w, res)
+    check_commit(w, res, d["k_cache"], d["v_cache"])
+    print(f"  attention error {worst:.3g}", flush=True)

@@ -92,3 +92,22 @@ def test_u_zero_keeps_what_the_target_allows():
     draft = rng.integers(0, V, L)
     acc, toks, _, _ = oracle.speculative_sample(pl, ql, draft, np.zeros(L), 0.5)
     assert acc == L
+
+
+def test_softmax64_equals_scipy_softmax():
+    """oracle.softmax64 against scipy.special.softmax (a library routine):
+    flat, peaked, very large and very negative logits, a single entry, and
+    ties; also sums to one and is invariant to a shift."""
+    from scipy.special import softmax
+    rng = np.random.default_rng(5)
+    rows = [rng.normal(size=32000), 30.0 * rng.normal(size=1001), rng.normal(size=7) + 1e4,
+            rng.normal(size=9) - 1e4, np.array([3.5]), np.zeros(5), np.array([2.0, 2.0, -1.0, 2.0])]
+    for x in rows:
+        got = oracle.softmax64(x)
+        ref = softmax(np.asarray(x, dtype=np.float64))
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-300)
+        assert abs(got.sum() - 1.0) < 1e-12
+        assert np.allclose(oracle.softmax64(x + 123.25), got, rtol=1e-12, atol=1e-300)
+    # a plausible mistake (no max shift, or a missing normalisation) fails
+    x = rows[2]
+    assert not np.all(np.isfinite(np.exp(x)))
