@@ -78,6 +78,87 @@ __device__ __forceinline__ RowStat combine(RowStat a, RowStat b) {
   return r;
 }
 
+// Wave-wide reductions without LDS: DPP moves within each row of 16 lanes
+// (swap neighbours, swap pairs, mirror each half-row, mirror the row) leave
+// every lane of a row holding the row's result, and the four rows' lanes 0,
+// 16, 32 and 48 are then read into scalars and combined; every lane gets the
+// wave's result.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ float wave_max_f(float v) {
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f<kDppMirror>(v));
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
+}
+__device__ __forceinline__ float wave_sum_f(float v) {
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  v += dpp_f<kDppMirror>(v);
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+}
+__device__ __forceinline__ int wave_min_i(int v) {
+  v = min(v, dpp_i<kDppXor1>(v));
+  v = min(v, dpp_i<kDppXor2>(v));
+  v = min(v, dpp_i<kDppHalfMirror>(v));
+  v = min(v, dpp_i<kDppMirror>(v));
+  return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
+// The workgroup's statistics from each wavefront's own: every thread rescales
+// its sums to the wave's largest reference, the wave adds them and keeps the
+// lowest index holding its maximum; lane 0 of each wave posts that to s_part,
+// and after the barrier the caller folds the kWaves partials with
+// fold_parts. (Thread statistics carry ref, and the maximum separately: the
+// reference may trail the maximum.)
+__device__ __forceinline__ void post_wave_stat(const RowStat& st, int tid, RowStat* s_part) {
+  const float wref = wave_max_f(st.ref);
+  const float wmx = wave_max_f(st.mx);
+  float z = 0.f, s = 0.f;
+  rescaled(st, wref, z, s);
+  z = wave_sum_f(z);
+  s = wave_sum_f(s);
+  const int widx = wave_min_i(st.mx == wmx ? st.idx : INT_MAX);
+  if ((tid & (kWave - 1)) == 0) s_part[tid / kWave] = RowStat{wmx, widx, wref, z, s};
+}
+
+// The kWaves partials folded at once: the largest reference and maximum
+// first, then every partial's sums moved to that reference (independent
+// steps), and the lowest index among the partials holding the maximum.
+__device__ __forceinline__ RowStat fold_parts(const RowStat* s_part) {
+  RowStat part[kWaves];
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) part[w] = s_part[w];
+  RowStat r{part[0].mx, INT_MAX, part[0].ref, 0.f, 0.f};
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) {
+    r.mx = fmaxf(r.mx, part[w].mx);
+    r.ref = fmaxf(r.ref, part[w].ref);
+  }
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    rescaled(part[w], r.ref, r.z, r.s);
+    r.idx = part[w].mx == r.mx ? min(r.idx, part[w].idx) : r.idx;
+  }
+  return r;
+}
+
 // A chunk is 16 bytes (8 bf16 or 4 fp32) on the vector path, one element
 // otherwise.
 template <typename T, int E>
@@ -235,26 +316,10 @@ __global__ __launch_bounds__(kThreads) void typical_stats_kernel(
       if (chunk_elem<T, E>(vmax, j) == st.mx) st.idx = cmax_at * E + j;
   }
 
-  // wave, then workgroup
-#pragma unroll
-  for (int off = kWave / 2; off >= 1; off >>= 1) {
-    RowStat o;
-    o.mx = __shfl_xor(st.mx, off);
-    o.idx = __shfl_xor(st.idx, off);
-    o.ref = __shfl_xor(st.ref, off);
-    o.z = __shfl_xor(st.z, off);
-    o.s = __shfl_xor(st.s, off);
-    st = combine(st, o);
-  }
-  if ((tid & (kWave - 1)) == 0) s_part[tid / kWave] = st;
+  post_wave_stat(st, tid, s_part);
   __syncthreads();
   if (tid >= kWave) return;
-  RowStat part[kWaves];
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) part[w] = s_part[w];
-  RowStat r = part[0];
-#pragma unroll
-  for (int w = 1; w < kWaves; ++w) r = combine(r, part[w]);
+  const RowStat r = fold_parts(s_part);
 
   if (child) p_tok[seq + tid] = tok_in ? exp2f(fmaf(x_tok, kLog2e, -r.ref)) / r.z : 0.f;
   if (tid == 0) {
@@ -303,21 +368,9 @@ __device__ __forceinline__ void row_ref_z(const T* row, int V, int tid, RowStat*
       }
     }
   }
-#pragma unroll
-  for (int off = kWave / 2; off >= 1; off >>= 1) {
-    RowStat o;
-    o.mx = -INFINITY;
-    o.idx = INT_MAX;
-    o.ref = __shfl_xor(st.ref, off);
-    o.z = __shfl_xor(st.z, off);
-    o.s = 0.f;
-    st = combine(st, o);
-  }
-  if ((tid & (kWave - 1)) == 0) s_part[tid / kWave] = st;
+  post_wave_stat(st, tid, s_part);
   __syncthreads();
-  RowStat r = s_part[0];
-#pragma unroll
-  for (int w = 1; w < kWaves; ++w) r = combine(r, s_part[w]);
+  const RowStat r = fold_parts(s_part);
   ref = r.ref;
   z = r.z;
   __syncthreads();
