@@ -191,8 +191,9 @@ size_t tv_tree_attention_workspace_size(const tv_attn_args* a);
 /*
  * Host checks: a non-null; tensor pointers non-null unless B == 0;
  * 1 <= n_max <= TV_MAX_NODES; Hq % Hkv == 0; D in {64, 128} (TV_BF16 needs
- * D == 128); cap >= n_max and cap % 64 == 0; workspace large enough.
- * B == 0 is a no-op.
+ * D == 128 and a query-head group Hq / Hkv of at most 4096, else
+ * TV_ERR_UNSUPPORTED); cap >= n_max and cap % 64 == 0; workspace large
+ * enough. B == 0 is a no-op.
  */
 tv_status tv_tree_attention(const tv_attn_args* a, hipStream_t stream);
 

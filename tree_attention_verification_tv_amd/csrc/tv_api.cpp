@@ -21,6 +21,7 @@ tv_status check_attn_shapes(const tv_attn_args* a) {
   if (a->cap < a->n_max || a->cap % 64 != 0 || a->D < 1) return TV_ERR_INVALID_ARG;
   if (!dtype_ok(a->dtype)) return TV_ERR_INVALID_ARG;
   if (a->dtype == TV_BF16 && a->D != 128) return TV_ERR_UNSUPPORTED;
+  if (a->dtype == TV_BF16 && a->Hq / a->Hkv > tv::kMaxGroup) return TV_ERR_UNSUPPORTED;
   if (a->dtype == TV_F32 && a->D != 64 && a->D != 128) return TV_ERR_UNSUPPORTED;
   return TV_OK;
 }

@@ -101,6 +101,26 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Division by a launch constant d without the divide sequence (about 25
+// instructions): q = umulhi(x, m) with m = ceil(2^32 / d), exact whenever
+// x * d <= 2^32 (write x = q d + f: x m / 2^32 = q + f / d + x e / (d 2^32)
+// with 0 <= e < d, below q + 1 as long as x e < 2^32). For d = 1, m = 0
+// and id = ~0 pass x through (no branch). DivU is used where the operands are
+// bounded so (query rows by the group size: the group is at most
+// kMaxGroup); DivUs, for the workgroup index, falls back to dividing when
+// the host finds the bound broken.
+struct DivU {
+  uint32_t d, m, id;
+  __device__ __forceinline__ uint32_t div(uint32_t x) const { return __umulhi(x, m) | (x & id); }
+};
+struct DivUs {
+  uint32_t d, m, id, slow;
+  __device__ __forceinline__ uint32_t div(uint32_t x) const {
+    if (slow) return x / d;
+    return __umulhi(x, m) | (x & id);
+  }
+};
+
 struct BfParams {
   const uint16_t* q;
   const uint16_t* k_new;
@@ -117,6 +137,8 @@ struct BfParams {
   float2* part_ml;   // split (reference, row sum) per lane
   int n_max, Hq, Hkv, G, cap;
   int splits, row_blocks;
+  DivU gdiv;        // by G (query rows -> node, head)
+  DivUs ph_div, rb_div, kv_div;   // by row_blocks * splits, row_blocks, Hkv (the workgroup index)
   float scale_log2;  // softmax scale * log2(e)
   int rope;          // 0: no rotation
   double log2_theta; // log2 of the RoPE base
@@ -651,7 +673,7 @@ __device__ __forceinline__ void write_rows(const BfParams& p, int b, int g, int 
     const int row = row0 + 32 * t + (lane & 31);
     if (row < rows_all) {
       const bool live = row < rows_live;
-      const int head = g * p.G + row % p.G, node = row / p.G;
+      const int node = p.gdiv.div(row), head = g * p.G + row - node * p.G;
       uint16_t* orow = p.out + ((static_cast<size_t>(b) * p.n_max + node) * p.Hq + head) * kD;
       const float inv = (live && l[t] > 0.0f) ? 1.0f / l[t] : 0.0f;
 #pragma unroll
@@ -951,7 +973,7 @@ __device__ __forceinline__ void merge_range(const BfParams& p, int b, int g, int
       const int wt = it[k] >> 8, dt = (it[k] >> 6) & 3, lane = it[k] & 63;
       const int row = rb * ROWS + wt * 32 + (lane & 31);
       if (row >= rows_all) continue;
-      const int head = g * p.G + row % p.G, node = row / p.G;
+      const int node = p.gdiv.div(row), head = g * p.G + row - node * p.G;
       uint16_t* dst = p.out + ((static_cast<size_t>(b) * p.n_max + node) * p.Hq + head) * kD + 32 * dt + 4 * (lane >> 5);
       if (row >= rows_live) {
 #pragma unroll
@@ -1033,19 +1055,20 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   // together: the row blocks of one split (adjacent there) read the same key
   // tiles, and every split reads the same query rows. (A placement hint
   // only: any bijection is correct.)
-  const int per_head = p.row_blocks * p.splits, n_heads = gridDim.x / per_head;
+  const int per_head = p.row_blocks * p.splits, n_heads = p.ph_div.div(gridDim.x);
   int s, rb, hd;
   if (n_heads % 8 == 0) {
-    const int L = blockIdx.x, k = L >> 3, w = k % per_head;
-    hd = (k / per_head) * 8 + (L & 7);
-    s = w / p.row_blocks;
-    rb = w % p.row_blocks;
+    const int L = blockIdx.x, k = L >> 3, kq = p.ph_div.div(k), w = k - kq * per_head;
+    hd = kq * 8 + (L & 7);
+    s = p.rb_div.div(w);
+    rb = w - s * p.row_blocks;
   } else {
-    hd = blockIdx.x / per_head;
-    s = (blockIdx.x % per_head) / p.row_blocks;
-    rb = blockIdx.x % p.row_blocks;
+    hd = p.ph_div.div(blockIdx.x);
+    const int w = blockIdx.x - hd * per_head;
+    s = p.rb_div.div(w);
+    rb = w - s * p.row_blocks;
   }
-  const int g = hd % p.Hkv, b = hd / p.Hkv;
+  const int b = p.kv_div.div(hd), g = hd - b * p.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = p.G;
@@ -1078,7 +1101,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
     my_row[t] = r0 + 32 * t + (lane & 31);
-    qdep[t] = ld_b32(p.depth + static_cast<size_t>(b) * p.n_max + min(my_row[t] / G, p.n_max - 1));
+    qdep[t] = ld_b32(p.depth + static_cast<size_t>(b) * p.n_max + min(static_cast<int>(p.gdiv.div(my_row[t])), p.n_max - 1));
   }
   uint32_t dep_lane = ld_b32(p.depth + static_cast<size_t>(b) * p.n_max + min(lane, p.n_max - 1));
   constexpr int kDepOps = QT + 1;
@@ -1090,8 +1113,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
 #pragma unroll
     for (int j = 0; j < QCPT; ++j) {
       const int c = j * NT + tid, r = c >> 4, piece = (c & 15) ^ (r & 15);
-      const int row = rb0 + r, node = min(row / G, p.n_max - 1);
-      const uint32_t voff = static_cast<uint32_t>(((node * p.Hq + g * G + row % G) * kD + 8 * piece) * 2);
+      const int row = rb0 + r, nq = p.gdiv.div(row), node = min(nq, p.n_max - 1);
+      const uint32_t voff = static_cast<uint32_t>(((node * p.Hq + g * G + row - nq * G) * kD + 8 * piece) * 2);
       dma16(qb, voff, lds_q + static_cast<uint32_t>(j * NT + wave * 64) * 16u);
     }
   }
@@ -1110,7 +1133,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
     wait_vm<0>();
     if (p.splits == 1 || (p.fused && s == 0)) {
       for (int r = first_row + tid / 16; r < min(rb0 + ROWS, rows_all); r += NT / 16) {
-        const int i = r / G, head = g * G + r % G;
+        const int i = p.gdiv.div(r), head = g * G + r - i * G;
         uint16_t* orow = p.out + ((static_cast<size_t>(b) * p.n_max + i) * p.Hq + head) * kD;
         reinterpret_cast<uint4*>(orow)[tid % 16] = make_uint4(0, 0, 0, 0);
       }
@@ -1171,7 +1194,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
     }
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
-      const uint64_t* asrc = p.anc + static_cast<size_t>(b) * p.n_max + min(my_row[t] / G, p.n_max - 1);
+      const uint64_t* asrc = p.anc + static_cast<size_t>(b) * p.n_max + min(static_cast<int>(p.gdiv.div(my_row[t])), p.n_max - 1);
       my_anc[t] = ASM ? ld_b64(asrc) : *asrc;
     }
   };
@@ -1312,10 +1335,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   landed(dep_lane);
   int n_cs;          // table entries: depths 0 .. deepest node of b
   {
-    int dmax = lane < n ? clamp_depth(static_cast<int>(dep_lane)) : 0;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) dmax = max(dmax, __shfl_xor(dmax, off));
-    n_cs = (__builtin_amdgcn_readfirstlane(dmax) + 1) * (kD / 2);
+    const int dmax = wave_max_i32(lane < n ? clamp_depth(static_cast<int>(dep_lane)) : 0);
+    n_cs = (dmax + 1) * (kD / 2);
   }
   auto build_table = [&]() {
     const double freq = rope_freq(p.log2_theta, tid & 63);   // column tid % 64 of every row
@@ -1848,7 +1869,7 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(BfParams p) {
   const int rows_all = p.G * p.n_max;
   if (row >= rows_all) return;
   const int rows_live = sq.skip ? 0 : p.G * sq.n;
-  const int head = g * p.G + row % p.G, node = row / p.G;
+  const int node = p.gdiv.div(row), head = g * p.G + row - node * p.G;
   uint16_t* dst = p.out + ((static_cast<size_t>(b) * p.n_max + node) * p.Hq + head) * kD + 32 * dt + 4 * (lane >> 5);
   if (row >= rows_live) {
 #pragma unroll
@@ -1989,6 +2010,16 @@ hipError_t scratch_workspace(void** ptr) {
   return hipSuccess;
 }
 
+// the multiplier of DivUs for divisor d >= 1 and operands up to x_end
+static DivUs make_divus(uint32_t d, uint64_t x_end) {
+  DivUs r;
+  r.d = d;
+  r.m = d == 1 ? 0u : static_cast<uint32_t>(((uint64_t{1} << 32) + d - 1) / d);
+  r.id = d == 1 ? ~0u : 0u;
+  r.slow = x_end * d > (uint64_t{1} << 32) ? 1u : 0u;
+  return r;
+}
+
 hipError_t launch_attention_bf16(const tv_attn_args* a, const AttnPlan& pl, const tv_paged_kv* pk,
                                  hipStream_t s) {
   BfParams p;
@@ -2013,6 +2044,17 @@ hipError_t launch_attention_bf16(const tv_attn_args* a, const AttnPlan& pl, cons
   p.num_pages = pk ? pk->num_pages : 0;
   p.splits = pl.splits;
   p.row_blocks = pl.row_blocks;
+  // each divisor with the largest index it divides (x * d <= 2^32 keeps the
+  // multiply exact)
+  // (query rows stay below G * 64 + 256, so with G <= kMaxGroup every
+  // quotient by G is exact)
+  const uint64_t n_wg = static_cast<uint64_t>(pl.splits) * pl.row_blocks * a->Hkv * a->B;
+  p.gdiv.d = static_cast<uint32_t>(p.G);
+  p.gdiv.m = p.G == 1 ? 0u : static_cast<uint32_t>(((uint64_t{1} << 32) + p.G - 1) / p.G);
+  p.gdiv.id = p.G == 1 ? ~0u : 0u;
+  p.ph_div = make_divus(static_cast<uint32_t>(pl.row_blocks * pl.splits), n_wg);
+  p.rb_div = make_divus(static_cast<uint32_t>(pl.row_blocks), static_cast<uint64_t>(pl.row_blocks) * pl.splits);
+  p.kv_div = make_divus(static_cast<uint32_t>(a->Hkv), static_cast<uint64_t>(a->Hkv) * a->B);
   p.rope = a->rope_theta != 0.0f;
   p.log2_theta = p.rope ? log2(static_cast<double>(a->rope_theta)) : 0.0;
   const float scale = a->softmax_scale > 0.0f ? a->softmax_scale : 1.0f / sqrtf(static_cast<float>(kD));

@@ -29,10 +29,17 @@ __device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
+// Wave-wide maximum, every lane active: DPP moves within each row of 16
+// lanes (swap neighbours, swap pairs, mirror each half-row, mirror the row)
+// leave every lane of a row with the row's maximum; the four rows' lanes 0,
+// 16, 32 and 48 are then read into scalars. Every lane gets the result.
 __device__ __forceinline__ int wave_max_i32(int v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off));
-  return v;
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false));    // quad_perm [1, 0, 3, 2]
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false));    // quad_perm [2, 3, 0, 1]
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false));   // row_half_mirror
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false));   // row_mirror
+  return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
 
 }  // namespace tv

@@ -76,6 +76,9 @@ hipError_t launch_attention_f32(const tv_attn_args* a, hipStream_t s);
 // workload of this library needs at most about 35 MB), and its device address
 // on the current device (looked up once per device).
 constexpr size_t kScratchBytes = size_t(48) << 20;
+// largest query-head group Hq / Hkv of the bf16 attention (its index
+// arithmetic divides query rows by the group with a bounded multiplier)
+constexpr int kMaxGroup = 4096;
 hipError_t scratch_workspace(void** ptr);
 
 }  // namespace tv
