@@ -42,7 +42,7 @@ if ROOT not in sys.path:
 METRIC = "tree-verify nodes/sec and achieved HBM GB/s (% of peak), 8B-shaped GQA batch 8"
 HBM_PEAK_GBS = 8000.0
 INFINITY_CACHE_BYTES = 256 << 20
-KERNEL_SOURCES = ["tv_attn_bf16.hip", "tv_attn_f32.hip", "tv_device.h"]
+KERNEL_SOURCES = ["tv_attn_bf16.hip", "tv_attn_waits.h", "tv_attn_f32.hip", "tv_device.h"]
 
 
 def kernel_source_hash() -> str:

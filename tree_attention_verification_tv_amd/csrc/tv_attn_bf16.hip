@@ -82,6 +82,7 @@
 #include <mutex>
 #include <type_traits>
 
+#include "tv_attn_waits.h"
 #include "tv_device.h"
 #include "tv_internal.h"
 
@@ -93,7 +94,8 @@ constexpr int kD = 128;                 // head dim (bf16 path)
 constexpr int kKT = 64;                 // keys per LDS stage (= V cache block)
 constexpr int kStageElems = kKT * kD;   // bf16 elements of one K (or V) stage
 constexpr int kStages = 5;              // LDS ring of key tiles
-constexpr int kAhead = 3;               // tiles in flight
+constexpr int kAhead = waits::kAhead;   // tiles in flight
+static_assert(waits::kKeys == 64 && waits::kDim == 128, "the wait model counts this kernel's tiles");
 constexpr int kMaxSplits = 16;          // key splits per row block
 constexpr int kCsElems = 64 * 64 * 4;   // bf16 units of the RoPE table: 64 depths x 64 (cos, sin) = one stage
 
@@ -1173,6 +1175,12 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   // wait for all of them).
   constexpr int KI = 8 * 64 / NT, VI = 16 * 64 / NT;   // tree items per thread: K pairs, V chunks
   constexpr int kTreeOps = 3 * KI + VI + QT;
+  // every loop bound above is the one the wait model counts
+  static_assert(CPT == waits::tile_chunks(WAVES) && QCPT == waits::query_ops(WAVES, QT) &&
+                    kDepOps == waits::depth_ops(QT) && kPageOps == waits::page_ops(PAGED) &&
+                    KI == waits::tree_k_items(WAVES) && VI == waits::tree_v_items(WAVES) &&
+                    kTreeOps == waits::tree_ops(WAVES, QT),
+                "the hand-counted waits follow tv_attn_waits.h");
   u32x4 tk_lo[KI], tk_hi[KI], tvv[VI];
   uint32_t t_dep[KI];
   auto load_tree = [&](auto asm_tag) __attribute__((always_inline)) {
@@ -1286,17 +1294,18 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   // issue until most of them have arrived, with its RoPE work still ahead.
   // Tile 1 goes out once the query rows are in registers, tile 2 after the
   // RoPE, so that work overlaps the first tiles' transfer.
-  constexpr int kStartOps = kPageOps + kDepOps + QCPT + kTreeOps;
+  // (every count below comes from the issue-order model in tv_attn_waits.h)
+  constexpr bool kGuard = waits::start_guard(WAVES, QT, PAGED);
   static_assert(kAhead == 3, "the start issues three tiles");
-  if constexpr (kStartOps + 2 * CPT > 63) wait_vm<63 - 2 * CPT>();
+  if constexpr (kGuard) wait_vm<waits::vm_start_guard(WAVES)>();
   if constexpr (PAGED) {
     // the page ids (the oldest loads) land; every block of slots [0, P + n)
     // must name a page of the pools (all workgroups of b check alike), else
     // b is flagged and skipped
     if (n_masked > 0)
-      wait_vm<kDepOps + QCPT + kTreeOps>();
+      wait_vm<waits::vm_pages(WAVES, QT, true)>();
     else
-      wait_vm<kDepOps + QCPT>();
+      wait_vm<waits::vm_pages(WAVES, QT, false)>();
     bool bad = false;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -1316,19 +1325,19 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   // (cos, sin) of angle (P + depth) f_j at [depth][j], is built in stage 2
   // (idle until tile 2 goes out) as soon as the depths have landed, while
   // the queries are still in flight.
-  if constexpr (kStartOps + 2 * CPT <= 63) {
+  if constexpr (!kGuard) {
     if (n_masked > 0)
-      wait_vm<QCPT + kTreeOps + 2 * CPT>();
+      wait_vm<waits::vm_depths(WAVES, QT, true, true)>();
     else if (n_tiles > 0)
-      wait_vm<QCPT + 2 * CPT>();
+      wait_vm<waits::vm_depths(WAVES, QT, false, true)>();
     else
-      wait_vm<QCPT>();
+      wait_vm<waits::vm_depths(WAVES, QT, false, false)>();
   } else {
     // (the guard above left an unknown count: wait for all but tile 0)
     if (n_tiles > 0)
-      wait_vm<2 * CPT>();
+      wait_vm<waits::vm_queries(WAVES, true)>();
     else
-      wait_vm<0>();
+      wait_vm<waits::vm_queries(WAVES, false)>();
   }
 #pragma unroll
   for (int t = 0; t < QT; ++t) landed(qdep[t]);
@@ -1351,9 +1360,9 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   // log2(e), in bf16, become the B operands of the score MFMA; the tree's
   // keys are rotated at P + depth(node) in their registers.
   if (n_tiles > 0)
-    wait_vm<2 * CPT>();
+    wait_vm<waits::vm_queries(WAVES, true)>();
   else
-    wait_vm<0>();
+    wait_vm<waits::vm_queries(WAVES, false)>();
 #pragma unroll
   for (int t = 0; t < QT; ++t) landed(my_anc[t]);
 #pragma unroll
@@ -1550,15 +1559,16 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
         tile_product<QT, M, SHIFT>(st, Ks(buf), Vs(buf), qf, k_addr, v_addr, h, rel0, my_anc, copy);
       }
     };
-    // Waits until the tile at position t has landed, given how many later
-    // tiles are in flight (at most kAhead - 1).
-    auto wait_tile = [&](int t) {
-      const int later = min(kAhead - 1, n_tiles - 1 - t);
+    // Waits until a tile has landed, `later` whole tiles having been issued
+    // after it (at most kAhead - 1).
+    auto wait_tiles_after = [&](int later) {
       static_assert(kAhead == 3, "waits below assume three tiles in flight");
-      if (later >= 2) wait_vm<2 * CPT * 2>();
-      else if (later == 1) wait_vm<2 * CPT>();
-      else wait_vm<0>();
+      if (later >= 2) wait_vm<waits::vm_tile(WAVES, 2)>();
+      else if (later == 1) wait_vm<waits::vm_tile(WAVES, 1)>();
+      else wait_vm<waits::vm_tile(WAVES, 0)>();
     };
+    // the tile at position t, at the top of iteration t
+    auto wait_tile = [&](int t) { wait_tiles_after(waits::later_tiles(t, n_tiles)); };
     // A ring of kStages LDS stages, kAhead tiles in flight; position t lives
     // in stage t % kStages, and the copy of position t + kAhead goes out
     // during iteration t, into the stage of position t - 2 (the barrier at
@@ -1576,10 +1586,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
       // after the last tree tile come min(kAhead, n_tiles) - n_masked tiles
       // (one fewer than wait_tile assumes when the tree spans two tiles).
       stage_tree_values();
-      const int after = min(kAhead, n_tiles) - n_masked;
-      if (after >= 2) wait_vm<2 * CPT * 2>();
-      else if (after == 1) wait_vm<2 * CPT>();
-      else wait_vm<0>();
+      wait_tiles_after(waits::after_tree(n_tiles, n_masked));
       __syncthreads();
       for (int m = 0; m < n_masked; ++m) fill_tree(m);
       __syncthreads();
@@ -1594,7 +1601,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
     }
     if constexpr (MODE == 1) {
       for (; t + kAhead < n_tiles; ++t) {
-        wait_vm<2 * CPT * (kAhead - 1)>();
+        wait_vm<waits::vm_tile(WAVES, kAhead - 1)>();
         __syncthreads();
         product(std::false_type{}, t, tile_copy(t + kAhead));
       }
