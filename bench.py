@@ -1,9 +1,11 @@
 """Throughput of one draft-tree verification step on one MI355X.
 
 A step is the whole verification path for one attention layer over one batch:
-tv_build_tree -> tv_tree_attention -> tv_accept_commit (greedy accept and the
-in-place KV commit in one launch; the paged step calls tv_accept and
-tv_commit_paged), all through the C ABI. The headline workload is the Llama-3-8B-shaped GQA batch (32 q / 8 kv
+tv_tree_attention_from_parents (the tree mask and depths built inside the
+attention kernel, which also writes them for the accept) -> tv_accept_commit
+(greedy accept and the in-place KV commit in one launch); the paged step calls
+tv_build_tree -> tv_tree_attention_paged -> tv_accept -> tv_commit_paged. All
+through the C ABI. The headline workload is the Llama-3-8B-shaped GQA batch (32 q / 8 kv
 heads, head dim 128, batch 8, prefix 4096, 60-node EAGLE-2-style trees, bf16).
 
 Inputs are generated once on the host, copied to HBM, and replicated into
@@ -15,7 +17,8 @@ steps do identical work.
 Prints one JSON line. `value` = tree nodes verified per second over the timed
 steps (wall clock between two device synchronisations; the timed loop calls
 the C ABI with arguments built once, as a native caller would). `roofline`
-reports the attention call (its two kernels): algorithmic HBM bytes per call
+reports the attention call (with the tree set-up in the dense step):
+algorithmic HBM bytes per call
 divided by its mean duration, from HIP events on the launch stream around the
 call in K further steps (an event pair adds a few microseconds to a step, so
 the timed steps carry none); `traffic` is the measured HBM bytes per call from
@@ -490,6 +493,8 @@ def main() -> None:
     ap.add_argument("--config", type=int, default=3, help="workload 1..5 (3 = headline)")
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated per step (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate-tree", action="store_true",
+                    help="dense step with tv_build_tree + tv_tree_attention instead of the combined call")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--workload", choices=("step", "typical", "paged", "draft-tree", "spec-sample"), default="step",
                     help="step: the verification step (default); typical: typical acceptance "
@@ -599,11 +604,19 @@ def main() -> None:
     ac = (P(tok), P(tgt), P(parents), P(anc), P(depth), P(n_nodes), P(err), B, n_max, P(acc_len),
           P(path), P(bonus), P(toks), sp)
 
+    # The dense step builds the tree inside the attention kernel
+    # (tv_tree_attention_from_parents writes anc, depth and err for the
+    # accept); the paged step calls tv_build_tree first.
+    separate = paged or args.separate_tree
+
     def attention(k: int) -> int:
         if paged:
             return lib.tv_tree_attention_paged(ctypes.byref(calls[k % copies][0]),
                                                ctypes.byref(sets[k % copies]["pk"]), sp)
-        return lib.tv_tree_attention(ctypes.byref(calls[k % copies][0]), sp)
+        if separate:
+            return lib.tv_tree_attention(ctypes.byref(calls[k % copies][0]), sp)
+        return lib.tv_tree_attention_from_parents(ctypes.byref(calls[k % copies][0]), P(parents), P(anc), P(depth),
+                                                  sp)
 
     def accept_commit(k: int) -> int:
         if paged:
@@ -611,7 +624,7 @@ def main() -> None:
         return lib.tv_accept_commit(*calls[k % copies][2])
 
     def step(k: int) -> None:
-        st = lib.tv_build_tree(*bt)
+        st = lib.tv_build_tree(*bt) if separate else 0
         st |= attention(k)
         st |= accept_commit(k)
         if st:
@@ -640,7 +653,7 @@ def main() -> None:
               for _ in range(args.steps)]
     torch.cuda.synchronize()
     for k in range(args.steps):
-        st = lib.tv_build_tree(*bt)
+        st = lib.tv_build_tree(*bt) if separate else 0
         events[k][0].record(stream)
         st |= attention(k)
         events[k][1].record(stream)
@@ -681,14 +694,17 @@ def main() -> None:
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": wname, "batch": B, "q_heads": w.Hq, "kv_heads": w.Hkv,
+                   "tree_set_up": "tv_build_tree" if separate else "inside the attention kernel",
                    "head_dim": w.D, "prefix_len_mean": float(np.mean(w.prefix_len)),
                    "tree_nodes": int(w.n_nodes.max()), "input_copies_rotated": copies,
                    "seed": args.config if args.seed is None else args.seed},
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": traffic,
-                     "kernel": "tv_tree_attention call: attn_bf16_kernel (key splits merged and tree appended "
-                               "inside the kernel on the automatic plan; merge_bf16_kernel otherwise); HIP events "
-                               "on its stream around each call, in the step",
+                     "kernel": ("tv_tree_attention_paged call" if paged else "tv_tree_attention call" if separate
+                                else "tv_tree_attention_from_parents call (the tree built in the kernel)") +
+                               ": attn_bf16_kernel (key splits merged and tree appended inside the kernel on the "
+                               "automatic plan; merge_bf16_kernel otherwise); HIP events on its stream around "
+                               "each call, in the step",
                      "algorithmic_bytes_per_launch": ab["total"],
                      "algorithmic_flops_per_launch": flops,
                      "hbm_frac": ab["total"] / attn_mean_s / 1e9 / HBM_PEAK_GBS,

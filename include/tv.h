@@ -198,6 +198,28 @@ size_t tv_tree_attention_workspace_size(const tv_attn_args* a);
 tv_status tv_tree_attention(const tv_attn_args* a, hipStream_t stream);
 
 /*
+ * tv_tree_attention_from_parents -- tv_build_tree and tv_tree_attention in
+ * one launch (bf16; fp32 makes the two launches). The tree mask and depths
+ * are those of infra-guide "5.3 Medusa、EAGLE 与 MTP", sections 3.1, 3.2 and
+ * 8; the attention is tv_tree_attention's.
+ *   a         as for tv_tree_attention, except that a->anc and a->depth are
+ *             not read, and a->err is output only: it receives what
+ *             tv_build_tree writes (0 or TV_ERR_BAD_TREE), then
+ *             TV_ERR_CAPACITY as tv_tree_attention sets it
+ *   parents   [B][n_max] int32 parent of each node (-1 for the root), as for
+ *             tv_build_tree
+ *   anc       [B][n_max] uint64 out: ancestors-or-self bitmasks
+ *   depth     [B][n_max] int32 out: depths
+ * anc, depth, err, out and the cache append are bit for bit those of
+ * tv_build_tree followed by tv_tree_attention; the pair feeds tv_accept /
+ * tv_accept_commit as usual.
+ * Host checks: those of tv_tree_attention, and parents, anc and depth
+ * non-null unless B == 0. The paged cache is not offered here.
+ */
+tv_status tv_tree_attention_from_parents(const tv_attn_args* a, const int32_t* parents, uint64_t* anc,
+                                         int32_t* depth, hipStream_t stream);
+
+/*
  * tv_tree_attention_noalloc -- tv_tree_attention for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc. Same arguments, computation, outputs and

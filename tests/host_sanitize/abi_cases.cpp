@@ -182,6 +182,34 @@ void attention() {
   EXPECT(tv_tree_attention_workspace_size(&a), 0);
   EXPECT(tv_tree_attention_workspace_size(nullptr), 0);
 
+  // the tree built inside the attention: the attention's checks plus the
+  // parents and the two tree outputs; fp32 takes the two launches
+  EXPECT(tv_tree_attention_from_parents(nullptr, I, U, I, nullptr), TV_ERR_INVALID_ARG);
+  a = attn();
+  a.workspace = F;
+  a.workspace_bytes = need;
+  EXPECT(tv_tree_attention_from_parents(&a, nullptr, U, I, nullptr), TV_ERR_INVALID_ARG);
+  EXPECT(tv_tree_attention_from_parents(&a, I, nullptr, I, nullptr), TV_ERR_INVALID_ARG);
+  EXPECT(tv_tree_attention_from_parents(&a, I, U, nullptr, nullptr), TV_ERR_INVALID_ARG);
+  a.workspace_bytes = need - 1;
+  EXPECT(tv_tree_attention_from_parents(&a, I, U, I, nullptr), TV_ERR_INVALID_ARG);
+  a.workspace_bytes = need;
+  a.anc = nullptr;   // (not read)
+  a.depth = nullptr;
+  c = stub::calls;
+  EXPECT(tv_tree_attention_from_parents(&a, I, U, I, nullptr), TV_OK);
+  REACHED(c, "attention_bf16_build");
+  a = attn(8, 60, 32, 8, 128, 4160, TV_F32);
+  c = stub::calls;
+  EXPECT(tv_tree_attention_from_parents(&a, I, U, I, nullptr), TV_OK);
+  ++checks;
+  if (stub::calls != c + 2 || std::strcmp(stub::last.name, "attention_f32") != 0) {
+    ++failures;
+    std::printf("FAIL from_parents fp32: expected build_tree then attention_f32\n");
+  }
+  a = attn(0);
+  EXPECT(tv_tree_attention_from_parents(&a, nullptr, nullptr, nullptr, nullptr), TV_OK);
+
   // the allocation-free entry point: same checks, its own scratch, a size limit
   EXPECT(tv_tree_attention_noalloc(nullptr, nullptr), TV_ERR_INVALID_ARG);
   a = attn(8, 0);

@@ -75,8 +75,10 @@ AttnPlan plan_attention_bf16(const tv_attn_args* a) {
   p.workspace_bytes = size_t(16384) + size_t(p.splits) * a->B * a->Hkv * p.rows_pad * (size_t(a->D) * 2 + 8);
   return p;
 }
-hipError_t launch_attention_bf16(const tv_attn_args* a, const AttnPlan&, const tv_paged_kv* pk, hipStream_t) {
-  stub::hit(pk ? "attention_bf16_paged" : "attention_bf16", a->B, a->n_max, 2, a->workspace_bytes, a->workspace);
+hipError_t launch_attention_bf16(const tv_attn_args* a, const AttnPlan&, const tv_paged_kv* pk, const int32_t* parents,
+                                 hipStream_t) {
+  stub::hit(pk ? "attention_bf16_paged" : parents ? "attention_bf16_build" : "attention_bf16", a->B, a->n_max, 2,
+            a->workspace_bytes, a->workspace);
   return hipSuccess;
 }
 hipError_t launch_attention_f32(const tv_attn_args* a, hipStream_t) {

@@ -5,7 +5,8 @@ register loads from inline asm, so the compiler inserts no waits for them;
 every count is instantiated from the issue-order model in
 csrc/tv_attn_waits.h. tests/wait_model_check.cpp replays, on the host, the
 operations one thread issues and the waits it executes for every
-instantiation, tile count, tree-tile count and pass, and checks that each
+instantiation (paged or not, tree built in the kernel or given), tile count,
+tree-tile count and pass, and checks that each
 wait covers what it guards, exactly, and that the counter never overflows.
 Compiled with the host compiler; no GPU is needed.
 """
@@ -35,7 +36,7 @@ def test_every_wait_covers_exactly_what_it_guards(checker):
     r = subprocess.run([checker], capture_output=True, text=True)
     assert r.returncode == 0, r.stdout + r.stderr
     ok, cases, waits = r.stdout.split()
-    assert ok == "ok" and int(cases) == 432 and int(waits) > 5000
+    assert ok == "ok" and int(cases) == 864 and int(waits) > 5000
 
 
 def test_the_earlier_tree_tile_wait_is_caught(checker):

@@ -1,6 +1,7 @@
 // Host check of the bf16 attention kernel's hand-counted waits.
 //
-// For every kernel instantiation (wavefronts, query tiles, paged or not),
+// For every kernel instantiation (wavefronts, query tiles, paged or not,
+// tree built by the kernel or given),
 // tile count, tree-tile count and pass (the fast pass, and the redo passes
 // that re-issue the first tiles), this program replays, in order, the vector
 // memory operations one thread issues and the waits it executes (the
@@ -100,19 +101,20 @@ void replay_pass(Replay& r, int waves, int n_tiles, int n_masked, bool legacy_tr
   }
 }
 
-void replay(Replay& r, int waves, int qt, bool paged, int n_tiles, int n_masked, bool redo, bool legacy_tree) {
+void replay(Replay& r, int waves, int qt, bool paged, bool build, int n_tiles, int n_masked, bool redo,
+            bool legacy_tree) {
   const bool tree = n_masked > 0;
-  const bool guard = w::start_guard(waves, qt, paged);
+  const bool guard = w::start_guard(waves, qt, paged, build);
   // start
   if (paged) r.issue("page", w::page_ops(true));
-  r.issue("depth", w::depth_ops(qt));
+  r.issue("depth", w::depth_ops(qt, build));
   r.issue("query", w::query_ops(waves, qt));
-  if (tree) r.issue("tree", w::tree_ops(waves, qt));
+  if (tree) r.issue("tree", w::tree_ops(waves, qt, build));
   if (guard) r.wait(w::vm_start_guard(waves), {}, "start guard");
-  if (paged) r.wait(w::vm_pages(waves, qt, tree), {"page"}, "page ids");
+  if (paged) r.wait(w::vm_pages(waves, qt, build, tree), {"page"}, "page ids");
   if (n_tiles > 0) r.issue_tile(0, waves);
   if (!guard)
-    r.wait(w::vm_depths(waves, qt, tree, n_tiles > 0), {"page", "depth"}, "depths");
+    r.wait(w::vm_depths(waves, qt, build, tree, n_tiles > 0), {"page", "depth"}, "depths");
   else
     r.wait(w::vm_queries(waves, n_tiles > 0), {"page", "depth", "query", "tree"}, "depths (guarded start)");
   r.wait(w::vm_queries(waves, n_tiles > 0), {"page", "depth", "query", "tree"}, "queries");
@@ -143,15 +145,17 @@ int main(int argc, char** argv) {
   long cases = 0, waits = 0, failures = 0;
   for (const auto& sh : shapes)
     for (int paged = 0; paged < 2; ++paged)
+      for (int build = 0; build < 2; ++build)
       for (int n_tiles = 0; n_tiles <= 12; ++n_tiles)
         // a tree of at most 64 nodes spans at most two 64-key tiles
         for (int n_masked = 0; n_masked <= 2 && n_masked <= n_tiles; ++n_masked)
           for (int redo = 0; redo < 2; ++redo) {
             Replay r;
             r.where = "waves=" + std::to_string(sh[0]) + " qt=" + std::to_string(sh[1]) +
-                      " paged=" + std::to_string(paged) + " n_tiles=" + std::to_string(n_tiles) +
+                      " paged=" + std::to_string(paged) + " build=" + std::to_string(build) +
+                      " n_tiles=" + std::to_string(n_tiles) +
                       " n_masked=" + std::to_string(n_masked) + " redo=" + std::to_string(redo);
-            replay(r, sh[0], sh[1], paged != 0, n_tiles, n_masked, redo != 0, legacy_tree);
+            replay(r, sh[0], sh[1], paged != 0, build != 0, n_tiles, n_masked, redo != 0, legacy_tree);
             ++cases;
             waits += r.waits;
             for (size_t e = 0; e < r.errors.size(); ++e)

@@ -26,7 +26,7 @@ from . import _lib
 from ._lib import (PAGE, TV_BF16, TV_ERR_BAD_PAGE, TV_ERR_BAD_TREE, TV_ERR_CAPACITY, TV_F32,  # noqa: F401
                    TV_MAX_NODES, TvAttnArgs, TvError, TvPagedKv)
 
-__all__ = ["build_tree", "tree_attention", "tree_attention_noalloc", "accept_commit", "tree_attention_workspace_size", "new_workspace", "accept",
+__all__ = ["build_tree", "tree_attention", "tree_attention_from_parents", "tree_attention_noalloc", "accept_commit", "tree_attention_workspace_size", "new_workspace", "accept",
            "accept_typical", "commit", "eagle2_tree", "speculative_sample", "tree_attention_paged", "commit_paged", "pages_from_dense",
            "dense_from_pages", "TV_ERR_BAD_PAGE", "PAGE",
            "version", "TvError", "TV_ERR_BAD_TREE", "TV_ERR_CAPACITY", "attn_args",
@@ -231,6 +231,36 @@ def tree_attention(q, k_new, v_new, k_cache, v_cache, prefix_len, n_nodes, anc, 
         a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
     _lib.check("tv_tree_attention", lib.tv_tree_attention(ctypes.byref(a), _stream(stream)))
     return out
+
+
+def tree_attention_from_parents(q, k_new, v_new, k_cache, v_cache, prefix_len, n_nodes, parents,
+                                rope_theta=10000.0, softmax_scale=0.0, out=None, workspace=None, stream=None):
+    """build_tree and tree_attention in one launch (bf16; fp32 takes two):
+    returns (out, anc, depth, err), bit for bit those of the two calls."""
+    lib = _lib.load()
+    _dev(parents, "parents", torch.int32)
+    B, n_max = q.shape[0], q.shape[1]
+    if tuple(parents.shape) != (B, n_max):
+        raise ValueError("parents must be [B, n_max]")
+    dev = q.device
+    anc = torch.empty(B, n_max, dtype=torch.int64, device=dev)
+    depth = torch.empty(B, n_max, dtype=torch.int32, device=dev)
+    err = torch.empty(B, dtype=torch.int32, device=dev)
+    if out is None:
+        out = torch.empty_like(q)
+    a = attn_args(q, k_new, v_new, k_cache, v_cache, prefix_len, n_nodes, anc, depth, err, out,
+                  rope_theta, softmax_scale, workspace)
+    need = tree_attention_workspace_size(a)
+    if need > a.workspace_bytes:
+        if workspace is not None:
+            raise ValueError(f"workspace holds {a.workspace_bytes} bytes, {need} needed")
+        workspace = _default_workspace(q.device, need, stream)
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
+    _lib.check("tv_tree_attention_from_parents",
+               lib.tv_tree_attention_from_parents(ctypes.byref(a), ctypes.c_void_p(parents.data_ptr()),
+                                                  ctypes.c_void_p(anc.data_ptr()), ctypes.c_void_p(depth.data_ptr()),
+                                                  _stream(stream)))
+    return out, anc, depth, err
 
 
 def tree_attention_noalloc(q, k_new, v_new, k_cache, v_cache, prefix_len, n_nodes, anc, depth, err, out,

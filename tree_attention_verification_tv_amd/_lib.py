@@ -49,6 +49,7 @@ SIGNATURES = {
     "tv_tree_attention_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(TvAttnArgs)]),
     "tv_tree_attention": (_I, [ctypes.POINTER(TvAttnArgs), _P]),
     "tv_tree_attention_noalloc": (_I, [ctypes.POINTER(TvAttnArgs), _P]),
+    "tv_tree_attention_from_parents": (_I, [ctypes.POINTER(TvAttnArgs), _P, _P, _P, _P]),
     "tv_tree_attention_paged": (_I, [ctypes.POINTER(TvAttnArgs), ctypes.POINTER(TvPagedKv), _P]),
     "tv_accept": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P]),
     "tv_eagle2_tree": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]),

@@ -71,7 +71,7 @@ tv_status tv_tree_attention(const tv_attn_args* a, hipStream_t stream) {
   const tv::AttnPlan plan = tv::plan_attention_bf16(a);
   if (plan.workspace_bytes > 0 && (a->workspace == nullptr || a->workspace_bytes < plan.workspace_bytes))
     return TV_ERR_INVALID_ARG;
-  return from_hip(tv::launch_attention_bf16(a, plan, nullptr, stream));
+  return from_hip(tv::launch_attention_bf16(a, plan, nullptr, nullptr, stream));
 }
 
 tv_status tv_tree_attention_noalloc(const tv_attn_args* a, hipStream_t stream) {
@@ -91,7 +91,30 @@ tv_status tv_tree_attention_noalloc(const tv_attn_args* a, hipStream_t stream) {
     if (tv::scratch_workspace(&b.workspace) != hipSuccess) return TV_ERR_HIP;
     b.workspace_bytes = tv::kScratchBytes;
   }
-  return from_hip(tv::launch_attention_bf16(&b, plan, nullptr, stream));
+  return from_hip(tv::launch_attention_bf16(&b, plan, nullptr, nullptr, stream));
+}
+
+tv_status tv_tree_attention_from_parents(const tv_attn_args* a, const int32_t* parents, uint64_t* anc,
+                                         int32_t* depth, hipStream_t stream) {
+  const tv_status st = check_attn_shapes(a);
+  if (st != TV_OK) return st;
+  if (a->B == 0) return TV_OK;
+  if (!a->q || !a->k_new || !a->v_new || !a->k_cache || !a->v_cache || !a->prefix_len ||
+      !a->n_nodes || !a->err || !a->out || !parents || !anc || !depth)
+    return TV_ERR_INVALID_ARG;
+  tv_attn_args b = *a;
+  b.anc = anc;
+  b.depth = depth;
+  if (a->dtype == TV_F32) {
+    // (the fp32 kernel reads a built tree: two launches)
+    const hipError_t e = tv::launch_build_tree(parents, a->n_nodes, a->B, a->n_max, anc, depth, a->err, stream);
+    if (e != hipSuccess) return TV_ERR_HIP;
+    return from_hip(tv::launch_attention_f32(&b, stream));
+  }
+  const tv::AttnPlan plan = tv::plan_attention_bf16(a);
+  if (plan.workspace_bytes > 0 && (a->workspace == nullptr || a->workspace_bytes < plan.workspace_bytes))
+    return TV_ERR_INVALID_ARG;
+  return from_hip(tv::launch_attention_bf16(&b, plan, nullptr, parents, stream));
 }
 
 tv_status tv_tree_attention_paged(const tv_attn_args* a, const tv_paged_kv* pk, hipStream_t stream) {
@@ -107,7 +130,7 @@ tv_status tv_tree_attention_paged(const tv_attn_args* a, const tv_paged_kv* pk, 
   const tv::AttnPlan plan = tv::plan_attention_bf16(a);
   if (plan.workspace_bytes > 0 && (a->workspace == nullptr || a->workspace_bytes < plan.workspace_bytes))
     return TV_ERR_INVALID_ARG;
-  return from_hip(tv::launch_attention_bf16(a, plan, pk, stream));
+  return from_hip(tv::launch_attention_bf16(a, plan, pk, nullptr, stream));
 }
 
 tv_status tv_accept(const int32_t* cand_tok, const int32_t* tgt_argmax, const int32_t* parents,

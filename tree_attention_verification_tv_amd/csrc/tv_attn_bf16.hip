@@ -131,9 +131,10 @@ struct BfParams {
   uint16_t* v_cache;     // [B][Hkv][cap/64][D][64]
   const int32_t* prefix_len;
   const int32_t* n_nodes;
-  const uint64_t* anc;
-  const int32_t* depth;
+  uint64_t* anc;   // (outputs when parents is set)
+  int32_t* depth;
   int32_t* err;
+  const int32_t* parents;   // non-null: the kernel builds the tree itself and writes anc, depth, err
   uint16_t* out;
   uint4* part_o;     // split partials, 16-bit, register order (see the main epilogue)
   float2* part_ml;   // split (reference, row sum) per lane
@@ -301,6 +302,19 @@ __device__ __forceinline__ const int* uniform_ptr(const int* a) {
   const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
   const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
   return reinterpret_cast<const int*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+// (node count and prefix length only: a kernel that builds the tree itself
+// has no error word to read)
+__device__ __forceinline__ SeqState seq_state_scalar_ne(const BfParams& p, int b) {
+  int n, P;
+  asm volatile(
+      "s_load_dword %0, %2, 0x0\n\t"
+      "s_load_dword %1, %3, 0x0\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&s"(n), "=&s"(P)
+      : "s"(uniform_ptr(p.n_nodes + b)), "s"(uniform_ptr(p.prefix_len + b))
+      : "memory");
+  return make_seq_state(p, n, P, 0);
 }
 __device__ __forceinline__ SeqState seq_state_scalar(const BfParams& p, int b) {
   int n, P, e;
@@ -1037,8 +1051,14 @@ __device__ __forceinline__ void merge_claim_and_run(const BfParams& p, int grp, 
   }
 }
 
-template <int WAVES, int QT, bool PAGED>
+// BUILD: the kernel builds the sequence's tree from p.parents itself (each
+// wavefront, by build_tree_lane, from one load of the parent of node `lane`)
+// instead of loading depths and ancestor masks, and the workgroup (b, g = 0,
+// row block 0, split 0) writes anc, depth and err as tv_build_tree would
+// (err also TV_ERR_CAPACITY as below).
+template <int WAVES, int QT, bool PAGED, bool BUILD>
 __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
+  static_assert(!(PAGED && BUILD), "the tree is built in the dense instances only");
   constexpr int NT = WAVES * 64;
   constexpr int ROWS = WAVES * 32 * QT;      // query rows of the workgroup
   constexpr int CPT = (kKT * kD / 8) / NT;   // 16-byte chunks per thread per K (or V) stage
@@ -1100,13 +1120,19 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   }
   int my_row[QT];
   uint32_t qdep[QT];
+  uint32_t dep_lane = 0u, par_lane = 0u;
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
     my_row[t] = r0 + 32 * t + (lane & 31);
-    qdep[t] = ld_b32(p.depth + static_cast<size_t>(b) * p.n_max + min(static_cast<int>(p.gdiv.div(my_row[t])), p.n_max - 1));
+    if constexpr (!BUILD)
+      qdep[t] = ld_b32(p.depth + static_cast<size_t>(b) * p.n_max +
+                       min(static_cast<int>(p.gdiv.div(my_row[t])), p.n_max - 1));
   }
-  uint32_t dep_lane = ld_b32(p.depth + static_cast<size_t>(b) * p.n_max + min(lane, p.n_max - 1));
-  constexpr int kDepOps = QT + 1;
+  if constexpr (BUILD)
+    par_lane = ld_b32(p.parents + static_cast<size_t>(b) * p.n_max + min(lane, p.n_max - 1));
+  else
+    dep_lane = ld_b32(p.depth + static_cast<size_t>(b) * p.n_max + min(lane, p.n_max - 1));
+  constexpr int kDepOps = BUILD ? 1 : QT + 1;
   constexpr int QCPT = ROWS * kD / 8 / NT;              // query chunks per thread
   static_assert(ROWS * kD <= 4 * kStageElems, "query rows must fit the last two stages");
   const uint32_t lds_q = lds_base + 2u * kStageElems * 2u * (kStages - 2);
@@ -1121,18 +1147,37 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
     }
   }
 
-  const SeqState sq = seq_state_scalar(p, b);
+  const SeqState sq = BUILD ? seq_state_scalar_ne(p, b) : seq_state_scalar(p, b);
   const int n = sq.n, P = sq.P;
   const int rows_live = sq.skip ? 0 : G * n;
   const int rows_all = G * p.n_max;
-  if (sq.cap_bad && g == 0 && rb == 0 && s == 0 && tid == 0) p.err[b] = TV_ERR_CAPACITY;
+  const bool tree_writer = g == 0 && rb == 0 && s == 0;
+  if (!BUILD && sq.cap_bad && tree_writer && tid == 0) p.err[b] = TV_ERR_CAPACITY;
   // (every workgroup of b reads err: before or after this store, b is skipped)
+
+  // BUILD: wavefront 0 of the writing workgroup stores the sequence's tree
+  // (as tv_build_tree: zeros for padding nodes and invalid trees) and its
+  // error word (a bad tree, else a capacity error, else 0). Called once all
+  // loads have landed and nothing else is in flight.
+  auto write_tree = [&](const LaneTree& tr) __attribute__((always_inline)) {
+    if (BUILD && tree_writer && wave == 0) {
+      if (lane < p.n_max) {
+        p.anc[static_cast<size_t>(b) * p.n_max + lane] = tr.anc;
+        p.depth[static_cast<size_t>(b) * p.n_max + lane] = tr.depth;
+      }
+      if (lane == 0) p.err[b] = !tr.ok ? TV_ERR_BAD_TREE : sq.cap_bad ? TV_ERR_CAPACITY : 0;
+    }
+  };
 
   // A workgroup with nothing to compute: its loads land before its LDS is
   // given up; with separate split merging the merge kernel writes the zero
   // rows, else (one split, or the fused merge: split 0) it does.
   auto retire = [&](int first_row) __attribute__((always_inline)) {
     wait_vm<0>();
+    if constexpr (BUILD) {
+      landed(par_lane);
+      write_tree(build_tree_lane(static_cast<int>(par_lane), n, p.n_max, lane));
+    }
     if (p.splits == 1 || (p.fused && s == 0)) {
       for (int r = first_row + tid / 16; r < min(rb0 + ROWS, rows_all); r += NT / 16) {
         const int i = p.gdiv.div(r), head = g * G + r - i * G;
@@ -1174,12 +1219,12 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   // operations complete in order, so anything queued behind the copies would
   // wait for all of them).
   constexpr int KI = 8 * 64 / NT, VI = 16 * 64 / NT;   // tree items per thread: K pairs, V chunks
-  constexpr int kTreeOps = 3 * KI + VI + QT;
+  constexpr int kTreeOps = BUILD ? 2 * KI + VI : 3 * KI + VI + QT;
   // every loop bound above is the one the wait model counts
   static_assert(CPT == waits::tile_chunks(WAVES) && QCPT == waits::query_ops(WAVES, QT) &&
-                    kDepOps == waits::depth_ops(QT) && kPageOps == waits::page_ops(PAGED) &&
+                    kDepOps == waits::depth_ops(QT, BUILD) && kPageOps == waits::page_ops(PAGED) &&
                     KI == waits::tree_k_items(WAVES) && VI == waits::tree_v_items(WAVES) &&
-                    kTreeOps == waits::tree_ops(WAVES, QT),
+                    kTreeOps == waits::tree_ops(WAVES, QT, BUILD),
                 "the hand-counted waits follow tv_attn_waits.h");
   u32x4 tk_lo[KI], tk_hi[KI], tvv[VI];
   uint32_t t_dep[KI];
@@ -1191,8 +1236,10 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
       const uint16_t* ksrc = p.k_new + ((static_cast<size_t>(b) * p.n_max + node) * p.Hkv + g) * kD + 8 * c;
       tk_lo[u] = ASM ? ld_b128(ksrc) : *reinterpret_cast<const u32x4*>(ksrc);
       tk_hi[u] = ASM ? ld_b128(ksrc + 64) : *reinterpret_cast<const u32x4*>(ksrc + 64);
-      const uint32_t* dsrc = reinterpret_cast<const uint32_t*>(p.depth) + static_cast<size_t>(b) * p.n_max + node;
-      t_dep[u] = ASM ? ld_b32(dsrc) : *dsrc;
+      if constexpr (!BUILD) {
+        const uint32_t* dsrc = reinterpret_cast<const uint32_t*>(p.depth) + static_cast<size_t>(b) * p.n_max + node;
+        t_dep[u] = ASM ? ld_b32(dsrc) : *dsrc;
+      }
     }
 #pragma unroll
     for (int u = 0; u < VI; ++u) {
@@ -1200,10 +1247,13 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
       const uint16_t* vsrc = p.v_new + ((static_cast<size_t>(b) * p.n_max + node) * p.Hkv + g) * kD + 8 * c;
       tvv[u] = ASM ? ld_b128(vsrc) : *reinterpret_cast<const u32x4*>(vsrc);
     }
+    if constexpr (!BUILD) {
 #pragma unroll
-    for (int t = 0; t < QT; ++t) {
-      const uint64_t* asrc = p.anc + static_cast<size_t>(b) * p.n_max + min(static_cast<int>(p.gdiv.div(my_row[t])), p.n_max - 1);
-      my_anc[t] = ASM ? ld_b64(asrc) : *asrc;
+      for (int t = 0; t < QT; ++t) {
+        const uint64_t* asrc =
+            p.anc + static_cast<size_t>(b) * p.n_max + min(static_cast<int>(p.gdiv.div(my_row[t])), p.n_max - 1);
+        my_anc[t] = ASM ? ld_b64(asrc) : *asrc;
+      }
     }
   };
   if (n_masked > 0) load_tree(std::true_type{});
@@ -1295,7 +1345,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   // Tile 1 goes out once the query rows are in registers, tile 2 after the
   // RoPE, so that work overlaps the first tiles' transfer.
   // (every count below comes from the issue-order model in tv_attn_waits.h)
-  constexpr bool kGuard = waits::start_guard(WAVES, QT, PAGED);
+  constexpr bool kGuard = waits::start_guard(WAVES, QT, PAGED, BUILD);
   static_assert(kAhead == 3, "the start issues three tiles");
   if constexpr (kGuard) wait_vm<waits::vm_start_guard(WAVES)>();
   if constexpr (PAGED) {
@@ -1303,9 +1353,9 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
     // must name a page of the pools (all workgroups of b check alike), else
     // b is flagged and skipped
     if (n_masked > 0)
-      wait_vm<waits::vm_pages(WAVES, QT, true)>();
+      wait_vm<waits::vm_pages(WAVES, QT, BUILD, true)>();
     else
-      wait_vm<waits::vm_pages(WAVES, QT, false)>();
+      wait_vm<waits::vm_pages(WAVES, QT, BUILD, false)>();
     bool bad = false;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -1327,17 +1377,38 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   // the queries are still in flight.
   if constexpr (!kGuard) {
     if (n_masked > 0)
-      wait_vm<waits::vm_depths(WAVES, QT, true, true)>();
+      wait_vm<waits::vm_depths(WAVES, QT, BUILD, true, true)>();
     else if (n_tiles > 0)
-      wait_vm<waits::vm_depths(WAVES, QT, false, true)>();
+      wait_vm<waits::vm_depths(WAVES, QT, BUILD, false, true)>();
     else
-      wait_vm<waits::vm_depths(WAVES, QT, false, false)>();
+      wait_vm<waits::vm_depths(WAVES, QT, BUILD, false, false)>();
   } else {
     // (the guard above left an unknown count: wait for all but tile 0)
     if (n_tiles > 0)
       wait_vm<waits::vm_queries(WAVES, true)>();
     else
       wait_vm<waits::vm_queries(WAVES, false)>();
+  }
+  // BUILD: the tree from the parents (every wavefront alike); the rows' and
+  // the tree items' depths and the rows' ancestor masks come from it by
+  // shuffles. A bad tree retires every workgroup of the sequence.
+  LaneTree tree{0ull, 0, true};
+  if constexpr (BUILD) {
+    landed(par_lane);
+    tree = build_tree_lane(static_cast<int>(par_lane), n, p.n_max, lane);
+    if (!tree.ok) {
+      retire(rb0);
+      return;
+    }
+    dep_lane = static_cast<uint32_t>(tree.depth);
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+      const int node = min(static_cast<int>(p.gdiv.div(my_row[t])), p.n_max - 1);
+      qdep[t] = static_cast<uint32_t>(__shfl(tree.depth, node));
+      my_anc[t] = shfl_u64(tree.anc, node);
+    }
+#pragma unroll
+    for (int u = 0; u < KI; ++u) t_dep[u] = static_cast<uint32_t>(__shfl(tree.depth, min((tid + NT * u) >> 3, n - 1)));
   }
 #pragma unroll
   for (int t = 0; t < QT; ++t) landed(qdep[t]);
@@ -1699,6 +1770,8 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
     run_pass(std::integral_constant<int, 2>{});
   }
 
+  if constexpr (BUILD) write_tree(tree);   // (nothing is in flight here)
+
   // ---- epilogue
   float l_row[QT];
 #pragma unroll
@@ -2028,7 +2101,7 @@ static DivUs make_divus(uint32_t d, uint64_t x_end) {
 }
 
 hipError_t launch_attention_bf16(const tv_attn_args* a, const AttnPlan& pl, const tv_paged_kv* pk,
-                                 hipStream_t s) {
+                                 const int32_t* parents, hipStream_t s) {
   BfParams p;
   p.q = static_cast<const uint16_t*>(a->q);
   p.k_new = static_cast<const uint16_t*>(a->k_new);
@@ -2037,8 +2110,9 @@ hipError_t launch_attention_bf16(const tv_attn_args* a, const AttnPlan& pl, cons
   p.v_cache = static_cast<uint16_t*>(a->v_cache);
   p.prefix_len = a->prefix_len;
   p.n_nodes = a->n_nodes;
-  p.anc = a->anc;
-  p.depth = a->depth;
+  p.anc = const_cast<uint64_t*>(a->anc);
+  p.depth = const_cast<int32_t*>(a->depth);
+  p.parents = parents;
   p.err = a->err;
   p.out = static_cast<uint16_t*>(a->out);
   p.n_max = a->n_max;
@@ -2078,13 +2152,17 @@ hipError_t launch_attention_bf16(const tv_attn_args* a, const AttnPlan& pl, cons
   const int wg_rows = pl.waves * 32 * pl.qt;
   dim3 mgrid(pl.row_blocks * wg_rows / 32 + 1, a->Hkv, a->B);   // (+ the value-append block)
   const int key = pl.waves * 10 + pl.qt;
-  switch (key + (pk ? 100 : 0)) {
-    case 21: hipLaunchKernelGGL((attn_bf16_kernel<2, 1, false>), grid, dim3(128), 0, s, p); break;
-    case 41: hipLaunchKernelGGL((attn_bf16_kernel<4, 1, false>), grid, dim3(256), 0, s, p); break;
-    case 42: hipLaunchKernelGGL((attn_bf16_kernel<4, 2, false>), grid, dim3(256), 0, s, p); break;
-    case 121: hipLaunchKernelGGL((attn_bf16_kernel<2, 1, true>), grid, dim3(128), 0, s, p); break;
-    case 141: hipLaunchKernelGGL((attn_bf16_kernel<4, 1, true>), grid, dim3(256), 0, s, p); break;
-    default: hipLaunchKernelGGL((attn_bf16_kernel<4, 2, true>), grid, dim3(256), 0, s, p); break;
+  switch (key + (pk ? 100 : 0) + (parents ? 200 : 0)) {
+    case 21: hipLaunchKernelGGL((attn_bf16_kernel<2, 1, false, false>), grid, dim3(128), 0, s, p); break;
+    case 41: hipLaunchKernelGGL((attn_bf16_kernel<4, 1, false, false>), grid, dim3(256), 0, s, p); break;
+    case 42: hipLaunchKernelGGL((attn_bf16_kernel<4, 2, false, false>), grid, dim3(256), 0, s, p); break;
+    case 121: hipLaunchKernelGGL((attn_bf16_kernel<2, 1, true, false>), grid, dim3(128), 0, s, p); break;
+    case 141: hipLaunchKernelGGL((attn_bf16_kernel<4, 1, true, false>), grid, dim3(256), 0, s, p); break;
+    case 142: hipLaunchKernelGGL((attn_bf16_kernel<4, 2, true, false>), grid, dim3(256), 0, s, p); break;
+    case 221: hipLaunchKernelGGL((attn_bf16_kernel<2, 1, false, true>), grid, dim3(128), 0, s, p); break;
+    case 241: hipLaunchKernelGGL((attn_bf16_kernel<4, 1, false, true>), grid, dim3(256), 0, s, p); break;
+    case 242: hipLaunchKernelGGL((attn_bf16_kernel<4, 2, false, true>), grid, dim3(256), 0, s, p); break;
+    default: return hipErrorInvalidValue;   // (a paged cache with a parents array: refused by the host checks)
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

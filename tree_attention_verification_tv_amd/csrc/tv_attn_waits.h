@@ -10,8 +10,10 @@
 //
 // Issue order, per thread:
 //   start   [the sequence's page ids (paged caches)], the depths of the
-//           wavefront's rows' nodes and of node `lane`, the query copies,
-//           [the tree's keys, values and depths and the rows' ancestor masks,
+//           wavefront's rows' nodes and of node `lane` (or, when the kernel
+//           builds the tree itself, the parent of node `lane`), the query
+//           copies, [the tree's keys, values and depths and the rows'
+//           ancestor masks (keys and values only when it builds the tree),
 //           when the split holds tree tiles], then tile 0; tiles 1 and 2 go
 //           out once the queries have landed;
 //   pass    before the tree fill (splits holding tree tiles) the tree tiles
@@ -39,32 +41,35 @@ constexpr int threads(int waves) { return waves * 64; }
 constexpr int tile_chunks(int waves) { return kKeys * kDim * 2 / 16 / threads(waves); }
 constexpr int tile_ops(int waves) { return 2 * tile_chunks(waves); }
 constexpr int page_ops(bool paged) { return paged ? 4 : 0; }
-constexpr int depth_ops(int qt) { return qt + 1; }
+constexpr int depth_ops(int qt, bool build) { return build ? 1 : qt + 1; }
 constexpr int query_ops(int waves, int qt) { return waves * 32 * qt * kDim / 8 / threads(waves); }
 // tree items per thread: 16-byte key pairs (8 per node) and value chunks (16 per node)
 constexpr int tree_k_items(int waves) { return 8 * 64 / threads(waves); }
 constexpr int tree_v_items(int waves) { return 16 * 64 / threads(waves); }
 // two loads per key pair plus its node's depth, one per value chunk, one
-// ancestor mask per query tile
-constexpr int tree_ops(int waves, int qt) { return 3 * tree_k_items(waves) + tree_v_items(waves) + qt; }
-constexpr int start_ops(int waves, int qt, bool paged, bool tree) {
-  return page_ops(paged) + depth_ops(qt) + query_ops(waves, qt) + (tree ? tree_ops(waves, qt) : 0);
+// ancestor mask per query tile (depths and masks are not loaded when the
+// kernel builds the tree)
+constexpr int tree_ops(int waves, int qt, bool build) {
+  return build ? 2 * tree_k_items(waves) + tree_v_items(waves) : 3 * tree_k_items(waves) + tree_v_items(waves) + qt;
+}
+constexpr int start_ops(int waves, int qt, bool paged, bool build, bool tree) {
+  return page_ops(paged) + depth_ops(qt, build) + query_ops(waves, qt) + (tree ? tree_ops(waves, qt, build) : 0);
 }
 
 // If the start's operations and tile 0 could overflow the counter, enough of
 // the former land first (no instantiation needs it today).
-constexpr bool start_guard(int waves, int qt, bool paged) {
-  return start_ops(waves, qt, paged, true) + tile_ops(waves) > kMaxCount;
+constexpr bool start_guard(int waves, int qt, bool paged, bool build) {
+  return start_ops(waves, qt, paged, build, true) + tile_ops(waves) > kMaxCount;
 }
 constexpr int vm_start_guard(int waves) { return kMaxCount - tile_ops(waves); }
 
 // The page ids (the oldest operations) have landed, tile 0 not yet issued.
-constexpr int vm_pages(int waves, int qt, bool tree) {
-  return depth_ops(qt) + query_ops(waves, qt) + (tree ? tree_ops(waves, qt) : 0);
+constexpr int vm_pages(int waves, int qt, bool build, bool tree) {
+  return depth_ops(qt, build) + query_ops(waves, qt) + (tree ? tree_ops(waves, qt, build) : 0);
 }
-// The depths have landed (after tile 0, if the split has tiles).
-constexpr int vm_depths(int waves, int qt, bool tree, bool tile0) {
-  return query_ops(waves, qt) + (tree ? tree_ops(waves, qt) : 0) + (tile0 ? tile_ops(waves) : 0);
+// The depths (or parents) have landed (after tile 0, if the split has tiles).
+constexpr int vm_depths(int waves, int qt, bool build, bool tree, bool tile0) {
+  return query_ops(waves, qt) + (tree ? tree_ops(waves, qt, build) : 0) + (tile0 ? tile_ops(waves) : 0);
 }
 // Everything of the start has landed, only tile 0 may be in flight.
 constexpr int vm_queries(int waves, bool tile0) { return tile0 ? tile_ops(waves) : 0; }

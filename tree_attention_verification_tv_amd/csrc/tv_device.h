@@ -42,4 +42,42 @@ __device__ __forceinline__ int wave_max_i32(int v) {
              max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
 
+// The tree of one sequence by one wavefront, lane i = node i, every lane
+// active (infra-guide "5.3 Medusa、EAGLE 与 MTP", sections 3.1, 3.2 and 8):
+// the node's ancestors-or-self bitmask and depth by pointer jumping, and
+// whether the sequence's parents array is a parents-first tree. p_in is
+// parents[i] (any value for i >= n), n the sequence's node count.
+//
+// Each lane keeps (J, A): J is an ancestor of node i (initially its parent),
+// A the set of nodes from i up to but excluding J. One round replaces J by
+// J's own J and merges A, so after round r, J is the 2^r-th ancestor; six
+// rounds cover any depth below 64, and the rounds stop once no lane has an
+// ancestor left (three for depths up to 7). The depth is then |A| - 1.
+// Nodes past n, and every node of an invalid tree, get A = 0 and depth 0.
+struct LaneTree {
+  uint64_t anc;
+  int depth;
+  bool ok;   // the whole sequence's tree is valid (uniform)
+};
+__device__ __forceinline__ LaneTree build_tree_lane(int p_in, int n, int n_max, int i) {
+  const bool n_ok = (n >= 0) && (n <= n_max);
+  const bool live = n_ok && (i < n);
+  const int p = live ? p_in : -1;
+  const bool ok_i = !live || (i == 0 ? (p == -1) : (p >= 0 && p < i));
+  const bool tree_ok = n_ok && __all(ok_i);
+  int J = (live && tree_ok) ? p : -1;
+  uint64_t A = live ? (1ull << i) : 0ull;
+  for (int r = 0; r < 6 && __any(J >= 0); ++r) {
+    const int src = (J >= 0) ? J : i;
+    const uint64_t A_src = shfl_u64(A, src);
+    const int J_src = __shfl(J, src);
+    if (J >= 0) {
+      A |= A_src;
+      J = J_src;
+    }
+  }
+  const bool keep = live && tree_ok;
+  return LaneTree{keep ? A : 0ull, keep ? __popcll(A) - 1 : 0, tree_ok};
+}
+
 }  // namespace tv

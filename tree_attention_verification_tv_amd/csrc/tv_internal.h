@@ -67,9 +67,10 @@ struct AttnPlan {
 
 AttnPlan plan_attention_bf16(const tv_attn_args* a);
 
-// pk: paged cache (nullptr: the dense layout)
+// pk: paged cache (nullptr: the dense layout); parents (dense only): the
+// kernel builds the tree from it and writes a->anc, a->depth and a->err
 hipError_t launch_attention_bf16(const tv_attn_args* a, const AttnPlan& plan, const tv_paged_kv* pk,
-                                 hipStream_t s);
+                                 const int32_t* parents, hipStream_t s);
 hipError_t launch_attention_f32(const tv_attn_args* a, hipStream_t s);
 
 // Bytes of the static device scratch behind tv_tree_attention_noalloc (every

@@ -12,13 +12,8 @@
 namespace tv {
 
 // ---------------------------------------------------------------------------
-// build_tree: ancestors-or-self bitmask and depth by pointer jumping.
-//
-// Each lane keeps (J, A, d): J is an ancestor of node i (initially its
-// parent), A the set of nodes from i up to but excluding J, d the number of
-// edges from i to J (or the depth once J == -1). One round replaces J by J's
-// own J and merges A and d, so after round r, J is the 2^r-th ancestor; six
-// rounds cover any depth below 64.
+// build_tree: ancestors-or-self bitmask and depth by pointer jumping
+// (build_tree_lane), one wavefront per sequence.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void build_tree_kernel(const int32_t* __restrict__ parents,
                                                         const int32_t* __restrict__ n_nodes,
@@ -30,33 +25,12 @@ __global__ __launch_bounds__(64) void build_tree_kernel(const int32_t* __restric
   // (the parent load does not wait for the node count: one memory round trip)
   const int p_in = i < n_max ? parents[static_cast<size_t>(b) * n_max + i] : -1;
   const int n = n_nodes[b];
-  const bool n_ok = (n >= 0) && (n <= n_max);
-  const bool live = n_ok && (i < n);
-  const int p = live ? p_in : -1;
-  const bool ok_i = !live || (i == 0 ? (p == -1) : (p >= 0 && p < i));
-  const bool tree_ok = n_ok && __all(ok_i);
-
-  int J = (live && tree_ok) ? p : -1;
-  uint64_t A = live ? (1ull << i) : 0ull;
-  int d = (J >= 0) ? 1 : 0;
-#pragma unroll
-  for (int r = 0; r < 6; ++r) {
-    const int src = (J >= 0) ? J : i;
-    const uint64_t A_src = shfl_u64(A, src);
-    const int d_src = __shfl(d, src);
-    const int J_src = __shfl(J, src);
-    if (J >= 0) {
-      A |= A_src;
-      d += d_src;
-      J = J_src;
-    }
-  }
+  const LaneTree t = build_tree_lane(p_in, n, n_max, i);
   if (i < n_max) {
-    const bool keep = live && tree_ok;
-    anc[static_cast<size_t>(b) * n_max + i] = keep ? A : 0ull;
-    depth[static_cast<size_t>(b) * n_max + i] = keep ? d : 0;
+    anc[static_cast<size_t>(b) * n_max + i] = t.anc;
+    depth[static_cast<size_t>(b) * n_max + i] = t.depth;
   }
-  if (i == 0) err[b] = tree_ok ? 0 : static_cast<int32_t>(TV_ERR_BAD_TREE);
+  if (i == 0) err[b] = t.ok ? 0 : static_cast<int32_t>(TV_ERR_BAD_TREE);
 }
 
 // ---------------------------------------------------------------------------
