@@ -118,6 +118,22 @@ def load_traffic(workload: str):
     return rec.get("bytes_per_launch")
 
 
+def device_warmup(step, seconds: float) -> float:
+    """Runs step(k) until `seconds` of wall clock have passed (synchronising
+    every 64 calls) and returns the time spent. The device's clocks take tens
+    of milliseconds of load to settle: the first ~50 ms of attention calls
+    measured 7% slower than the rest. This precedes the W warmup steps."""
+    import torch
+    t0 = time.perf_counter()
+    k = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(64):
+            step(k)
+            k += 1
+        torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
 def cpu_baseline(w, budget_s: float = 12.0, paged: bool = False) -> dict:
     """The oracle, as it is, on whole sequences of the same workload until
     about budget_s seconds of CPU work; one BLAS thread. paged: each
@@ -256,6 +272,7 @@ def bench_typical(args) -> None:
         if lib.tv_accept_typical(*heads[k % copies], *tail):
             raise RuntimeError("tv_accept_typical failed")
 
+    warm_s = device_warmup(step, args.device_warmup)
     for k in range(args.warmup):
         step(k)
     torch.cuda.synchronize()
@@ -281,6 +298,7 @@ def bench_typical(args) -> None:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "device_warmup_s": round(warm_s, 3),
         "ms_per_step": (t1 - t0) * 1e3 / args.steps,
         "higher_is_better": True,
         "scaling": "weak",
@@ -335,6 +353,7 @@ def bench_draft_tree(args) -> None:
         if lib.tv_eagle2_tree(*call):
             raise RuntimeError("tv_eagle2_tree failed")
 
+    warm_s = device_warmup(lambda k: step(), args.device_warmup)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -367,6 +386,7 @@ def bench_draft_tree(args) -> None:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "device_warmup_s": round(warm_s, 3),
         "ms_per_step": (t1 - t0) * 1e3 / args.steps,
         "higher_is_better": True,
         "scaling": "weak",
@@ -429,6 +449,7 @@ def bench_spec_sample(args) -> None:
         if lib.tv_speculative_sample(P(pp), P(qq), tv._lib.TV_BF16, V, *tail):
             raise RuntimeError("tv_speculative_sample failed")
 
+    warm_s = device_warmup(step, args.device_warmup)
     for k in range(args.warmup):
         step(k)
     torch.cuda.synchronize()
@@ -454,6 +475,7 @@ def bench_spec_sample(args) -> None:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "device_warmup_s": round(warm_s, 3),
         "ms_per_step": (t1 - t0) * 1e3 / args.steps,
         "higher_is_better": True,
         "scaling": "weak",
@@ -493,6 +515,8 @@ def main() -> None:
     ap.add_argument("--config", type=int, default=3, help="workload 1..5 (3 = headline)")
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated per step (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--device-warmup", type=float, default=0.3,
+                    help="seconds of untimed steps before the W warmup steps (the clocks settle)")
     ap.add_argument("--separate-tree", action="store_true",
                     help="dense step with tv_build_tree + tv_tree_attention instead of the combined call")
     ap.add_argument("--seed", type=int, default=None)
@@ -630,6 +654,7 @@ def main() -> None:
         if st:
             raise RuntimeError(f"library call failed with status {st}")
 
+    warm_s = device_warmup(step, args.device_warmup)
     for k in range(args.warmup):
         step(k)
     torch.cuda.synchronize()
@@ -687,6 +712,7 @@ def main() -> None:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "device_warmup_s": round(warm_s, 3),
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",

@@ -63,13 +63,14 @@
 //   merge  with several splits, each writes (reference, row sum) in fp32
 //          and its output divided by the row sum in 16 bits (fp16, or bf16
 //          for a row beyond fp16's range) to the workspace in register order;
-//          the merge combines them in split order (deterministic) with fp32
-//          weights and sums and writes the rows.
-//          It also appends the tree to cache slots P + i (keys rotated in the
-//          same rounding order as in LDS); with one split a small kernel does
-//          only that. The attention kernel never reads those slots back, and
-//          stores issued between its tile copies would delay every later
-//          wait for a tile.
+//          the merge (inside this kernel when the grid runs at once, else a
+//          kernel of its own) combines them in split order (deterministic)
+//          with fp32 weights and sums and writes the rows.
+//   append row block 0 of the split holding the tree tiles appends the tree
+//          to cache slots P + i (the keys as rotated for the tiles, the raw
+//          values) after its last tile: no workgroup of the call reads those
+//          slots back, and stores issued between the tile copies would
+//          delay every later wait for a tile.
 //
 // RoPE angles: a table entry forms pos * 2^(-2j/D log2 theta) in double
 // precision, reduces it to [-pi, pi] and takes a single-precision sincos.
@@ -706,14 +707,7 @@ __device__ __forceinline__ void write_rows(const BfParams& p, int b, int g, int 
 }
 
 // ---------------------------------------------------------------------------
-// tree append: cache slot P + i receives node i's key, rotated at
-// P + depth(i) exactly as the attention kernel rotated it in LDS, and its
-// value. Thread it of nthreads (a multiple of 64) for head (b, g) takes key
-// pairs k = it, it + nthreads, ... (node k/64, dims k%64 and 64 + k%64), two
-// at a time with both pairs' loads issued before either is used, so
-// consecutive lanes write consecutive cache addresses; the values go through
-// one block of their own per head. It runs after the attention kernel, which
-// never reads these slots back.
+// tree append helpers
 // ---------------------------------------------------------------------------
 // Element offsets of the (at most two) 64-slot blocks that hold a tree's
 // slots [P, P + n) for KV head (b, g), n <= 64: the dense cache's blocks, or
@@ -742,87 +736,6 @@ __device__ __forceinline__ TreeBlocks tree_blocks(const BfParams& p, int b, int 
   return t;
 }
 
-struct KeyPairs {
-  uint16_t xl[2], xh[2];
-  int dep[2];
-};
-// Loads the two key pairs k0, k0 + nthreads (clamped to the n_max rows of
-// k_new, not to n, so that they need not wait for the node count).
-__device__ __forceinline__ KeyPairs load_keys(const BfParams& p, int b, int g, int k0, int nthreads) {
-  KeyPairs kp;
-  const int j = k0 & 63;
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int i = min((k0 + u * nthreads) >> 6, p.n_max - 1);
-    const uint16_t* src = p.k_new + ((static_cast<size_t>(b) * p.n_max + i) * p.Hkv + g) * kD;
-    kp.xl[u] = src[j];
-    kp.xh[u] = src[64 + j];
-    kp.dep[u] = p.depth[static_cast<size_t>(b) * p.n_max + i];
-  }
-  return kp;
-}
-// Rotates and stores the loaded pairs, then loads and stores the thread's
-// further pairs (k0 += 2 nthreads) until n * 64.
-__device__ __forceinline__ void append_keys(const BfParams& p, const SeqState& sq, int b, int g, int it,
-                                            int nthreads, KeyPairs kp) {
-  if (sq.skip) return;
-  const int j = it & 63;   // the same dimension pair for every k of this thread
-  const TreeBlocks tb = tree_blocks(p, b, g, sq.P);
-  const double freq = p.rope ? rope_freq(p.log2_theta, j) : 0.0;
-  for (int k0 = it; k0 < sq.n * 64; k0 += 2 * nthreads) {
-    if (k0 != it) kp = load_keys(p, b, g, k0, nthreads);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int k = k0 + u * nthreads;
-      if (k >= sq.n * 64) break;
-      const int i = k >> 6;
-      const float l = bf16_bits_to_f32(kp.xl[u]), h = bf16_bits_to_f32(kp.xh[u]);
-      const float2 cs = p.rope ? rope_cs(sq.P + clamp_depth(kp.dep[u]), freq) : make_float2(1.0f, 0.0f);
-      const uint32_t w = pack_bf16(rope_lo(l, h, cs) * 1.0f, rope_hi(l, h, cs) * 1.0f);
-      const int slot = sq.P + i;
-      uint16_t* dst = p.k_cache + tb.of(slot) + static_cast<size_t>(slot & 63) * kD;
-      dst[j] = static_cast<uint16_t>(w & 0xFFFFu);
-      dst[64 + j] = static_cast<uint16_t>(w >> 16);
-    }
-  }
-}
-__device__ __forceinline__ void write_tree_values(const BfParams& p, int P, int n, const TreeBlocks& tb,
-                                                  const uint4* vtr, int tid, int nthreads);
-__device__ __forceinline__ void append_values(const BfParams& p, int b, int g, uint4* vtr) {
-  // Values (a block of their own per KV head): node rows are read as whole
-  // 16-byte chunks (all of a thread's loads in flight together, clamped to
-  // the n_max rows of v_new so that they need not wait for the node count:
-  // at most TV_MAX_NODES_DEV * 16 = 4 * 256 chunks) and staged in LDS as
-  // [node][chunk], chunk c of node i at position c ^ (i % 16) (both passes
-  // then touch every bank once per 16 lanes). A thread then takes one chunk
-  // (8 head dims) of one aligned unit of 8 slots touching [P, P + n), gathers
-  // the unit's nodes, and writes the 8 dims' rows of consecutive slots as the
-  // blocked cache holds them: one 16-byte store per dim for a unit inside
-  // [P, P + n), single elements at the ends.
-  static_assert(TV_MAX_NODES_DEV * (kD / 8) == 4 * 256, "four value chunks per thread");
-  // (the loads are issued from assembly and the sequence state is read by
-  // the scalar loader after them, so neither waits for the other)
-  const int tid = threadIdx.x;
-  u32x4 v4[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int i = min((tid + 256 * u) >> 4, p.n_max - 1), c = tid & 15;
-    v4[u] = ld_b128(p.v_new + ((static_cast<size_t>(b) * p.n_max + i) * p.Hkv + g) * kD + 8 * c);
-  }
-  const SeqState sq = seq_state_scalar(p, b);
-  wait_vm<0>();
-  if (sq.skip) return;
-  const int n = sq.n, P = sq.P;
-  const TreeBlocks tb = tree_blocks(p, b, g, P);
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    landed(v4[u]);
-    const int i = (tid >> 4) + 16 * u, c = tid & 15;   // item tid + 256 u
-    vtr[i * 16 + (c ^ (i & 15))] = make_uint4(v4[u][0], v4[u][1], v4[u][2], v4[u][3]);
-  }
-  __syncthreads();
-  write_tree_values(p, P, n, tb, vtr, tid, 256);
-}
 // The write half of the value append: vtr holds the tree's value chunks as
 // [node][chunk] (chunk c of node i at position c ^ (i % 16)); thread it of
 // nthreads takes (chunk, 8-slot unit) pairs and writes the unit's 8 head-dim
@@ -1525,6 +1438,30 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
       vtr[node * 16 + (c ^ (node & 15))] = make_uint4(tvv[u][0], tvv[u][1], tvv[u][2], tvv[u][3]);
     }
   };
+  // The tree's append to the cache (a2), by row block 0 of the split that
+  // holds the tree tiles, once its ring is idle: the rotated keys straight
+  // from the lane items, the raw values through the [node][chunk] transpose
+  // in stage 3. The slots [P, P + n) it writes are read by no workgroup of
+  // this call (the tree tiles take their tree rows from these registers, and
+  // whatever their copies read past P is overwritten or zeroed in LDS).
+  // Every thread of the workgroup calls it (it holds a barrier).
+  const bool appends = n_masked > 0 && !sq.skip && rb == 0;
+  auto append_tree = [&]() __attribute__((always_inline)) {
+    const TreeBlocks tb = tree_blocks(p, b, g, P);
+#pragma unroll
+    for (int u = 0; u < KI; ++u) {
+      const int item = tid + NT * u, node = item >> 3, c = item & 7;
+      if (node < n) {
+        const int slot = P + node;
+        uint16_t* dst = p.k_cache + tb.of(slot) + static_cast<size_t>(slot & 63) * kD + 8 * c;
+        *reinterpret_cast<u32x4*>(dst) = tk_lo[u];
+        *reinterpret_cast<u32x4*>(dst + 64) = tk_hi[u];
+      }
+    }
+    stage_tree_values();
+    __syncthreads();
+    write_tree_values(p, P, n, tb, vtr, tid, NT);
+  };
   auto fill_tree = [&](int pos) __attribute__((always_inline)) {
     const int kt0 = tile_k0(pos), off = P - kt0;   // tile key k holds node k - off (k >= off)
     uint16_t* kd = Ks(pos % kStages);
@@ -1776,15 +1713,6 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   float l_row[QT];
 #pragma unroll
   for (int t = 0; t < QT; ++t) l_row[t] = row_sum2(st[t].l);
-  if (p.splits == 1) {
-    f32x16 o[QT][4];
-#pragma unroll
-    for (int t = 0; t < QT; ++t)
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) o[t][dt] = st[t].o[dt];
-    write_rows<QT>(p, b, g, r0, rows_live, rows_all, lane, o, l_row);
-    return;
-  }
   // Split partial, per row: the output divided by the split's row sum (a
   // convex combination of value rows, so bounded by the largest value
   // element), as 16-bit floats: fp16 when the largest magnitude of every row
@@ -1796,115 +1724,98 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   // block (elements 8j .. 8j + 7 of the lane's dt accumulator); the (r, +-l)
   // pair of (wave, t) for lane l at ((wave * QT + t) * 64 + l). Blocks are
   // ordered (b, g, rb, s).
-  const size_t wg_id = ((static_cast<size_t>(b) * p.Hkv + g) * p.row_blocks + rb) * p.splits + s;
-  const __amdgpu_buffer_rsrc_t rml = ws_rsrc(p.part_ml, p.ws_bytes), ro = ws_rsrc(p.part_o, p.ws_bytes);
-  uint4* po = p.part_o + wg_id * (ROWS * 16) + wave * (QT * 8 * 64) + lane;
-  float2* pm = p.part_ml + wg_id * (ROWS * 2) + wave * (QT * 64) + lane;
   // (rows past the live ones are never read by the merge). For the merge
   // kernel the partials are stored non-temporally: each is read once, by the
   // merge, and keeping them out of the way in L2 shortens the whole call by
   // about 3% on the 8-sequence, 4096-token workload. For the fused merge they
   // are stored agent-coherently: another compute unit, possibly on another
   // XCD, reads them while this kernel runs.
+  // The epilogue has one call site of the tree append, whichever way the
+  // rows go (a second call site made the compiler keep the tile copies'
+  // uniform base addresses in vector registers).
+  const bool fused_merge = p.splits > 1 && p.fused;
+  const size_t wg_id = ((static_cast<size_t>(b) * p.Hkv + g) * p.row_blocks + rb) * p.splits + s;
+  const __amdgpu_buffer_rsrc_t rml = ws_rsrc(p.part_ml, p.ws_bytes), ro = ws_rsrc(p.part_o, p.ws_bytes);
+  if (p.splits == 1) {
+    f32x16 o[QT][4];
 #pragma unroll
-  for (int t = 0; t < QT; ++t) {
-    if (!row_live[t]) continue;
-    const float inv = l_row[t] > 0.0f ? 1.0f / l_row[t] : 0.0f;
-    float amax = 0.0f;
+    for (int t = 0; t < QT; ++t)
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+      for (int dt = 0; dt < 4; ++dt) o[t][dt] = st[t].o[dt];
+    write_rows<QT>(p, b, g, r0, rows_live, rows_all, lane, o, l_row);
+  } else {
+    uint4* po = p.part_o + wg_id * (ROWS * 16) + wave * (QT * 8 * 64) + lane;
+    float2* pm = p.part_ml + wg_id * (ROWS * 2) + wave * (QT * 64) + lane;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        st[t].o[dt][e] *= inv;
-        amax = fmaxf(amax, fabsf(st[t].o[dt][e]));
-      }
-    const bool use_f16 = __all(row_max2(amax) < 32768.0f);   // (over the tile's live rows)
-    auto store16 = [&](auto f16_tag) __attribute__((always_inline)) {
+    for (int t = 0; t < QT; ++t) {
+      if (!row_live[t]) continue;
+      const float inv = l_row[t] > 0.0f ? 1.0f / l_row[t] : 0.0f;
+      float amax = 0.0f;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          uint32_t w[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const float x0 = st[t].o[dt][8 * j + 2 * u], x1 = st[t].o[dt][8 * j + 2 * u + 1];
-            w[u] = decltype(f16_tag)::value ? pack_f16(x0, x1) : pack_bf16(x0, x1);
-          }
-          const u32x4 x = {w[0], w[1], w[2], w[3]};
-          uint4* dst = po + (t * 8 + dt * 2 + j) * 64;
-          if (p.fused)
-            __builtin_amdgcn_raw_buffer_store_b128(x, ro, static_cast<int>((dst - p.part_o) * 16), 0, kCoherent);
-          else
-            __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(dst));
+        for (int e = 0; e < 16; ++e) {
+          st[t].o[dt][e] *= inv;
+          amax = fmaxf(amax, fabsf(st[t].o[dt][e]));
         }
-    };
-    if (use_f16)
-      store16(std::true_type{});
-    else
-      store16(std::false_type{});
-    // A row that saw no key in this split (an empty split, or one whose
-    // keys are all invisible to it) has row sum 0 and stores the reference
-    // -inf, so that the merge leaves it out of the largest reference.
-    const f32x2 m = {l_row[t] > 0.0f ? st[t].r : -INFINITY, use_f16 ? l_row[t] : -l_row[t]};
-    if (p.fused) {
-      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, m), rml,
-                                            static_cast<int>((pm + t * 64 - p.part_ml) * 8), 0, kCoherent);
-    } else {
-      __builtin_nontemporal_store(m, reinterpret_cast<f32x2*>(pm + t * 64));
-    }
-  }
-  if (!p.fused) return;   // the merge kernel follows
-
-  // ---- fused merge (merge_in_kernel): publish, arrive, claim, merge; the
-  // workgroup holding the tree appends it to the cache meanwhile
-  wait_vm<0>();          // this wavefront's partials are performed
-  __syncthreads();
-  uint32_t* const words = reinterpret_cast<uint32_t*>(smem);   // (the ring is idle now)
-  const int grp = (b * p.Hkv + g) * p.row_blocks + rb;
-  merge_arrive(p, grp, words);
-  if (n_masked > 0 && !sq.skip) {
-    // rotated tree keys straight from the lane items; values through the
-    // [node][chunk] transpose in stage 3 (as the merge kernel's append)
-    const TreeBlocks tb = tree_blocks(p, b, g, P);
+      const bool use_f16 = __all(row_max2(amax) < 32768.0f);   // (over the tile's live rows)
+      auto store16 = [&](auto f16_tag) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < KI; ++u) {
-      const int item = tid + NT * u, node = item >> 3, c = item & 7;
-      if (node < n) {
-        const int slot = P + node;
-        uint16_t* dst = p.k_cache + tb.of(slot) + static_cast<size_t>(slot & 63) * kD + 8 * c;
-        *reinterpret_cast<u32x4*>(dst) = tk_lo[u];
-        *reinterpret_cast<u32x4*>(dst + 64) = tk_hi[u];
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            uint32_t w[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const float x0 = st[t].o[dt][8 * j + 2 * u], x1 = st[t].o[dt][8 * j + 2 * u + 1];
+              w[u] = decltype(f16_tag)::value ? pack_f16(x0, x1) : pack_bf16(x0, x1);
+            }
+            const u32x4 x = {w[0], w[1], w[2], w[3]};
+            uint4* dst = po + (t * 8 + dt * 2 + j) * 64;
+            if (p.fused)
+              __builtin_amdgcn_raw_buffer_store_b128(x, ro, static_cast<int>((dst - p.part_o) * 16), 0, kCoherent);
+            else
+              __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(dst));
+          }
+      };
+      if (use_f16)
+        store16(std::true_type{});
+      else
+        store16(std::false_type{});
+      // A row that saw no key in this split (an empty split, or one whose
+      // keys are all invisible to it) has row sum 0 and stores the reference
+      // -inf, so that the merge leaves it out of the largest reference.
+      const f32x2 m = {l_row[t] > 0.0f ? st[t].r : -INFINITY, use_f16 ? l_row[t] : -l_row[t]};
+      if (p.fused) {
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, m), rml,
+                                              static_cast<int>((pm + t * 64 - p.part_ml) * 8), 0, kCoherent);
+      } else {
+        __builtin_nontemporal_store(m, reinterpret_cast<f32x2*>(pm + t * 64));
       }
     }
-    stage_tree_values();
-    __syncthreads();
-    write_tree_values(p, P, n, tb, vtr, tid, NT);
   }
+  uint32_t* const words = reinterpret_cast<uint32_t*>(smem);   // (the ring is idle after the barrier)
+  const int grp = (b * p.Hkv + g) * p.row_blocks + rb;
+  if (fused_merge) {
+    // ---- fused merge (merge_in_kernel): publish, arrive, claim, merge; the
+    // workgroup holding the tree appends it to the cache in between
+    wait_vm<0>();          // this wavefront's partials are performed
+    __syncthreads();
+    merge_arrive(p, grp, words);
+  } else if (appends) {
+    __syncthreads();       // every wavefront is done with the ring
+  }
+  if (appends) append_tree();
+  if (!fused_merge) return;   // (with several splits the merge kernel follows)
   __syncthreads();
   merge_claim_and_run<WAVES, QT>(p, grp, s, b, g, rb, rows_live, words, rml, ro);
 }
 
-// With one split there is no merge: the append runs alone, grid
-// (kAppendBlocks, Hkv, B), 256 threads.
-constexpr int kAppendBlocks = 32;
-// Block 0 of each KV head appends the values (it is dispatched first).
-__global__ __launch_bounds__(256) void append_bf16_kernel(BfParams p) {
-  __shared__ uint4 vtr[TV_MAX_NODES_DEV * 16];
-  if (blockIdx.x == 0) {
-    append_values(p, blockIdx.z, blockIdx.y, vtr);
-  } else {
-    const int it = (blockIdx.x - 1) * 256 + threadIdx.x, nthreads = (gridDim.x - 1) * 256;
-    const KeyPairs kp = load_keys(p, blockIdx.z, blockIdx.y, it, nthreads);
-    asm volatile("" ::: "memory");   // the sequence state is read after these loads go out
-    append_keys(p, seq_state(p, blockIdx.z), blockIdx.z, blockIdx.y, it, nthreads, kp);
-  }
-}
-
 // ---------------------------------------------------------------------------
-// merge: grid (1 + row_blocks * ROWS / 32, Hkv, B), 256 threads; thread =
-// the four float4 of one (32-row tile, head-dim block) of one lane's partial
-// (same register order as the main kernel); block 0 appends the values.
+// merge: grid (row_blocks * ROWS / 32, Hkv, B), 256 threads; thread = the
+// four float4 of one (32-row tile, head-dim block) of one lane's partial
+// (same register order as the main kernel).
 // S >= splits is the number of partials a thread loads: split min(s,
 // splits - 1) for s < S, so the loads need no branches; copies past splits
 // get weight 0.
@@ -1913,14 +1824,7 @@ template <int WAVES, int QT, int S>
 __global__ __launch_bounds__(256) void merge_bf16_kernel(BfParams p) {
   constexpr int ROWS = WAVES * 32 * QT;
   const int g = blockIdx.y, b = blockIdx.z;
-  const int idx = (blockIdx.x - 1) * 256 + threadIdx.x;
-  // block 0 of each KV head (dispatched first) appends the tree's values,
-  // the others merge and append the keys
-  __shared__ uint4 vtr[TV_MAX_NODES_DEV * 16];
-  if (blockIdx.x == 0) {
-    append_values(p, b, g, vtr);
-    return;
-  }
+  const int idx = blockIdx.x * 256 + threadIdx.x;
   // thread = (row block, 32-row tile wt, head-dim block dt, lane): the four
   // float4 of that lane's (wt, dt) block, which share the lane's (r, l)
   const int rb = idx / (ROWS * 8);
@@ -1931,7 +1835,7 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(BfParams p) {
   // The partials are loaded first, for every thread of the grid (the
   // workspace holds all rows_pad rows of each split; rows the attention
   // kernel did not write are dropped below), so that their latency overlaps
-  // the key append.
+  // the sequence state's.
   const size_t wg0 = ((static_cast<size_t>(b) * p.Hkv + g) * p.row_blocks + rb) * p.splits;
   float2 ml[S];
   uint4 o[S][2];
@@ -1942,10 +1846,8 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(BfParams p) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) o[ss][j] = p.part_o[wg * (ROWS * 16) + (wt * 8 + dt * 2 + j) * 64 + lane];
   }
-  const KeyPairs kp = load_keys(p, b, g, idx, (gridDim.x - 1) * 256);
   asm volatile("" ::: "memory");   // the sequence state is read after these loads go out
   const SeqState sq = seq_state(p, b);
-  append_keys(p, sq, b, g, idx, (gridDim.x - 1) * 256, kp);
   const int rows_all = p.G * p.n_max;
   if (row >= rows_all) return;
   const int rows_live = sq.skip ? 0 : p.G * sq.n;
@@ -2150,7 +2052,7 @@ hipError_t launch_attention_bf16(const tv_attn_args* a, const AttnPlan& pl, cons
 
   dim3 grid(pl.splits * pl.row_blocks * a->Hkv * a->B);
   const int wg_rows = pl.waves * 32 * pl.qt;
-  dim3 mgrid(pl.row_blocks * wg_rows / 32 + 1, a->Hkv, a->B);   // (+ the value-append block)
+  dim3 mgrid(pl.row_blocks * wg_rows / 32, a->Hkv, a->B);
   const int key = pl.waves * 10 + pl.qt;
   switch (key + (pk ? 100 : 0) + (parents ? 200 : 0)) {
     case 21: hipLaunchKernelGGL((attn_bf16_kernel<2, 1, false, false>), grid, dim3(128), 0, s, p); break;
@@ -2166,11 +2068,9 @@ hipError_t launch_attention_bf16(const tv_attn_args* a, const AttnPlan& pl, cons
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (pl.splits == 1) {
-    hipLaunchKernelGGL(append_bf16_kernel, dim3(kAppendBlocks + 1, a->Hkv, a->B), dim3(256), 0, s, p);
-    return hipGetLastError();
-  }
-  if (pl.fused) return hipSuccess;   // the main kernel merged and appended
+  // the main kernel appended the tree; with one split, or the splits merged
+  // inside it, it is the only kernel
+  if (pl.splits == 1 || pl.fused) return hipSuccess;
   const int sk = pl.splits <= 2 ? 2 : pl.splits <= 4 ? 4 : pl.splits <= 8 ? 8 : 16;
   static_assert(kMaxSplits == 16, "merge instances cover up to sixteen splits");
   switch (key * 100 + sk) {

@@ -67,7 +67,10 @@ __device__ __forceinline__ LaneTree build_tree_lane(int p_in, int n, int n_max, 
   const bool tree_ok = n_ok && __all(ok_i);
   int J = (live && tree_ok) ? p : -1;
   uint64_t A = live ? (1ull << i) : 0ull;
-  for (int r = 0; r < 6 && __any(J >= 0); ++r) {
+#pragma unroll
+  for (int r = 0; r < 6; ++r) {
+    // (a uniform exit, read into a scalar: no lane has an ancestor left)
+    if (__builtin_amdgcn_readfirstlane(static_cast<int>(__any(J >= 0))) == 0) break;
     const int src = (J >= 0) ? J : i;
     const uint64_t A_src = shfl_u64(A, src);
     const int J_src = __shfl(J, src);
@@ -77,7 +80,7 @@ __device__ __forceinline__ LaneTree build_tree_lane(int p_in, int n, int n_max, 
     }
   }
   const bool keep = live && tree_ok;
-  return LaneTree{keep ? A : 0ull, keep ? __popcll(A) - 1 : 0, tree_ok};
+  return LaneTree{keep ? A : 0ull, keep ? static_cast<int>(__popcll(A)) - 1 : 0, tree_ok};
 }
 
 }  // namespace tv
