@@ -18,10 +18,11 @@ Prints one JSON line. `value` = tree nodes verified per second over the timed
 steps (wall clock between two device synchronisations; the timed loop calls
 the C ABI with arguments built once, as a native caller would). `roofline`
 reports the attention call (with the tree set-up in the dense step):
-algorithmic HBM bytes per call
-divided by its mean duration, from HIP events on the launch stream around the
-call in K further steps (an event pair adds a few microseconds to a step, so
-the timed steps carry none); `traffic` is the measured HBM bytes per call from
+algorithmic HBM bytes per call divided by the call's average duration, from
+HIP events on its launch stream around K calls back to back after the timed
+steps (the rocprofv3 average of its kernels agrees with this figure); the
+line also carries the call timed inside K further steps, an event pair around
+each (which adds a few microseconds, so the timed steps carry none); `traffic` is the measured HBM bytes per call from
 profiles/ when it matches the source.
 
 `--workload typical` measures typical acceptance instead (tv_accept_typical on
@@ -699,9 +700,9 @@ def main() -> None:
     flops = algorithmic_flops(w)
     bound = roofline_bound(w, ab["total"], flops)
     if bound == "mfma":
-        achieved, peak, unit = flops / attn_mean_s / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+        achieved, peak, unit = flops / attn_b2b_s / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
     else:
-        achieved, peak, unit = ab["total"] / attn_mean_s / 1e9, HBM_PEAK_GBS, "GB/s"
+        achieved, peak, unit = ab["total"] / attn_b2b_s / 1e9, HBM_PEAK_GBS, "GB/s"
     wname = f"{w.name}-paged" if paged else w.name
     traffic = load_traffic(wname)
 
@@ -729,12 +730,14 @@ def main() -> None:
                      "kernel": ("tv_tree_attention_paged call" if paged else "tv_tree_attention call" if separate
                                 else "tv_tree_attention_from_parents call (the tree built in the kernel)") +
                                ": attn_bf16_kernel (key splits merged and tree appended inside the kernel on the "
-                               "automatic plan; merge_bf16_kernel otherwise); HIP events on its stream around "
-                               "each call, in the step",
+                               "automatic plan; merge_bf16_kernel otherwise); its average duration from HIP "
+                               "events on its stream around K calls back to back (attention_us_mean: an event pair "
+                               "around the call inside each of K further steps, event overheads included)",
                      "algorithmic_bytes_per_launch": ab["total"],
                      "algorithmic_flops_per_launch": flops,
-                     "hbm_frac": ab["total"] / attn_mean_s / 1e9 / HBM_PEAK_GBS,
-                     "mfma_frac": flops / attn_mean_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                     "hbm_frac": ab["total"] / attn_b2b_s / 1e9 / HBM_PEAK_GBS,
+                     "mfma_frac": flops / attn_b2b_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                     "hbm_frac_in_step": ab["total"] / attn_mean_s / 1e9 / HBM_PEAK_GBS,
                      "attention_us_mean": attn_mean_s * 1e6,
                      "attention_us_p10": float(np.percentile(attn_ms, 10)) * 1e3,
                      "attention_us_p90": float(np.percentile(attn_ms, 90)) * 1e3,
