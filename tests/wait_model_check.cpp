@@ -109,6 +109,8 @@ void replay(Replay& r, int waves, int qt, bool paged, bool build, int n_tiles, i
   if (paged) r.issue("page", w::page_ops(true));
   r.issue("depth", w::depth_ops(qt, build));
   r.issue("query", w::query_ops(waves, qt));
+  // the kernel that builds the tree waits for the parents before the rest
+  if (build) r.wait(w::vm_parents(waves, qt), {"page", "depth"}, "parents");
   if (tree) r.issue("tree", w::tree_ops(waves, qt, build));
   if (guard) r.wait(w::vm_start_guard(waves), {}, "start guard");
   if (paged) r.wait(w::vm_pages(waves, qt, build, tree), {"page"}, "page ids");

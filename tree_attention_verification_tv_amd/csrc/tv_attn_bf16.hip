@@ -1110,6 +1110,27 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
     row_live[t] = my_row[t] < rows_live;
     my_anc[t] = 0;
   }
+  // BUILD: the tree from the parents (every wavefront alike), while the query
+  // copies are in flight and before anything else goes out; the rows' and
+  // the tree items' depths and the rows' ancestor masks come from it by
+  // shuffles. A bad tree retires every workgroup of the sequence.
+  LaneTree tree{0ull, 0, true};
+  if constexpr (BUILD) {
+    wait_vm<waits::vm_parents(WAVES, QT)>();   // (only the query copies stay in flight)
+    landed(par_lane);
+    tree = build_tree_lane(static_cast<int>(par_lane), n, p.n_max, lane);
+    if (!tree.ok) {
+      retire(rb0);
+      return;
+    }
+    dep_lane = static_cast<uint32_t>(tree.depth);
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+      const int node = min(static_cast<int>(p.gdiv.div(my_row[t])), p.n_max - 1);
+      qdep[t] = static_cast<uint32_t>(__shfl(tree.depth, node));
+      my_anc[t] = shfl_u64(tree.anc, node);
+    }
+  }
 
   // Keys of b: slots [0, P + n), in aligned 64-key tiles shared out over the
   // splits. A split takes its tiles in DESCENDING order, so the at most two
@@ -1149,7 +1170,9 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
       const uint16_t* ksrc = p.k_new + ((static_cast<size_t>(b) * p.n_max + node) * p.Hkv + g) * kD + 8 * c;
       tk_lo[u] = ASM ? ld_b128(ksrc) : *reinterpret_cast<const u32x4*>(ksrc);
       tk_hi[u] = ASM ? ld_b128(ksrc + 64) : *reinterpret_cast<const u32x4*>(ksrc + 64);
-      if constexpr (!BUILD) {
+      if constexpr (BUILD) {
+        t_dep[u] = static_cast<uint32_t>(__shfl(tree.depth, node));
+      } else {
         const uint32_t* dsrc = reinterpret_cast<const uint32_t*>(p.depth) + static_cast<size_t>(b) * p.n_max + node;
         t_dep[u] = ASM ? ld_b32(dsrc) : *dsrc;
       }
@@ -1301,27 +1324,6 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
       wait_vm<waits::vm_queries(WAVES, true)>();
     else
       wait_vm<waits::vm_queries(WAVES, false)>();
-  }
-  // BUILD: the tree from the parents (every wavefront alike); the rows' and
-  // the tree items' depths and the rows' ancestor masks come from it by
-  // shuffles. A bad tree retires every workgroup of the sequence.
-  LaneTree tree{0ull, 0, true};
-  if constexpr (BUILD) {
-    landed(par_lane);
-    tree = build_tree_lane(static_cast<int>(par_lane), n, p.n_max, lane);
-    if (!tree.ok) {
-      retire(rb0);
-      return;
-    }
-    dep_lane = static_cast<uint32_t>(tree.depth);
-#pragma unroll
-    for (int t = 0; t < QT; ++t) {
-      const int node = min(static_cast<int>(p.gdiv.div(my_row[t])), p.n_max - 1);
-      qdep[t] = static_cast<uint32_t>(__shfl(tree.depth, node));
-      my_anc[t] = shfl_u64(tree.anc, node);
-    }
-#pragma unroll
-    for (int u = 0; u < KI; ++u) t_dep[u] = static_cast<uint32_t>(__shfl(tree.depth, min((tid + NT * u) >> 3, n - 1)));
   }
 #pragma unroll
   for (int t = 0; t < QT; ++t) landed(qdep[t]);

@@ -11,7 +11,8 @@
 // Issue order, per thread:
 //   start   [the sequence's page ids (paged caches)], the depths of the
 //           wavefront's rows' nodes and of node `lane` (or, when the kernel
-//           builds the tree itself, the parent of node `lane`), the query
+//           builds the tree itself, the parent of node `lane`, which it
+//           waits for right after the next group), the query
 //           copies, [the tree's keys, values and depths and the rows'
 //           ancestor masks (keys and values only when it builds the tree),
 //           when the split holds tree tiles], then tile 0; tiles 1 and 2 go
@@ -67,6 +68,9 @@ constexpr int vm_start_guard(int waves) { return kMaxCount - tile_ops(waves); }
 constexpr int vm_pages(int waves, int qt, bool build, bool tree) {
   return depth_ops(qt, build) + query_ops(waves, qt) + (tree ? tree_ops(waves, qt, build) : 0);
 }
+// (Kernel building the tree) the parents have landed, right after the
+// query copies went out.
+constexpr int vm_parents(int waves, int qt) { return query_ops(waves, qt); }
 // The depths (or parents) have landed (after tile 0, if the split has tiles).
 constexpr int vm_depths(int waves, int qt, bool build, bool tree, bool tile0) {
   return query_ops(waves, qt) + (tree ? tree_ops(waves, qt, build) : 0) + (tile0 ? tile_ops(waves) : 0);
