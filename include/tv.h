@@ -190,10 +190,11 @@ size_t tv_tree_attention_workspace_size(const tv_attn_args* a);
 
 /*
  * Host checks: a non-null; tensor pointers non-null unless B == 0;
- * 1 <= n_max <= TV_MAX_NODES; Hq % Hkv == 0; D in {64, 128} (TV_BF16 needs
- * D == 128 and a query-head group Hq / Hkv of at most 4096, else
- * TV_ERR_UNSUPPORTED); cap >= n_max and cap % 64 == 0; workspace large
- * enough. B == 0 is a no-op.
+ * 1 <= n_max <= TV_MAX_NODES; Hq % Hkv == 0; D in {64, 128} (TV_BF16 at
+ * D == 128 runs the matrix-core kernels and needs a query-head group
+ * Hq / Hkv of at most 4096; fp32, and bf16 at D == 64, run a vector-ALU
+ * kernel that needs no workspace), else TV_ERR_UNSUPPORTED; cap >= n_max and
+ * cap % 64 == 0; workspace large enough. B == 0 is a no-op.
  */
 tv_status tv_tree_attention(const tv_attn_args* a, hipStream_t stream);
 
@@ -270,7 +271,7 @@ typedef struct tv_paged_kv {
  * outside [0, num_pages) gets err = TV_ERR_BAD_PAGE and zero output rows;
  * no page outside the pools is read or written.
  * Host checks as tv_tree_attention, plus pk non-null with a non-null table,
- * max_pages >= 1, num_pages >= 1, a->cap == 64 * max_pages; TV_BF16 only and
+ * max_pages >= 1, num_pages >= 1, a->cap == 64 * max_pages; TV_BF16 at D == 128 only and
  * max_pages <= TV_MAX_PAGES_PER_SEQ, else TV_ERR_UNSUPPORTED.
  */
 tv_status tv_tree_attention_paged(const tv_attn_args* a, const tv_paged_kv* pk,

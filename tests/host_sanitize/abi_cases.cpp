@@ -150,8 +150,15 @@ void attention() {
   EXPECT(tv_tree_attention(&a, nullptr), TV_ERR_INVALID_ARG);
   a = attn(8, 60, 32, 8, 128, 4156);
   EXPECT(tv_tree_attention(&a, nullptr), TV_ERR_INVALID_ARG);
-  a = attn(8, 60, 32, 8, 64);
+  a = attn(8, 60, 32, 8, 96);
   EXPECT(tv_tree_attention(&a, nullptr), TV_ERR_UNSUPPORTED);
+  a = attn(8, 60, 32, 8, 64);   // bf16 at head dim 64: the vector-ALU kernel, no workspace
+  EXPECT(tv_tree_attention_workspace_size(&a), 0);
+  {
+    const int c0 = stub::calls;
+    EXPECT(tv_tree_attention(&a, nullptr), TV_OK);
+    REACHED(c0, "attention_f32");
+  }
   a = attn(8, 60, 32, 8, 96, 4160, TV_F32);
   EXPECT(tv_tree_attention(&a, nullptr), TV_ERR_UNSUPPORTED);
   a = attn(8, 60, 32, 8, 128, 4160, 9);

@@ -114,7 +114,7 @@ def test_attention_host_validation_and_workspace():
     assert run(attn(n_max=65)) == _lib.TV_ERR_INVALID_ARG
     assert run(attn(cap=10)) == _lib.TV_ERR_INVALID_ARG
     assert run(attn(cap=4156)) == _lib.TV_ERR_INVALID_ARG        # V blocks of 64 slots
-    assert run(attn(D=64)) == _lib.TV_ERR_UNSUPPORTED            # bf16 needs D = 128
+    assert run(attn(D=96)) == _lib.TV_ERR_UNSUPPORTED            # head dim 64 or 128
     assert run(attn(dtype=_lib.TV_F32, D=96)) == _lib.TV_ERR_UNSUPPORTED
     assert run(attn(dtype=9)) == _lib.TV_ERR_INVALID_ARG
     assert run(attn(q=None)) == _lib.TV_ERR_INVALID_ARG

@@ -56,10 +56,10 @@ def _compare(w, alias=False):
     return r
 
 
-CASES = [(3, {}), (5, {}), (1, {}), (2, dict(prefix=300)), (4, dict(B=2, prefix=200))]
+CASES = [(3, {}), (5, {}), (1, {}), (2, dict(prefix=300)), (4, dict(B=2, prefix=200)), (3, dict(D=64, prefix=150))]
 
 
-@pytest.mark.parametrize("cfg,over", CASES, ids=[f"cfg{c}" for c, _ in CASES])
+@pytest.mark.parametrize("cfg,over", CASES, ids=[f"cfg{c}" + ("-d64" if o.get("D") == 64 else "") for c, o in CASES])
 @pytest.mark.parametrize("alias", [False, True])
 def test_fused_equals_separate(cfg, over, alias):
     print(f"[gpu] accept+commit cfg={cfg} {over} alias={alias}", flush=True)

@@ -59,6 +59,7 @@ CASES = [
     (5, dict(B=6, prefix=(16, 300))),   # ragged prefixes
     (2, dict(prefix=0)),
     (5, dict(B=3, prefix=(1, 70), n=7)),
+    (3, dict(B=3, prefix=150, D=64)),   # bf16 head dim 64: two launches
 ]
 
 

@@ -411,3 +411,19 @@ def test_fp32_head_dim_128(over):
     worst = check_step(w, res)
     check_commit(w, res, d["k_cache"], d["v_cache"])
     print(f"  attention error {worst:.3g}", flush=True)
+
+
+@pytest.mark.parametrize("cfg,over", [(3, dict(B=3, prefix=150, D=64)), (2, dict(prefix=70, D=64)),
+                                      (5, dict(B=4, prefix=(1, 200), D=64))],
+                         ids=["gqa", "mha", "ragged"])
+def test_bf16_head_dim_64(over, cfg):
+    """bf16 at head dim 64 (the vector-ALU kernel): every row against the
+    oracle, the tree append and the commit as for head dim 128."""
+    print(f"[gpu] bf16 head dim 64 cfg={cfg} {over}", flush=True)
+    w = generate(cfg, **over)
+    assert w.dtype == "bf16" and w.D == 64
+    d = upload(w, DEV)
+    res = run_step(w, d)
+    worst = check_step(w, res)
+    check_commit(w, res, d["k_cache"], d["v_cache"])
+    print(f"  attention error {worst:.3g}", flush=True)

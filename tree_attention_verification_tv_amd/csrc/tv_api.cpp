@@ -20,11 +20,14 @@ tv_status check_attn_shapes(const tv_attn_args* a) {
   if (a->Hq < 1 || a->Hkv < 1 || a->Hq % a->Hkv != 0) return TV_ERR_INVALID_ARG;
   if (a->cap < a->n_max || a->cap % 64 != 0 || a->D < 1) return TV_ERR_INVALID_ARG;
   if (!dtype_ok(a->dtype)) return TV_ERR_INVALID_ARG;
-  if (a->dtype == TV_BF16 && a->D != 128) return TV_ERR_UNSUPPORTED;
-  if (a->dtype == TV_BF16 && a->Hq / a->Hkv > tv::kMaxGroup) return TV_ERR_UNSUPPORTED;
-  if (a->dtype == TV_F32 && a->D != 64 && a->D != 128) return TV_ERR_UNSUPPORTED;
+  if (a->D != 64 && a->D != 128) return TV_ERR_UNSUPPORTED;
+  if (a->dtype == TV_BF16 && a->D == 128 && a->Hq / a->Hkv > tv::kMaxGroup) return TV_ERR_UNSUPPORTED;
   return TV_OK;
 }
+
+// fp32 inputs, and bf16 at head dim 64, take the vector-ALU kernel (no
+// workspace); bf16 at head dim 128 the matrix-core kernels.
+bool vector_path(const tv_attn_args* a) { return a->dtype == TV_F32 || a->D != 128; }
 
 }  // namespace
 
@@ -56,7 +59,7 @@ tv_status tv_build_tree(const int32_t* parents, const int32_t* n_nodes, int32_t 
 
 size_t tv_tree_attention_workspace_size(const tv_attn_args* a) {
   if (check_attn_shapes(a) != TV_OK || a->B == 0) return 0;
-  if (a->dtype != TV_BF16) return 0;
+  if (vector_path(a)) return 0;
   return tv::plan_attention_bf16(a).workspace_bytes;
 }
 
@@ -67,7 +70,7 @@ tv_status tv_tree_attention(const tv_attn_args* a, hipStream_t stream) {
   if (!a->q || !a->k_new || !a->v_new || !a->k_cache || !a->v_cache || !a->prefix_len ||
       !a->n_nodes || !a->anc || !a->depth || !a->err || !a->out)
     return TV_ERR_INVALID_ARG;
-  if (a->dtype == TV_F32) return from_hip(tv::launch_attention_f32(a, stream));
+  if (vector_path(a)) return from_hip(tv::launch_attention_f32(a, stream));
   const tv::AttnPlan plan = tv::plan_attention_bf16(a);
   if (plan.workspace_bytes > 0 && (a->workspace == nullptr || a->workspace_bytes < plan.workspace_bytes))
     return TV_ERR_INVALID_ARG;
@@ -81,7 +84,7 @@ tv_status tv_tree_attention_noalloc(const tv_attn_args* a, hipStream_t stream) {
   if (!a->q || !a->k_new || !a->v_new || !a->k_cache || !a->v_cache || !a->prefix_len ||
       !a->n_nodes || !a->anc || !a->depth || !a->err || !a->out)
     return TV_ERR_INVALID_ARG;
-  if (a->dtype == TV_F32) return from_hip(tv::launch_attention_f32(a, stream));   // (no workspace)
+  if (vector_path(a)) return from_hip(tv::launch_attention_f32(a, stream));   // (no workspace)
   const tv::AttnPlan plan = tv::plan_attention_bf16(a);
   if (plan.workspace_bytes > tv::kScratchBytes) return TV_ERR_SCRATCH;
   tv_attn_args b = *a;
@@ -105,8 +108,8 @@ tv_status tv_tree_attention_from_parents(const tv_attn_args* a, const int32_t* p
   tv_attn_args b = *a;
   b.anc = anc;
   b.depth = depth;
-  if (a->dtype == TV_F32) {
-    // (the fp32 kernel reads a built tree: two launches)
+  if (vector_path(a)) {
+    // (the vector-ALU kernel reads a built tree: two launches)
     const hipError_t e = tv::launch_build_tree(parents, a->n_nodes, a->B, a->n_max, anc, depth, a->err, stream);
     if (e != hipSuccess) return TV_ERR_HIP;
     return from_hip(tv::launch_attention_f32(&b, stream));
@@ -122,7 +125,7 @@ tv_status tv_tree_attention_paged(const tv_attn_args* a, const tv_paged_kv* pk, 
   if (st != TV_OK) return st;
   if (pk == nullptr || pk->max_pages < 1 || pk->num_pages < 1) return TV_ERR_INVALID_ARG;
   if (a->cap != 64 * pk->max_pages) return TV_ERR_INVALID_ARG;
-  if (a->dtype != TV_BF16 || pk->max_pages > TV_MAX_PAGES_PER_SEQ) return TV_ERR_UNSUPPORTED;
+  if (a->dtype != TV_BF16 || a->D != 128 || pk->max_pages > TV_MAX_PAGES_PER_SEQ) return TV_ERR_UNSUPPORTED;
   if (a->B == 0) return TV_OK;
   if (!a->q || !a->k_new || !a->v_new || !a->k_cache || !a->v_cache || !a->prefix_len ||
       !a->n_nodes || !a->anc || !a->depth || !a->err || !a->out || !pk->block_table)
