@@ -692,7 +692,16 @@ def main() -> None:
         if attention(k):
             raise RuntimeError("tv_tree_attention failed")
     e1.record(stream)
+    # the rest of the step alone, K calls back to back (the same moves each
+    # time: the prefix lengths are not advanced)
+    e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e2.record(stream)
+    for k in range(args.steps):
+        if accept_commit(k):
+            raise RuntimeError("accept and commit failed")
+    e3.record(stream)
     torch.cuda.synchronize()
+    rest_b2b_s = e2.elapsed_time(e3) * 1e-3 / args.steps
     attn_ms = [a.elapsed_time(b) for a, b in events]
     attn_mean_s = float(np.mean(attn_ms)) * 1e-3
     attn_b2b_s = e0.elapsed_time(e1) * 1e-3 / args.steps
@@ -743,6 +752,7 @@ def main() -> None:
                      "attention_us_p90": float(np.percentile(attn_ms, 90)) * 1e3,
                      "attention_us_back_to_back": attn_b2b_s * 1e6},
         "attention_only_nodes_per_s": nodes / attn_mean_s,
+        "accept_commit_us_back_to_back": rest_b2b_s * 1e6,
         "mean_accept_len": mean_accept,
         "kernel_source_hash": kernel_source_hash(),
     }

@@ -43,50 +43,69 @@ __global__ __launch_bounds__(64) void build_tree_kernel(const int32_t* __restric
 // bit in ascending order, is the path. The bonus token is tgt at that node
 // (the target's argmax there, for both rules).
 // ---------------------------------------------------------------------------
-// Accept of sequence b by one wavefront (lane i = node i); writes the
-// outputs and returns the accepted length (-1: skipped) in every lane, and in
-// `on_pos` the path position of node i (-1 if i is not on the path).
+// The accept's inputs of node i (lane i) and of its sequence. Every load is
+// unconditional (the node index is clamped into the row; lanes past n_max
+// are masked when the inputs are used), so all of them go out together,
+// before the first wait, and none is moved behind a branch.
+struct AcceptIn {
+  uint64_t a;
+  int p, tk, tg, dp, n, e;
+  float pt, h;
+};
+
 template <bool TYPICAL>
-__device__ __forceinline__ int accept_sequence(
+__device__ __forceinline__ AcceptIn accept_load(
     const int32_t* __restrict__ cand_tok, const int32_t* __restrict__ tgt,
     const int32_t* __restrict__ parents, const uint64_t* __restrict__ anc,
     const int32_t* __restrict__ depth, const int32_t* __restrict__ n_nodes,
-    const int32_t* __restrict__ err, int n_max, int32_t* __restrict__ accept_len,
-    int32_t* __restrict__ path, int32_t* __restrict__ bonus, int32_t* __restrict__ out_tokens,
-    const float* __restrict__ p_tok, const float* __restrict__ entropy, float eps, float delta, int b, int i,
+    const int32_t* __restrict__ err, int n_max, const float* __restrict__ p_tok,
+    const float* __restrict__ entropy, int b, int i) {
+  const size_t at = static_cast<size_t>(b) * n_max + min(i, n_max - 1);
+  AcceptIn in;
+  in.p = parents[at];
+  in.tk = cand_tok[at];
+  in.tg = tgt[at];
+  in.a = anc[at];
+  in.dp = depth[at];
+  if constexpr (TYPICAL) {
+    in.pt = p_tok[at];
+    in.h = entropy[at];
+  } else {
+    in.pt = in.h = 0.f;
+  }
+  in.n = n_nodes[b];
+  in.e = err ? err[b] : 0;
+  return in;
+}
+
+// Accept of sequence b by one wavefront (lane i = node i) from its loaded
+// inputs; writes the outputs (if `write`) and returns the accepted length
+// (-1: skipped) in every lane, and in `on_pos` the path position of node i
+// (-1 if i is not on the path).
+template <bool TYPICAL>
+__device__ __forceinline__ int accept_decide(
+    const AcceptIn& in, int n_max, int32_t* __restrict__ accept_len, int32_t* __restrict__ path,
+    int32_t* __restrict__ bonus, int32_t* __restrict__ out_tokens, float eps, float delta, int b, int i,
     int& on_pos, bool write = true) {
   on_pos = -1;
   const size_t row = static_cast<size_t>(b) * n_max;
-  // every load goes out at once (node data does not wait for the count)
-  const bool in_row = i < n_max;
-  const int p_in = in_row ? parents[row + i] : -1;
-  const int tk_in = in_row ? cand_tok[row + i] : 0;
-  const int tg_in = in_row ? tgt[row + i] : 0;
-  const uint64_t a_in = in_row ? anc[row + i] : 0ull;
-  const int dp_in = in_row ? depth[row + i] : 0;
-  float pt_in = 0.f, h_in = 0.f;
-  if constexpr (TYPICAL) {
-    pt_in = in_row ? p_tok[row + i] : 0.f;
-    h_in = in_row ? entropy[row + i] : 0.f;
-  }
-  const int n = n_nodes[b];
-  const int e_in = err ? err[b] : 0;
-  bool active = (e_in == 0) && (n > 0) && (n <= n_max);
+  const int n = in.n;
+  bool active = (in.e == 0) && (n > 0) && (n <= n_max);
 
   const bool live = active && (i < n);
-  const int p = live ? p_in : -1;
-  const int tk = live ? tk_in : 0;
-  const int tg = live ? tg_in : 0;
-  const uint64_t a = live ? a_in : 0ull;
-  const int dp = live ? dp_in : 0;
+  const int p = live ? in.p : -1;
+  const int tk = live ? in.tk : 0;
+  const int tg = live ? in.tg : 0;
+  const uint64_t a = live ? in.a : 0ull;
+  const int dp = live ? in.dp : 0;
 
   // every lane takes part in the shuffles (none sits behind a branch)
   const int src = (p >= 0 && p < 64) ? p : i;
   const int tg_parent = __shfl(tg, src);
-  const float h_parent = TYPICAL ? __shfl(h_in, src) : 0.f;
+  const float h_parent = TYPICAL ? __shfl(in.h, src) : 0.f;
   bool match;
   if constexpr (TYPICAL) {
-    match = live && (i == 0 || pt_in > fminf(eps, delta * expf(-h_parent)));
+    match = live && (i == 0 || in.pt > fminf(eps, delta * expf(-h_parent)));
   } else {
     match = live && (i == 0 || tk == tg_parent);
   }
@@ -143,8 +162,10 @@ __global__ __launch_bounds__(64) void accept_kernel(
     int32_t* __restrict__ path, int32_t* __restrict__ bonus, int32_t* __restrict__ out_tokens,
     const float* __restrict__ p_tok, const float* __restrict__ entropy, float eps, float delta) {
   int on_pos;
-  accept_sequence<TYPICAL>(cand_tok, tgt, parents, anc, depth, n_nodes, err, n_max, accept_len, path, bonus,
-                           out_tokens, p_tok, entropy, eps, delta, blockIdx.x, threadIdx.x, on_pos);
+  const AcceptIn in = accept_load<TYPICAL>(cand_tok, tgt, parents, anc, depth, n_nodes, err, n_max, p_tok, entropy,
+                                           blockIdx.x, threadIdx.x);
+  accept_decide<TYPICAL>(in, n_max, accept_len, path, bonus, out_tokens, eps, delta, blockIdx.x, threadIdx.x,
+                         on_pos);
 }
 
 // ---------------------------------------------------------------------------
@@ -255,9 +276,9 @@ __global__ __launch_bounds__(256) void commit_kernel(
 
 // ---------------------------------------------------------------------------
 // accept + commit in one launch: grid (Hkv / heads_per_block, B), 256
-// threads. Wave 0 of every workgroup of sequence b runs the accept of
-// accept_kernel (a few hundred bytes of loads, repeated per KV head rather
-// than waited for across a launch); the workgroup of heads 0.. writes its
+// threads. Every wavefront of every workgroup of sequence b runs the accept
+// of accept_kernel (a few hundred bytes of loads, repeated rather than
+// waited for across a launch); the workgroup of heads 0.. writes its
 // outputs. The length and path stay in LDS, and the workgroup moves the
 // path's K and V of its KV heads (slot P + d <- slot P + path[d]) in batches
 // whose sources fit the LDS stage: all of a batch's sources are read before
@@ -267,6 +288,15 @@ __global__ __launch_bounds__(256) void commit_kernel(
 // -1) or a move outside [P, cap) leaves the cache and the prefix length
 // unchanged.
 // ---------------------------------------------------------------------------
+// A 16-byte chunk held as four words: rows kept in registers between their
+// load and their LDS store are copied word by word, so the compiler does not
+// turn the pair into a memory-to-memory copy through a stack buffer.
+struct Words4 {
+  uint32_t w[4];
+};
+__device__ __forceinline__ Words4 words(uint4 x) { return Words4{{x.x, x.y, x.z, x.w}}; }
+__device__ __forceinline__ uint4 chunk(const Words4& x) { return make_uint4(x.w[0], x.w[1], x.w[2], x.w[3]); }
+
 template <typename T>
 __global__ __launch_bounds__(256) void accept_commit_kernel(
     const int32_t* __restrict__ cand_tok, const int32_t* __restrict__ tgt,
@@ -282,7 +312,8 @@ __global__ __launch_bounds__(256) void accept_commit_kernel(
   // V rows: head dim c, slots from P rounded down to a 16-byte chunk
   constexpr int kVSlots = kRows + EPC;
   __shared__ uint4 k_rows[kRows * kMaxD / EPC];
-  __shared__ __attribute__((aligned(16))) T v_rows[kMaxD * kVSlots];
+  // (plus one 16-byte chunk that takes the stores of lanes with no chunk)
+  __shared__ __attribute__((aligned(16))) T v_rows[kMaxD * kVSlots + EPC];
   __shared__ int s_path[TV_MAX_NODES_DEV];
   __shared__ int s_L;
   const int b = blockIdx.y;
@@ -294,7 +325,7 @@ __global__ __launch_bounds__(256) void accept_commit_kernel(
   const int nr = (P >= 0 && n_in > 0 && n_in <= n_max) ? max(0, min(n_in, cap - P)) : 0;
   const int kpr = D / EPC;   // 16-byte chunks per K row
   // element offset of the 64-slot block holding `slot` (head g)
-  auto base = [&](int g, int slot) {
+  auto base = [=](int g, int slot) {
     return ((static_cast<size_t>(b) * Hkv + g) * cap + static_cast<size_t>(slot >> 6) * 64) * D;
   };
   // The tree rows of head g are loaded into registers, every load of a
@@ -308,61 +339,43 @@ __global__ __launch_bounds__(256) void accept_commit_kernel(
   const int v0 = P & ~(EPC - 1);                                       // first slot of the first V chunk
   const int vchunks = nr > 0 ? ((P + nr - 1 - v0) / EPC + 1) : 0;     // V chunks per head-dim row
   const int ktotal = nr * kpr, vtotal = vchunks * D;
-  uint4 kv[KU], vv[VU];
-  auto load_rows = [&](int g) __attribute__((always_inline)) {
+  const int p_safe = nr > 0 ? P : 0, v0_safe = nr > 0 ? v0 : 0;
+  auto load_rows = [=](int g, Words4 (&kv)[KU], Words4 (&vv)[VU]) __attribute__((always_inline)) {
+    // Every load is unconditional, so the compiler counts them exactly and the
+    // accept waits only for its own: with no tree rows (nr == 0) they read
+    // slot 0 of the head (p_safe = v0_safe = 0, idx = 0), which always
+    // exists, and are never used.
 #pragma unroll
     for (int u = 0; u < KU; ++u) {
       const int idx = min(tid + u * 256, max(ktotal - 1, 0)), r = idx / kpr, c = idx % kpr;
-      const int slot = P + r;
-      kv[u] = ktotal > 0 ? *reinterpret_cast<const uint4*>(k_cache + base(g, slot) +
-                                                           static_cast<size_t>(slot & 63) * D + EPC * c)
-                         : make_uint4(0u, 0u, 0u, 0u);
+      const int slot = p_safe + r;
+      kv[u] = words(*reinterpret_cast<const uint4*>(k_cache + base(g, slot) + static_cast<size_t>(slot & 63) * D +
+                                                    EPC * c));
     }
 #pragma unroll
     for (int u = 0; u < VU; ++u) {
       // consecutive lanes walk the chunks of one head-dim row
       const int idx = min(tid + u * 256, max(vtotal - 1, 0)), c = idx / max(vchunks, 1), k = idx % max(vchunks, 1);
-      const int slot = v0 + EPC * k;
-      vv[u] = vtotal > 0 ? *reinterpret_cast<const uint4*>(v_cache + base(g, slot) + static_cast<size_t>(c) * 64 +
-                                                           (slot & 63))
-                         : make_uint4(0u, 0u, 0u, 0u);
+      const int slot = v0_safe + EPC * k;
+      vv[u] = words(*reinterpret_cast<const uint4*>(v_cache + base(g, slot) + static_cast<size_t>(c) * 64 +
+                                                    (slot & 63)));
     }
   };
-  auto put_rows = [&]() __attribute__((always_inline)) {
+  // Unconditional stores as well: K chunks past the tree's rows are never
+  // read, and V lanes with no chunk all write the spare chunk.
+  auto put_rows = [=](const Words4 (&kv)[KU], const Words4 (&vv)[VU]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < KU; ++u)
-      if (tid + u * 256 < ktotal) k_rows[tid + u * 256] = kv[u];
+    for (int u = 0; u < KU; ++u) k_rows[tid + u * 256] = chunk(kv[u]);
 #pragma unroll
     for (int u = 0; u < VU; ++u) {
-      const int idx = tid + u * 256;
-      if (idx < vtotal)
-        *reinterpret_cast<uint4*>(&v_rows[(idx / vchunks) * kVSlots + EPC * (idx % vchunks)]) = vv[u];
+      const int idx = tid + u * 256, vc = max(vchunks, 1);
+      const int at = idx < vtotal ? (idx / vc) * kVSlots + EPC * (idx % vc) : kMaxD * kVSlots;
+      *reinterpret_cast<uint4*>(&v_rows[at]) = chunk(vv[u]);
     }
   };
-  // the first head's rows go out together with the accept's loads
-  load_rows(g_first);
-  if (tid < 64) {
-    int on_pos;
-    const int L = accept_sequence<false>(cand_tok, tgt, parents, anc, depth, n_nodes, err, n_max, accept_len, path,
-                                         bonus, out_tokens, nullptr, nullptr, 0.f, 0.f, b, tid, on_pos,
-                                         blockIdx.x == 0);
-    if (on_pos >= 0) s_path[on_pos] = tid;
-    if (tid == 0) s_L = L;
-  }
-  put_rows();
-  __syncthreads();
-  // the path ascends, so its end node path[L] is the largest moved slot
-  const int L = (s_L >= 0 && P >= 0 && s_path[max(s_L, 0)] < nr) ? s_L : -1;
-  if (blockIdx.x == 0 && tid == 0) prefix_len_out[b] = L >= 0 ? P + L + 1 : P;
-  if (L < 0) return;
-  for (int g = g_first; g < g_last; ++g) {
-    if (g != g_first) {
-      __syncthreads();   // (the previous head's rows are written)
-      load_rows(g);
-      put_rows();
-      __syncthreads();
-    }
-    // slot P + d <- tree row path[d], d = 0 .. L (rows on their own slot stay)
+  // slot P + d <- tree row path[d], d = 0 .. L, of head g (rows on their own
+  // slot stay)
+  auto move_rows = [&](int g, int L) __attribute__((always_inline)) {
     for (int idx = tid; idx < (L + 1) * kpr; idx += 256) {
       const int d = idx / kpr, c = idx % kpr, src = s_path[d];
       if (src == d) continue;
@@ -376,6 +389,36 @@ __global__ __launch_bounds__(256) void accept_commit_kernel(
       const int dst = P + d;
       v_cache[base(g, dst) + static_cast<size_t>(c) * 64 + (dst & 63)] = v_rows[c * kVSlots + (P + src - v0)];
     }
+  };
+  // The accept's loads go out first (every wavefront makes them: they need
+  // no prefix length), then the first head's rows; every wavefront decides
+  // the accept, wavefront 0 keeps the path and (workgroup of heads 0..)
+  // writes the outputs.
+  const AcceptIn ain = accept_load<false>(cand_tok, tgt, parents, anc, depth, n_nodes, err, n_max, nullptr, nullptr,
+                                          b, tid & 63);
+  Words4 kv[KU], vv[VU];
+  load_rows(g_first, kv, vv);
+  {
+    int on_pos;
+    const int L = accept_decide<false>(ain, n_max, accept_len, path, bonus, out_tokens, 0.f, 0.f, b, tid & 63,
+                                       on_pos, blockIdx.x == 0 && tid < 64);
+    if (tid < 64 && on_pos >= 0) s_path[on_pos] = tid;
+    if (tid == 0) s_L = L;
+  }
+  put_rows(kv, vv);
+  __syncthreads();
+  // the path ascends, so its end node path[L] is the largest moved slot
+  const int L = (s_L >= 0 && P >= 0 && s_path[max(s_L, 0)] < nr) ? s_L : -1;
+  if (blockIdx.x == 0 && tid == 0) prefix_len_out[b] = L >= 0 ? P + L + 1 : P;
+  if (L < 0) return;
+  move_rows(g_first, L);
+  for (int g = g_first + 1; g < g_last; ++g) {
+    Words4 kv_g[KU], vv_g[VU];
+    __syncthreads();   // (the previous head's rows are written)
+    load_rows(g, kv_g, vv_g);
+    put_rows(kv_g, vv_g);
+    __syncthreads();
+    move_rows(g, L);
   }
 }
 
