@@ -20,8 +20,13 @@ CASES = [(2, dict(prefix=300)), (3, dict(B=2, prefix=1100)), (4, dict(B=2, prefi
          (5, dict(B=6, prefix=(16, 300)))]
 # fused=0: the separate merge kernel on plans the automatic choice merges in
 # the kernel; splits=2 / 4: the fused merge with two and four splits
+# waves=8: eight wavefronts of one 32-row tile each (two per SIMD), also
+# through the tree-building and paged instances
 PLANS = ["waves=2,qt=1", "waves=2,qt=1,splits=1", "waves=4,qt=1,splits=8", "qt=2,splits=2", "splits=1",
-         "splits=16", "fused=0", "splits=2", "waves=4,qt=1,splits=4", "splits=4,fused=0"]
+         "splits=16", "fused=0", "splits=2", "waves=4,qt=1,splits=4", "splits=4,fused=0",
+         "waves=8", "waves=8,splits=1", "waves=8,fused=0", "waves=8,splits=16"]
+# the extra checks an eight-wavefront plan runs
+EIGHT = 3
 
 
 def child_main(plan: str) -> None:
@@ -32,6 +37,17 @@ def child_main(plan: str) -> None:
         print(f"ok plan={plan} cfg={cfg} {over}", flush=True)
     test_uniformly_low_scores_with_empty_splits()
     print(f"ok plan={plan} low scores", flush=True)
+    if "waves=8" in plan:
+        from tests.test_gpu_from_parents import test_invalid_trees_and_capacity_like_build_tree, \
+            test_small_cases_equal_separate_calls_and_oracle
+        from tests.test_gpu_paged import test_paged_ragged_trees_against_oracle_and_dense
+        for cfg, over in CASES:
+            test_small_cases_equal_separate_calls_and_oracle(cfg, over)
+        print(f"ok plan={plan} tree built in the kernel", flush=True)
+        test_invalid_trees_and_capacity_like_build_tree()
+        print(f"ok plan={plan} invalid trees", flush=True)
+        test_paged_ragged_trees_against_oracle_and_dense()
+        print(f"ok plan={plan} paged", flush=True)
 
 
 @pytest.mark.parametrize("plan", PLANS)
@@ -42,7 +58,7 @@ def test_plan_parity(plan):
                        capture_output=True, text=True, timeout=110)
     print(r.stdout[-2000:], flush=True)
     assert r.returncode == 0, r.stderr[-3000:]
-    assert r.stdout.count("ok plan=") == len(CASES) + 1
+    assert r.stdout.count("ok plan=") == len(CASES) + 1 + (EIGHT if "waves=8" in plan else 0)
 
 
 if __name__ == "__main__":

@@ -36,7 +36,7 @@ def test_every_wait_covers_exactly_what_it_guards(checker):
     r = subprocess.run([checker], capture_output=True, text=True)
     assert r.returncode == 0, r.stdout + r.stderr
     ok, cases, waits = r.stdout.split()
-    assert ok == "ok" and int(cases) == 864 and int(waits) > 5000
+    assert ok == "ok" and int(cases) == 1152 and int(waits) > 5000
 
 
 def test_the_earlier_tree_tile_wait_is_caught(checker):

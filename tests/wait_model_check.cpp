@@ -143,7 +143,7 @@ void replay(Replay& r, int waves, int qt, bool paged, bool build, int n_tiles, i
 int main(int argc, char** argv) {
   const bool legacy_tree = argc > 1 && std::strcmp(argv[1], "--legacy-tree") == 0;
   // the kernel's instantiations: (wavefronts, query tiles per wavefront)
-  const int shapes[][2] = {{2, 1}, {4, 1}, {4, 2}};
+  const int shapes[][2] = {{2, 1}, {4, 1}, {4, 2}, {8, 1}};
   long cases = 0, waits = 0, failures = 0;
   for (const auto& sh : shapes)
     for (int paged = 0; paged < 2; ++paged)

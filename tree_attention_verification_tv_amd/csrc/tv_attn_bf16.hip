@@ -1226,10 +1226,11 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
     const int d = c >> 3, vpos = c & 7;
     v_voff[j] = static_cast<uint32_t>(d * kKT + ((vpos ^ (d & 7)) << 3)) * 2u;
   }
-  // A tile's copy in 8 slots of 2 * CPT / 8 instructions each (instruction
-  // 2j: K chunk j, 2j + 1: V chunk j), so that a tile product can spread
-  // them over its steps.
-  static_assert(2 * CPT % 8 == 0, "copy slots");
+  // A tile's copy in 8 slots (instruction 2j: K chunk j, 2j + 1: V chunk j;
+  // slot k holds instructions [2 CPT k / 8, 2 CPT (k + 1) / 8): two, one, or
+  // with eight wavefronts one in every other slot), so that a tile product
+  // can spread them over its steps.
+  static_assert(2 * CPT % 8 == 0 || 8 % (2 * CPT) == 0, "copy slots");
   struct TileCopy {
     const uint16_t* ktile;
     const uint16_t* vtile;
@@ -1238,7 +1239,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
     const uint32_t* v_voff;
     __device__ __forceinline__ void operator()(int slot) const {
 #pragma unroll
-      for (int part = slot * (2 * CPT / 8); part < (slot + 1) * (2 * CPT / 8); ++part) {
+      for (int part = slot * 2 * CPT / 8; part < (slot + 1) * 2 * CPT / 8; ++part) {
         const int j = part >> 1;
         if (part & 1)
           dma16(vtile, v_voff[j], vl + j * NT * 16);
@@ -1430,7 +1431,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   // the tree zeroed, prefix keys (below P) kept (only a thread whose keys
   // include some reads the old piece first).
   constexpr int KPL = 64 * 16 / NT;   // tile keys per thread in the value fill
-  static_assert(KPL == 4 || KPL == 8, "value fill in 8- or 16-byte pieces");
+  static_assert(KPL == 2 || KPL == 4 || KPL == 8, "value fill in 4-, 8- or 16-byte pieces");
   static_assert(kStages > 3 && 64 * kD * 2 <= 2 * kStageElems * 2, "the value transpose fits stage 3");
   uint4* const vtr = reinterpret_cast<uint4*>(smem + 2 * 3 * kStageElems);   // [node][chunk]
   auto stage_tree_values = [&]() __attribute__((always_inline)) {
@@ -1492,7 +1493,9 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
       if (any_prefix) {
 #pragma unroll
         for (int dd = 0; dd < 8; ++dd) {
-          if constexpr (KPL == 4) {
+          if constexpr (KPL == 2) {
+            wo[dd][0] = *reinterpret_cast<const uint32_t*>(rows[dd]);
+          } else if constexpr (KPL == 4) {
             const uint2 o2 = *reinterpret_cast<const uint2*>(rows[dd]);
             wo[dd][0] = o2.x;
             wo[dd][1] = o2.y;
@@ -1519,7 +1522,9 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
           }
           wv[k2] = e[0] | (e[1] << 16);
         }
-        if constexpr (KPL == 4)
+        if constexpr (KPL == 2)
+          *reinterpret_cast<uint32_t*>(rows[dd]) = wv[0];
+        else if constexpr (KPL == 4)
           *reinterpret_cast<uint2*>(rows[dd]) = make_uint2(wv[0], wv[1]);
         else
           *reinterpret_cast<uint4*>(rows[dd]) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
@@ -1936,7 +1941,8 @@ AttnPlan plan_attention_bf16(const tv_attn_args* a) {
   pl.waves = 4;
   const Tune& tn = tune();
   if (tn.qt == 1 || tn.qt == 2) pl.qt = tn.qt;
-  if (tn.waves == 2 || tn.waves == 4) pl.waves = tn.waves;
+  if (tn.waves == 2 || tn.waves == 4 || tn.waves == 8) pl.waves = tn.waves;
+  if (pl.waves == 8) pl.qt = 1;   // (two wavefronts per SIMD: one 32-row tile each)
   if (pl.qt == 2) pl.waves = 4;
   const int wg_rows = pl.waves * 32 * pl.qt;
   pl.row_blocks = (rows + wg_rows - 1) / wg_rows;
@@ -2066,6 +2072,9 @@ hipError_t launch_attention_bf16(const tv_attn_args* a, const AttnPlan& pl, cons
     case 221: hipLaunchKernelGGL((attn_bf16_kernel<2, 1, false, true>), grid, dim3(128), 0, s, p); break;
     case 241: hipLaunchKernelGGL((attn_bf16_kernel<4, 1, false, true>), grid, dim3(256), 0, s, p); break;
     case 242: hipLaunchKernelGGL((attn_bf16_kernel<4, 2, false, true>), grid, dim3(256), 0, s, p); break;
+    case 81: hipLaunchKernelGGL((attn_bf16_kernel<8, 1, false, false>), grid, dim3(512), 0, s, p); break;
+    case 181: hipLaunchKernelGGL((attn_bf16_kernel<8, 1, true, false>), grid, dim3(512), 0, s, p); break;
+    case 281: hipLaunchKernelGGL((attn_bf16_kernel<8, 1, false, true>), grid, dim3(512), 0, s, p); break;
     default: return hipErrorInvalidValue;   // (a paged cache with a parents array: refused by the host checks)
   }
   hipError_t e = hipGetLastError();
@@ -2087,6 +2096,10 @@ hipError_t launch_attention_bf16(const tv_attn_args* a, const AttnPlan& pl, cons
     case 4202: hipLaunchKernelGGL((merge_bf16_kernel<4, 2, 2>), mgrid, dim3(256), 0, s, p); break;
     case 4204: hipLaunchKernelGGL((merge_bf16_kernel<4, 2, 4>), mgrid, dim3(256), 0, s, p); break;
     case 4208: hipLaunchKernelGGL((merge_bf16_kernel<4, 2, 8>), mgrid, dim3(256), 0, s, p); break;
+    case 8102: hipLaunchKernelGGL((merge_bf16_kernel<8, 1, 2>), mgrid, dim3(256), 0, s, p); break;
+    case 8104: hipLaunchKernelGGL((merge_bf16_kernel<8, 1, 4>), mgrid, dim3(256), 0, s, p); break;
+    case 8108: hipLaunchKernelGGL((merge_bf16_kernel<8, 1, 8>), mgrid, dim3(256), 0, s, p); break;
+    case 8116: hipLaunchKernelGGL((merge_bf16_kernel<8, 1, 16>), mgrid, dim3(256), 0, s, p); break;
     default: hipLaunchKernelGGL((merge_bf16_kernel<4, 2, 16>), mgrid, dim3(256), 0, s, p); break;
   }
   return hipGetLastError();
