@@ -192,8 +192,10 @@ size_t tv_tree_attention_workspace_size(const tv_attn_args* a);
  * Host checks: a non-null; tensor pointers non-null unless B == 0;
  * 1 <= n_max <= TV_MAX_NODES; Hq % Hkv == 0; D in {64, 128} (TV_BF16 at
  * D == 128 runs the matrix-core kernels and needs a query-head group
- * Hq / Hkv of at most 4096; fp32, and bf16 at D == 64, run a vector-ALU
- * kernel that needs no workspace), else TV_ERR_UNSUPPORTED; cap >= n_max and
+ * Hq / Hkv of at most 4096; fp32, and bf16 at D == 64, run a tree-append
+ * kernel and a second attention kernel (fp32 or bf16 matrix products,
+ * streaming the cache after the append) that need no workspace), else
+ * TV_ERR_UNSUPPORTED; cap >= n_max and
  * cap % 64 == 0; workspace large enough. B == 0 is a no-op.
  */
 tv_status tv_tree_attention(const tv_attn_args* a, hipStream_t stream);
