@@ -153,7 +153,9 @@ struct BfParams {
   int max_pages, num_pages;
   // fused split merge (see merge_in_kernel): the partials are published with
   // agent-coherent stores and merged by the workgroups themselves; sync holds
-  // four words per (sequence, KV head, row block), zero between calls
+  // four words per (sequence, KV head, row block), zero between calls.
+  // 0: no fused merge; 1: every split merges its range (waiting, bounded,
+  // for the others); 2: the last split to arrive merges every range
   int fused;
   uint32_t* sync;
   size_t ws_bytes;   // workspace bytes (buffer-resource range of the partials)
@@ -927,6 +929,16 @@ __device__ __forceinline__ void merge_claim_and_run(const BfParams& p, int grp, 
   const uint32_t full = (1u << splits) - 1u, mine = 1u << s;
   uint32_t* w = group_words(p, grp);
   const bool last = words[0] == splits;   // (uniform: read after a barrier)
+  if (p.fused == 2) {
+    // only the last arrival merges, every range; the others leave at once
+    if (last) {
+      if (threadIdx.x == 0) words[2] = full & ~__hip_atomic_fetch_or(&w[1], full, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      const uint32_t todo = words[2];
+      for (int r = 0; r < static_cast<int>(splits); ++r)
+        if ((todo >> r) & 1u) merge_range<WAVES, QT, S>(p, b, g, rb, r, rows_live, rml, ro);
+    }
+  } else {
   if (threadIdx.x == 0) {
     bool all = last;
     if (!all) {
@@ -954,6 +966,7 @@ __device__ __forceinline__ void merge_claim_and_run(const BfParams& p, int grp, 
     const uint32_t todo = words[2];
     for (int r = 0; r < static_cast<int>(splits); ++r)
       if ((todo >> r) & 1u) merge_range<WAVES, QT, S>(p, b, g, rb, r, rows_live, rml, ro);
+  }
   }
   if (threadIdx.x == 0) {
     if (__hip_atomic_fetch_add(&w[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u == splits) {
@@ -1964,7 +1977,14 @@ AttnPlan plan_attention_bf16(const tv_attn_args* a) {
   // The splits merge in the kernel (no second launch, partials read while
   // still near) when there are at most four and the whole grid runs at once
   // (one workgroup per compute unit); otherwise the merge kernel follows.
-  pl.fused = splits > 1 && splits <= 4 && units * splits <= cus && units <= kMaxFusedGroups && tn.fused != 0;
+  // (fused=2 of the override: only the last split to arrive merges, and no
+  // split waits, so it also serves grids that do not run at once; measured
+  // no faster than the merge kernel there, 161.0 against 160.9 us on 64
+  // ragged sequences, and slower at the headline shape, 51.7 against 48.8,
+  // where one workgroup then does every group's whole merge)
+  const bool at_once = units * splits <= cus;
+  pl.fused = splits > 1 && splits <= 4 && units <= kMaxFusedGroups && ((tn.fused == 1 && at_once) || tn.fused == 2);
+  pl.last_merges = pl.fused && tn.fused == 2;
   pl.workspace_bytes = ws_layout(a, pl).total;
   return pl;
 }
@@ -2055,7 +2075,7 @@ hipError_t launch_attention_bf16(const tv_attn_args* a, const AttnPlan& pl, cons
   p.part_ml = pl.splits > 1 ? reinterpret_cast<float2*>(ws + w.part_ml) : nullptr;
   p.part_o = pl.splits > 1 ? reinterpret_cast<uint4*>(ws + w.part_o) : nullptr;
   p.sync = pl.splits > 1 ? reinterpret_cast<uint32_t*>(ws + w.sync) : nullptr;
-  p.fused = pl.fused ? 1 : 0;
+  p.fused = !pl.fused ? 0 : pl.last_merges ? 2 : 1;
   p.ws_bytes = pl.workspace_bytes;
 
   dim3 grid(pl.splits * pl.row_blocks * a->Hkv * a->B);

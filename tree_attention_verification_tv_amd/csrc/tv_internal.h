@@ -62,6 +62,8 @@ struct AttnPlan {
   int splits;      // workgroups along the prefix keys
   int rows_pad;    // row_blocks * waves * 32
   bool fused;      // the splits merge inside the main kernel (no merge kernel)
+  bool last_merges;  // (fused) the last split to arrive merges every range
+                     // and none waits: for grids that do not run at once
   size_t workspace_bytes;
 };
 
