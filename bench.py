@@ -3,9 +3,10 @@
 A step is the whole verification path for one attention layer over one batch:
 tv_tree_attention_from_parents (the tree mask and depths built inside the
 attention kernel, which also writes them for the accept) -> tv_accept_commit
-(greedy accept and the in-place KV commit in one launch); the paged step calls
-tv_build_tree -> tv_tree_attention_paged -> tv_accept -> tv_commit_paged. All
-through the C ABI. The headline workload is the Llama-3-8B-shaped GQA batch (32 q / 8 kv
+(greedy accept and the in-place KV commit in one launch); the paged step is
+tv_tree_attention_paged_from_parents -> tv_accept_commit_paged (--separate-tree:
+tv_build_tree -> tv_tree_attention(_paged) -> tv_accept -> tv_commit(_paged)).
+All through the C ABI. The headline workload is the Llama-3-8B-shaped GQA batch (32 q / 8 kv
 heads, head dim 128, batch 8, prefix 4096, 60-node EAGLE-2-style trees, bf16).
 
 Inputs are generated once on the host, copied to HBM, and replicated into
@@ -620,32 +621,45 @@ def main() -> None:
         else:
             cm = (P(s["k_cache"]), P(s["v_cache"]), B, w.Hkv, w.cap, w.D, a.dtype, P(plen), P(acc_len),
                   P(path), n_max, P(plen_out), sp)
-        acm = (P(tok), P(tgt), P(parents), P(anc), P(depth), P(n_nodes), P(err), B, n_max, P(acc_len), P(path),
-               P(bonus), P(toks), P(s["k_cache"]), P(s["v_cache"]), w.Hkv, w.cap, w.D, a.dtype, P(plen), P(plen_out),
-               sp)
+        if paged:
+            acm = (P(tok), P(tgt), P(parents), P(anc), P(depth), P(n_nodes), P(err), B, n_max, P(acc_len), P(path),
+                   P(bonus), P(toks), P(s["k_cache"]), P(s["v_cache"]), ctypes.byref(s["pk"]), w.Hkv, w.D, a.dtype,
+                   P(plen), P(plen_out), sp)
+        else:
+            acm = (P(tok), P(tgt), P(parents), P(anc), P(depth), P(n_nodes), P(err), B, n_max, P(acc_len), P(path),
+                   P(bonus), P(toks), P(s["k_cache"]), P(s["v_cache"]), w.Hkv, w.cap, w.D, a.dtype, P(plen),
+                   P(plen_out), sp)
         calls.append((a, cm, acm))
     commit_fn = lib.tv_commit_paged if paged else lib.tv_commit
     bt = (P(parents), P(n_nodes), B, n_max, P(anc), P(depth), P(err), sp)
     ac = (P(tok), P(tgt), P(parents), P(anc), P(depth), P(n_nodes), P(err), B, n_max, P(acc_len),
           P(path), P(bonus), P(toks), sp)
 
-    # The dense step builds the tree inside the attention kernel
-    # (tv_tree_attention_from_parents writes anc, depth and err for the
-    # accept); the paged step calls tv_build_tree first.
-    separate = paged or args.separate_tree
+    # The step builds the tree inside the attention kernel
+    # (tv_tree_attention_from_parents, or its paged form, writes anc, depth
+    # and err for the accept), then accepts and commits in one launch;
+    # --separate-tree makes it tv_build_tree + tv_tree_attention(_paged) +
+    # tv_accept + tv_commit(_paged) for comparison.
+    separate = args.separate_tree
 
     def attention(k: int) -> int:
         if paged:
-            return lib.tv_tree_attention_paged(ctypes.byref(calls[k % copies][0]),
-                                               ctypes.byref(sets[k % copies]["pk"]), sp)
+            if separate:
+                return lib.tv_tree_attention_paged(ctypes.byref(calls[k % copies][0]),
+                                                   ctypes.byref(sets[k % copies]["pk"]), sp)
+            return lib.tv_tree_attention_paged_from_parents(ctypes.byref(calls[k % copies][0]),
+                                                            ctypes.byref(sets[k % copies]["pk"]), P(parents),
+                                                            P(anc), P(depth), sp)
         if separate:
             return lib.tv_tree_attention(ctypes.byref(calls[k % copies][0]), sp)
         return lib.tv_tree_attention_from_parents(ctypes.byref(calls[k % copies][0]), P(parents), P(anc), P(depth),
                                                   sp)
 
     def accept_commit(k: int) -> int:
-        if paged:
+        if separate:
             return lib.tv_accept(*ac) | commit_fn(*calls[k % copies][1])
+        if paged:
+            return lib.tv_accept_commit_paged(*calls[k % copies][2])
         return lib.tv_accept_commit(*calls[k % copies][2])
 
     def step(k: int) -> None:
@@ -736,8 +750,9 @@ def main() -> None:
                    "seed": args.config if args.seed is None else args.seed},
         "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                      "frac": achieved / peak, "traffic": traffic,
-                     "kernel": ("tv_tree_attention_paged call" if paged else "tv_tree_attention call" if separate
-                                else "tv_tree_attention_from_parents call (the tree built in the kernel)") +
+                     "kernel": (("tv_tree_attention_paged" if paged else "tv_tree_attention") + " call" if separate
+                                else ("tv_tree_attention_paged_from_parents" if paged else
+                                      "tv_tree_attention_from_parents") + " call (the tree built in the kernel)") +
                                ": attn_bf16_kernel (key splits merged and tree appended inside the kernel on the "
                                "automatic plan; merge_bf16_kernel otherwise); its average duration from HIP "
                                "events on its stream around K calls back to back (attention_us_mean: an event pair "

@@ -218,7 +218,8 @@ tv_status tv_tree_attention(const tv_attn_args* a, hipStream_t stream);
  * tv_build_tree followed by tv_tree_attention; the pair feeds tv_accept /
  * tv_accept_commit as usual.
  * Host checks: those of tv_tree_attention, and parents, anc and depth
- * non-null unless B == 0. The paged cache is not offered here.
+ * non-null unless B == 0. tv_tree_attention_paged_from_parents is the
+ * paged-cache form.
  */
 tv_status tv_tree_attention_from_parents(const tv_attn_args* a, const int32_t* parents, uint64_t* anc,
                                          int32_t* depth, hipStream_t stream);
@@ -279,6 +280,26 @@ typedef struct tv_paged_kv {
  */
 tv_status tv_tree_attention_paged(const tv_attn_args* a, const tv_paged_kv* pk,
                                   hipStream_t stream);
+
+/*
+ * tv_tree_attention_paged_from_parents -- tv_build_tree and
+ * tv_tree_attention_paged in one launch: the tree mask and depths of
+ * infra-guide "5.3 Medusa、EAGLE 与 MTP" (sections 3.1, 3.2, 8) built inside
+ * the attention kernel over a paged cache (the page-table layout and the
+ * per-request tree boundaries of that page's section 8).
+ *   a, pk     as for tv_tree_attention_paged, except that a->anc and
+ *             a->depth are not read, and a->err is output only: it receives
+ *             TV_ERR_BAD_TREE as tv_build_tree writes it, else
+ *             TV_ERR_CAPACITY, else TV_ERR_BAD_PAGE as
+ *             tv_tree_attention_paged sets them, else 0
+ *   parents, anc, depth  as for tv_tree_attention_from_parents
+ * anc, depth, err, out and the append into the pages are bit for bit those of
+ * tv_build_tree followed by tv_tree_attention_paged.
+ * Host checks: those of tv_tree_attention_paged, and parents, anc and depth
+ * non-null unless B == 0.
+ */
+tv_status tv_tree_attention_paged_from_parents(const tv_attn_args* a, const tv_paged_kv* pk, const int32_t* parents,
+                                               uint64_t* anc, int32_t* depth, hipStream_t stream);
 
 /*
  * tv_accept -- greedy longest-accepted-path selection.
@@ -461,6 +482,23 @@ tv_status tv_commit_paged(void* k_pool, void* v_pool, const tv_paged_kv* pk, int
                           int32_t Hkv, int32_t D, int32_t dtype, const int32_t* prefix_len_in,
                           const int32_t* accept_len, const int32_t* path, int32_t n_max,
                           int32_t* prefix_len_out, hipStream_t stream);
+
+/*
+ * tv_accept_commit_paged -- tv_accept followed by tv_commit_paged, in one
+ * launch: the arguments, outputs and effect of tv_accept_commit with the K
+ * and V page pools and block table of tv_commit_paged instead of the dense
+ * cache (cap = 64 * pk->max_pages). A move touching a page outside the pools
+ * leaves that sequence's cache and prefix length unchanged, as with
+ * tv_commit_paged; the accept outputs are written regardless.
+ * Host checks as tv_accept_commit and tv_commit_paged, plus
+ * max_pages <= TV_MAX_PAGES_PER_SEQ, else TV_ERR_UNSUPPORTED.
+ */
+tv_status tv_accept_commit_paged(const int32_t* cand_tok, const int32_t* tgt_argmax, const int32_t* parents,
+                                 const uint64_t* anc, const int32_t* depth, const int32_t* n_nodes,
+                                 const int32_t* err, int32_t B, int32_t n_max, int32_t* accept_len, int32_t* path,
+                                 int32_t* bonus_tok, int32_t* out_tokens, void* k_pool, void* v_pool,
+                                 const tv_paged_kv* pk, int32_t Hkv, int32_t D, int32_t dtype,
+                                 const int32_t* prefix_len_in, int32_t* prefix_len_out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

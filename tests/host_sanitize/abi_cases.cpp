@@ -275,6 +275,37 @@ void attention() {
   c = stub::calls;
   EXPECT(tv_commit_paged(F, F, &p, 2, 2, 128, TV_BF16, I, I, I, 5, I, nullptr), TV_OK);
   REACHED(c, "commit_paged");
+
+  // the paged fused calls: the checks of their separate calls
+  EXPECT(tv_tree_attention_paged_from_parents(&ok, nullptr, I, U, I, nullptr), TV_ERR_INVALID_ARG);
+  EXPECT(tv_tree_attention_paged_from_parents(&ok, &pn, I, U, I, nullptr), TV_ERR_INVALID_ARG);
+  EXPECT(tv_tree_attention_paged_from_parents(&ok, &p, nullptr, U, I, nullptr), TV_ERR_INVALID_ARG);
+  EXPECT(tv_tree_attention_paged_from_parents(&ok, &p, I, nullptr, I, nullptr), TV_ERR_INVALID_ARG);
+  EXPECT(tv_tree_attention_paged_from_parents(&ok, &p, I, U, nullptr, nullptr), TV_ERR_INVALID_ARG);
+  a = attn(8, 60, 32, 8, 128, 300 * 64);
+  EXPECT(tv_tree_attention_paged_from_parents(&a, &p300, I, U, I, nullptr), TV_ERR_UNSUPPORTED);
+  a = attn(8, 60, 32, 8, 64, 65 * 64, TV_F32);
+  EXPECT(tv_tree_attention_paged_from_parents(&a, &p, I, U, I, nullptr), TV_ERR_UNSUPPORTED);
+  a = attn(0, 60, 32, 8, 128, 65 * 64);
+  EXPECT(tv_tree_attention_paged_from_parents(&a, &p, nullptr, nullptr, nullptr, nullptr), TV_OK);
+  c = stub::calls;
+  EXPECT(tv_tree_attention_paged_from_parents(&ok, &p, I, U, I, nullptr), TV_OK);
+  REACHED(c, "attention_bf16_paged_build");
+  auto acp = [](const tv_paged_kv* pp, int B, int n_max, int D, int dtype, void* k) {
+    return tv_accept_commit_paged(I, I, I, U, I, I, nullptr, B, n_max, I, I, I, nullptr, k, F, pp, 8, D, dtype, I, I,
+                                  nullptr);
+  };
+  EXPECT(acp(nullptr, 1, 5, 128, TV_BF16, F), TV_ERR_INVALID_ARG);
+  EXPECT(acp(&pn, 1, 5, 128, TV_BF16, F), TV_ERR_INVALID_ARG);
+  EXPECT(acp(&p, 1, 65, 128, TV_BF16, F), TV_ERR_INVALID_ARG);
+  EXPECT(acp(&p, 1, 5, 96, TV_BF16, F), TV_ERR_UNSUPPORTED);
+  EXPECT(acp(&p300, 1, 5, 128, TV_BF16, F), TV_ERR_UNSUPPORTED);
+  EXPECT(acp(&p, 1, 5, 128, 7, F), TV_ERR_INVALID_ARG);
+  EXPECT(acp(&p, 1, 5, 128, TV_BF16, nullptr), TV_ERR_INVALID_ARG);
+  EXPECT(acp(&p, 0, 5, 128, TV_BF16, nullptr), TV_OK);
+  c = stub::calls;
+  EXPECT(acp(&p, 8, 60, 128, TV_BF16, F), TV_OK);
+  REACHED(c, "accept_commit");
 }
 
 void drafting_and_sampling() {

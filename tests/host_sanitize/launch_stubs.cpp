@@ -52,8 +52,9 @@ hipError_t launch_typical_stats(const void*, int elem_bytes, int, const int32_t*
 hipError_t launch_accept_commit(const int32_t*, const int32_t*, const int32_t*, const uint64_t*, const int32_t*,
                                 const int32_t*, const int32_t*, int B, int n_max, int32_t*, int32_t*, int32_t*,
                                 int32_t*, void*, void*, int, int, int, int elem_bytes, const int32_t*, int32_t*,
-                                hipStream_t) {
+                                const tv_paged_kv* pk, hipStream_t) {
   stub::hit("accept_commit", B, n_max, elem_bytes, 0, nullptr);
+  (void)pk;
   return hipSuccess;
 }
 hipError_t launch_commit(void*, void*, int B, int, int, int, int elem_bytes, const int32_t*, const int32_t*,
@@ -77,8 +78,9 @@ AttnPlan plan_attention_bf16(const tv_attn_args* a) {
 }
 hipError_t launch_attention_bf16(const tv_attn_args* a, const AttnPlan&, const tv_paged_kv* pk, const int32_t* parents,
                                  hipStream_t) {
-  stub::hit(pk ? "attention_bf16_paged" : parents ? "attention_bf16_build" : "attention_bf16", a->B, a->n_max, 2,
-            a->workspace_bytes, a->workspace);
+  stub::hit(pk ? (parents ? "attention_bf16_paged_build" : "attention_bf16_paged")
+               : parents ? "attention_bf16_build" : "attention_bf16",
+            a->B, a->n_max, 2, a->workspace_bytes, a->workspace);
   return hipSuccess;
 }
 hipError_t launch_attention_f32(const tv_attn_args* a, hipStream_t) {

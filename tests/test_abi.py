@@ -24,7 +24,8 @@ def declared_functions():
 def test_header_declares_expected_calls():
     names = declared_functions()
     for must in ("tv_build_tree", "tv_tree_attention", "tv_accept", "tv_commit", "tv_accept_typical",
-                 "tv_tree_attention_paged", "tv_commit_paged", "tv_eagle2_tree", "tv_speculative_sample"):
+                 "tv_tree_attention_paged", "tv_commit_paged", "tv_eagle2_tree", "tv_speculative_sample",
+                 "tv_tree_attention_paged_from_parents", "tv_accept_commit_paged"):
         assert must in names
 
 
@@ -245,3 +246,50 @@ def test_accept_commit_host_validation_without_device():
     assert call(k=None) == _lib.TV_ERR_INVALID_ARG
     assert call(plen_out=None) == _lib.TV_ERR_INVALID_ARG
     assert call(B=0, k=None) == _lib.TV_OK
+
+
+def test_paged_fused_host_validation_without_device():
+    """tv_tree_attention_paged_from_parents and tv_accept_commit_paged: the
+    checks of their separate calls, no device needed."""
+    lib = _lib.load()
+    fake = ctypes.c_void_p(0x1000)
+    null = None
+
+    def pk(max_pages=65, num_pages=100, table=0x2000):
+        p = _lib.TvPagedKv()
+        p.block_table, p.max_pages, p.num_pages = table, max_pages, num_pages
+        return p
+
+    def attn_call(a, p, parents=fake, anc=fake, depth=fake):
+        return lib.tv_tree_attention_paged_from_parents(ctypes.byref(a), None if p is None else ctypes.byref(p),
+                                                        parents, anc, depth, null)
+    ok_args = attn(cap=65 * 64, workspace=0x3000, workspace_bytes=1 << 40)
+    assert attn_call(ok_args, None) == _lib.TV_ERR_INVALID_ARG
+    assert attn_call(ok_args, pk(table=0)) == _lib.TV_ERR_INVALID_ARG
+    assert attn_call(ok_args, pk(num_pages=0)) == _lib.TV_ERR_INVALID_ARG
+    assert attn_call(attn(cap=64 * 64), pk()) == _lib.TV_ERR_INVALID_ARG          # cap != 64 max_pages
+    assert attn_call(attn(cap=300 * 64), pk(max_pages=300)) == _lib.TV_ERR_UNSUPPORTED
+    assert attn_call(attn(cap=65 * 64, dtype=_lib.TV_F32, D=64), pk()) == _lib.TV_ERR_UNSUPPORTED
+    assert attn_call(ok_args, pk(), parents=None) == _lib.TV_ERR_INVALID_ARG
+    assert attn_call(ok_args, pk(), anc=None) == _lib.TV_ERR_INVALID_ARG
+    assert attn_call(ok_args, pk(), depth=None) == _lib.TV_ERR_INVALID_ARG
+    assert attn_call(attn(cap=65 * 64, B=0), pk(), parents=None) == _lib.TV_OK
+
+    def ac_call(p, B=1, n_max=5, Hkv=8, D=128, dtype=_lib.TV_BF16, k=fake, plen_out=fake):
+        return lib.tv_accept_commit_paged(fake, fake, fake, fake, fake, fake, null, B, n_max, fake, fake, fake, null,
+                                          k, fake, None if p is None else ctypes.byref(p), Hkv, D, dtype, fake,
+                                          plen_out, null)
+    assert ac_call(None) == _lib.TV_ERR_INVALID_ARG
+    assert ac_call(pk(table=0)) == _lib.TV_ERR_INVALID_ARG
+    assert ac_call(pk(max_pages=0)) == _lib.TV_ERR_INVALID_ARG
+    assert ac_call(pk(num_pages=0)) == _lib.TV_ERR_INVALID_ARG
+    assert ac_call(pk(), B=-1) == _lib.TV_ERR_INVALID_ARG
+    assert ac_call(pk(), n_max=65) == _lib.TV_ERR_INVALID_ARG
+    assert ac_call(pk(max_pages=1, num_pages=1), n_max=65) == _lib.TV_ERR_INVALID_ARG
+    assert ac_call(pk(), Hkv=0) == _lib.TV_ERR_INVALID_ARG
+    assert ac_call(pk(), dtype=7) == _lib.TV_ERR_INVALID_ARG
+    assert ac_call(pk(), D=96) == _lib.TV_ERR_UNSUPPORTED
+    assert ac_call(pk(max_pages=300)) == _lib.TV_ERR_UNSUPPORTED
+    assert ac_call(pk(), k=None) == _lib.TV_ERR_INVALID_ARG
+    assert ac_call(pk(), plen_out=None) == _lib.TV_ERR_INVALID_ARG
+    assert ac_call(pk(), B=0, k=None) == _lib.TV_OK

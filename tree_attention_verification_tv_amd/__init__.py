@@ -26,9 +26,10 @@ from . import _lib
 from ._lib import (PAGE, TV_BF16, TV_ERR_BAD_PAGE, TV_ERR_BAD_TREE, TV_ERR_CAPACITY, TV_F32,  # noqa: F401
                    TV_MAX_NODES, TvAttnArgs, TvError, TvPagedKv)
 
-__all__ = ["build_tree", "tree_attention", "tree_attention_from_parents", "tree_attention_noalloc", "accept_commit", "tree_attention_workspace_size", "new_workspace", "accept",
-           "accept_typical", "commit", "eagle2_tree", "speculative_sample", "tree_attention_paged", "commit_paged", "pages_from_dense",
-           "dense_from_pages", "TV_ERR_BAD_PAGE", "PAGE",
+__all__ = ["build_tree", "tree_attention", "tree_attention_from_parents", "tree_attention_paged_from_parents",
+           "tree_attention_noalloc", "accept_commit", "accept_commit_paged", "tree_attention_workspace_size",
+           "new_workspace", "accept", "accept_typical", "commit", "eagle2_tree", "speculative_sample",
+           "tree_attention_paged", "commit_paged", "pages_from_dense", "dense_from_pages", "TV_ERR_BAD_PAGE", "PAGE",
            "version", "TvError", "TV_ERR_BAD_TREE", "TV_ERR_CAPACITY", "attn_args",
            "v_cache_blocked", "v_cache_rows", "V_BLOCK"]
 
@@ -309,6 +310,38 @@ def tree_attention_paged(q, k_new, v_new, k_pool, v_pool, block_table, prefix_le
     return out
 
 
+def tree_attention_paged_from_parents(q, k_new, v_new, k_pool, v_pool, block_table, prefix_len, n_nodes, parents,
+                                      rope_theta=10000.0, softmax_scale=0.0, out=None, workspace=None, stream=None):
+    """build_tree and tree_attention_paged in one launch: returns
+    (out, anc, depth, err), bit for bit those of the two calls."""
+    lib = _lib.load()
+    _dev(parents, "parents", torch.int32)
+    B, n_max = q.shape[0], q.shape[1]
+    if tuple(parents.shape) != (B, n_max):
+        raise ValueError("parents must be [B, n_max]")
+    dev = q.device
+    anc = torch.empty(B, n_max, dtype=torch.int64, device=dev)
+    depth = torch.empty(B, n_max, dtype=torch.int32, device=dev)
+    err = torch.empty(B, dtype=torch.int32, device=dev)
+    if out is None:
+        out = torch.empty_like(q)
+    a = attn_args(q, k_new, v_new, k_pool, v_pool, prefix_len, n_nodes, anc, depth, err, out,
+                  rope_theta, softmax_scale, workspace, block_table=block_table)
+    pk = paged_kv(block_table, k_pool)
+    need = tree_attention_workspace_size(a)
+    if need > a.workspace_bytes:
+        if workspace is not None:
+            raise ValueError(f"workspace holds {a.workspace_bytes} bytes, {need} needed")
+        workspace = _default_workspace(q.device, need, stream)
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
+    _lib.check("tv_tree_attention_paged_from_parents",
+               lib.tv_tree_attention_paged_from_parents(ctypes.byref(a), ctypes.byref(pk),
+                                                        ctypes.c_void_p(parents.data_ptr()),
+                                                        ctypes.c_void_p(anc.data_ptr()),
+                                                        ctypes.c_void_p(depth.data_ptr()), _stream(stream)))
+    return out, anc, depth, err
+
+
 def commit_paged(k_pool, v_pool, block_table, prefix_len_in, accept_len, path, prefix_len_out=None,
                  stream=None):
     """commit over a paged cache (layout as tree_attention_paged)."""
@@ -506,4 +539,40 @@ def accept_commit(cand_tok, tgt_argmax, parents, anc, depth, n_nodes, err, k_cac
         _ptr(cand_tok), _ptr(tgt_argmax), _ptr(parents), _ptr(anc), _ptr(depth), _ptr(n_nodes), _ptr(err), B, n_max,
         _ptr(accept_len), _ptr(path), _ptr(bonus), _ptr(out_tokens), _ptr(k_cache), _ptr(v_cache), Hkv, cap, D,
         _DTYPES[k_cache.dtype], _ptr(prefix_len_in), _ptr(prefix_len_out), _stream(stream)))
+    return accept_len, path, bonus, out_tokens, prefix_len_out
+
+
+def accept_commit_paged(cand_tok, tgt_argmax, parents, anc, depth, n_nodes, err, k_pool, v_pool, block_table,
+                        prefix_len_in, prefix_len_out=None, want_tokens=True, stream=None):
+    """accept followed by commit_paged in one launch (pools and table as
+    tree_attention_paged): returns (accept_len, path, bonus, out_tokens or
+    None, prefix_len_out)."""
+    lib = _lib.load()
+    for name, t in (("cand_tok", cand_tok), ("tgt_argmax", tgt_argmax), ("parents", parents),
+                    ("depth", depth), ("n_nodes", n_nodes), ("prefix_len_in", prefix_len_in)):
+        _dev(t, name, torch.int32)
+    _dev(anc, "anc", torch.int64)
+    if err is not None:
+        _dev(err, "err", torch.int32)
+    if k_pool.dtype not in _DTYPES:
+        raise ValueError("pools must be float32 or bfloat16")
+    _dev(k_pool, "k_pool", k_pool.dtype)
+    _dev(v_pool, "v_pool", k_pool.dtype)
+    n_pages, Hkv, _, D = k_pool.shape
+    if tuple(v_pool.shape) != (n_pages, Hkv, D, PAGE):
+        raise ValueError("v_pool must be [num_pages, Hkv, D, 64]")
+    pk = paged_kv(block_table, k_pool)
+    B, n_max = parents.shape
+    dev = parents.device
+    accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    path = torch.empty((B, n_max), dtype=torch.int32, device=dev)
+    bonus = torch.empty(B, dtype=torch.int32, device=dev)
+    out_tokens = torch.empty((B, n_max), dtype=torch.int32, device=dev) if want_tokens else None
+    if prefix_len_out is None:
+        prefix_len_out = torch.empty_like(prefix_len_in)
+    _dev(prefix_len_out, "prefix_len_out", torch.int32)
+    _lib.check("tv_accept_commit_paged", lib.tv_accept_commit_paged(
+        _ptr(cand_tok), _ptr(tgt_argmax), _ptr(parents), _ptr(anc), _ptr(depth), _ptr(n_nodes), _ptr(err), B, n_max,
+        _ptr(accept_len), _ptr(path), _ptr(bonus), _ptr(out_tokens), _ptr(k_pool), _ptr(v_pool), ctypes.byref(pk),
+        Hkv, D, _DTYPES[k_pool.dtype], _ptr(prefix_len_in), _ptr(prefix_len_out), _stream(stream)))
     return accept_len, path, bonus, out_tokens, prefix_len_out

@@ -51,6 +51,8 @@ SIGNATURES = {
     "tv_tree_attention_noalloc": (_I, [ctypes.POINTER(TvAttnArgs), _P]),
     "tv_tree_attention_from_parents": (_I, [ctypes.POINTER(TvAttnArgs), _P, _P, _P, _P]),
     "tv_tree_attention_paged": (_I, [ctypes.POINTER(TvAttnArgs), ctypes.POINTER(TvPagedKv), _P]),
+    "tv_tree_attention_paged_from_parents": (_I, [ctypes.POINTER(TvAttnArgs), ctypes.POINTER(TvPagedKv), _P, _P, _P,
+                                                  _P]),
     "tv_accept": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P]),
     "tv_eagle2_tree": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]),
     "tv_speculative_sample_workspace_size": (ctypes.c_size_t, [_I, _I]),
@@ -61,6 +63,8 @@ SIGNATURES = {
     "tv_accept_commit": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P,
                               _P]),
     "tv_commit_paged": (_I, [_P, _P, ctypes.POINTER(TvPagedKv), _I, _I, _I, _I, _P, _P, _P, _I, _P, _P]),
+    "tv_accept_commit_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P,
+                                    ctypes.POINTER(TvPagedKv), _I, _I, _I, _P, _P, _P]),
 }
 
 _lib = None

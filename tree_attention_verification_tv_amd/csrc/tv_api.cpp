@@ -136,6 +136,26 @@ tv_status tv_tree_attention_paged(const tv_attn_args* a, const tv_paged_kv* pk, 
   return from_hip(tv::launch_attention_bf16(a, plan, pk, nullptr, stream));
 }
 
+tv_status tv_tree_attention_paged_from_parents(const tv_attn_args* a, const tv_paged_kv* pk, const int32_t* parents,
+                                               uint64_t* anc, int32_t* depth, hipStream_t stream) {
+  const tv_status st = check_attn_shapes(a);
+  if (st != TV_OK) return st;
+  if (pk == nullptr || pk->max_pages < 1 || pk->num_pages < 1) return TV_ERR_INVALID_ARG;
+  if (a->cap != 64 * pk->max_pages) return TV_ERR_INVALID_ARG;
+  if (a->dtype != TV_BF16 || a->D != 128 || pk->max_pages > TV_MAX_PAGES_PER_SEQ) return TV_ERR_UNSUPPORTED;
+  if (a->B == 0) return TV_OK;
+  if (!a->q || !a->k_new || !a->v_new || !a->k_cache || !a->v_cache || !a->prefix_len ||
+      !a->n_nodes || !a->err || !a->out || !pk->block_table || !parents || !anc || !depth)
+    return TV_ERR_INVALID_ARG;
+  const tv::AttnPlan plan = tv::plan_attention_bf16(a);
+  if (plan.workspace_bytes > 0 && (a->workspace == nullptr || a->workspace_bytes < plan.workspace_bytes))
+    return TV_ERR_INVALID_ARG;
+  tv_attn_args b = *a;
+  b.anc = anc;
+  b.depth = depth;
+  return from_hip(tv::launch_attention_bf16(&b, plan, pk, parents, stream));
+}
+
 tv_status tv_accept(const int32_t* cand_tok, const int32_t* tgt_argmax, const int32_t* parents,
                     const uint64_t* anc, const int32_t* depth, const int32_t* n_nodes,
                     const int32_t* err, int32_t B, int32_t n_max, int32_t* accept_len,
@@ -165,7 +185,28 @@ tv_status tv_accept_commit(const int32_t* cand_tok, const int32_t* tgt_argmax, c
     return TV_ERR_INVALID_ARG;
   return from_hip(tv::launch_accept_commit(cand_tok, tgt_argmax, parents, anc, depth, n_nodes, err, B, n_max,
                                            accept_len, path, bonus_tok, out_tokens, k_cache, v_cache, Hkv, cap, D,
-                                           elem_bytes(dtype), prefix_len_in, prefix_len_out, stream));
+                                           elem_bytes(dtype), prefix_len_in, prefix_len_out, nullptr, stream));
+}
+
+tv_status tv_accept_commit_paged(const int32_t* cand_tok, const int32_t* tgt_argmax, const int32_t* parents,
+                                 const uint64_t* anc, const int32_t* depth, const int32_t* n_nodes,
+                                 const int32_t* err, int32_t B, int32_t n_max, int32_t* accept_len, int32_t* path,
+                                 int32_t* bonus_tok, int32_t* out_tokens, void* k_pool, void* v_pool,
+                                 const tv_paged_kv* pk, int32_t Hkv, int32_t D, int32_t dtype,
+                                 const int32_t* prefix_len_in, int32_t* prefix_len_out, hipStream_t stream) {
+  if (pk == nullptr || pk->max_pages < 1 || pk->num_pages < 1) return TV_ERR_INVALID_ARG;
+  if (B < 0 || n_max < 1 || n_max > TV_MAX_NODES || Hkv < 1 || 64 * pk->max_pages < n_max)
+    return TV_ERR_INVALID_ARG;
+  if (!dtype_ok(dtype)) return TV_ERR_INVALID_ARG;
+  if ((D != 64 && D != 128) || pk->max_pages > TV_MAX_PAGES_PER_SEQ) return TV_ERR_UNSUPPORTED;
+  if (B == 0) return TV_OK;
+  if (!cand_tok || !tgt_argmax || !parents || !anc || !depth || !n_nodes || !accept_len || !path ||
+      !bonus_tok || !k_pool || !v_pool || !pk->block_table || !prefix_len_in || !prefix_len_out)
+    return TV_ERR_INVALID_ARG;
+  return from_hip(tv::launch_accept_commit(cand_tok, tgt_argmax, parents, anc, depth, n_nodes, err, B, n_max,
+                                           accept_len, path, bonus_tok, out_tokens, k_pool, v_pool, Hkv,
+                                           64 * pk->max_pages, D, elem_bytes(dtype), prefix_len_in, prefix_len_out,
+                                           pk, stream));
 }
 
 tv_status tv_eagle2_tree(const float* conf, const int32_t* cand, const int32_t* root_tok, int32_t B,

@@ -981,10 +981,10 @@ __device__ __forceinline__ void merge_claim_and_run(const BfParams& p, int grp, 
 // wavefront, by build_tree_lane, from one load of the parent of node `lane`)
 // instead of loading depths and ancestor masks, and the workgroup (b, g = 0,
 // row block 0, split 0) writes anc, depth and err as tv_build_tree would
-// (err also TV_ERR_CAPACITY as below).
+// (err also TV_ERR_CAPACITY, and with a paged cache TV_ERR_BAD_PAGE, as the
+// attention call after tv_build_tree would set them).
 template <int WAVES, int QT, bool PAGED, bool BUILD>
 __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
-  static_assert(!(PAGED && BUILD), "the tree is built in the dense instances only");
   constexpr int NT = WAVES * 64;
   constexpr int ROWS = WAVES * 32 * QT;      // query rows of the workgroup
   constexpr int CPT = (kKT * kD / 8) / NT;   // 16-byte chunks per thread per K (or V) stage
@@ -1083,26 +1083,28 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
 
   // BUILD: wavefront 0 of the writing workgroup stores the sequence's tree
   // (as tv_build_tree: zeros for padding nodes and invalid trees) and its
-  // error word (a bad tree, else a capacity error, else 0). Called once all
+  // error word (a bad tree, else a capacity error, else a page outside the
+  // pools, else 0: the precedence of the separate calls). Called once all
   // loads have landed and nothing else is in flight.
-  auto write_tree = [&](const LaneTree& tr) __attribute__((always_inline)) {
+  auto write_tree = [&](const LaneTree& tr, bool bad_page) __attribute__((always_inline)) {
     if (BUILD && tree_writer && wave == 0) {
       if (lane < p.n_max) {
         p.anc[static_cast<size_t>(b) * p.n_max + lane] = tr.anc;
         p.depth[static_cast<size_t>(b) * p.n_max + lane] = tr.depth;
       }
-      if (lane == 0) p.err[b] = !tr.ok ? TV_ERR_BAD_TREE : sq.cap_bad ? TV_ERR_CAPACITY : 0;
+      if (lane == 0)
+        p.err[b] = !tr.ok ? TV_ERR_BAD_TREE : sq.cap_bad ? TV_ERR_CAPACITY : bad_page ? TV_ERR_BAD_PAGE : 0;
     }
   };
 
   // A workgroup with nothing to compute: its loads land before its LDS is
   // given up; with separate split merging the merge kernel writes the zero
   // rows, else (one split, or the fused merge: split 0) it does.
-  auto retire = [&](int first_row) __attribute__((always_inline)) {
+  auto retire = [&](int first_row, bool bad_page) __attribute__((always_inline)) {
     wait_vm<0>();
     if constexpr (BUILD) {
       landed(par_lane);
-      write_tree(build_tree_lane(static_cast<int>(par_lane), n, p.n_max, lane));
+      write_tree(build_tree_lane(static_cast<int>(par_lane), n, p.n_max, lane), bad_page);
     }
     if (p.splits == 1 || (p.fused && s == 0)) {
       for (int r = first_row + tid / 16; r < min(rb0 + ROWS, rows_all); r += NT / 16) {
@@ -1113,7 +1115,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
     }
   };
   if (rb0 >= rows_live) {
-    retire(rb0);   // nothing live in this row block
+    retire(rb0, false);   // nothing live in this row block
     return;
   }
   bool row_live[QT];
@@ -1133,7 +1135,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
     landed(par_lane);
     tree = build_tree_lane(static_cast<int>(par_lane), n, p.n_max, lane);
     if (!tree.ok) {
-      retire(rb0);
+      retire(rb0, false);
       return;
     }
     dep_lane = static_cast<uint32_t>(tree.depth);
@@ -1314,8 +1316,9 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
       bad |= lane + 64 * u < tiles_all && (page < 0 || page >= p.num_pages);
     }
     if (__any(bad)) {
-      if (g == 0 && rb == 0 && s == 0 && tid == 0) p.err[b] = TV_ERR_BAD_PAGE;
-      retire(rb0);
+      // (building the tree, the writing workgroup stores the error with it)
+      if (!BUILD && g == 0 && rb == 0 && s == 0 && tid == 0) p.err[b] = TV_ERR_BAD_PAGE;
+      retire(rb0, true);
       return;
     }
   }
@@ -1727,7 +1730,7 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
     run_pass(std::integral_constant<int, 2>{});
   }
 
-  if constexpr (BUILD) write_tree(tree);   // (nothing is in flight here)
+  if constexpr (BUILD) write_tree(tree, false);   // (nothing is in flight here)
 
   // ---- epilogue
   float l_row[QT];
@@ -2095,7 +2098,11 @@ hipError_t launch_attention_bf16(const tv_attn_args* a, const AttnPlan& pl, cons
     case 81: hipLaunchKernelGGL((attn_bf16_kernel<8, 1, false, false>), grid, dim3(512), 0, s, p); break;
     case 181: hipLaunchKernelGGL((attn_bf16_kernel<8, 1, true, false>), grid, dim3(512), 0, s, p); break;
     case 281: hipLaunchKernelGGL((attn_bf16_kernel<8, 1, false, true>), grid, dim3(512), 0, s, p); break;
-    default: return hipErrorInvalidValue;   // (a paged cache with a parents array: refused by the host checks)
+    case 321: hipLaunchKernelGGL((attn_bf16_kernel<2, 1, true, true>), grid, dim3(128), 0, s, p); break;
+    case 341: hipLaunchKernelGGL((attn_bf16_kernel<4, 1, true, true>), grid, dim3(256), 0, s, p); break;
+    case 342: hipLaunchKernelGGL((attn_bf16_kernel<4, 2, true, true>), grid, dim3(256), 0, s, p); break;
+    case 381: hipLaunchKernelGGL((attn_bf16_kernel<8, 1, true, true>), grid, dim3(512), 0, s, p); break;
+    default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

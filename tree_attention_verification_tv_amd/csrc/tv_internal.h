@@ -45,7 +45,7 @@ hipError_t launch_accept_commit(const int32_t* cand_tok, const int32_t* tgt, con
                                 const int32_t* err, int B, int n_max, int32_t* accept_len, int32_t* path,
                                 int32_t* bonus, int32_t* out_tokens, void* k_cache, void* v_cache, int Hkv,
                                 int cap, int D, int elem_bytes, const int32_t* prefix_len_in,
-                                int32_t* prefix_len_out, hipStream_t s);
+                                int32_t* prefix_len_out, const tv_paged_kv* pk, hipStream_t s);
 
 // pk: paged cache (nullptr: the dense layout)
 hipError_t launch_commit(void* k_cache, void* v_cache, int B, int Hkv, int cap, int D,

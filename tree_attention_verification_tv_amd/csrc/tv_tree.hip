@@ -305,7 +305,8 @@ __global__ __launch_bounds__(256) void accept_commit_kernel(
     const int32_t* __restrict__ err, int n_max, int32_t* __restrict__ accept_len,
     int32_t* __restrict__ path, int32_t* __restrict__ bonus, int32_t* __restrict__ out_tokens,
     T* __restrict__ k_cache, T* __restrict__ v_cache, int Hkv, int cap, int D,
-    const int32_t* prefix_len_in, int32_t* prefix_len_out, int heads_per_block) {
+    const int32_t* prefix_len_in, int32_t* prefix_len_out, int heads_per_block,
+    const int32_t* __restrict__ bt, int max_pages, int num_pages) {
   // the tree's slots [P, P + n) of one KV head: K rows [slot][D], V [D][slot]
   constexpr int kRows = TV_MAX_NODES_DEV, kMaxD = 128;
   constexpr int EPC = 16 / static_cast<int>(sizeof(T));   // elements per 16-byte chunk
@@ -324,8 +325,38 @@ __global__ __launch_bounds__(256) void accept_commit_kernel(
   // tree rows that lie in the cache (any move from outside it is refused)
   const int nr = (P >= 0 && n_in > 0 && n_in <= n_max) ? max(0, min(n_in, cap - P)) : 0;
   const int kpr = D / EPC;   // 16-byte chunks per K row
-  // element offset of the 64-slot block holding `slot` (head g)
+  // With a paged cache (bt non-null, max_pages <= 256) lane l of pg[u] holds
+  // the page of block l + 64 u (loaded with the accept's loads, needing no
+  // prefix length); the tree's slots lie in the two blocks from P >> 6,
+  // whose pages are picked once (uniform) and clamped into the pools for
+  // addressing; whether they are pages of the pools is decided after the
+  // accept, like tv_commit_paged (a move through a bad page leaves the
+  // sequence unchanged).
+  // (the loads are unconditional, reading the prefix length again without a
+  // table, so that the compiler's wait counts stay exact)
+  uint32_t pg[4];
+  {
+    const int32_t* row = bt ? bt + static_cast<size_t>(b) * max_pages : prefix_len_in + b;
+    const int last = bt ? max_pages - 1 : 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) pg[u] = static_cast<uint32_t>(row[min((tid & 63) + 64 * u, last)]);
+  }
+  const int blk0 = nr > 0 ? P >> 6 : 0;
+  auto page_entry = [&](int blk) {
+    const int bc = min(blk, max_pages - 1);
+    const uint32_t reg = bc < 64 ? pg[0] : bc < 128 ? pg[1] : bc < 192 ? pg[2] : pg[3];
+    return static_cast<int>(__builtin_amdgcn_readlane(reg, bc & 63));
+  };
+  int e0 = 0, e1 = 0;
+  if (bt) {
+    e0 = page_entry(blk0);
+    e1 = page_entry(blk0 + 1);
+  }
+  const int page0 = min(max(e0, 0), max(num_pages - 1, 0)), page1 = min(max(e1, 0), max(num_pages - 1, 0));
+  // element offset of the 64-slot block holding `slot` (head g); paged: of
+  // the page holding it (slots of the two blocks from P >> 6 only)
   auto base = [=](int g, int slot) {
+    if (bt) return (static_cast<size_t>((slot >> 6) == blk0 ? page0 : page1) * Hkv + g) * 64 * D;
     return ((static_cast<size_t>(b) * Hkv + g) * cap + static_cast<size_t>(slot >> 6) * 64) * D;
   };
   // The tree rows of head g are loaded into registers, every load of a
@@ -407,8 +438,13 @@ __global__ __launch_bounds__(256) void accept_commit_kernel(
   }
   put_rows(kv, vv);
   __syncthreads();
-  // the path ascends, so its end node path[L] is the largest moved slot
-  const int L = (s_L >= 0 && P >= 0 && s_path[max(s_L, 0)] < nr) ? s_L : -1;
+  // the path ascends, so its end node path[L] is the largest moved slot;
+  // paged: the blocks from P >> 6 to that of slot P + path[L] must be pages
+  // of the pools
+  const int top = s_path[max(s_L, 0)];
+  const bool pages_ok = !bt || ((e0 >= 0 && e0 < num_pages) &&
+                                (((P + top) >> 6) == blk0 || (e1 >= 0 && e1 < num_pages)));
+  const int L = (s_L >= 0 && P >= 0 && top < nr && pages_ok) ? s_L : -1;
   if (blockIdx.x == 0 && tid == 0) prefix_len_out[b] = L >= 0 ? P + L + 1 : P;
   if (L < 0) return;
   move_rows(g_first, L);
@@ -458,7 +494,9 @@ hipError_t launch_accept_commit(const int32_t* cand_tok, const int32_t* tgt, con
                                 const int32_t* err, int B, int n_max, int32_t* accept_len, int32_t* path,
                                 int32_t* bonus, int32_t* out_tokens, void* k_cache, void* v_cache, int Hkv,
                                 int cap, int D, int elem_bytes, const int32_t* prefix_len_in,
-                                int32_t* prefix_len_out, hipStream_t s) {
+                                int32_t* prefix_len_out, const tv_paged_kv* pk, hipStream_t s) {
+  const int32_t* bt = pk ? pk->block_table : nullptr;
+  const int max_pages = pk ? pk->max_pages : 1, num_pages = pk ? pk->num_pages : 1;
   // one workgroup per (KV head, sequence), or per sequence when the new
   // prefix lengths overwrite the old ones
   const int hpb = (prefix_len_in == prefix_len_out) ? Hkv : 1;
@@ -466,11 +504,13 @@ hipError_t launch_accept_commit(const int32_t* cand_tok, const int32_t* tgt, con
   if (elem_bytes == 2) {
     hipLaunchKernelGGL(accept_commit_kernel<uint16_t>, grid, dim3(256), 0, s, cand_tok, tgt, parents, anc, depth,
                        n_nodes, err, n_max, accept_len, path, bonus, out_tokens, static_cast<uint16_t*>(k_cache),
-                       static_cast<uint16_t*>(v_cache), Hkv, cap, D, prefix_len_in, prefix_len_out, hpb);
+                       static_cast<uint16_t*>(v_cache), Hkv, cap, D, prefix_len_in, prefix_len_out, hpb, bt,
+                       max_pages, num_pages);
   } else {
     hipLaunchKernelGGL(accept_commit_kernel<uint32_t>, grid, dim3(256), 0, s, cand_tok, tgt, parents, anc, depth,
                        n_nodes, err, n_max, accept_len, path, bonus, out_tokens, static_cast<uint32_t*>(k_cache),
-                       static_cast<uint32_t*>(v_cache), Hkv, cap, D, prefix_len_in, prefix_len_out, hpb);
+                       static_cast<uint32_t*>(v_cache), Hkv, cap, D, prefix_len_in, prefix_len_out, hpb, bt,
+                       max_pages, num_pages);
   }
   return hipGetLastError();
 }
