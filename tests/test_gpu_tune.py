@@ -20,13 +20,17 @@ CASES = [(2, dict(prefix=300)), (3, dict(B=2, prefix=1100)), (4, dict(B=2, prefi
          (5, dict(B=6, prefix=(16, 300)))]
 # fused=0: the separate merge kernel on plans the automatic choice merges in
 # the kernel; splits=2 / 4: the fused merge with two and four splits;
-# fused=2: the fused merge in which only the last split to arrive merges
+# fused=2: the fused merge in which only the last split to arrive merges;
+# splits=3 / 6: split counts that do not divide the merge's items (the last
+# range takes the rest); splits 6 and 8 with fused=1: the fused merge for
+# five to eight splits (without fused=1 the merge kernel serves them)
 # waves=8: eight wavefronts of one 32-row tile each (two per SIMD), also
 # through the tree-building and paged instances
 PLANS = ["waves=2,qt=1", "waves=2,qt=1,splits=1", "waves=4,qt=1,splits=8", "qt=2,splits=2", "splits=1",
          "splits=16", "fused=0", "splits=2", "waves=4,qt=1,splits=4", "splits=4,fused=0",
          "waves=8", "waves=8,splits=1", "waves=8,fused=0", "waves=8,splits=16",
-         "fused=2", "splits=2,fused=2", "waves=4,qt=1,splits=4,fused=2"]
+         "fused=2", "splits=2,fused=2", "waves=4,qt=1,splits=4,fused=2",
+         "splits=3", "splits=6,fused=1", "waves=2,qt=1,splits=8,fused=1"]
 # the extra checks an eight-wavefront plan runs
 EIGHT = 3
 

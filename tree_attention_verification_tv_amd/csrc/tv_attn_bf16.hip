@@ -874,7 +874,9 @@ __device__ __forceinline__ void merge_range(const BfParams& p, int b, int g, int
                                             __amdgpu_buffer_rsrc_t rml, __amdgpu_buffer_rsrc_t ro) {
   constexpr int ROWS = WAVES * 32 * QT, NT = WAVES * 64, ITEMS = ROWS / 32 * 256;
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-  const int per = ITEMS / p.splits, lo = r * per, hi = lo + per;
+  // (the last range takes the remainder when the split count does not
+  // divide the items, e.g. three splits from the launch-plan override)
+  const int per = ITEMS / p.splits, lo = r * per, hi = r == p.splits - 1 ? ITEMS : lo + per;
   const int rows_all = p.G * p.n_max;
   const int wg0 = ((b * p.Hkv + g) * p.row_blocks + rb) * p.splits;
   for (int base = lo; base < hi; base += 2 * NT) {
@@ -920,11 +922,11 @@ __device__ __forceinline__ void merge_range(const BfParams& p, int b, int g, int
 // split's range; the last arrival also claims and merges every range still
 // unclaimed. Then counts this split out (and the last one out zeroes the
 // words). words: three LDS words, words[0] = the arrival count this split saw.
-template <int WAVES, int QT>
+template <int WAVES, int QT, int S>
 __device__ __forceinline__ void merge_claim_and_run(const BfParams& p, int grp, int s, int b, int g, int rb,
                                                     int rows_live, uint32_t* words, __amdgpu_buffer_rsrc_t rml,
                                                     __amdgpu_buffer_rsrc_t ro) {
-  constexpr int S = 4;   // the fused merge serves up to four splits
+  static_assert(S == 4 || S == 8, "the fused merge serves up to four or eight splits");
   const uint32_t splits = static_cast<uint32_t>(p.splits);
   const uint32_t full = (1u << splits) - 1u, mine = 1u << s;
   uint32_t* w = group_words(p, grp);
@@ -1832,7 +1834,10 @@ __global__ __launch_bounds__(WAVES * 64) void attn_bf16_kernel(BfParams p) {
   if (appends) append_tree();
   if (!fused_merge) return;   // (with several splits the merge kernel follows)
   __syncthreads();
-  merge_claim_and_run<WAVES, QT>(p, grp, s, b, g, rb, rows_live, words, rml, ro);
+  if (p.splits <= 4)
+    merge_claim_and_run<WAVES, QT, 4>(p, grp, s, b, g, rb, rows_live, words, rml, ro);
+  else
+    merge_claim_and_run<WAVES, QT, 8>(p, grp, s, b, g, rb, rows_live, words, rml, ro);
 }
 
 // ---------------------------------------------------------------------------
@@ -1886,8 +1891,10 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(BfParams p) {
 
 // Optional launch-shape override for tuning sweeps, read once:
 // TV_ATTN_TUNE="waves=4,qt=2,splits=4,fused=0" (any subset; 0 = automatic,
-// except fused: 0 = the merge kernel, 1 = automatic).
-struct Tune { int waves = 0, qt = 0, splits = 0, fused = 1; };
+// except fused: 0 = the merge kernel, 1 = the fused merge at up to eight
+// splits when the grid runs at once, 2 = the last split merges; left out =
+// automatic, the fused merge at up to four splits when the grid runs at once).
+struct Tune { int waves = 0, qt = 0, splits = 0, fused = -1; };
 const Tune& tune() {
   static const Tune t = [] {
     Tune r;
@@ -1980,13 +1987,18 @@ AttnPlan plan_attention_bf16(const tv_attn_args* a) {
   // The splits merge in the kernel (no second launch, partials read while
   // still near) when there are at most four and the whole grid runs at once
   // (one workgroup per compute unit); otherwise the merge kernel follows.
+  // (Eight splits can merge in the kernel too, on request: measured slower
+  // than the merge kernel, 89.4 against 85.0 us on 4 sequences of 16384
+  // tokens, 47.6 against 46.6 on 2.)
   // (fused=2 of the override: only the last split to arrive merges, and no
   // split waits, so it also serves grids that do not run at once; measured
   // no faster than the merge kernel there, 161.0 against 160.9 us on 64
   // ragged sequences, and slower at the headline shape, 51.7 against 48.8,
   // where one workgroup then does every group's whole merge)
   const bool at_once = units * splits <= cus;
-  pl.fused = splits > 1 && splits <= 4 && units <= kMaxFusedGroups && ((tn.fused == 1 && at_once) || tn.fused == 2);
+  const int fuse_max = tn.fused < 0 ? 4 : 8;
+  pl.fused = splits > 1 && splits <= fuse_max && units <= kMaxFusedGroups &&
+             ((tn.fused != 0 && tn.fused != 2 && at_once) || tn.fused == 2);
   pl.last_merges = pl.fused && tn.fused == 2;
   pl.workspace_bytes = ws_layout(a, pl).total;
   return pl;
