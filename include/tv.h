@@ -32,13 +32,15 @@
  *     inactive sequence. At most TV_MAX_NODES nodes per tree.
  *   - Integer arrays are int32 unless noted; tensors are row-major in the
  *     shapes given, all of one dtype (TV_F32 or TV_BF16).
- *   - Environment: TV_ATTN_TUNE="waves=W qt=Q splits=S fused=F" (any subset)
- *     overrides the bf16 attention's launch plan (wavefronts per workgroup 2,
- *     4 or 8, query tiles per wavefront 1 or 2, key splits 1..16; fused=0
- *     makes a separate kernel merge the key splits, fused=1 merges up to
- *     eight splits in the attention kernel when its grid runs at once
- *     (automatic: up to four), fused=2 lets only the last split to arrive
- *     merge them), read once per process, for
+ *   - Environment: TV_ATTN_TUNE="waves=W qt=Q splits=S fused=F spin=T"
+ *     (any subset) overrides the bf16 attention's launch plan (wavefronts
+ *     per workgroup 2, 4 or 8, query tiles per wavefront 1 or 2, key splits
+ *     1..16; fused=0 makes a separate kernel merge the key splits, fused=1
+ *     merges up to eight splits in the attention kernel when its grid runs
+ *     at once (automatic: up to four), fused=2 lets only the last split to
+ *     arrive merge them; spin=T bounds the fused merge's wait for the other
+ *     splits at T ticks of 10 ns, 0 = one look, default 20000), read once
+ *     per process, for
  *     tuning sweeps; tv_tree_attention_workspace_size follows the same plan.
  *     Results do not depend on it beyond rounding order.
  */

@@ -293,3 +293,16 @@ def test_paged_fused_host_validation_without_device():
     assert ac_call(pk(), k=None) == _lib.TV_ERR_INVALID_ARG
     assert ac_call(pk(), plen_out=None) == _lib.TV_ERR_INVALID_ARG
     assert ac_call(pk(), B=0, k=None) == _lib.TV_OK
+
+
+def test_no_kernel_spills_registers():
+    """Every kernel of the built library has a zero private segment: no
+    register spills. The attention kernels issue register loads from inline
+    assembly and wait for them by hand, so a spill between such a load and
+    its wait would store a value that has not arrived (the build refuses
+    such a library; this checks the library that is there)."""
+    from tree_attention_verification_tv_amd.build import kernel_private_segments
+    seg = kernel_private_segments(_lib.LIB_PATH)
+    assert sum("attn_bf16_kernel" in k for k in seg) == 16, sorted(seg)
+    assert len(seg) >= 50, len(seg)
+    assert {k: v for k, v in seg.items() if v} == {}

@@ -157,6 +157,11 @@ struct BfParams {
   // 0: no fused merge; 1: every split merges its range (waiting, bounded,
   // for the others); 2: the last split to arrive merges every range
   int fused;
+  // the bounded wait of the fused merge, in ticks of the 100 MHz real-time
+  // clock (the launch-plan override can shorten it, down to one look at the
+  // arrival count, so that the path in which a split leaves its range to the
+  // last arrival runs)
+  uint32_t spin_ticks;
   uint32_t* sync;
   size_t ws_bytes;   // workspace bytes (buffer-resource range of the partials)
 };
@@ -798,7 +803,7 @@ __device__ __forceinline__ void write_tree_values(const BfParams& p, int P, int 
 // them and sc1 loads read from there, so no cache flush or invalidation is
 // needed; the partials may be on another XCD's side.
 // ---------------------------------------------------------------------------
-constexpr uint64_t kSpinTicks = 20000;   // 200 us of the 100 MHz real-time clock
+constexpr uint32_t kSpinTicks = 20000;   // 200 us of the 100 MHz real-time clock (default)
 
 __device__ __forceinline__ uint32_t* group_words(const BfParams& p, int grp) { return p.sync + 4 * static_cast<size_t>(grp); }
 
@@ -950,7 +955,7 @@ __device__ __forceinline__ void merge_claim_and_run(const BfParams& p, int grp, 
           all = true;
           break;
         }
-        if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) break;
+        if (__builtin_amdgcn_s_memrealtime() - t0 >= p.spin_ticks) break;
         __builtin_amdgcn_s_sleep(2);
       }
     }
@@ -1893,8 +1898,10 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(BfParams p) {
 // TV_ATTN_TUNE="waves=4,qt=2,splits=4,fused=0" (any subset; 0 = automatic,
 // except fused: 0 = the merge kernel, 1 = the fused merge at up to eight
 // splits when the grid runs at once, 2 = the last split merges; left out =
-// automatic, the fused merge at up to four splits when the grid runs at once).
-struct Tune { int waves = 0, qt = 0, splits = 0, fused = -1; };
+// automatic, the fused merge at up to four splits when the grid runs at once;
+// spin: the fused merge's bounded wait in 10 ns ticks, 0 = one look at the
+// arrival count, so that waiting splits leave their ranges to the last one).
+struct Tune { int waves = 0, qt = 0, splits = 0, fused = -1, spin = -1; };
 const Tune& tune() {
   static const Tune t = [] {
     Tune r;
@@ -1903,6 +1910,7 @@ const Tune& tune() {
       if (const char* q = strstr(e, "qt=")) sscanf(q, "qt=%d", &r.qt);
       if (const char* s = strstr(e, "splits=")) sscanf(s, "splits=%d", &r.splits);
       if (const char* f = strstr(e, "fused=")) sscanf(f, "fused=%d", &r.fused);
+      if (const char* f = strstr(e, "spin=")) sscanf(f, "spin=%d", &r.spin);
     }
     return r;
   }();
@@ -2091,6 +2099,7 @@ hipError_t launch_attention_bf16(const tv_attn_args* a, const AttnPlan& pl, cons
   p.part_o = pl.splits > 1 ? reinterpret_cast<uint4*>(ws + w.part_o) : nullptr;
   p.sync = pl.splits > 1 ? reinterpret_cast<uint32_t*>(ws + w.sync) : nullptr;
   p.fused = !pl.fused ? 0 : pl.last_merges ? 2 : 1;
+  p.spin_ticks = tune().spin >= 0 ? static_cast<uint32_t>(tune().spin) : kSpinTicks;
   p.ws_bytes = pl.workspace_bytes;
 
   dim3 grid(pl.splits * pl.row_blocks * a->Hkv * a->B);
