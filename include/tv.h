@@ -504,6 +504,30 @@ tv_status tv_accept_commit_paged(const int32_t* cand_tok, const int32_t* tgt_arg
                                  const tv_paged_kv* pk, int32_t Hkv, int32_t D, int32_t dtype,
                                  const int32_t* prefix_len_in, int32_t* prefix_len_out, hipStream_t stream);
 
+/*
+ * tv_v_cache_layout -- converts a V cache between the row layout a model's
+ * KV cache usually has and the blocked layout the calls above read.
+ * Not an operation of the pages: the blocked layout is this library's (it
+ * gives the attention's value-times-probability product contiguous 64-key
+ * runs per head dim), and this call lets a caller that holds rows convert
+ * once, when the prefix is written, instead of per step.
+ *   rows:    [n][cap][D]       slot s, dim d at s*D + d
+ *   blocked: [n][cap/64][D][64] slot s, dim d at ((s/64)*D + d)*64 + s%64
+ * n = B*Hkv for a dense cache ([B][Hkv][...]); for page pools n =
+ * num_pages*Hkv and cap = 64 (a page's V is one block).
+ *   src, dst    device buffers of n*cap*D elements of dtype, 16-byte
+ *               aligned, not overlapping (the conversion is out of place);
+ *               the caller owns both.
+ *   to_rows     0: rows -> blocked; 1: blocked -> rows.
+ * One kernel on stream (a 64 x D transpose per block through LDS; each byte
+ * read and written once). TV_ERR_INVALID_ARG for n < 0, cap not a positive
+ * multiple of 64, a bad dtype or to_rows, null, misaligned or overlapping
+ * buffers; TV_ERR_UNSUPPORTED for D other than 64 or 128 or more than
+ * 2^31 - 1 blocks. n == 0 launches nothing.
+ */
+tv_status tv_v_cache_layout(const void* src, void* dst, int64_t n, int32_t cap, int32_t D, int32_t dtype,
+                            int32_t to_rows, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

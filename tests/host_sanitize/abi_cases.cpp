@@ -345,6 +345,37 @@ void drafting_and_sampling() {
   REACHED(c, "speculative_sample");
 }
 
+void layout() {
+  // addresses only: the checks are arithmetic on them, the stub touches nothing
+  void* a = reinterpret_cast<void*>(uintptr_t{0x10000});
+  void* b = reinterpret_cast<void*>(uintptr_t{0x40000000});
+  auto lay = [](const void* s, void* d, int64_t n, int cap, int D, int dtype, int to_rows) {
+    return tv_v_cache_layout(s, d, n, cap, D, dtype, to_rows, nullptr);
+  };
+  EXPECT(lay(a, b, -1, 128, 128, TV_BF16, 0), TV_ERR_INVALID_ARG);
+  EXPECT(lay(a, b, 16, 0, 128, TV_BF16, 0), TV_ERR_INVALID_ARG);
+  EXPECT(lay(a, b, 16, 100, 128, TV_BF16, 0), TV_ERR_INVALID_ARG);
+  EXPECT(lay(a, b, 16, 128, 128, TV_BF16, 2), TV_ERR_INVALID_ARG);
+  EXPECT(lay(a, b, 16, 128, 128, 7, 0), TV_ERR_INVALID_ARG);
+  EXPECT(lay(a, b, 16, 128, 96, TV_BF16, 0), TV_ERR_UNSUPPORTED);
+  EXPECT(lay(a, b, int64_t{1} << 31, 64, 128, TV_BF16, 0), TV_ERR_UNSUPPORTED);
+  EXPECT(lay(a, b, int64_t{1} << 62, 128, 128, TV_BF16, 0), TV_ERR_UNSUPPORTED);   // n * cap/64 overflows
+  EXPECT(lay(nullptr, b, 16, 128, 128, TV_BF16, 0), TV_ERR_INVALID_ARG);
+  EXPECT(lay(static_cast<char*>(a) + 8, b, 16, 128, 128, TV_BF16, 0), TV_ERR_INVALID_ARG);
+  EXPECT(lay(a, a, 16, 128, 128, TV_BF16, 0), TV_ERR_INVALID_ARG);
+  EXPECT(lay(a, static_cast<char*>(a) + 0x7fff0, 16, 128, 128, TV_BF16, 0), TV_ERR_INVALID_ARG);
+  EXPECT(lay(nullptr, nullptr, 0, 128, 128, TV_BF16, 0), TV_OK);
+  int c = stub::calls;
+  EXPECT(lay(a, static_cast<char*>(a) + 0x80000, 16, 128, 128, TV_BF16, 0), TV_OK);   // adjacent, no overlap
+  REACHED(c, "v_layout_blocked");
+  EXPECT(stub::last.B, 32);
+  EXPECT(stub::last.n_max, 128);
+  c = stub::calls;
+  EXPECT(lay(a, b, 100, 64, 64, TV_F32, 1), TV_OK);
+  REACHED(c, "v_layout_rows");
+  EXPECT(stub::last.elem_bytes, 4);
+}
+
 void strings() {
   for (int s = TV_OK; s <= TV_ERR_SCRATCH; ++s) {
     const char* t = tv_status_string(static_cast<tv_status>(s));
@@ -368,6 +399,7 @@ int main() {
   typical();
   attention();
   drafting_and_sampling();
+  layout();
   strings();
   if (failures) {
     std::printf("failures %d of %d checks\n", failures, checks);

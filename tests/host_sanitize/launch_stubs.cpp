@@ -16,6 +16,10 @@ static void hit(const char* name, int B, int n_max, int elem_bytes, size_t ws_by
 
 namespace tv {
 
+hipError_t launch_v_layout(const void*, void*, long n_blocks, int D, int elem_bytes, bool to_rows, hipStream_t) {
+  stub::hit(to_rows ? "v_layout_rows" : "v_layout_blocked", static_cast<int>(n_blocks), D, elem_bytes, 0, nullptr);
+  return hipSuccess;
+}
 hipError_t launch_build_tree(const int32_t*, const int32_t*, int B, int n_max, uint64_t*, int32_t*, int32_t*,
                              hipStream_t) {
   stub::hit("build_tree", B, n_max, 0, 0, nullptr);

@@ -25,7 +25,7 @@ def test_header_declares_expected_calls():
     names = declared_functions()
     for must in ("tv_build_tree", "tv_tree_attention", "tv_accept", "tv_commit", "tv_accept_typical",
                  "tv_tree_attention_paged", "tv_commit_paged", "tv_eagle2_tree", "tv_speculative_sample",
-                 "tv_tree_attention_paged_from_parents", "tv_accept_commit_paged"):
+                 "tv_tree_attention_paged_from_parents", "tv_accept_commit_paged", "tv_v_cache_layout"):
         assert must in names
 
 
@@ -293,6 +293,32 @@ def test_paged_fused_host_validation_without_device():
     assert ac_call(pk(), k=None) == _lib.TV_ERR_INVALID_ARG
     assert ac_call(pk(), plen_out=None) == _lib.TV_ERR_INVALID_ARG
     assert ac_call(pk(), B=0, k=None) == _lib.TV_OK
+
+
+def test_v_cache_layout_host_validation_without_device():
+    """Every rejection of tv_v_cache_layout happens before any HIP call; no
+    case below reaches a launch (a call that passes every check would)."""
+    lib = _lib.load()
+    a, b = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x20000000)   # never dereferenced
+    BF16, F32 = _lib.TV_BF16, _lib.TV_F32
+
+    def call(src=a, dst=b, n=16, cap=128, D=128, dtype=BF16, to_rows=0):
+        return lib.tv_v_cache_layout(src, dst, n, cap, D, dtype, to_rows, None)
+    assert call(n=-1) == _lib.TV_ERR_INVALID_ARG
+    assert call(cap=0) == _lib.TV_ERR_INVALID_ARG
+    assert call(cap=100) == _lib.TV_ERR_INVALID_ARG
+    assert call(to_rows=2) == _lib.TV_ERR_INVALID_ARG
+    assert call(dtype=7) == _lib.TV_ERR_INVALID_ARG
+    assert call(D=96) == _lib.TV_ERR_UNSUPPORTED
+    assert call(n=0) == _lib.TV_OK                                   # nothing to do, no launch
+    assert call(n=1 << 31, cap=64) == _lib.TV_ERR_UNSUPPORTED         # more than 2^31 - 1 blocks
+    assert call(src=None) == _lib.TV_ERR_INVALID_ARG
+    assert call(dst=None) == _lib.TV_ERR_INVALID_ARG
+    assert call(src=ctypes.c_void_p(0x10008)) == _lib.TV_ERR_INVALID_ARG   # not 16-byte aligned
+    assert call(dst=a) == _lib.TV_ERR_INVALID_ARG                     # in place
+    # 16 * 128 * 128 bf16 = 512 KiB: a buffer starting inside the other overlaps it
+    assert call(dst=ctypes.c_void_p(0x10000 + 0x7fff0)) == _lib.TV_ERR_INVALID_ARG
+    assert call(src=ctypes.c_void_p(0x20000000 + 0x70000), dtype=F32) == _lib.TV_ERR_INVALID_ARG
 
 
 def test_no_kernel_spills_registers():

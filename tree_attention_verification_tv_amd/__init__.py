@@ -31,7 +31,7 @@ __all__ = ["build_tree", "tree_attention", "tree_attention_from_parents", "tree_
            "new_workspace", "accept", "accept_typical", "commit", "eagle2_tree", "speculative_sample",
            "tree_attention_paged", "commit_paged", "pages_from_dense", "dense_from_pages", "TV_ERR_BAD_PAGE", "PAGE",
            "version", "TvError", "TV_ERR_BAD_TREE", "TV_ERR_CAPACITY", "attn_args",
-           "v_cache_blocked", "v_cache_rows", "V_BLOCK"]
+           "v_cache_blocked", "v_cache_rows", "v_cache_layout", "V_BLOCK"]
 
 V_BLOCK = 64   # slots per block of the V cache
 
@@ -482,6 +482,38 @@ def accept_typical(logits, cand_tok, parents, anc, depth, n_nodes, err=None, *, 
         _ptr(n_nodes), _ptr(err), B, n_max, float(epsilon), float(delta), _ptr(entropy), _ptr(p_tok),
         _ptr(tgt_argmax), _ptr(accept_len), _ptr(path), _ptr(bonus), _ptr(out_tokens), _stream(stream)))
     return accept_len, path, bonus, out_tokens, entropy, p_tok, tgt_argmax
+
+
+def v_cache_layout(src, to_rows=False, out=None, stream=None):
+    """tv_v_cache_layout on the GPU: a V cache in rows [..., cap, D] ->
+    blocked [..., cap/64, D, 64] (to_rows False), or blocked -> rows
+    (to_rows True); the leading dims ([B, Hkv], or [num_pages, Hkv] with
+    cap 64) flatten to n. Returns out (allocated when None)."""
+    lib = _lib.load()
+    if src.dtype not in _DTYPES:
+        raise ValueError("V cache must be float32 or bfloat16")
+    _dev(src, "src", src.dtype)
+    if to_rows:
+        if src.dim() < 3 or src.shape[-1] != V_BLOCK:
+            raise ValueError("blocked V must be [..., cap/64, D, 64]")
+        lead, nb, D = tuple(src.shape[:-3]), src.shape[-3], src.shape[-2]
+        cap, shape = nb * V_BLOCK, tuple(src.shape[:-3]) + (nb * V_BLOCK, src.shape[-2])
+    else:
+        if src.dim() < 2 or src.shape[-2] % V_BLOCK:
+            raise ValueError("V rows must be [..., cap, D] with cap a multiple of 64")
+        lead, cap, D = tuple(src.shape[:-2]), src.shape[-2], src.shape[-1]
+        shape = lead + (cap // V_BLOCK, D, V_BLOCK)
+    if out is None:
+        out = torch.empty(shape, dtype=src.dtype, device=src.device)
+    _dev(out, "out", src.dtype)
+    if tuple(out.shape) != shape:
+        raise ValueError(f"out must be {list(shape)}")
+    n = 1
+    for x in lead:
+        n *= x
+    _lib.check("tv_v_cache_layout", lib.tv_v_cache_layout(_ptr(src), _ptr(out), n, cap, D, _DTYPES[src.dtype],
+                                                          1 if to_rows else 0, _stream(stream)))
+    return out
 
 
 def commit(k_cache, v_cache, prefix_len_in, accept_len, path, prefix_len_out=None, stream=None):

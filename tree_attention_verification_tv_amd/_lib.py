@@ -65,6 +65,7 @@ SIGNATURES = {
     "tv_commit_paged": (_I, [_P, _P, ctypes.POINTER(TvPagedKv), _I, _I, _I, _I, _P, _P, _P, _I, _P, _P]),
     "tv_accept_commit_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _P, _P, _P,
                                     ctypes.POINTER(TvPagedKv), _I, _I, _I, _P, _P, _P]),
+    "tv_v_cache_layout": (_I, [_P, _P, ctypes.c_int64, _I, _I, _I, _I, _P]),
 }
 
 _lib = None

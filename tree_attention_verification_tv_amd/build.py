@@ -22,7 +22,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libtv.so")
 
 ARCH = "gfx950"
-SOURCES = ["tv_tree.hip", "tv_typical.hip", "tv_draft.hip", "tv_attn_f32.hip", "tv_attn_bf16.hip", "tv_api.cpp"]
+SOURCES = ["tv_tree.hip", "tv_typical.hip", "tv_draft.hip", "tv_attn_f32.hip", "tv_attn_bf16.hip", "tv_layout.hip",
+           "tv_api.cpp"]
 # Packed fp32 arithmetic is switched off for device code (host passes only
 # warn that they do not know the feature).
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

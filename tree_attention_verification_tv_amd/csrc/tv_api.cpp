@@ -298,4 +298,22 @@ tv_status tv_commit_paged(void* k_pool, void* v_pool, const tv_paged_kv* pk, int
                                     stream));
 }
 
+tv_status tv_v_cache_layout(const void* src, void* dst, int64_t n, int32_t cap, int32_t D, int32_t dtype,
+                            int32_t to_rows, hipStream_t stream) {
+  if (n < 0 || cap < 64 || cap % 64 != 0 || (to_rows != 0 && to_rows != 1)) return TV_ERR_INVALID_ARG;
+  if (!dtype_ok(dtype)) return TV_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return TV_ERR_UNSUPPORTED;
+  if (n == 0) return TV_OK;
+  if (n > 0x7fffffffll / (cap / 64)) return TV_ERR_UNSUPPORTED;   // (more than 2^31 - 1 blocks)
+  const int64_t blocks = n * (cap / 64);
+  if (!src || !dst) return TV_ERR_INVALID_ARG;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+  if (a % 16 != 0 || b % 16 != 0) return TV_ERR_INVALID_ARG;
+  const uintptr_t bytes = static_cast<uintptr_t>(blocks) * 64u * static_cast<uintptr_t>(D) *
+                          static_cast<uintptr_t>(elem_bytes(dtype));
+  if (a < b + bytes && b < a + bytes) return TV_ERR_INVALID_ARG;   // (out of place only)
+  return from_hip(tv::launch_v_layout(src, dst, static_cast<long>(blocks), D, elem_bytes(dtype), to_rows != 0,
+                                      stream));
+}
+
 }  // extern "C"

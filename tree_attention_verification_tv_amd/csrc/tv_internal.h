@@ -48,6 +48,10 @@ hipError_t launch_accept_commit(const int32_t* cand_tok, const int32_t* tgt, con
                                 int32_t* prefix_len_out, const tv_paged_kv* pk, hipStream_t s);
 
 // pk: paged cache (nullptr: the dense layout)
+// V cache layout conversion (tv_layout.hip): n_blocks 64-slot blocks of D
+// dims, rows -> blocked, or blocked -> rows when to_rows.
+hipError_t launch_v_layout(const void* src, void* dst, long n_blocks, int D, int elem_bytes, bool to_rows,
+                           hipStream_t s);
 hipError_t launch_commit(void* k_cache, void* v_cache, int B, int Hkv, int cap, int D,
                          int elem_bytes, const int32_t* prefix_len_in, const int32_t* accept_len,
                          const int32_t* path, int n_max, int32_t* prefix_len_out,
