@@ -815,9 +815,34 @@ __device__ __forceinline__ void merge_arrive(const BfParams& p, int grp, uint32_
   }
 }
 
+// Writes the 32 outputs of one row and head-dim block that lanes l and
+// l + 32 hold as 4-element pieces (lane half h holds elements 8 i4 + 4 h ..
+// + 3, i4 = 0..3): the halves swap pieces so that each lane writes 8
+// contiguous elements twice, 16 bytes each (elements 8 h .. and 16 + 8 h ..
+// from dst, the block's first element). Lanes l and l + 32 must both be
+// active (they hold the same row, so they branch alike).
+__device__ __forceinline__ void store_row32(uint16_t* dst, const uint32_t (&w)[4][2]) {
+  const int h = static_cast<int>(threadIdx.x >> 5) & 1;
+  uint32_t a[2][2], c[2][2];
+#pragma unroll
+  for (int pr = 0; pr < 2; ++pr)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      // lower half: (own piece 2 pr, the upper lane's piece 2 pr); upper
+      // half: (the lower lane's piece 2 pr + 1, own piece 2 pr + 1)
+      const auto r = __builtin_amdgcn_permlane32_swap(w[2 * pr][k], w[2 * pr + 1][k], false, false);
+      a[pr][k] = r[0];
+      c[pr][k] = r[1];
+    }
+#pragma unroll
+  for (int pr = 0; pr < 2; ++pr)
+    *reinterpret_cast<uint4*>(dst + 16 * pr + 8 * h) = make_uint4(a[pr][0], a[pr][1], c[pr][0], c[pr][1]);
+}
+
 // Combines one item (32-row tile wt, head-dim block dt, lane) of S split
 // partials: fp32 weights 2^(r_s - max r) * l_s over the splits that saw a
-// key, fp32 sums, one division; writes the row's 16 values (4 x 8 bytes).
+// key, fp32 sums, one division; writes the row's 16 values (with the other
+// lane half's 16: two 16-byte stores per lane, see store_row32).
 // Partials of copies ss >= splits have weight 0.
 // Every caller gives the 64 lanes of a wavefront the items of one (tile,
 // head-dim block), lane = item lane, so lane 0 holds the tile's lowest row,
@@ -865,10 +890,13 @@ __device__ __forceinline__ void merge_item(int splits, const float2 (&ml)[S], co
       accumulate(std::false_type{});
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  uint32_t w[4][2];   // piece i4: elements 8 i4 + 4 h .. + 3 of the row's 32, h = lane / 32
 #pragma unroll
-  for (int i4 = 0; i4 < 4; ++i4)
-    *reinterpret_cast<uint2*>(dst + 8 * i4) = make_uint2(pack_bf16(acc[i4].x * inv, acc[i4].y * inv),
-                                                        pack_bf16(acc[i4].z * inv, acc[i4].w * inv));
+  for (int i4 = 0; i4 < 4; ++i4) {
+    w[i4][0] = pack_bf16(acc[i4].x * inv, acc[i4].y * inv);
+    w[i4][1] = pack_bf16(acc[i4].z * inv, acc[i4].w * inv);
+  }
+  store_row32(dst, w);
 }
 
 // Merges range r of the row block's items (item = (wt, dt, lane) in the
@@ -879,9 +907,12 @@ __device__ __forceinline__ void merge_range(const BfParams& p, int b, int g, int
                                             __amdgpu_buffer_rsrc_t rml, __amdgpu_buffer_rsrc_t ro) {
   constexpr int ROWS = WAVES * 32 * QT, NT = WAVES * 64, ITEMS = ROWS / 32 * 256;
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-  // (the last range takes the remainder when the split count does not
-  // divide the items, e.g. three splits from the launch-plan override)
-  const int per = ITEMS / p.splits, lo = r * per, hi = r == p.splits - 1 ? ITEMS : lo + per;
+  // Ranges are whole groups of 64 items (one (tile, head-dim block) each),
+  // so every wavefront holds one group with item lane = its own lane, as
+  // merge_item and store_row32 need; the last range takes the remainder when
+  // the split count does not divide the groups (e.g. three splits from the
+  // launch-plan override).
+  const int per = ITEMS / 64 / p.splits * 64, lo = r * per, hi = r == p.splits - 1 ? ITEMS : lo + per;
   const int rows_all = p.G * p.n_max;
   const int wg0 = ((b * p.Hkv + g) * p.row_blocks + rb) * p.splits;
   for (int base = lo; base < hi; base += 2 * NT) {
@@ -912,10 +943,10 @@ __device__ __forceinline__ void merge_range(const BfParams& p, int b, int g, int
       const int row = rb * ROWS + wt * 32 + (lane & 31);
       if (row >= rows_all) continue;
       const int node = p.gdiv.div(row), head = g * p.G + row - node * p.G;
-      uint16_t* dst = p.out + ((static_cast<size_t>(b) * p.n_max + node) * p.Hq + head) * kD + 32 * dt + 4 * (lane >> 5);
+      uint16_t* dst = p.out + ((static_cast<size_t>(b) * p.n_max + node) * p.Hq + head) * kD + 32 * dt;
       if (row >= rows_live) {
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) *reinterpret_cast<uint2*>(dst + 8 * i4) = make_uint2(0u, 0u);
+        for (int pr = 0; pr < 2; ++pr) *reinterpret_cast<uint4*>(dst + 16 * pr + 8 * (lane >> 5)) = make_uint4(0u, 0u, 0u, 0u);
         continue;
       }
       merge_item<S>(p.splits, ml[k], o[k], dst);
@@ -1885,10 +1916,10 @@ __global__ __launch_bounds__(256) void merge_bf16_kernel(BfParams p) {
   if (row >= rows_all) return;
   const int rows_live = sq.skip ? 0 : p.G * sq.n;
   const int node = p.gdiv.div(row), head = g * p.G + row - node * p.G;
-  uint16_t* dst = p.out + ((static_cast<size_t>(b) * p.n_max + node) * p.Hq + head) * kD + 32 * dt + 4 * (lane >> 5);
+  uint16_t* dst = p.out + ((static_cast<size_t>(b) * p.n_max + node) * p.Hq + head) * kD + 32 * dt;
   if (row >= rows_live) {
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) *reinterpret_cast<uint2*>(dst + 8 * i4) = make_uint2(0u, 0u);
+    for (int pr = 0; pr < 2; ++pr) *reinterpret_cast<uint4*>(dst + 16 * pr + 8 * (lane >> 5)) = make_uint4(0u, 0u, 0u, 0u);
     return;
   }
   merge_item<S>(p.splits, ml, o, dst);
