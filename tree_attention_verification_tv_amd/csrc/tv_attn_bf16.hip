@@ -686,12 +686,35 @@ __device__ __forceinline__ void tile_max(float (&mx)[QT], const uint16_t* __rest
   }
 }
 
+// Writes the 32 outputs of one row and head-dim block that lanes l and
+// l + 32 hold as 4-element pieces (lane half h holds elements 8 i4 + 4 h ..
+// + 3, i4 = 0..3): the halves swap pieces so that each lane writes 8
+// contiguous elements twice, 16 bytes each (elements 8 h .. and 16 + 8 h ..
+// from dst, the block's first element). Lanes l and l + 32 must both be
+// active (they hold the same row, so they branch alike).
+__device__ __forceinline__ void store_row32(uint16_t* dst, const uint32_t (&w)[4][2]) {
+  const int h = static_cast<int>(threadIdx.x >> 5) & 1;
+  uint32_t a[2][2], c[2][2];
+#pragma unroll
+  for (int pr = 0; pr < 2; ++pr)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      // lower half: (own piece 2 pr, the upper lane's piece 2 pr); upper
+      // half: (the lower lane's piece 2 pr + 1, own piece 2 pr + 1)
+      const auto r = __builtin_amdgcn_permlane32_swap(w[2 * pr][k], w[2 * pr + 1][k], false, false);
+      a[pr][k] = r[0];
+      c[pr][k] = r[1];
+    }
+#pragma unroll
+  for (int pr = 0; pr < 2; ++pr)
+    *reinterpret_cast<uint4*>(dst + 16 * pr + 8 * h) = make_uint4(a[pr][0], a[pr][1], c[pr][0], c[pr][1]);
+}
+
 // Writes normalised rows of one wavefront (lane: row row0 + 32 t + l%32,
 // dims 32 dt + 8 i4 + 4 h + 0..3); dead rows get zeros.
 template <int QT>
 __device__ __forceinline__ void write_rows(const BfParams& p, int b, int g, int row0, int rows_live, int rows_all,
                                            int lane, const f32x16 (&o)[QT][4], const float (&l)[QT]) {
-  const int h = lane >> 5;
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
     const int row = row0 + 32 * t + (lane & 31);
@@ -701,14 +724,15 @@ __device__ __forceinline__ void write_rows(const BfParams& p, int b, int g, int 
       uint16_t* orow = p.out + ((static_cast<size_t>(b) * p.n_max + node) * p.Hq + head) * kD;
       const float inv = (live && l[t] > 0.0f) ? 1.0f / l[t] : 0.0f;
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+      for (int dt = 0; dt < 4; ++dt) {
+        uint32_t w[4][2];
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
-          uint2 w;
-          w.x = live ? pack_bf16(o[t][dt][4 * i4 + 0] * inv, o[t][dt][4 * i4 + 1] * inv) : 0u;
-          w.y = live ? pack_bf16(o[t][dt][4 * i4 + 2] * inv, o[t][dt][4 * i4 + 3] * inv) : 0u;
-          *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * i4 + 4 * h) = w;
+          w[i4][0] = live ? pack_bf16(o[t][dt][4 * i4 + 0] * inv, o[t][dt][4 * i4 + 1] * inv) : 0u;
+          w[i4][1] = live ? pack_bf16(o[t][dt][4 * i4 + 2] * inv, o[t][dt][4 * i4 + 3] * inv) : 0u;
         }
+        store_row32(orow + 32 * dt, w);
+      }
     }
   }
 }
@@ -813,30 +837,6 @@ __device__ __forceinline__ void merge_arrive(const BfParams& p, int grp, uint32_
     uint32_t* w = group_words(p, grp);
     words[0] = __hip_atomic_fetch_add(&w[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
   }
-}
-
-// Writes the 32 outputs of one row and head-dim block that lanes l and
-// l + 32 hold as 4-element pieces (lane half h holds elements 8 i4 + 4 h ..
-// + 3, i4 = 0..3): the halves swap pieces so that each lane writes 8
-// contiguous elements twice, 16 bytes each (elements 8 h .. and 16 + 8 h ..
-// from dst, the block's first element). Lanes l and l + 32 must both be
-// active (they hold the same row, so they branch alike).
-__device__ __forceinline__ void store_row32(uint16_t* dst, const uint32_t (&w)[4][2]) {
-  const int h = static_cast<int>(threadIdx.x >> 5) & 1;
-  uint32_t a[2][2], c[2][2];
-#pragma unroll
-  for (int pr = 0; pr < 2; ++pr)
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      // lower half: (own piece 2 pr, the upper lane's piece 2 pr); upper
-      // half: (the lower lane's piece 2 pr + 1, own piece 2 pr + 1)
-      const auto r = __builtin_amdgcn_permlane32_swap(w[2 * pr][k], w[2 * pr + 1][k], false, false);
-      a[pr][k] = r[0];
-      c[pr][k] = r[1];
-    }
-#pragma unroll
-  for (int pr = 0; pr < 2; ++pr)
-    *reinterpret_cast<uint4*>(dst + 16 * pr + 8 * h) = make_uint4(a[pr][0], a[pr][1], c[pr][0], c[pr][1]);
 }
 
 // Combines one item (32-row tile wt, head-dim block dt, lane) of S split
